@@ -1,0 +1,435 @@
+"""Pins that fix the oracle independently of itself.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError when the
+module disagrees with something the pages or the mathematics fix: a
+hand-worked example, a brute-force definition on tiny inputs, a closed form,
+an invariant, or a library routine of a *different* operation that the
+method reduces to in a special case (torch's scaled_dot_product_attention
+when no span is summarised, a constructed SVD with known factors).
+
+The same pins are run against mutated copies of the oracle (see
+test_oracle_mutants.py) to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+
+def _close(a, b, tol, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ----------------------------------------------------------------- segmentation
+
+def pin_segment_hand(O):
+    """Worked by hand from Metodologia 1: the top-n_a surprisal tokens are
+    anchors; runs strictly between neighbouring anchors are spans; lead and
+    tail runs stay at full resolution; adjacent anchors make no span."""
+    H = np.array([0.5, 3.0, 0.1, 0.2, 2.0, 2.5, 0.3, 4.0, 0.1, 0.2], np.float32)
+    sg = O.segment(H, 4)            # anchors at 7 (4.0), 1 (3.0), 5 (2.5), 4 (2.0)
+    assert sg["span_id"].tolist() == [-2, -1, 0, 0, -1, -1, 1, -1, -2, -2]
+    assert sg["span_start"].tolist() == [2, 6]
+    assert sg["span_len"].tolist() == [2, 1]
+    assert sg["fr_pos"].tolist() == [0, 1, 4, 5, 7, 8, 9]
+    assert sg["n_a"] == 4
+
+
+def pin_segment_ties_hand(O):
+    """Equal surprisal: the lower position wins the last anchor slot."""
+    H = np.array([0.5, 3.0, 0.1, 0.2, 2.0, 2.0, 0.3, 4.0, 0.1, 0.2], np.float32)
+    sg = O.segment(H, 3)            # 7, 1, then 4 beats 5
+    assert sg["span_id"].tolist() == [-2, -1, 0, 0, -1, 1, 1, -1, -2, -2]
+    sg = O.segment(np.zeros(6, np.float32), 2)   # all tied: positions 0, 1
+    assert sg["span_id"].tolist() == [-1, -1, -2, -2, -2, -2]
+    Hz = np.array([-0.0, 0.0, 1.0, -0.0], np.float32)  # -0 == +0: 2, then 0
+    assert O.segment(Hz, 2)["span_id"].tolist() == [-1, 0, -1, -2]
+
+
+def pin_n_anchors(O):
+    """floor(p*T) for the five workloads' (p, T), computed by hand."""
+    assert O.n_anchors(2048, 0.05) == 102
+    assert O.n_anchors(32768, 0.04) == 1310
+    assert O.n_anchors(131072, 0.03) == 3932
+    assert O.n_anchors(32768, 0.05) == 1638
+    assert O.n_anchors(1048576, 0.02) == 20971
+    assert O.n_anchors(100, 0.0) == 0
+    assert O.n_anchors(100, 1.0) == 100
+
+
+def _brute_segment(H, n_a):
+    T = len(H)
+    rank = [sum(1 for u in range(T) if H[u] > H[t] or (H[u] == H[t] and u < t))
+            for t in range(T)]
+    anchor = [rk < n_a for rk in rank]
+    spans = []
+    for i in range(T):
+        for j in range(i + 2, T):
+            if anchor[i] and anchor[j] and not any(anchor[i + 1:j]):
+                spans.append((i + 1, j - i - 1))
+    sid = [-1 if anchor[t] else -2 for t in range(T)]
+    for k, (st, ln) in enumerate(sorted(spans)):
+        for t in range(st, st + ln):
+            sid[t] = k
+    return sid, sorted(spans)
+
+
+def pin_segment_bruteforce(O):
+    """Brute-force rank definition on every T <= 12, random and tie-heavy H."""
+    rng = np.random.default_rng(11)
+    for T in range(1, 13):
+        for trial in range(12):
+            if trial % 3 == 0:
+                H = rng.integers(0, 3, T).astype(np.float32)
+            elif trial % 3 == 1:
+                H = rng.choice(np.array([-0.0, 0.0, 1.5], np.float32), T)
+            else:
+                H = rng.standard_normal(T).astype(np.float32)
+            for n_a in range(T + 1):
+                sg = O.segment(H, n_a)
+                sid, spans = _brute_segment([float(x) for x in H], n_a)
+                assert sg["span_id"].tolist() == sid, (H, n_a)
+                got = list(zip(sg["span_start"].tolist(), sg["span_len"].tolist()))
+                assert got == spans
+                assert sg["fr_pos"].tolist() == [t for t in range(T) if sid[t] < 0]
+
+
+# ---------------------------------------------------------------- summaries
+
+def pin_summary_equal_keys(O):
+    """All keys of a span equal a unit vector u: the summary is u."""
+    rng = np.random.default_rng(1)
+    u = rng.standard_normal(16)
+    u /= np.linalg.norm(u)
+    H = rng.exponential(1.0, 9)
+    _close(O.span_summary(H, np.tile(u, (9, 1))), u, 1e-15, "equal keys")
+
+
+def pin_summary_weighted_hand(O):
+    """Surprisal-weighted (Metodologia 2), then normalised: keys e1, e2 with
+    H = (3, 1) give (3, 1)/sqrt(10)."""
+    K = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0]])
+    _close(O.span_summary(np.array([3.0, 1.0]), K),
+           np.array([3.0, 1.0, 0.0]) / math.sqrt(10.0), 1e-15, "weighted")
+
+
+def pin_summary_constant_weight(O):
+    """Constant surprisal: the summary is the normalised plain mean."""
+    rng = np.random.default_rng(2)
+    K = rng.standard_normal((7, 12))
+    m = np.mean(K, axis=0)
+    _close(O.span_summary(np.full(7, 2.5), K), m / np.linalg.norm(m), 1e-14, "const H")
+
+
+def pin_summary_norm_and_scale(O):
+    """Unit norm; invariant to a positive rescaling of the surprisal."""
+    rng = np.random.default_rng(3)
+    for n in (1, 2, 5, 40):
+        K = rng.standard_normal((n, 32))
+        H = rng.lognormal(0, 1, n)
+        s = O.span_summary(H, K)
+        assert abs(np.linalg.norm(s) - 1.0) <= 1e-14
+        _close(O.span_summary(7.25 * H, K), s, 1e-14, "scale")
+    _close(O.span_summary(np.ones(3), np.zeros((3, 4))), np.zeros(4), 0, "zero")
+
+
+def pin_value_mean(O):
+    """Unexpanded value: numpy's mean; constant values give the constant."""
+    rng = np.random.default_rng(4)
+    V = rng.standard_normal((13, 8))
+    _close(O.span_value_mean(V), np.mean(V, axis=0), 1e-15, "mean")
+    _close(O.span_value_mean(np.tile([1.5, -2.0], (5, 1))), [1.5, -2.0], 0, "const")
+
+
+def pin_bf16_rounding(O):
+    """Round-to-nearest-even to 8 significant bits, worked by hand, and the
+    generator's independent fp32->bf16 rounding on fp32-exact values."""
+    r = O.round_stored(np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8,
+                                 1.0 + 2.0 ** -8 + 2.0 ** -30, -(1.0 + 2.0 ** -8),
+                                 0.0, 2.0 - 2.0 ** -9]), "bf16")
+    assert r.tolist() == [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7,
+                          -1.0, 0.0, 2.0]
+    from routed_sparse_kv_amd import workloads as W
+    x = np.random.default_rng(5).standard_normal(4096).astype(np.float32)
+    via_gen = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).astype(np.float64)
+    _close(O.round_stored(x.astype(np.float64), "bf16"), via_gen, 0, "bf16 vs gen")
+    _close(O.round_stored(np.array([1.0 + 2.0 ** -30]), "f32"), [1.0], 0, "f32")
+
+
+# ---------------------------------------------------------------- SVD factors
+
+def _householder_basis(rng, n, m):
+    """n x m matrix with orthonormal columns from three Householder reflectors."""
+    Q = np.eye(n)
+    for _ in range(3):
+        v = rng.standard_normal(n)
+        Q = Q - 2.0 * np.outer(Q @ v, v) / (v @ v)
+    return Q[:, :m]
+
+
+def pin_svd_constructed(O):
+    """X = U diag(sig) W^T built from known orthonormal U, W: the rank-r
+    factors reproduce sum_{i<r} sig_i u_i w_i^T (Eckart-Young's minimiser),
+    the residual is sum_{i>=r} sig_i^2, and W_r has orthonormal rows."""
+    rng = np.random.default_rng(6)
+    for n, d, r in ((9, 16, 4), (20, 8, 3), (12, 12, 5), (6, 32, 8)):
+        m = min(n, d)
+        U = _householder_basis(rng, n, m)
+        Wm = _householder_basis(rng, d, m)
+        sig = np.sort(rng.uniform(0.5, 10.0, m))[::-1] + np.arange(m)[::-1]
+        X = (U * sig) @ Wm.T
+        A, Wt = O.truncated_svd(X, r)
+        rj = min(r, n, d)
+        assert A.shape == (n, r) and Wt.shape == (r, d)
+        best = (U[:, :rj] * sig[:rj]) @ Wm[:, :rj].T
+        _close(A @ Wt, best, 1e-11 * sig[0], "rank-r product")
+        res = np.sum((X - A @ Wt) ** 2)
+        assert abs(res - np.sum(sig[rj:] ** 2)) <= 1e-9 * np.sum(sig ** 2)
+        _close(Wt[:rj] @ Wt[:rj].T, np.eye(rj), 1e-12, "orthonormal W")
+        _close(A, X @ Wt.T, 1e-11 * sig[0], "A = X W")
+        assert not np.any(A[:, rj:]) and not np.any(Wt[rj:])
+
+
+def pin_svd_full_rank_exact(O):
+    """r >= min(|S|, d): the factors rebuild the span exactly."""
+    rng = np.random.default_rng(7)
+    for n, d in ((1, 8), (3, 8), (8, 3), (16, 16)):
+        X = rng.standard_normal((n, d))
+        A, Wt = O.truncated_svd(X, max(n, d) + 2)
+        _close(A @ Wt, X, 1e-12, "full rank")
+
+
+def pin_svd_eckart_young(O):
+    """No rank-r projection of X onto random subspaces beats the factors."""
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((24, 16)) + np.outer(rng.standard_normal(24), rng.standard_normal(16))
+    r = 4
+    A, Wt = O.truncated_svd(X, r)
+    best = np.sum((X - A @ Wt) ** 2)
+    for _ in range(200):
+        Qm, _ = np.linalg.qr(rng.standard_normal((16, r)))
+        assert np.sum((X - X @ Qm @ Qm.T) ** 2) >= best - 1e-9
+
+
+# ------------------------------------------------------------------ routing
+
+def _basis_route(O, zvals, tau, k, alpha=8.0):
+    """s_j = e_j and q = z/alpha make alpha<q, s_j> equal z_j exactly."""
+    n = len(zvals)
+    return O.route_unit(np.eye(n), (np.asarray(zvals) / alpha)[None, :], tau, k, alpha)
+
+
+def pin_route_bruteforce(O):
+    """Expansion set = the unique subset of the candidates (z > tau) of size
+    min(|C|, k_max) whose every member precedes every non-member in the
+    (z descending, index ascending) order; checked by enumeration."""
+    rng = np.random.default_rng(9)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        z = rng.integers(-3, 4, n).astype(np.float64) / 2.0   # many ties
+        tau = float(rng.choice([-1.0, -0.5, 0.0, 0.25, 1.0]))
+        k = int(rng.integers(0, n + 2))
+        C = [j for j in range(n) if z[j] > tau]
+        size = min(len(C), k)
+        ok = []
+        for E in itertools.combinations(C, size):
+            rest = [j for j in C if j not in E]
+            if all(z[a] > z[b] or (z[a] == z[b] and a < b) for a in E for b in rest):
+                ok.append(list(E))
+        assert len(ok) == 1
+        rt = _basis_route(O, z, tau, k)
+        assert rt["E"].tolist() == ok[0], (z, tau, k, rt["E"])
+        _close(rt["z"], z, 0, "z closed form")
+
+
+def pin_route_extremes(O):
+    """tau = +inf selects nothing; tau = -inf with k >= n_s selects all;
+    k_max = 0 selects nothing; the gate exceeds 1/2 exactly on candidates."""
+    z = np.array([0.5, -2.0, 3.0, 0.0, 1.0])
+    assert _basis_route(O, z, math.inf, 5)["E"].tolist() == []
+    assert _basis_route(O, z, -math.inf, 5)["E"].tolist() == [0, 1, 2, 3, 4]
+    assert _basis_route(O, z, -math.inf, 0)["E"].tolist() == []
+    rt = _basis_route(O, z, 0.0, 5)
+    assert rt["E"].tolist() == [0, 2, 4]
+    assert ((rt["gate"] > 0.5) == (z > 0.0)).all()
+    _close(rt["gate"], 1.0 / (1.0 + np.exp(-z)), 1e-15, "gate")
+    rt = _basis_route(O, np.array([1e-6, 2.0, 0.5, 0.5 + 1e-7]), 0.0, 2)
+    assert rt["near_tau"].tolist() == [0] and rt["rank_tie"]
+
+
+def pin_route_projection(O):
+    """rho = P q-bar: a permutation P permutes z; P = c I scales it."""
+    n = 6
+    q = np.array([[0.3, -0.2, 0.9, 0.1, -0.7, 0.4]])
+    perm = np.array([3, 0, 5, 1, 2, 4])
+    Pm = np.eye(n)[perm]                   # (P q)_j = q_perm[j]
+    rt = O.route_unit(np.eye(n), q, 0.0, n, 8.0, Pm)
+    _close(rt["z"], 8.0 * q[0, perm], 1e-15, "permutation")
+    rt = O.route_unit(np.eye(n), q, 0.0, n, 8.0, 2.0 * np.eye(n))
+    _close(rt["z"], 16.0 * q[0], 1e-15, "scaled")
+
+
+def pin_route_group_mean(O):
+    """One decision per KV head from the mean of its G queries."""
+    rng = np.random.default_rng(10)
+    s = rng.standard_normal((7, 5))
+    qg = rng.standard_normal((3, 5))
+    a = O.route_unit(s, qg, 0.1, 3)
+    b = O.route_unit(s, qg.mean(axis=0)[None, :], 0.1, 3)
+    _close(a["z"], b["z"], 1e-14, "group mean")
+    assert a["E"].tolist() == b["E"].tolist()
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa(q, K, V):
+    """torch SDPA in fp64: q [B][Hq][d], K/V [B][Hkv][T][d] (GQA grouping)."""
+    qt = torch.from_numpy(np.ascontiguousarray(q))[:, :, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(K))
+    vt = torch.from_numpy(np.ascontiguousarray(V))
+    o = F.scaled_dot_product_attention(qt, kt, vt, enable_gqa=True)
+    return o[:, :, 0, :].numpy()
+
+
+def _rand_kv(rng, B, Hkv, T, d):
+    return (rng.standard_normal((B, Hkv, T, d)) * 1.5,
+            rng.standard_normal((B, Hkv, T, d)))
+
+
+def pin_attend_all_anchors(O):
+    """p = 1: every token is an anchor and decode is dense attention."""
+    rng = np.random.default_rng(12)
+    B, Hkv, G, T, d = 2, 2, 3, 37, 16
+    K, V = _rand_kv(rng, B, Hkv, T, d)
+    H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    c = O.build_cache(H, K, V, 4, 1.0, "f64", Hq=Hkv * G)
+    assert c["n_s"].tolist() == [0, 0]
+    q = rng.standard_normal((B, Hkv * G, d))
+    out = O.decode_step(c, q, 0.0, 4)["out"]
+    _close(out, _sdpa(q, K, V), 1e-12, "all anchors")
+
+
+def pin_attend_no_anchors(O):
+    """p = 0: no anchors, the whole context stays at full resolution."""
+    rng = np.random.default_rng(13)
+    B, Hkv, G, T, d = 1, 3, 2, 29, 8
+    K, V = _rand_kv(rng, B, Hkv, T, d)
+    H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    c = O.build_cache(H, K, V, 2, 0.0, "f64", Hq=Hkv * G)
+    q = rng.standard_normal((B, Hkv * G, d))
+    _close(O.decode_step(c, q, 0.0, 3)["out"], _sdpa(q, K, V), 1e-12, "no anchors")
+
+
+def pin_attend_full_rank_expanded(O):
+    """Every span expanded at full rank (tau = -inf, k >= n_s): the rebuilt
+    tokens are exact and decode is dense attention over the real tokens."""
+    rng = np.random.default_rng(14)
+    B, Hkv, G, T, d = 2, 2, 2, 64, 8
+    K, V = _rand_kv(rng, B, Hkv, T, d)
+    H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    c = O.build_cache(H, K, V, d, 0.2, "f64", Hq=Hkv * G)
+    assert (c["n_s"] > 3).all()
+    q = rng.standard_normal((B, Hkv * G, d))
+    res = O.decode_step(c, q, -math.inf, int(c["n_s"].max()))
+    for (b, h), rt in res["routes"].items():
+        assert rt["E"].tolist() == list(range(int(c["n_s"][b])))
+    _close(res["out"], _sdpa(q, K, V), 1e-11, "full rank expanded")
+
+
+def _structured_sequence(rng, T, d, anchors):
+    H = rng.uniform(0.1, 1.0, T).astype(np.float32)
+    H[anchors] = 5.0 + np.arange(len(anchors), dtype=np.float32)
+    return H
+
+
+def pin_attend_equal_key_closed_form(O):
+    """Span keys all equal to a unit u and the span left unexpanded: the
+    summary entry exp(<q,u>/sqrt(d) + ln|S|) v-bar equals the sum over the
+    span's real tokens, so decode equals dense attention over the context."""
+    rng = np.random.default_rng(15)
+    B, Hkv, G, T, d = 1, 2, 3, 40, 8
+    anchors = np.array([3, 9, 10, 17, 30, 33])
+    H = _structured_sequence(rng, T, d, anchors)[None, :]
+    K, V = _rand_kv(rng, B, Hkv, T, d)
+    sg = O.segment(H[0], len(anchors))
+    for h in range(Hkv):
+        for st, ln in zip(sg["span_start"], sg["span_len"]):
+            u = rng.standard_normal(d)
+            K[0, h, st:st + ln] = u / np.linalg.norm(u)
+    c = O.build_cache(H, K, V, 2, len(anchors) / T, "f64", Hq=Hkv * G)
+    assert c["n_s"][0] == len(sg["span_len"]) == 4
+    q = 3.0 * rng.standard_normal((B, Hkv * G, d))
+    out = O.decode_step(c, q, math.inf, 4)["out"]
+    _close(out, _sdpa(q, K, V), 1e-12, "closed form")
+
+
+def pin_attend_constant_values(O):
+    """All values equal c: the output is c whatever the selection."""
+    rng = np.random.default_rng(16)
+    B, Hkv, G, T, d = 2, 1, 4, 50, 8
+    K, _ = _rand_kv(rng, B, Hkv, T, d)
+    cval = rng.standard_normal(d)
+    V = np.tile(cval, (B, Hkv, T, 1))
+    H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    c = O.build_cache(H, K, V, 2, 0.15, "f64", Hq=Hkv * G)
+    q = rng.standard_normal((B, Hkv * G, d))
+    for tau, k in ((0.0, 2), (math.inf, 0), (-math.inf, 100)):
+        out = O.decode_step(c, q, tau, k)["out"]
+        _close(out, np.broadcast_to(cval, out.shape), 1e-12, "constant V")
+
+
+def pin_attend_convex_hull(O):
+    """Each output coordinate lies between the min and max of the values
+    that entered the softmax (tokens, rebuilt tokens, span means)."""
+    rng = np.random.default_rng(17)
+    B, Hkv, G, T, d = 1, 2, 2, 80, 8
+    K, V = _rand_kv(rng, B, Hkv, T, d)
+    H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    c = O.build_cache(H, K, V, 3, 0.1, "f64", Hq=Hkv * G)
+    q = 4.0 * rng.standard_normal((B, Hkv * G, d))
+    res = O.decode_step(c, q, 0.0, 3)
+    for (b, h), rt in res["routes"].items():
+        ns, nf = int(c["n_s"][b]), int(c["n_F"][b])
+        offs = np.concatenate([[0], np.cumsum(c["span_len"][b, :ns])])
+        vals = [c["VF"][b, h, :nf], c["vbar"][b, h, :ns]]
+        for j in rt["E"]:
+            vals.append(c["AV"][b, h, offs[j]:offs[j + 1]] @ c["BV"][b, h, j])
+        allv = np.concatenate(vals)
+        o = res["out"][b, h * G:(h + 1) * G]
+        assert (o >= allv.min(axis=0) - 1e-12).all() and (o <= allv.max(axis=0) + 1e-12).all()
+
+
+def pin_append(O):
+    """Appended tokens join the full-resolution set: with p = 1 decode after
+    two appends is dense attention over context + appended tokens."""
+    rng = np.random.default_rng(18)
+    B, Hkv, G, T, d = 2, 2, 2, 20, 8
+    K, V = _rand_kv(rng, B, Hkv, T, d)
+    H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    c = O.build_cache(H, K, V, 2, 1.0, "f64", Hq=Hkv * G, tail_capacity=2)
+    Ks, Vs = [K], [V]
+    for _ in range(2):
+        k1, v1 = _rand_kv(rng, B, Hkv, 1, d)
+        O.append_kv(c, k1[:, :, 0], v1[:, :, 0])
+        Ks.append(k1)
+        Vs.append(v1)
+    q = rng.standard_normal((B, Hkv * G, d))
+    _close(O.decode_step(c, q, 0.0, 2)["out"],
+           _sdpa(q, np.concatenate(Ks, 2), np.concatenate(Vs, 2)), 1e-12, "append")
+    try:
+        O.append_kv(c, k1[:, :, 0], v1[:, :, 0])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("append past the tail capacity must fail")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
