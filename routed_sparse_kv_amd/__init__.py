@@ -1,0 +1,7 @@
+"""Span-routed mixed-resolution KV-cache decode for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``lib/librskv.so`` (C ABI declared in
+``include/rskv.h``); this package only marshals arguments to it.
+"""
+from .binding import (BF16, F32, Cache, RskvError, append_kv, build_spans, cache_import,  # noqa: F401
+                      decode_step, lib, version)

@@ -1,0 +1,120 @@
+// Device helpers shared by the rskv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace rskv {
+
+constexpr int kWave = 64;
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp64 -> bf16, round to nearest, ties to even, done on the fp64 pattern:
+// bf16 keeps 7 explicit mantissa bits of the 52, so 45 low bits are dropped.
+// The rounded value has 8 significant bits and converts to fp32 exactly.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  u += ((1ull << 44) - 1ull) + ((u >> 45) & 1ull);
+  u &= ~((1ull << 45) - 1ull);
+  const float f = static_cast<float>(__longlong_as_double(static_cast<long long>(u)));
+  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+// Element access by storage type.  F32 arrays hold float, BF16 raw bits.
+template <int DT> struct Elem;
+template <> struct Elem<kF32> {
+  typedef float T;
+  static __device__ __forceinline__ float ld(const T* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ T from_f64(double x) { return static_cast<float>(x); }
+  static __device__ __forceinline__ T from_f32(float x) { return x; }
+};
+template <> struct Elem<kBF16> {
+  typedef uint16_t T;
+  static __device__ __forceinline__ float ld(const T* p, size_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ T from_f64(double x) { return f64_to_bf16(x); }
+  static __device__ __forceinline__ T from_f32(float x) { return f64_to_bf16(static_cast<double>(x)); }
+};
+
+// -------------------------------------------------------------- orderings
+
+// Monotone map of fp32 onto uint32 (ascending), with -0 folded onto +0.
+__device__ __forceinline__ uint32_t f32_order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Monotone map of fp64 onto uint64 (ascending), with -0 folded onto +0.
+__device__ __forceinline__ unsigned long long f64_order_key(double x) {
+  unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  if ((u << 1) == 0ull) u = 0ull;
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// ------------------------------------------------------------ reductions
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <typename T>
+__device__ __forceinline__ T group_sum(T v, int width) {
+  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over the whole block (blockDim.x a multiple of 64,
+// at most 1024).  `scratch` holds >= 17 ints of shared memory.  Returns the
+// exclusive prefix of v and the block total in *total.  Contains barriers:
+// every thread of the block must call it.
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) scratch[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < nw ? scratch[lane] : 0;
+    int ws = wave_incl_scan(w);
+    if (lane < nw) scratch[lane] = ws - w;
+    if (lane == nw - 1) scratch[16] = ws;
+  }
+  __syncthreads();
+  const int r = scratch[wid] + incl - v;
+  *total = scratch[16];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace rskv

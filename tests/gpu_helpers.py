@@ -1,0 +1,124 @@
+"""Helpers for the GPU parity tests: device transfer, export -> oracle view,
+selection comparison with the ambiguity band."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(arr, dtype_name, device="cuda"):
+    import torch
+    if dtype_name == "bf16" and arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def gpu_build(wl, device="cuda", **over):
+    import torch
+
+    import routed_sparse_kv_amd as rskv
+    cfg = dict(wl.cfg)
+    cfg.update(over)
+    dt = cfg["dtype"]
+    H = torch.from_numpy(wl.H).to(device)
+    K = dev_tensor(wl.K, dt, device)
+    V = dev_tensor(wl.V, dt, device)
+    P = torch.from_numpy(wl.P).to(device) if wl.P is not None else None
+    cache = rskv.build_spans(H, K, V, cfg["rank"], cfg["anchor_frac"], n_q_heads=cfg["Hq"],
+                             alpha=cfg["alpha"], proj=P, tail_capacity=cfg["tail_capacity"],
+                             k_max_cap=cfg.get("k_max_cap", 0))
+    del K, V
+    return cache
+
+
+def oracle_view(ex):
+    """Canonical export -> the oracle's cache dictionary (fp64 values)."""
+    info = ex["info"]
+    dt = "bf16" if info["dtype"] == 1 else "f32"
+    f = lambda k: oracle.from_stored(ex[k], dt)  # noqa: E731
+    return dict(B=info["batch"], Hq=info["n_q_heads"], Hkv=info["n_kv_heads"],
+                d=info["head_dim"], T=info["context_len"], rank=info["rank"], dtype=dt,
+                tail_capacity=info["tail_capacity"], appended=info["appended"],
+                n_s=ex["n_spans"].astype(np.int64), n_F=ex["n_full"].astype(np.int64),
+                n_a=ex["n_anchor"].astype(np.int64), nt=ex["n_span_tokens"].astype(np.int64),
+                span_id=ex["span_id"], span_start=ex["span_start"].astype(np.int64),
+                span_len=ex["span_len"].astype(np.int64), fr_pos=ex["full_pos"].astype(np.int64),
+                s=f("summary"), vbar=f("vmean"), ell=ex["log_len"].astype(np.float64),
+                KF=f("k_full"), VF=f("v_full"), AK=f("a_k"), AV=f("a_v"), BK=f("w_k"),
+                BV=f("w_v"))
+
+
+def decode_gpu(cache, q_np, tau, k_max, device="cuda"):
+    """Returns (out [B][Hq][d] fp64, sel lists [b][h])."""
+    import torch
+
+    import routed_sparse_kv_amd as rskv
+    i = cache.info
+    B, Hkv = i["batch"], i["n_kv_heads"]
+    dt = "bf16" if i["dtype"] == 1 else "f32"
+    q = dev_tensor(q_np, dt, device)
+    sel = torch.full((B, Hkv, k_max), -7, dtype=torch.int32, device=device) if k_max > 0 else None
+    nsel = torch.full((B, Hkv), -7, dtype=torch.int32, device=device)
+    out = rskv.decode_step(cache, q, tau, k_max, sel=sel, n_sel=nsel)
+    torch.cuda.synchronize()
+    s = sel.cpu().numpy() if sel is not None else np.zeros((B, Hkv, 0), np.int32)
+    n = nsel.cpu().numpy()
+    sels = [[s[b, h, :n[b, h]].astype(np.int64) for h in range(Hkv)] for b in range(B)]
+    if k_max > 0:
+        for b in range(B):
+            for h in range(Hkv):
+                assert (s[b, h, n[b, h]:k_max] == -1).all(), "sel padding must be -1"
+    return out.cpu().numpy().astype(np.float64), sels
+
+
+def check_selection(rt, gsel, tau, k_max, what=""):
+    """GPU selection equals the oracle's, except spans inside the ambiguity
+    band (|z - tau| <= band, or tied with the k-th largest within the band).
+    Returns the number of excused spans."""
+    E = rt["E"]
+    if np.array_equal(E, gsel):
+        return 0
+    z = rt["z"]
+    diff = np.setxor1d(E, gsel)
+    band = oracle.AMBIGUITY_BAND
+    ok = np.abs(z[diff] - tau) <= band
+    if rt["rank_tie"] or len(E) == k_max:
+        cand = np.flatnonzero(z > tau)
+        zs = np.sort(z[cand])[::-1]
+        if k_max > 0 and len(zs) >= k_max:
+            ok |= np.abs(z[diff] - zs[k_max - 1]) <= band
+    assert ok.all(), (f"{what}: selections differ outside the ambiguity band: "
+                      f"oracle-only {np.setdiff1d(E, gsel)[:10]}, gpu-only "
+                      f"{np.setdiff1d(gsel, E)[:10]}")
+    assert len(gsel) == len(E) or k_max == 0, f"{what}: selection sizes differ"
+    return int(len(diff))
+
+
+def compare_decode(oc, q_np, out_gpu, sels, tau, k_max, alpha, P, dtype, units=None, what=""):
+    """Oracle decode on the exported cache; selections exact (band aside),
+    outputs within the dtype tolerance with the GPU selection forced."""
+    q = oracle.from_stored(q_np, dtype)
+    res = oracle.decode_step(oc, q, tau, k_max, alpha, P, units=units)
+    excused = 0
+    for (b, h), rt in res["routes"].items():
+        excused += check_selection(rt, sels[b][h], tau, k_max, f"{what} unit {(b, h)}")
+    forced = [[sels[b][h] for h in range(oc["Hkv"])] for b in range(oc["B"])]
+    ref = oracle.decode_step(oc, q, tau, k_max, alpha, P, forced_sel=forced, units=units)
+    G = oc["Hq"] // oc["Hkv"]
+    todo = units if units is not None else [(b, h) for b in range(oc["B"]) for h in range(oc["Hkv"])]
+    err = 0.0
+    for b, h in todo:
+        sl = slice(h * G, (h + 1) * G)
+        err = max(err, float(np.max(np.abs(out_gpu[b, sl] - ref["out"][b, sl]))))
+    assert err <= TOL[dtype], f"{what}: max abs err {err:.3e} > {TOL[dtype]}"
+    return err, excused

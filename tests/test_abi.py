@@ -1,0 +1,51 @@
+"""The C-ABI library loads and exports every symbol the header declares
+(CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rskv.h")
+LIB = os.path.join(ROOT, "routed_sparse_kv_amd", "lib", "librskv.so")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rskv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for s in ("rskv_build_spans", "rskv_decode_step", "rskv_append_kv", "rskv_cache_export",
+              "rskv_cache_import", "rskv_cache_destroy", "rskv_last_error"):
+        assert s in syms
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="librskv.so not built")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, missing
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="librskv.so not built")
+def test_version_and_error_strings_without_gpu():
+    lib = ctypes.CDLL(LIB)
+    lib.rskv_version.restype = ctypes.c_char_p
+    lib.rskv_last_error.restype = ctypes.c_char_p
+    assert lib.rskv_version().startswith(b"rskv")
+    # invalid handle: rejected on the host before any HIP call
+    lib.rskv_append_kv.argtypes = [ctypes.c_void_p] * 4
+    assert lib.rskv_append_kv(None, None, None, None) == -6
+    assert b"invalid cache handle" in lib.rskv_last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    from routed_sparse_kv_amd import binding
+    monkeypatch.setattr(binding, "LIB_PATH", os.path.join(ROOT, "nonexistent.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

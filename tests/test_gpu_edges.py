@@ -1,0 +1,197 @@
+"""Edge cases and error paths of the HIP path (GPU).
+
+Degenerate segmentations (no anchors, every token an anchor, one anchor,
+tiny contexts, tied surprisal), routing extremes (k_max = 0, tau = +-inf,
+k_max above the span count), full-rank expansion (the method reduces to
+dense attention), an oracle-built cache imported into the library, run-to-
+run determinism, and every error code a caller can trigger from the host.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_sparse_kv_amd as rskv
+from gpu_helpers import TOL, compare_decode, decode_gpu, dev_tensor, oracle_view, say
+from routed_sparse_kv_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, Hkv, G, T, d, dtype, seed, ties=False):
+    rng = np.random.default_rng(seed)
+    if ties:
+        H = rng.integers(0, 3, (B, T)).astype(np.float32)
+    else:
+        H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    K = W.store((rng.standard_normal((B, Hkv, T, d)) * 1.3).astype(np.float32), dtype)
+    V = W.store(rng.standard_normal((B, Hkv, T, d)).astype(np.float32), dtype)
+    q = W.store(rng.standard_normal((B, Hkv * G, d)).astype(np.float32) * 2.0, dtype)
+    return H, K, V, q
+
+
+def _build(H, K, V, dtype, rank, p, G, tail=0, k_cap=0):
+    Hkv = K.shape[1]
+    return rskv.build_spans(torch.from_numpy(H).cuda(), dev_tensor(K, dtype), dev_tensor(V, dtype),
+                            rank, p, n_q_heads=Hkv * G, tail_capacity=tail, k_max_cap=k_cap)
+
+
+def _check_segmentation(cache, H, p):
+    ex = cache.export()
+    n_a = oracle.n_anchors(H.shape[1], p)
+    for b in range(H.shape[0]):
+        sg = oracle.segment(H[b], n_a)
+        assert np.array_equal(ex["span_id"][b], sg["span_id"])
+        assert ex["n_spans"][b] == len(sg["span_len"])
+    return ex
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p", [0.0, 1.0, 0.5, 0.02])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 97])
+def test_degenerate_segmentations(dtype, p, T):
+    say(f"[edge] dtype={dtype} p={p} T={T}")
+    H, K, V, q = _case(2, 2, 3, T, 64, dtype, seed=T)
+    cache = _build(H, K, V, dtype, 4, p, 3, k_cap=8)
+    _check_segmentation(cache, H, p)
+    for tau, k in ((0.0, 2), (-math.inf, 8), (math.inf, 8), (0.0, 0)):
+        out, sels = decode_gpu(cache, q, tau, k)
+        compare_decode(oracle_view(cache.export()), q, out, sels, tau, k, 8.0, None, dtype,
+                       what=f"p={p} T={T} tau={tau} k={k}")
+    cache.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tied_surprisal(dtype):
+    H, K, V, q = _case(3, 1, 1, 700, 64, dtype, seed=5, ties=True)
+    cache = _build(H, K, V, dtype, 4, 0.3, 1)
+    _check_segmentation(cache, H, 0.3)
+    out, sels = decode_gpu(cache, q, 0.0, 6)
+    compare_decode(oracle_view(cache.export()), q, out, sels, 0.0, 6, 8.0, None, dtype)
+    cache.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_rank_expansion_is_dense_attention(dtype):
+    """rank >= every span length, tau = -inf, k_max >= n_s: every token is
+    rebuilt exactly (up to factor rounding) and decode is dense attention."""
+    B, Hkv, G, T, d = 2, 2, 4, 600, 128
+    H, K, V, q = _case(B, Hkv, G, T, d, dtype, seed=9)
+    # anchors every 4th to 20th token: every span shorter than the rank
+    rng = np.random.default_rng(10)
+    for b in range(B):
+        pos = np.cumsum(rng.integers(4, 21, T))
+        pos = pos[pos < T]
+        H[b] = rng.uniform(0.0, 1.0, T)
+        H[b, pos] = 5.0 + rng.uniform(0.0, 1.0, len(pos))
+    p = min(len(np.flatnonzero(H[b] >= 5.0)) for b in range(B)) / T
+    cache = _build(H, K, V, dtype, 20, p, G)
+    ex = cache.export()
+    ns = int(ex["n_spans"].max())
+    assert ex["span_len"].max() <= 20
+    out, sels = decode_gpu(cache, q, -math.inf, ns)
+    for b in range(B):
+        for h in range(Hkv):
+            assert len(sels[b][h]) == cache.export()["n_spans"][b]
+    qt = torch.from_numpy(oracle.from_stored(q, dtype))[:, :, None, :]
+    kt = torch.from_numpy(oracle.from_stored(K, dtype))
+    vt = torch.from_numpy(oracle.from_stored(V, dtype))
+    dense = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, enable_gqa=True)[:, :, 0]
+    err = float(np.max(np.abs(out - dense.numpy())))
+    say(f"[full rank {dtype}] err vs dense {err:.2e}")
+    assert err <= TOL[dtype]
+    cache.close()
+
+
+def test_k_max_above_span_count_and_cap():
+    H, K, V, q = _case(1, 2, 2, 400, 64, "f32", seed=3)
+    cache = _build(H, K, V, "f32", 4, 0.1, 2, k_cap=100)
+    ns = int(cache.export()["n_spans"][0])
+    out, sels = decode_gpu(cache, q, -math.inf, 100)
+    assert all(len(s) == ns for s in sels[0])
+    with pytest.raises(rskv.RskvError) as ei:
+        decode_gpu(cache, q, 0.0, 101)
+    assert ei.value.code == -4
+    cache.close()
+
+
+def test_imported_oracle_cache():
+    """Decode kernels on a cache built by the oracle and imported."""
+    B, Hkv, G, T, d = 2, 2, 4, 900, 128
+    H, K, V, q = _case(B, Hkv, G, T, d, "bf16", seed=21)
+    oc = oracle.build_cache(H, oracle.from_stored(K, "bf16"), oracle.from_stored(V, "bf16"), 8,
+                            0.05, "bf16", Hq=Hkv * G)
+    arrays = _oracle_to_arrays(oc)
+    cache = rskv.cache_import(arrays, n_q_heads=Hkv * G, rank=8, dtype="bf16", context_len=T)
+    out, sels = decode_gpu(cache, q, 0.0, 7)
+    compare_decode(oc, q, out, sels, 0.0, 7, 8.0, None, "bf16", what="imported")
+    # and the export of the imported cache returns the same stored values
+    ex = cache.export()
+    assert np.array_equal(oracle.from_stored(ex["w_v"], "bf16")[:, :, :oc["s"].shape[2]], oc["BV"])
+    cache.close()
+
+
+def _oracle_to_arrays(oc):
+    dt = oc["dtype"]
+
+    def raw(x):
+        x = np.asarray(x, np.float64)
+        if dt == "bf16":
+            return W.f32_to_bf16_bits(x.astype(np.float32))  # exact: x is bf16-valued
+        return x.astype(np.float32)
+    return dict(n_anchor=oc["n_a"], n_spans=oc["n_s"], n_full=oc["n_F"], n_span_tokens=oc["nt"],
+                span_id=oc["span_id"], span_start=oc["span_start"], span_len=oc["span_len"],
+                full_pos=oc["fr_pos"], summary=raw(oc["s"]), vmean=raw(oc["vbar"]),
+                log_len=oc["ell"].astype(np.float32), k_full=raw(oc["KF"]), v_full=raw(oc["VF"]),
+                a_k=raw(oc["AK"]), a_v=raw(oc["AV"]), w_k=raw(oc["BK"]), w_v=raw(oc["BV"]))
+
+
+def test_repeat_is_deterministic():
+    wl = W.generate("gqa_32k_bf16", T=5000, steps=1)
+    from gpu_helpers import gpu_build
+    cache = gpu_build(wl)
+    a, sa = decode_gpu(cache, wl.queries[0], wl.cfg["tau"], wl.cfg["k_max"])
+    b, sb = decode_gpu(cache, wl.queries[0], wl.cfg["tau"], wl.cfg["k_max"])
+    assert np.array_equal(a, b)
+    assert all(np.array_equal(x, y) for r1, r2 in zip(sa, sb) for x, y in zip(r1, r2))
+    cache.close()
+
+
+def test_error_codes():
+    H, K, V, q = _case(1, 1, 1, 64, 64, "f32", seed=1)
+    Ht = torch.from_numpy(H).cuda()
+    Kt, Vt = dev_tensor(K, "f32"), dev_tensor(V, "f32")
+    with pytest.raises(rskv.RskvError) as ei:
+        rskv.build_spans(Ht, Kt, Vt, 0, 0.1)
+    assert ei.value.code == -1
+    with pytest.raises(rskv.RskvError) as ei:
+        rskv.build_spans(Ht, Kt, Vt, 4, 1.5)
+    assert ei.value.code == -1
+    Hn = Ht.clone()
+    Hn[0, 5] = float("nan")
+    with pytest.raises(rskv.RskvError) as ei:
+        rskv.build_spans(Hn, Kt, Vt, 4, 0.1)
+    assert ei.value.code == -1 and "NaN" in str(ei.value)
+    with pytest.raises(TypeError):
+        rskv.build_spans(Ht, Kt.to(torch.float16), Vt, 4, 0.1)
+    cache = rskv.build_spans(Ht, Kt, Vt, 4, 0.1, tail_capacity=1)
+    qt = dev_tensor(q, "f32")
+    with pytest.raises(rskv.RskvError) as ei:
+        rskv.decode_step(cache, qt, float("nan"), 1)
+    assert ei.value.code == -1
+    with pytest.raises(rskv.RskvError) as ei:
+        rskv.decode_step(cache, qt, 0.0, -1)
+    assert ei.value.code == -1
+    kv = torch.zeros((1, 1, 64), device="cuda")
+    rskv.append_kv(cache, kv, kv)
+    with pytest.raises(rskv.RskvError) as ei:
+        rskv.append_kv(cache, kv, kv)
+    assert ei.value.code == -4
+    with pytest.raises(ValueError):
+        rskv.decode_step(cache, qt[:, :, :32].contiguous(), 0.0, 1)
+    cache.close()
+    with pytest.raises(rskv.RskvError) as ei:
+        rskv.decode_step(cache, qt, 0.0, 1)
+    assert ei.value.code == -6
