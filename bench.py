@@ -1,0 +1,327 @@
+"""Decode-step throughput of span-routed mixed-resolution KV attention.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one ``decode_step`` over the whole batch: routing GEMV, top-k cap,
+split-K mixed-resolution attention and merge (plus the tail append on
+workloads that append).  Inputs are resident in HBM before timing starts.
+The 256 MB last-level cache is defeated by rotating over ``--replicas``
+identical caches (each step reads a different copy).
+
+Prints ONE JSON line.  ``value`` is context tokens per second per KV head,
+B*T / t_step.  ``roofline`` describes the attention kernel: algorithmic
+bytes per launch (from each step's actual selection) over its mean duration
+from HIP events recorded on the launch stream.  ``cpu_baseline`` times the
+fp64 oracle on a bounded sample of units of one step, scaled to a full step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "decode_step context-tokens/sec per head and achieved HBM GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_128k_bf16")
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB per rotation")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (units)")
+    return ap.parse_args()
+
+
+def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg):
+    """Algorithmic bytes of one step, total and of the attention kernel.
+
+    Per unit (sequence b, KV head h), with b_e bytes per stored element:
+      routing  : n_s d b_e                       (summaries, read once)
+      attention: (n_s - |E|) d b_e               (means of unexpanded spans)
+               + n_s * 8                         (span offsets and lengths)
+               + n_F 2 d b_e                     (full-resolution K and V)
+               + sum_{j in E} 2 (|S_j| + d) r_j b_e   (factors of K and V)
+               + G d b_e                         (queries)
+      output   : G d 4
+    with r_j = min(r, |S_j|, d).
+    """
+    d, r, G = cfg["d"], cfg["rank"], cfg["Hq"] // cfg["Hkv"]
+    be = 2 if cfg["dtype"] == "bf16" else 4
+    B, Hkv = cfg["B"], cfg["Hkv"]
+    route = attend = out = 0
+    for b in range(B):
+        ns, nf = int(n_spans[b]), int(n_full[b])
+        lens = span_len[b]
+        for h in range(Hkv):
+            E = sels[b, h, :int(nsels[b, h])]
+            le = lens[E].astype(np.int64)
+            rj = np.minimum(np.minimum(le, r), d)
+            route += ns * d * be
+            attend += ((ns - len(E)) * d * be + ns * 8 + nf * 2 * d * be
+                       + int(np.sum(2 * (le + d) * rj * be)) + G * d * be)
+            out += G * d * 4
+    return route + attend + out, attend
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in ("attend.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "routed_sparse_kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(ex_unit_views, q_steps, cfg, n_units_total, budget_s=20.0):
+    """Time the oracle's decode on sampled units; scale to one full step."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    G = cfg["Hq"] // cfg["Hkv"]
+    P = None
+    done, el = 0, 0.0
+    views = list(ex_unit_views)
+    with threadpool_limits(limits=1):
+        for rep in range(1000):
+            for (b, h), oc in views:
+                qs = q_steps[(rep + b) % len(q_steps)]
+                q = oracle.from_stored(qs[b:b + 1, h * G:(h + 1) * G], cfg["dtype"])
+                if cfg.get("P") is not None:
+                    P = cfg["_P"][0:1] if cfg["_P"].shape[0] == 1 else cfg["_P"][h:h + 1]
+                t0 = time.perf_counter()
+                oracle.decode_step(oc, q, cfg["tau"], cfg["k_max"], cfg["alpha"], P)
+                el += time.perf_counter() - t0
+                done += 1
+            if el > budget_s:
+                break
+    t_step = el / done * n_units_total
+    return done, el, t_step
+
+
+def unit_view(ex, b, h):
+    """Oracle cache dictionary holding one unit (B = Hkv = 1)."""
+    import oracle
+    info = ex["info"]
+    dt = "bf16" if info["dtype"] == 1 else "f32"
+    f = lambda k: oracle.from_stored(ex[k][b:b + 1, h:h + 1], dt)  # noqa: E731
+    return dict(B=1, Hq=info["n_q_heads"] // info["n_kv_heads"], Hkv=1, d=info["head_dim"],
+                T=info["context_len"], rank=info["rank"], dtype=dt,
+                n_s=ex["n_spans"][b:b + 1].astype(np.int64),
+                n_F=ex["n_full"][b:b + 1].astype(np.int64),
+                span_len=ex["span_len"][b:b + 1].astype(np.int64),
+                s=f("summary"), vbar=f("vmean"), ell=ex["log_len"][b:b + 1].astype(np.float64),
+                KF=f("k_full"), VF=f("v_full"), AK=f("a_k"), AV=f("a_v"), BK=f("w_k"),
+                BV=f("w_v"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import routed_sparse_kv_amd as rskv
+    from routed_sparse_kv_amd import workloads as W
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    over = {}
+    if W.CONFIGS[args.workload].get("append"):
+        over["tail_capacity"] = args.warmup + 3 * args.steps + 2
+    wl = W.generate(args.workload, **over)
+    cfg = wl.cfg
+    cfg["_P"] = wl.P
+    log(f"generated {args.workload} in {time.perf_counter() - t0:.1f}s")
+
+    def to_dev(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    dt = cfg["dtype"]
+    H = torch.from_numpy(wl.H).to(dev)
+    K = to_dev(wl.K, dt)
+    V = to_dev(wl.V, dt)
+    P = torch.from_numpy(wl.P).to(dev) if wl.P is not None else None
+
+    def build():
+        return rskv.build_spans(H, K, V, cfg["rank"], cfg["anchor_frac"], n_q_heads=cfg["Hq"],
+                                alpha=cfg["alpha"], proj=P, tail_capacity=cfg["tail_capacity"])
+
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    caches = [build()]
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - tb
+    log(f"build_spans {build_s:.2f}s")
+    ex = caches[0].export()
+    # replicas so that one rotation touches >= 1 GB
+    qs = [to_dev(q, dt) for q in wl.queries]
+    B, Hkv = cfg["B"], cfg["Hkv"]
+    kmax = cfg["k_max"]
+    sel = torch.zeros((B, Hkv, kmax), dtype=torch.int32, device=dev) if kmax else None
+    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    out = torch.empty((B, cfg["Hq"], cfg["d"]), dtype=torch.float32, device=dev)
+    rskv.decode_step(caches[0], qs[0], cfg["tau"], kmax, out=out, sel=sel, n_sel=nsel)
+    torch.cuda.synchronize()
+    s0 = sel.cpu().numpy() if kmax else np.zeros((B, Hkv, 0), np.int32)
+    b_total, _ = step_bytes(ex["span_len"], ex["n_spans"], ex["n_full"], s0,
+                            nsel.cpu().numpy(), cfg)
+    R = args.replicas or max(1, math.ceil(1.0e9 / b_total))
+    R = min(R, 16)
+    for _ in range(R - 1):
+        caches.append(build())
+    del K, V
+    torch.cuda.empty_cache()
+    log(f"{R} cache replicas, {caches[0].info['device_bytes'] / 1e9:.2f} GB each")
+
+    apps = None
+    if wl.appends is not None:
+        apps = [(to_dev(k, dt), to_dev(v, dt)) for k, v in wl.appends]
+
+    n_steps = args.steps
+    sels = [torch.zeros((B, Hkv, kmax), dtype=torch.int32, device=dev) if kmax else None
+            for _ in range(n_steps)]
+    nsels = [torch.zeros((B, Hkv), dtype=torch.int32, device=dev) for _ in range(n_steps)]
+    appended_at = [0] * n_steps
+
+    def step(i, cache, s_buf=None, n_buf=None):
+        if apps is not None:
+            k, v = apps[i % len(apps)]
+            rskv.append_kv(cache, k, v)
+        rskv.decode_step(cache, qs[i % len(qs)], cfg["tau"], kmax, out=out, sel=s_buf,
+                         n_sel=n_buf)
+        return cache.info["appended"]
+
+    for i in range(args.warmup):
+        step(i, caches[i % R], sel, nsel)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_steps):
+        appended_at[i] = step(i, caches[i % R], sels[i], nsels[i])
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / n_steps
+
+    # warm (single cache, last-level cache resident) figure
+    e0.record()
+    for i in range(n_steps):
+        step(i, caches[0], None, None)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / n_steps
+
+    # per-kernel durations: same steps, HIP events around each kernel
+    for c in caches:
+        c.profile_enable(True)
+    for i in range(n_steps):
+        step(i, caches[i % R], None, None)
+    torch.cuda.synchronize()
+    prof = {"route_ms": 0.0, "topk_ms": 0.0, "attend_ms": 0.0, "merge_ms": 0.0, "steps": 0}
+    for c in caches:
+        p = c.profile_read()
+        for k in prof:
+            prof[k] += p[k]
+        c.profile_enable(False)
+    kern = {k: prof[k] / max(1, prof["steps"]) for k in ("route_ms", "topk_ms", "attend_ms", "merge_ms")}
+
+    # algorithmic bytes from the timed steps' selections
+    tot_b, att_b = [], []
+    for i in range(n_steps):
+        # replicas hold identical tables; appends add rows per replica
+        n_full = ex["n_full"] + (appended_at[i] - ex["info"]["appended"])
+        s_np = sels[i].cpu().numpy() if kmax else np.zeros((B, Hkv, 0), np.int32)
+        tb_, ab_ = step_bytes(ex["span_len"], ex["n_spans"], n_full, s_np,
+                              nsels[i].cpu().numpy(), cfg)
+        tot_b.append(tb_)
+        att_b.append(ab_)
+    step_bytes_avg = float(np.mean(tot_b))
+    att_bytes_avg = float(np.mean(att_b))
+    ctx_tokens = cfg["B"] * cfg["T"]
+    value = ctx_tokens / (ms_step / 1e3)
+    att_gbps = att_bytes_avg / (kern["attend_ms"] / 1e3) / 1e9
+    step_gbps = step_bytes_avg / (ms_step / 1e3) / 1e9
+
+    traffic = committed_traffic(args.workload)
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "context-tokens/s/head",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": cfg["B"], "context": cfg["T"],
+                   "q_heads": cfg["Hq"], "kv_heads": cfg["Hkv"], "head_dim": cfg["d"],
+                   "rank": cfg["rank"], "k_max": kmax, "tau": cfg["tau"],
+                   "anchor_frac": cfg["anchor_frac"], "replicas": R},
+        "roofline": {"bound": "hbm", "achieved": att_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": att_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic, "kernel": "attend_kernel",
+                     "algorithmic_bytes_per_launch": att_bytes_avg,
+                     "mean_launch_ms": kern["attend_ms"]},
+        "step_algorithmic_bytes": step_bytes_avg,
+        "step_algorithmic_gbps": step_gbps,
+        "step_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "kernel_ms": kern,
+        "profiled_ms_per_step": sum(kern.values()),
+        "warm_ms_per_step": warm_ms,
+        "tokens_per_s_all_kv_heads": value * cfg["Hkv"],
+        "build_s": build_s,
+    }
+
+    if not args.no_cpu_baseline:
+        U = B * Hkv
+        n_cpu = args.cpu_units or min(U, 8)
+        rng = np.random.default_rng(0)
+        units = [(int(u // Hkv), int(u % Hkv)) for u in rng.permutation(U)[:n_cpu]]
+        views = ((u, unit_view(ex, *u)) for u in units)
+        done, el, t_step = cpu_baseline(views, wl.queries, cfg, U, budget_s=15.0)
+        res["cpu_baseline"] = {"value": ctx_tokens / t_step, "unit": "context-tokens/s/head",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{done} oracle unit decodes ({n_cpu} distinct "
+                                         f"(sequence, KV head) units of {U}, the workload's "
+                                         f"queries in turn), {el:.1f}s single-threaded, "
+                                         f"scaled to one {U}-unit step",
+                               "seconds_per_step": t_step}
+    for c in caches:
+        c.close()
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
