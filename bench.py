@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB per rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (units)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -151,6 +153,13 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        # a plain copy of known size: reads and writes exactly 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t0 = time.perf_counter()
     over = {}
     if W.CONFIGS[args.workload].get("append"):

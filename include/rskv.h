@@ -159,7 +159,8 @@ int rskv_cache_export(const rskv_cache* cache, rskv_host_arrays* arrays);
 /* Create a cache from host arrays in the canonical layout (padded with the
  * given S, F, N; F counts rows, the new cache adds opts->tail_capacity).
  * Lets tests and benchmarks decode on a cache built elsewhere.  K/V inputs
- * are not needed.  Synchronous. */
+ * are not needed, and opts->proj, if given, is a HOST pointer here.
+ * Synchronous. */
 int rskv_cache_import(const rskv_host_arrays* arrays, const rskv_build_opts* opts,
                       int32_t rank, int32_t S, int32_t F, int32_t N, void* stream,
                       rskv_cache** out);
@@ -169,7 +170,8 @@ int rskv_cache_import(const rskv_host_arrays* arrays, const rskv_build_opts* opt
 void rskv_cache_destroy(rskv_cache* cache);
 
 /* Per-kernel timing of decode_step with HIP events recorded on the caller's
- * stream around each kernel.  Enabling clears the totals. */
+ * stream around each of its four kernels (routing GEMV, top-k cap,
+ * attention partials, merge).  Enabling clears the totals. */
 typedef struct rskv_profile {
   int64_t steps;
   double route_ms, topk_ms, attend_ms, merge_ms; /* summed over steps */

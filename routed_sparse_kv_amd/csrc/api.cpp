@@ -102,12 +102,25 @@ struct CacheGuard {
   }
 };
 
-// Allocates the stored arrays and the decode workspace once S, F, N and the
-// counts are known.  Everything is zero-filled.
+// Sizes of the stored arrays, in elements.
+struct Sizes {
+  size_t summary, vmean, full, a, w, slogit;
+};
+
+Sizes sizes_of(const rskv_cache* c) {
+  const size_t U = static_cast<size_t>(c->B) * c->Hkv;
+  const size_t d = c->d, r = c->rank;
+  return Sizes{U * c->S * d, U * c->Sp * d, U * c->Fp * d, U * c->Np * r, U * c->S * r * d,
+               U * c->Sp * c->G};
+}
+
+// Allocates the stored arrays and the decode workspace once the padded
+// dimensions are known.  Everything is zero-filled.
 int alloc_arrays(rskv_cache* c, hipStream_t st) {
   const size_t U = static_cast<size_t>(c->B) * c->Hkv;
   const size_t es = elem_size(c->dtype);
-  const size_t d = c->d, S = c->S, F = c->F, N = c->N, r = c->rank;
+  const size_t d = c->d, S = c->S;
+  const Sizes z = sizes_of(c);
   auto& v = c->dev;
   int rc;
 #define ALLOC(ptr, n, what) \
@@ -117,38 +130,38 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   ALLOC(v.span_start, c->B * S, "span_start");
   ALLOC(v.span_len, c->B * S, "span_len");
   ALLOC(v.tok_off, c->B * (S + 1), "tok_off");
-  ALLOC(v.full_pos, c->B * F, "full_pos");
+  ALLOC(v.tok_pad, c->B * (S + 1), "tok_pad");
+  ALLOC(v.full_pos, static_cast<size_t>(c->B) * c->F, "full_pos");
   ALLOC(v.n_spans, c->B, "n_spans");
   ALLOC(v.n_full, c->B, "n_full");
   ALLOC(v.n_full0, c->B, "n_full0");
-  ALLOCB(v.summary, U * S * d * es, "summary");
-  ALLOCB(v.vmean, U * S * d * es, "vmean");
+  ALLOCB(v.summary, z.summary * es, "summary");
+  ALLOCB(v.vmean, z.vmean * es, "vmean");
   ALLOC(v.log_len, c->B * S, "log_len");
-  ALLOCB(v.k_full, U * F * d * es, "k_full");
-  ALLOCB(v.v_full, U * F * d * es, "v_full");
-  ALLOCB(v.a_k, U * N * r * es, "a_k");
-  ALLOCB(v.a_v, U * N * r * es, "a_v");
-  ALLOCB(v.w_k, U * S * r * d * es, "w_k");
-  ALLOCB(v.w_v, U * S * r * d * es, "w_v");
+  ALLOCB(v.k_full, z.full * es, "k_full");
+  ALLOCB(v.v_full, z.full * es, "v_full");
+  ALLOCB(v.a_k, z.a * es, "a_k");
+  ALLOCB(v.a_v, z.a * es, "a_v");
+  ALLOCB(v.w_k, z.w * es, "w_k");
+  ALLOCB(v.w_v, z.w * es, "w_v");
   ALLOC(v.z, U * S, "z");
-  ALLOC(v.slogit, U * S * c->G, "slogit");
-  ALLOC(v.expanded, U * S, "expanded");
+  ALLOC(v.slogit, z.slogit, "slogit");
   ALLOC(v.sel, U * S, "sel");
   ALLOC(v.n_sel, U, "n_sel");
   c->nsplit_max = rskv::decode_nsplit_max(c->B, c->Hkv, c->S, c->F, c->k_max_cap);
   ALLOC(v.part, U * c->nsplit_max * c->G * (d + 2), "part");
 #undef ALLOC
 #undef ALLOCB
-  RSKV_HIP(hipMemsetAsync(v.summary, 0, U * S * d * es, st), "memset summary");
-  RSKV_HIP(hipMemsetAsync(v.vmean, 0, U * S * d * es, st), "memset vmean");
-  RSKV_HIP(hipMemsetAsync(v.k_full, 0, U * F * d * es, st), "memset k_full");
-  RSKV_HIP(hipMemsetAsync(v.v_full, 0, U * F * d * es, st), "memset v_full");
-  RSKV_HIP(hipMemsetAsync(v.a_k, 0, U * N * r * es, st), "memset a_k");
-  RSKV_HIP(hipMemsetAsync(v.a_v, 0, U * N * r * es, st), "memset a_v");
-  RSKV_HIP(hipMemsetAsync(v.w_k, 0, U * S * r * d * es, st), "memset w_k");
-  RSKV_HIP(hipMemsetAsync(v.w_v, 0, U * S * r * d * es, st), "memset w_v");
+  RSKV_HIP(hipMemsetAsync(v.summary, 0, z.summary * es, st), "memset summary");
+  RSKV_HIP(hipMemsetAsync(v.vmean, 0, z.vmean * es, st), "memset vmean");
+  RSKV_HIP(hipMemsetAsync(v.k_full, 0, z.full * es, st), "memset k_full");
+  RSKV_HIP(hipMemsetAsync(v.v_full, 0, z.full * es, st), "memset v_full");
+  RSKV_HIP(hipMemsetAsync(v.a_k, 0, z.a * es, st), "memset a_k");
+  RSKV_HIP(hipMemsetAsync(v.a_v, 0, z.a * es, st), "memset a_v");
+  RSKV_HIP(hipMemsetAsync(v.w_k, 0, z.w * es, st), "memset w_k");
+  RSKV_HIP(hipMemsetAsync(v.w_v, 0, z.w * es, st), "memset w_v");
   RSKV_HIP(hipMemsetAsync(v.log_len, 0, c->B * S * sizeof(float), st), "memset log_len");
-  RSKV_HIP(hipMemsetAsync(v.expanded, 0, U * S, st), "memset expanded");
+  RSKV_HIP(hipMemsetAsync(v.slogit, 0, z.slogit * sizeof(float), st), "memset slogit");
   RSKV_HIP(hipMemsetAsync(v.n_sel, 0, U * sizeof(int32_t), st), "memset n_sel");
   return RSKV_OK;
 }
@@ -179,17 +192,194 @@ int copy_proj(rskv_cache* c, const rskv_build_opts* o, hipStream_t st, bool from
   return RSKV_OK;
 }
 
-int finish_sizes(rskv_cache* c, const rskv_build_opts* o) {
-  int s_max = 0, f_max = 0, n_max = 0;
+void finish_sizes(rskv_cache* c, const rskv_build_opts* o) {
+  int s_max = 0, f_max = 0, n_max = 0, p_max = 0;
   for (int b = 0; b < c->B; ++b) {
     s_max = std::max(s_max, c->h_n_spans[b]);
     f_max = std::max(f_max, c->h_n_full0[b]);
     n_max = std::max(n_max, c->h_n_span_tokens[b]);
+    p_max = std::max(p_max, c->h_n_tok_pad[b]);
   }
   c->S = std::max(1, s_max);
   c->F = std::max(1, f_max + c->tail_cap);
   c->N = std::max(1, n_max);
+  c->Sp = rskv::round_up(c->S, 32);
+  c->Fp = rskv::round_up(c->F, 32);
+  c->Np = std::max(16, p_max);
   c->k_max_cap = o->k_max_cap > 0 ? o->k_max_cap : 0x7fffffff;  // <= 0: no limit
+}
+
+// Host-side offsets of every span: plain and padded to 16 rows.
+void span_offsets(const int32_t* len, int ns, std::vector<int>* off, std::vector<int>* pad) {
+  off->assign(ns + 1, 0);
+  pad->assign(ns + 1, 0);
+  for (int j = 0; j < ns; ++j) {
+    (*off)[j + 1] = (*off)[j] + len[j];
+    (*pad)[j + 1] = (*pad)[j] + rskv::round_up(len[j], 16);
+  }
+}
+
+// Conversion between the device layouts (layout.h) and the canonical
+// row-major layout of rskv_host_arrays.  E is the element type by size.
+template <typename E>
+struct Relayout {
+  const rskv_cache* c;
+  const int32_t* span_len;  // [B][S_host], pitch ls
+  int ls;
+
+  // dir = +1: device -> canonical; -1: canonical -> device.
+  void full(E* canon, int F_c, E* dev, bool keys, int dir) const {
+    const int d = c->d;
+    for (int u = 0; u < c->B * c->Hkv; ++u)
+      for (int r = 0; r < std::min(F_c, c->F); ++r)
+        for (int k = 0; k < d; ++k) {
+          const size_t dv = static_cast<size_t>(u) * c->Fp * d +
+                            (keys ? rskv::k16_off(r, k, d) : rskv::v32_off(r, k, d));
+          E& cv = canon[(static_cast<size_t>(u) * F_c + r) * d + k];
+          if (dir > 0) cv = dev[dv]; else dev[dv] = cv;
+        }
+  }
+  void vmean(E* canon, int S_c, E* dev, int dir) const {
+    const int d = c->d;
+    for (int u = 0; u < c->B * c->Hkv; ++u)
+      for (int j = 0; j < std::min(S_c, c->S); ++j)
+        for (int k = 0; k < d; ++k) {
+          const size_t dv = static_cast<size_t>(u) * c->Sp * d + rskv::v32_off(j, k, d);
+          E& cv = canon[(static_cast<size_t>(u) * S_c + j) * d + k];
+          if (dir > 0) cv = dev[dv]; else dev[dv] = cv;
+        }
+  }
+  void factors_a(E* canon, int N_c, E* dev, bool transposed, int dir) const {
+    const int r = c->rank;
+    std::vector<int> off, pad;
+    for (int b = 0; b < c->B; ++b) {
+      const int ns = c->h_n_spans[b];
+      span_offsets(span_len + static_cast<size_t>(b) * ls, ns, &off, &pad);
+      for (int h = 0; h < c->Hkv; ++h) {
+        const size_t u = static_cast<size_t>(b) * c->Hkv + h;
+        for (int j = 0; j < ns; ++j)
+          for (int t = 0; t < off[j + 1] - off[j]; ++t)
+            for (int k = 0; k < r; ++k) {
+              const int tp = pad[j] + t;
+              const size_t dv = u * c->Np * r + (transposed ? rskv::avt_off(tp, k, r)
+                                                            : static_cast<size_t>(tp) * r + k);
+              E& cv = canon[(u * N_c + off[j] + t) * r + k];
+              if (dir > 0) cv = dev[dv]; else dev[dv] = cv;
+            }
+      }
+    }
+  }
+  void factors_wv(E* canon, int S_c, E* dev, int dir) const {
+    const int r = c->rank, d = c->d;
+    for (int u = 0; u < c->B * c->Hkv; ++u)
+      for (int j = 0; j < std::min(S_c, c->S); ++j)
+        for (int k = 0; k < r; ++k)
+          for (int e = 0; e < d; ++e) {
+            const size_t dv = static_cast<size_t>(u) * c->S * d * r + rskv::wvt_off(j, k, e, d, r);
+            E& cv = canon[((static_cast<size_t>(u) * S_c + j) * r + k) * d + e];
+            if (dir > 0) cv = dev[dv]; else dev[dv] = cv;
+          }
+  }
+};
+
+template <typename E>
+int export_arrays(const rskv_cache* c, rskv_host_arrays* a) {
+  const auto& v = c->dev;
+  const Sizes z = sizes_of(c);
+  const size_t U = static_cast<size_t>(c->B) * c->Hkv;
+  const int S = c->S, F = c->F, N = c->N, d = c->d, r = c->rank;
+  std::vector<int32_t> lens(static_cast<size_t>(c->B) * S);
+  RSKV_HIP(hipMemcpy(lens.data(), v.span_len, lens.size() * 4, hipMemcpyDeviceToHost), "export");
+  Relayout<E> rl{c, lens.data(), S};
+  std::vector<E> tmp;
+  auto fetch = [&](const void* src, size_t n) -> int {
+    tmp.assign(n, E(0));
+    hipError_t e = hipMemcpy(tmp.data(), src, n * sizeof(E), hipMemcpyDeviceToHost);
+    return e == hipSuccess ? RSKV_OK : hip_fail(e, "export copy");
+  };
+  int rc;
+  if (a->summary) {
+    RSKV_HIP(hipMemcpy(a->summary, v.summary, z.summary * sizeof(E), hipMemcpyDeviceToHost),
+             "export summary");
+  }
+  if (a->w_k) {
+    RSKV_HIP(hipMemcpy(a->w_k, v.w_k, z.w * sizeof(E), hipMemcpyDeviceToHost), "export w_k");
+  }
+  if (a->vmean) {
+    if ((rc = fetch(v.vmean, z.vmean))) return rc;
+    rl.vmean(static_cast<E*>(a->vmean), S, tmp.data(), +1);
+  }
+  if (a->k_full) {
+    if ((rc = fetch(v.k_full, z.full))) return rc;
+    rl.full(static_cast<E*>(a->k_full), F, tmp.data(), true, +1);
+  }
+  if (a->v_full) {
+    if ((rc = fetch(v.v_full, z.full))) return rc;
+    rl.full(static_cast<E*>(a->v_full), F, tmp.data(), false, +1);
+  }
+  if (a->a_k) {
+    if ((rc = fetch(v.a_k, z.a))) return rc;
+    memset(a->a_k, 0, U * N * r * sizeof(E));
+    rl.factors_a(static_cast<E*>(a->a_k), N, tmp.data(), false, +1);
+  }
+  if (a->a_v) {
+    if ((rc = fetch(v.a_v, z.a))) return rc;
+    memset(a->a_v, 0, U * N * r * sizeof(E));
+    rl.factors_a(static_cast<E*>(a->a_v), N, tmp.data(), true, +1);
+  }
+  if (a->w_v) {
+    if ((rc = fetch(v.w_v, z.w))) return rc;
+    rl.factors_wv(static_cast<E*>(a->w_v), S, tmp.data(), +1);
+  }
+  (void)d;
+  return RSKV_OK;
+}
+
+template <typename E>
+int import_arrays(rskv_cache* c, const rskv_host_arrays* a, int S_in, int F_in, int N_in) {
+  auto& v = c->dev;
+  const Sizes z = sizes_of(c);
+  const size_t U = static_cast<size_t>(c->B) * c->Hkv;
+  const int d = c->d, r = c->rank;
+  Relayout<E> rl{c, a->span_len, S_in};
+  std::vector<E> tmp;
+  auto put = [&](void* dst, size_t n, const char* what) -> int {
+    hipError_t e = hipMemcpy(dst, tmp.data(), n * sizeof(E), hipMemcpyHostToDevice);
+    return e == hipSuccess ? RSKV_OK : hip_fail(e, what);
+  };
+  int rc;
+  // summary and W_K: canonical on both sides, re-pitched
+  tmp.assign(z.summary, E(0));
+  for (size_t u = 0; u < U; ++u)
+    for (int j = 0; j < std::min(S_in, c->S); ++j)
+      memcpy(&tmp[(u * c->S + j) * d], static_cast<const E*>(a->summary) + (u * S_in + j) * d,
+             d * sizeof(E));
+  if ((rc = put(v.summary, z.summary, "import summary"))) return rc;
+  tmp.assign(z.w, E(0));
+  for (size_t u = 0; u < U; ++u)
+    for (int j = 0; j < std::min(S_in, c->S); ++j)
+      memcpy(&tmp[(u * c->S + j) * r * d],
+             static_cast<const E*>(a->w_k) + (u * S_in + j) * r * d, r * d * sizeof(E));
+  if ((rc = put(v.w_k, z.w, "import w_k"))) return rc;
+  tmp.assign(z.vmean, E(0));
+  rl.vmean(static_cast<E*>(const_cast<void*>(static_cast<const void*>(a->vmean))), S_in,
+           tmp.data(), -1);
+  if ((rc = put(v.vmean, z.vmean, "import vmean"))) return rc;
+  tmp.assign(z.full, E(0));
+  rl.full(static_cast<E*>(a->k_full), F_in, tmp.data(), true, -1);
+  if ((rc = put(v.k_full, z.full, "import k_full"))) return rc;
+  tmp.assign(z.full, E(0));
+  rl.full(static_cast<E*>(a->v_full), F_in, tmp.data(), false, -1);
+  if ((rc = put(v.v_full, z.full, "import v_full"))) return rc;
+  tmp.assign(z.a, E(0));
+  rl.factors_a(static_cast<E*>(a->a_k), N_in, tmp.data(), false, -1);
+  if ((rc = put(v.a_k, z.a, "import a_k"))) return rc;
+  tmp.assign(z.a, E(0));
+  rl.factors_a(static_cast<E*>(a->a_v), N_in, tmp.data(), true, -1);
+  if ((rc = put(v.a_v, z.a, "import a_v"))) return rc;
+  tmp.assign(z.w, E(0));
+  rl.factors_wv(static_cast<E*>(a->w_v), S_in, tmp.data(), -1);
+  if ((rc = put(v.w_v, z.w, "import w_v"))) return rc;
   return RSKV_OK;
 }
 
@@ -199,7 +389,7 @@ extern "C" {
 
 const char* rskv_last_error(void) { return g_err.c_str(); }
 
-const char* rskv_version(void) { return "rskv 0.1.0 (gfx950)"; }
+const char* rskv_version(void) { return "rskv 0.2.0 (gfx950)"; }
 
 int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32_t rank,
                      const rskv_build_opts* opts, void* stream, rskv_cache** out) {
@@ -216,14 +406,11 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
     init_header(c, opts, rank);
     c->last_stream = st;
     const int B = c->B, T = c->T;
-    const double na_d = floor(opts->anchor_frac * static_cast<double>(T));
-    const int n_anchor = static_cast<int>(na_d);
+    const int n_anchor = static_cast<int>(floor(opts->anchor_frac * static_cast<double>(T)));
 
-    // ---- segmentation into temporaries of pitch T
+    // ---- segmentation into temporaries of pitch T (T + 1 for offsets)
     rc = dev_alloc(c, &c->dev.span_id, static_cast<size_t>(B) * T, "span_id");
     if (rc != RSKV_OK) return rc;
-    int32_t *start_tmp = nullptr, *len_tmp = nullptr, *tokoff_tmp = nullptr,
-            *full_tmp = nullptr, *counts = nullptr;
     std::vector<void*> tmps;
     auto tmp_alloc = [&](int32_t** p, size_t n) -> int {
       void* q = nullptr;
@@ -243,16 +430,18 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
         for (void* p : *v) (void)hipFree(p);
       }
     } tmp_free{&tmps, st};
-    const size_t BT = static_cast<size_t>(B) * T;
+    int32_t *start_tmp, *len_tmp, *tokoff_tmp, *tokpad_tmp, *full_tmp, *counts;
+    const size_t BT = static_cast<size_t>(B) * T, BT1 = static_cast<size_t>(B) * (T + 1);
     if ((rc = tmp_alloc(&start_tmp, BT)) != RSKV_OK) return rc;
     if ((rc = tmp_alloc(&len_tmp, BT)) != RSKV_OK) return rc;
-    if ((rc = tmp_alloc(&tokoff_tmp, static_cast<size_t>(B) * (T + 1))) != RSKV_OK) return rc;
+    if ((rc = tmp_alloc(&tokoff_tmp, BT1)) != RSKV_OK) return rc;
+    if ((rc = tmp_alloc(&tokpad_tmp, BT1)) != RSKV_OK) return rc;
     if ((rc = tmp_alloc(&full_tmp, BT)) != RSKV_OK) return rc;
-    if ((rc = tmp_alloc(&counts, static_cast<size_t>(B) * 4)) != RSKV_OK) return rc;
+    if ((rc = tmp_alloc(&counts, static_cast<size_t>(B) * rskv::kCounts)) != RSKV_OK) return rc;
     RSKV_HIP(rskv::launch_segment(surprisal, B, T, n_anchor, c->dev.span_id, start_tmp, len_tmp,
-                                  tokoff_tmp, full_tmp, counts, st),
+                                  tokoff_tmp, tokpad_tmp, full_tmp, counts, st),
              "segment kernel");
-    std::vector<int32_t> hc(static_cast<size_t>(B) * 4);
+    std::vector<int32_t> hc(static_cast<size_t>(B) * rskv::kCounts);
     RSKV_HIP(hipMemcpyAsync(hc.data(), counts, hc.size() * sizeof(int32_t),
                             hipMemcpyDeviceToHost, st),
              "copy counts");
@@ -261,25 +450,32 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
     c->h_n_spans.resize(B);
     c->h_n_full0.resize(B);
     c->h_n_span_tokens.resize(B);
+    c->h_n_tok_pad.resize(B);
     for (int b = 0; b < B; ++b) {
-      if (hc[4 * b] < 0) return fail(RSKV_EINVAL, "surprisal holds NaN");
-      c->h_n_anchor[b] = hc[4 * b];
-      c->h_n_spans[b] = hc[4 * b + 1];
-      c->h_n_full0[b] = hc[4 * b + 2];
-      c->h_n_span_tokens[b] = hc[4 * b + 3];
+      const int32_t* cb = &hc[rskv::kCounts * b];
+      if (cb[0] < 0) return fail(RSKV_EINVAL, "surprisal holds NaN");
+      c->h_n_anchor[b] = cb[0];
+      c->h_n_spans[b] = cb[1];
+      c->h_n_full0[b] = cb[2];
+      c->h_n_span_tokens[b] = cb[3];
+      c->h_n_tok_pad[b] = cb[4];
     }
     finish_sizes(c, opts);
     if ((rc = alloc_arrays(c, st)) != RSKV_OK) return rc;
     if ((rc = copy_proj(c, opts, st, false)) != RSKV_OK) return rc;
     auto& v = c->dev;
-    RSKV_HIP(rskv::launch_copy_rows(v.span_start, c->S, start_tmp, T, counts, 4, 1, 0, 0, B, st),
+    const int kc = rskv::kCounts;
+    RSKV_HIP(rskv::launch_copy_rows(v.span_start, c->S, start_tmp, T, counts, kc, 1, 0, 0, B, st),
              "copy span_start");
-    RSKV_HIP(rskv::launch_copy_rows(v.span_len, c->S, len_tmp, T, counts, 4, 1, 0, 0, B, st),
+    RSKV_HIP(rskv::launch_copy_rows(v.span_len, c->S, len_tmp, T, counts, kc, 1, 0, 0, B, st),
              "copy span_len");
-    RSKV_HIP(rskv::launch_copy_rows(v.tok_off, c->S + 1, tokoff_tmp, T + 1, counts, 4, 1, 1, 0,
+    RSKV_HIP(rskv::launch_copy_rows(v.tok_off, c->S + 1, tokoff_tmp, T + 1, counts, kc, 1, 1, 0,
                                     B, st),
              "copy tok_off");
-    RSKV_HIP(rskv::launch_copy_rows(v.full_pos, c->F, full_tmp, T, counts, 4, 2, 0, -1, B, st),
+    RSKV_HIP(rskv::launch_copy_rows(v.tok_pad, c->S + 1, tokpad_tmp, T + 1, counts, kc, 1, 1, 0,
+                                    B, st),
+             "copy tok_pad");
+    RSKV_HIP(rskv::launch_copy_rows(v.full_pos, c->F, full_tmp, T, counts, kc, 2, 0, -1, B, st),
              "copy full_pos");
     RSKV_HIP(hipMemcpyAsync(v.n_spans, c->h_n_spans.data(), B * sizeof(int32_t),
                             hipMemcpyHostToDevice, st),
@@ -321,10 +517,11 @@ int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, flo
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
     const int nsplit = rskv::decode_nsplit(c, k_max);
-    hipEvent_t ev[5] = {};
+    constexpr int kEv = rskv::kProfileEvents;
+    hipEvent_t ev[kEv] = {};
     const bool prof = c->prof.on;
     if (prof) {
-      for (int i = 0; i < 5; ++i) {
+      for (int i = 0; i < kEv; ++i) {
         if (c->prof.pool.empty()) {
           hipEvent_t e;
           RSKV_HIP(hipEventCreate(&e), "event create");
@@ -339,12 +536,12 @@ int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, flo
     if (prof) RSKV_HIP(hipEventRecord(ev[1], st), "event record");
     RSKV_HIP(rskv::launch_topk(c, tau, k_max, sel, n_sel, st), "topk kernel");
     if (prof) RSKV_HIP(hipEventRecord(ev[2], st), "event record");
-    RSKV_HIP(rskv::launch_attend(c, q, k_max, nsplit, st), "attend kernel");
+    RSKV_HIP(rskv::launch_attend(c, q, nsplit, st), "attend kernel");
     if (prof) RSKV_HIP(hipEventRecord(ev[3], st), "event record");
     RSKV_HIP(rskv::launch_merge(c, nsplit, out, st), "merge kernel");
     if (prof) {
       RSKV_HIP(hipEventRecord(ev[4], st), "event record");
-      for (int i = 0; i < 5; ++i) c->prof.pending.push_back(ev[i]);
+      for (int i = 0; i < kEv; ++i) c->prof.pending.push_back(ev[i]);
     }
     return RSKV_OK;
   } catch (const std::bad_alloc&) {
@@ -392,40 +589,29 @@ int rskv_cache_export(const rskv_cache* c, rskv_host_arrays* a) {
     if (a == nullptr) return fail(RSKV_EINVAL, "arrays is NULL");
     RSKV_HIP(hipDeviceSynchronize(), "export sync");
     const int B = c->B;
-    const size_t U = static_cast<size_t>(B) * c->Hkv;
-    const size_t es = elem_size(c->dtype);
-    const size_t d = c->d, S = c->S, F = c->F, N = c->N, r = c->rank;
+    const size_t S = c->S, F = c->F;
     for (int b = 0; b < B; ++b) {
       if (a->n_anchor) a->n_anchor[b] = c->h_n_anchor[b];
       if (a->n_spans) a->n_spans[b] = c->h_n_spans[b];
       if (a->n_full) a->n_full[b] = c->h_n_full0[b] + c->appended;
       if (a->n_span_tokens) a->n_span_tokens[b] = c->h_n_span_tokens[b];
     }
+    const auto& v = c->dev;
     auto cp = [&](void* dst, const void* src, size_t bytes, const char* what) -> int {
       if (dst == nullptr) return RSKV_OK;
       hipError_t e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
-      if (e != hipSuccess) return hip_fail(e, what);
-      return RSKV_OK;
+      return e == hipSuccess ? RSKV_OK : hip_fail(e, what);
     };
     int rc;
-#define CP(dst, src, bytes) \
-  if ((rc = cp(dst, src, bytes, "export " #dst)) != RSKV_OK) return rc
-    const auto& v = c->dev;
-    CP(a->span_id, v.span_id, static_cast<size_t>(B) * c->T * 4);
-    CP(a->span_start, v.span_start, B * S * 4);
-    CP(a->span_len, v.span_len, B * S * 4);
-    CP(a->full_pos, v.full_pos, B * F * 4);
-    CP(a->summary, v.summary, U * S * d * es);
-    CP(a->vmean, v.vmean, U * S * d * es);
-    CP(a->log_len, v.log_len, B * S * 4);
-    CP(a->k_full, v.k_full, U * F * d * es);
-    CP(a->v_full, v.v_full, U * F * d * es);
-    CP(a->a_k, v.a_k, U * N * r * es);
-    CP(a->a_v, v.a_v, U * N * r * es);
-    CP(a->w_k, v.w_k, U * S * r * d * es);
-    CP(a->w_v, v.w_v, U * S * r * d * es);
-#undef CP
-    return RSKV_OK;
+    if ((rc = cp(a->span_id, v.span_id, static_cast<size_t>(B) * c->T * 4, "export span_id")))
+      return rc;
+    if ((rc = cp(a->span_start, v.span_start, B * S * 4, "export span_start"))) return rc;
+    if ((rc = cp(a->span_len, v.span_len, B * S * 4, "export span_len"))) return rc;
+    if ((rc = cp(a->full_pos, v.full_pos, B * F * 4, "export full_pos"))) return rc;
+    if ((rc = cp(a->log_len, v.log_len, B * S * 4, "export log_len"))) return rc;
+    return c->dtype == RSKV_BF16 ? export_arrays<uint16_t>(c, a) : export_arrays<uint32_t>(c, a);
+  } catch (const std::bad_alloc&) {
+    return fail(RSKV_ENOMEM, "host allocation failed");
   } catch (...) {
     return fail(RSKV_EINVAL, "unexpected error in rskv_cache_export");
   }
@@ -455,82 +641,73 @@ int rskv_cache_import(const rskv_host_arrays* a, const rskv_build_opts* opts, in
     c->h_n_spans.resize(B);
     c->h_n_full0.resize(B);
     c->h_n_span_tokens.resize(B);
+    c->h_n_tok_pad.resize(B);
     for (int b = 0; b < B; ++b) {
       const int ns = a->n_spans[b], nf = a->n_full[b], nt = a->n_span_tokens[b];
       if (ns < 0 || ns > S_in || nf < 0 || nf > F_in || nt < 0 || nt > N_in)
         return fail(RSKV_EINVAL, "counts exceed the padded dimensions");
-      long long sum = 0;
+      long long sum = 0, pad = 0;
       for (int j = 0; j < ns; ++j) {
         const int len = a->span_len[static_cast<size_t>(b) * S_in + j];
         if (len < 1) return fail(RSKV_EINVAL, "span lengths must be >= 1");
         sum += len;
+        pad += rskv::round_up(len, 16);
       }
       if (sum != nt) return fail(RSKV_EINVAL, "n_span_tokens differs from the sum of lengths");
       c->h_n_anchor[b] = a->n_anchor ? a->n_anchor[b] : 0;
       c->h_n_spans[b] = ns;
       c->h_n_full0[b] = nf;
       c->h_n_span_tokens[b] = nt;
+      c->h_n_tok_pad[b] = static_cast<int>(pad);
     }
     finish_sizes(c, opts);
     if ((rc = alloc_arrays(c, st)) != RSKV_OK) return rc;
     rc = dev_alloc(c, &c->dev.span_id, static_cast<size_t>(B) * c->T, "span_id");
     if (rc != RSKV_OK) return rc;
     if ((rc = copy_proj(c, opts, st, true)) != RSKV_OK) return rc;
+    RSKV_HIP(hipStreamSynchronize(st), "import memset");
     auto& v = c->dev;
-    const size_t U = static_cast<size_t>(B) * c->Hkv;
-    const size_t es = elem_size(c->dtype);
-    const size_t d = c->d, r = c->rank;
-    // tok_off on the host from the lengths
-    std::vector<int32_t> tok(static_cast<size_t>(B) * (c->S + 1), 0);
+    // span tables and offsets
+    std::vector<int32_t> starts(static_cast<size_t>(B) * c->S, 0), lens(starts.size(), 0),
+        off(static_cast<size_t>(B) * (c->S + 1), 0), pad(off.size(), 0),
+        fpos(static_cast<size_t>(B) * c->F, -1);
+    std::vector<float> ell(starts.size(), 0.f);
+    std::vector<int> o, p;
     for (int b = 0; b < B; ++b) {
-      int acc = 0;
-      for (int j = 0; j < c->h_n_spans[b]; ++j) {
-        tok[static_cast<size_t>(b) * (c->S + 1) + j] = acc;
-        acc += a->span_len[static_cast<size_t>(b) * S_in + j];
+      const int ns = c->h_n_spans[b];
+      const int32_t* L = a->span_len + static_cast<size_t>(b) * S_in;
+      span_offsets(L, ns, &o, &p);
+      for (int j = 0; j < ns; ++j) {
+        starts[static_cast<size_t>(b) * c->S + j] = a->span_start[static_cast<size_t>(b) * S_in + j];
+        lens[static_cast<size_t>(b) * c->S + j] = L[j];
+        ell[static_cast<size_t>(b) * c->S + j] = a->log_len[static_cast<size_t>(b) * S_in + j];
       }
-      tok[static_cast<size_t>(b) * (c->S + 1) + c->h_n_spans[b]] = acc;
-    }
-    RSKV_HIP(hipMemcpy(v.tok_off, tok.data(), tok.size() * 4, hipMemcpyHostToDevice), "tok_off");
-    auto cp2d = [&](void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
-                    size_t rows, const char* what) -> int {
-      hipError_t e = hipMemcpy2D(dst, dpitch, src, spitch, width, rows, hipMemcpyHostToDevice);
-      if (e != hipSuccess) return hip_fail(e, what);
-      return RSKV_OK;
-    };
-    const size_t Sd = c->S, Fd = c->F, Nd = c->N;
-    const size_t sw = std::min<size_t>(S_in, Sd), fw = std::min<size_t>(F_in, Fd),
-                 nw = std::min<size_t>(N_in, Nd);
-    if ((rc = cp2d(v.span_start, Sd * 4, a->span_start, S_in * 4ul, sw * 4, B, "span_start")))
-      return rc;
-    if ((rc = cp2d(v.span_len, Sd * 4, a->span_len, S_in * 4ul, sw * 4, B, "span_len"))) return rc;
-    if ((rc = cp2d(v.log_len, Sd * 4, a->log_len, S_in * 4ul, sw * 4, B, "log_len"))) return rc;
-    // full_pos: pad -1
-    std::vector<int32_t> fp(static_cast<size_t>(B) * Fd, -1);
-    for (int b = 0; b < B; ++b)
+      for (int j = 0; j <= ns; ++j) {
+        off[static_cast<size_t>(b) * (c->S + 1) + j] = o[j];
+        pad[static_cast<size_t>(b) * (c->S + 1) + j] = p[j];
+      }
       for (int i = 0; i < c->h_n_full0[b]; ++i)
-        fp[static_cast<size_t>(b) * Fd + i] = a->full_pos[static_cast<size_t>(b) * F_in + i];
-    RSKV_HIP(hipMemcpy(v.full_pos, fp.data(), fp.size() * 4, hipMemcpyHostToDevice), "full_pos");
-    if (a->span_id != nullptr)
-      RSKV_HIP(hipMemcpy(v.span_id, a->span_id, static_cast<size_t>(B) * c->T * 4,
-                         hipMemcpyHostToDevice),
-               "span_id");
-    if ((rc = cp2d(v.summary, Sd * d * es, a->summary, S_in * d * es, sw * d * es, U, "summary")))
+        fpos[static_cast<size_t>(b) * c->F + i] = a->full_pos[static_cast<size_t>(b) * F_in + i];
+    }
+    auto put = [&](void* dst, const void* src, size_t bytes, const char* what) -> int {
+      hipError_t e = hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
+      return e == hipSuccess ? RSKV_OK : hip_fail(e, what);
+    };
+    if ((rc = put(v.span_start, starts.data(), starts.size() * 4, "import span_start"))) return rc;
+    if ((rc = put(v.span_len, lens.data(), lens.size() * 4, "import span_len"))) return rc;
+    if ((rc = put(v.log_len, ell.data(), ell.size() * 4, "import log_len"))) return rc;
+    if ((rc = put(v.tok_off, off.data(), off.size() * 4, "import tok_off"))) return rc;
+    if ((rc = put(v.tok_pad, pad.data(), pad.size() * 4, "import tok_pad"))) return rc;
+    if ((rc = put(v.full_pos, fpos.data(), fpos.size() * 4, "import full_pos"))) return rc;
+    if (a->span_id != nullptr &&
+        (rc = put(v.span_id, a->span_id, static_cast<size_t>(B) * c->T * 4, "import span_id")))
       return rc;
-    if ((rc = cp2d(v.vmean, Sd * d * es, a->vmean, S_in * d * es, sw * d * es, U, "vmean")))
-      return rc;
-    if ((rc = cp2d(v.k_full, Fd * d * es, a->k_full, F_in * d * es, fw * d * es, U, "k_full")))
-      return rc;
-    if ((rc = cp2d(v.v_full, Fd * d * es, a->v_full, F_in * d * es, fw * d * es, U, "v_full")))
-      return rc;
-    if ((rc = cp2d(v.a_k, Nd * r * es, a->a_k, N_in * r * es, nw * r * es, U, "a_k"))) return rc;
-    if ((rc = cp2d(v.a_v, Nd * r * es, a->a_v, N_in * r * es, nw * r * es, U, "a_v"))) return rc;
-    if ((rc = cp2d(v.w_k, Sd * r * d * es, a->w_k, S_in * r * d * es, sw * r * d * es, U, "w_k")))
-      return rc;
-    if ((rc = cp2d(v.w_v, Sd * r * d * es, a->w_v, S_in * r * d * es, sw * r * d * es, U, "w_v")))
-      return rc;
-    RSKV_HIP(hipMemcpy(v.n_spans, c->h_n_spans.data(), B * 4, hipMemcpyHostToDevice), "n_spans");
-    RSKV_HIP(hipMemcpy(v.n_full, c->h_n_full0.data(), B * 4, hipMemcpyHostToDevice), "n_full");
-    RSKV_HIP(hipMemcpy(v.n_full0, c->h_n_full0.data(), B * 4, hipMemcpyHostToDevice), "n_full0");
+    if ((rc = put(v.n_spans, c->h_n_spans.data(), B * 4, "import n_spans"))) return rc;
+    if ((rc = put(v.n_full, c->h_n_full0.data(), B * 4, "import n_full"))) return rc;
+    if ((rc = put(v.n_full0, c->h_n_full0.data(), B * 4, "import n_full0"))) return rc;
+    rc = c->dtype == RSKV_BF16 ? import_arrays<uint16_t>(c, a, S_in, F_in, N_in)
+                               : import_arrays<uint32_t>(c, a, S_in, F_in, N_in);
+    if (rc != RSKV_OK) return rc;
     RSKV_HIP(hipDeviceSynchronize(), "import");
     guard.c = nullptr;
     *out = c;
@@ -561,9 +738,10 @@ int rskv_profile_read(rskv_cache* c, rskv_profile* p) {
   if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
   if (p == nullptr) return fail(RSKV_EINVAL, "profile is NULL");
   auto& pr = c->prof;
-  for (size_t i = 0; i + 5 <= pr.pending.size(); i += 5) {
-    RSKV_HIP(hipEventSynchronize(pr.pending[i + 4]), "event sync");
-    for (int k = 0; k < 4; ++k) {
+  constexpr int kEv = rskv::kProfileEvents;
+  for (size_t i = 0; i + kEv <= pr.pending.size(); i += kEv) {
+    RSKV_HIP(hipEventSynchronize(pr.pending[i + kEv - 1]), "event sync");
+    for (int k = 0; k < kEv - 1; ++k) {
       float ms = 0.f;
       RSKV_HIP(hipEventElapsedTime(&ms, pr.pending[i + k], pr.pending[i + k + 1]), "elapsed");
       pr.ms[k] += ms;

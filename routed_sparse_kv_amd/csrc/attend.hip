@@ -4,18 +4,32 @@
 //   - every token of an expanded span, rebuilt from its factors:
 //     k-hat_i = A_K[i] W_K, v-hat_i = A_V[i] W_V;
 //   - every other span as one entry: key s_j with logit <q, s_j>/sqrt(d) +
-//     ln|S_j| (precomputed by the routing pass), value the span mean.
-//
-// Split-K: the unit's work items (32-row full-resolution chunks, expanded
-// spans, 32-span summary chunks) are dealt round-robin to `nsplit`
-// workgroups; each keeps an online-softmax state (m, l, acc) per query head
-// and writes it as a partial; merge_kernel combines the partials with the
-// log-sum-exp rule.
+//     ln|S_j| (written by the routing pass, -inf once the span is expanded),
+//     value the span mean.
 //
 // The rank-r contraction is applied to the small operands instead of
 // materialising K-hat and V-hat:  <q, A_i W_K> = A_i (W_K q)  and
-// sum_i p_i A_i W_V = (sum_i p_i A_i) W_V,  which is the same arithmetic up
-// to association and reads each factor exactly once.
+// sum_i p_i A_i W_V = (sum_i p_i A_i) W_V,  the same arithmetic up to
+// association, reading every factor exactly once.
+//
+// bf16 caches, r in {8, 16}: attend_mfma_kernel.  Work items of a unit
+// (32-row full-resolution chunks, expanded spans, 32-span summary chunks)
+// are dealt round-robin to the waves of `nsplit` workgroups.  A wave loads a
+// whole item with 16-byte MFMA-operand loads from the tiled layouts of
+// layout.h and keeps its online-softmax state (max, sum, out^T) in the MFMA
+// accumulator layout; all products are 16x16 MFMAs with fp32 accumulation
+// (fp32 intermediates enter as a bf16 hi + lo pair).  The workgroup merges
+// its four waves in LDS and writes one partial.
+//
+// Other caches (fp32, or other ranks): attend_valu_kernel, a block-
+// cooperative fp32 version of the same computation.
+//
+// merge_kernel (next launch) combines the partials of a unit with the
+// log-sum-exp rule.  Merging inside the attention kernel would need a
+// device-scope release per workgroup, which on gfx950 writes back the XCD's
+// L2 and serialises across workgroups; the kernel boundary is cheaper.
+#include <stdlib.h>
+
 #include "cache.h"
 #include "common.h"
 
@@ -26,7 +40,328 @@ constexpr int kAttThreads = 256;
 constexpr int kChunk = 32;
 constexpr int kMaxG = 8;
 constexpr int kMaxRank = 32;
-constexpr int kMaxOut = 4;  // outputs per thread: G * d <= 1024
+constexpr int kMaxOut = 4;           // VALU path: outputs per thread, G*d <= 1024
+constexpr int kMaxSplitMfma = 256;   // final merge keeps nsplit*G weights in LDS
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x4 ld4(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x4*>(p);
+}
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// fp32 x as bf16 hi + lo (hi + lo equals x to ~16 significant bits)
+__device__ __forceinline__ void split4(const float* x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 hb = static_cast<__bf16>(x[e]);
+    hi[e] = hb;
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hb));
+  }
+}
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 hb = static_cast<__bf16>(x[e]);
+    hi[e] = hb;
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hb));
+  }
+}
+
+// Online-softmax update of a wave for 8 logits per lane (lane: head l % 16,
+// rows 4 g + i and 16 + 4 g + i).  Turns x into probabilities relative to
+// the new running max and returns the factor that rescales older state.
+__device__ __forceinline__ float wave_softmax8(float* x, float& m, float& l) {
+  float cm = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
+  cm = fmaxf(cm, __shfl_xor(cm, 16, kWave));
+  cm = fmaxf(cm, __shfl_xor(cm, 32, kWave));
+  const float mn = fmaxf(m, cm);
+  const float sc = mn == -INFINITY ? 1.f : __expf(m - mn);
+  float ps = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = x[e] == -INFINITY ? 0.f : __expf(x[e] - mn);
+    ps += x[e];
+  }
+  ps += __shfl_xor(ps, 16, kWave);
+  ps += __shfl_xor(ps, 32, kWave);
+  l = l * sc + ps;
+  m = mn;
+  return sc;
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kf,
+    const uint16_t* __restrict__ vf, const int32_t* __restrict__ n_full,
+    const uint16_t* __restrict__ vmean, const float* __restrict__ slogit,
+    const int32_t* __restrict__ n_spans, const uint16_t* __restrict__ a_k,
+    const uint16_t* __restrict__ a_v, const uint16_t* __restrict__ w_k,
+    const uint16_t* __restrict__ w_v, const int32_t* __restrict__ span_len,
+    const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ n_sel, int Hkv, int G, int S, int Sp, int Fp, int Np,
+    int nsplit, int nsplit_max, float inv_sqrt_d, float* __restrict__ part) {
+  constexpr int KK = D / 32;  // 32-column chunks of the QK product
+  constexpr int CB = D / 16;  // 16-column blocks of the PV product
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int g16 = lane & 15;
+  const int grp = lane >> 4;
+  const int s = blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / Hkv;
+  const int h = u - b * Hkv;
+  const bool head_ok = g16 < G;
+
+  // Q as the B operand: head g16, columns 32 kk + 8 grp + 0..7
+  bf16x8 qb[KK];
+  {
+    const uint16_t* qp = q + (static_cast<size_t>(b) * Hkv * G + static_cast<size_t>(h) * G +
+                              (head_ok ? g16 : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qb[kk] = ld8(qp + 32 * kk + 8 * grp);
+      if (!head_ok) qb[kk] = bf16x8{};
+    }
+  }
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kf_u = kf + static_cast<size_t>(u) * Fp * D;
+  const uint16_t* vf_u = vf + static_cast<size_t>(u) * Fp * D;
+  const uint16_t* vm_u = vmean + static_cast<size_t>(u) * Sp * D;
+  const float* sl_u = slogit + static_cast<size_t>(u) * Sp * G;
+  const uint16_t* ak_u = a_k + static_cast<size_t>(u) * Np * R;
+  const uint16_t* av_u = a_v + static_cast<size_t>(u) * Np * R;
+  const uint16_t* wk_u = w_k + static_cast<size_t>(u) * S * R * D;
+  const uint16_t* wv_u = w_v + static_cast<size_t>(u) * S * D * R;
+
+  const int nf = n_full[b];
+  const int ns = n_spans[b];
+  const int nsel = n_sel[u];
+  const int nFI = (nf + kChunk - 1) / kChunk;
+  const int nSI = (ns + kChunk - 1) / kChunk;
+  const int NI = nFI + nsel + nSI;
+  const int nwaves = nsplit * 4;
+
+  for (int it = s * 4 + wave; it < NI; it += nwaves) {
+    if (it < nFI || it >= nFI + nsel) {
+      // ------------- 32 full-resolution rows, or 32 span summaries
+      const bool full = it < nFI;
+      const int r0 = (full ? it : it - nFI - nsel) * kChunk;
+      const int lim = full ? nf : ns;
+      bf16x8 va[CB];
+      const uint16_t* vt = (full ? vf_u : vm_u) + static_cast<size_t>(r0 / 32) * CB * 512;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) va[cb] = ld8(vt + cb * 512 + lane * 8);
+      float x[8];
+      if (full) {
+        bf16x8 ka[2][KK];
+        const uint16_t* kt = kf_u + static_cast<size_t>(r0 / 16) * KK * 512;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) ka[t][kk] = ld8(kt + (t * KK + kk) * 512 + lane * 8);
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          s0 = mma32(ka[0][kk], qb[kk], s0);
+          s1 = mma32(ka[1][kk], qb[kk], s1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = s0[i] * inv_sqrt_d;
+          x[4 + i] = s1[i] * inv_sqrt_d;
+        }
+      } else {
+        f32x4 l0 = {0.f, 0.f, 0.f, 0.f}, l1 = l0;
+        if (head_ok) {
+          l0 = *reinterpret_cast<const f32x4*>(sl_u + (static_cast<size_t>(r0 / 16) * G + g16) * 16 + 4 * grp);
+          l1 = *reinterpret_cast<const f32x4*>(sl_u + (static_cast<size_t>(r0 / 16 + 1) * G + g16) * 16 + 4 * grp);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = l0[i];
+          x[4 + i] = l1[i];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = r0 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4));
+        if (!head_ok || row >= lim) x[e] = -INFINITY;
+      }
+      const float sc = wave_softmax8(x, m, l);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] *= sc;
+      bf16x8 phi, plo;
+      split8(x, phi, plo);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        acc[cb] = mma32(va[cb], phi, acc[cb]);
+        acc[cb] = mma32(va[cb], plo, acc[cb]);
+      }
+    } else {
+      // ------------- expanded span: factors of K and V
+      const int j = sel[static_cast<size_t>(u) * S + (it - nFI)];
+      const int len = span_len[static_cast<size_t>(b) * S + j];
+      const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
+      const bool kgrp_ok = grp < R / 4;   // lane group holds ranks 4 grp..4 grp+3
+      // Issue the span's loads in the order they are used: W_K, the first
+      // 32 rows of A_K and A_V, then W_V.
+      bf16x8 wka[KK];
+      {
+        const uint16_t* wk = wk_u + static_cast<size_t>(j) * R * D + (g16 < R ? g16 : 0) * D;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          wka[kk] = ld8(wk + 32 * kk + 8 * grp);
+          if (g16 >= R) wka[kk] = bf16x8{};
+        }
+      }
+      auto load_a = [&](int t0, bf16x4* ak, bf16x4* av) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          ak[t] = bf16x4{};
+          av[t] = bf16x4{};
+          if (t0 + 16 * t < len) {
+            ak[t] = ld4(ak_u + static_cast<size_t>(tp + t0 + 16 * t + g16) * R +
+                        (kgrp_ok ? 4 * grp : 0));
+            av[t] = ld4(av_u + (static_cast<size_t>((tp + t0 + 16 * t) >> 4) * R +
+                                (g16 < R ? g16 : 0)) * 16 + 4 * grp);
+            if (!kgrp_ok) ak[t] = bf16x4{};
+            if (g16 >= R) av[t] = bf16x4{};
+          }
+        }
+      };
+      bf16x4 ak[2], av[2];
+      load_a(0, ak, av);
+      bf16x4 wva[CB];
+      {
+        const uint16_t* wv = wv_u + static_cast<size_t>(j) * D * R;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          wva[cb] = ld4(wv + static_cast<size_t>(16 * cb + g16) * R + (kgrp_ok ? 4 * grp : 0));
+          if (!kgrp_ok) wva[cb] = bf16x4{};
+        }
+      }
+      // uk[k][head] = sum_c W_K[k][c] q[head][c]
+      f32x4 uk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) uk = mma32(wka[kk], qb[kk], uk);
+      bf16x4 uhi, ulo;
+      {
+        float t4[4] = {uk[0], uk[1], uk[2], uk[3]};
+        split4(t4, uhi, ulo);
+      }
+      f32x4 wacc = {0.f, 0.f, 0.f, 0.f};  // w[k = 4 grp + i][head]
+      for (int t0 = 0; t0 < len; t0 += kChunk) {
+        bf16x4 akn[2], avn[2];
+        if (t0 + kChunk < len) load_a(t0 + kChunk, akn, avn);  // prefetch the next rows
+        const bool t1_ok = t0 + 16 < len;
+        f32x4 sv[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (t == 0 || t1_ok) {
+            sv[t] = mma16(ak[t], uhi, sv[t]);
+            sv[t] = mma16(ak[t], ulo, sv[t]);
+          }
+        }
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = (head_ok && t0 + 4 * grp + i < len) ? sv[0][i] * inv_sqrt_d : -INFINITY;
+          x[4 + i] = (head_ok && t0 + 16 + 4 * grp + i < len) ? sv[1][i] * inv_sqrt_d : -INFINITY;
+        }
+        const float sc = wave_softmax8(x, m, l);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[cb] *= sc;
+        wacc *= sc;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (t == 0 || t1_ok) {
+            bf16x4 phi, plo;
+            split4(x + 4 * t, phi, plo);
+            wacc = mma16(av[t], phi, wacc);
+            wacc = mma16(av[t], plo, wacc);
+          }
+        }
+        if (t0 + kChunk < len) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            ak[t] = akn[t];
+            av[t] = avn[t];
+          }
+        }
+      }
+      // out^T += W_V^T w
+      bf16x4 whi, wlo;
+      {
+        float t4[4] = {wacc[0], wacc[1], wacc[2], wacc[3]};
+        split4(t4, whi, wlo);
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        acc[cb] = mma16(wva[cb], whi, acc[cb]);
+        acc[cb] = mma16(wva[cb], wlo, acc[cb]);
+      }
+    }
+  }
+
+  // ---- merge the four waves of the workgroup in LDS, write one partial
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  __shared__ float sm_buf[4 * D * 16];  // per wave out^T[c][head]
+  if (grp == 0) {
+    sm_m[wave][g16] = m;
+    sm_l[wave][g16] = l;
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_buf[(wave * D + 16 * cb + 4 * grp + i) * 16 + g16] = acc[cb][i];
+  __syncthreads();
+  const size_t ps = static_cast<size_t>(G) * (D + 2);
+  float* Pb = part + (static_cast<size_t>(u) * nsplit_max + s) * ps;
+  for (int o = tid; o < G * D; o += kAttThreads) {
+    const int g = o / D;
+    const int c = o - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][g]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __expf(sm_m[w][g] - M);
+        num += f * sm_buf[(w * D + c) * 16 + g];
+        den += f * sm_l[w][g];
+      }
+    }
+    Pb[g * (D + 2) + 2 + c] = num;
+    if (c == 0) {
+      Pb[g * (D + 2)] = M;
+      Pb[g * (D + 2) + 1] = den;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// fp32 (and any-rank) path: block-cooperative fp32 attention
 
 struct SoftmaxState {
   float m[kMaxG];
@@ -62,17 +397,16 @@ __device__ __forceinline__ void chunk_softmax(float (*lg)[kMaxG + 1], SoftmaxSta
 }
 
 template <int DT>
-__global__ __launch_bounds__(kAttThreads) void attend_kernel(
+__global__ __launch_bounds__(kAttThreads) void attend_valu_kernel(
     const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ kf,
     const typename Elem<DT>::T* __restrict__ vf, const int32_t* __restrict__ n_full,
     const typename Elem<DT>::T* __restrict__ vmean, const float* __restrict__ slogit,
-    const uint8_t* __restrict__ expanded, const int32_t* __restrict__ n_spans,
-    const typename Elem<DT>::T* __restrict__ a_k, const typename Elem<DT>::T* __restrict__ a_v,
-    const typename Elem<DT>::T* __restrict__ w_k, const typename Elem<DT>::T* __restrict__ w_v,
-    const int32_t* __restrict__ span_len, const int32_t* __restrict__ tok_off,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int Hkv, int G, int d,
-    int S, int F, int N, int rank, int k_slots, int nsplit, int nsplit_max, int nFC, int nSC,
-    float inv_sqrt_d, float* __restrict__ part) {
+    const int32_t* __restrict__ n_spans, const typename Elem<DT>::T* __restrict__ a_k,
+    const typename Elem<DT>::T* __restrict__ a_v, const typename Elem<DT>::T* __restrict__ w_k,
+    const typename Elem<DT>::T* __restrict__ w_v, const int32_t* __restrict__ span_len,
+    const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ n_sel, int Hkv, int G, int d, int S, int Sp, int Fp, int Np,
+    int rank, int nsplit, int nsplit_max, float inv_sqrt_d, float* __restrict__ part) {
   typedef Elem<DT> E;
   const int s = blockIdx.x;
   const int u = blockIdx.y;
@@ -105,15 +439,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const int nf = n_full[b];
   const int ns = n_spans[b];
   const int nsel = n_sel[u];
-  const int NI = nFC + k_slots + nSC;
-  const size_t ubase_f = static_cast<size_t>(u) * F;
-  const size_t ubase_s = static_cast<size_t>(u) * S;
+  const int nFI = (nf + kChunk - 1) / kChunk;
+  const int nSI = (ns + kChunk - 1) / kChunk;
+  const int NI = nFI + nsel + nSI;
+  const size_t fbase = static_cast<size_t>(u) * Fp * d;
+  const size_t sbase = static_cast<size_t>(u) * Sp * d;
+  const float* sl_u = slogit + static_cast<size_t>(u) * Sp * G;
 
   for (int it = s; it < NI; it += nsplit) {
-    if (it < nFC) {
+    if (it < nFI) {
       // ---------------- full-resolution rows r0 .. r0+31
       const int r0 = it * kChunk;
-      if (r0 >= nf) continue;
       {
         const int i = tid >> 3;
         const int p = tid & 7;
@@ -124,10 +460,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
         for (int g = 0; g < kMaxG; ++g) dot[g] = 0.f;
         if (valid) {
           const int cpl = d / 8;
-          const size_t base = (ubase_f + row) * d + static_cast<size_t>(p) * cpl;
           for (int e = 0; e < cpl; ++e) {
-            const float kv = E::ld(kf, base + e);
             const int c = p * cpl + e;
+            const float kv = E::ld(kf, fbase + k16_off(row, c, d));
 #pragma unroll
             for (int g = 0; g < kMaxG; ++g)
               if (g < G) dot[g] += qs[g][c] * kv;
@@ -140,6 +475,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
       }
       __syncthreads();
       chunk_softmax(lg, &st, G);
+      const int nr = min(kChunk, nf - r0);
 #pragma unroll
       for (int oi = 0; oi < kMaxOut; ++oi) {
         const int o = tid + oi * kAttThreads;
@@ -147,27 +483,24 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
           const int g = o / d;
           const int c = o - g * d;
           float a = acc[oi] * st.sc[g];
-          const int nr = min(kChunk, nf - r0);
-          for (int i = 0; i < nr; ++i)
-            a += lg[i][g] * E::ld(vf, (ubase_f + r0 + i) * d + c);
+          for (int i = 0; i < nr; ++i) a += lg[i][g] * E::ld(vf, fbase + v32_off(r0 + i, c, d));
           acc[oi] = a;
         }
       }
       __syncthreads();
-    } else if (it < nFC + k_slots) {
+    } else if (it < nFI + nsel) {
       // ---------------- expanded span sel[e], rebuilt from its factors
-      const int e = it - nFC;
-      if (e >= nsel) continue;
-      const int j = sel[ubase_s + e];
+      const int j = sel[static_cast<size_t>(u) * S + (it - nFI)];
       const int len = span_len[static_cast<size_t>(b) * S + j];
-      const size_t toff = static_cast<size_t>(u) * N + tok_off[static_cast<size_t>(b) * (S + 1) + j];
-      const size_t wbase = (ubase_s + j) * rank;
+      const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
+      const size_t abase = static_cast<size_t>(u) * Np * rank;
+      const size_t wkbase = (static_cast<size_t>(u) * S + j) * rank * d;
+      const size_t wvbase = static_cast<size_t>(u) * S * d * rank;
       for (int pi = tid; pi < G * rank; pi += kAttThreads) {
         const int g = pi / rank;
         const int k = pi - g * rank;
-        const size_t wrow = (wbase + k) * d;
         float a = 0.f;
-        for (int c = 0; c < d; ++c) a += E::ld(w_k, wrow + c) * qs[g][c];
+        for (int c = 0; c < d; ++c) a += E::ld(w_k, wkbase + static_cast<size_t>(k) * d + c) * qs[g][c];
         uk[g][k] = a;
         wv[g][k] = 0.f;
       }
@@ -179,7 +512,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
           const int t = i0 + i;
           float a = -INFINITY;
           if (t < len) {
-            const size_t arow = (toff + t) * rank;
+            const size_t arow = abase + static_cast<size_t>(tp + t) * rank;
             a = 0.f;
             for (int k = 0; k < rank; ++k) a += E::ld(a_k, arow + k) * uk[g][k];
             a *= inv_sqrt_d;
@@ -193,7 +526,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
           const int g = pi / rank;
           const int k = pi - g * rank;
           float a = wv[g][k] * st.sc[g];
-          for (int i = 0; i < nr; ++i) a += lg[i][g] * E::ld(a_v, (toff + i0 + i) * rank + k);
+          for (int i = 0; i < nr; ++i)
+            a += lg[i][g] * E::ld(a_v, abase + avt_off(tp + i0 + i, k, rank));
           wv[g][k] = a;
         }
 #pragma unroll
@@ -210,22 +544,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
           const int g = o / d;
           const int c = o - g * d;
           float a = acc[oi];
-          for (int k = 0; k < rank; ++k) a += wv[g][k] * E::ld(w_v, (wbase + k) * d + c);
+          for (int k = 0; k < rank; ++k) a += wv[g][k] * E::ld(w_v, wvbase + wvt_off(j, k, c, d, rank));
           acc[oi] = a;
         }
       }
       __syncthreads();
     } else {
       // ---------------- unexpanded spans j0 .. j0+31 (summary entries)
-      const int j0 = (it - nFC - k_slots) * kChunk;
-      if (j0 >= ns) continue;
+      const int j0 = (it - nFI - nsel) * kChunk;
       for (int pi = tid; pi < kChunk * G; pi += kAttThreads) {
         const int i = pi / G;
         const int g = pi - i * G;
         const int j = j0 + i;
-        float a = -INFINITY;
-        if (j < ns && !expanded[ubase_s + j]) a = slogit[(ubase_s + j) * G + g];
-        lg[i][g] = a;
+        lg[i][g] = j < ns ? sl_u[slogit_off(j, g, G)] : -INFINITY;
       }
       __syncthreads();
       chunk_softmax(lg, &st, G);
@@ -239,7 +570,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
           float a = acc[oi] * st.sc[g];
           for (int i = 0; i < nr; ++i) {
             const float p = lg[i][g];
-            if (p != 0.f) a += p * E::ld(vmean, (ubase_s + j0 + i) * d + c);
+            if (p != 0.f) a += p * E::ld(vmean, sbase + v32_off(j0 + i, c, d));
           }
           acc[oi] = a;
         }
@@ -264,88 +595,140 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 }
 
 // out[b][h*G+g][c] = sum_s e^{m_s-M} acc_s / sum_s e^{m_s-M} l_s.
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part, int nsplit,
+// One workgroup per (unit, query head).  The split weights e^{m_s - M} and
+// the denominator are formed once in LDS; thread c then sums its column over
+// the splits with independent loads.
+__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part, int nsplit,
                                                     int nsplit_max, int Hkv, int G, int d,
                                                     float* __restrict__ out) {
   const int u = blockIdx.x;
+  const int g = blockIdx.y;
   const int b = u / Hkv;
   const int h = u - b * Hkv;
+  const int tid = threadIdx.x;
   const size_t ps = static_cast<size_t>(G) * (d + 2);
-  const float* P = part + static_cast<size_t>(u) * nsplit_max * ps;
-  for (int o = threadIdx.x; o < G * d; o += blockDim.x) {
-    const int g = o / d;
-    const int c = o - g * d;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, P[s * ps + g * (d + 2)]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* ps_g = P + s * ps + g * (d + 2);
-        const float w = expf(ps_g[0] - M);
-        num += w * ps_g[2 + c];
-        den += w * ps_g[1];
-      }
-    }
+  const float* P = part + static_cast<size_t>(u) * nsplit_max * ps + static_cast<size_t>(g) * (d + 2);
+  __shared__ float w[kMaxSplitMfma > 2048 ? kMaxSplitMfma : 2048];
+  __shared__ float red[2];
+  // max over splits
+  float M = -INFINITY;
+  for (int s = tid; s < nsplit; s += blockDim.x) {
+    const float m = P[s * ps];
+    w[s] = m;
+    M = fmaxf(M, m);
+  }
+  M = wave_max(M);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float den = 0.f;
+  for (int s = tid; s < nsplit; s += blockDim.x) {
+    const float f = (M == -INFINITY || w[s] == -INFINITY) ? 0.f : expf(w[s] - M);
+    w[s] = f;
+    den += f * P[s * ps + 1];
+  }
+  den = wave_sum(den);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = den;
+  __syncthreads();
+  den = red[0] + red[1];
+  for (int c = tid; c < d; c += blockDim.x) {
+    float num = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) num += w[s] * P[s * ps + 2 + c];
     out[(static_cast<size_t>(b) * Hkv * G + static_cast<size_t>(h) * G + g) * d + c] =
-        M == -INFINITY ? 0.f : num / den;
+        den > 0.f ? num / den : 0.f;
   }
 }
 
-template <int DT>
-hipError_t attend_impl(const rskv_cache* c, const void* q, int k_max, int nsplit,
-                       hipStream_t st) {
-  typedef typename Elem<DT>::T T;
-  const int nFC = (c->F + kChunk - 1) / kChunk;
-  const int nSC = (c->S + kChunk - 1) / kChunk;
-  const int k_slots = k_max < c->S ? k_max : c->S;
+bool use_mfma(const rskv_cache* c) {
+  return c->dtype == kBF16 && (c->rank == 8 || c->rank == 16) && (c->d == 64 || c->d == 128);
+}
+
+template <int D, int R>
+hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st) {
   dim3 grid(nsplit, c->B * c->Hkv);
-  hipLaunchKernelGGL(attend_kernel<DT>, grid, dim3(kAttThreads), 0, st,
+  hipLaunchKernelGGL((attend_mfma_kernel<D, R>), grid, dim3(kAttThreads), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c->dev.k_full),
+                     static_cast<const uint16_t*>(c->dev.v_full), c->dev.n_full,
+                     static_cast<const uint16_t*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
+                     static_cast<const uint16_t*>(c->dev.a_k),
+                     static_cast<const uint16_t*>(c->dev.a_v),
+                     static_cast<const uint16_t*>(c->dev.w_k),
+                     static_cast<const uint16_t*>(c->dev.w_v), c->dev.span_len, c->dev.tok_pad,
+                     c->dev.sel, c->dev.n_sel, c->Hkv, c->G, c->S, c->Sp, c->Fp, c->Np, nsplit,
+                     c->nsplit_max, 1.0f / sqrtf(static_cast<float>(D)), c->dev.part);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t attend_valu_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  dim3 grid(nsplit, c->B * c->Hkv);
+  hipLaunchKernelGGL(attend_valu_kernel<DT>, grid, dim3(kAttThreads), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(c->dev.k_full),
                      static_cast<const T*>(c->dev.v_full), c->dev.n_full,
-                     static_cast<const T*>(c->dev.vmean), c->dev.slogit, c->dev.expanded,
-                     c->dev.n_spans, static_cast<const T*>(c->dev.a_k),
-                     static_cast<const T*>(c->dev.a_v), static_cast<const T*>(c->dev.w_k),
-                     static_cast<const T*>(c->dev.w_v), c->dev.span_len, c->dev.tok_off,
-                     c->dev.sel, c->dev.n_sel, c->Hkv, c->G, c->d, c->S, c->F, c->N, c->rank,
-                     k_slots, nsplit, c->nsplit_max, nFC, nSC,
+                     static_cast<const T*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
+                     static_cast<const T*>(c->dev.a_k), static_cast<const T*>(c->dev.a_v),
+                     static_cast<const T*>(c->dev.w_k), static_cast<const T*>(c->dev.w_v),
+                     c->dev.span_len, c->dev.tok_pad, c->dev.sel, c->dev.n_sel, c->Hkv, c->G,
+                     c->d, c->S, c->Sp, c->Fp, c->Np, c->rank, nsplit, c->nsplit_max,
                      1.0f / sqrtf(static_cast<float>(c->d)), c->dev.part);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_nsplit(const rskv_cache* c, int k_max) {
-  const int nFC = (c->F + kChunk - 1) / kChunk;
-  const int nSC = (c->S + kChunk - 1) / kChunk;
-  const int k_slots = k_max < c->S ? k_max : c->S;
-  const int NI = nFC + k_slots + nSC;
-  const int U = c->B * c->Hkv;
-  int ns = (2048 + U - 1) / U;
-  if (ns > NI) ns = NI;
-  if (ns > c->nsplit_max) ns = c->nsplit_max;
+// Split count: about `target` workgroups over all units, at least one item
+// per wave (MFMA path) or per workgroup (VALU path).
+static int nsplit_for(int B, int Hkv, int S, int F, int k_slots, bool mfma) {
+  const int U = B * Hkv;
+  const int NI = (F + kChunk - 1) / kChunk + k_slots + (S + kChunk - 1) / kChunk;
+  const int target = mfma ? 1024 : 2048;
+  int ns = (target + U - 1) / U;
+  const int per_block = mfma ? 4 : 1;
+  if (ns > (NI + per_block - 1) / per_block) ns = (NI + per_block - 1) / per_block;
+  if (mfma && ns > kMaxSplitMfma) ns = kMaxSplitMfma;
   return ns < 1 ? 1 : ns;
+}
+
+int decode_nsplit(const rskv_cache* c, int k_max) {
+  const int k_slots = k_max < c->S ? k_max : c->S;
+  int ns = nsplit_for(c->B, c->Hkv, c->S, c->F, k_slots, use_mfma(c));
+  // RSKV_ATTEND_SPLITS overrides the workgroups per unit (tuning only)
+  if (const char* e = getenv("RSKV_ATTEND_SPLITS")) {
+    const int v = atoi(e);
+    if (v > 0) ns = use_mfma(c) && v > kMaxSplitMfma ? kMaxSplitMfma : v;
+  }
+  return ns > c->nsplit_max ? c->nsplit_max : ns;
 }
 
 int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap) {
-  const int nFC = (F + kChunk - 1) / kChunk;
-  const int nSC = (S + kChunk - 1) / kChunk;
   const int k_slots = k_max_cap < S ? k_max_cap : S;
-  const int NI = nFC + k_slots + nSC;
-  const int U = B * Hkv;
-  int ns = (2048 + U - 1) / U;
-  if (ns > NI) ns = NI;
-  return ns < 1 ? 1 : ns;
+  const int a = nsplit_for(B, Hkv, S, F, k_slots, true);
+  const int v = nsplit_for(B, Hkv, S, F, k_slots, false);
+  // room for the tuning override as well (at most one workgroup per item)
+  const int NI = (F + kChunk - 1) / kChunk + k_slots + (S + kChunk - 1) / kChunk;
+  const int o = NI < kMaxSplitMfma ? NI : kMaxSplitMfma;
+  const int m = a > v ? a : v;
+  return m > o ? m : o;
 }
 
-hipError_t launch_attend(const rskv_cache* c, const void* q, int k_max, int nsplit,
-                         hipStream_t st) {
-  return c->dtype == kBF16 ? attend_impl<kBF16>(c, q, k_max, nsplit, st)
-                           : attend_impl<kF32>(c, q, k_max, nsplit, st);
+hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st) {
+  if (use_mfma(c)) {
+    if (c->d == 128)
+      return c->rank == 16 ? attend_mfma_impl<128, 16>(c, q, nsplit, st)
+                           : attend_mfma_impl<128, 8>(c, q, nsplit, st);
+    return c->rank == 16 ? attend_mfma_impl<64, 16>(c, q, nsplit, st)
+                         : attend_mfma_impl<64, 8>(c, q, nsplit, st);
+  }
+  return c->dtype == kBF16 ? attend_valu_impl<kBF16>(c, q, nsplit, st)
+                           : attend_valu_impl<kF32>(c, q, nsplit, st);
 }
 
 hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(merge_kernel, dim3(c->B * c->Hkv), dim3(256), 0, st, c->dev.part, nsplit,
-                     c->nsplit_max, c->Hkv, c->G, c->d, out);
+  hipLaunchKernelGGL(merge_kernel, dim3(c->B * c->Hkv, c->G), dim3(128), 0, st, c->dev.part,
+                     nsplit, c->nsplit_max, c->Hkv, c->G, c->d, out);
   return hipGetLastError();
 }
 

@@ -8,47 +8,54 @@
 #include <vector>
 
 #include "../../include/rskv.h"
+#include "layout.h"
 
 namespace rskv {
 
-// Device memory layout of a cache (all row-major; U = B*Hkv units, unit
-// u = b*Hkv + h; S, F, N are the padded span, full-row and span-token
-// dimensions).
+// Device memory of a cache.  U = B*Hkv units, unit u = b*Hkv + h.  S, F, N
+// are the batch maxima of spans, full-resolution rows (incl. tail capacity)
+// and span tokens; Sp = round_up(S, 32), Fp = round_up(F, 32) and Np (span
+// tokens with every span padded to 16 rows) size the tiled arrays (see
+// layout.h).
 struct DeviceArrays {
   // segmentation tables
   int32_t* span_id = nullptr;     // [B][T]
   int32_t* span_start = nullptr;  // [B][S]
   int32_t* span_len = nullptr;    // [B][S]
   int32_t* tok_off = nullptr;     // [B][S+1] exclusive prefix of span_len
+  int32_t* tok_pad = nullptr;     // [B][S+1] same with lengths rounded up to 16
   int32_t* full_pos = nullptr;    // [B][F]
   int32_t* n_spans = nullptr;     // [B]
   int32_t* n_full = nullptr;      // [B] current full rows (grows on append)
   int32_t* n_full0 = nullptr;     // [B] full rows at build time
   // stored representation (cache dtype unless noted)
-  void* summary = nullptr;        // [U][S][d]
-  void* vmean = nullptr;          // [U][S][d]
+  void* summary = nullptr;        // [U][S][d] row-major (routing GEMV rows)
+  void* vmean = nullptr;          // [U] V32 tiles over Sp spans
   float* log_len = nullptr;       // [B][S]
-  void* k_full = nullptr;         // [U][F][d]
-  void* v_full = nullptr;         // [U][F][d]
-  void* a_k = nullptr;            // [U][N][r]
-  void* a_v = nullptr;            // [U][N][r]
+  void* k_full = nullptr;         // [U] K16 tiles over Fp rows
+  void* v_full = nullptr;         // [U] V32 tiles over Fp rows
+  void* a_k = nullptr;            // [U][Np][r]
+  void* a_v = nullptr;            // [U] transposed 16-row tiles over Np rows
   void* w_k = nullptr;            // [U][S][r][d]
-  void* w_v = nullptr;            // [U][S][r][d]
+  void* w_v = nullptr;            // [U][S][d][r]
   float* proj = nullptr;          // [n_proj][d][d] or null
   // decode workspace
   double* z = nullptr;            // [U][S] routing scores
-  float* slogit = nullptr;        // [U][S][G] summary logits incl. ln|S|
-  uint8_t* expanded = nullptr;    // [U][S] 1 if span j expanded this step
-  int32_t* sel = nullptr;         // [U][kcap] expanded spans, ascending
+  float* slogit = nullptr;        // [U] summary logits incl. ln|S| (slogit_off, Sp spans)
+  int32_t* sel = nullptr;         // [U][S] expanded spans, ascending
   int32_t* n_sel = nullptr;       // [U]
   float* part = nullptr;          // [U][nsplit_max][G][d + 2] partial states
 };
 
+// Events recorded per profiled decode step: before route, top-k, attend,
+// merge and after merge.
+constexpr int kProfileEvents = 5;
+
 struct Profile {
   bool on = false;
   int64_t steps = 0;
-  double ms[4] = {0, 0, 0, 0};
-  std::vector<hipEvent_t> pending;  // 5 events per recorded step
+  double ms[kProfileEvents - 1] = {0, 0, 0, 0};
+  std::vector<hipEvent_t> pending;  // kProfileEvents per recorded step
   std::vector<hipEvent_t> pool;
 };
 
@@ -59,10 +66,10 @@ struct rskv_cache {
   int B = 0, Hq = 0, Hkv = 0, d = 0, T = 0, rank = 0, dtype = 0, G = 0;
   float alpha = 8.f;
   int n_proj = 0;
-  int S = 1, F = 1, N = 1;
+  int S = 1, F = 1, N = 1, Sp = 32, Fp = 32, Np = 16;
   int tail_cap = 0, appended = 0, k_max_cap = 0;
   int nsplit_max = 1;
-  std::vector<int32_t> h_n_anchor, h_n_spans, h_n_full0, h_n_span_tokens;
+  std::vector<int32_t> h_n_anchor, h_n_spans, h_n_full0, h_n_span_tokens, h_n_tok_pad;
   rskv::DeviceArrays dev;
   std::vector<void*> allocs;
   size_t bytes = 0;
@@ -77,11 +84,13 @@ constexpr uint32_t kMagic = 0x52534b56u;  // "RSKV"
 // ---- launchers (each returns hipSuccess or the first launch error)
 
 // Segmentation of every sequence; writes span_id, span starts/lengths,
-// token offsets, full-resolution positions (pitch T) and counts[B][4] =
-// {n_anchor, n_spans, n_full, n_span_tokens}.
+// token offsets (plain and padded), full-resolution positions (pitch T) and
+// counts[B][5] = {n_anchor, n_spans, n_full, n_span_tokens, n_tok_pad}.
+constexpr int kCounts = 5;
 hipError_t launch_segment(const float* H, int B, int T, int n_anchor, int32_t* span_id,
                           int32_t* start_tmp, int32_t* len_tmp, int32_t* tokoff_tmp,
-                          int32_t* full_tmp, int32_t* counts, hipStream_t st);
+                          int32_t* tokpad_tmp, int32_t* full_tmp, int32_t* counts,
+                          hipStream_t st);
 
 // dst[b][i] = i < counts[b*stride+index] + extra ? src[b][i] : pad.
 hipError_t launch_copy_rows(int32_t* dst, int dst_pitch, const int32_t* src, int src_pitch,
@@ -99,14 +108,14 @@ hipError_t launch_pack(const rskv_cache* c, const void* K, const void* V, hipStr
 hipError_t launch_factor(rskv_cache* c, const void* K, const void* V, hipStream_t st,
                          std::string* err);
 
-// Decode: route (z, summary logits), top-k, attention partials, merge.
+// Decode, four launches in stream order: routing GEMV (z, summary logits),
+// top-k cap, attention partials, merge of the partials into `out`.
 hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st);
 hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int32_t* sel_out,
                        int32_t* nsel_out, hipStream_t st);
 int decode_nsplit(const rskv_cache* c, int k_max);
 int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap);
-hipError_t launch_attend(const rskv_cache* c, const void* q, int k_max, int nsplit,
-                         hipStream_t st);
+hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st);
 hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st);
 
 hipError_t launch_append(rskv_cache* c, const void* k, const void* v, hipStream_t st);

@@ -34,8 +34,8 @@ template <int DT, bool kLds>
 __global__ __launch_bounds__(kFacThreads) void factor_kernel(
     const typename Elem<DT>::T* __restrict__ K, const typename Elem<DT>::T* __restrict__ V,
     const int32_t* __restrict__ span_start, const int32_t* __restrict__ span_len,
-    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ n_spans, int T, int d,
-    int S, int N, int Hkv, int rank, long long n_items, typename Elem<DT>::T* __restrict__ a_k,
+    const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ n_spans, int T, int d,
+    int S, int Np, int Hkv, int rank, long long n_items, typename Elem<DT>::T* __restrict__ a_k,
     typename Elem<DT>::T* __restrict__ a_v, typename Elem<DT>::T* __restrict__ w_k,
     typename Elem<DT>::T* __restrict__ w_v, double* __restrict__ scratch, size_t slab) {
   typedef Elem<DT> E;
@@ -155,16 +155,23 @@ __global__ __launch_bounds__(kFacThreads) void factor_kernel(
     }
     __syncthreads();
 
-    // ---- factors
-    ST* A = (kv ? a_v : a_k) +
-           (static_cast<size_t>(u) * N + tok_off[static_cast<size_t>(b) * (S + 1) + j]) * rank;
-    ST* W = (kv ? w_v : w_k) + (static_cast<size_t>(u) * S + j) * rank * d;
+    // ---- factors: A_K rows (padded span offsets), A_V transposed 16-row
+    // tiles, W_K rows [r][d], W_V transposed [d][r] (layout.h)
+    const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
+    auto a_at = [&](int t, int k) -> ST& {
+      if (kv) return a_v[static_cast<size_t>(u) * Np * rank + avt_off(tp + t, k, rank)];
+      return a_k[(static_cast<size_t>(u) * Np + tp + t) * rank + k];
+    };
+    auto w_at = [&](int k, int e) -> ST& {
+      if (kv) return w_v[static_cast<size_t>(u) * S * d * rank + wvt_off(j, k, e, d, rank)];
+      return w_k[((static_cast<size_t>(u) * S + j) * rank + k) * d + e];
+    };
     if (by_rows) {
       for (int idx = tid; idx < rj * d; idx += kFacThreads) {
         const int k = idx / d;
         const int e = idx - k * d;
         const double s = sig[top[k]];
-        W[k * d + e] = E::from_f64(s > 0.0 ? work[static_cast<size_t>(top[k]) * L + e] / s : 0.0);
+        w_at(k, e) = E::from_f64(s > 0.0 ? work[static_cast<size_t>(top[k]) * L + e] / s : 0.0);
       }
       for (int idx = tid; idx < n * rj; idx += kFacThreads) {
         const int t = idx / rj;
@@ -177,14 +184,13 @@ __global__ __launch_bounds__(kFacThreads) void factor_kernel(
             acc += static_cast<double>(E::ld(X, static_cast<size_t>(t) * d + e)) * wi[e];
           acc /= s;
         }
-        A[static_cast<size_t>(t) * rank + k] = E::from_f64(acc);
+        a_at(t, k) = E::from_f64(acc);
       }
     } else {
       for (int idx = tid; idx < n * rj; idx += kFacThreads) {
         const int t = idx / rj;
         const int k = idx - t * rj;
-        A[static_cast<size_t>(t) * rank + k] =
-            E::from_f64(work[static_cast<size_t>(top[k]) * L + t]);
+        a_at(t, k) = E::from_f64(work[static_cast<size_t>(top[k]) * L + t]);
       }
       for (int idx = tid; idx < rj * d; idx += kFacThreads) {
         const int k = idx / d;
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(kFacThreads) void factor_kernel(
             acc += static_cast<double>(E::ld(X, static_cast<size_t>(t) * d + e)) * xi[t];
           acc /= s * s;
         }
-        W[k * d + e] = E::from_f64(acc);
+        w_at(k, e) = E::from_f64(acc);
       }
     }
     __syncthreads();
@@ -229,7 +235,7 @@ hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t 
   if (n_items > 0) {
     hipLaunchKernelGGL((factor_kernel<DT, true>), dim3(grid_small), dim3(kFacThreads), 0, st,
                        static_cast<const T*>(K), static_cast<const T*>(V), c->dev.span_start,
-                       c->dev.span_len, c->dev.tok_off, c->dev.n_spans, c->T, c->d, c->S, c->N,
+                       c->dev.span_len, c->dev.tok_pad, c->dev.n_spans, c->T, c->d, c->S, c->Np,
                        c->Hkv, c->rank, n_items, static_cast<T*>(c->dev.a_k),
                        static_cast<T*>(c->dev.a_v), static_cast<T*>(c->dev.w_k),
                        static_cast<T*>(c->dev.w_v), nullptr, size_t(0));
@@ -250,7 +256,7 @@ hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t 
     hipLaunchKernelGGL((factor_kernel<DT, false>), dim3(static_cast<unsigned>(nb)),
                        dim3(kFacThreads), 0, st, static_cast<const T*>(K),
                        static_cast<const T*>(V), c->dev.span_start, c->dev.span_len,
-                       c->dev.tok_off, c->dev.n_spans, c->T, c->d, c->S, c->N, c->Hkv, c->rank,
+                       c->dev.tok_pad, c->dev.n_spans, c->T, c->d, c->S, c->Np, c->Hkv, c->rank,
                        n_items, static_cast<T*>(c->dev.a_k), static_cast<T*>(c->dev.a_v),
                        static_cast<T*>(c->dev.w_k), static_cast<T*>(c->dev.w_v), scratch, slab);
     e = hipGetLastError();

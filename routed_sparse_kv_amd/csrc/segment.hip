@@ -23,8 +23,8 @@ constexpr int kSegThreads = 1024;
 __global__ __launch_bounds__(kSegThreads) void segment_kernel(
     const float* __restrict__ H_all, int T, int n_a, int32_t* __restrict__ span_id_all,
     int32_t* __restrict__ start_all, int32_t* __restrict__ len_all,
-    int32_t* __restrict__ tokoff_all, int32_t* __restrict__ full_all,
-    int32_t* __restrict__ counts) {
+    int32_t* __restrict__ tokoff_all, int32_t* __restrict__ tokpad_all,
+    int32_t* __restrict__ full_all, int32_t* __restrict__ counts) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const float* H = H_all + static_cast<size_t>(b) * T;
@@ -32,6 +32,7 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(
   int32_t* starts = start_all + static_cast<size_t>(b) * T;
   int32_t* ends = len_all + static_cast<size_t>(b) * T;  // ends first, lengths later
   int32_t* tokoff = tokoff_all + static_cast<size_t>(b) * (T + 1);
+  int32_t* tokpad = tokpad_all + static_cast<size_t>(b) * (T + 1);
   int32_t* full = full_all + static_cast<size_t>(b) * T;
 
   __shared__ unsigned hist[256];
@@ -139,26 +140,32 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(
   }
   __syncthreads();
 
-  // ---- 4. lengths and token offsets
-  int n_tok = 0;
+  // ---- 4. lengths and token offsets (plain, and with spans padded to 16)
+  int n_tok = 0, n_pad = 0;
   for (int base = 0; base < n_spans; base += kSegThreads) {
     const int j = base + tid;
     int len = 0;
     if (j < n_spans) len = ends[j] - starts[j];
-    int tot;
+    int tot, tot_pad;
     const int before = block_excl_scan(len, scan_tmp, &tot);
+    const int before_pad = block_excl_scan(round_up(len, 16), scan_tmp, &tot_pad);
     if (j < n_spans) {
       ends[j] = len;
       tokoff[j] = n_tok + before;
+      tokpad[j] = n_pad + before_pad;
     }
     n_tok += tot;
+    n_pad += tot_pad;
   }
   if (tid == 0) {
     tokoff[n_spans] = n_tok;
-    counts[4 * b + 0] = s_nan ? -1 : n_a;  // -1 flags NaN surprisal
-    counts[4 * b + 1] = n_spans;
-    counts[4 * b + 2] = n_full;
-    counts[4 * b + 3] = n_tok;
+    tokpad[n_spans] = n_pad;
+    int32_t* cnt = counts + kCounts * b;
+    cnt[0] = s_nan ? -1 : n_a;  // -1 flags NaN surprisal
+    cnt[1] = n_spans;
+    cnt[2] = n_full;
+    cnt[3] = n_tok;
+    cnt[4] = n_pad;
   }
 }
 
@@ -179,9 +186,10 @@ __global__ void copy_rows_kernel(int32_t* __restrict__ dst, int dst_pitch,
 
 hipError_t launch_segment(const float* H, int B, int T, int n_anchor, int32_t* span_id,
                           int32_t* start_tmp, int32_t* len_tmp, int32_t* tokoff_tmp,
-                          int32_t* full_tmp, int32_t* counts, hipStream_t st) {
+                          int32_t* tokpad_tmp, int32_t* full_tmp, int32_t* counts,
+                          hipStream_t st) {
   hipLaunchKernelGGL(segment_kernel, dim3(B), dim3(kSegThreads), 0, st, H, T, n_anchor,
-                     span_id, start_tmp, len_tmp, tokoff_tmp, full_tmp, counts);
+                     span_id, start_tmp, len_tmp, tokoff_tmp, tokpad_tmp, full_tmp, counts);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(128) void summary_kernel(
     const float* __restrict__ H_all, const typename Elem<DT>::T* __restrict__ K,
     const typename Elem<DT>::T* __restrict__ V, const int32_t* __restrict__ span_start,
     const int32_t* __restrict__ span_len, const int32_t* __restrict__ n_spans, int T, int d,
-    int S, int Hkv, typename Elem<DT>::T* __restrict__ s_out,
+    int S, int Sp, int Hkv, typename Elem<DT>::T* __restrict__ s_out,
     typename Elem<DT>::T* __restrict__ v_out, float* __restrict__ log_len) {
   typedef Elem<DT> E;
   const int j = blockIdx.x;
@@ -49,9 +49,10 @@ __global__ __launch_bounds__(128) void summary_kernel(
   __syncthreads();
   const double norm2 = red[0] + red[1];
   if (c < d) {
-    const size_t o = (static_cast<size_t>(u) * S + j) * d + c;
-    s_out[o] = E::from_f64(norm2 > 0.0 ? us / sqrt(norm2) : 0.0);
-    v_out[o] = E::from_f64(vs / static_cast<double>(len));
+    s_out[(static_cast<size_t>(u) * S + j) * d + c] =
+        E::from_f64(norm2 > 0.0 ? us / sqrt(norm2) : 0.0);
+    v_out[static_cast<size_t>(u) * Sp * d + v32_off(j, c, d)] =
+        E::from_f64(vs / static_cast<double>(len));
   }
   if (c == 0 && h == 0)
     log_len[static_cast<size_t>(b) * S + j] = static_cast<float>(log(static_cast<double>(len)));
@@ -62,17 +63,18 @@ template <int DT>
 __global__ __launch_bounds__(128) void pack_kernel(
     const typename Elem<DT>::T* __restrict__ K, const typename Elem<DT>::T* __restrict__ V,
     const int32_t* __restrict__ full_pos, const int32_t* __restrict__ n_full0, int T, int d,
-    int F, int Hkv, typename Elem<DT>::T* __restrict__ kf, typename Elem<DT>::T* __restrict__ vf) {
+    int F, int Fp, int Hkv, typename Elem<DT>::T* __restrict__ kf,
+    typename Elem<DT>::T* __restrict__ vf) {
   const int i = blockIdx.x;
   const int u = blockIdx.y;
   const int b = u / Hkv;
   if (i >= n_full0[b]) return;
   const int pos = full_pos[static_cast<size_t>(b) * F + i];
   const size_t src = (static_cast<size_t>(u) * T + pos) * d;
-  const size_t dst = (static_cast<size_t>(u) * F + i) * d;
+  const size_t dst = static_cast<size_t>(u) * Fp * d;
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    kf[dst + c] = K[src + c];
-    vf[dst + c] = V[src + c];
+    kf[dst + k16_off(i, c, d)] = K[src + c];
+    vf[dst + v32_off(i, c, d)] = V[src + c];
   }
 }
 
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(128) void pack_kernel(
 template <int DT>
 __global__ __launch_bounds__(256) void append_kernel(
     const typename Elem<DT>::T* __restrict__ k, const typename Elem<DT>::T* __restrict__ v,
-    int Hkv, int d, int F, int T, int32_t* __restrict__ n_full,
+    int Hkv, int d, int F, int Fp, int T, int32_t* __restrict__ n_full,
     const int32_t* __restrict__ n_full0, int32_t* __restrict__ full_pos,
     typename Elem<DT>::T* __restrict__ kf, typename Elem<DT>::T* __restrict__ vf) {
   const int b = blockIdx.x;
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int h = idx / d;
     const int c = idx - h * d;
     const size_t u = static_cast<size_t>(b) * Hkv + h;
-    kf[(u * F + row) * d + c] = k[(static_cast<size_t>(b) * Hkv + h) * d + c];
-    vf[(u * F + row) * d + c] = v[(static_cast<size_t>(b) * Hkv + h) * d + c];
+    kf[u * Fp * d + k16_off(row, c, d)] = k[u * d + c];
+    vf[u * Fp * d + v32_off(row, c, d)] = v[u * d + c];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -107,7 +109,7 @@ hipError_t summary_impl(const rskv_cache* c, const float* H, const void* K, cons
   dim3 grid(c->S, c->B * c->Hkv);
   hipLaunchKernelGGL(summary_kernel<DT>, grid, dim3(128), 0, st, H,
                      static_cast<const T*>(K), static_cast<const T*>(V), c->dev.span_start,
-                     c->dev.span_len, c->dev.n_spans, c->T, c->d, c->S, c->Hkv,
+                     c->dev.span_len, c->dev.n_spans, c->T, c->d, c->S, c->Sp, c->Hkv,
                      static_cast<T*>(c->dev.summary), static_cast<T*>(c->dev.vmean),
                      c->dev.log_len);
   return hipGetLastError();
@@ -119,7 +121,8 @@ hipError_t pack_impl(const rskv_cache* c, const void* K, const void* V, hipStrea
   dim3 grid(c->F, c->B * c->Hkv);
   hipLaunchKernelGGL(pack_kernel<DT>, grid, dim3(128), 0, st, static_cast<const T*>(K),
                      static_cast<const T*>(V), c->dev.full_pos, c->dev.n_full0, c->T, c->d,
-                     c->F, c->Hkv, static_cast<T*>(c->dev.k_full), static_cast<T*>(c->dev.v_full));
+                     c->F, c->Fp, c->Hkv, static_cast<T*>(c->dev.k_full),
+                     static_cast<T*>(c->dev.v_full));
   return hipGetLastError();
 }
 
@@ -127,7 +130,7 @@ template <int DT>
 hipError_t append_impl(rskv_cache* c, const void* k, const void* v, hipStream_t st) {
   typedef typename Elem<DT>::T T;
   hipLaunchKernelGGL(append_kernel<DT>, dim3(c->B), dim3(256), 0, st, static_cast<const T*>(k),
-                     static_cast<const T*>(v), c->Hkv, c->d, c->F, c->T, c->dev.n_full,
+                     static_cast<const T*>(v), c->Hkv, c->d, c->F, c->Fp, c->T, c->dev.n_full,
                      c->dev.n_full0, c->dev.full_pos, static_cast<T*>(c->dev.k_full),
                      static_cast<T*>(c->dev.v_full));
   return hipGetLastError();

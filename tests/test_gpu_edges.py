@@ -79,14 +79,15 @@ def test_full_rank_expansion_is_dense_attention(dtype):
     rebuilt exactly (up to factor rounding) and decode is dense attention."""
     B, Hkv, G, T, d = 2, 2, 4, 600, 128
     H, K, V, q = _case(B, Hkv, G, T, d, dtype, seed=9)
-    # anchors every 4th to 20th token: every span shorter than the rank
+    # one anchor in every block of 10 tokens (same count in every sequence):
+    # every span is shorter than 20 tokens, so rank 20 rebuilds it exactly
     rng = np.random.default_rng(10)
+    n_a = T // 10
     for b in range(B):
-        pos = np.cumsum(rng.integers(4, 21, T))
-        pos = pos[pos < T]
+        pos = np.arange(n_a) * 10 + rng.integers(0, 10, n_a)
         H[b] = rng.uniform(0.0, 1.0, T)
-        H[b, pos] = 5.0 + rng.uniform(0.0, 1.0, len(pos))
-    p = min(len(np.flatnonzero(H[b] >= 5.0)) for b in range(B)) / T
+        H[b, pos] = 5.0 + rng.uniform(0.0, 1.0, n_a)
+    p = (n_a + 0.5) / T
     cache = _build(H, K, V, dtype, 20, p, G)
     ex = cache.export()
     ns = int(ex["n_spans"].max())
@@ -101,7 +102,12 @@ def test_full_rank_expansion_is_dense_attention(dtype):
     dense = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, enable_gqa=True)[:, :, 0]
     err = float(np.max(np.abs(out - dense.numpy())))
     say(f"[full rank {dtype}] err vs dense {err:.2e}")
-    assert err <= TOL[dtype]
+    # kernel parity on the same stored cache
+    compare_decode(oracle_view(cache.export()), q, out, sels, -math.inf, ns, 8.0, None, dtype,
+                   what="full rank")
+    # the method itself: fp32 factors rebuild the tokens to fp32 rounding;
+    # bf16 factors carry 2^-8 relative rounding into every rebuilt key/value
+    assert err <= (TOL[dtype] if dtype == "f32" else 4e-2)
     cache.close()
 
 
