@@ -147,6 +147,7 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   ALLOC(v.z, U * S, "z");
   ALLOC(v.slogit, z.slogit, "slogit");
   ALLOC(v.sel, U * S, "sel");
+  ALLOC(v.sel_desc, U * S * 4, "sel_desc");
   ALLOC(v.n_sel, U, "n_sel");
   c->nsplit_max = rskv::decode_nsplit_max(c->B, c->Hkv, c->S, c->F, c->k_max_cap);
   ALLOC(v.part, U * c->nsplit_max * c->G * (d + 2), "part");

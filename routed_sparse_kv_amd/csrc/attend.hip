@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
     const int32_t* __restrict__ n_spans, const uint16_t* __restrict__ a_k,
     const uint16_t* __restrict__ a_v, const uint16_t* __restrict__ w_k,
     const uint16_t* __restrict__ w_v, const int32_t* __restrict__ span_len,
-    const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ sel_desc,
     const int32_t* __restrict__ n_sel, int Hkv, int G, int S, int Sp, int Fp, int Np,
     int nsplit, int nsplit_max, float inv_sqrt_d, float* __restrict__ part) {
   constexpr int KK = D / 32;  // 32-column chunks of the QK product
@@ -158,6 +158,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
   const int nSI = (ns + kChunk - 1) / kChunk;
   const int NI = nFI + nsel + nSI;
   const int nwaves = nsplit * 4;
+  // descriptor of this wave's first expanded span, loaded ahead of time
+  // (the items of a wave are F chunks, then expanded spans, then summaries)
+  const int4* desc_u = reinterpret_cast<const int4*>(sel_desc) + static_cast<size_t>(u) * S;
+  int4 dnext = make_int4(0, 0, 0, 0);
+  {
+    const int it0 = s * 4 + wave;
+    const int k = it0 >= nFI ? 0 : (nFI - it0 + nwaves - 1) / nwaves;
+    const int e_it = it0 + k * nwaves;
+    if (e_it >= nFI && e_it < nFI + nsel) dnext = desc_u[e_it - nFI];
+  }
 
   for (int it = s * 4 + wave; it < NI; it += nwaves) {
     if (it < nFI || it >= nFI + nsel) {
@@ -167,16 +177,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
       const int lim = full ? nf : ns;
       bf16x8 va[CB];
       const uint16_t* vt = (full ? vf_u : vm_u) + static_cast<size_t>(r0 / 32) * CB * 512;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) va[cb] = ld8(vt + cb * 512 + lane * 8);
       float x[8];
       if (full) {
+        // issue every load of the item (keys first: they are used first),
+        // then keep the scheduler from interleaving waits with the loads
         bf16x8 ka[2][KK];
         const uint16_t* kt = kf_u + static_cast<size_t>(r0 / 16) * KK * 512;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk) ka[t][kk] = ld8(kt + (t * KK + kk) * 512 + lane * 8);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) va[cb] = ld8(vt + cb * 512 + lane * 8);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -189,11 +202,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
           x[4 + i] = s1[i] * inv_sqrt_d;
         }
       } else {
-        f32x4 l0 = {0.f, 0.f, 0.f, 0.f}, l1 = l0;
-        if (head_ok) {
-          l0 = *reinterpret_cast<const f32x4*>(sl_u + (static_cast<size_t>(r0 / 16) * G + g16) * 16 + 4 * grp);
-          l1 = *reinterpret_cast<const f32x4*>(sl_u + (static_cast<size_t>(r0 / 16 + 1) * G + g16) * 16 + 4 * grp);
-        }
+        const float* lp = sl_u + (static_cast<size_t>(r0 / 16) * G + (head_ok ? g16 : 0)) * 16 + 4 * grp;
+        f32x4 l0 = *reinterpret_cast<const f32x4*>(lp);
+        f32x4 l1 = *reinterpret_cast<const f32x4*>(lp + G * 16);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) va[cb] = ld8(vt + cb * 512 + lane * 8);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x[i] = l0[i];
@@ -217,12 +231,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
       }
     } else {
       // ------------- expanded span: factors of K and V
-      const int j = sel[static_cast<size_t>(u) * S + (it - nFI)];
-      const int len = span_len[static_cast<size_t>(b) * S + j];
-      const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
+      const int4 dcur = dnext;  // {j, |S_j|, padded row offset}
+      if (it + nwaves < nFI + nsel) dnext = desc_u[it + nwaves - nFI];
+      const int j = dcur.x;
+      const int len = dcur.y;
+      const int tp = dcur.z;
       const bool kgrp_ok = grp < R / 4;   // lane group holds ranks 4 grp..4 grp+3
       // Issue the span's loads in the order they are used: W_K, the first
-      // 32 rows of A_K and A_V, then W_V.
+      // 32 rows of A_K and A_V, then W_V.  Loads are unconditional (rows
+      // past the span re-read a valid row and are zeroed) so that the code
+      // stays straight-line and every wait sits after all loads.
       bf16x8 wka[KK];
       {
         const uint16_t* wk = wk_u + static_cast<size_t>(j) * R * D + (g16 < R ? g16 : 0) * D;
@@ -235,16 +253,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
       auto load_a = [&](int t0, bf16x4* ak, bf16x4* av) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          ak[t] = bf16x4{};
-          av[t] = bf16x4{};
-          if (t0 + 16 * t < len) {
-            ak[t] = ld4(ak_u + static_cast<size_t>(tp + t0 + 16 * t + g16) * R +
-                        (kgrp_ok ? 4 * grp : 0));
-            av[t] = ld4(av_u + (static_cast<size_t>((tp + t0 + 16 * t) >> 4) * R +
-                                (g16 < R ? g16 : 0)) * 16 + 4 * grp);
-            if (!kgrp_ok) ak[t] = bf16x4{};
-            if (g16 >= R) av[t] = bf16x4{};
-          }
+          const bool ok = t0 + 16 * t < len;
+          const int r = ok ? t0 + 16 * t : t0;
+          ak[t] = ld4(ak_u + static_cast<size_t>(tp + r + g16) * R + (kgrp_ok ? 4 * grp : 0));
+          av[t] = ld4(av_u + (static_cast<size_t>((tp + r) >> 4) * R + (g16 < R ? g16 : 0)) * 16 +
+                      4 * grp);
+          if (!ok || !kgrp_ok) ak[t] = bf16x4{};
+          if (!ok || g16 >= R) av[t] = bf16x4{};
         }
       };
       bf16x4 ak[2], av[2];
@@ -258,6 +273,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
           if (!kgrp_ok) wva[cb] = bf16x4{};
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       // uk[k][head] = sum_c W_K[k][c] q[head][c]
       f32x4 uk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -268,18 +284,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
         split4(t4, uhi, ulo);
       }
       f32x4 wacc = {0.f, 0.f, 0.f, 0.f};  // w[k = 4 grp + i][head]
-      for (int t0 = 0; t0 < len; t0 += kChunk) {
-        bf16x4 akn[2], avn[2];
-        if (t0 + kChunk < len) load_a(t0 + kChunk, akn, avn);  // prefetch the next rows
-        const bool t1_ok = t0 + 16 < len;
+      // 32 rows of the span: logits A_K (W_K q), softmax, w += A_V^T p
+      auto chunk = [&](int t0, const bf16x4* akc, const bf16x4* avc) {
         f32x4 sv[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          sv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (t == 0 || t1_ok) {
-            sv[t] = mma16(ak[t], uhi, sv[t]);
-            sv[t] = mma16(ak[t], ulo, sv[t]);
-          }
+          sv[t] = mma16(akc[t], uhi, f32x4{0.f, 0.f, 0.f, 0.f});
+          sv[t] = mma16(akc[t], ulo, sv[t]);
         }
         float x[8];
 #pragma unroll
@@ -293,20 +304,27 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
         wacc *= sc;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          if (t == 0 || t1_ok) {
-            bf16x4 phi, plo;
-            split4(x + 4 * t, phi, plo);
-            wacc = mma16(av[t], phi, wacc);
-            wacc = mma16(av[t], plo, wacc);
-          }
+          bf16x4 phi, plo;
+          split4(x + 4 * t, phi, plo);
+          wacc = mma16(avc[t], phi, wacc);
+          wacc = mma16(avc[t], plo, wacc);
         }
-        if (t0 + kChunk < len) {
+      };
+      // rows 32..63 are requested before rows 0..31 are used; every further
+      // chunk keeps one chunk of loads in flight
+      bf16x4 akn[2], avn[2];
+      load_a(len > kChunk ? kChunk : 0, akn, avn);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk(0, ak, av);
+      for (int t0 = kChunk; t0 < len; t0 += kChunk) {
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            ak[t] = akn[t];
-            av[t] = avn[t];
-          }
+        for (int t = 0; t < 2; ++t) {
+          ak[t] = akn[t];
+          av[t] = avn[t];
         }
+        load_a(t0 + kChunk < len ? t0 + kChunk : t0, akn, avn);
+        __builtin_amdgcn_sched_barrier(0);
+        chunk(t0, ak, av);
       }
       // out^T += W_V^T w
       bf16x4 whi, wlo;
@@ -656,7 +674,7 @@ hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, hipS
                      static_cast<const uint16_t*>(c->dev.a_v),
                      static_cast<const uint16_t*>(c->dev.w_k),
                      static_cast<const uint16_t*>(c->dev.w_v), c->dev.span_len, c->dev.tok_pad,
-                     c->dev.sel, c->dev.n_sel, c->Hkv, c->G, c->S, c->Sp, c->Fp, c->Np, nsplit,
+                     c->dev.sel_desc, c->dev.n_sel, c->Hkv, c->G, c->S, c->Sp, c->Fp, c->Np, nsplit,
                      c->nsplit_max, 1.0f / sqrtf(static_cast<float>(D)), c->dev.part);
   return hipGetLastError();
 }

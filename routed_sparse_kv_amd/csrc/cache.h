@@ -43,6 +43,7 @@ struct DeviceArrays {
   double* z = nullptr;            // [U][S] routing scores
   float* slogit = nullptr;        // [U] summary logits incl. ln|S| (slogit_off, Sp spans)
   int32_t* sel = nullptr;         // [U][S] expanded spans, ascending
+  int32_t* sel_desc = nullptr;    // [U][S][4] per expanded span: j, |S_j|, padded offset, 0
   int32_t* n_sel = nullptr;       // [U]
   float* part = nullptr;          // [U][nsplit_max][G][d + 2] partial states
 };

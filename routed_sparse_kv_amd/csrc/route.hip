@@ -209,16 +209,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 // Top-k cap of one unit by a whole 1024-thread workgroup.  Thread t owns the
 // contiguous indices [t*kpt, t*kpt + kpt).
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const double* __restrict__ z_all, const int32_t* __restrict__ n_spans, int Hkv, int G, int S,
-    int Sp, double tau, int k_max, float* __restrict__ slogit, int32_t* __restrict__ sel_ws,
-    int32_t* __restrict__ nsel_ws, int32_t* __restrict__ sel_out,
-    int32_t* __restrict__ nsel_out) {
+    const double* __restrict__ z_all, const int32_t* __restrict__ n_spans,
+    const int32_t* __restrict__ span_len, const int32_t* __restrict__ tok_pad, int Hkv, int G,
+    int S, int Sp, double tau, int k_max, float* __restrict__ slogit,
+    int32_t* __restrict__ sel_ws, int32_t* __restrict__ desc_ws, int32_t* __restrict__ nsel_ws,
+    int32_t* __restrict__ sel_out, int32_t* __restrict__ nsel_out) {
   const int u = blockIdx.x;
   const int b = u / Hkv;
   const int tid = threadIdx.x;
   const int n = n_spans[b];
   const double* z = z_all + static_cast<size_t>(u) * S;
   int32_t* sel = sel_ws + static_cast<size_t>(u) * S;
+  int4* desc = reinterpret_cast<int4*>(desc_ws) + static_cast<size_t>(u) * S;
   float* slogit_u = slogit + static_cast<size_t>(u) * Sp * G;
   const int kpt = (n + kTopkThreads - 1) / kTopkThreads;
   const int i0 = tid * kpt;
@@ -324,6 +326,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       eb += km == P ? 1 : 0;
       if (pick) {
         const int j = i0 + i;
+        desc[pos] = make_int4(j, span_len[static_cast<size_t>(b) * S + j],
+                              tok_pad[static_cast<size_t>(b) * (S + 1) + j], 0);
         sel[pos++] = j;
         for (int g = 0; g < G; ++g) slogit_u[slogit_off(j, g, G)] = -INFINITY;
       }
@@ -363,8 +367,9 @@ hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st) {
 hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int32_t* sel_out,
                        int32_t* nsel_out, hipStream_t st) {
   hipLaunchKernelGGL(topk_kernel, dim3(c->B * c->Hkv), dim3(kTopkThreads), 0, st, c->dev.z,
-                     c->dev.n_spans, c->Hkv, c->G, c->S, c->Sp, static_cast<double>(tau), k_max,
-                     c->dev.slogit, c->dev.sel, c->dev.n_sel, sel_out, nsel_out);
+                     c->dev.n_spans, c->dev.span_len, c->dev.tok_pad, c->Hkv, c->G, c->S, c->Sp,
+                     static_cast<double>(tau), k_max, c->dev.slogit, c->dev.sel,
+                     c->dev.sel_desc, c->dev.n_sel, sel_out, nsel_out);
   return hipGetLastError();
 }
 
