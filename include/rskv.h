@@ -169,9 +169,10 @@ int rskv_cache_import(const rskv_host_arrays* arrays, const rskv_build_opts* opt
  * queued on the cache's last stream.  NULL is accepted. */
 void rskv_cache_destroy(rskv_cache* cache);
 
-/* Per-kernel timing of decode_step with HIP events recorded on the caller's
- * stream around each of its four kernels (routing GEMV, top-k cap,
- * attention partials, merge).  Enabling clears the totals. */
+/* Per-kernel timing of decode_step: each of its four kernels (routing GEMV,
+ * top-k cap, attention partials, merge) is dispatched with a start and a stop
+ * HIP event of its own, so the totals are kernel execution times (the gaps
+ * between launches are not included).  Enabling clears the totals. */
 typedef struct rskv_profile {
   int64_t steps;
   double route_ms, topk_ms, attend_ms, merge_ms; /* summed over steps */

@@ -104,14 +104,14 @@ struct CacheGuard {
 
 // Sizes of the stored arrays, in elements.
 struct Sizes {
-  size_t summary, vmean, full, a, w, slogit;
+  size_t summary, vmean, full, a, w, wv, slogit;
 };
 
 Sizes sizes_of(const rskv_cache* c) {
   const size_t U = static_cast<size_t>(c->B) * c->Hkv;
   const size_t d = c->d, r = c->rank;
   return Sizes{U * c->S * d, U * c->Sp * d, U * c->Fp * d, U * c->Np * r, U * c->S * r * d,
-               U * c->Sp * c->G};
+               U * c->S * rskv::rank4(c->rank) * d, U * c->Sp * c->G};
 }
 
 // Allocates the stored arrays and the decode workspace once the padded
@@ -143,13 +143,14 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   ALLOCB(v.a_k, z.a * es, "a_k");
   ALLOCB(v.a_v, z.a * es, "a_v");
   ALLOCB(v.w_k, z.w * es, "w_k");
-  ALLOCB(v.w_v, z.w * es, "w_v");
+  ALLOCB(v.w_v, z.wv * es, "w_v");
   ALLOC(v.z, U * S, "z");
   ALLOC(v.slogit, z.slogit, "slogit");
   ALLOC(v.sel, U * S, "sel");
   ALLOC(v.sel_desc, U * S * 4, "sel_desc");
   ALLOC(v.n_sel, U, "n_sel");
   c->nsplit_max = rskv::decode_nsplit_max(c->B, c->Hkv, c->S, c->F, c->k_max_cap);
+  ALLOC(v.wstart, U * (4 * c->nsplit_max + 1), "wstart");
   ALLOC(v.part, U * c->nsplit_max * c->G * (d + 2), "part");
 #undef ALLOC
 #undef ALLOCB
@@ -160,7 +161,7 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   RSKV_HIP(hipMemsetAsync(v.a_k, 0, z.a * es, st), "memset a_k");
   RSKV_HIP(hipMemsetAsync(v.a_v, 0, z.a * es, st), "memset a_v");
   RSKV_HIP(hipMemsetAsync(v.w_k, 0, z.w * es, st), "memset w_k");
-  RSKV_HIP(hipMemsetAsync(v.w_v, 0, z.w * es, st), "memset w_v");
+  RSKV_HIP(hipMemsetAsync(v.w_v, 0, z.wv * es, st), "memset w_v");
   RSKV_HIP(hipMemsetAsync(v.log_len, 0, c->B * S * sizeof(float), st), "memset log_len");
   RSKV_HIP(hipMemsetAsync(v.slogit, 0, z.slogit * sizeof(float), st), "memset slogit");
   RSKV_HIP(hipMemsetAsync(v.n_sel, 0, U * sizeof(int32_t), st), "memset n_sel");
@@ -276,7 +277,7 @@ struct Relayout {
       for (int j = 0; j < std::min(S_c, c->S); ++j)
         for (int k = 0; k < r; ++k)
           for (int e = 0; e < d; ++e) {
-            const size_t dv = static_cast<size_t>(u) * c->S * d * r + rskv::wvt_off(j, k, e, d, r);
+            const size_t dv = static_cast<size_t>(u) * c->S * d * rskv::rank4(r) + rskv::wvt_off(j, k, e, d, r);
             E& cv = canon[((static_cast<size_t>(u) * S_c + j) * r + k) * d + e];
             if (dir > 0) cv = dev[dv]; else dev[dv] = cv;
           }
@@ -329,7 +330,7 @@ int export_arrays(const rskv_cache* c, rskv_host_arrays* a) {
     rl.factors_a(static_cast<E*>(a->a_v), N, tmp.data(), true, +1);
   }
   if (a->w_v) {
-    if ((rc = fetch(v.w_v, z.w))) return rc;
+    if ((rc = fetch(v.w_v, z.wv))) return rc;
     rl.factors_wv(static_cast<E*>(a->w_v), S, tmp.data(), +1);
   }
   (void)d;
@@ -378,9 +379,9 @@ int import_arrays(rskv_cache* c, const rskv_host_arrays* a, int S_in, int F_in, 
   tmp.assign(z.a, E(0));
   rl.factors_a(static_cast<E*>(a->a_v), N_in, tmp.data(), true, -1);
   if ((rc = put(v.a_v, z.a, "import a_v"))) return rc;
-  tmp.assign(z.w, E(0));
+  tmp.assign(z.wv, E(0));
   rl.factors_wv(static_cast<E*>(a->w_v), S_in, tmp.data(), -1);
-  if ((rc = put(v.w_v, z.w, "import w_v"))) return rc;
+  if ((rc = put(v.w_v, z.wv, "import w_v"))) return rc;
   return RSKV_OK;
 }
 
@@ -518,31 +519,33 @@ int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, flo
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
     const int nsplit = rskv::decode_nsplit(c, k_max);
-    constexpr int kEv = rskv::kProfileEvents;
-    hipEvent_t ev[kEv] = {};
+    const int nwaves = rskv::attend_uses_mfma(c) ? 4 * nsplit : 0;
+    constexpr int kK = rskv::kProfileKernels;
+    rskv::KernelEvents ev[kK];
     const bool prof = c->prof.on;
     if (prof) {
-      for (int i = 0; i < kEv; ++i) {
-        if (c->prof.pool.empty()) {
-          hipEvent_t e;
-          RSKV_HIP(hipEventCreate(&e), "event create");
-          c->prof.pool.push_back(e);
+      for (int i = 0; i < kK; ++i) {
+        for (hipEvent_t* e : {&ev[i].start, &ev[i].stop}) {
+          if (c->prof.pool.empty()) {
+            hipEvent_t n;
+            RSKV_HIP(hipEventCreate(&n), "event create");
+            c->prof.pool.push_back(n);
+          }
+          *e = c->prof.pool.back();
+          c->prof.pool.pop_back();
         }
-        ev[i] = c->prof.pool.back();
-        c->prof.pool.pop_back();
       }
-      RSKV_HIP(hipEventRecord(ev[0], st), "event record");
     }
-    RSKV_HIP(rskv::launch_route(c, q, st), "route kernel");
-    if (prof) RSKV_HIP(hipEventRecord(ev[1], st), "event record");
-    RSKV_HIP(rskv::launch_topk(c, tau, k_max, sel, n_sel, st), "topk kernel");
-    if (prof) RSKV_HIP(hipEventRecord(ev[2], st), "event record");
-    RSKV_HIP(rskv::launch_attend(c, q, nsplit, st), "attend kernel");
-    if (prof) RSKV_HIP(hipEventRecord(ev[3], st), "event record");
-    RSKV_HIP(rskv::launch_merge(c, nsplit, out, st), "merge kernel");
+    RSKV_HIP(rskv::launch_route(c, q, st, prof ? &ev[0] : nullptr), "route kernel");
+    RSKV_HIP(rskv::launch_topk(c, tau, k_max, nwaves, sel, n_sel, st, prof ? &ev[1] : nullptr),
+             "topk kernel");
+    RSKV_HIP(rskv::launch_attend(c, q, nsplit, st, prof ? &ev[2] : nullptr), "attend kernel");
+    RSKV_HIP(rskv::launch_merge(c, nsplit, out, st, prof ? &ev[3] : nullptr), "merge kernel");
     if (prof) {
-      RSKV_HIP(hipEventRecord(ev[4], st), "event record");
-      for (int i = 0; i < kEv; ++i) c->prof.pending.push_back(ev[i]);
+      for (int i = 0; i < kK; ++i) {
+        c->prof.pending.push_back(ev[i].start);
+        c->prof.pending.push_back(ev[i].stop);
+      }
     }
     return RSKV_OK;
   } catch (const std::bad_alloc&) {
@@ -739,12 +742,13 @@ int rskv_profile_read(rskv_cache* c, rskv_profile* p) {
   if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
   if (p == nullptr) return fail(RSKV_EINVAL, "profile is NULL");
   auto& pr = c->prof;
-  constexpr int kEv = rskv::kProfileEvents;
+  constexpr int kEv = 2 * rskv::kProfileKernels;
   for (size_t i = 0; i + kEv <= pr.pending.size(); i += kEv) {
     RSKV_HIP(hipEventSynchronize(pr.pending[i + kEv - 1]), "event sync");
-    for (int k = 0; k < kEv - 1; ++k) {
+    for (int k = 0; k < rskv::kProfileKernels; ++k) {
       float ms = 0.f;
-      RSKV_HIP(hipEventElapsedTime(&ms, pr.pending[i + k], pr.pending[i + k + 1]), "elapsed");
+      RSKV_HIP(hipEventElapsedTime(&ms, pr.pending[i + 2 * k], pr.pending[i + 2 * k + 1]),
+               "elapsed");
       pr.ms[k] += ms;
     }
     pr.steps += 1;

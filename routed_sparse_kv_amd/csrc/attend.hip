@@ -12,14 +12,15 @@
 // sum_i p_i A_i W_V = (sum_i p_i A_i) W_V,  the same arithmetic up to
 // association, reading every factor exactly once.
 //
-// bf16 caches, r in {8, 16}: attend_mfma_kernel.  Work items of a unit
-// (32-row full-resolution chunks, expanded spans, 32-span summary chunks)
-// are dealt round-robin to the waves of `nsplit` workgroups.  A wave loads a
-// whole item with 16-byte MFMA-operand loads from the tiled layouts of
-// layout.h and keeps its online-softmax state (max, sum, out^T) in the MFMA
-// accumulator layout; all products are 16x16 MFMAs with fp32 accumulation
-// (fp32 intermediates enter as a bf16 hi + lo pair).  The workgroup merges
-// its four waves in LDS and writes one partial.
+// bf16 caches, r in {8, 16}: attend_mfma_kernel.  The work items of a unit
+// (expanded spans, 32-row full-resolution chunks, 32-span summary chunks)
+// are split by the top-k kernel into one contiguous, cost-balanced range
+// per wave.  A wave loads each item with MFMA-operand loads from the tiled
+// layouts of layout.h, one item ahead of the one it computes, and keeps its
+// online-softmax state (max, sum, out^T) in the MFMA accumulator layout; all
+// products are 16x16 MFMAs with fp32 accumulation (fp32 intermediates enter
+// as a bf16 hi + lo pair).  The workgroup merges its four waves in LDS and
+// writes one partial.
 //
 // Other caches (fp32, or other ranks): attend_valu_kernel, a block-
 // cooperative fp32 version of the same computation.
@@ -46,12 +47,26 @@ constexpr int kMaxSplitMfma = 256;   // final merge keeps nsplit*G weights in LD
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ld8b(const uint16_t* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+__device__ __forceinline__ bf16x8 as8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x4 lo4(const u32x4& v) {
+  return __builtin_bit_cast(bf16x4, u32x2{v.x, v.y});
+}
+__device__ __forceinline__ bf16x4 hi4(const u32x4& v) {
+  return __builtin_bit_cast(bf16x4, u32x2{v.z, v.w});
+}
+__device__ __forceinline__ f32x4 asf(const u32x4& v) { return __builtin_bit_cast(f32x4, v); }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
-}
-__device__ __forceinline__ bf16x4 ld4(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x4*>(p);
 }
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -102,22 +117,42 @@ __device__ __forceinline__ float wave_softmax8(float* x, float& m, float& l) {
   return sc;
 }
 
+// Loads per work item and register slots (16 bytes per lane each) of the
+// MFMA kernel; a wave issues all loads of an item before it waits:
+//   full-resolution chunk (32 rows): K as 2 x KK tiles, V as CB tiles;
+//   summary chunk (32 spans): CB mean tiles + 2 logit vectors;
+//   expanded span: KK W_K rows, CB/2 W_V column pairs, and the first 64 rows
+//   of A_K and A_V (4 + 4 eight-byte loads packed two per slot).
+template <int D>
+struct ItemPlan {
+  static constexpr int KK = D / 32;
+  static constexpr int CB = D / 16;
+  static constexpr int kF = 2 * KK + CB;
+  static constexpr int kS = CB + 2;
+  static constexpr int kE = KK + CB / 2 + 8;
+  static constexpr int NL = kF > kS ? (kF > kE ? kF : kE) : (kS > kE ? kS : kE);
+  static constexpr int kEA = KK + CB / 2;  // first A slot of a span item
+};
+
 template <int D, int R>
-__global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kf,
-    const uint16_t* __restrict__ vf, const int32_t* __restrict__ n_full,
-    const uint16_t* __restrict__ vmean, const float* __restrict__ slogit,
-    const int32_t* __restrict__ n_spans, const uint16_t* __restrict__ a_k,
-    const uint16_t* __restrict__ a_v, const uint16_t* __restrict__ w_k,
-    const uint16_t* __restrict__ w_v, const int32_t* __restrict__ span_len,
-    const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ sel_desc,
-    const int32_t* __restrict__ n_sel, int Hkv, int G, int S, int Sp, int Fp, int Np,
-    int nsplit, int nsplit_max, float inv_sqrt_d, float* __restrict__ part) {
-  constexpr int KK = D / 32;  // 32-column chunks of the QK product
-  constexpr int CB = D / 16;  // 16-column blocks of the PV product
+__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kf,
+                   const uint16_t* __restrict__ vf, const int32_t* __restrict__ n_full,
+                   const uint16_t* __restrict__ vmean, const float* __restrict__ slogit,
+                   const int32_t* __restrict__ n_spans, const uint16_t* __restrict__ a_k,
+                   const uint16_t* __restrict__ a_v, const uint16_t* __restrict__ w_k,
+                   const uint16_t* __restrict__ w_v, const int32_t* __restrict__ sel_desc,
+                   const int32_t* __restrict__ n_sel, const int32_t* __restrict__ wstart,
+                   int Hkv, int G, int S, int Sp, int Fp, int Np, int wpitch, int nsplit_max,
+                   float inv_sqrt_d, float* __restrict__ part) {
+  typedef ItemPlan<D> IP;
+  constexpr int KK = IP::KK;
+  constexpr int CB = IP::CB;
+  constexpr int NL = IP::NL;
+  constexpr int R4 = (R + 3) & ~3;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g16 = lane & 15;
   const int grp = lane >> 4;
   const int s = blockIdx.x;
@@ -149,194 +184,236 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(
   const uint16_t* ak_u = a_k + static_cast<size_t>(u) * Np * R;
   const uint16_t* av_u = a_v + static_cast<size_t>(u) * Np * R;
   const uint16_t* wk_u = w_k + static_cast<size_t>(u) * S * R * D;
-  const uint16_t* wv_u = w_v + static_cast<size_t>(u) * S * D * R;
+  const uint16_t* wv_u = w_v + static_cast<size_t>(u) * S * D * R4;
+  const int4* desc_u = reinterpret_cast<const int4*>(sel_desc) + static_cast<size_t>(u) * S;
 
   const int nf = n_full[b];
   const int ns = n_spans[b];
   const int nsel = n_sel[u];
   const int nFI = (nf + kChunk - 1) / kChunk;
-  const int nSI = (ns + kChunk - 1) / kChunk;
-  const int NI = nFI + nsel + nSI;
-  const int nwaves = nsplit * 4;
-  // descriptor of this wave's first expanded span, loaded ahead of time
-  // (the items of a wave are F chunks, then expanded spans, then summaries)
-  const int4* desc_u = reinterpret_cast<const int4*>(sel_desc) + static_cast<size_t>(u) * S;
-  int4 dnext = make_int4(0, 0, 0, 0);
-  {
-    const int it0 = s * 4 + wave;
-    const int k = it0 >= nFI ? 0 : (nFI - it0 + nwaves - 1) / nwaves;
-    const int e_it = it0 + k * nwaves;
-    if (e_it >= nFI && e_it < nFI + nsel) dnext = desc_u[e_it - nFI];
-  }
+  const int* ws = wstart + static_cast<size_t>(u) * wpitch + s * 4 + wave;
+  const int i0 = ws[0];
+  const int i1 = ws[1];
 
-  for (int it = s * 4 + wave; it < NI; it += nwaves) {
-    if (it < nFI || it >= nFI + nsel) {
-      // ------------- 32 full-resolution rows, or 32 span summaries
-      const bool full = it < nFI;
-      const int r0 = (full ? it : it - nFI - nsel) * kChunk;
-      const int lim = full ? nf : ns;
-      bf16x8 va[CB];
-      const uint16_t* vt = (full ? vf_u : vm_u) + static_cast<size_t>(r0 / 32) * CB * 512;
-      float x[8];
-      if (full) {
-        // issue every load of the item (keys first: they are used first),
-        // then keep the scheduler from interleaving waits with the loads
-        bf16x8 ka[2][KK];
-        const uint16_t* kt = kf_u + static_cast<size_t>(r0 / 16) * KK * 512;
+  // lane-constant parts of the span addresses (ranks past R read rank 0 and
+  // are zeroed after the load)
+  const bool krow_ok = g16 < R;        // W_K row / A_V rank held by this lane
+  const bool kgrp_ok = grp < R / 4;    // ranks 4 grp..4 grp+3 exist
+  const int wk_lane = (krow_ok ? g16 : 0) * D + 8 * grp;
+  const int wv_lane = (g16 * (R4 / 4) + (grp < R4 / 4 ? grp : 0)) * 8;
+  const int ak_lane = g16 * R + 4 * (kgrp_ok ? grp : 0);
+  const int av_lane = (krow_ok ? g16 : 0) * 16 + 4 * grp;
+
+  auto issue = [&](int i, const int4& dsc, u32x4 (&buf)[NL]) {
+    if (i < nsel) {
+      const int j = dsc.x;
+      const int len = dsc.y;
+      const int tp = dsc.z;
+      const uint16_t* wk = wk_u + static_cast<size_t>(j) * R * D + wk_lane;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int kk = 0; kk < KK; ++kk) buf[kk] = ld16(wk + 32 * kk);
+      const uint16_t* wv = wv_u + static_cast<size_t>(j) * D * R4 + wv_lane;
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) ka[t][kk] = ld8(kt + (t * KK + kk) * 512 + lane * 8);
+      for (int p = 0; p < CB / 2; ++p) buf[KK + p] = ld16(wv + p * 32 * R4);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) va[cb] = ld8(vt + cb * 512 + lane * 8);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          s0 = mma32(ka[0][kk], qb[kk], s0);
-          s1 = mma32(ka[1][kk], qb[kk], s1);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = s0[i] * inv_sqrt_d;
-          x[4 + i] = s1[i] * inv_sqrt_d;
-        }
-      } else {
-        const float* lp = sl_u + (static_cast<size_t>(r0 / 16) * G + (head_ok ? g16 : 0)) * 16 + 4 * grp;
-        f32x4 l0 = *reinterpret_cast<const f32x4*>(lp);
-        f32x4 l1 = *reinterpret_cast<const f32x4*>(lp + G * 16);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) va[cb] = ld8(vt + cb * 512 + lane * 8);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = l0[i];
-          x[4 + i] = l1[i];
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t < len ? 16 * t : 0;
+        const u32x2 k2 = ld8b(ak_u + static_cast<size_t>(tp + r) * R + ak_lane);
+        const u32x2 v2 = ld8b(av_u + static_cast<size_t>((tp + r) >> 4) * R * 16 + av_lane);
+        u32x4& ks = buf[IP::kEA + t / 2];
+        u32x4& vs = buf[IP::kEA + 2 + t / 2];
+        if (t & 1) {
+          ks.z = k2.x;
+          ks.w = k2.y;
+          vs.z = v2.x;
+          vs.w = v2.y;
+        } else {
+          ks.x = k2.x;
+          ks.y = k2.y;
+          vs.x = v2.x;
+          vs.y = v2.y;
         }
       }
+    } else if (i < nsel + nFI) {
+      const int r0 = (i - nsel) * kChunk;
+      const uint16_t* kt = kf_u + static_cast<size_t>(r0 >> 4) * KK * 512 + lane * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = r0 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4));
-        if (!head_ok || row >= lim) x[e] = -INFINITY;
-      }
-      const float sc = wave_softmax8(x, m, l);
+      for (int t = 0; t < 2 * KK; ++t) buf[t] = ld16(kt + t * 512);
+      const uint16_t* vt = vf_u + static_cast<size_t>(r0 >> 5) * CB * 512 + lane * 8;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) acc[cb] *= sc;
-      bf16x8 phi, plo;
-      split8(x, phi, plo);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        acc[cb] = mma32(va[cb], phi, acc[cb]);
-        acc[cb] = mma32(va[cb], plo, acc[cb]);
-      }
+      for (int cb = 0; cb < CB; ++cb) buf[2 * KK + cb] = ld16(vt + cb * 512);
     } else {
-      // ------------- expanded span: factors of K and V
-      const int4 dcur = dnext;  // {j, |S_j|, padded row offset}
-      if (it + nwaves < nFI + nsel) dnext = desc_u[it + nwaves - nFI];
-      const int j = dcur.x;
-      const int len = dcur.y;
-      const int tp = dcur.z;
-      const bool kgrp_ok = grp < R / 4;   // lane group holds ranks 4 grp..4 grp+3
-      // Issue the span's loads in the order they are used: W_K, the first
-      // 32 rows of A_K and A_V, then W_V.  Loads are unconditional (rows
-      // past the span re-read a valid row and are zeroed) so that the code
-      // stays straight-line and every wait sits after all loads.
-      bf16x8 wka[KK];
-      {
-        const uint16_t* wk = wk_u + static_cast<size_t>(j) * R * D + (g16 < R ? g16 : 0) * D;
+      const int r0 = (i - nsel - nFI) * kChunk;
+      const uint16_t* vt = vm_u + static_cast<size_t>(r0 >> 5) * CB * 512 + lane * 8;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          wka[kk] = ld8(wk + 32 * kk + 8 * grp);
-          if (g16 >= R) wka[kk] = bf16x8{};
-        }
+      for (int cb = 0; cb < CB; ++cb) buf[cb] = ld16(vt + cb * 512);
+      const float* lp = sl_u + (static_cast<size_t>(r0 >> 4) * G + (head_ok ? g16 : 0)) * 16 + 4 * grp;
+      buf[CB] = *reinterpret_cast<const u32x4*>(lp);
+      buf[CB + 1] = *reinterpret_cast<const u32x4*>(lp + G * 16);
+    }
+  };
+
+  // softmax over 8 logits per lane, then acc += V^T p with V the A operand
+  auto attend8 = [&](float* x, int r0, int lim, const u32x4* vbuf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = r0 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4));
+      if (!head_ok || row >= lim) x[e] = -INFINITY;
+    }
+    const float sc = wave_softmax8(x, m, l);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] *= sc;
+    bf16x8 phi, plo;
+    split8(x, phi, plo);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      acc[cb] = mma32(as8(vbuf[cb]), phi, acc[cb]);
+      acc[cb] = mma32(as8(vbuf[cb]), plo, acc[cb]);
+    }
+  };
+
+  auto compute = [&](int i, const int4& dsc, const u32x4 (&buf)[NL]) {
+    if (i < nsel) {
+      // ---- expanded span: logits A_K (W_K q), softmax, w += A_V^T p,
+      // then out^T += W_V^T w
+      const int j = dsc.x;
+      const int len = dsc.y;
+      const int tp = dsc.z;
+      (void)j;
+      f32x4 uk = {0.f, 0.f, 0.f, 0.f};  // uk[k = 4 grp + i][head]
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        bf16x8 w8 = as8(buf[kk]);
+        if (!krow_ok) w8 = bf16x8{};
+        uk = mma32(w8, qb[kk], uk);
       }
-      auto load_a = [&](int t0, bf16x4* ak, bf16x4* av) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bool ok = t0 + 16 * t < len;
-          const int r = ok ? t0 + 16 * t : t0;
-          ak[t] = ld4(ak_u + static_cast<size_t>(tp + r + g16) * R + (kgrp_ok ? 4 * grp : 0));
-          av[t] = ld4(av_u + (static_cast<size_t>((tp + r) >> 4) * R + (g16 < R ? g16 : 0)) * 16 +
-                      4 * grp);
-          if (!ok || !kgrp_ok) ak[t] = bf16x4{};
-          if (!ok || g16 >= R) av[t] = bf16x4{};
-        }
-      };
-      bf16x4 ak[2], av[2];
-      load_a(0, ak, av);
-      bf16x4 wva[CB];
-      {
-        const uint16_t* wv = wv_u + static_cast<size_t>(j) * D * R;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          wva[cb] = ld4(wv + static_cast<size_t>(16 * cb + g16) * R + (kgrp_ok ? 4 * grp : 0));
-          if (!kgrp_ok) wva[cb] = bf16x4{};
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // uk[k][head] = sum_c W_K[k][c] q[head][c]
-      f32x4 uk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) uk = mma32(wka[kk], qb[kk], uk);
       bf16x4 uhi, ulo;
       {
         float t4[4] = {uk[0], uk[1], uk[2], uk[3]};
         split4(t4, uhi, ulo);
       }
       f32x4 wacc = {0.f, 0.f, 0.f, 0.f};  // w[k = 4 grp + i][head]
-      // 32 rows of the span: logits A_K (W_K q), softmax, w += A_V^T p
-      auto chunk = [&](int t0, const bf16x4* akc, const bf16x4* avc) {
-        f32x4 sv[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          sv[t] = mma16(akc[t], uhi, f32x4{0.f, 0.f, 0.f, 0.f});
-          sv[t] = mma16(akc[t], ulo, sv[t]);
-        }
+      auto chunk = [&](int t0, bf16x4 ak0, bf16x4 ak1, bf16x4 av0, bf16x4 av1) {
+        f32x4 sv0 = mma16(ak0, uhi, f32x4{0.f, 0.f, 0.f, 0.f});
+        sv0 = mma16(ak0, ulo, sv0);
+        f32x4 sv1 = mma16(ak1, uhi, f32x4{0.f, 0.f, 0.f, 0.f});
+        sv1 = mma16(ak1, ulo, sv1);
         float x[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = (head_ok && t0 + 4 * grp + i < len) ? sv[0][i] * inv_sqrt_d : -INFINITY;
-          x[4 + i] = (head_ok && t0 + 16 + 4 * grp + i < len) ? sv[1][i] * inv_sqrt_d : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          x[e] = (head_ok && t0 + 4 * grp + e < len) ? sv0[e] * inv_sqrt_d : -INFINITY;
+          x[4 + e] = (head_ok && t0 + 16 + 4 * grp + e < len) ? sv1[e] * inv_sqrt_d : -INFINITY;
         }
         const float sc = wave_softmax8(x, m, l);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[cb] *= sc;
         wacc *= sc;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x4 phi, plo;
-          split4(x + 4 * t, phi, plo);
-          wacc = mma16(avc[t], phi, wacc);
-          wacc = mma16(avc[t], plo, wacc);
-        }
+        bf16x4 phi, plo;
+        split4(x, phi, plo);
+        wacc = mma16(av0, phi, wacc);
+        wacc = mma16(av0, plo, wacc);
+        split4(x + 4, phi, plo);
+        wacc = mma16(av1, phi, wacc);
+        wacc = mma16(av1, plo, wacc);
       };
-      // rows 32..63 are requested before rows 0..31 are used; every further
-      // chunk keeps one chunk of loads in flight
-      bf16x4 akn[2], avn[2];
-      load_a(len > kChunk ? kChunk : 0, akn, avn);
-      __builtin_amdgcn_sched_barrier(0);
-      chunk(0, ak, av);
-      for (int t0 = kChunk; t0 < len; t0 += kChunk) {
+      auto tile_k = [&](const u32x4& v, int half, int t) {
+        bf16x4 r = half ? hi4(v) : lo4(v);
+        if (!kgrp_ok || 16 * t >= len) r = bf16x4{};
+        return r;
+      };
+      auto tile_v = [&](const u32x4& v, int half, int t) {
+        bf16x4 r = half ? hi4(v) : lo4(v);
+        if (!krow_ok || 16 * t >= len) r = bf16x4{};
+        return r;
+      };
+      chunk(0, tile_k(buf[IP::kEA], 0, 0), tile_k(buf[IP::kEA], 1, 1),
+            tile_v(buf[IP::kEA + 2], 0, 0), tile_v(buf[IP::kEA + 2], 1, 1));
+      if (len > 32)
+        chunk(32, tile_k(buf[IP::kEA + 1], 0, 2), tile_k(buf[IP::kEA + 1], 1, 3),
+              tile_v(buf[IP::kEA + 3], 0, 2), tile_v(buf[IP::kEA + 3], 1, 3));
+      if (len > 64) {
+        // rows past 64: 32 at a time, one group of loads kept in flight
+        auto load_a = [&](int t0, bf16x4* ak, bf16x4* av) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          ak[t] = akn[t];
-          av[t] = avn[t];
+          for (int t = 0; t < 2; ++t) {
+            const bool ok = t0 + 16 * t < len;
+            const int r = ok ? t0 + 16 * t : t0;
+            ak[t] = __builtin_bit_cast(bf16x4, ld8b(ak_u + static_cast<size_t>(tp + r) * R + ak_lane));
+            av[t] = __builtin_bit_cast(bf16x4, ld8b(av_u + static_cast<size_t>((tp + r) >> 4) * R * 16 + av_lane));
+            if (!ok || !kgrp_ok) ak[t] = bf16x4{};
+            if (!ok || !krow_ok) av[t] = bf16x4{};
+          }
+        };
+        bf16x4 akc[2], avc[2], akn[2], avn[2];
+        load_a(64, akc, avc);
+        for (int t0 = 64; t0 < len; t0 += kChunk) {
+          load_a(t0 + kChunk < len ? t0 + kChunk : t0, akn, avn);
+          chunk(t0, akc[0], akc[1], avc[0], avc[1]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            akc[t] = akn[t];
+            avc[t] = avn[t];
+          }
         }
-        load_a(t0 + kChunk < len ? t0 + kChunk : t0, akn, avn);
-        __builtin_amdgcn_sched_barrier(0);
-        chunk(t0, ak, av);
       }
-      // out^T += W_V^T w
       bf16x4 whi, wlo;
       {
         float t4[4] = {wacc[0], wacc[1], wacc[2], wacc[3]};
         split4(t4, whi, wlo);
       }
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        acc[cb] = mma16(wva[cb], whi, acc[cb]);
-        acc[cb] = mma16(wva[cb], wlo, acc[cb]);
+      for (int p = 0; p < CB / 2; ++p) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x4 wv4 = hh ? hi4(buf[KK + p]) : lo4(buf[KK + p]);
+          if (!kgrp_ok) wv4 = bf16x4{};
+          acc[2 * p + hh] = mma16(wv4, whi, acc[2 * p + hh]);
+          acc[2 * p + hh] = mma16(wv4, wlo, acc[2 * p + hh]);
+        }
       }
+    } else if (i < nsel + nFI) {
+      // ---- 32 full-resolution rows
+      const int r0 = (i - nsel) * kChunk;
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s0 = mma32(as8(buf[kk]), qb[kk], s0);
+        s1 = mma32(as8(buf[KK + kk]), qb[kk], s1);
+      }
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = s0[e] * inv_sqrt_d;
+        x[4 + e] = s1[e] * inv_sqrt_d;
+      }
+      attend8(x, r0, nf, buf + 2 * KK);
+    } else {
+      // ---- 32 summary entries
+      const int r0 = (i - nsel - nFI) * kChunk;
+      const f32x4 l0 = asf(buf[CB]);
+      const f32x4 l1 = asf(buf[CB + 1]);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = l0[e];
+        x[4 + e] = l1[e];
+      }
+      attend8(x, r0, ns, buf);
+    }
+  };
+
+  // Item loop: all loads of an item are issued before any of them is
+  // waited for; the next span descriptor is fetched (scalar) meanwhile.
+  if (i0 < i1) {
+    auto desc_at = [&](int i) { return i < nsel ? desc_u[i] : make_int4(0, 0, 0, 0); };
+    int4 dn = desc_at(i0);
+    for (int i = i0; i < i1; ++i) {
+      const int4 dc = dn;
+      dn = desc_at(min(i + 1, i1 - 1));
+      u32x4 buf[NL];
+      issue(i, dc, buf);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i, dc, buf);
     }
   }
 
@@ -513,7 +590,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_valu_kernel(
       const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
       const size_t abase = static_cast<size_t>(u) * Np * rank;
       const size_t wkbase = (static_cast<size_t>(u) * S + j) * rank * d;
-      const size_t wvbase = static_cast<size_t>(u) * S * d * rank;
+      const size_t wvbase = static_cast<size_t>(u) * S * d * rank4(rank);
       for (int pi = tid; pi < G * rank; pi += kAttThreads) {
         const int g = pi / rank;
         const int k = pi - g * rank;
@@ -664,45 +741,48 @@ bool use_mfma(const rskv_cache* c) {
 }
 
 template <int D, int R>
-hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st) {
+hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
+                            const KernelEvents* ev) {
   dim3 grid(nsplit, c->B * c->Hkv);
-  hipLaunchKernelGGL((attend_mfma_kernel<D, R>), grid, dim3(kAttThreads), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c->dev.k_full),
-                     static_cast<const uint16_t*>(c->dev.v_full), c->dev.n_full,
-                     static_cast<const uint16_t*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
-                     static_cast<const uint16_t*>(c->dev.a_k),
-                     static_cast<const uint16_t*>(c->dev.a_v),
-                     static_cast<const uint16_t*>(c->dev.w_k),
-                     static_cast<const uint16_t*>(c->dev.w_v), c->dev.span_len, c->dev.tok_pad,
-                     c->dev.sel_desc, c->dev.n_sel, c->Hkv, c->G, c->S, c->Sp, c->Fp, c->Np, nsplit,
-                     c->nsplit_max, 1.0f / sqrtf(static_cast<float>(D)), c->dev.part);
-  return hipGetLastError();
+  return launch(attend_mfma_kernel<D, R>, grid, dim3(kAttThreads), 0, st, ev,
+                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c->dev.k_full),
+                static_cast<const uint16_t*>(c->dev.v_full), c->dev.n_full,
+                static_cast<const uint16_t*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
+                static_cast<const uint16_t*>(c->dev.a_k), static_cast<const uint16_t*>(c->dev.a_v),
+                static_cast<const uint16_t*>(c->dev.w_k), static_cast<const uint16_t*>(c->dev.w_v),
+                c->dev.sel_desc, c->dev.n_sel, c->dev.wstart, c->Hkv, c->G, c->S, c->Sp, c->Fp,
+                c->Np, 4 * c->nsplit_max + 1, c->nsplit_max, 1.0f / sqrtf(static_cast<float>(D)),
+                c->dev.part);
 }
 
 template <int DT>
-hipError_t attend_valu_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st) {
+hipError_t attend_valu_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
+                            const KernelEvents* ev) {
   typedef typename Elem<DT>::T T;
   dim3 grid(nsplit, c->B * c->Hkv);
-  hipLaunchKernelGGL(attend_valu_kernel<DT>, grid, dim3(kAttThreads), 0, st,
-                     static_cast<const T*>(q), static_cast<const T*>(c->dev.k_full),
-                     static_cast<const T*>(c->dev.v_full), c->dev.n_full,
-                     static_cast<const T*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
-                     static_cast<const T*>(c->dev.a_k), static_cast<const T*>(c->dev.a_v),
-                     static_cast<const T*>(c->dev.w_k), static_cast<const T*>(c->dev.w_v),
-                     c->dev.span_len, c->dev.tok_pad, c->dev.sel, c->dev.n_sel, c->Hkv, c->G,
-                     c->d, c->S, c->Sp, c->Fp, c->Np, c->rank, nsplit, c->nsplit_max,
-                     1.0f / sqrtf(static_cast<float>(c->d)), c->dev.part);
-  return hipGetLastError();
+  return launch(attend_valu_kernel<DT>, grid, dim3(kAttThreads), 0, st, ev,
+                static_cast<const T*>(q), static_cast<const T*>(c->dev.k_full),
+                static_cast<const T*>(c->dev.v_full), c->dev.n_full,
+                static_cast<const T*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
+                static_cast<const T*>(c->dev.a_k), static_cast<const T*>(c->dev.a_v),
+                static_cast<const T*>(c->dev.w_k), static_cast<const T*>(c->dev.w_v),
+                c->dev.span_len, c->dev.tok_pad, c->dev.sel, c->dev.n_sel, c->Hkv, c->G, c->d,
+                c->S, c->Sp, c->Fp, c->Np, c->rank, nsplit, c->nsplit_max,
+                1.0f / sqrtf(static_cast<float>(c->d)), c->dev.part);
 }
 
 }  // namespace
 
-// Split count: about `target` workgroups over all units, at least one item
-// per wave (MFMA path) or per workgroup (VALU path).
+bool attend_uses_mfma(const rskv_cache* c) { return use_mfma(c); }
+
+// Workgroups per unit.  MFMA path: about two resident workgroups per CU
+// (512 over all units; each wave then works through a long item range with
+// its loads pipelined), at most one wave per item.  VALU path: about 2048
+// workgroups, at most one per item.
 static int nsplit_for(int B, int Hkv, int S, int F, int k_slots, bool mfma) {
   const int U = B * Hkv;
   const int NI = (F + kChunk - 1) / kChunk + k_slots + (S + kChunk - 1) / kChunk;
-  const int target = mfma ? 1024 : 2048;
+  const int target = mfma ? 512 : 2048;
   int ns = (target + U - 1) / U;
   const int per_block = mfma ? 4 : 1;
   if (ns > (NI + per_block - 1) / per_block) ns = (NI + per_block - 1) / per_block;
@@ -732,22 +812,23 @@ int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap) {
   return m > o ? m : o;
 }
 
-hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st) {
+hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
+                         const KernelEvents* ev) {
   if (use_mfma(c)) {
     if (c->d == 128)
-      return c->rank == 16 ? attend_mfma_impl<128, 16>(c, q, nsplit, st)
-                           : attend_mfma_impl<128, 8>(c, q, nsplit, st);
-    return c->rank == 16 ? attend_mfma_impl<64, 16>(c, q, nsplit, st)
-                         : attend_mfma_impl<64, 8>(c, q, nsplit, st);
+      return c->rank == 16 ? attend_mfma_impl<128, 16>(c, q, nsplit, st, ev)
+                           : attend_mfma_impl<128, 8>(c, q, nsplit, st, ev);
+    return c->rank == 16 ? attend_mfma_impl<64, 16>(c, q, nsplit, st, ev)
+                         : attend_mfma_impl<64, 8>(c, q, nsplit, st, ev);
   }
-  return c->dtype == kBF16 ? attend_valu_impl<kBF16>(c, q, nsplit, st)
-                           : attend_valu_impl<kF32>(c, q, nsplit, st);
+  return c->dtype == kBF16 ? attend_valu_impl<kBF16>(c, q, nsplit, st, ev)
+                           : attend_valu_impl<kF32>(c, q, nsplit, st, ev);
 }
 
-hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(merge_kernel, dim3(c->B * c->Hkv, c->G), dim3(128), 0, st, c->dev.part,
-                     nsplit, c->nsplit_max, c->Hkv, c->G, c->d, out);
-  return hipGetLastError();
+hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st,
+                        const KernelEvents* ev) {
+  return launch(merge_kernel, dim3(c->B * c->Hkv, c->G), dim3(128), 0, st, ev, c->dev.part,
+                nsplit, c->nsplit_max, c->Hkv, c->G, c->d, out);
 }
 
 }  // namespace rskv

@@ -1,6 +1,7 @@
 // Host-side cache object and kernel launchers of librskv.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,21 +44,53 @@ struct DeviceArrays {
   double* z = nullptr;            // [U][S] routing scores
   float* slogit = nullptr;        // [U] summary logits incl. ln|S| (slogit_off, Sp spans)
   int32_t* sel = nullptr;         // [U][S] expanded spans, ascending
-  int32_t* sel_desc = nullptr;    // [U][S][4] per expanded span: j, |S_j|, padded offset, 0
+  int32_t* sel_desc = nullptr;    // [U][S][4] per expanded span: j, |S_j|, padded offset,
+                                  // exclusive work-cost prefix
   int32_t* n_sel = nullptr;       // [U]
+  int32_t* wstart = nullptr;      // [U][4 nsplit_max + 1] first work item of each wave
   float* part = nullptr;          // [U][nsplit_max][G][d + 2] partial states
 };
 
-// Events recorded per profiled decode step: before route, top-k, attend,
-// merge and after merge.
-constexpr int kProfileEvents = 5;
+// Decode kernels timed per profiled step (route, top-k, attend, merge); each
+// has a start and a stop event carried by its own dispatch.
+constexpr int kProfileKernels = 4;
 
 struct Profile {
   bool on = false;
   int64_t steps = 0;
-  double ms[kProfileEvents - 1] = {0, 0, 0, 0};
-  std::vector<hipEvent_t> pending;  // kProfileEvents per recorded step
+  double ms[kProfileKernels] = {0, 0, 0, 0};
+  std::vector<hipEvent_t> pending;  // 2 * kProfileKernels per recorded step
   std::vector<hipEvent_t> pool;
+};
+
+// Start/stop events of one kernel dispatch (timestamps of the kernel itself).
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launches `kernel`; with `ev`, the dispatch records ev->start and ev->stop.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                  const KernelEvents* ev, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev ? ev->start : nullptr,
+                        ev ? ev->stop : nullptr, 0u, args...);
+  return hipGetLastError();
+}
+
+// Integer work cost (64-byte units) of the attention kernel's items, used by
+// the top-k kernel to give each wave a contiguous, balanced item range.
+struct WorkCost {
+  int span_base;   // an expanded span: factor matrices W_K, W_V + overhead
+  int span_row;    // bytes of A_K and A_V per padded row
+  int span_extra;  // each further 32 rows past the first 64 (a load round)
+  int full;        // 32 full-resolution rows
+  int summ;        // 32 summary entries
+  __host__ __device__ long long span(int len) const {
+    const long long pad = (len + 15) & ~15;
+    const long long extra = len > 64 ? (len - 64 + 31) / 32 : 0;
+    return span_base + pad * span_row / 64 + extra * span_extra;
+  }
 };
 
 }  // namespace rskv
@@ -110,14 +143,20 @@ hipError_t launch_factor(rskv_cache* c, const void* K, const void* V, hipStream_
                          std::string* err);
 
 // Decode, four launches in stream order: routing GEMV (z, summary logits),
-// top-k cap, attention partials, merge of the partials into `out`.
-hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st);
-hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int32_t* sel_out,
-                       int32_t* nsel_out, hipStream_t st);
+// top-k cap (and the attention work partition when `nwaves` > 0),
+// attention partials, merge of the partials into `out`.  `ev` (may be
+// null) receives the kernel's own start and stop times.
+hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st,
+                        const KernelEvents* ev);
+hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int nwaves, int32_t* sel_out,
+                       int32_t* nsel_out, hipStream_t st, const KernelEvents* ev);
 int decode_nsplit(const rskv_cache* c, int k_max);
 int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap);
-hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st);
-hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st);
+bool attend_uses_mfma(const rskv_cache* c);
+hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
+                         const KernelEvents* ev);
+hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st,
+                        const KernelEvents* ev);
 
 hipError_t launch_append(rskv_cache* c, const void* k, const void* v, hipStream_t st);
 

@@ -83,38 +83,65 @@ __device__ __forceinline__ T group_sum(T v, int width) {
 }
 
 // Inclusive prefix sum over a wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
+    const T t = __shfl_up(v, o, kWave);
     if (lane >= o) v += t;
   }
   return v;
 }
 
 // Exclusive prefix sum over the whole block (blockDim.x a multiple of 64,
-// at most 1024).  `scratch` holds >= 17 ints of shared memory.  Returns the
-// exclusive prefix of v and the block total in *total.  Contains barriers:
-// every thread of the block must call it.
-__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
+// at most 1024).  `scratch` holds >= 17 values of shared memory.  Returns
+// the exclusive prefix of v and the block total in *total.  Contains
+// barriers: every thread of the block must call it.
+template <typename T>
+__device__ __forceinline__ T block_excl_scan(T v, T* scratch, T* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int nw = blockDim.x / kWave;
-  const int incl = wave_incl_scan(v);
+  const T incl = wave_incl_scan(v);
   if (lane == kWave - 1) scratch[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    int w = lane < nw ? scratch[lane] : 0;
-    int ws = wave_incl_scan(w);
+    const T w = lane < nw ? scratch[lane] : T(0);
+    const T ws = wave_incl_scan(w);
     if (lane < nw) scratch[lane] = ws - w;
     if (lane == nw - 1) scratch[16] = ws;
   }
   __syncthreads();
-  const int r = scratch[wid] + incl - v;
+  const T r = scratch[wid] + incl - v;
   *total = scratch[16];
   __syncthreads();
   return r;
+}
+
+// Block-wide minimum and maximum (same calling rules as block_excl_scan;
+// `scratch` holds >= 32 doubles of shared memory).
+__device__ __forceinline__ void block_min_max(double& mn, double& mx, double* scratch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    mn = fmin(mn, __shfl_xor(mn, o, kWave));
+    mx = fmax(mx, __shfl_xor(mx, o, kWave));
+  }
+  if (lane == 0) {
+    scratch[wid] = mn;
+    scratch[16 + wid] = mx;
+  }
+  __syncthreads();
+  mn = scratch[0];
+  mx = scratch[16];
+  for (int w = 1; w < nw; ++w) {
+    mn = fmin(mn, scratch[w]);
+    mx = fmax(mx, scratch[16 + w]);
+  }
+  __syncthreads();
 }
 
 }  // namespace rskv

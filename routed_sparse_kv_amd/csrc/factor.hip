@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kFacThreads) void factor_kernel(
       return a_k[(static_cast<size_t>(u) * Np + tp + t) * rank + k];
     };
     auto w_at = [&](int k, int e) -> ST& {
-      if (kv) return w_v[static_cast<size_t>(u) * S * d * rank + wvt_off(j, k, e, d, rank)];
+      if (kv) return w_v[static_cast<size_t>(u) * S * d * rank4(rank) + wvt_off(j, k, e, d, rank)];
       return w_k[((static_cast<size_t>(u) * S + j) * rank + k) * d + e];
     };
     if (by_rows) {

@@ -57,11 +57,19 @@ RSKV_HD size_t avt_off(int t, int k, int r) {
   return (static_cast<size_t>(t >> 4) * r + k) * 16 + (t & 15);
 }
 
-// W_K is row-major [span][r][d] (row k = k-th right singular vector).  W_V
-// is stored transposed, [span][d][r], so lane (c = l % 16, group g) reads
-// components 4 g..4 g+3 of column c.
+// W_K is row-major [span][r][d] (row k = k-th right singular vector).
+//
+// W_V feeds the transposed PV product out^T += W_V^T w, whose A operand for
+// the 16-column block cb is lane (c = l % 16, group g) -> W_V[4 g..4 g+3][c].
+// Blocks are stored in pairs so that one 16-byte load per lane serves two
+// of them: per span, per 32-column pair, lane (c, g) finds the four ranks
+// of column c of the first block followed by those of the second.  Ranks
+// are padded to a multiple of 4 (rank4), with zeros.
+RSKV_HD int rank4(int r) { return (r + 3) & ~3; }
 RSKV_HD size_t wvt_off(int j, int k, int c, int d, int r) {
-  return (static_cast<size_t>(j) * d + c) * r + k;
+  const int r4 = rank4(r);
+  return static_cast<size_t>(j) * d * r4 + static_cast<size_t>(c >> 5) * 32 * r4 +
+         static_cast<size_t>((c & 15) * (r4 >> 2) + (k >> 2)) * 8 + ((c >> 4) & 1) * 4 + (k & 3);
 }
 
 RSKV_HD int round_up(int x, int m) { return (x + m - 1) / m * m; }

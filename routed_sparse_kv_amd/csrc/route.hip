@@ -18,15 +18,13 @@
 // elements of one span row per lane, so z needs 32 fp64 FMAs per lane and a
 // two-step reduction over the four lane groups.  fp32 caches use a VALU
 // version (16 lanes per span row).
-// topk_kernel (next launch, one workgroup per unit): keys are order-
-// preserving uint64 images of z, staged in LDS when they fit; an 8-bit-digit
-// radix select from the top stops as soon as the bucket holding the k-th
-// largest key is taken whole, and a block scan writes the selected indices
-// in ascending order.  It also overwrites the summary logits of the
-// selected spans with -inf, so that attention skips their summary entries.
-// (Handing z from one workgroup to another inside one kernel would need a
-// device-scope release per workgroup, which on gfx950 writes back the XCD's
-// L2 and serialises; the kernel boundary is cheaper.)
+// topk_kernel (next launch, one workgroup per unit): exact selection by a
+// narrowing fp64 histogram search for the k-th entry, compaction in index
+// order, -inf over the summary logits of the selected spans (attention then
+// skips their summary entries), and the per-wave work partition of the
+// attention kernel.  (Handing z from one workgroup to another inside one
+// kernel would need a device-scope release per workgroup, which on gfx950
+// writes back the XCD's L2 and serialises; the kernel boundary is cheaper.)
 #include "cache.h"
 #include "common.h"
 
@@ -38,7 +36,10 @@ constexpr int kRouteThreads = 256;               // 4 waves
 constexpr int kTilesPerWave = 2;                 // 16 spans per tile
 constexpr int kSpansPerBlock = 4 * kTilesPerWave * 16;
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkLds = 6144;                   // keys staged in LDS (48 KB)
+constexpr int kTopkLds = 6144;                   // values staged in LDS (48 KB)
+constexpr int kTopkBins = kTopkThreads;          // histogram bins of the threshold search
+constexpr int kItemOverhead = 16;                // work-item fixed cost (64-byte units)
+constexpr int kSpanRoundTrip = 64;               // per extra 32-row load round of a span
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -206,14 +207,35 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
 }
 
-// Top-k cap of one unit by a whole 1024-thread workgroup.  Thread t owns the
-// contiguous indices [t*kpt, t*kpt + kpt).
+// Top-k cap of one unit by a whole 1024-thread workgroup, then the
+// compaction of the selection and the work partition of the attention pass.
+//
+// Selection.  The kept set is the first k entries of the order (z
+// descending, index ascending) restricted to z > tau, so it is fixed by its
+// last entry (z*, j*): pick j iff z_j > tau and (z_j > z* or (z_j == z* and
+// j <= j*)).  z* is found by narrowing a value interval [lo, hi] that holds
+// it: a 1024-bin histogram of the values in the interval, bin
+// floor((z - lo) / (hi - lo) * 1024) (monotone in z under fp64 rounding),
+// locates the bin holding the k-th largest, whose own value range becomes
+// the next interval.  Each round shrinks the interval about 1024-fold, so
+// smooth data needs two or three rounds; once lo == hi, j* is the rem-th
+// lowest index among the values equal to lo.
+//
+// Partition.  The attention kernel's work items of a unit, in order, are
+// the expanded spans (ascending index), 32-row full-resolution chunks and
+// 32-span summary chunks.  Each item has an integer cost (bytes / 64 plus
+// a fixed overhead, plus a round-trip penalty per 32 rows of a span past
+// the 64 its first load covers); item i goes to wave
+// floor((2 P_i + c_i) W / (2 C)) (P_i the exclusive cost prefix, C the
+// total), so every wave receives a contiguous item range of about C / W.
+// wstart[u][w] is the first item of wave w, wstart[u][W] the item count.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const double* __restrict__ z_all, const int32_t* __restrict__ n_spans,
-    const int32_t* __restrict__ span_len, const int32_t* __restrict__ tok_pad, int Hkv, int G,
-    int S, int Sp, double tau, int k_max, float* __restrict__ slogit,
-    int32_t* __restrict__ sel_ws, int32_t* __restrict__ desc_ws, int32_t* __restrict__ nsel_ws,
-    int32_t* __restrict__ sel_out, int32_t* __restrict__ nsel_out) {
+    const int32_t* __restrict__ n_full, const int32_t* __restrict__ span_len,
+    const int32_t* __restrict__ tok_pad, int Hkv, int G, int S, int Sp, double tau, int k_max,
+    float* __restrict__ slogit, int32_t* __restrict__ sel_ws, int32_t* __restrict__ desc_ws,
+    int32_t* __restrict__ nsel_ws, int32_t* __restrict__ sel_out, int32_t* __restrict__ nsel_out,
+    WorkCost wc, int nwaves, int wpitch, int32_t* __restrict__ wstart) {
   const int u = blockIdx.x;
   const int b = u / Hkv;
   const int tid = threadIdx.x;
@@ -222,155 +244,220 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   int32_t* sel = sel_ws + static_cast<size_t>(u) * S;
   int4* desc = reinterpret_cast<int4*>(desc_ws) + static_cast<size_t>(u) * S;
   float* slogit_u = slogit + static_cast<size_t>(u) * Sp * G;
+  const int32_t* len_b = span_len + static_cast<size_t>(b) * S;
   const int kpt = (n + kTopkThreads - 1) / kTopkThreads;
   const int i0 = tid * kpt;
-  const int mine = max(0, min(kpt, n - i0));  // valid indices of this thread
+  const int i1 = min(n, i0 + kpt);  // this thread's indices [i0, i1)
 
-  __shared__ unsigned long long skey[kTopkLds];
+  __shared__ double sz[kTopkLds];
+  __shared__ int hist[kTopkBins];
   __shared__ int red[17];
-  __shared__ unsigned hist[256];
-  __shared__ int s_dg, s_above, s_cnt;
+  __shared__ long long red64[17];
+  __shared__ double redd[32];
+  __shared__ int s_bin, s_above, s_cnt, s_js;
 
   const bool staged = n <= kTopkLds;
   if (staged) {
-    for (int i = tid; i < n; i += kTopkThreads) skey[i] = f64_order_key(z[i]);
+    for (int i = tid; i < n; i += kTopkThreads) sz[i] = z[i];
     __syncthreads();
   }
-  // f(i, key) for this thread's valid keys, in index order
-  auto for_keys = [&](auto&& f) {
-    if (staged) {
-      for (int i = 0; i < mine; ++i) f(i, skey[i0 + i]);
-    } else {
-      for (int i = 0; i < mine; ++i) f(i, f64_order_key(z[i0 + i]));
-    }
-  };
+  auto zat = [&](int i) -> double { return staged ? sz[i] : z[i]; };
 
-  const unsigned long long ktau = f64_order_key(tau);
+  // candidates z > tau: count and value range
   int c_loc = 0;
-  for_keys([&](int, unsigned long long k) { c_loc += k > ktau ? 1 : 0; });
+  double mn = INFINITY, mx = -INFINITY;
+  for (int i = i0; i < i1; ++i) {
+    const double v = zat(i);
+    if (v > tau) {
+      ++c_loc;
+      mn = fmin(mn, v);
+      mx = fmax(mx, v);
+    }
+  }
   int n_cand;
   block_excl_scan(c_loc, red, &n_cand);
+  block_min_max(mn, mx, redd);
 
-  // selection rule: (key & M) > P, or (key & M) == P among the first `rem`
-  unsigned long long P = ktau, M = ~0ull;
-  int rem = 0;
-  if (k_max == 0) {
-    P = ~0ull;  // nothing above
-  } else if (n_cand > k_max) {
-    P = 0ull;
-    M = 0ull;
-    rem = k_max;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0u;
-      __syncthreads();
-      for_keys([&](int, unsigned long long k) {
-        if ((k & M) == P) atomicAdd(&hist[(k >> shift) & 255ull], 1u);
-      });
-      __syncthreads();
-      if (tid < kWave) {
-        // lane l covers bins 255-4l .. 252-4l, highest first
-        int hb[4], ts = 0;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          hb[qq] = static_cast<int>(hist[255 - 4 * tid - qq]);
-          ts += hb[qq];
-        }
-        const int incl = wave_incl_scan(ts);
-        const unsigned long long hit = __ballot(incl >= rem);
-        const int first = __ffsll(static_cast<long long>(hit)) - 1;
-        if (tid == first) {
-          int acc = incl - ts;
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            if (acc + hb[qq] >= rem) {
-              s_dg = 255 - 4 * tid - qq;
-              s_above = acc;
-              s_cnt = hb[qq];
-              break;
+  double zs = INFINITY;  // pick: z > tau && (z > zs || (z == zs && j <= js))
+  int js = -1;
+  if (k_max > 0 && n_cand > 0) {
+    if (n_cand <= k_max) {
+      zs = mn;  // every candidate
+      js = 0x7fffffff;
+    } else {
+      double lo = mn, hi = mx;
+      int rem = k_max;  // entries still to take from [lo, hi]
+      for (int round = 0; round < 256; ++round) {
+        if (lo == hi) {
+          // rem lowest indices among the values equal to lo
+          int e_loc = 0;
+          for (int i = i0; i < i1; ++i) e_loc += zat(i) == lo ? 1 : 0;
+          int e_tot;
+          const int e_before = block_excl_scan(e_loc, red, &e_tot);
+          if (e_before < rem && rem <= e_before + e_loc) {
+            int cnt = e_before;
+            for (int i = i0; i < i1; ++i) {
+              if (zat(i) == lo && ++cnt == rem) {
+                s_js = i;
+                break;
+              }
             }
-            acc += hb[qq];
+          }
+          __syncthreads();
+          zs = lo;
+          js = s_js;
+          break;
+        }
+        const double w = hi - lo;
+        auto bin_of = [&](double v) {
+          return min(kTopkBins - 1, static_cast<int>((v - lo) / w * kTopkBins));
+        };
+        hist[tid] = 0;
+        __syncthreads();
+        for (int i = i0; i < i1; ++i) {
+          const double v = zat(i);
+          if (v >= lo && v <= hi) atomicAdd(&hist[bin_of(v)], 1);
+        }
+        __syncthreads();
+        // thread t holds bin 1023 - t: the exclusive scan counts the bins above
+        const int cnt = hist[kTopkBins - 1 - tid];
+        int tot;
+        const int above = block_excl_scan(cnt, red, &tot);
+        if (above < rem && rem <= above + cnt) {
+          s_bin = kTopkBins - 1 - tid;
+          s_above = above;
+          s_cnt = cnt;
+        }
+        __syncthreads();
+        const int bs = s_bin;
+        rem -= s_above;
+        const int cb = s_cnt;
+        mn = INFINITY;
+        mx = -INFINITY;
+        for (int i = i0; i < i1; ++i) {
+          const double v = zat(i);
+          if (v >= lo && v <= hi && bin_of(v) == bs) {
+            mn = fmin(mn, v);
+            mx = fmax(mx, v);
           }
         }
+        block_min_max(mn, mx, redd);
+        if (cb == rem) {  // the whole bin is taken
+          zs = mn;
+          js = 0x7fffffff;
+          break;
+        }
+        lo = mn;
+        hi = mx;
       }
-      __syncthreads();
-      P |= static_cast<unsigned long long>(s_dg) << shift;
-      M |= 255ull << shift;
-      rem -= s_above;
-      const bool whole = s_cnt == rem;
-      __syncthreads();
-      if (whole) break;
     }
   }
 
-  // flags, rank among the keys equal to P under M, compaction
-  int eq_loc = 0;
-  for_keys([&](int, unsigned long long k) { eq_loc += (k & M) == P ? 1 : 0; });
-  int eq_tot;
-  const int eq_before = block_excl_scan(eq_loc, red, &eq_tot);
-  int pick_loc = 0;
+  // compaction in index order; the scan carries (count << 40) + cost
+  auto picked = [&](int i, double v) { return v > tau && (v > zs || (v == zs && i <= js)); };
+  long long loc = 0;
+  for (int i = i0; i < i1; ++i)
+    if (picked(i, zat(i))) loc += (1ll << 40) + wc.span(len_b[i]);
+  long long tot;
+  long long before = block_excl_scan(loc, red64, &tot);
+  const int n_sel = static_cast<int>(tot >> 40);
+  const long long e_cost = tot & ((1ll << 40) - 1);
   {
-    int eb = eq_before;
-    for_keys([&](int, unsigned long long k) {
-      const unsigned long long km = k & M;
-      pick_loc += (km > P || (km == P && eb < rem)) ? 1 : 0;
-      eb += km == P ? 1 : 0;
-    });
-  }
-  int n_sel;
-  int pos = block_excl_scan(pick_loc, red, &n_sel);
-  {
-    int eb = eq_before;
-    for_keys([&](int i, unsigned long long k) {
-      const unsigned long long km = k & M;
-      const bool pick = km > P || (km == P && eb < rem);
-      eb += km == P ? 1 : 0;
-      if (pick) {
-        const int j = i0 + i;
-        desc[pos] = make_int4(j, span_len[static_cast<size_t>(b) * S + j],
-                              tok_pad[static_cast<size_t>(b) * (S + 1) + j], 0);
-        sel[pos++] = j;
-        for (int g = 0; g < G; ++g) slogit_u[slogit_off(j, g, G)] = -INFINITY;
+    int pos = static_cast<int>(before >> 40);
+    int pre = static_cast<int>(before & ((1ll << 40) - 1));
+    for (int i = i0; i < i1; ++i) {
+      if (picked(i, zat(i))) {
+        const int len = len_b[i];
+        desc[pos] = make_int4(i, len, tok_pad[static_cast<size_t>(b) * (S + 1) + i], pre);
+        sel[pos++] = i;
+        pre += wc.span(len);
+        for (int g = 0; g < G; ++g) slogit_u[slogit_off(i, g, G)] = -INFINITY;
       }
-    });
+    }
   }
   if (tid == 0) nsel_ws[u] = n_sel;
-  if (sel_out != nullptr || nsel_out != nullptr) {
-    __syncthreads();
-    if (sel_out != nullptr)
-      for (int i = tid; i < k_max; i += kTopkThreads)
-        sel_out[static_cast<size_t>(u) * k_max + i] = i < n_sel ? sel[i] : -1;
-    if (nsel_out != nullptr && tid == 0) nsel_out[u] = n_sel;
+  __syncthreads();  // desc and sel visible to the whole workgroup
+  if (sel_out != nullptr)
+    for (int i = tid; i < k_max; i += kTopkThreads)
+      sel_out[static_cast<size_t>(u) * k_max + i] = i < n_sel ? sel[i] : -1;
+  if (nsel_out != nullptr && tid == 0) nsel_out[u] = n_sel;
+
+  if (nwaves > 0) {
+    int32_t* ws = wstart + static_cast<size_t>(u) * wpitch;
+    const int nFI = (n_full[b] + 31) / 32;
+    const int nSI = (n + 31) / 32;
+    const int NI = n_sel + nFI + nSI;
+    const long long C = e_cost + static_cast<long long>(nFI) * wc.full +
+                        static_cast<long long>(nSI) * wc.summ;
+    const long long W = nwaves;
+    if (NI == 0) {
+      for (int w = tid; w <= nwaves; w += kTopkThreads) ws[w] = 0;
+    }
+    // cost of item i, and its exclusive prefix
+    auto item = [&](int i, long long* P) -> long long {
+      if (i < n_sel) {
+        const int4 d = desc[i];
+        *P = d.w;
+        return wc.span(d.y);
+      }
+      if (i < n_sel + nFI) {
+        *P = e_cost + static_cast<long long>(i - n_sel) * wc.full;
+        return wc.full;
+      }
+      *P = e_cost + static_cast<long long>(nFI) * wc.full +
+           static_cast<long long>(i - n_sel - nFI) * wc.summ;
+      return wc.summ;
+    };
+    for (int i = tid; i < NI; i += kTopkThreads) {
+      long long P, Pp;
+      const long long c = item(i, &P);
+      const long long a = (2 * P + c) * W / (2 * C);
+      long long ap = -1;
+      if (i > 0) {
+        const long long cp = item(i - 1, &Pp);
+        ap = (2 * Pp + cp) * W / (2 * C);
+      }
+      for (long long w = ap + 1; w <= a; ++w) ws[w] = i;
+      if (i == NI - 1)
+        for (long long w = a + 1; w <= W; ++w) ws[w] = NI;
+    }
   }
 }
 
 template <int DT, int D>
-hipError_t route_impl(const rskv_cache* c, const void* q, hipStream_t st) {
+hipError_t route_impl(const rskv_cache* c, const void* q, hipStream_t st, const KernelEvents* ev) {
   typedef typename Elem<DT>::T T;
   const int nblk = (c->S + kSpansPerBlock - 1) / kSpansPerBlock;
   dim3 grid(nblk, c->B * c->Hkv);
-  hipLaunchKernelGGL((route_kernel<DT, D>), grid, dim3(kRouteThreads), 0, st,
-                     static_cast<const T*>(q), static_cast<const T*>(c->dev.summary),
-                     c->dev.log_len, c->dev.n_spans, c->dev.proj, c->n_proj, c->Hkv, c->G, c->S,
-                     c->Sp, c->alpha, 1.0f / sqrtf(static_cast<float>(D)), c->dev.z,
-                     c->dev.slogit);
-  return hipGetLastError();
+  return launch(route_kernel<DT, D>, grid, dim3(kRouteThreads), 0, st, ev,
+                static_cast<const T*>(q), static_cast<const T*>(c->dev.summary), c->dev.log_len,
+                c->dev.n_spans, c->dev.proj, c->n_proj, c->Hkv, c->G, c->S, c->Sp, c->alpha,
+                1.0f / sqrtf(static_cast<float>(D)), c->dev.z, c->dev.slogit);
 }
 
 }  // namespace
 
-hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st) {
+hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st,
+                        const KernelEvents* ev) {
   if (c->dtype == kBF16)
-    return c->d == 128 ? route_impl<kBF16, 128>(c, q, st) : route_impl<kBF16, 64>(c, q, st);
-  return c->d == 128 ? route_impl<kF32, 128>(c, q, st) : route_impl<kF32, 64>(c, q, st);
+    return c->d == 128 ? route_impl<kBF16, 128>(c, q, st, ev) : route_impl<kBF16, 64>(c, q, st, ev);
+  return c->d == 128 ? route_impl<kF32, 128>(c, q, st, ev) : route_impl<kF32, 64>(c, q, st, ev);
 }
 
-hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int32_t* sel_out,
-                       int32_t* nsel_out, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3(c->B * c->Hkv), dim3(kTopkThreads), 0, st, c->dev.z,
-                     c->dev.n_spans, c->dev.span_len, c->dev.tok_pad, c->Hkv, c->G, c->S, c->Sp,
-                     static_cast<double>(tau), k_max, c->dev.slogit, c->dev.sel,
-                     c->dev.sel_desc, c->dev.n_sel, sel_out, nsel_out);
-  return hipGetLastError();
+hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int nwaves, int32_t* sel_out,
+                       int32_t* nsel_out, hipStream_t st, const KernelEvents* ev) {
+  const int be = c->dtype == kBF16 ? 2 : 4;
+  WorkCost wc;
+  wc.span_base = (2 * c->rank * c->d * be) / 64 + kItemOverhead;
+  wc.span_row = 2 * c->rank * be;  // bytes per padded row
+  wc.span_extra = kSpanRoundTrip;
+  wc.full = (2 * 32 * c->d * be) / 64 + kItemOverhead;
+  wc.summ = (32 * c->d * be + 32 * c->G * 4) / 64 + kItemOverhead;
+  return launch(topk_kernel, dim3(c->B * c->Hkv), dim3(kTopkThreads), 0, st, ev, c->dev.z,
+                c->dev.n_spans, c->dev.n_full, c->dev.span_len, c->dev.tok_pad, c->Hkv, c->G, c->S,
+                c->Sp, static_cast<double>(tau), k_max, c->dev.slogit, c->dev.sel,
+                c->dev.sel_desc, c->dev.n_sel, sel_out, nsel_out, wc, nwaves,
+                4 * c->nsplit_max + 1, c->dev.wstart);
 }
 
 }  // namespace rskv
