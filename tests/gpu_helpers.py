@@ -58,6 +58,24 @@ def oracle_view(ex):
                 BV=f("w_v"))
 
 
+def unit_view(ex, b, h):
+    """Oracle cache dictionary holding the single unit (sequence b, KV head
+    h) of a canonical export (B = Hkv = 1; converts only that unit)."""
+    info = ex["info"]
+    dt = "bf16" if info["dtype"] == 1 else "f32"
+    f = lambda k: oracle.from_stored(ex[k][b:b + 1, h:h + 1], dt)  # noqa: E731
+    return dict(B=1, Hq=info["n_q_heads"] // info["n_kv_heads"], Hkv=1, d=info["head_dim"],
+                T=info["context_len"], rank=info["rank"], dtype=dt,
+                tail_capacity=info["tail_capacity"], appended=info["appended"],
+                n_s=ex["n_spans"][b:b + 1].astype(np.int64),
+                n_F=ex["n_full"][b:b + 1].astype(np.int64).copy(),
+                span_len=ex["span_len"][b:b + 1].astype(np.int64),
+                fr_pos=ex["full_pos"][b:b + 1].astype(np.int64).copy(),
+                s=f("summary"), vbar=f("vmean"), ell=ex["log_len"][b:b + 1].astype(np.float64),
+                KF=f("k_full"), VF=f("v_full"), AK=f("a_k"), AV=f("a_v"), BK=f("w_k"),
+                BV=f("w_v"))
+
+
 def decode_gpu(cache, q_np, tau, k_max, device="cuda"):
     """Returns (out [B][Hq][d] fp64, sel lists [b][h])."""
     import torch
