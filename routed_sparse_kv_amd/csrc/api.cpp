@@ -537,9 +537,20 @@ int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, flo
       }
     }
     RSKV_HIP(rskv::launch_route(c, q, st, prof ? &ev[0] : nullptr), "route kernel");
-    RSKV_HIP(rskv::launch_topk(c, tau, k_max, nwaves, sel, n_sel, st, prof ? &ev[1] : nullptr),
-             "topk kernel");
-    RSKV_HIP(rskv::launch_attend(c, q, nsplit, st, prof ? &ev[2] : nullptr), "attend kernel");
+    const bool fused = rskv::attend_fuses_topk(c, k_max);
+    const rskv::SelectArgs sa{tau, k_max, sel, n_sel};
+    if (fused) {
+      // the attention kernel selects; the top-k slot of the profile stays empty
+      if (prof) {
+        RSKV_HIP(hipEventRecord(ev[1].start, st), "event record");
+        RSKV_HIP(hipEventRecord(ev[1].stop, st), "event record");
+      }
+    } else {
+      RSKV_HIP(rskv::launch_topk(c, tau, k_max, nwaves, sel, n_sel, st, prof ? &ev[1] : nullptr),
+               "topk kernel");
+    }
+    RSKV_HIP(rskv::launch_attend(c, q, nsplit, fused ? &sa : nullptr, st, prof ? &ev[2] : nullptr),
+             "attend kernel");
     RSKV_HIP(rskv::launch_merge(c, nsplit, out, st, prof ? &ev[3] : nullptr), "merge kernel");
     if (prof) {
       for (int i = 0; i < kK; ++i) {

@@ -134,7 +134,76 @@ struct ItemPlan {
   static constexpr int kEA = KK + CB / 2;  // first A slot of a span item
 };
 
-template <int D, int R>
+// LDS of the fused variant (spans of one unit held in LDS; indices padded by
+// one slot per 16 so that a thread's contiguous run avoids bank conflicts).
+constexpr int kFuseSpans = 4096;
+constexpr int kFuseSel = 1024;
+constexpr int kFusePad = kFuseSpans + kFuseSpans / 16;
+__device__ __forceinline__ int pidx(int i) { return i + (i >> 4); }
+
+struct FusedLds {
+  union {
+    int2 elist[kFuseSel];      // item loop: {span, exclusive work-cost prefix}
+    float merge[4 * 128 * 16]; // end: per-wave out^T
+  };
+  int len[kFusePad];
+  int tpad[kFusePad];
+  int hist[1024];
+  unsigned mask[kFuseSpans / 32];  // expanded spans
+  int rowcnt[kFuseSpans / 256][4];
+  int rowcost[kFuseSpans / 256][4];
+  int ired[3][4];
+  double dred[2][4];
+  double cand_z[256];
+  int cand_j[256];
+  double s_zs;
+  int s_bin, s_above, s_cnt, s_js;
+  int rng[5];
+};
+
+// Sum of v over the block (4 waves) and min/max of 64-bit keys; `slot`
+// selects one of the LDS scratch rows (consecutive calls use different
+// rows, so a single barrier per call suffices).
+__device__ __forceinline__ int block4_sum(int v, FusedLds& L, int slot) {
+  const int wave = threadIdx.x >> 6;
+  const int t = __builtin_amdgcn_readlane(wave_incl_scan_dpp(v), 63);
+  if ((threadIdx.x & 63) == 0) L.ired[slot][wave] = t;
+  __syncthreads();
+  return L.ired[slot][0] + L.ired[slot][1] + L.ired[slot][2] + L.ired[slot][3];
+}
+// Exclusive prefix of v over the block (thread order) and the total.
+__device__ __forceinline__ int block4_excl(int v, FusedLds& L, int slot, int* total) {
+  const int wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan_dpp(v);
+  if ((threadIdx.x & 63) == 63) L.ired[slot][wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int x = L.ired[slot][w];
+    before += w < wave ? x : 0;
+    tot += x;
+  }
+  *total = tot;
+  return before + incl - v;
+}
+__device__ __forceinline__ void block4_min_max_f64(double& mn, double& mx, FusedLds& L) {
+  const int wave = threadIdx.x >> 6;
+  wave_min_max_f64(mn, mx);
+  if ((threadIdx.x & 63) == 0) {
+    L.dred[0][wave] = mn;
+    L.dred[1][wave] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mn = fmin(mn, L.dred[0][w]);
+    mx = fmax(mx, L.dred[1][w]);
+  }
+  __syncthreads();
+}
+
+template <int D, int R, bool FUSED>
 __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kf,
                    const uint16_t* __restrict__ vf, const int32_t* __restrict__ n_full,
@@ -143,7 +212,10 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    const uint16_t* __restrict__ a_v, const uint16_t* __restrict__ w_k,
                    const uint16_t* __restrict__ w_v, const int32_t* __restrict__ sel_desc,
                    const int32_t* __restrict__ n_sel, const int32_t* __restrict__ wstart,
-                   int Hkv, int G, int S, int Sp, int Fp, int Np, int wpitch, int nsplit_max,
+                   const double* __restrict__ z_all, const int32_t* __restrict__ span_len,
+                   const int32_t* __restrict__ tok_pad, double tau, int k_max, WorkCost wc,
+                   int32_t* __restrict__ sel_out, int32_t* __restrict__ nsel_out, int Hkv,
+                   int G, int S, int Sp, int Fp, int Np, int wpitch, int nsplit_max,
                    float inv_sqrt_d, float* __restrict__ part) {
   typedef ItemPlan<D> IP;
   constexpr int KK = IP::KK;
@@ -185,15 +257,367 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const uint16_t* av_u = a_v + static_cast<size_t>(u) * Np * R;
   const uint16_t* wk_u = w_k + static_cast<size_t>(u) * S * R * D;
   const uint16_t* wv_u = w_v + static_cast<size_t>(u) * S * D * R4;
-  const int4* desc_u = reinterpret_cast<const int4*>(sel_desc) + static_cast<size_t>(u) * S;
 
   const int nf = n_full[b];
   const int ns = n_spans[b];
-  const int nsel = n_sel[u];
   const int nFI = (nf + kChunk - 1) / kChunk;
-  const int* ws = wstart + static_cast<size_t>(u) * wpitch + s * 4 + wave;
-  const int i0 = ws[0];
-  const int i1 = ws[1];
+
+  // softmax over 8 logits per lane, then acc += V^T p with V the A operand
+  auto attend8 = [&](float* x, int r0, int lim, const u32x4* vbuf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = r0 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4));
+      if (!head_ok || row >= lim) x[e] = -INFINITY;
+    }
+    const float sc = wave_softmax8(x, m, l);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] *= sc;
+    bf16x8 phi, plo;
+    split8(x, phi, plo);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      acc[cb] = mma32(as8(vbuf[cb]), phi, acc[cb]);
+      acc[cb] = mma32(as8(vbuf[cb]), plo, acc[cb]);
+    }
+  };
+
+  // a 32-row full-resolution chunk: K as 2 x KK tiles, V as CB tiles
+  auto issue_full = [&](int r0, u32x4* buf) {
+    const uint16_t* kt = kf_u + static_cast<size_t>(r0 >> 4) * KK * 512 + lane * 8;
+#pragma unroll
+    for (int t = 0; t < 2 * KK; ++t) buf[t] = ld16(kt + t * 512);
+    const uint16_t* vt = vf_u + static_cast<size_t>(r0 >> 5) * CB * 512 + lane * 8;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) buf[2 * KK + cb] = ld16(vt + cb * 512);
+  };
+  auto compute_full = [&](int r0, const u32x4* buf) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s0 = mma32(as8(buf[kk]), qb[kk], s0);
+      s1 = mma32(as8(buf[KK + kk]), qb[kk], s1);
+    }
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = s0[e] * inv_sqrt_d;
+      x[4 + e] = s1[e] * inv_sqrt_d;
+    }
+    attend8(x, r0, nf, buf + 2 * KK);
+  };
+
+  // ---- expanded spans and this wave's item range
+  __shared__ __align__(16) unsigned char lds_raw[FUSED ? sizeof(FusedLds) : 4 * (2 * 16 + D * 16) * 4];
+  int nsel, i0, i1;
+  int fb = 0;  // first full-resolution chunk that belongs to the item ranges
+  const int wglob = 4 * s + wave;
+  const bool pre = FUSED && wglob < nFI;
+  u32x4 pbuf[2 * KK + CB];
+  if constexpr (FUSED) {
+    // Selection of the unit by the same rule as the top-k kernel (the kept
+    // set is fixed by its last entry (z*, j*)), compaction with work costs,
+    // and the cost-balanced ranges of this workgroup's four waves.  Thread
+    // t owns spans t + 256 k (k < 16) and keeps their scores and lengths in
+    // registers; ordering by (k, t) is ordering by span index.
+    FusedLds& L = *reinterpret_cast<FusedLds*>(lds_raw);
+    const double* z_u = z_all + static_cast<size_t>(u) * S;
+    const int32_t* len_b = span_len + static_cast<size_t>(b) * S;
+    const int32_t* tp_b = tok_pad + static_cast<size_t>(b) * (S + 1);
+    constexpr int KR = kFuseSpans / kAttThreads;
+    double zr[KR];
+    {
+      int lr[KR], tr[KR];
+#pragma unroll
+      for (int k = 0; k < KR; ++k) {
+        const int i = tid + kAttThreads * k;
+        zr[k] = -INFINITY;
+        if (i < ns) {
+          zr[k] = z_u[i];
+          lr[k] = len_b[i];
+          tr[k] = tp_b[i];
+        }
+      }
+      // wave w of the unit takes chunk w before the ranges exist: its loads
+      // are in flight while the workgroup selects.  Issued unconditionally
+      // (a wave without a chunk re-reads the last one and drops it), so
+      // that waits for the values above count exactly these loads.
+      issue_full(min(wglob, max(nFI, 1) - 1) * kChunk, pbuf);
+#pragma unroll
+      for (int k = 0; k < KR; ++k) {
+        const int i = tid + kAttThreads * k;
+        if (i < ns) {
+          L.len[pidx(i)] = lr[k];
+          L.tpad[pidx(i)] = tr[k];
+        }
+      }
+      for (int w = tid; w < kFuseSpans / 32; w += kAttThreads) L.mask[w] = 0u;
+    }
+    // candidates z > tau: count and value range (padding slots hold -inf)
+    int c_loc = 0;
+    double lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      if (zr[k] > tau) {
+        ++c_loc;
+        lo = fmin(lo, zr[k]);
+        hi = fmax(hi, zr[k]);
+      }
+    }
+    const int n_cand = block4_sum(c_loc, L, 0);
+    block4_min_max_f64(lo, hi, L);
+    // Position in index order of this thread's flagged slots: ballots per
+    // slot row, wave totals in LDS, one barrier.  Returns the count before
+    // slot k of this thread through base[k] and the total.
+    const unsigned long long below = (1ull << lane) - 1ull;
+    auto order_prefix = [&](const bool* flag, int* base, int* total) {
+      unsigned long long bal[KR];
+#pragma unroll
+      for (int k = 0; k < KR; ++k) {
+        bal[k] = __ballot(flag[k]);
+        if (lane == 0) L.rowcnt[k][wave] = __popcll(bal[k]);
+      }
+      __syncthreads();
+      int run = 0;
+#pragma unroll
+      for (int k = 0; k < KR; ++k) {
+        int before_w = 0, row = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int c = L.rowcnt[k][w];
+          before_w += w < wave ? c : 0;
+          row += c;
+        }
+        base[k] = run + before_w + __popcll(bal[k] & below);
+        run += row;
+      }
+      *total = run;
+      __syncthreads();
+    };
+    double zs = INFINITY;  // pick: z > tau && (z > zs || (z == zs && j <= js))
+    int js = -1;
+    if (k_max > 0 && n_cand > 0) {
+      if (n_cand <= k_max) {
+        zs = lo;
+        js = 0x7fffffff;
+      } else {
+        int rem = k_max;  // entries still to take from [lo, hi]
+        for (int round = 0; round < 256; ++round) {
+          if (lo == hi) {
+            // rem lowest indices among the values equal to lo
+            bool f[KR];
+            int base[KR], tot;
+#pragma unroll
+            for (int k = 0; k < KR; ++k) f[k] = zr[k] == lo;
+            order_prefix(f, base, &tot);
+#pragma unroll
+            for (int k = 0; k < KR; ++k)
+              if (f[k] && base[k] == rem - 1) L.s_js = tid + kAttThreads * k;
+            __syncthreads();
+            zs = lo;
+            js = L.s_js;
+            break;
+          }
+          // 1024 bins over [lo, hi]: any map that is monotone in z gives an
+          // exact answer; fp32 arithmetic is used unless the range is too
+          // small for it, where fp64 division takes over.
+          const double w = hi - lo;
+          const float wf = static_cast<float>(w);
+          const bool f32ok = wf > 1e-30f;  // uniform across the workgroup
+          const float sf = 1024.f / wf;
+          // bin of each owned slot (-1 outside [lo, hi]); the precision is a
+          // uniform branch, so only one of the two formulas is executed
+          int bin[KR];
+          if (f32ok) {
+#pragma unroll
+            for (int k = 0; k < KR; ++k)
+              bin[k] = (zr[k] >= lo && zr[k] <= hi)
+                           ? min(1023, static_cast<int>(static_cast<float>(zr[k] - lo) * sf))
+                           : -1;
+          } else {
+#pragma unroll
+            for (int k = 0; k < KR; ++k)
+              bin[k] = (zr[k] >= lo && zr[k] <= hi)
+                           ? min(1023, static_cast<int>((zr[k] - lo) / w * 1024.0))
+                           : -1;
+          }
+          for (int x = tid; x < 1024; x += kAttThreads) L.hist[x] = 0;
+          if (tid == 0) L.s_cnt = 0;
+          __syncthreads();
+#pragma unroll
+          for (int k = 0; k < KR; ++k)
+            if (bin[k] >= 0) atomicAdd(&L.hist[bin[k]], 1);
+          __syncthreads();
+          // thread t holds bins 1023 - 4t .. 1020 - 4t, highest first
+          int c4[4], cs = 0;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            c4[x] = L.hist[1023 - 4 * tid - x];
+            cs += c4[x];
+          }
+          int tot;
+          const int above = block4_excl(cs, L, 1, &tot);
+          if (above < rem && rem <= above + cs) {
+            int a2 = above;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              if (a2 < rem && rem <= a2 + c4[x]) {
+                L.s_bin = 1023 - 4 * tid - x;
+                L.s_above = a2;
+                L.s_cnt = c4[x];
+              }
+              a2 += c4[x];
+            }
+          }
+          __syncthreads();
+          const int bs = L.s_bin;
+          rem -= L.s_above;
+          const int cb = L.s_cnt;
+          if (cb <= kAttThreads) {
+            // few values left: rank them exactly, (z descending, index
+            // ascending); the one of rank rem - 1 is the last kept entry
+            __syncthreads();
+            if (tid == 0) L.s_above = 0;
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < KR; ++k) {
+              if (bin[k] == bs) {
+                const int slot = atomicAdd(&L.s_above, 1);
+                L.cand_z[slot] = zr[k];
+                L.cand_j[slot] = tid + kAttThreads * k;
+              }
+            }
+            __syncthreads();
+            if (tid < cb) {
+              const double v = L.cand_z[tid];
+              const int j = L.cand_j[tid];
+              int rank = 0;
+              for (int y = 0; y < cb; ++y) {
+                const double vy = L.cand_z[y];
+                rank += (vy > v || (vy == v && L.cand_j[y] < j)) ? 1 : 0;
+              }
+              if (rank == rem - 1) {
+                L.s_zs = v;
+                L.s_js = j;
+              }
+            }
+            __syncthreads();
+            zs = L.s_zs;
+            js = L.s_js;
+            break;
+          }
+          // many values left: narrow to their range and repeat
+          double nlo = INFINITY, nhi = -INFINITY;
+#pragma unroll
+          for (int k = 0; k < KR; ++k) {
+            if (bin[k] == bs) {
+              nlo = fmin(nlo, zr[k]);
+              nhi = fmax(nhi, zr[k]);
+            }
+          }
+          block4_min_max_f64(nlo, nhi, L);
+          lo = nlo;
+          hi = nhi;
+        }
+      }
+    }
+    // compaction in index order, with exclusive work-cost prefixes: per
+    // slot row, a ballot and a DPP scan of the costs within each wave, wave
+    // totals in LDS, one barrier
+    auto picked = [&](int k) {
+      const int i = tid + kAttThreads * k;
+      return zr[k] > tau && (zr[k] > zs || (zr[k] == zs && i <= js));
+    };
+    int cpre[KR];  // exclusive cost prefix of slot k within its wave row
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      const bool f = picked(k);
+      const unsigned long long bal = __ballot(f);
+      const int c = f ? wc.span(L.len[pidx(tid + kAttThreads * k)]) : 0;
+      const int incl = wave_incl_scan_dpp(c);
+      cpre[k] = incl - c;
+      if (lane == 63) {
+        L.rowcnt[k][wave] = __popcll(bal);
+        L.rowcost[k][wave] = incl;
+      }
+    }
+    __syncthreads();
+    int e_cost = 0;
+    nsel = 0;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      int cw = 0, crow = 0, kw = 0, krow = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c = L.rowcnt[k][w], q = L.rowcost[k][w];
+        cw += w < wave ? c : 0;
+        crow += c;
+        kw += w < wave ? q : 0;
+        krow += q;
+      }
+      const bool f = picked(k);
+      const unsigned long long bal = __ballot(f);
+      if (f) {
+        const int i = tid + kAttThreads * k;
+        const int pos = nsel + cw + __popcll(bal & below);
+        L.elist[pos] = make_int2(i, e_cost + kw + cpre[k]);
+        atomicOr(&L.mask[i >> 5], 1u << (i & 31));
+      }
+      nsel += crow;
+      e_cost += krow;
+    }
+    __syncthreads();
+    if (s == 0) {
+      if (sel_out != nullptr)
+        for (int i = tid; i < k_max; i += kAttThreads)
+          sel_out[static_cast<size_t>(u) * k_max + i] = i < nsel ? L.elist[i].x : -1;
+      if (nsel_out != nullptr && tid == 0) nsel_out[u] = nsel;
+    }
+    // Ranges of the remaining items [expanded spans | chunks fb.. | summary
+    // chunks]: item i goes to wave floor((2 P_i + c_i) W / (2 C)), so the
+    // first item of wave w is the first i with (2 P_i + c_i) W >= 2 C w;
+    // each thread tests its items against the five boundaries of this
+    // workgroup.
+    const long long W = 4ll * gridDim.x;
+    fb = static_cast<int>(min(static_cast<long long>(nFI), W));
+    {
+      const int nFP = nFI - fb;
+      const int nSI = (ns + kChunk - 1) / kChunk;
+      const int NI = nsel + nFP + nSI;
+      const long long C = static_cast<long long>(e_cost) + static_cast<long long>(nFP) * wc.full +
+                          static_cast<long long>(nSI) * wc.summ;
+      auto mid2 = [&](int i) -> long long {  // 2 P_i + c_i
+        if (i < nsel) {
+          const int2 e = L.elist[i];
+          return 2ll * e.y + wc.span(L.len[pidx(e.x)]);
+        }
+        if (i < nsel + nFP)
+          return 2ll * (e_cost + static_cast<long long>(i - nsel) * wc.full) + wc.full;
+        return 2ll * (e_cost + static_cast<long long>(nFP) * wc.full +
+                      static_cast<long long>(i - nsel - nFP) * wc.summ) + wc.summ;
+      };
+      if (tid < 5) L.rng[tid] = NI;
+      __syncthreads();
+      for (int i = tid; i < NI; i += kAttThreads) {
+        const long long mi = mid2(i) * W;
+        const long long mp = i > 0 ? mid2(i - 1) * W : -1;
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+          const long long t = 2 * C * (4ll * s + k);
+          if (mp < t && t <= mi) L.rng[k] = i;
+        }
+      }
+      __syncthreads();
+    }
+    i0 = L.rng[wave];
+    i1 = L.rng[wave + 1];
+  } else {
+    nsel = n_sel[u];
+    const int* ws = wstart + static_cast<size_t>(u) * wpitch + s * 4 + wave;
+    i0 = ws[0];
+    i1 = ws[1];
+  }
+  const int nFP = nFI - fb;  // full-resolution chunks inside the item ranges
+  const int4* desc_u = reinterpret_cast<const int4*>(sel_desc) + static_cast<size_t>(u) * S;
 
   // lane-constant parts of the span addresses (ranks past R read rank 0 and
   // are zeroed after the load)
@@ -234,16 +658,10 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           vs.y = v2.y;
         }
       }
-    } else if (i < nsel + nFI) {
-      const int r0 = (i - nsel) * kChunk;
-      const uint16_t* kt = kf_u + static_cast<size_t>(r0 >> 4) * KK * 512 + lane * 8;
-#pragma unroll
-      for (int t = 0; t < 2 * KK; ++t) buf[t] = ld16(kt + t * 512);
-      const uint16_t* vt = vf_u + static_cast<size_t>(r0 >> 5) * CB * 512 + lane * 8;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) buf[2 * KK + cb] = ld16(vt + cb * 512);
+    } else if (i < nsel + nFP) {
+      issue_full((i - nsel + fb) * kChunk, buf);
     } else {
-      const int r0 = (i - nsel - nFI) * kChunk;
+      const int r0 = (i - nsel - nFP) * kChunk;
       const uint16_t* vt = vm_u + static_cast<size_t>(r0 >> 5) * CB * 512 + lane * 8;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) buf[cb] = ld16(vt + cb * 512);
@@ -253,26 +671,7 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   };
 
-  // softmax over 8 logits per lane, then acc += V^T p with V the A operand
-  auto attend8 = [&](float* x, int r0, int lim, const u32x4* vbuf) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = r0 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4));
-      if (!head_ok || row >= lim) x[e] = -INFINITY;
-    }
-    const float sc = wave_softmax8(x, m, l);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[cb] *= sc;
-    bf16x8 phi, plo;
-    split8(x, phi, plo);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      acc[cb] = mma32(as8(vbuf[cb]), phi, acc[cb]);
-      acc[cb] = mma32(as8(vbuf[cb]), plo, acc[cb]);
-    }
-  };
-
-  auto compute = [&](int i, const int4& dsc, const u32x4 (&buf)[NL]) {
+  auto compute = [&](int i, const int4& dsc, const u32x4 (&buf)[NL], const unsigned* xmask) {
     if (i < nsel) {
       // ---- expanded span: logits A_K (W_K q), softmax, w += A_V^T p,
       // then out^T += W_V^T w
@@ -371,56 +770,65 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           acc[2 * p + hh] = mma16(wv4, wlo, acc[2 * p + hh]);
         }
       }
-    } else if (i < nsel + nFI) {
+    } else if (i < nsel + nFP) {
       // ---- 32 full-resolution rows
-      const int r0 = (i - nsel) * kChunk;
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s0 = mma32(as8(buf[kk]), qb[kk], s0);
-        s1 = mma32(as8(buf[KK + kk]), qb[kk], s1);
-      }
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = s0[e] * inv_sqrt_d;
-        x[4 + e] = s1[e] * inv_sqrt_d;
-      }
-      attend8(x, r0, nf, buf + 2 * KK);
+      compute_full((i - nsel + fb) * kChunk, buf);
     } else {
-      // ---- 32 summary entries
-      const int r0 = (i - nsel - nFI) * kChunk;
+      // ---- 32 summary entries (expanded spans enter through their tokens)
+      const int r0 = (i - nsel - nFP) * kChunk;
       const f32x4 l0 = asf(buf[CB]);
       const f32x4 l1 = asf(buf[CB + 1]);
+      const unsigned xm = xmask != nullptr ? xmask[r0 >> 5] : 0u;
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = l0[e];
-        x[4 + e] = l1[e];
+        x[e] = (xm >> (4 * grp + e)) & 1u ? -INFINITY : l0[e];
+        x[4 + e] = (xm >> (16 + 4 * grp + e)) & 1u ? -INFINITY : l1[e];
       }
       attend8(x, r0, ns, buf);
     }
   };
 
+  if (pre) compute_full(wglob * kChunk, pbuf);
+
   // Item loop: all loads of an item are issued before any of them is
-  // waited for; the next span descriptor is fetched (scalar) meanwhile.
+  // waited for.
   if (i0 < i1) {
-    auto desc_at = [&](int i) { return i < nsel ? desc_u[i] : make_int4(0, 0, 0, 0); };
-    int4 dn = desc_at(i0);
-    for (int i = i0; i < i1; ++i) {
-      const int4 dc = dn;
-      dn = desc_at(min(i + 1, i1 - 1));
-      u32x4 buf[NL];
-      issue(i, dc, buf);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(i, dc, buf);
+    if constexpr (FUSED) {
+      const FusedLds& L = *reinterpret_cast<const FusedLds*>(lds_raw);
+      for (int i = i0; i < i1; ++i) {
+        int4 dc = make_int4(0, 0, 0, 0);
+        if (i < nsel) {
+          const int j = L.elist[i].x;
+          dc = make_int4(j, L.len[pidx(j)], L.tpad[pidx(j)], 0);
+        }
+        u32x4 buf[NL];
+        issue(i, dc, buf);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, dc, buf, L.mask);
+      }
+    } else {
+      // the next span descriptor is fetched (scalar) while an item is in flight
+      auto desc_at = [&](int i) { return i < nsel ? desc_u[i] : make_int4(0, 0, 0, 0); };
+      int4 dn = desc_at(i0);
+      for (int i = i0; i < i1; ++i) {
+        const int4 dc = dn;
+        dn = desc_at(min(i + 1, i1 - 1));
+        u32x4 buf[NL];
+        issue(i, dc, buf);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, dc, buf, static_cast<const unsigned*>(nullptr));
+      }
     }
   }
 
   // ---- merge the four waves of the workgroup in LDS, write one partial
-  __shared__ float sm_m[4][16];
-  __shared__ float sm_l[4][16];
-  __shared__ float sm_buf[4 * D * 16];  // per wave out^T[c][head]
+  float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(
+      lds_raw + (FUSED ? offsetof(FusedLds, hist) : 0));
+  float (*sm_l)[16] = sm_m + 4;
+  float* sm_buf = FUSED ? reinterpret_cast<float*>(lds_raw)
+                        : reinterpret_cast<float*>(lds_raw) + 2 * 4 * 16;
+  if constexpr (FUSED) __syncthreads();  // the span list is no longer read
   if (grp == 0) {
     sm_m[wave][g16] = m;
     sm_l[wave][g16] = l;
@@ -741,17 +1149,24 @@ bool use_mfma(const rskv_cache* c) {
 }
 
 template <int D, int R>
-hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
-                            const KernelEvents* ev) {
+hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, const SelectArgs* sa,
+                            hipStream_t st, const KernelEvents* ev) {
   dim3 grid(nsplit, c->B * c->Hkv);
-  return launch(attend_mfma_kernel<D, R>, grid, dim3(kAttThreads), 0, st, ev,
-                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c->dev.k_full),
+  const WorkCost wc = work_cost(c);
+  const double tau = sa ? static_cast<double>(sa->tau) : 0.0;
+  const int k_max = sa ? sa->k_max : 0;
+  int32_t* so = sa ? sa->sel_out : nullptr;
+  int32_t* no = sa ? sa->nsel_out : nullptr;
+  auto kern = sa ? attend_mfma_kernel<D, R, true> : attend_mfma_kernel<D, R, false>;
+  return launch(kern, grid, dim3(kAttThreads), 0, st, ev, static_cast<const uint16_t*>(q),
+                static_cast<const uint16_t*>(c->dev.k_full),
                 static_cast<const uint16_t*>(c->dev.v_full), c->dev.n_full,
                 static_cast<const uint16_t*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
                 static_cast<const uint16_t*>(c->dev.a_k), static_cast<const uint16_t*>(c->dev.a_v),
                 static_cast<const uint16_t*>(c->dev.w_k), static_cast<const uint16_t*>(c->dev.w_v),
-                c->dev.sel_desc, c->dev.n_sel, c->dev.wstart, c->Hkv, c->G, c->S, c->Sp, c->Fp,
-                c->Np, 4 * c->nsplit_max + 1, c->nsplit_max, 1.0f / sqrtf(static_cast<float>(D)),
+                c->dev.sel_desc, c->dev.n_sel, c->dev.wstart, c->dev.z, c->dev.span_len,
+                c->dev.tok_pad, tau, k_max, wc, so, no, c->Hkv, c->G, c->S, c->Sp, c->Fp, c->Np,
+                4 * c->nsplit_max + 1, c->nsplit_max, 1.0f / sqrtf(static_cast<float>(D)),
                 c->dev.part);
 }
 
@@ -774,6 +1189,27 @@ hipError_t attend_valu_impl(const rskv_cache* c, const void* q, int nsplit, hipS
 }  // namespace
 
 bool attend_uses_mfma(const rskv_cache* c) { return use_mfma(c); }
+
+bool attend_fuses_topk(const rskv_cache* c, int k_max) {
+  const int k_slots = k_max < c->S ? k_max : c->S;
+  return use_mfma(c) && c->S <= kFuseSpans && k_slots <= kFuseSel;
+}
+
+// Work cost model of the attention items (64-byte units): bytes an item
+// reads plus a fixed per-item overhead, plus one load round trip for every
+// 32 rows of a span past the 64 loaded with its factor matrices.
+WorkCost work_cost(const rskv_cache* c) {
+  constexpr int kItemOverhead = 16;
+  constexpr int kSpanRoundTrip = 64;
+  const int be = c->dtype == kBF16 ? 2 : 4;
+  WorkCost wc;
+  wc.span_base = (2 * c->rank * c->d * be) / 64 + kItemOverhead;
+  wc.span_row = 2 * c->rank * be;
+  wc.span_extra = kSpanRoundTrip;
+  wc.full = (2 * kChunk * c->d * be) / 64 + kItemOverhead;
+  wc.summ = (kChunk * c->d * be + kChunk * c->G * 4) / 64 + kItemOverhead;
+  return wc;
+}
 
 // Workgroups per unit.  MFMA path: about two resident workgroups per CU
 // (512 over all units; each wave then works through a long item range with
@@ -812,14 +1248,14 @@ int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap) {
   return m > o ? m : o;
 }
 
-hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
-                         const KernelEvents* ev) {
+hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, const SelectArgs* sa,
+                         hipStream_t st, const KernelEvents* ev) {
   if (use_mfma(c)) {
     if (c->d == 128)
-      return c->rank == 16 ? attend_mfma_impl<128, 16>(c, q, nsplit, st, ev)
-                           : attend_mfma_impl<128, 8>(c, q, nsplit, st, ev);
-    return c->rank == 16 ? attend_mfma_impl<64, 16>(c, q, nsplit, st, ev)
-                         : attend_mfma_impl<64, 8>(c, q, nsplit, st, ev);
+      return c->rank == 16 ? attend_mfma_impl<128, 16>(c, q, nsplit, sa, st, ev)
+                           : attend_mfma_impl<128, 8>(c, q, nsplit, sa, st, ev);
+    return c->rank == 16 ? attend_mfma_impl<64, 16>(c, q, nsplit, sa, st, ev)
+                         : attend_mfma_impl<64, 8>(c, q, nsplit, sa, st, ev);
   }
   return c->dtype == kBF16 ? attend_valu_impl<kBF16>(c, q, nsplit, st, ev)
                            : attend_valu_impl<kF32>(c, q, nsplit, st, ev);

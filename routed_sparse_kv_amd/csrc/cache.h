@@ -86,10 +86,11 @@ struct WorkCost {
   int span_extra;  // each further 32 rows past the first 64 (a load round)
   int full;        // 32 full-resolution rows
   int summ;        // 32 summary entries
-  __host__ __device__ long long span(int len) const {
-    const long long pad = (len + 15) & ~15;
-    const long long extra = len > 64 ? (len - 64 + 31) / 32 : 0;
-    return span_base + pad * span_row / 64 + extra * span_extra;
+  // (fits in int for spans of up to 2^24 rows)
+  __host__ __device__ int span(int len) const {
+    const int pad = (len + 15) & ~15;
+    const int extra = len > 64 ? (len - 33) >> 5 : 0;
+    return span_base + ((pad * span_row) >> 6) + extra * span_extra;
   }
 };
 
@@ -153,8 +154,19 @@ hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int nwaves, in
 int decode_nsplit(const rskv_cache* c, int k_max);
 int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap);
 bool attend_uses_mfma(const rskv_cache* c);
-hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
-                         const KernelEvents* ev);
+WorkCost work_cost(const rskv_cache* c);
+
+// Arguments of the attention launch when it also makes the top-k selection
+// (attend_fuses_topk): the spans of a unit fit in the kernel's LDS.
+struct SelectArgs {
+  float tau;
+  int k_max;
+  int32_t* sel_out;   // may be null
+  int32_t* nsel_out;  // may be null
+};
+bool attend_fuses_topk(const rskv_cache* c, int k_max);
+hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, const SelectArgs* sel,
+                         hipStream_t st, const KernelEvents* ev);
 hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st,
                         const KernelEvents* ev);
 

@@ -94,6 +94,88 @@ __device__ __forceinline__ T wave_incl_scan(T v) {
   return v;
 }
 
+// Inclusive prefix sum over a wave with DPP row shifts and row broadcasts
+// (no LDS traffic): shifts by 1, 2, 4, 8 scan each row of 16 lanes, then
+// lane 15 of rows 0 and 2 is added to rows 1 and 3, and lane 31 to rows 2
+// and 3.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Wave-wide minimum and maximum of 64-bit unsigned keys (result in every
+// lane).  Each DPP step moves both 32-bit halves; lanes without a source
+// keep their own value, the identity of min and max.
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v, int ctrl_id) {
+  const int lo = static_cast<int>(v & 0xffffffffull);
+  const int hi = static_cast<int>(v >> 32);
+  int a, b;
+  switch (ctrl_id) {
+    case 0: a = __builtin_amdgcn_update_dpp(lo, lo, 0x111, 0xf, 0xf, false);
+            b = __builtin_amdgcn_update_dpp(hi, hi, 0x111, 0xf, 0xf, false); break;
+    case 1: a = __builtin_amdgcn_update_dpp(lo, lo, 0x112, 0xf, 0xf, false);
+            b = __builtin_amdgcn_update_dpp(hi, hi, 0x112, 0xf, 0xf, false); break;
+    case 2: a = __builtin_amdgcn_update_dpp(lo, lo, 0x114, 0xf, 0xf, false);
+            b = __builtin_amdgcn_update_dpp(hi, hi, 0x114, 0xf, 0xf, false); break;
+    case 3: a = __builtin_amdgcn_update_dpp(lo, lo, 0x118, 0xf, 0xf, false);
+            b = __builtin_amdgcn_update_dpp(hi, hi, 0x118, 0xf, 0xf, false); break;
+    case 4: a = __builtin_amdgcn_update_dpp(lo, lo, 0x142, 0xa, 0xf, false);
+            b = __builtin_amdgcn_update_dpp(hi, hi, 0x142, 0xa, 0xf, false); break;
+    default: a = __builtin_amdgcn_update_dpp(lo, lo, 0x143, 0xc, 0xf, false);
+             b = __builtin_amdgcn_update_dpp(hi, hi, 0x143, 0xc, 0xf, false); break;
+  }
+  return (static_cast<unsigned long long>(static_cast<unsigned>(b)) << 32) |
+         static_cast<unsigned>(a);
+}
+__device__ __forceinline__ void wave_min_max_u64(unsigned long long& mn, unsigned long long& mx) {
+#pragma unroll
+  for (int c = 0; c < 6; ++c) {
+    const unsigned long long a = dpp_u64(mn, c);
+    const unsigned long long b = dpp_u64(mx, c);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  // lane 63 holds the wave result
+  mn = (static_cast<unsigned long long>(static_cast<unsigned>(
+            __builtin_amdgcn_readlane(static_cast<int>(mn >> 32), 63))) << 32) |
+       static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(mn & 0xffffffffull), 63));
+  mx = (static_cast<unsigned long long>(static_cast<unsigned>(
+            __builtin_amdgcn_readlane(static_cast<int>(mx >> 32), 63))) << 32) |
+       static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(mx & 0xffffffffull), 63));
+}
+
+// Wave-wide minimum and maximum of doubles (result in every lane; NaN-free
+// inputs).
+__device__ __forceinline__ void wave_min_max_f64(double& mn, double& mx) {
+#pragma unroll
+  for (int c = 0; c < 6; ++c) {
+    const double a = __longlong_as_double(static_cast<long long>(
+        dpp_u64(static_cast<unsigned long long>(__double_as_longlong(mn)), c)));
+    const double b = __longlong_as_double(static_cast<long long>(
+        dpp_u64(static_cast<unsigned long long>(__double_as_longlong(mx)), c)));
+    mn = fmin(mn, a);
+    mx = fmax(mx, b);
+  }
+  const long long a = __double_as_longlong(mn), b = __double_as_longlong(mx);
+  const int alo = __builtin_amdgcn_readlane(static_cast<int>(a & 0xffffffffll), 63);
+  const int ahi = __builtin_amdgcn_readlane(static_cast<int>(a >> 32), 63);
+  const int blo = __builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffffll), 63);
+  const int bhi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
+  mn = __longlong_as_double((static_cast<long long>(ahi) << 32) | static_cast<unsigned>(alo));
+  mx = __longlong_as_double((static_cast<long long>(bhi) << 32) | static_cast<unsigned>(blo));
+}
+
+// Inverse of f64_order_key.
+__device__ __forceinline__ double f64_from_order_key(unsigned long long k) {
+  const unsigned long long b = (k & 0x8000000000000000ull) ? (k ^ 0x8000000000000000ull) : ~k;
+  return __longlong_as_double(static_cast<long long>(b));
+}
+
 // Exclusive prefix sum over the whole block (blockDim.x a multiple of 64,
 // at most 1024).  `scratch` holds >= 17 values of shared memory.  Returns
 // the exclusive prefix of v and the block total in *total.  Contains

@@ -38,8 +38,6 @@ constexpr int kSpansPerBlock = 4 * kTilesPerWave * 16;
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkLds = 6144;                   // values staged in LDS (48 KB)
 constexpr int kTopkBins = kTopkThreads;          // histogram bins of the threshold search
-constexpr int kItemOverhead = 16;                // work-item fixed cost (64-byte units)
-constexpr int kSpanRoundTrip = 64;               // per extra 32-row load round of a span
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -446,13 +444,7 @@ hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st,
 
 hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int nwaves, int32_t* sel_out,
                        int32_t* nsel_out, hipStream_t st, const KernelEvents* ev) {
-  const int be = c->dtype == kBF16 ? 2 : 4;
-  WorkCost wc;
-  wc.span_base = (2 * c->rank * c->d * be) / 64 + kItemOverhead;
-  wc.span_row = 2 * c->rank * be;  // bytes per padded row
-  wc.span_extra = kSpanRoundTrip;
-  wc.full = (2 * 32 * c->d * be) / 64 + kItemOverhead;
-  wc.summ = (32 * c->d * be + 32 * c->G * 4) / 64 + kItemOverhead;
+  const WorkCost wc = work_cost(c);
   return launch(topk_kernel, dim3(c->B * c->Hkv), dim3(kTopkThreads), 0, st, ev, c->dev.z,
                 c->dev.n_spans, c->dev.n_full, c->dev.span_len, c->dev.tok_pad, c->Hkv, c->G, c->S,
                 c->Sp, static_cast<double>(tau), k_max, c->dev.slogit, c->dev.sel,
