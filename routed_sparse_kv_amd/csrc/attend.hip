@@ -327,16 +327,18 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     double zr[KR];
     {
       int lr[KR], tr[KR];
+      // slots past the last span read span 0 and hold z = -inf (no branch)
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
         const int i = tid + kAttThreads * k;
-        zr[k] = -INFINITY;
-        if (i < ns) {
-          zr[k] = z_u[i];
-          lr[k] = len_b[i];
-          tr[k] = tp_b[i];
-        }
+        const int ic = i < ns ? i : 0;
+        zr[k] = z_u[ic];
+        lr[k] = len_b[ic];
+        tr[k] = tp_b[ic];
       }
+#pragma unroll
+      for (int k = 0; k < KR; ++k)
+        if (tid + kAttThreads * k >= ns) zr[k] = -INFINITY;
       // wave w of the unit takes chunk w before the ranges exist: its loads
       // are in flight while the workgroup selects.  Issued unconditionally
       // (a wave without a chunk re-reads the last one and drops it), so
@@ -344,27 +346,12 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       issue_full(min(wglob, max(nFI, 1) - 1) * kChunk, pbuf);
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
-        const int i = tid + kAttThreads * k;
-        if (i < ns) {
-          L.len[pidx(i)] = lr[k];
-          L.tpad[pidx(i)] = tr[k];
-        }
+        const int i = tid + kAttThreads * k;  // < kFuseSpans: padding slots are never read
+        L.len[pidx(i)] = lr[k];
+        L.tpad[pidx(i)] = tr[k];
       }
       for (int w = tid; w < kFuseSpans / 32; w += kAttThreads) L.mask[w] = 0u;
     }
-    // candidates z > tau: count and value range (padding slots hold -inf)
-    int c_loc = 0;
-    double lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < KR; ++k) {
-      if (zr[k] > tau) {
-        ++c_loc;
-        lo = fmin(lo, zr[k]);
-        hi = fmax(hi, zr[k]);
-      }
-    }
-    const int n_cand = block4_sum(c_loc, L, 0);
-    block4_min_max_f64(lo, hi, L);
     // Position in index order of this thread's flagged slots: ballots per
     // slot row, wave totals in LDS, one barrier.  Returns the count before
     // slot k of this thread through base[k] and the total.
@@ -393,14 +380,83 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       *total = run;
       __syncthreads();
     };
+    // Bin bs holds the k-th largest and cb <= 256 values: rank them exactly,
+    // (z descending, index ascending); the one of rank rem - 1 is the last
+    // kept entry (z*, j*).
+    auto rank_bin = [&](const int* bin, int bs, int cb, int rem, double& zs_, int& js_) {
+      __syncthreads();
+      if (tid == 0) L.s_above = 0;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < KR; ++k) {
+        if (bin[k] == bs) {
+          const int slot = atomicAdd(&L.s_above, 1);
+          if (slot < kAttThreads) {
+            L.cand_z[slot] = zr[k];
+            L.cand_j[slot] = tid + kAttThreads * k;
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < cb) {
+        const double v = L.cand_z[tid];
+        const int j = L.cand_j[tid];
+        int rank = 0;
+        for (int y = 0; y < cb; ++y) {
+          const double vy = L.cand_z[y];
+          rank += (vy > v || (vy == v && L.cand_j[y] < j)) ? 1 : 0;
+        }
+        if (rank == rem - 1) {
+          L.s_zs = v;
+          L.s_js = j;
+        }
+      }
+      __syncthreads();
+      zs_ = L.s_zs;
+      js_ = L.s_js;
+    };
+    // the bin holding the rem-th largest among the 1024 counts c (thread t
+    // holds bins 1023 - 4t .. 1020 - 4t, highest first): sets s_bin,
+    // s_above (values in higher bins) and s_cnt
+    auto find_bin = [&](const int* c4, int rem, int* total) {
+      const int cs = c4[0] + c4[1] + c4[2] + c4[3];
+      const int above = block4_excl(cs, L, 1, total);
+      if (above < rem && rem <= above + cs) {
+        int a2 = above;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (a2 < rem && rem <= a2 + c4[x]) {
+            L.s_bin = 1023 - 4 * tid - x;
+            L.s_above = a2;
+            L.s_cnt = c4[x];
+          }
+          a2 += c4[x];
+        }
+      }
+      __syncthreads();
+    };
+    // candidates z > tau: count and value range (padding slots hold -inf)
+    int c_loc = 0;
+    double lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      if (zr[k] > tau) {
+        ++c_loc;
+        lo = fmin(lo, zr[k]);
+        hi = fmax(hi, zr[k]);
+      }
+    }
+    const int n_cand = block4_sum(c_loc, L, 0);
+    block4_min_max_f64(lo, hi, L);
     double zs = INFINITY;  // pick: z > tau && (z > zs || (z == zs && j <= js))
     int js = -1;
     if (k_max > 0 && n_cand > 0) {
       if (n_cand <= k_max) {
-        zs = lo;
-        js = 0x7fffffff;
+        zs = -INFINITY;  // every candidate
       } else {
         int rem = k_max;  // entries still to take from [lo, hi]
+        // narrow [lo, hi] with 1024-bin histograms of the values in it until
+        // the bin holding the rem-th largest has few enough values to rank
         for (int round = 0; round < 256; ++round) {
           if (lo == hi) {
             // rem lowest indices among the values equal to lo
@@ -419,19 +475,18 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           }
           // 1024 bins over [lo, hi]: any map that is monotone in z gives an
           // exact answer; fp32 arithmetic is used unless the range is too
-          // small for it, where fp64 division takes over.
+          // small for it, where fp64 division takes over (a uniform branch,
+          // so only one of the two formulas is executed)
           const double w = hi - lo;
           const float wf = static_cast<float>(w);
-          const bool f32ok = wf > 1e-30f;  // uniform across the workgroup
-          const float sf = 1024.f / wf;
-          // bin of each owned slot (-1 outside [lo, hi]); the precision is a
-          // uniform branch, so only one of the two formulas is executed
-          int bin[KR];
+          const bool f32ok = wf > 1e-30f;
+          const float sr = 1024.f / wf;
+          int bin[KR];  // -1 outside [lo, hi]
           if (f32ok) {
 #pragma unroll
             for (int k = 0; k < KR; ++k)
               bin[k] = (zr[k] >= lo && zr[k] <= hi)
-                           ? min(1023, static_cast<int>(static_cast<float>(zr[k] - lo) * sf))
+                           ? min(1023, static_cast<int>(static_cast<float>(zr[k] - lo) * sr))
                            : -1;
           } else {
 #pragma unroll
@@ -441,68 +496,20 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                            : -1;
           }
           for (int x = tid; x < 1024; x += kAttThreads) L.hist[x] = 0;
-          if (tid == 0) L.s_cnt = 0;
           __syncthreads();
 #pragma unroll
           for (int k = 0; k < KR; ++k)
             if (bin[k] >= 0) atomicAdd(&L.hist[bin[k]], 1);
           __syncthreads();
-          // thread t holds bins 1023 - 4t .. 1020 - 4t, highest first
-          int c4[4], cs = 0;
+          int c4[4], tot;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            c4[x] = L.hist[1023 - 4 * tid - x];
-            cs += c4[x];
-          }
-          int tot;
-          const int above = block4_excl(cs, L, 1, &tot);
-          if (above < rem && rem <= above + cs) {
-            int a2 = above;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              if (a2 < rem && rem <= a2 + c4[x]) {
-                L.s_bin = 1023 - 4 * tid - x;
-                L.s_above = a2;
-                L.s_cnt = c4[x];
-              }
-              a2 += c4[x];
-            }
-          }
-          __syncthreads();
+          for (int x = 0; x < 4; ++x) c4[x] = L.hist[1023 - 4 * tid - x];
+          find_bin(c4, rem, &tot);
           const int bs = L.s_bin;
           rem -= L.s_above;
           const int cb = L.s_cnt;
           if (cb <= kAttThreads) {
-            // few values left: rank them exactly, (z descending, index
-            // ascending); the one of rank rem - 1 is the last kept entry
-            __syncthreads();
-            if (tid == 0) L.s_above = 0;
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < KR; ++k) {
-              if (bin[k] == bs) {
-                const int slot = atomicAdd(&L.s_above, 1);
-                L.cand_z[slot] = zr[k];
-                L.cand_j[slot] = tid + kAttThreads * k;
-              }
-            }
-            __syncthreads();
-            if (tid < cb) {
-              const double v = L.cand_z[tid];
-              const int j = L.cand_j[tid];
-              int rank = 0;
-              for (int y = 0; y < cb; ++y) {
-                const double vy = L.cand_z[y];
-                rank += (vy > v || (vy == v && L.cand_j[y] < j)) ? 1 : 0;
-              }
-              if (rank == rem - 1) {
-                L.s_zs = v;
-                L.s_js = j;
-              }
-            }
-            __syncthreads();
-            zs = L.s_zs;
-            js = L.s_js;
+            rank_bin(bin, bs, cb, rem, zs, js);
             break;
           }
           // many values left: narrow to their range and repeat
@@ -520,50 +527,64 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
       }
     }
-    // compaction in index order, with exclusive work-cost prefixes: per
-    // slot row, a ballot and a DPP scan of the costs within each wave, wave
-    // totals in LDS, one barrier
-    auto picked = [&](int k) {
-      const int i = tid + kAttThreads * k;
-      return zr[k] > tau && (zr[k] > zs || (zr[k] == zs && i <= js));
-    };
-    int cpre[KR];  // exclusive cost prefix of slot k within its wave row
+    // compaction in index order: per slot row a ballot; lane k of each
+    // wave turns the row counts into the wave's base position for row k
+    unsigned pm = 0u;  // picked slots of this thread
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
-      const bool f = picked(k);
+      const int i = tid + kAttThreads * k;
+      if (zr[k] > tau && (zr[k] > zs || (zr[k] == zs && i <= js))) pm |= 1u << k;
+    }
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      const unsigned long long bal = __ballot((pm >> k) & 1u);
+      if (lane == 0) L.rowcnt[k][wave] = __popcll(bal);
+    }
+    __syncthreads();
+    int rbase = 0;  // lane k < KR: slots of rows < k plus earlier waves of row k
+    {
+      int rowtot = 0, before_w = 0;
+      if (lane < KR) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int c = L.rowcnt[lane][w];
+          rowtot += c;
+          before_w += w < wave ? c : 0;
+        }
+      }
+      const int incl = wave_incl_scan_dpp(rowtot);
+      rbase = incl - rowtot + before_w;
+      nsel = __builtin_amdgcn_readlane(incl, KR - 1);
+    }
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      const bool f = (pm >> k) & 1u;
       const unsigned long long bal = __ballot(f);
-      const int c = f ? wc.span(L.len[pidx(tid + kAttThreads * k)]) : 0;
-      const int incl = wave_incl_scan_dpp(c);
-      cpre[k] = incl - c;
-      if (lane == 63) {
-        L.rowcnt[k][wave] = __popcll(bal);
-        L.rowcost[k][wave] = incl;
+      const int base = __builtin_amdgcn_readlane(rbase, k);
+      if (f) {
+        const int i = tid + kAttThreads * k;
+        L.elist[base + __popcll(bal & below)].x = i;
+        atomicOr(&L.mask[i >> 5], 1u << (i & 31));
       }
     }
     __syncthreads();
-    int e_cost = 0;
-    nsel = 0;
+    // exclusive work-cost prefix over the list (4 consecutive entries per
+    // thread; nsel <= 1024)
+    int e_cost;
+    {
+      const int q0 = 4 * tid;
+      int c4[4], csum = 0;
 #pragma unroll
-    for (int k = 0; k < KR; ++k) {
-      int cw = 0, crow = 0, kw = 0, krow = 0;
+      for (int x = 0; x < 4; ++x) {
+        c4[x] = q0 + x < nsel ? wc.span(L.len[pidx(L.elist[q0 + x].x)]) : 0;
+        csum += c4[x];
+      }
+      int pre = block4_excl(csum, L, 2, &e_cost);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int c = L.rowcnt[k][w], q = L.rowcost[k][w];
-        cw += w < wave ? c : 0;
-        crow += c;
-        kw += w < wave ? q : 0;
-        krow += q;
+      for (int x = 0; x < 4; ++x) {
+        if (q0 + x < nsel) L.elist[q0 + x].y = pre;
+        pre += c4[x];
       }
-      const bool f = picked(k);
-      const unsigned long long bal = __ballot(f);
-      if (f) {
-        const int i = tid + kAttThreads * k;
-        const int pos = nsel + cw + __popcll(bal & below);
-        L.elist[pos] = make_int2(i, e_cost + kw + cpre[k]);
-        atomicOr(&L.mask[i >> 5], 1u << (i & 31));
-      }
-      nsel += crow;
-      e_cost += krow;
     }
     __syncthreads();
     if (s == 0) {
@@ -1109,6 +1130,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   const int b = u / Hkv;
   const int h = u - b * Hkv;
   const int tid = threadIdx.x;
+
   const size_t ps = static_cast<size_t>(G) * (d + 2);
   const float* P = part + static_cast<size_t>(u) * nsplit_max * ps + static_cast<size_t>(g) * (d + 2);
   __shared__ float w[kMaxSplitMfma > 2048 ? kMaxSplitMfma : 2048];

@@ -42,14 +42,46 @@ constexpr int kTopkBins = kTopkThreads;          // histogram bins of the thresh
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// bf16 summaries: MFMA logits, fp64 VALU z (see the file comment).
+// bf16 summaries: MFMA logits, fp64 VALU z (see the file comment).  The
+// summary tiles are loaded by route_load_bf16 before rho is formed.
 template <int D>
-__device__ __forceinline__ void route_tiles_bf16(const uint16_t* __restrict__ q,
-                                                 const uint16_t* __restrict__ summ,
-                                                 const float* __restrict__ log_len, int b,
-                                                 int u, int h, int Hkv, int ns, int S, int G,
-                                                 float alpha, float inv_sqrt_d,
-                                                 const double* rho, double* __restrict__ z_out,
+struct RouteTiles {
+  bf16x8 sa[kTilesPerWave][D / 32];
+  bf16x8 qb[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void route_load_bf16(const uint16_t* __restrict__ q,
+                                                const uint16_t* __restrict__ summ, int b, int u,
+                                                int h, int Hkv, int ns, int S, int G,
+                                                RouteTiles<D>& rt) {
+  constexpr int KK = D / 32;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int g16 = lane & 15;
+  const int grp = lane >> 4;
+  const bool head_ok = g16 < G;
+  const int jw = blockIdx.x * kSpansPerBlock + wave * kTilesPerWave * 16;
+#pragma unroll
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    const int j = jw + 16 * t + g16;  // row of the A operand held by this lane
+    const uint16_t* row = summ + (static_cast<size_t>(u) * S + (j < ns ? j : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      rt.sa[t][kk] = *reinterpret_cast<const bf16x8*>(row + 32 * kk + 8 * grp);
+  }
+  const uint16_t* qp = q + (static_cast<size_t>(b) * Hkv * G + static_cast<size_t>(h) * G +
+                            (head_ok ? g16 : 0)) * D;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    rt.qb[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk + 8 * grp);
+}
+
+template <int D>
+__device__ __forceinline__ void route_tiles_bf16(RouteTiles<D>& rt, const float* __restrict__ log_len,
+                                                 int b, int u, int ns, int S, int G, float alpha,
+                                                 float inv_sqrt_d, const double* rho,
+                                                 double* __restrict__ z_out,
                                                  float* __restrict__ slogit_u) {
   constexpr int KK = D / 32;
   const int lane = threadIdx.x & (kWave - 1);
@@ -57,40 +89,25 @@ __device__ __forceinline__ void route_tiles_bf16(const uint16_t* __restrict__ q,
   const int g16 = lane & 15;
   const int grp = lane >> 4;
   const bool head_ok = g16 < G;
-  bf16x8 qb[KK];
-  {
-    const uint16_t* qp = q + (static_cast<size_t>(b) * Hkv * G + static_cast<size_t>(h) * G +
-                              (head_ok ? g16 : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qb[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk + 8 * grp);
-      if (!head_ok) qb[kk] = bf16x8{};
-    }
-  }
   const int jw = blockIdx.x * kSpansPerBlock + wave * kTilesPerWave * 16;
-  bf16x8 sa[kTilesPerWave][KK];
 #pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int j = jw + 16 * t + g16;  // row of the A operand held by this lane
-    const uint16_t* row = summ + (static_cast<size_t>(u) * S + (j < ns ? j : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      sa[t][kk] = *reinterpret_cast<const bf16x8*>(row + 32 * kk + 8 * grp);
-      if (j >= ns) sa[t][kk] = bf16x8{};
-    }
-  }
+  for (int kk = 0; kk < KK; ++kk)
+    if (!head_ok) rt.qb[kk] = bf16x8{};
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
     const int j0 = jw + 16 * t;
     if (j0 >= ns) break;
+    if (j0 + g16 >= ns)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) rt.sa[t][kk] = bf16x8{};
     f32x4 lg = {0.f, 0.f, 0.f, 0.f};
     double zp = 0.0;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[t][kk], qb[kk], lg, 0, 0, 0);
+      lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rt.sa[t][kk], rt.qb[kk], lg, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        zp += rho[32 * kk + 8 * grp + e] * static_cast<double>(static_cast<float>(sa[t][kk][e]));
+        zp += rho[32 * kk + 8 * grp + e] * static_cast<double>(static_cast<float>(rt.sa[t][kk][e]));
     }
     zp += __shfl_xor(zp, 16, kWave);
     zp += __shfl_xor(zp, 32, kWave);
@@ -170,6 +187,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   if (static_cast<int>(blockIdx.x) * kSpansPerBlock >= ns) return;
   float* slogit_u = slogit + static_cast<size_t>(u) * Sp * G;
 
+  // summary tiles first: their loads overlap forming rho
+  [[maybe_unused]] RouteTiles<D> rt;
+  if constexpr (DT == kBF16) route_load_bf16<D>(q, summ, b, u, h, Hkv, ns, S, G, rt);
+
   __shared__ double qbar[D];
   __shared__ double rho[D];
   __shared__ float qh[kMaxG][D];
@@ -197,8 +218,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
   __syncthreads();
   if constexpr (DT == kBF16) {
-    route_tiles_bf16<D>(q, summ, log_len, b, u, h, Hkv, ns, S, G, alpha, inv_sqrt_d, rho,
-                        z_all, slogit_u);
+    route_tiles_bf16<D>(rt, log_len, b, u, ns, S, G, alpha, inv_sqrt_d, rho, z_all, slogit_u);
   } else {
     route_spans_f32<D>(summ, log_len, b, u, ns, S, G, alpha, inv_sqrt_d, rho, qh, z_all,
                        slogit_u);
