@@ -300,7 +300,7 @@ def main():
                    "anchor_frac": cfg["anchor_frac"], "replicas": R},
         "roofline": {"bound": "hbm", "achieved": att_gbps, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": att_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic, "kernel": "attend_kernel",
+                     "traffic": traffic, "kernel": "attend_mfma_kernel",
                      "algorithmic_bytes_per_launch": att_bytes_avg,
                      "mean_launch_ms": kern["attend_ms"]},
         "step_algorithmic_bytes": step_bytes_avg,

@@ -89,7 +89,8 @@ void free_cache(rskv_cache* c) {
   if (c->last_stream != nullptr) (void)hipStreamSynchronize(c->last_stream);
   (void)hipDeviceSynchronize();
   for (void* p : c->allocs) (void)hipFree(p);
-  for (hipEvent_t e : c->prof.pending) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->prof.pending)
+    if (e != nullptr) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof.pool) (void)hipEventDestroy(e);
   c->magic = 0;
   delete c;
@@ -540,10 +541,11 @@ int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, flo
     const bool fused = rskv::attend_fuses_topk(c, k_max);
     const rskv::SelectArgs sa{tau, k_max, sel, n_sel};
     if (fused) {
-      // the attention kernel selects; the top-k slot of the profile stays empty
+      // the attention kernel selects: the top-k slot of the profile stays at 0
       if (prof) {
-        RSKV_HIP(hipEventRecord(ev[1].start, st), "event record");
-        RSKV_HIP(hipEventRecord(ev[1].stop, st), "event record");
+        c->prof.pool.push_back(ev[1].start);
+        c->prof.pool.push_back(ev[1].stop);
+        ev[1] = rskv::KernelEvents{};
       }
     } else {
       RSKV_HIP(rskv::launch_topk(c, tau, k_max, nwaves, sel, n_sel, st, prof ? &ev[1] : nullptr),
@@ -741,7 +743,8 @@ void rskv_cache_destroy(rskv_cache* c) {
 
 int rskv_profile_enable(rskv_cache* c, int32_t on) {
   if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
-  for (hipEvent_t e : c->prof.pending) c->prof.pool.push_back(e);
+  for (hipEvent_t e : c->prof.pending)
+    if (e != nullptr) c->prof.pool.push_back(e);
   c->prof.pending.clear();
   c->prof.on = on != 0;
   c->prof.steps = 0;
@@ -757,6 +760,7 @@ int rskv_profile_read(rskv_cache* c, rskv_profile* p) {
   for (size_t i = 0; i + kEv <= pr.pending.size(); i += kEv) {
     RSKV_HIP(hipEventSynchronize(pr.pending[i + kEv - 1]), "event sync");
     for (int k = 0; k < rskv::kProfileKernels; ++k) {
+      if (pr.pending[i + 2 * k] == nullptr) continue;  // kernel not launched this step
       float ms = 0.f;
       RSKV_HIP(hipEventElapsedTime(&ms, pr.pending[i + 2 * k], pr.pending[i + 2 * k + 1]),
                "elapsed");
@@ -764,7 +768,8 @@ int rskv_profile_read(rskv_cache* c, rskv_profile* p) {
     }
     pr.steps += 1;
   }
-  for (hipEvent_t e : pr.pending) pr.pool.push_back(e);
+  for (hipEvent_t e : pr.pending)
+    if (e != nullptr) pr.pool.push_back(e);
   pr.pending.clear();
   p->steps = pr.steps;
   p->route_ms = pr.ms[0];

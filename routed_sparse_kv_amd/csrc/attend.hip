@@ -38,6 +38,7 @@ namespace rskv {
 namespace {
 
 constexpr int kAttThreads = 256;
+constexpr int kXcds = 8;  // accelerator dies of the device
 constexpr int kChunk = 32;
 constexpr int kMaxG = 8;
 constexpr int kMaxRank = 32;
@@ -143,6 +144,7 @@ __device__ __forceinline__ int pidx(int i) { return i + (i >> 4); }
 
 struct FusedLds {
   union {
+    double z[kFusePad];        // selection: routing scores (-inf past the last span)
     int2 elist[kFuseSel];      // item loop: {span, exclusive work-cost prefix}
     float merge[4 * 128 * 16]; // end: per-wave out^T
   };
@@ -227,8 +229,16 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g16 = lane & 15;
   const int grp = lane >> 4;
-  const int s = blockIdx.x;
-  const int u = blockIdx.y;
+  // Workgroups reach the XCDs round-robin in linear id order; when the units
+  // divide evenly, all workgroups of a unit go to one XCD, whose L2 then
+  // serves the unit's shared reads (scores, span tables, queries) once.
+  int s = blockIdx.x, u = blockIdx.y;
+  if (gridDim.y % kXcds == 0) {
+    const int L = blockIdx.x + gridDim.x * blockIdx.y;
+    const int m = L / kXcds;
+    u = (L % kXcds) * (gridDim.y / kXcds) + m / gridDim.x;
+    s = m % gridDim.x;
+  }
   const int b = u / Hkv;
   const int h = u - b * Hkv;
   const bool head_ok = g16 < G;
@@ -310,9 +320,23 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   __shared__ __align__(16) unsigned char lds_raw[FUSED ? sizeof(FusedLds) : 4 * (2 * 16 + D * 16) * 4];
   int nsel, i0, i1;
   int fb = 0;  // first full-resolution chunk that belongs to the item ranges
+  // Fused variant: every full-resolution chunk is assigned statically (wave
+  // w of the unit takes chunks w, w + W, ...) and processed between the
+  // selection steps, each step computing the chunk whose loads are in
+  // flight and issuing the next; the cost-balanced ranges cover the
+  // expanded spans and the summary chunks.
   const int wglob = 4 * s + wave;
-  const bool pre = FUSED && wglob < nFI;
+  const int Wu = 4 * static_cast<int>(gridDim.x);
+  const int nfr = FUSED && wglob < nFI ? (nFI - 1 - wglob) / Wu + 1 : 0;
+  int fr = 0;  // next of this wave's chunks to compute
   u32x4 pbuf[2 * KK + CB];
+  auto f_step = [&]() {
+    if (fr < nfr) {
+      compute_full((wglob + fr * Wu) * kChunk, pbuf);
+      ++fr;
+      if (fr < nfr) issue_full((wglob + fr * Wu) * kChunk, pbuf);
+    }
+  };
   if constexpr (FUSED) {
     // Selection of the unit by the same rule as the top-k kernel (the kept
     // set is fixed by its last entry (z*, j*)), compaction with work costs,
@@ -324,8 +348,14 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int32_t* len_b = span_len + static_cast<size_t>(b) * S;
     const int32_t* tp_b = tok_pad + static_cast<size_t>(b) * (S + 1);
     constexpr int KR = kFuseSpans / kAttThreads;
-    double zr[KR];
+    // a pass loads this thread's scores from LDS (16 batched reads); they
+    // are dead between passes, where the chunk computations run
+    auto load_z = [&](double* zr) {
+#pragma unroll
+      for (int k = 0; k < KR; ++k) zr[k] = L.z[pidx(tid + kAttThreads * k)];
+    };
     {
+      double zr[KR];
       int lr[KR], tr[KR];
       // slots past the last span read span 0 and hold z = -inf (no branch)
 #pragma unroll
@@ -339,14 +369,15 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int k = 0; k < KR; ++k)
         if (tid + kAttThreads * k >= ns) zr[k] = -INFINITY;
-      // wave w of the unit takes chunk w before the ranges exist: its loads
-      // are in flight while the workgroup selects.  Issued unconditionally
-      // (a wave without a chunk re-reads the last one and drops it), so
-      // that waits for the values above count exactly these loads.
+      // the first chunk of this wave is in flight while the workgroup
+      // selects; issued unconditionally (a wave without chunks re-reads the
+      // last one and drops it), so that waits for the values above count
+      // exactly these loads
       issue_full(min(wglob, max(nFI, 1) - 1) * kChunk, pbuf);
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
-        const int i = tid + kAttThreads * k;  // < kFuseSpans: padding slots are never read
+        const int i = tid + kAttThreads * k;  // < kFuseSpans
+        L.z[pidx(i)] = zr[k];
         L.len[pidx(i)] = lr[k];
         L.tpad[pidx(i)] = tr[k];
       }
@@ -383,7 +414,8 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // Bin bs holds the k-th largest and cb <= 256 values: rank them exactly,
     // (z descending, index ascending); the one of rank rem - 1 is the last
     // kept entry (z*, j*).
-    auto rank_bin = [&](const int* bin, int bs, int cb, int rem, double& zs_, int& js_) {
+    auto rank_bin = [&](const double* zr, const int* bin, int bs, int cb, int rem, double& zs_,
+                        int& js_) {
       __syncthreads();
       if (tid == 0) L.s_above = 0;
       __syncthreads();
@@ -435,19 +467,25 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
       __syncthreads();
     };
-    // candidates z > tau: count and value range (padding slots hold -inf)
+    // candidates z > tau: count and value range (padding slots hold -inf;
+    // each thread reads back the score slots it wrote)
     int c_loc = 0;
     double lo = INFINITY, hi = -INFINITY;
+    {
+      double zr[KR];
+      load_z(zr);
 #pragma unroll
-    for (int k = 0; k < KR; ++k) {
-      if (zr[k] > tau) {
-        ++c_loc;
-        lo = fmin(lo, zr[k]);
-        hi = fmax(hi, zr[k]);
+      for (int k = 0; k < KR; ++k) {
+        if (zr[k] > tau) {
+          ++c_loc;
+          lo = fmin(lo, zr[k]);
+          hi = fmax(hi, zr[k]);
+        }
       }
     }
     const int n_cand = block4_sum(c_loc, L, 0);
     block4_min_max_f64(lo, hi, L);
+    f_step();
     double zs = INFINITY;  // pick: z > tau && (z > zs || (z == zs && j <= js))
     int js = -1;
     if (k_max > 0 && n_cand > 0) {
@@ -458,6 +496,8 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         // narrow [lo, hi] with 1024-bin histograms of the values in it until
         // the bin holding the rem-th largest has few enough values to rank
         for (int round = 0; round < 256; ++round) {
+          double zr[KR];
+          load_z(zr);
           if (lo == hi) {
             // rem lowest indices among the values equal to lo
             bool f[KR];
@@ -509,7 +549,7 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           rem -= L.s_above;
           const int cb = L.s_cnt;
           if (cb <= kAttThreads) {
-            rank_bin(bin, bs, cb, rem, zs, js);
+            rank_bin(zr, bin, bs, cb, rem, zs, js);
             break;
           }
           // many values left: narrow to their range and repeat
@@ -527,13 +567,18 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
       }
     }
+    f_step();
     // compaction in index order: per slot row a ballot; lane k of each
     // wave turns the row counts into the wave's base position for row k
     unsigned pm = 0u;  // picked slots of this thread
+    {
+      double zr[KR];
+      load_z(zr);
 #pragma unroll
-    for (int k = 0; k < KR; ++k) {
-      const int i = tid + kAttThreads * k;
-      if (zr[k] > tau && (zr[k] > zs || (zr[k] == zs && i <= js))) pm |= 1u << k;
+      for (int k = 0; k < KR; ++k) {
+        const int i = tid + kAttThreads * k;
+        if (zr[k] > tau && (zr[k] > zs || (zr[k] == zs && i <= js))) pm |= 1u << k;
+      }
     }
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
@@ -593,13 +638,14 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           sel_out[static_cast<size_t>(u) * k_max + i] = i < nsel ? L.elist[i].x : -1;
       if (nsel_out != nullptr && tid == 0) nsel_out[u] = nsel;
     }
+    f_step();
     // Ranges of the remaining items [expanded spans | chunks fb.. | summary
     // chunks]: item i goes to wave floor((2 P_i + c_i) W / (2 C)), so the
     // first item of wave w is the first i with (2 P_i + c_i) W >= 2 C w;
     // each thread tests its items against the five boundaries of this
     // workgroup.
     const long long W = 4ll * gridDim.x;
-    fb = static_cast<int>(min(static_cast<long long>(nFI), W));
+    fb = nFI;  // every chunk is assigned statically
     {
       const int nFP = nFI - fb;
       const int nSI = (ns + kChunk - 1) / kChunk;
@@ -810,7 +856,7 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   };
 
-  if (pre) compute_full(wglob * kChunk, pbuf);
+  while (fr < nfr) f_step();
 
   // Item loop: all loads of an item are issued before any of them is
   // waited for.
