@@ -38,6 +38,12 @@ the rest of the text supports):
       extra "f64" storage mode (no rounding at all) exists for the pins.
   R8  decode-time appends join the trailing full-resolution run before the
       step's attention and are not routed.
+  R9  streaming segmentation: an appended token is an anchor iff its
+      surprisal exceeds the sequence's threshold theta, the smallest
+      surprisal among the prefill anchors (+inf without anchors); the
+      full-resolution run after the previous anchor then becomes a span
+      (closed with the build's summary, mean, ln|S| and factors).  A token
+      appended without a surprisal value counts as surprisal 0.
 """
 from __future__ import annotations
 
@@ -48,7 +54,7 @@ import numpy as np
 
 __all__ = [
     "n_anchors", "select_anchors", "segment", "span_summary", "span_value_mean",
-    "truncated_svd", "round_stored", "from_stored", "build_cache", "append_kv",
+    "truncated_svd", "round_stored", "from_stored", "build_cache", "append_kv", "close_span",
     "route_unit", "attend_unit", "decode_step", "AMBIGUITY_BAND",
 ]
 
@@ -190,20 +196,26 @@ def truncated_svd(X: np.ndarray, r: int):
 
 
 def build_cache(H, K, V, rank: int, anchor_frac: float, dtype: str,
-                Hq: Optional[int] = None, tail_capacity: int = 0) -> dict:
+                Hq: Optional[int] = None, tail_capacity: int = 0,
+                n_anchor: Optional[int] = None) -> dict:
     """Segment, summarise and factor a batch of prefilled contexts.
 
     H: [B][T] surprisal (fp32 values); K, V: [B][Hkv][T][d] fp64 values of the
     stored inputs.  Returns the canonical cache dictionary: every stored
     array as fp64 values already rounded to ``dtype`` (R7), zero-padded to
-    the batch maxima, with per-sequence counts.
+    the batch maxima, with per-sequence counts.  ``n_anchor`` replaces
+    floor(p*T) when given.  For streaming segmentation (R9) the cache also
+    keeps the surprisal of every full-resolution row (HF), the anchor
+    threshold of each sequence (theta: the smallest anchor surprisal, +inf
+    without anchors) and the full-resolution row of its last anchor (la, -1
+    without anchors).
     """
     H = np.asarray(H, np.float32)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
     B, T = H.shape
     Hkv, d = K.shape[1], K.shape[3]
-    n_a = n_anchors(T, anchor_frac)
+    n_a = n_anchors(T, anchor_frac) if n_anchor is None else int(n_anchor)
     segs = [segment(H[b], n_a) for b in range(B)]
     n_s = np.array([len(sg["span_len"]) for sg in segs], dtype=np.int64)
     n_F = np.array([len(sg["fr_pos"]) for sg in segs], dtype=np.int64)
@@ -223,12 +235,18 @@ def build_cache(H, K, V, rank: int, anchor_frac: float, dtype: str,
              ell=np.zeros((B, S)),
              KF=np.zeros((B, Hkv, F, d)), VF=np.zeros((B, Hkv, F, d)),
              AK=np.zeros((B, Hkv, N, rank)), AV=np.zeros((B, Hkv, N, rank)),
-             BK=np.zeros((B, Hkv, S, rank, d)), BV=np.zeros((B, Hkv, S, rank, d)))
+             BK=np.zeros((B, Hkv, S, rank, d)), BV=np.zeros((B, Hkv, S, rank, d)),
+             HF=np.zeros((B, F)), theta=np.full(B, np.inf), la=np.full(B, -1, np.int64))
     for b, sg in enumerate(segs):
         ns, nf = int(n_s[b]), int(n_F[b])
         c["span_start"][b, :ns] = sg["span_start"]
         c["span_len"][b, :ns] = sg["span_len"]
         c["fr_pos"][b, :nf] = sg["fr_pos"]
+        c["HF"][b, :nf] = H[b, sg["fr_pos"]].astype(np.float64)
+        anchors = np.flatnonzero(sg["span_id"] == -1)
+        if len(anchors):
+            c["theta"][b] = float(H[b, anchors].min())
+            c["la"][b] = int(np.searchsorted(sg["fr_pos"], anchors[-1]))
         # ln|S| is kept in fp32 (R7); the oracle-only "f64" mode keeps fp64
         ell = np.log(sg["span_len"].astype(np.float64))
         c["ell"][b, :ns] = ell if dtype == "f64" else ell.astype(np.float32)
@@ -249,20 +267,90 @@ def build_cache(H, K, V, rank: int, anchor_frac: float, dtype: str,
     return c
 
 
-def append_kv(cache: dict, k: np.ndarray, v: np.ndarray) -> None:
-    """Append one decoded token per sequence to the trailing full-resolution
-    run (R8).  k, v: [B][Hkv][d] fp64 values of the stored token."""
+def _grow(cache: dict, key: str, axis: int, size: int) -> None:
+    """Zero-pad cache[key] along ``axis`` to at least ``size`` entries."""
+    a = cache[key]
+    if a.shape[axis] >= size:
+        return
+    pad = [(0, 0)] * a.ndim
+    pad[axis] = (0, size - a.shape[axis])
+    cache[key] = np.pad(a, pad)
+
+
+def close_span(cache: dict, b: int) -> None:
+    """Streaming segmentation (R9): turn the run of full-resolution rows
+    after the last anchor of sequence b into a new span, exactly as the
+    build would for a run with an anchor on both sides (Metodologia 1 and
+    2): summary, value mean, ln|S| and factors from the stored rows, which
+    then leave the full-resolution set.  No-op when there is no anchor or
+    the run is empty."""
+    la, nf = int(cache["la"][b]), int(cache["n_F"][b])
+    ln = nf - la - 1
+    if la < 0 or ln <= 0:
+        return
+    dtype, rank = cache["dtype"], cache["rank"]
+    j, off = int(cache["n_s"][b]), int(cache["nt"][b])
+    _grow(cache, "span_start", 1, j + 1)
+    _grow(cache, "span_len", 1, j + 1)
+    _grow(cache, "ell", 1, j + 1)
+    for key in ("s", "vbar", "BK", "BV"):
+        _grow(cache, key, 2, j + 1)
+    for key in ("AK", "AV"):
+        _grow(cache, key, 2, off + ln)
+    rows = slice(la + 1, nf)
+    st = int(cache["fr_pos"][b, la + 1])
+    cache["span_start"][b, j] = st
+    cache["span_len"][b, j] = ln
+    ell = math.log(ln)
+    cache["ell"][b, j] = ell if dtype == "f64" else float(np.float32(ell))
+    for h in range(cache["Hkv"]):
+        ks, vs = cache["KF"][b, h, rows], cache["VF"][b, h, rows]
+        cache["s"][b, h, j] = round_stored(span_summary(cache["HF"][b, rows], ks), dtype)
+        cache["vbar"][b, h, j] = round_stored(span_value_mean(vs), dtype)
+        for kind, X in (("K", ks), ("V", vs)):
+            A, W = truncated_svd(X, rank)
+            cache["A" + kind][b, h, off:off + ln] = round_stored(A, dtype)
+            cache["B" + kind][b, h, j] = round_stored(W, dtype)
+    T = cache["T"]
+    if st < T:
+        cache["span_id"][b, st:min(st + ln, T)] = j
+    cache["n_s"][b] = j + 1
+    cache["nt"][b] = off + ln
+    cache["KF"][b, :, rows] = 0.0
+    cache["VF"][b, :, rows] = 0.0
+    cache["HF"][b, rows] = 0.0
+    cache["fr_pos"][b, rows] = -1
+    cache["n_F"][b] = la + 1
+
+
+def append_kv(cache: dict, k: np.ndarray, v: np.ndarray, h: Optional[np.ndarray] = None) -> None:
+    """Append one decoded token per sequence (R8).  k, v: [B][Hkv][d] fp64
+    values of the stored token; h: [B] its surprisal (fp32 values) or None.
+
+    Streaming segmentation (R9): a token whose surprisal exceeds the
+    sequence's anchor threshold (strictly; an earlier anchor keeps ties) is
+    a new anchor; the full-resolution run before it, after the previous
+    anchor, is first closed into a span (close_span).  A token without a
+    surprisal is never an anchor and weighs 0 in a later span summary.
+    """
     B = cache["B"]
     if cache["appended"] >= cache["tail_capacity"]:
         raise ValueError("tail capacity exhausted")
     for b in range(B):
+        hb = 0.0 if h is None else float(np.float32(h[b]))
+        anchor = h is not None and hb > cache["theta"][b]
+        if anchor:
+            close_span(cache, b)
         i = int(cache["n_F"][b])
         if i >= cache["KF"].shape[2]:
             raise ValueError("tail capacity exhausted")
         cache["KF"][b, :, i] = round_stored(k[b], cache["dtype"])
         cache["VF"][b, :, i] = round_stored(v[b], cache["dtype"])
+        cache["HF"][b, i] = hb
         cache["fr_pos"][b, i] = cache["T"] + cache["appended"]
         cache["n_F"][b] = i + 1
+        if anchor:
+            cache["la"][b] = i
     cache["appended"] += 1
 
 

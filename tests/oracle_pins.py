@@ -432,4 +432,60 @@ def pin_append(O):
         raise AssertionError("append past the tail capacity must fail")
 
 
+def pin_streaming_matches_build(O):
+    """Streaming segmentation reproduces segmentation of the whole sequence:
+    appending tokens with surprisal (some above the anchor threshold, two
+    anchors in a row, one exactly at the threshold) gives the cache that the
+    build makes from prefill + appended tokens when its anchors are the
+    prefill anchors plus the appended ones above the threshold."""
+    rng = np.random.default_rng(19)
+    B, Hkv, G, T, d, r = 2, 2, 2, 40, 8, 3
+    K, V = _rand_kv(rng, B, Hkv, T, d)
+    H = rng.exponential(1.0, (B, T)).astype(np.float32)
+    c = O.build_cache(H, K, V, r, 0.15, "f64", Hq=Hkv * G, tail_capacity=12)
+    ns0 = c["n_s"].copy()
+    n_a = int(c["n_a"][0])
+    assert (c["n_a"] == n_a).all() and n_a == 6
+    theta = np.array([H[b][np.argsort(-H[b].astype(np.float64), kind="stable")[n_a - 1]]
+                      for b in range(B)], np.float32)
+    # pattern: 'a' above the threshold, 'b' below, 't' exactly at it
+    pattern = "aabbtbabbbab"
+    hs, ks, vs = [], [], []
+    for ch in pattern:
+        if ch == "a":
+            h = theta * np.float32(2.0) + np.float32(1.0)
+        elif ch == "t":
+            h = theta.copy()
+        else:
+            h = (theta * rng.uniform(0.1, 0.9, B)).astype(np.float32)
+        k1, v1 = _rand_kv(rng, B, Hkv, 1, d)
+        O.append_kv(c, k1[:, :, 0], v1[:, :, 0], h)
+        hs.append(h)
+        ks.append(k1)
+        vs.append(v1)
+    Hx = np.concatenate([H, np.stack(hs, 1)], 1)
+    Kx = np.concatenate([K] + ks, 2)
+    Vx = np.concatenate([V] + vs, 2)
+    ref = O.build_cache(Hx, Kx, Vx, r, 0.0, "f64", Hq=Hkv * G,
+                        n_anchor=n_a + pattern.count("a"))
+    for b in range(B):
+        ns, nf, nt = int(ref["n_s"][b]), int(ref["n_F"][b]), int(ref["nt"][b])
+        assert int(c["n_s"][b]) == ns and int(c["n_F"][b]) == nf and int(c["nt"][b]) == nt
+        assert np.array_equal(c["span_start"][b, :ns], ref["span_start"][b, :ns])
+        assert np.array_equal(c["span_len"][b, :ns], ref["span_len"][b, :ns])
+        assert np.array_equal(c["span_id"][b], ref["span_id"][b, :T])
+        assert np.array_equal(c["fr_pos"][b, :nf], ref["fr_pos"][b, :nf])
+        for key in ("KF", "VF"):
+            assert np.array_equal(c[key][b, :, :nf], ref[key][b, :, :nf]), key
+        for key in ("s", "vbar", "BK", "BV"):
+            assert np.array_equal(c[key][b, :, :ns], ref[key][b, :, :ns]), key
+        for key in ("AK", "AV"):
+            assert np.array_equal(c[key][b, :, :nt], ref[key][b, :, :nt]), key
+        assert np.array_equal(c["ell"][b, :ns], ref["ell"][b, :ns])
+        assert int(c["la"][b]) == int(ref["la"][b])
+    # the anchors appended 6th and 10th close non-empty runs of appended
+    # tokens (the 2nd follows an anchor: no empty span is made)
+    assert (c["n_s"] >= ns0 + 2).all()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

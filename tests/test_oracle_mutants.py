@@ -44,6 +44,13 @@ MUTATIONS = {
     "expanded spans also summarised": ("rest = np.flatnonzero(~expanded)", "rest = np.arange(ns)"),
     "bf16 ties away": ("half = np.uint64((1 << 44) - 1)", "half = np.uint64(1 << 44)"),
     "append invisible": ('cache["n_F"][b] = i + 1', 'cache["n_F"][b] = i'),
+    "streaming anchor at the threshold": ('anchor = h is not None and hb > cache["theta"][b]',
+                                          'anchor = h is not None and hb >= cache["theta"][b]'),
+    "threshold from the strongest anchor": ('c["theta"][b] = float(H[b, anchors].min())',
+                                            'c["theta"][b] = float(H[b, anchors].max())'),
+    "closed span keeps the anchor": ("    rows = slice(la + 1, nf)\n    st = int(cache[\"fr_pos\"][b, la + 1])",
+                                     "    rows = slice(la, nf)\n    st = int(cache[\"fr_pos\"][b, la])"),
+    "new anchor forgotten": ('            cache["la"][b] = i\n', '            cache["la"][b] = i - 1\n'),
 }
 
 
