@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one ``decode_step`` over the whole batch: routing GEMV, top-k cap,
-split-K mixed-resolution attention and merge (plus the tail append on
-workloads that append).  Inputs are resident in HBM before timing starts.
+split-K mixed-resolution attention and merge (plus, on workloads that
+append, the append of one token per sequence with its surprisal: streaming
+segmentation, whose decoded anchors close the run before them into a span).  Inputs are resident in HBM before timing starts.
 The 256 MB last-level cache is defeated by rotating over ``--replicas``
 identical caches (each step reads a different copy).
 
@@ -213,7 +214,9 @@ def main():
 
     apps = None
     if wl.appends is not None:
-        apps = [(to_dev(k, dt), to_dev(v, dt)) for k, v in wl.appends]
+        # each append carries its surprisal: decoded anchors close spans
+        apps = [(to_dev(k, dt), to_dev(v, dt), torch.from_numpy(h).to(dev))
+                for (k, v), h in zip(wl.appends, wl.append_h)]
 
     n_steps = args.steps
     sels = [torch.zeros((B, Hkv, kmax), dtype=torch.int32, device=dev) if kmax else None
@@ -223,8 +226,8 @@ def main():
 
     def step(i, cache, s_buf=None, n_buf=None):
         if apps is not None:
-            k, v = apps[i % len(apps)]
-            rskv.append_kv(cache, k, v)
+            k, v, h = apps[i % len(apps)]
+            rskv.append_token(cache, k, v, h)
         rskv.decode_step(cache, qs[i % len(qs)], cfg["tau"], kmax, out=out, sel=s_buf,
                          n_sel=n_buf)
         return cache.info["appended"]
@@ -255,18 +258,25 @@ def main():
     for i in range(n_steps):
         step(i, caches[i % R], None, None)
     torch.cuda.synchronize()
-    prof = {"route_ms": 0.0, "topk_ms": 0.0, "attend_ms": 0.0, "merge_ms": 0.0, "steps": 0}
+    prof = {"route_ms": 0.0, "topk_ms": 0.0, "attend_ms": 0.0, "merge_ms": 0.0, "steps": 0,
+            "close_ms": 0.0, "append_ms": 0.0, "appends": 0}
     for c in caches:
         p = c.profile_read()
         for k in prof:
             prof[k] += p[k]
         c.profile_enable(False)
     kern = {k: prof[k] / max(1, prof["steps"]) for k in ("route_ms", "topk_ms", "attend_ms", "merge_ms")}
+    if prof["appends"]:
+        # the streaming-segmentation kernels of the step's append
+        kern["close_ms"] = prof["close_ms"] / prof["steps"]
+        kern["append_ms"] = prof["append_ms"] / prof["steps"]
 
     # algorithmic bytes from the timed steps' selections
     tot_b, att_b = [], []
     for i in range(n_steps):
-        # replicas hold identical tables; appends add rows per replica
+        # replicas hold identical tables; appends add rows per replica (rows
+        # that decoded anchors closed into spans are still counted as full
+        # rows: a few dozen rows per sequence over a run)
         n_full = ex["n_full"] + (appended_at[i] - ex["info"]["appended"])
         s_np = sels[i].cpu().numpy() if kmax else np.zeros((B, Hkv, 0), np.int32)
         tb_, ab_ = step_bytes(ex["span_len"], ex["n_spans"], n_full, s_np,

@@ -105,16 +105,38 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V,
 int rskv_decode_step(rskv_cache* cache, const void* q, float tau, int32_t k_max,
                      float* out, int32_t* sel, int32_t* n_sel, void* stream);
 
-/* Append one decoded token per sequence to its trailing full-resolution run
- * (it is attended at full resolution by later steps and never routed).
+/* Append one decoded token per sequence, with streaming segmentation
+ * (Metodologia 1 applied to decoded tokens; the page fixes the anchor rule
+ * only for a whole context, and the library reads it this way):
  *   k, v: device [B][Hkv][d] in the cache dtype.
+ *   h:    device fp32 [B] surprisal of the new tokens, or NULL (then every
+ *         token counts as surprisal 0 and is never an anchor).
+ * The token joins the full-resolution rows at position T + (appends so
+ * far).  It is an anchor iff h[b] > theta_b, the smallest surprisal among
+ * the prefill anchors of sequence b (no decoded anchor when the prefill had
+ * none).  Before a decoded anchor is stored, the non-empty run of
+ * full-resolution rows after the previous anchor becomes a new span j =
+ * n_spans[b], exactly as the build would make it from a run between two
+ * anchors (summary weighted by the rows' surprisal, value mean, ln|S|,
+ * rank-r factors of the stored rows), and those rows leave the
+ * full-resolution set.  Later decode steps route and attend the new span
+ * like any other; span_id covers only the prefill positions.
  * Returns RSKV_ECAPACITY when tail_capacity appends have already been made.
- * Asynchronous on `stream`. */
+ * Asynchronous on `stream` (two kernel launches when h is given and some
+ * sequence has an anchor, else one); no allocation.  Must not overlap a
+ * decode step or another append on the same cache. */
+int rskv_append_token(rskv_cache* cache, const void* k, const void* v, const float* h,
+                      void* stream);
+
+/* rskv_append_token with h = NULL: the token joins the trailing
+ * full-resolution run (attended at full resolution, never routed). */
 int rskv_append_kv(rskv_cache* cache, const void* k, const void* v, void* stream);
 
 /* Sizes of a cache.  S, F and N are the padded dimensions of the exported
  * arrays: S >= every n_spans[b], F >= every n_full[b] + remaining tail
- * capacity, N >= every n_span_tokens[b]. */
+ * capacity, N >= every n_span_tokens[b], including the spans and span
+ * tokens that decoded anchors may still add (with a tail capacity t, at
+ * most ceil(t/2) more spans per sequence). */
 typedef struct rskv_cache_info {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, context_len, rank, dtype;
   int32_t n_spans_max;       /* S */
@@ -151,6 +173,11 @@ typedef struct rskv_host_arrays {
   void* w_k;               /* [B][Hkv][S][r][d] row k = k-th right singular
                               vector; K-hat of span j = A_K(j) @ W_K(j) */
   void* w_v;               /* [B][Hkv][S][r][d] */
+  /* streaming segmentation state (see rskv_append_token) */
+  float* h_full;           /* [B][F] surprisal of full-resolution row i
+                              (0 for tokens appended without one) */
+  float* theta;            /* [B] anchor threshold, +inf without anchors */
+  int32_t* last_anchor;    /* [B] full-resolution row of the last anchor, -1 */
 } rskv_host_arrays;
 
 /* Copy every stored array of the cache to host memory (synchronous). */
@@ -158,6 +185,8 @@ int rskv_cache_export(const rskv_cache* cache, rskv_host_arrays* arrays);
 
 /* Create a cache from host arrays in the canonical layout (padded with the
  * given S, F, N; F counts rows, the new cache adds opts->tail_capacity).
+ * h_full, theta and last_anchor may be NULL: then no decoded token is an
+ * anchor (theta = +inf, last_anchor = -1, h_full = 0).
  * Lets tests and benchmarks decode on a cache built elsewhere.  K/V inputs
  * are not needed, and opts->proj, if given, is a HOST pointer here.
  * Synchronous. */
@@ -172,10 +201,13 @@ void rskv_cache_destroy(rskv_cache* cache);
 /* Per-kernel timing of decode_step: each of its four kernels (routing GEMV,
  * top-k cap, attention partials, merge) is dispatched with a start and a stop
  * HIP event of its own, so the totals are kernel execution times (the gaps
- * between launches are not included).  Enabling clears the totals. */
+ * between launches are not included); the same holds for the two kernels of
+ * rskv_append_token.  Enabling clears the totals. */
 typedef struct rskv_profile {
   int64_t steps;
   double route_ms, topk_ms, attend_ms, merge_ms; /* summed over steps */
+  int64_t appends;                /* rskv_append_token calls recorded */
+  double close_ms, append_ms;     /* span-closing and append kernels */
 } rskv_profile;
 
 int rskv_profile_enable(rskv_cache* cache, int32_t on);

@@ -38,7 +38,7 @@ the rest of the text supports):
       extra "f64" storage mode (no rounding at all) exists for the pins.
   R8  decode-time appends join the trailing full-resolution run before the
       step's attention and are not routed.
-  R9  streaming segmentation: an appended token is an anchor iff its
+  R11 streaming segmentation: an appended token is an anchor iff its
       surprisal exceeds the sequence's threshold theta, the smallest
       surprisal among the prefill anchors (+inf without anchors); the
       full-resolution run after the previous anchor then becomes a span
@@ -204,7 +204,7 @@ def build_cache(H, K, V, rank: int, anchor_frac: float, dtype: str,
     stored inputs.  Returns the canonical cache dictionary: every stored
     array as fp64 values already rounded to ``dtype`` (R7), zero-padded to
     the batch maxima, with per-sequence counts.  ``n_anchor`` replaces
-    floor(p*T) when given.  For streaming segmentation (R9) the cache also
+    floor(p*T) when given.  For streaming segmentation (R11) the cache also
     keeps the surprisal of every full-resolution row (HF), the anchor
     threshold of each sequence (theta: the smallest anchor surprisal, +inf
     without anchors) and the full-resolution row of its last anchor (la, -1
@@ -278,7 +278,7 @@ def _grow(cache: dict, key: str, axis: int, size: int) -> None:
 
 
 def close_span(cache: dict, b: int) -> None:
-    """Streaming segmentation (R9): turn the run of full-resolution rows
+    """Streaming segmentation (R11): turn the run of full-resolution rows
     after the last anchor of sequence b into a new span, exactly as the
     build would for a run with an anchor on both sides (Metodologia 1 and
     2): summary, value mean, ln|S| and factors from the stored rows, which
@@ -327,7 +327,7 @@ def append_kv(cache: dict, k: np.ndarray, v: np.ndarray, h: Optional[np.ndarray]
     """Append one decoded token per sequence (R8).  k, v: [B][Hkv][d] fp64
     values of the stored token; h: [B] its surprisal (fp32 values) or None.
 
-    Streaming segmentation (R9): a token whose surprisal exceeds the
+    Streaming segmentation (R11): a token whose surprisal exceeds the
     sequence's anchor threshold (strictly; an earlier anchor keeps ties) is
     a new anchor; the full-resolution run before it, after the previous
     anchor, is first closed into a span (close_span).  A token without a

@@ -3,5 +3,6 @@
 The compute path is the HIP library ``lib/librskv.so`` (C ABI declared in
 ``include/rskv.h``); this package only marshals arguments to it.
 """
-from .binding import (BF16, F32, Cache, RskvError, append_kv, build_spans, cache_import,  # noqa: F401
+from .binding import (BF16, F32, Cache, RskvError, append_kv, append_token, build_spans,  # noqa: F401
+                      cache_import,
                       decode_step, lib, version)

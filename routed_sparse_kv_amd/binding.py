@@ -44,7 +44,10 @@ class CacheInfo(C.Structure):
 
 _ARRAY_FIELDS = ["n_anchor", "n_spans", "n_full", "n_span_tokens", "span_id", "span_start",
                  "span_len", "full_pos", "summary", "vmean", "log_len", "k_full", "v_full",
-                 "a_k", "a_v", "w_k", "w_v"]
+                 "a_k", "a_v", "w_k", "w_v", "h_full", "theta", "last_anchor"]
+_INT_FIELDS = ("n_anchor", "n_spans", "n_full", "n_span_tokens", "span_id", "span_start",
+               "span_len", "full_pos", "last_anchor")
+_F32_FIELDS = ("log_len", "h_full", "theta")
 
 
 class HostArrays(C.Structure):
@@ -53,7 +56,8 @@ class HostArrays(C.Structure):
 
 class Profile(C.Structure):
     _fields_ = [("steps", C.c_int64), ("route_ms", C.c_double), ("topk_ms", C.c_double),
-                ("attend_ms", C.c_double), ("merge_ms", C.c_double)]
+                ("attend_ms", C.c_double), ("merge_ms", C.c_double), ("appends", C.c_int64),
+                ("close_ms", C.c_double), ("append_ms", C.c_double)]
 
 
 _lib = None
@@ -71,6 +75,7 @@ def lib():
         L.rskv_build_spans.argtypes = [vp, vp, vp, i32, C.POINTER(BuildOpts), vp, C.POINTER(vp)]
         L.rskv_decode_step.argtypes = [vp, vp, C.c_float, i32, vp, vp, vp, vp]
         L.rskv_append_kv.argtypes = [vp, vp, vp, vp]
+        L.rskv_append_token.argtypes = [vp, vp, vp, vp, vp]
         L.rskv_cache_info_get.argtypes = [vp, C.POINTER(CacheInfo)]
         L.rskv_cache_export.argtypes = [vp, C.POINTER(HostArrays)]
         L.rskv_cache_import.argtypes = [C.POINTER(HostArrays), C.POINTER(BuildOpts), i32, i32,
@@ -81,7 +86,7 @@ def lib():
         L.rskv_profile_read.argtypes = [vp, C.POINTER(Profile)]
         L.rskv_last_error.restype = C.c_char_p
         L.rskv_version.restype = C.c_char_p
-        for fn in ("rskv_build_spans", "rskv_decode_step", "rskv_append_kv",
+        for fn in ("rskv_build_spans", "rskv_decode_step", "rskv_append_kv", "rskv_append_token",
                    "rskv_cache_info_get", "rskv_cache_export", "rskv_cache_import",
                    "rskv_profile_enable", "rskv_profile_read"):
             getattr(L, fn).restype = C.c_int
@@ -178,7 +183,8 @@ class Cache:
                       log_len=((B, S), np.float32), k_full=((B, Hkv, F, d), et),
                       v_full=((B, Hkv, F, d), et), a_k=((B, Hkv, N, r), et),
                       a_v=((B, Hkv, N, r), et), w_k=((B, Hkv, S, r, d), et),
-                      w_v=((B, Hkv, S, r, d), et))
+                      w_v=((B, Hkv, S, r, d), et), h_full=((B, F), np.float32),
+                      theta=((B,), np.float32), last_anchor=((B,), np.int32))
         out = {k: np.zeros(sh, dt) for k, (sh, dt) in shapes.items()}
         ha = HostArrays(**{k: v.ctypes.data for k, v in out.items()})
         _check(lib().rskv_cache_export(self.handle, C.byref(ha)))
@@ -236,11 +242,25 @@ def decode_step(cache: Cache, q, tau: float, k_max: int, out=None, sel=None, n_s
 
 
 def append_kv(cache: Cache, k, v):
-    """Append one token per sequence: k, v [B][Hkv][d] in the cache dtype."""
+    """Append one token per sequence: k, v [B][Hkv][d] in the cache dtype
+    (no surprisal: the token is never an anchor)."""
     i = cache.info
     shape = (i["batch"], i["n_kv_heads"], i["head_dim"])
     _check(lib().rskv_append_kv(cache.handle, _dev(k, "k", shape, cache.torch_dtype),
                                 _dev(v, "v", shape, cache.torch_dtype), _stream()))
+    cache.info["appended"] += 1
+
+
+def append_token(cache: Cache, k, v, h=None):
+    """Append one token per sequence with streaming segmentation: k, v
+    [B][Hkv][d] in the cache dtype, h [B] fp32 surprisal on the GPU (or
+    None: surprisal 0, never an anchor)."""
+    torch = _torch()
+    i = cache.info
+    shape = (i["batch"], i["n_kv_heads"], i["head_dim"])
+    hp = _dev(h, "h", (i["batch"],), torch.float32) if h is not None else None
+    _check(lib().rskv_append_token(cache.handle, _dev(k, "k", shape, cache.torch_dtype),
+                                   _dev(v, "v", shape, cache.torch_dtype), hp, _stream()))
     cache.info["appended"] += 1
 
 
@@ -254,9 +274,7 @@ def cache_import(arrays: dict, n_q_heads: int, rank: int, dtype: str, context_le
     for k in _ARRAY_FIELDS:
         if k not in arrays:
             continue
-        want = np.int32 if k in ("n_anchor", "n_spans", "n_full", "n_span_tokens", "span_id",
-                                 "span_start", "span_len", "full_pos") else (
-            np.float32 if k == "log_len" else et)
+        want = np.int32 if k in _INT_FIELDS else (np.float32 if k in _F32_FIELDS else et)
         keep[k] = np.ascontiguousarray(arrays[k], dtype=want)
     B, Hkv, S, d = keep["summary"].shape
     F = keep["k_full"].shape[2]

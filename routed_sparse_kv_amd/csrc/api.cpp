@@ -89,8 +89,9 @@ void free_cache(rskv_cache* c) {
   if (c->last_stream != nullptr) (void)hipStreamSynchronize(c->last_stream);
   (void)hipDeviceSynchronize();
   for (void* p : c->allocs) (void)hipFree(p);
-  for (hipEvent_t e : c->prof.pending)
-    if (e != nullptr) (void)hipEventDestroy(e);
+  for (auto* list : {&c->prof.pending, &c->prof.app_pending})
+    for (hipEvent_t e : *list)
+      if (e != nullptr) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof.pool) (void)hipEventDestroy(e);
   c->magic = 0;
   delete c;
@@ -136,6 +137,9 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   ALLOC(v.n_spans, c->B, "n_spans");
   ALLOC(v.n_full, c->B, "n_full");
   ALLOC(v.n_full0, c->B, "n_full0");
+  ALLOC(v.h_full, static_cast<size_t>(c->B) * c->F, "h_full");
+  ALLOC(v.theta, c->B, "theta");
+  ALLOC(v.last_anchor, c->B, "last_anchor");
   ALLOCB(v.summary, z.summary * es, "summary");
   ALLOCB(v.vmean, z.vmean * es, "vmean");
   ALLOC(v.log_len, c->B * S, "log_len");
@@ -153,6 +157,9 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   c->nsplit_max = rskv::decode_nsplit_max(c->B, c->Hkv, c->S, c->F, c->k_max_cap);
   ALLOC(v.wstart, U * (4 * c->nsplit_max + 1), "wstart");
   ALLOC(v.part, U * c->nsplit_max * c->G * (d + 2), "part");
+  // span closing: one workgroup per (unit, K or V), launched only when some
+  // sequence can see a decoded anchor
+  c->close_grid = c->close_rows > 0 ? static_cast<int>(2 * U) : 0;
 #undef ALLOC
 #undef ALLOCB
   RSKV_HIP(hipMemsetAsync(v.summary, 0, z.summary * es, st), "memset summary");
@@ -166,6 +173,8 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   RSKV_HIP(hipMemsetAsync(v.log_len, 0, c->B * S * sizeof(float), st), "memset log_len");
   RSKV_HIP(hipMemsetAsync(v.slogit, 0, z.slogit * sizeof(float), st), "memset slogit");
   RSKV_HIP(hipMemsetAsync(v.n_sel, 0, U * sizeof(int32_t), st), "memset n_sel");
+  RSKV_HIP(hipMemsetAsync(v.h_full, 0, static_cast<size_t>(c->B) * c->F * sizeof(float), st),
+           "memset h_full");
   return RSKV_OK;
 }
 
@@ -195,20 +204,35 @@ int copy_proj(rskv_cache* c, const rskv_build_opts* o, hipStream_t st, bool from
   return RSKV_OK;
 }
 
-void finish_sizes(rskv_cache* c, const rskv_build_opts* o) {
-  int s_max = 0, f_max = 0, n_max = 0, p_max = 0;
+// Padded dimensions from the per-sequence counts.  `la` holds the
+// full-resolution row of each sequence's last anchor (-1 if none) and
+// `theta` its anchor threshold: with a tail capacity, decoded anchors may
+// close spans (streaming segmentation), so the span and span-token
+// dimensions reserve room for them.  A closing needs a decoded anchor, and
+// two closings at least one decoded non-anchor between them, so a sequence
+// closes at most ceil(tail/2) spans, holding at most its tail run after the
+// last anchor plus the decoded tokens.
+void finish_sizes(rskv_cache* c, const rskv_build_opts* o, const std::vector<int>& la,
+                  const std::vector<float>& theta) {
+  int s_max = 0, f_max = 0, n_max = 0, p_max = 0, trail_max = 0;
+  bool anchors = false;  // some sequence may see a decoded anchor
   for (int b = 0; b < c->B; ++b) {
     s_max = std::max(s_max, c->h_n_spans[b]);
     f_max = std::max(f_max, c->h_n_full0[b]);
     n_max = std::max(n_max, c->h_n_span_tokens[b]);
     p_max = std::max(p_max, c->h_n_tok_pad[b]);
+    if (la[b] >= 0) trail_max = std::max(trail_max, c->h_n_full0[b] - la[b] - 1);
+    anchors = anchors || la[b] >= 0 || theta[b] < HUGE_VALF;
   }
-  c->S = std::max(1, s_max);
+  const int closings = anchors && c->tail_cap > 0 ? (c->tail_cap + 1) / 2 : 0;
+  c->close_rows = closings > 0 ? trail_max + c->tail_cap : 0;
+  c->S = std::max(1, s_max + closings);
   c->F = std::max(1, f_max + c->tail_cap);
-  c->N = std::max(1, n_max);
+  c->N = std::max(1, n_max + c->close_rows);
   c->Sp = rskv::round_up(c->S, 32);
   c->Fp = rskv::round_up(c->F, 32);
-  c->Np = std::max(16, p_max);
+  c->Np = std::max(16, p_max + (closings > 0 ? rskv::round_up(c->close_rows, 16) + 16 * closings
+                                              : 0));
   c->k_max_cap = o->k_max_cap > 0 ? o->k_max_cap : 0x7fffffff;  // <= 0: no limit
 }
 
@@ -229,6 +253,7 @@ struct Relayout {
   const rskv_cache* c;
   const int32_t* span_len;  // [B][S_host], pitch ls
   int ls;
+  const int* n_spans;       // [B] spans per sequence
 
   // dir = +1: device -> canonical; -1: canonical -> device.
   void full(E* canon, int F_c, E* dev, bool keys, int dir) const {
@@ -256,7 +281,7 @@ struct Relayout {
     const int r = c->rank;
     std::vector<int> off, pad;
     for (int b = 0; b < c->B; ++b) {
-      const int ns = c->h_n_spans[b];
+      const int ns = n_spans[b];
       span_offsets(span_len + static_cast<size_t>(b) * ls, ns, &off, &pad);
       for (int h = 0; h < c->Hkv; ++h) {
         const size_t u = static_cast<size_t>(b) * c->Hkv + h;
@@ -286,14 +311,14 @@ struct Relayout {
 };
 
 template <typename E>
-int export_arrays(const rskv_cache* c, rskv_host_arrays* a) {
+int export_arrays(const rskv_cache* c, const std::vector<int>& ns, rskv_host_arrays* a) {
   const auto& v = c->dev;
   const Sizes z = sizes_of(c);
   const size_t U = static_cast<size_t>(c->B) * c->Hkv;
   const int S = c->S, F = c->F, N = c->N, d = c->d, r = c->rank;
   std::vector<int32_t> lens(static_cast<size_t>(c->B) * S);
   RSKV_HIP(hipMemcpy(lens.data(), v.span_len, lens.size() * 4, hipMemcpyDeviceToHost), "export");
-  Relayout<E> rl{c, lens.data(), S};
+  Relayout<E> rl{c, lens.data(), S, ns.data()};
   std::vector<E> tmp;
   auto fetch = [&](const void* src, size_t n) -> int {
     tmp.assign(n, E(0));
@@ -344,7 +369,7 @@ int import_arrays(rskv_cache* c, const rskv_host_arrays* a, int S_in, int F_in, 
   const Sizes z = sizes_of(c);
   const size_t U = static_cast<size_t>(c->B) * c->Hkv;
   const int d = c->d, r = c->rank;
-  Relayout<E> rl{c, a->span_len, S_in};
+  Relayout<E> rl{c, a->span_len, S_in, c->h_n_spans.data()};
   std::vector<E> tmp;
   auto put = [&](void* dst, size_t n, const char* what) -> int {
     hipError_t e = hipMemcpy(dst, tmp.data(), n * sizeof(E), hipMemcpyHostToDevice);
@@ -454,6 +479,8 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
     c->h_n_full0.resize(B);
     c->h_n_span_tokens.resize(B);
     c->h_n_tok_pad.resize(B);
+    std::vector<int> la(B);
+    std::vector<float> theta(B);
     for (int b = 0; b < B; ++b) {
       const int32_t* cb = &hc[rskv::kCounts * b];
       if (cb[0] < 0) return fail(RSKV_EINVAL, "surprisal holds NaN");
@@ -462,11 +489,18 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
       c->h_n_full0[b] = cb[2];
       c->h_n_span_tokens[b] = cb[3];
       c->h_n_tok_pad[b] = cb[4];
+      la[b] = cb[5];
+      memcpy(&theta[b], &cb[6], sizeof(float));
     }
-    finish_sizes(c, opts);
+    finish_sizes(c, opts, la, theta);
     if ((rc = alloc_arrays(c, st)) != RSKV_OK) return rc;
     if ((rc = copy_proj(c, opts, st, false)) != RSKV_OK) return rc;
     auto& v = c->dev;
+    RSKV_HIP(hipMemcpyAsync(v.last_anchor, la.data(), B * sizeof(int32_t), hipMemcpyHostToDevice,
+                            st),
+             "copy last_anchor");
+    RSKV_HIP(hipMemcpyAsync(v.theta, theta.data(), B * sizeof(float), hipMemcpyHostToDevice, st),
+             "copy theta");
     const int kc = rskv::kCounts;
     RSKV_HIP(rskv::launch_copy_rows(v.span_start, c->S, start_tmp, T, counts, kc, 1, 0, 0, B, st),
              "copy span_start");
@@ -491,7 +525,7 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
              "copy n_full0");
     // ---- summaries, packed rows, factors
     RSKV_HIP(rskv::launch_summary(c, surprisal, K, V, st), "summary kernel");
-    RSKV_HIP(rskv::launch_pack(c, K, V, st), "pack kernel");
+    RSKV_HIP(rskv::launch_pack(c, surprisal, K, V, st), "pack kernel");
     std::string ferr;
     hipError_t fe = rskv::launch_factor(c, K, V, st, &ferr);
     if (fe != hipSuccess) {
@@ -568,15 +602,55 @@ int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, flo
   }
 }
 
+int rskv_append_token(rskv_cache* c, const void* k, const void* v, const float* h,
+                      void* stream) {
+  try {
+    if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
+    if (k == nullptr || v == nullptr) return fail(RSKV_EINVAL, "k and v must be non-NULL");
+    if (c->appended >= c->tail_cap) return fail(RSKV_ECAPACITY, "tail capacity exhausted");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    auto& pr = c->prof;
+    rskv::KernelEvents ev[2];
+    if (pr.on) {
+      for (auto* e : {&ev[0].start, &ev[0].stop, &ev[1].start, &ev[1].stop}) {
+        if (pr.pool.empty()) {
+          hipEvent_t n;
+          RSKV_HIP(hipEventCreate(&n), "event create");
+          pr.pool.push_back(n);
+        }
+        *e = pr.pool.back();
+        pr.pool.pop_back();
+      }
+    }
+    // a closing needs an anchor threshold and the surprisal of the token
+    const bool may_close = h != nullptr && c->close_grid > 0;
+    if (may_close) {
+      RSKV_HIP(rskv::launch_close(c, h, st, pr.on ? &ev[0] : nullptr), "close kernel");
+    } else if (pr.on) {
+      pr.pool.push_back(ev[0].start);
+      pr.pool.push_back(ev[0].stop);
+      ev[0] = rskv::KernelEvents{};
+    }
+    RSKV_HIP(rskv::launch_append(c, k, v, h, may_close, c->T + c->appended, st,
+                                 pr.on ? &ev[1] : nullptr),
+             "append kernel");
+    if (pr.on)
+      for (const auto& e : ev) {
+        pr.app_pending.push_back(e.start);
+        pr.app_pending.push_back(e.stop);
+      }
+    c->appended += 1;
+    return RSKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(RSKV_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(RSKV_EINVAL, "unexpected error in rskv_append_token");
+  }
+}
+
 int rskv_append_kv(rskv_cache* c, const void* k, const void* v, void* stream) {
-  if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
-  if (k == nullptr || v == nullptr) return fail(RSKV_EINVAL, "k and v must be non-NULL");
-  if (c->appended >= c->tail_cap) return fail(RSKV_ECAPACITY, "tail capacity exhausted");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  c->last_stream = st;
-  RSKV_HIP(rskv::launch_append(c, k, v, st), "append kernel");
-  c->appended += 1;
-  return RSKV_OK;
+  return rskv_append_token(c, k, v, nullptr, stream);
 }
 
 int rskv_cache_info_get(const rskv_cache* c, rskv_cache_info* info) {
@@ -607,13 +681,21 @@ int rskv_cache_export(const rskv_cache* c, rskv_host_arrays* a) {
     RSKV_HIP(hipDeviceSynchronize(), "export sync");
     const int B = c->B;
     const size_t S = c->S, F = c->F;
+    const auto& v = c->dev;
+    // counts as they stand on the device (appends and closings change them)
+    std::vector<int> ns(B), nf(B), la(B), off(static_cast<size_t>(B) * (S + 1));
+    RSKV_HIP(hipMemcpy(ns.data(), v.n_spans, B * 4, hipMemcpyDeviceToHost), "export n_spans");
+    RSKV_HIP(hipMemcpy(nf.data(), v.n_full, B * 4, hipMemcpyDeviceToHost), "export n_full");
+    RSKV_HIP(hipMemcpy(la.data(), v.last_anchor, B * 4, hipMemcpyDeviceToHost), "export la");
+    RSKV_HIP(hipMemcpy(off.data(), v.tok_off, off.size() * 4, hipMemcpyDeviceToHost),
+             "export tok_off");
     for (int b = 0; b < B; ++b) {
       if (a->n_anchor) a->n_anchor[b] = c->h_n_anchor[b];
-      if (a->n_spans) a->n_spans[b] = c->h_n_spans[b];
-      if (a->n_full) a->n_full[b] = c->h_n_full0[b] + c->appended;
-      if (a->n_span_tokens) a->n_span_tokens[b] = c->h_n_span_tokens[b];
+      if (a->n_spans) a->n_spans[b] = ns[b];
+      if (a->n_full) a->n_full[b] = nf[b];
+      if (a->n_span_tokens) a->n_span_tokens[b] = off[static_cast<size_t>(b) * (S + 1) + ns[b]];
+      if (a->last_anchor) a->last_anchor[b] = la[b];
     }
-    const auto& v = c->dev;
     auto cp = [&](void* dst, const void* src, size_t bytes, const char* what) -> int {
       if (dst == nullptr) return RSKV_OK;
       hipError_t e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
@@ -626,7 +708,10 @@ int rskv_cache_export(const rskv_cache* c, rskv_host_arrays* a) {
     if ((rc = cp(a->span_len, v.span_len, B * S * 4, "export span_len"))) return rc;
     if ((rc = cp(a->full_pos, v.full_pos, B * F * 4, "export full_pos"))) return rc;
     if ((rc = cp(a->log_len, v.log_len, B * S * 4, "export log_len"))) return rc;
-    return c->dtype == RSKV_BF16 ? export_arrays<uint16_t>(c, a) : export_arrays<uint32_t>(c, a);
+    if ((rc = cp(a->h_full, v.h_full, B * F * 4, "export h_full"))) return rc;
+    if ((rc = cp(a->theta, v.theta, B * 4, "export theta"))) return rc;
+    return c->dtype == RSKV_BF16 ? export_arrays<uint16_t>(c, ns, a)
+                                 : export_arrays<uint32_t>(c, ns, a);
   } catch (const std::bad_alloc&) {
     return fail(RSKV_ENOMEM, "host allocation failed");
   } catch (...) {
@@ -659,10 +744,21 @@ int rskv_cache_import(const rskv_host_arrays* a, const rskv_build_opts* opts, in
     c->h_n_full0.resize(B);
     c->h_n_span_tokens.resize(B);
     c->h_n_tok_pad.resize(B);
+    std::vector<int> la(B, -1);
+    std::vector<float> theta(B, HUGE_VALF);
     for (int b = 0; b < B; ++b) {
       const int ns = a->n_spans[b], nf = a->n_full[b], nt = a->n_span_tokens[b];
       if (ns < 0 || ns > S_in || nf < 0 || nf > F_in || nt < 0 || nt > N_in)
         return fail(RSKV_EINVAL, "counts exceed the padded dimensions");
+      if (a->last_anchor != nullptr) {
+        la[b] = a->last_anchor[b];
+        if (la[b] < -1 || la[b] >= nf)
+          return fail(RSKV_EINVAL, "last_anchor must be -1 or a full-resolution row");
+      }
+      if (a->theta != nullptr) {
+        theta[b] = a->theta[b];
+        if (theta[b] != theta[b]) return fail(RSKV_EINVAL, "theta holds NaN");
+      }
       long long sum = 0, pad = 0;
       for (int j = 0; j < ns; ++j) {
         const int len = a->span_len[static_cast<size_t>(b) * S_in + j];
@@ -677,7 +773,7 @@ int rskv_cache_import(const rskv_host_arrays* a, const rskv_build_opts* opts, in
       c->h_n_span_tokens[b] = nt;
       c->h_n_tok_pad[b] = static_cast<int>(pad);
     }
-    finish_sizes(c, opts);
+    finish_sizes(c, opts, la, theta);
     if ((rc = alloc_arrays(c, st)) != RSKV_OK) return rc;
     rc = dev_alloc(c, &c->dev.span_id, static_cast<size_t>(B) * c->T, "span_id");
     if (rc != RSKV_OK) return rc;
@@ -688,7 +784,7 @@ int rskv_cache_import(const rskv_host_arrays* a, const rskv_build_opts* opts, in
     std::vector<int32_t> starts(static_cast<size_t>(B) * c->S, 0), lens(starts.size(), 0),
         off(static_cast<size_t>(B) * (c->S + 1), 0), pad(off.size(), 0),
         fpos(static_cast<size_t>(B) * c->F, -1);
-    std::vector<float> ell(starts.size(), 0.f);
+    std::vector<float> ell(starts.size(), 0.f), hfull(fpos.size(), 0.f);
     std::vector<int> o, p;
     for (int b = 0; b < B; ++b) {
       const int ns = c->h_n_spans[b];
@@ -703,8 +799,11 @@ int rskv_cache_import(const rskv_host_arrays* a, const rskv_build_opts* opts, in
         off[static_cast<size_t>(b) * (c->S + 1) + j] = o[j];
         pad[static_cast<size_t>(b) * (c->S + 1) + j] = p[j];
       }
-      for (int i = 0; i < c->h_n_full0[b]; ++i)
+      for (int i = 0; i < c->h_n_full0[b]; ++i) {
         fpos[static_cast<size_t>(b) * c->F + i] = a->full_pos[static_cast<size_t>(b) * F_in + i];
+        if (a->h_full != nullptr)
+          hfull[static_cast<size_t>(b) * c->F + i] = a->h_full[static_cast<size_t>(b) * F_in + i];
+      }
     }
     auto put = [&](void* dst, const void* src, size_t bytes, const char* what) -> int {
       hipError_t e = hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
@@ -716,6 +815,9 @@ int rskv_cache_import(const rskv_host_arrays* a, const rskv_build_opts* opts, in
     if ((rc = put(v.tok_off, off.data(), off.size() * 4, "import tok_off"))) return rc;
     if ((rc = put(v.tok_pad, pad.data(), pad.size() * 4, "import tok_pad"))) return rc;
     if ((rc = put(v.full_pos, fpos.data(), fpos.size() * 4, "import full_pos"))) return rc;
+    if ((rc = put(v.h_full, hfull.data(), hfull.size() * 4, "import h_full"))) return rc;
+    if ((rc = put(v.theta, theta.data(), theta.size() * 4, "import theta"))) return rc;
+    if ((rc = put(v.last_anchor, la.data(), la.size() * 4, "import last_anchor"))) return rc;
     if (a->span_id != nullptr &&
         (rc = put(v.span_id, a->span_id, static_cast<size_t>(B) * c->T * 4, "import span_id")))
       return rc;
@@ -743,12 +845,16 @@ void rskv_cache_destroy(rskv_cache* c) {
 
 int rskv_profile_enable(rskv_cache* c, int32_t on) {
   if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
-  for (hipEvent_t e : c->prof.pending)
-    if (e != nullptr) c->prof.pool.push_back(e);
-  c->prof.pending.clear();
+  for (auto* list : {&c->prof.pending, &c->prof.app_pending}) {
+    for (hipEvent_t e : *list)
+      if (e != nullptr) c->prof.pool.push_back(e);
+    list->clear();
+  }
   c->prof.on = on != 0;
   c->prof.steps = 0;
+  c->prof.appends = 0;
   for (double& m : c->prof.ms) m = 0.0;
+  c->prof.close_ms = c->prof.append_ms = 0.0;
   return RSKV_OK;
 }
 
@@ -768,10 +874,26 @@ int rskv_profile_read(rskv_cache* c, rskv_profile* p) {
     }
     pr.steps += 1;
   }
-  for (hipEvent_t e : pr.pending)
-    if (e != nullptr) pr.pool.push_back(e);
-  pr.pending.clear();
+  for (size_t i = 0; i + 4 <= pr.app_pending.size(); i += 4) {
+    RSKV_HIP(hipEventSynchronize(pr.app_pending[i + 3]), "event sync");
+    float ms = 0.f;
+    if (pr.app_pending[i] != nullptr) {
+      RSKV_HIP(hipEventElapsedTime(&ms, pr.app_pending[i], pr.app_pending[i + 1]), "elapsed");
+      pr.close_ms += ms;
+    }
+    RSKV_HIP(hipEventElapsedTime(&ms, pr.app_pending[i + 2], pr.app_pending[i + 3]), "elapsed");
+    pr.append_ms += ms;
+    pr.appends += 1;
+  }
+  for (auto* list : {&pr.pending, &pr.app_pending}) {
+    for (hipEvent_t e : *list)
+      if (e != nullptr) pr.pool.push_back(e);
+    list->clear();
+  }
   p->steps = pr.steps;
+  p->appends = pr.appends;
+  p->close_ms = pr.close_ms;
+  p->append_ms = pr.append_ms;
   p->route_ms = pr.ms[0];
   p->topk_ms = pr.ms[1];
   p->attend_ms = pr.ms[2];

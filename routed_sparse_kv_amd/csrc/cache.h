@@ -29,6 +29,11 @@ struct DeviceArrays {
   int32_t* n_spans = nullptr;     // [B]
   int32_t* n_full = nullptr;      // [B] current full rows (grows on append)
   int32_t* n_full0 = nullptr;     // [B] full rows at build time
+  // streaming segmentation state
+  float* h_full = nullptr;        // [B][F] surprisal of each full-resolution row
+  float* theta = nullptr;         // [B] anchor threshold (smallest prefill anchor
+                                  // surprisal, +inf without anchors)
+  int32_t* last_anchor = nullptr; // [B] full-resolution row of the last anchor, -1
   // stored representation (cache dtype unless noted)
   void* summary = nullptr;        // [U][S][d] row-major (routing GEMV rows)
   void* vmean = nullptr;          // [U] V32 tiles over Sp spans
@@ -60,6 +65,10 @@ struct Profile {
   int64_t steps = 0;
   double ms[kProfileKernels] = {0, 0, 0, 0};
   std::vector<hipEvent_t> pending;  // 2 * kProfileKernels per recorded step
+  // appends: close start/stop (null when not launched), append start/stop
+  int64_t appends = 0;
+  double close_ms = 0, append_ms = 0;
+  std::vector<hipEvent_t> app_pending;
   std::vector<hipEvent_t> pool;
 };
 
@@ -103,6 +112,10 @@ struct rskv_cache {
   int n_proj = 0;
   int S = 1, F = 1, N = 1, Sp = 32, Fp = 32, Np = 16;
   int tail_cap = 0, appended = 0, k_max_cap = 0;
+  // span closing at append time: longest run a closing can see (0: no
+  // decoded token can be an anchor) and the close kernel's workgroups
+  int close_rows = 0;
+  int close_grid = 0;
   int nsplit_max = 1;
   std::vector<int32_t> h_n_anchor, h_n_spans, h_n_full0, h_n_span_tokens, h_n_tok_pad;
   rskv::DeviceArrays dev;
@@ -120,8 +133,10 @@ constexpr uint32_t kMagic = 0x52534b56u;  // "RSKV"
 
 // Segmentation of every sequence; writes span_id, span starts/lengths,
 // token offsets (plain and padded), full-resolution positions (pitch T) and
-// counts[B][5] = {n_anchor, n_spans, n_full, n_span_tokens, n_tok_pad}.
-constexpr int kCounts = 5;
+// counts[B][7] = {n_anchor (-1: NaN surprisal), n_spans, n_full,
+// n_span_tokens, n_tok_pad, full-resolution row of the last anchor (-1 if
+// none), bits of the anchor threshold (fp32; +inf if none)}.
+constexpr int kCounts = 7;
 hipError_t launch_segment(const float* H, int B, int T, int n_anchor, int32_t* span_id,
                           int32_t* start_tmp, int32_t* len_tmp, int32_t* tokoff_tmp,
                           int32_t* tokpad_tmp, int32_t* full_tmp, int32_t* counts,
@@ -136,8 +151,9 @@ hipError_t launch_copy_rows(int32_t* dst, int dst_pitch, const int32_t* src, int
 hipError_t launch_summary(const rskv_cache* c, const float* H, const void* K, const void* V,
                           hipStream_t st);
 
-// Packs full-resolution rows of K and V.
-hipError_t launch_pack(const rskv_cache* c, const void* K, const void* V, hipStream_t st);
+// Packs full-resolution rows of K and V and their surprisal.
+hipError_t launch_pack(const rskv_cache* c, const float* H, const void* K, const void* V,
+                       hipStream_t st);
 
 // Per-span rank-r factors of K and V (fp64 one-sided Jacobi).
 hipError_t launch_factor(rskv_cache* c, const void* K, const void* V, hipStream_t st,
@@ -170,6 +186,15 @@ hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, const S
 hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st,
                         const KernelEvents* ev);
 
-hipError_t launch_append(rskv_cache* c, const void* k, const void* v, hipStream_t st);
+// Streaming segmentation at append time, two launches: launch_close turns
+// the full-resolution run after the last anchor into a new span for every
+// sequence whose new token (surprisal h[b], device) is an anchor;
+// launch_append then stores the token (surprisal h[b], or 0 when h is null)
+// at position `pos` and updates the counts; `closed` tells it whether
+// launch_close ran before it.  `ev` may be null.
+hipError_t launch_close(const rskv_cache* c, const float* h, hipStream_t st,
+                        const KernelEvents* ev);
+hipError_t launch_append(const rskv_cache* c, const void* k, const void* v, const float* h,
+                         bool closed, int pos, hipStream_t st, const KernelEvents* ev);
 
 }  // namespace rskv

@@ -16,6 +16,7 @@
 // cnt/2 disjoint pairs in parallel; a group of lanes handles one pair.
 // Build-time only: this kernel is not on the decode path.
 #include <algorithm>
+#include <type_traits>
 #include <string>
 #include <vector>
 
@@ -28,8 +29,364 @@ namespace {
 constexpr int kFacThreads = 256;
 constexpr int kLdsWork = 6144;   // doubles of LDS working matrix (48 KB)
 constexpr int kMaxSweeps = 40;
-constexpr double kOrthTol = 1e-15;
+// A pair of rows counts as orthogonal once |<a,b>| <= L eps ||a|| ||b||:
+// the rounding error of a length-L fp64 dot product can reach that size,
+// so a tighter test would keep rotating on rounding noise.
+constexpr double kEps = 2.220446049250313e-16;
 
+// One DPP lane exchange of a double (both halves with the same control).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long i = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(i), kCtrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(i >> 32), kCtrl, 0xf, 0xf, false);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+// Sums of three values over aligned groups of GS lanes (a power of two
+// <= 64), left in every lane of the group.  Inside a 16-lane row the
+// partners come from DPP (quad xor 1, quad xor 2, half-row mirror, row
+// mirror: each step adds the other half of the current block, so every lane
+// ends with the same sum); across rows from lane shuffles.
+template <int GS>
+__device__ __forceinline__ void group_sum3(double& a, double& b, double& c) {
+  if constexpr (GS >= 2) {
+    a += dpp_f64<0xb1>(a); b += dpp_f64<0xb1>(b); c += dpp_f64<0xb1>(c);
+  }
+  if constexpr (GS >= 4) {
+    a += dpp_f64<0x4e>(a); b += dpp_f64<0x4e>(b); c += dpp_f64<0x4e>(c);
+  }
+  if constexpr (GS >= 8) {
+    a += dpp_f64<0x141>(a); b += dpp_f64<0x141>(b); c += dpp_f64<0x141>(c);
+  }
+  if constexpr (GS >= 16) {
+    a += dpp_f64<0x140>(a); b += dpp_f64<0x140>(b); c += dpp_f64<0x140>(c);
+  }
+#pragma unroll
+  for (int o = 16; o < GS; o <<= 1) {
+    const double pa = __shfl_xor(a, o, kWave);
+    const double pb = __shfl_xor(b, o, kWave);
+    const double pc = __shfl_xor(c, o, kWave);
+    a += pa;
+    b += pb;
+    c += pc;
+  }
+}
+
+// 1/x and 1/sqrt(x): the hardware estimate refined by one Newton step,
+// which squares its relative error (a rotation then stays orthogonal to
+// far below the storage rounding, and its angle is accurate enough for the
+// sweep's quadratic convergence).
+__device__ __forceinline__ double recip(double x) {
+  const double r = __builtin_amdgcn_rcp(x);
+  return fma(r, fma(-x, r, 1.0), r);
+}
+__device__ __forceinline__ double rsqrt_nr(double x) {
+  const double y = __builtin_amdgcn_rsq(x);
+  return y * fma(-0.5 * x * y, y, 1.5);
+}
+
+// LDS of one factorisation: singular values, the order of the top ones and
+// the "a pair was rotated" flag of the current sweep.
+struct FactorShared {
+  double sig[128];
+  int top[128];
+  int rot;
+};
+
+// One-sided Jacobi sweeps over the `cnt` rows (length L, pitch P) of
+// `work` until no pair of rows needs a rotation (or kMaxSweeps).  A round
+// rotates cnt/2 disjoint pairs in parallel (round-robin ordering) with GS
+// lanes per pair.  The cost of a round is its instruction count (a wave64
+// VALU instruction takes 4 cycles), so the rotation comes from reciprocal
+// and rsqrt estimates, the pair indices need no integer division, and with
+// E > 0 (L = E * GS) a lane keeps its E elements of both rows in registers
+// (addressed with immediate offsets, loaded together without branches)
+// between the dot products and the rotation; E = 0 loops over L with
+// stride GS instead.  NW waves take part: with one
+// wave the rounds need no workgroup barrier (a wave's LDS accesses complete
+// in order) and the "rotated" flag is a wave vote.  Returns the number of
+// sweeps; ends with a barrier of the NW waves.
+template <int GS, int NW, int E>
+__device__ __forceinline__ int jacobi_sweeps_gs(double* work, int cnt, int L, int P,
+                                                FactorShared& sh) {
+  constexpr int kReg = E > 0 ? E : 1;
+  const int tid = threadIdx.x;
+  const int cnt2 = cnt + (cnt & 1);
+  const int m = cnt2 - 1;  // rounds per sweep
+  const int npairs = cnt2 / 2;
+  const int g = tid / GS;
+  const int li = tid - g * GS;
+  const double tol2 = (L * kEps) * (L * kEps);
+  auto round_sync = [] {
+    if constexpr (NW == 1) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      __syncthreads();
+    }
+  };
+  for (int sweep = 0; sweep < kMaxSweeps && cnt2 > 1; ++sweep) {
+    bool did = false;
+    if constexpr (NW > 1) {
+      if (tid == 0) sh.rot = 0;
+      __syncthreads();
+    }
+    for (int r = 0; r < m; ++r) {
+      if (g < npairs) {
+        int pa = 0;
+        if (g > 0) {
+          pa = g - 1 + r;  // < 2m
+          pa = (pa >= m ? pa - m : pa) + 1;
+        }
+        int pb = cnt2 - 2 - g + r;  // in [0, 2m)
+        pb = (pb >= m ? pb - m : pb) + 1;
+        if (pa < cnt && pb < cnt) {
+          double* xa = work + static_cast<size_t>(pa) * P + li;
+          double* xb = work + static_cast<size_t>(pb) * P + li;
+          double al = 0.0, be = 0.0, ga = 0.0;
+          double va[kReg], vb[kReg];
+          if constexpr (E > 0) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+              va[i] = xa[i * GS];
+              vb[i] = xb[i * GS];
+            }
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+              al = fma(va[i], va[i], al);
+              be = fma(vb[i], vb[i], be);
+              ga = fma(va[i], vb[i], ga);
+            }
+          } else {
+            for (int e = 0; e < L - li; e += GS) {
+              const double p = xa[e], q = xb[e];
+              al = fma(p, p, al);
+              be = fma(q, q, be);
+              ga = fma(p, q, ga);
+            }
+          }
+          group_sum3<GS>(al, be, ga);
+          if (ga != 0.0 && ga * ga > tol2 * (al * be)) {
+            // tan of the angle that zeroes <a,b>: t = sign(tau) rho /
+            // (|tau| + sqrt(tau^2 + rho^2)), tau = be - al, rho = 2 ga
+            const double tau = be - al, rho = 2.0 * ga;
+            const double q = fma(tau, tau, rho * rho);
+            const double root = q * rsqrt_nr(q);
+            const double t = copysign(1.0, tau) * rho * recip(fabs(tau) + root);
+            const double cs = rsqrt_nr(fma(t, t, 1.0));
+            const double sn = cs * t;
+            if constexpr (E > 0) {
+#pragma unroll
+              for (int i = 0; i < E; ++i) {
+                xa[i * GS] = cs * va[i] - sn * vb[i];
+                xb[i * GS] = sn * va[i] + cs * vb[i];
+              }
+            } else {
+              for (int e = 0; e < L - li; e += GS) {
+                const double p = xa[e], q = xb[e];
+                xa[e] = cs * p - sn * q;
+                xb[e] = sn * p + cs * q;
+              }
+            }
+            did = true;
+            if constexpr (NW > 1) {
+              if (li == 0) sh.rot = 1;
+            }
+          }
+        }
+      }
+      round_sync();
+    }
+    int rotated;
+    if constexpr (NW == 1) {
+      rotated = __any(did);
+    } else {
+      rotated = sh.rot;
+      __syncthreads();
+    }
+    if (!rotated) return sweep + 1;
+  }
+  return kMaxSweeps;
+}
+
+// Lanes per pair that make a Jacobi round over `cnt` rows occupy about NT
+// threads: the largest power of two <= 64 with lanes * pairs <= NT.
+template <int NT>
+__device__ __forceinline__ int jacobi_group(int cnt) {
+  const int npairs = (cnt + 1) / 2;
+  int gs = kWave;
+  while (gs > 1 && gs * npairs > NT) gs >>= 1;
+  return gs;
+}
+
+// Row pitch (doubles) of an LDS working matrix with rows of length L for
+// Jacobi with gs lanes per pair.  A wave reads rows of consecutive indices
+// (the round-robin ordering advances pairs by one row), so a pitch of
+// gs (mod 32) doubles starts each row 2 gs banks after the previous one and
+// the wave's groups tile the 64 banks instead of colliding.
+__device__ __forceinline__ int jacobi_pitch(int L, int gs) {
+  return gs >= 32 ? L : L + (((gs - L) % 32) + 32) % 32;
+}
+
+// jacobi_sweeps_gs with E = L / GS registers per lane when that is a power
+// of two (and GS * E <= 128), else the strided loop.
+template <int GS, int NW>
+__device__ __forceinline__ int jacobi_sweeps_e(double* work, int cnt, int L, int P,
+                                               FactorShared& sh) {
+  const int e = L % GS == 0 ? L / GS : 0;
+  switch (e) {
+    case 1: return jacobi_sweeps_gs<GS, NW, 1>(work, cnt, L, P, sh);
+    case 2:
+      if constexpr (2 * GS <= 128) return jacobi_sweeps_gs<GS, NW, 2>(work, cnt, L, P, sh);
+      break;
+    case 4:
+      if constexpr (4 * GS <= 128) return jacobi_sweeps_gs<GS, NW, 4>(work, cnt, L, P, sh);
+      break;
+    case 8:
+      if constexpr (8 * GS <= 128) return jacobi_sweeps_gs<GS, NW, 8>(work, cnt, L, P, sh);
+      break;
+    case 16:
+      if constexpr (16 * GS <= 128) return jacobi_sweeps_gs<GS, NW, 16>(work, cnt, L, P, sh);
+      break;
+    case 32:
+      if constexpr (32 * GS <= 128) return jacobi_sweeps_gs<GS, NW, 32>(work, cnt, L, P, sh);
+      break;
+    default:
+      break;
+  }
+  return jacobi_sweeps_gs<GS, NW, 0>(work, cnt, L, P, sh);
+}
+
+// Jacobi sweeps (see jacobi_sweeps_gs) by the first NT threads (a multiple
+// of the wave size) with jacobi_group<NT>(cnt) lanes per pair.
+template <int NT>
+__device__ __forceinline__ int jacobi_sweeps(double* work, int cnt, int L, int P,
+                                             FactorShared& sh) {
+  constexpr int NW = NT / kWave;
+  switch (jacobi_group<NT>(cnt)) {
+    case 64: return jacobi_sweeps_e<64, NW>(work, cnt, L, P, sh);
+    case 32: return jacobi_sweeps_e<32, NW>(work, cnt, L, P, sh);
+    case 16: return jacobi_sweeps_e<16, NW>(work, cnt, L, P, sh);
+    case 8: return jacobi_sweeps_e<8, NW>(work, cnt, L, P, sh);
+    case 4: return jacobi_sweeps_e<4, NW>(work, cnt, L, P, sh);
+    case 2: return jacobi_sweeps_gs<2, NW, 0>(work, cnt, L, P, sh);
+    default: return jacobi_sweeps_gs<1, NW, 0>(work, cnt, L, P, sh);
+  }
+}
+
+// Norms of the `cnt` rows (length L, pitch P) of `work` into sh.sig and the indices of the
+// min(rank, cnt) largest into sh.top (largest first, ties to the lower
+// index).  Returns that count.  Ends with a barrier.
+template <int NT>
+__device__ int top_rows(const double* work, int cnt, int L, int P, int rank,
+                        FactorShared& sh) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < cnt; i += NT) {
+    double s2 = 0.0;
+    const double* xi = work + static_cast<size_t>(i) * P;
+    for (int e = 0; e < L; ++e) s2 += xi[e] * xi[e];
+    sh.sig[i] = sqrt(s2);
+  }
+  __syncthreads();
+  const int rj = min(rank, cnt);
+  if (tid < kWave) {
+    bool taken0 = tid >= cnt, taken1 = tid + kWave >= cnt;
+    for (int k = 0; k < rj; ++k) {
+      double bv = -1.0;
+      int bi = 1 << 30;
+      if (!taken0) { bv = sh.sig[tid]; bi = tid; }
+      if (!taken1 && sh.sig[tid + kWave] > bv) { bv = sh.sig[tid + kWave]; bi = tid + kWave; }
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const double ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (bi == tid) taken0 = true;
+      if (bi == tid + kWave) taken1 = true;
+      if (tid == 0) sh.top[k] = bi;
+    }
+  }
+  __syncthreads();
+  return rj;
+}
+
+// Rank-r factors of the n x d matrix X whose element (t, c) is x(t, c), in
+// fp64 (build path, kFacThreads threads).  `work` holds n*d doubles (LDS or
+// global).  Jacobi runs on the shorter side of X:
+//   n <= d: rows of X; the rotated rows are sigma_i w_i^T and A = X W_r;
+//   n >  d: columns of X; they become sigma_i u_i, so A = X'[:, top] and
+//           w_i = X^T x'_i / sigma_i^2.
+// A (n x r_j) goes out through a_out(t, k, value), W (r_j x d) through
+// w_out(k, e, value); entries beyond r_j are not written.  Every thread of
+// the block calls it; it ends with a barrier.
+template <class Ld, class AOut, class WOut>
+__device__ void factor_matrix(const Ld& x, int n, int d, int rank, double* work,
+                              FactorShared& sh, const AOut& a_out, const WOut& w_out) {
+  const int tid = threadIdx.x;
+  const bool by_rows = n <= d;
+  const int cnt = by_rows ? n : d;  // vectors to orthogonalise
+  const int L = by_rows ? d : n;    // their length
+
+  for (int idx = tid; idx < n * d; idx += kFacThreads) {
+    const int t = idx / d;
+    const int c = idx - t * d;
+    const double v = x(t, c);
+    if (by_rows)
+      work[t * d + c] = v;
+    else
+      work[static_cast<size_t>(c) * n + t] = v;
+  }
+  __syncthreads();
+  jacobi_sweeps<kFacThreads>(work, cnt, L, L, sh);
+  const int rj = top_rows<kFacThreads>(work, cnt, L, L, rank, sh);
+
+  if (by_rows) {
+    for (int idx = tid; idx < rj * d; idx += kFacThreads) {
+      const int k = idx / d;
+      const int e = idx - k * d;
+      const double s = sh.sig[sh.top[k]];
+      w_out(k, e, s > 0.0 ? work[static_cast<size_t>(sh.top[k]) * L + e] / s : 0.0);
+    }
+    for (int idx = tid; idx < n * rj; idx += kFacThreads) {
+      const int t = idx / rj;
+      const int k = idx - t * rj;
+      const double s = sh.sig[sh.top[k]];
+      double acc = 0.0;
+      if (s > 0.0) {
+        const double* wi = work + static_cast<size_t>(sh.top[k]) * L;
+        for (int e = 0; e < d; ++e) acc += x(t, e) * wi[e];
+        acc /= s;
+      }
+      a_out(t, k, acc);
+    }
+  } else {
+    for (int idx = tid; idx < n * rj; idx += kFacThreads) {
+      const int t = idx / rj;
+      const int k = idx - t * rj;
+      a_out(t, k, work[static_cast<size_t>(sh.top[k]) * L + t]);
+    }
+    for (int idx = tid; idx < rj * d; idx += kFacThreads) {
+      const int k = idx / d;
+      const int e = idx - k * d;
+      const double s = sh.sig[sh.top[k]];
+      double acc = 0.0;
+      if (s > 0.0) {
+        const double* xi = work + static_cast<size_t>(sh.top[k]) * L;
+        for (int t = 0; t < n; ++t) acc += x(t, e) * xi[t];
+        acc /= s * s;
+      }
+      w_out(k, e, acc);
+    }
+  }
+  __syncthreads();
+}
+
+// Build: one item per (unit, span, K or V); the span's rows are read from
+// the row-major K/V inputs.  A_K rows at the span's padded offset, A_V in
+// transposed 16-row tiles, W_K rows [r][d], W_V in the paired layout
+// (layout.h).
 template <int DT, bool kLds>
 __global__ __launch_bounds__(kFacThreads) void factor_kernel(
     const typename Elem<DT>::T* __restrict__ K, const typename Elem<DT>::T* __restrict__ V,
@@ -40,10 +397,7 @@ __global__ __launch_bounds__(kFacThreads) void factor_kernel(
     typename Elem<DT>::T* __restrict__ w_v, double* __restrict__ scratch, size_t slab) {
   typedef Elem<DT> E;
   typedef typename E::T ST;
-  const int tid = threadIdx.x;
-  __shared__ double sig[128];
-  __shared__ int top[128];
-  __shared__ int s_rot;
+  __shared__ FactorShared sh;
   double* work;
   if constexpr (kLds) {
     __shared__ double lds_work[kLdsWork];
@@ -64,148 +418,429 @@ __global__ __launch_bounds__(kFacThreads) void factor_kernel(
     if (small != kLds) continue;
     const int st = span_start[static_cast<size_t>(b) * S + j];
     const ST* X = (kv ? V : K) + (static_cast<size_t>(u) * T + st) * d;
-    const bool by_rows = n <= d;
-    const int cnt = by_rows ? n : d;  // vectors to orthogonalise
-    const int L = by_rows ? d : n;    // their length
-
-    for (int idx = tid; idx < n * d; idx += kFacThreads) {
-      const int t = idx / d;
-      const int c = idx - t * d;
-      const double x = static_cast<double>(E::ld(X, idx));
-      if (by_rows)
-        work[t * d + c] = x;
+    const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
+    auto x = [&](int t, int c) -> double {
+      return static_cast<double>(E::ld(X, static_cast<size_t>(t) * d + c));
+    };
+    auto a_out = [&](int t, int k, double val) {
+      if (kv)
+        a_v[static_cast<size_t>(u) * Np * rank + avt_off(tp + t, k, rank)] = E::from_f64(val);
       else
-        work[static_cast<size_t>(c) * n + t] = x;
-    }
-    __syncthreads();
+        a_k[(static_cast<size_t>(u) * Np + tp + t) * rank + k] = E::from_f64(val);
+    };
+    auto w_out = [&](int k, int e, double val) {
+      if (kv)
+        w_v[static_cast<size_t>(u) * S * d * rank4(rank) + wvt_off(j, k, e, d, rank)] =
+            E::from_f64(val);
+      else
+        w_k[((static_cast<size_t>(u) * S + j) * rank + k) * d + e] = E::from_f64(val);
+    };
+    factor_matrix(x, n, d, rank, work, sh, a_out, w_out);
+  }
+}
 
-    // ---- one-sided Jacobi sweeps
-    const int cnt2 = cnt + (cnt & 1);
-    const int npairs = cnt2 / 2;
-    int gs = kWave;
-    while (gs > 1 && gs * npairs > kFacThreads) gs >>= 1;
-    const int g = tid / gs;
-    const int li = tid - g * gs;
-    for (int sweep = 0; sweep < kMaxSweeps && cnt2 > 1; ++sweep) {
-      if (tid == 0) s_rot = 0;
-      __syncthreads();
-      for (int r = 0; r < cnt2 - 1; ++r) {
-        if (g < npairs) {
-          const int pa = g == 0 ? 0 : ((g - 1 + r) % (cnt2 - 1)) + 1;
-          const int pb = ((cnt2 - 2 - g + r) % (cnt2 - 1)) + 1;
-          if (pa < cnt && pb < cnt) {
-            double* xa = work + static_cast<size_t>(pa) * L;
-            double* xb = work + static_cast<size_t>(pb) * L;
-            double al = 0.0, be = 0.0, ga = 0.0;
-            for (int e = li; e < L; e += gs) {
-              const double x = xa[e], y = xb[e];
-              al += x * x;
-              be += y * y;
-              ga += x * y;
-            }
-            al = group_sum(al, gs);
-            be = group_sum(be, gs);
-            ga = group_sum(ga, gs);
-            if (ga != 0.0 && fabs(ga) > kOrthTol * sqrt(al * be)) {
-              const double zeta = (be - al) / (2.0 * ga);
-              const double t = copysign(1.0, zeta) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-              const double cs = 1.0 / sqrt(1.0 + t * t);
-              const double sn = cs * t;
-              for (int e = li; e < L; e += gs) {
-                const double x = xa[e], y = xb[e];
-                xa[e] = cs * x - sn * y;
-                xb[e] = sn * x + cs * y;
-              }
-              if (li == 0) s_rot = 1;
-            }
-          }
+// Streaming segmentation (SEKV, Metodologia 1 and 2 applied to decoded
+// tokens): a sequence whose new token is an anchor (surprisal above the
+// threshold) closes the non-empty full-resolution run after its previous
+// anchor into span j = n_spans[b], with the build's summary, value mean,
+// ln|S| and factors, computed from the stored rows.  One workgroup per
+// (unit, K or V) item; the K item also writes the summary, the V item the
+// value mean, and the K item of KV head 0 the span tables.  Each item then
+// zeroes its unit's rows of the run, which leave the full-resolution set
+// (the append kernel, next in stream order, updates counts and positions).
+//
+// A closing sits on the decode loop's critical path, so this kernel is built
+// for latency: one wave per SIMD (a Jacobi round costs the dependency depth
+// of its fp64 arithmetic, not parallelism), the run's rows X (n x d) read
+// once from the tiled store with 16-byte lane loads, and an LDS-resident
+// fp64 Gram matrix:
+//   rows form, G = X X^T = U S^2 U^T (n x n), when X fits in LDS beside it:
+//     the rotated rows are sigma_i^2 u_i^T, so A = U_r S_r and
+//     W = S_r^-1 U_r^T X;
+//   cols form, G = X^T X = W S^2 W^T (d x d), otherwise (X streamed in
+//     32-row blocks): the rotated rows are sigma_i^2 w_i^T, so W = W_r^T
+//     and A = X W_r.
+// Squaring the singular values costs accuracy only in the small ones, far
+// below the storage rounding for the leading r.
+constexpr int kCloseThreads = 256;
+constexpr int kCloseWaves = kCloseThreads / kWave;
+constexpr int kCloseWork = 128 * 132;  // doubles: G with its padded pitch (+ X)
+constexpr int kBlock = 32;             // rows of X per streamed block
+
+// 8 consecutive stored elements (16-byte aligned) as floats.
+template <int DT>
+__device__ __forceinline__ void load8(const typename Elem<DT>::T* p, float (&v)[8]) {
+  if constexpr (DT == kBF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// Visits the lane vectors of a unit's tiled full-resolution store (K16 for
+// keys, V32 for values) that hold rows [lo, hi): f(p, row[8], col[8]) gets
+// the vector's address and the row and column of each of its 8 elements
+// (row -1: outside [lo, hi)).  Vectors are dealt to the block's waves.
+template <class Fn>
+__device__ __forceinline__ void for_row_vectors(bool vtile, int lo, int hi, int d, const Fn& f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  if (!vtile) {  // K16: 16 rows x 32 columns per block; a lane holds 8 columns of one row
+    const int ncb = d >> 5, tb0 = lo >> 4, nt = ((hi - 1) >> 4) - tb0 + 1;
+    for (int blk = wave; blk < nt * ncb; blk += kCloseWaves) {
+      const int tile = tb0 + blk / ncb, kk = blk % ncb;
+      const int row = tile * 16 + (lane & 15);
+      int rr[8], cc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        rr[e] = row >= lo && row < hi ? row : -1;
+        cc[e] = kk * 32 + (lane >> 4) * 8 + e;
+      }
+      f(static_cast<size_t>(tile * ncb + kk) * 512 + lane * 8, rr, cc);
+    }
+  } else {  // V32: 32 rows x 16 columns per block; a lane holds 8 rows of one column
+    const int ncb = d >> 4, tb0 = lo >> 5, nt = ((hi - 1) >> 5) - tb0 + 1;
+    for (int blk = wave; blk < nt * ncb; blk += kCloseWaves) {
+      const int tile = tb0 + blk / ncb, cb = blk % ncb;
+      const int g = lane >> 4;
+      int rr[8], cc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = tile * 32 + v32_row(g, e);
+        rr[e] = row >= lo && row < hi ? row : -1;
+        cc[e] = cb * 16 + (lane & 15);
+      }
+      f(static_cast<size_t>(tile * ncb + cb) * 512 + lane * 8, rr, cc);
+    }
+  }
+}
+
+// G[a][b] (a, b < m, pitch P) += sum over q < len of Y(q, a) Y(q, b) for
+// an LDS matrix of floats, in fp64 and in order of q; thread -> B x B block
+// of G (accumulated in registers g).  kByRow: Y(q, i) = y[i * ys + q] (X
+// rows, ys the row pitch; len and ys multiples of 4, so four values of q
+// come as one 16-byte vector); otherwise Y(q, i) = y[q * ys + i] (a
+// thread's B values are contiguous and, for B >= 4, read as vectors).
+template <int B, bool kByRow>
+__device__ __forceinline__ void gram_accumulate(const float* y, int ys, int m, int len,
+                                                double (&g)[B][B]) {
+  const int tid = threadIdx.x;
+  const int nb = (m + B - 1) / B;
+  if (tid >= nb * nb) return;
+  const int a0 = B * (tid / nb), b0 = B * (tid % nb);
+  const bool full = a0 + B <= m && b0 + B <= m;
+  if constexpr (kByRow) {
+    for (int q = 0; q < len; q += 4) {
+      float4 va[B], vb[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        va[i] = a0 + i < m ? *reinterpret_cast<const float4*>(y + (a0 + i) * ys + q)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        vb[i] = b0 + i < m ? *reinterpret_cast<const float4*>(y + (b0 + i) * ys + q)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+          double acc = g[i][k];
+          acc = fma(static_cast<double>(va[i].x), static_cast<double>(vb[k].x), acc);
+          acc = fma(static_cast<double>(va[i].y), static_cast<double>(vb[k].y), acc);
+          acc = fma(static_cast<double>(va[i].z), static_cast<double>(vb[k].z), acc);
+          g[i][k] = fma(static_cast<double>(va[i].w), static_cast<double>(vb[k].w), acc);
         }
+    }
+  } else {
+#pragma unroll 4
+    for (int q = 0; q < len; ++q) {
+      double ya[B], yb[B];
+      if (B % 4 == 0 && full) {
+#pragma unroll
+        for (int i = 0; i < B; i += 4) {
+          const float4 wa = *reinterpret_cast<const float4*>(y + q * ys + a0 + i);
+          const float4 wb = *reinterpret_cast<const float4*>(y + q * ys + b0 + i);
+          ya[i] = wa.x; ya[i + 1] = wa.y; ya[i + 2] = wa.z; ya[i + 3] = wa.w;
+          yb[i] = wb.x; yb[i + 1] = wb.y; yb[i + 2] = wb.z; yb[i + 3] = wb.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          ya[i] = a0 + i < m ? static_cast<double>(y[q * ys + a0 + i]) : 0.0;
+          yb[i] = b0 + i < m ? static_cast<double>(y[q * ys + b0 + i]) : 0.0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+#pragma unroll
+        for (int k = 0; k < B; ++k) g[i][k] = fma(ya[i], yb[k], g[i][k]);
+    }
+  }
+}
+
+// Writes the thread's block of G and zeroes columns m..Lp-1.  Ends with a
+// barrier.
+template <int B>
+__device__ __forceinline__ void gram_store(const double (&g)[B][B], int m, int Lp, double* G,
+                                           int P) {
+  const int tid = threadIdx.x;
+  const int nb = (m + B - 1) / B;
+  if (tid < nb * nb) {
+    const int a0 = B * (tid / nb), b0 = B * (tid % nb);
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+#pragma unroll
+      for (int k = 0; k < B; ++k)
+        if (a0 + i < m && b0 + k < m) G[(a0 + i) * P + b0 + k] = g[i][k];
+  }
+  for (int idx = tid; idx < m * (Lp - m); idx += kCloseThreads) {
+    const int a = idx / (Lp - m);
+    G[a * P + m + (idx - a * (Lp - m))] = 0.0;
+  }
+  __syncthreads();
+}
+
+template <int DT>
+__global__ __launch_bounds__(kCloseThreads) void close_kernel(
+    const float* __restrict__ h_new, const float* __restrict__ theta,
+    const int32_t* __restrict__ last_anchor, const int32_t* __restrict__ n_full,
+    const int32_t* __restrict__ n_spans, const float* __restrict__ h_full,
+    const int32_t* __restrict__ full_pos, int32_t* __restrict__ span_start,
+    int32_t* __restrict__ span_len, int32_t* __restrict__ tok_off,
+    int32_t* __restrict__ tok_pad, float* __restrict__ log_len, int32_t* __restrict__ span_id,
+    typename Elem<DT>::T* __restrict__ k_full, typename Elem<DT>::T* __restrict__ v_full,
+    typename Elem<DT>::T* __restrict__ summary, typename Elem<DT>::T* __restrict__ vmean,
+    typename Elem<DT>::T* __restrict__ a_k, typename Elem<DT>::T* __restrict__ a_v,
+    typename Elem<DT>::T* __restrict__ w_k, typename Elem<DT>::T* __restrict__ w_v, int T,
+    int d, int S, int Sp, int F, int Fp, int Np, int Hkv, int rank, int n_items) {
+  typedef Elem<DT> E;
+  typedef typename E::T ST;
+  __shared__ FactorShared sh;
+  __shared__ __align__(16) double work[kCloseWork];
+  __shared__ __align__(16) float stage[kBlock * (128 + 4)];  // a streamed block of X rows
+  __shared__ double part[kCloseThreads];  // partial column sums
+  __shared__ double red[kCloseWaves];
+  const int tid = threadIdx.x;
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int kv = item & 1;
+    const int u = item >> 1;
+    const int b = u / Hkv;
+    const int h = u - b * Hkv;
+    const int la = last_anchor[b];
+    const int n = n_full[b] - la - 1;
+    if (!(h_new[b] > theta[b]) || la < 0 || n <= 0) continue;
+    const int j = n_spans[b];
+    const int r0 = la + 1;
+    const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
+    ST* xs = (kv ? v_full : k_full) + static_cast<size_t>(u) * Fp * d;
+
+    // ---- layout.  Rows form (G = X X^T, m = n) when n <= d, else cols
+    // form (G = X^T X, m = d).  X rows are staged as floats with pitch
+    // xp = d + 4 (rows start 4 banks apart, so a wave reading one element
+    // of 16 rows hits 16 bank groups, and stay 16-byte aligned).  While the
+    // rows form accumulates G in registers, X sits at the start of `work`,
+    // where G goes afterwards; X is kept after G (x_after) when both fit,
+    // and is otherwise streamed from global memory in 32-row blocks.
+    const int xp = d + 4;
+    const bool rows_form = n <= d;
+    const int m = rows_form ? n : d;
+    const int gs = jacobi_group<kCloseThreads>(m);
+    int Lp = gs;  // rows of G padded with zeros to gs * E columns, E a power of two
+    while (Lp < m) Lp *= 2;
+    const int P = jacobi_pitch(Lp, gs);
+    const bool x_after = sizeof(double) * m * P + sizeof(float) * static_cast<size_t>(n) * xp <=
+                         sizeof(double) * kCloseWork;
+    float* const x_post = x_after ? reinterpret_cast<float*>(work + m * P) : nullptr;
+    float* const x_pre = rows_form ? reinterpret_cast<float*>(work) : x_post;
+    // rows [t0, t0 + rb) of X into dst (row pitch xp)
+    auto load_rows = [&](int t0, int rb, float* dst) {
+      for_row_vectors(kv != 0, r0 + t0, r0 + t0 + rb, d, [&](size_t off, const int (&rr)[8],
+                                                               const int (&cc)[8]) {
+        float v[8];
+        load8<DT>(xs + off, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (rr[e] >= 0) dst[(rr[e] - r0 - t0) * xp + cc[e]] = v[e];
+      });
+      __syncthreads();
+    };
+    // visits X in order of rows: f(rows pointer, t0, rb), whole when
+    // resident at x, else in 32-row blocks through `stage`
+    auto for_blocks = [&](const float* x, const auto& f) {
+      if (x != nullptr) {
+        f(x, 0, n);
+        return;
+      }
+      for (int t0 = 0; t0 < n; t0 += kBlock) {
+        const int rb = min(kBlock, n - t0);
+        load_rows(t0, rb, stage);
+        f(static_cast<const float*>(stage), t0, rb);
         __syncthreads();
       }
-      const int rotated = s_rot;
+    };
+    if (x_pre != nullptr) load_rows(0, n, x_pre);
+
+    // ---- summary (K item) or value mean (V item): column sums in fp64, in
+    // row order; ng groups of d threads take interleaved rows, then the
+    // groups are added in order
+    const int ng = kCloseThreads / d;
+    const int gi = tid / d;
+    const int c = tid - gi * d;
+    const float* hr = h_full + static_cast<size_t>(b) * F + r0;
+    double acc = 0.0;
+    for_blocks(x_pre, [&](const float* xr, int t0, int rb) {
+      for (int t = gi; t < rb; t += ng)
+        acc += kv ? static_cast<double>(xr[t * xp + c])
+                  : static_cast<double>(hr[t0 + t]) * static_cast<double>(xr[t * xp + c]);
+    });
+    part[gi * d + c] = acc;
+    __syncthreads();
+    double tot = 0.0;
+    if (tid < d)
+      for (int q = 0; q < ng; ++q) tot += part[q * d + tid];
+    if (kv == 0) {
+      const double sq = wave_sum(tot * tot);
+      if ((tid & (kWave - 1)) == 0) red[tid / kWave] = sq;
       __syncthreads();
-      if (!rotated) break;
+      double norm2 = 0.0;
+      for (int w = 0; w < d / kWave; ++w) norm2 += red[w];
+      if (tid < d)
+        summary[(static_cast<size_t>(u) * S + j) * d + tid] =
+            E::from_f64(norm2 > 0.0 ? tot / sqrt(norm2) : 0.0);
+    } else if (tid < d) {
+      vmean[static_cast<size_t>(u) * Sp * d + v32_off(j, tid, d)] =
+          E::from_f64(tot / static_cast<double>(n));
     }
-
-    // ---- singular values, top r_j (largest first, ties to lower index)
-    for (int i = tid; i < cnt; i += kFacThreads) {
-      double s2 = 0.0;
-      const double* xi = work + static_cast<size_t>(i) * L;
-      for (int e = 0; e < L; ++e) s2 += xi[e] * xi[e];
-      sig[i] = sqrt(s2);
-    }
-    __syncthreads();
-    const int rj = min(rank, cnt);
-    if (tid < kWave) {
-      bool taken0 = tid >= cnt, taken1 = tid + kWave >= cnt;
-      for (int k = 0; k < rj; ++k) {
-        double bv = -1.0;
-        int bi = 1 << 30;
-        if (!taken0) { bv = sig[tid]; bi = tid; }
-        if (!taken1 && sig[tid + kWave] > bv) { bv = sig[tid + kWave]; bi = tid + kWave; }
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-          const double ov = __shfl_xor(bv, o, kWave);
-          const int oi = __shfl_xor(bi, o, kWave);
-          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        if (bi == tid) taken0 = true;
-        if (bi == tid + kWave) taken1 = true;
-        if (tid == 0) top[k] = bi;
+    if (kv == 0 && h == 0) {
+      const int st = full_pos[static_cast<size_t>(b) * F + r0];
+      if (tid == 0) {
+        span_start[static_cast<size_t>(b) * S + j] = st;
+        span_len[static_cast<size_t>(b) * S + j] = n;
+        tok_off[static_cast<size_t>(b) * (S + 1) + j + 1] =
+            tok_off[static_cast<size_t>(b) * (S + 1) + j] + n;
+        tok_pad[static_cast<size_t>(b) * (S + 1) + j + 1] = tp + round_up(n, 16);
+        log_len[static_cast<size_t>(b) * S + j] = static_cast<float>(log(static_cast<double>(n)));
       }
+      for (int p = st + tid; p < min(st + n, T); p += kCloseThreads)
+        span_id[static_cast<size_t>(b) * T + p] = j;
     }
     __syncthreads();
 
-    // ---- factors: A_K rows (padded span offsets), A_V transposed 16-row
-    // tiles, W_K rows [r][d], W_V transposed [d][r] (layout.h)
-    const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
-    auto a_at = [&](int t, int k) -> ST& {
-      if (kv) return a_v[static_cast<size_t>(u) * Np * rank + avt_off(tp + t, k, rank)];
-      return a_k[(static_cast<size_t>(u) * Np + tp + t) * rank + k];
-    };
-    auto w_at = [&](int k, int e) -> ST& {
-      if (kv) return w_v[static_cast<size_t>(u) * S * d * rank4(rank) + wvt_off(j, k, e, d, rank)];
-      return w_k[((static_cast<size_t>(u) * S + j) * rank + k) * d + e];
-    };
-    if (by_rows) {
-      for (int idx = tid; idx < rj * d; idx += kFacThreads) {
-        const int k = idx / d;
-        const int e = idx - k * d;
-        const double s = sig[top[k]];
-        w_at(k, e) = E::from_f64(s > 0.0 ? work[static_cast<size_t>(top[k]) * L + e] / s : 0.0);
+    // ---- Gram matrix, Jacobi, the r_j largest (sig = sigma^2)
+    auto gram = [&](auto bsize) {
+      constexpr int B = decltype(bsize)::value;
+      double g[B][B] = {};
+      if (rows_form) {
+        gram_accumulate<B, true>(x_pre, xp, m, d, g);
+        __syncthreads();  // X is read before G takes its place
+      } else {
+        for_blocks(x_pre, [&](const float* xr, int, int rb) {
+          gram_accumulate<B, false>(xr, xp, m, rb, g);
+        });
       }
-      for (int idx = tid; idx < n * rj; idx += kFacThreads) {
-        const int t = idx / rj;
-        const int k = idx - t * rj;
-        const double s = sig[top[k]];
-        double acc = 0.0;
-        if (s > 0.0) {
-          const double* wi = work + static_cast<size_t>(top[k]) * L;
-          for (int e = 0; e < d; ++e)
-            acc += static_cast<double>(E::ld(X, static_cast<size_t>(t) * d + e)) * wi[e];
-          acc /= s;
+      gram_store<B>(g, m, Lp, work, P);
+    };
+    if (m > 64)
+      gram(std::integral_constant<int, 8>());
+    else if (m > 32)
+      gram(std::integral_constant<int, 4>());
+    else if (m > 16)
+      gram(std::integral_constant<int, 2>());
+    else
+      gram(std::integral_constant<int, 1>());
+    jacobi_sweeps<kCloseThreads>(work, m, Lp, P, sh);
+    const int rj = top_rows<kCloseThreads>(work, m, Lp, P, rank, sh);
+    if (rows_form && x_post != nullptr) load_rows(0, n, x_post);
+
+    auto a_store = [&](int t, int k, double val) {
+      if (kv)
+        a_v[static_cast<size_t>(u) * Np * rank + avt_off(tp + t, k, rank)] = E::from_f64(val);
+      else
+        a_k[(static_cast<size_t>(u) * Np + tp + t) * rank + k] = E::from_f64(val);
+    };
+    auto w_store = [&](int k, int e, double val) {
+      if (kv)
+        w_v[static_cast<size_t>(u) * S * d * rank4(rank) + wvt_off(j, k, e, d, rank)] =
+            E::from_f64(val);
+      else
+        w_k[((static_cast<size_t>(u) * S + j) * rank + k) * d + e] = E::from_f64(val);
+    };
+    if (rows_form) {
+      // A[t][k] = sigma_k u_k[t] = row_k[t] / sigma_k
+      for (int o = tid; o < n * rj; o += kCloseThreads) {
+        const int t = o / rj;
+        const int k = o - t * rj;
+        const double lam = sh.sig[sh.top[k]];
+        a_store(t, k, lam > 0.0 ? work[sh.top[k] * P + t] / sqrt(lam) : 0.0);
+      }
+      // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3; thread -> kOut outputs
+      constexpr int kOut = 32 * 128 / kCloseThreads;
+      double wacc[kOut] = {};
+      for_blocks(x_post, [&](const float* xr, int t0, int rb) {
+#pragma unroll
+        for (int q = 0; q < kOut; ++q) {
+          const int o = tid + q * kCloseThreads;
+          if (o < rj * d) {
+            const int k = o / d;
+            const int e = o - k * d;
+            const double* uk = work + sh.top[k] * P + t0;
+            for (int t = 0; t < rb; ++t)
+              wacc[q] = fma(static_cast<double>(xr[t * xp + e]), uk[t], wacc[q]);
+          }
         }
-        a_at(t, k) = E::from_f64(acc);
+      });
+#pragma unroll
+      for (int q = 0; q < kOut; ++q) {
+        const int o = tid + q * kCloseThreads;
+        if (o < rj * d) {
+          const int k = o / d;
+          const double lam = sh.sig[sh.top[k]];
+          w_store(k, o - k * d, lam > 0.0 ? wacc[q] / (lam * sqrt(lam)) : 0.0);
+        }
       }
     } else {
-      for (int idx = tid; idx < n * rj; idx += kFacThreads) {
-        const int t = idx / rj;
-        const int k = idx - t * rj;
-        a_at(t, k) = E::from_f64(work[static_cast<size_t>(top[k]) * L + t]);
+      // W[k] = w_k = row_k / sigma_k^2
+      for (int o = tid; o < rj * d; o += kCloseThreads) {
+        const int k = o / d;
+        const int e = o - k * d;
+        const double lam = sh.sig[sh.top[k]];
+        w_store(k, e, lam > 0.0 ? work[sh.top[k] * P + e] / lam : 0.0);
       }
-      for (int idx = tid; idx < rj * d; idx += kFacThreads) {
-        const int k = idx / d;
-        const int e = idx - k * d;
-        const double s = sig[top[k]];
-        double acc = 0.0;
-        if (s > 0.0) {
-          const double* xi = work + static_cast<size_t>(top[k]) * L;
-          for (int t = 0; t < n; ++t)
-            acc += static_cast<double>(E::ld(X, static_cast<size_t>(t) * d + e)) * xi[t];
-          acc /= s * s;
+      // A[t][k] = X[t] . w_k
+      for_blocks(x_post, [&](const float* xr, int t0, int rb) {
+        for (int o = tid; o < rb * rj; o += kCloseThreads) {
+          const int t = o / rj;
+          const int k = o - t * rj;
+          const double lam = sh.sig[sh.top[k]];
+          double s = 0.0;
+          if (lam > 0.0) {
+            const double* wk = work + sh.top[k] * P;
+            for (int e = 0; e < d; ++e) s = fma(static_cast<double>(xr[t * xp + e]), wk[e], s);
+            s /= lam;
+          }
+          a_store(t0 + t, k, s);
         }
-        w_at(k, e) = E::from_f64(acc);
-      }
+      });
     }
+    __syncthreads();
+
+    // ---- the run leaves the full-resolution set
+    for_row_vectors(kv != 0, r0, r0 + n, d, [&](size_t off, const int (&rr)[8],
+                                                const int (&cc)[8]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (rr[e] >= 0) xs[off + e] = E::from_f64(0.0);
+      (void)cc;
+    });
     __syncthreads();
   }
 }
@@ -268,7 +903,29 @@ hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t 
   return hipSuccess;
 }
 
+template <int DT>
+hipError_t close_impl(const rskv_cache* c, const float* h, hipStream_t st,
+                      const KernelEvents* ev) {
+  typedef typename Elem<DT>::T T;
+  const auto& v = c->dev;
+  const int n_items = 2 * c->B * c->Hkv;
+  return launch(close_kernel<DT>, dim3(c->close_grid), dim3(kCloseThreads), 0, st, ev, h,
+                static_cast<const float*>(v.theta), static_cast<const int32_t*>(v.last_anchor),
+                static_cast<const int32_t*>(v.n_full), static_cast<const int32_t*>(v.n_spans),
+                static_cast<const float*>(v.h_full), static_cast<const int32_t*>(v.full_pos),
+                v.span_start, v.span_len, v.tok_off, v.tok_pad, v.log_len, v.span_id,
+                static_cast<T*>(v.k_full), static_cast<T*>(v.v_full), static_cast<T*>(v.summary),
+                static_cast<T*>(v.vmean), static_cast<T*>(v.a_k), static_cast<T*>(v.a_v),
+                static_cast<T*>(v.w_k), static_cast<T*>(v.w_v), c->T, c->d, c->S, c->Sp, c->F,
+                c->Fp, c->Np, c->Hkv, c->rank, n_items);
+}
+
 }  // namespace
+
+hipError_t launch_close(const rskv_cache* c, const float* h, hipStream_t st,
+                        const KernelEvents* ev) {
+  return c->dtype == kBF16 ? close_impl<kBF16>(c, h, st, ev) : close_impl<kF32>(c, h, st, ev);
+}
 
 hipError_t launch_factor(rskv_cache* c, const void* K, const void* V, hipStream_t st,
                          std::string* err) {

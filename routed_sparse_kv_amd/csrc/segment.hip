@@ -11,7 +11,11 @@
 //   3. a second chunked scan numbers spans, records span starts/ends and
 //      compacts the full-resolution positions;
 //   4. a scan over spans turns ends into lengths and token offsets.
-// The sequence is read a handful of times; segmentation runs once per cache.
+// It also reports what streaming segmentation needs at append time: the
+// anchor threshold (the smallest anchor surprisal, whose order key is K*)
+// and the full-resolution row of the last anchor (the rows after it are
+// the tail run).  The sequence is read a handful of times; segmentation runs
+// once per cache.
 #include "cache.h"
 #include "common.h"
 
@@ -19,6 +23,11 @@ namespace rskv {
 namespace {
 
 constexpr int kSegThreads = 1024;
+
+// Inverse of f32_order_key (a folded zero comes back as +0).
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
 
 __global__ __launch_bounds__(kSegThreads) void segment_kernel(
     const float* __restrict__ H_all, int T, int n_a, int32_t* __restrict__ span_id_all,
@@ -166,6 +175,10 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(
     cnt[2] = n_full;
     cnt[3] = n_tok;
     cnt[4] = n_pad;
+    // the tail run holds the T - 1 - last positions after the last anchor
+    cnt[5] = last >= 0 ? n_full - (T - 1 - last) - 1 : -1;
+    const float inf = __builtin_huge_valf();
+    cnt[6] = __float_as_int(last >= 0 ? f32_from_order_key(kstar) : inf);
   }
 }
 

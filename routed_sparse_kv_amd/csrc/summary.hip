@@ -8,7 +8,8 @@
 //   ell_j  = ln |S_j|,
 // accumulated in fp64 and rounded once to the cache dtype.  The anchors and
 // the lead/tail runs are copied row by row into the packed full-resolution
-// store, which also receives decode-time appends.
+// store, which also receives decode-time appends (with streaming
+// segmentation: a decoded anchor closes the run before it into a span).
 #include "cache.h"
 #include "common.h"
 
@@ -58,13 +59,16 @@ __global__ __launch_bounds__(128) void summary_kernel(
     log_len[static_cast<size_t>(b) * S + j] = static_cast<float>(log(static_cast<double>(len)));
 }
 
-// Row i < n_full0[b] of unit u: K/V row full_pos[b][i] of the context.
+// Row i < n_full0[b] of unit u: K/V row full_pos[b][i] of the context; the
+// blocks of KV head 0 also keep the row's surprisal (streaming segmentation
+// weighs the rows of a later span by it).
 template <int DT>
 __global__ __launch_bounds__(128) void pack_kernel(
-    const typename Elem<DT>::T* __restrict__ K, const typename Elem<DT>::T* __restrict__ V,
-    const int32_t* __restrict__ full_pos, const int32_t* __restrict__ n_full0, int T, int d,
-    int F, int Fp, int Hkv, typename Elem<DT>::T* __restrict__ kf,
-    typename Elem<DT>::T* __restrict__ vf) {
+    const float* __restrict__ H, const typename Elem<DT>::T* __restrict__ K,
+    const typename Elem<DT>::T* __restrict__ V, const int32_t* __restrict__ full_pos,
+    const int32_t* __restrict__ n_full0, int T, int d, int F, int Fp, int Hkv,
+    typename Elem<DT>::T* __restrict__ kf, typename Elem<DT>::T* __restrict__ vf,
+    float* __restrict__ h_full) {
   const int i = blockIdx.x;
   const int u = blockIdx.y;
   const int b = u / Hkv;
@@ -76,18 +80,41 @@ __global__ __launch_bounds__(128) void pack_kernel(
     kf[dst + k16_off(i, c, d)] = K[src + c];
     vf[dst + v32_off(i, c, d)] = V[src + c];
   }
+  if (u == b * Hkv && threadIdx.x == 0)
+    h_full[static_cast<size_t>(b) * F + i] = H[static_cast<size_t>(b) * T + pos];
 }
 
-// One workgroup per sequence: append (k, v) of every KV head at row
-// n_full[b], record its position T + (row - n_full0[b]), then bump n_full.
+// One workgroup per sequence: store the decoded token (k, v of every KV
+// head, surprisal h[b] or 0 without h) as a full-resolution row at
+// position `pos`.  Streaming segmentation (SEKV, Metodologia 1, applied to
+// decoded tokens): the token is an anchor iff its surprisal exceeds the
+// sequence's threshold.  If it is and the run after the previous anchor is
+// non-empty, the close kernel has just turned that run into span
+// n_spans[b]: the run's rows are released and the token takes the first of
+// them (only when `closed` says the close kernel ran).  The token then
+// becomes the last anchor.
 template <int DT>
 __global__ __launch_bounds__(256) void append_kernel(
     const typename Elem<DT>::T* __restrict__ k, const typename Elem<DT>::T* __restrict__ v,
-    int Hkv, int d, int F, int Fp, int T, int32_t* __restrict__ n_full,
-    const int32_t* __restrict__ n_full0, int32_t* __restrict__ full_pos,
-    typename Elem<DT>::T* __restrict__ kf, typename Elem<DT>::T* __restrict__ vf) {
+    const float* __restrict__ h_new, int closed, int pos, int Hkv, int d, int F, int Fp,
+    const float* __restrict__ theta, int32_t* __restrict__ n_full, int32_t* __restrict__ n_spans,
+    int32_t* __restrict__ last_anchor, int32_t* __restrict__ full_pos,
+    float* __restrict__ h_full, typename Elem<DT>::T* __restrict__ kf,
+    typename Elem<DT>::T* __restrict__ vf) {
   const int b = blockIdx.x;
-  const int row = n_full[b];
+  const int nf = n_full[b];
+  const int la = last_anchor[b];
+  const float hb = h_new != nullptr ? h_new[b] : 0.f;
+  const bool anchor = h_new != nullptr && hb > theta[b];
+  const bool close = closed && anchor && la >= 0 && nf - la - 1 > 0;
+  const int row = close ? la + 1 : nf;
+  float* hf = h_full + static_cast<size_t>(b) * F;
+  int32_t* fp = full_pos + static_cast<size_t>(b) * F;
+  __syncthreads();  // every thread has read the counts
+  for (int i = row + threadIdx.x; i < nf; i += blockDim.x) {
+    fp[i] = -1;
+    hf[i] = 0.f;
+  }
   for (int idx = threadIdx.x; idx < Hkv * d; idx += blockDim.x) {
     const int h = idx / d;
     const int c = idx - h * d;
@@ -97,8 +124,11 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    full_pos[static_cast<size_t>(b) * F + row] = T + (row - n_full0[b]);
+    fp[row] = pos;
+    hf[row] = hb;
     n_full[b] = row + 1;
+    if (close) n_spans[b] += 1;
+    if (anchor) last_anchor[b] = row;
   }
 }
 
@@ -116,24 +146,26 @@ hipError_t summary_impl(const rskv_cache* c, const float* H, const void* K, cons
 }
 
 template <int DT>
-hipError_t pack_impl(const rskv_cache* c, const void* K, const void* V, hipStream_t st) {
+hipError_t pack_impl(const rskv_cache* c, const float* H, const void* K, const void* V,
+                     hipStream_t st) {
   typedef typename Elem<DT>::T T;
   dim3 grid(c->F, c->B * c->Hkv);
-  hipLaunchKernelGGL(pack_kernel<DT>, grid, dim3(128), 0, st, static_cast<const T*>(K),
+  hipLaunchKernelGGL(pack_kernel<DT>, grid, dim3(128), 0, st, H, static_cast<const T*>(K),
                      static_cast<const T*>(V), c->dev.full_pos, c->dev.n_full0, c->T, c->d,
                      c->F, c->Fp, c->Hkv, static_cast<T*>(c->dev.k_full),
-                     static_cast<T*>(c->dev.v_full));
+                     static_cast<T*>(c->dev.v_full), c->dev.h_full);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t append_impl(rskv_cache* c, const void* k, const void* v, hipStream_t st) {
+hipError_t append_impl(const rskv_cache* c, const void* k, const void* v, const float* h,
+                       bool closed, int pos, hipStream_t st, const KernelEvents* ev) {
   typedef typename Elem<DT>::T T;
-  hipLaunchKernelGGL(append_kernel<DT>, dim3(c->B), dim3(256), 0, st, static_cast<const T*>(k),
-                     static_cast<const T*>(v), c->Hkv, c->d, c->F, c->Fp, c->T, c->dev.n_full,
-                     c->dev.n_full0, c->dev.full_pos, static_cast<T*>(c->dev.k_full),
-                     static_cast<T*>(c->dev.v_full));
-  return hipGetLastError();
+  const auto& a = c->dev;
+  return launch(append_kernel<DT>, dim3(c->B), dim3(256), 0, st, ev, static_cast<const T*>(k),
+                static_cast<const T*>(v), h, closed ? 1 : 0, pos, c->Hkv, c->d, c->F, c->Fp,
+                static_cast<const float*>(a.theta), a.n_full, a.n_spans, a.last_anchor,
+                a.full_pos, a.h_full, static_cast<T*>(a.k_full), static_cast<T*>(a.v_full));
 }
 
 }  // namespace
@@ -144,12 +176,15 @@ hipError_t launch_summary(const rskv_cache* c, const float* H, const void* K, co
                            : summary_impl<kF32>(c, H, K, V, st);
 }
 
-hipError_t launch_pack(const rskv_cache* c, const void* K, const void* V, hipStream_t st) {
-  return c->dtype == kBF16 ? pack_impl<kBF16>(c, K, V, st) : pack_impl<kF32>(c, K, V, st);
+hipError_t launch_pack(const rskv_cache* c, const float* H, const void* K, const void* V,
+                       hipStream_t st) {
+  return c->dtype == kBF16 ? pack_impl<kBF16>(c, H, K, V, st) : pack_impl<kF32>(c, H, K, V, st);
 }
 
-hipError_t launch_append(rskv_cache* c, const void* k, const void* v, hipStream_t st) {
-  return c->dtype == kBF16 ? append_impl<kBF16>(c, k, v, st) : append_impl<kF32>(c, k, v, st);
+hipError_t launch_append(const rskv_cache* c, const void* k, const void* v, const float* h,
+                         bool closed, int pos, hipStream_t st, const KernelEvents* ev) {
+  return c->dtype == kBF16 ? append_impl<kBF16>(c, k, v, h, closed, pos, st, ev)
+                           : append_impl<kF32>(c, k, v, h, closed, pos, st, ev);
 }
 
 }  // namespace rskv

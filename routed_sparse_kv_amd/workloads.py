@@ -206,6 +206,7 @@ class Workload:
     V: np.ndarray                 # [B][Hkv][T][d] stored dtype
     queries: List[np.ndarray]     # per step [B][Hq][d] stored dtype
     appends: Optional[List[tuple]]  # per step (k, v) [B][Hkv][d] or None
+    append_h: Optional[List[np.ndarray]]  # per step [B] fp32 surprisal of the appends
     P: Optional[np.ndarray]       # [1][d][d] fp32 or None
     anchor_pos: List[np.ndarray]  # per b, sorted anchor positions
     needles: Optional[List[np.ndarray]] = None  # per b, needle span starts
@@ -221,7 +222,9 @@ def generate(name: str, workers: Optional[int] = None, **overrides) -> Workload:
     Streams: sequence structure (anchors, surprisal, run directions, needles)
     comes from ``default_rng([seed, b])``; the token noise of KV head h of
     sequence b from ``default_rng([seed, b, h])``; queries and appends from
-    ``default_rng([seed, b, 'q'])``.  Units are generated on a thread pool;
+    ``default_rng([seed, b, 2**21])``; the surprisal of the appended tokens,
+    drawn from the configuration's law, from ``default_rng([seed, b, 2**23])``.
+    Units are generated on a thread pool;
     the result does not depend on the number of workers.
     """
     cfg = config(name, **overrides)
@@ -240,6 +243,7 @@ def generate(name: str, workers: Optional[int] = None, **overrides) -> Workload:
     q_all = np.zeros((steps, B, Hq, d), np.float32)
     app_k = np.zeros((steps, B, Hkv, d), np.float32) if cfg.get("append") else None
     app_v = np.zeros((steps, B, Hkv, d), np.float32) if cfg.get("append") else None
+    app_h = np.zeros((steps, B), np.float32) if cfg.get("append") else None
     anchors, needles = [], []
 
     P = None
@@ -319,6 +323,8 @@ def generate(name: str, workers: Optional[int] = None, **overrides) -> Workload:
             else:
                 raise ValueError(cfg["query"])
         if app_k is not None:
+            hrng = np.random.default_rng([seed, b, 1 << 23])
+            app_h[:, b] = _draw_h(hrng, cfg["h_law"], steps).astype(np.float32)
             for h in range(Hkv):
                 mK, mV = tables[h][2], tables[h][3]
                 app_k[:, b, h] = qrng.standard_normal((steps, d)) + 2.0 * mK[-1]
@@ -357,10 +363,11 @@ def generate(name: str, workers: Optional[int] = None, **overrides) -> Workload:
             list(ex.map(unit_job, jobs))
 
     queries = [store(q_all[s], dt) for s in range(steps)]
-    appends = None
+    appends, append_h = None, None
     if app_k is not None:
         appends = [(store(app_k[s], dt), store(app_v[s], dt)) for s in range(steps)]
-    return Workload(cfg=cfg, H=H, K=K, V=V, queries=queries, appends=appends,
+        append_h = [app_h[s].copy() for s in range(steps)]
+    return Workload(cfg=cfg, H=H, K=K, V=V, queries=queries, appends=appends, append_h=append_h,
                     P=P, anchor_pos=anchors,
                     needles=needles if recipe == "clustered" else None)
 

@@ -55,7 +55,8 @@ def oracle_view(ex):
                 span_len=ex["span_len"].astype(np.int64), fr_pos=ex["full_pos"].astype(np.int64),
                 s=f("summary"), vbar=f("vmean"), ell=ex["log_len"].astype(np.float64),
                 KF=f("k_full"), VF=f("v_full"), AK=f("a_k"), AV=f("a_v"), BK=f("w_k"),
-                BV=f("w_v"))
+                BV=f("w_v"), HF=ex["h_full"].astype(np.float64),
+                theta=ex["theta"].astype(np.float64), la=ex["last_anchor"].astype(np.int64))
 
 
 def unit_view(ex, b, h):
@@ -73,7 +74,11 @@ def unit_view(ex, b, h):
                 fr_pos=ex["full_pos"][b:b + 1].astype(np.int64).copy(),
                 s=f("summary"), vbar=f("vmean"), ell=ex["log_len"][b:b + 1].astype(np.float64),
                 KF=f("k_full"), VF=f("v_full"), AK=f("a_k"), AV=f("a_v"), BK=f("w_k"),
-                BV=f("w_v"))
+                BV=f("w_v"), HF=ex["h_full"][b:b + 1].astype(np.float64),
+                theta=ex["theta"][b:b + 1].astype(np.float64),
+                la=ex["last_anchor"][b:b + 1].astype(np.int64), span_id=ex["span_id"][b:b + 1].copy(),
+                span_start=ex["span_start"][b:b + 1].astype(np.int64),
+                nt=ex["n_span_tokens"][b:b + 1].astype(np.int64))
 
 
 def decode_gpu(cache, q_np, tau, k_max, device="cuda"):

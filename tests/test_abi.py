@@ -19,7 +19,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     syms = declared_symbols()
-    for s in ("rskv_build_spans", "rskv_decode_step", "rskv_append_kv", "rskv_cache_export",
+    for s in ("rskv_build_spans", "rskv_decode_step", "rskv_append_kv", "rskv_append_token",
+              "rskv_cache_export",
               "rskv_cache_import", "rskv_cache_destroy", "rskv_last_error"):
         assert s in syms
 
@@ -41,6 +42,8 @@ def test_version_and_error_strings_without_gpu():
     lib.rskv_append_kv.argtypes = [ctypes.c_void_p] * 4
     assert lib.rskv_append_kv(None, None, None, None) == -6
     assert b"invalid cache handle" in lib.rskv_last_error()
+    lib.rskv_append_token.argtypes = [ctypes.c_void_p] * 5
+    assert lib.rskv_append_token(None, None, None, None, None) == -6
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
