@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (units)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--close-runs", default="",
+                    help="instead of the decode bench: span-closing latency for these run "
+                         "lengths, e.g. 4,16,32,64,128 (streaming segmentation)")
     return ap.parse_args()
 
 
@@ -139,12 +142,76 @@ def unit_view(ex, b, h):
                 BV=f("w_v"))
 
 
+def close_latency(args):
+    """Streaming segmentation: duration of the span-closing and append
+    kernels (HIP events carried by their dispatches) when every sequence of
+    the workload closes a run of n appended tokens at once.  Each run is
+    appended without anchors, then one token above every threshold closes
+    it; the first closing (the prefill tail runs) is not reported."""
+    import torch
+
+    import routed_sparse_kv_amd as rskv
+    from routed_sparse_kv_amd import workloads as W
+    runs = [int(x) for x in args.close_runs.split(",") if x]
+    reps = 3
+    cap = 1 + reps * sum(n + 1 for n in runs)
+    wl = W.generate(args.workload, steps=1)
+    cfg = wl.cfg
+    dev = torch.device("cuda:0")
+    dt = cfg["dtype"]
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+
+    def to_dev(a):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    cache = rskv.build_spans(torch.from_numpy(wl.H).to(dev), to_dev(wl.K), to_dev(wl.V),
+                             cfg["rank"], cfg["anchor_frac"], n_q_heads=cfg["Hq"],
+                             alpha=cfg["alpha"], tail_capacity=cap)
+    B, Hkv, d = cfg["B"], cfg["Hkv"], cfg["d"]
+    gen = torch.Generator(device=dev).manual_seed(int(cfg["seed"]))
+    h_none = torch.zeros(B, dtype=torch.float32, device=dev)
+    h_anchor = torch.full((B,), float(np.finfo(np.float32).max), dtype=torch.float32, device=dev)
+
+    def append(h):
+        k = torch.randn((B, Hkv, d), generator=gen, device=dev).to(tdt)
+        v = torch.randn((B, Hkv, d), generator=gen, device=dev).to(tdt)
+        rskv.append_token(cache, k, v, h)
+
+    append(h_anchor)  # closes the prefill tail runs
+    res = {}
+    for n in runs:
+        close_us, append_us = [], []
+        for _ in range(reps):
+            for _ in range(n):
+                append(h_none)
+            torch.cuda.synchronize()
+            cache.profile_enable(True)
+            append(h_anchor)
+            p = cache.profile_read()
+            cache.profile_enable(False)
+            close_us.append(p["close_ms"] * 1e3)
+            append_us.append(p["append_ms"] * 1e3)
+        res[str(n)] = {"close_us": float(np.mean(close_us)), "append_us": float(np.mean(append_us))}
+    torch.cuda.synchronize()
+    print(json.dumps({"metric": "span-closing kernel latency (streaming segmentation)",
+                      "unit": "us per closing append", "workload": args.workload,
+                      "closings_per_append": B, "workgroup_items": 2 * B * Hkv,
+                      "dtype": dt, "head_dim": d, "rank": cfg["rank"], "repeats": reps,
+                      "runs": res}))
+    cache.close()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.close_runs:
+        close_latency(args)
+        return
     import torch
 
     import routed_sparse_kv_amd as rskv
