@@ -45,14 +45,19 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (units)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--factor-tier", default="hbm", choices=["hbm", "host"],
+                    help="where the span factors live (host: pinned host memory, read by "
+                         "the kernels over the host link)")
     ap.add_argument("--close-runs", default="",
                     help="instead of the decode bench: span-closing latency for these run "
                          "lengths, e.g. 4,16,32,64,128 (streaming segmentation)")
     return ap.parse_args()
 
 
-def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg):
-    """Algorithmic bytes of one step, total and of the attention kernel.
+def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg, factors_only=False):
+    """Algorithmic bytes of one step, total and of the attention kernel
+    (with factors_only: the expanded spans' factor bytes, what the host
+    factor tier moves over the host link).
 
     Per unit (sequence b, KV head h), with b_e bytes per stored element:
       routing  : n_s d b_e                       (summaries, read once)
@@ -67,7 +72,7 @@ def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg):
     d, r, G = cfg["d"], cfg["rank"], cfg["Hq"] // cfg["Hkv"]
     be = 2 if cfg["dtype"] == "bf16" else 4
     B, Hkv = cfg["B"], cfg["Hkv"]
-    route = attend = out = 0
+    route = attend = out = fac = 0
     for b in range(B):
         ns, nf = int(n_spans[b]), int(n_full[b])
         lens = span_len[b]
@@ -76,9 +81,12 @@ def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg):
             le = lens[E].astype(np.int64)
             rj = np.minimum(np.minimum(le, r), d)
             route += ns * d * be
-            attend += ((ns - len(E)) * d * be + ns * 8 + nf * 2 * d * be
-                       + int(np.sum(2 * (le + d) * rj * be)) + G * d * be)
+            f = int(np.sum(2 * (le + d) * rj * be))
+            fac += f
+            attend += ((ns - len(E)) * d * be + ns * 8 + nf * 2 * d * be + f + G * d * be)
             out += G * d * 4
+    if factors_only:
+        return fac
     return route + attend + out, attend
 
 
@@ -250,7 +258,8 @@ def main():
 
     def build():
         return rskv.build_spans(H, K, V, cfg["rank"], cfg["anchor_frac"], n_q_heads=cfg["Hq"],
-                                alpha=cfg["alpha"], proj=P, tail_capacity=cfg["tail_capacity"])
+                                alpha=cfg["alpha"], proj=P, tail_capacity=cfg["tail_capacity"],
+                                factor_tier=args.factor_tier)
 
     torch.cuda.synchronize()
     tb = time.perf_counter()
@@ -339,7 +348,7 @@ def main():
         kern["append_ms"] = prof["append_ms"] / prof["steps"]
 
     # algorithmic bytes from the timed steps' selections
-    tot_b, att_b = [], []
+    tot_b, att_b, fac_b = [], [], []
     for i in range(n_steps):
         # replicas hold identical tables; appends add rows per replica (rows
         # that decoded anchors closed into spans are still counted as full
@@ -350,6 +359,8 @@ def main():
                               nsels[i].cpu().numpy(), cfg)
         tot_b.append(tb_)
         att_b.append(ab_)
+        fac_b.append(step_bytes(ex["span_len"], ex["n_spans"], n_full, s_np,
+                                nsels[i].cpu().numpy(), cfg, factors_only=True))
     step_bytes_avg = float(np.mean(tot_b))
     att_bytes_avg = float(np.mean(att_b))
     ctx_tokens = cfg["B"] * cfg["T"]
@@ -374,7 +385,8 @@ def main():
         "config": {"workload": args.workload, "batch": cfg["B"], "context": cfg["T"],
                    "q_heads": cfg["Hq"], "kv_heads": cfg["Hkv"], "head_dim": cfg["d"],
                    "rank": cfg["rank"], "k_max": kmax, "tau": cfg["tau"],
-                   "anchor_frac": cfg["anchor_frac"], "replicas": R},
+                   "anchor_frac": cfg["anchor_frac"], "replicas": R,
+                   "factor_tier": args.factor_tier},
         "roofline": {"bound": "hbm", "achieved": att_gbps, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": att_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "kernel": "attend_mfma_kernel",
@@ -388,7 +400,16 @@ def main():
         "warm_ms_per_step": warm_ms,
         "tokens_per_s_all_kv_heads": value * cfg["Hkv"],
         "build_s": build_s,
+        "cache_hbm_bytes": caches[0].info["device_bytes"],
+        "cache_host_bytes": caches[0].info["host_bytes"],
     }
+    if args.factor_tier == "host":
+        # the expanded spans' factors cross the host link inside the attention
+        # kernel; PCIe 5.0 x16 moves 64 GB/s per direction
+        fb = float(np.mean(fac_b))
+        gbps = fb / (kern["attend_ms"] / 1e3) / 1e9
+        res["host_link"] = {"bytes_per_step": fb, "achieved": gbps, "peak": 64.0,
+                            "unit": "GB/s", "frac": gbps / 64.0}
 
     if not args.no_cpu_baseline:
         U = B * Hkv

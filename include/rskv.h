@@ -74,7 +74,19 @@ typedef struct rskv_build_opts {
   int32_t tail_capacity; /* slots reserved for decode-time appends (>= 0) */
   int32_t k_max_cap;     /* largest k_max decode_step accepts; <= 0 means no
                             limit (at most n_spans are ever expanded) */
+  int32_t factor_tier;   /* where the span factors (A_K, A_V, W_K, W_V) live:
+                            RSKV_TIER_HBM, or RSKV_TIER_HOST: pinned host
+                            memory that the kernels read over the host link
+                            (SEKV keeps the low-rank bases in CPU memory and
+                            fetches the expanded spans on demand; Metodologia
+                            2 and 3).  Results are identical; only the
+                            expanded spans' factors cross the link. */
 } rskv_build_opts;
+
+typedef enum rskv_factor_tier {
+  RSKV_TIER_HBM = 0,
+  RSKV_TIER_HOST = 1
+} rskv_factor_tier;
 
 /* Build a cache from prefilled contexts (Metodologia 1 and 2).
  *   surprisal: device fp32 [B][T] token surprisal H_t (no NaN).
@@ -145,6 +157,8 @@ typedef struct rskv_cache_info {
   int32_t tail_capacity, appended, k_max_cap;
   float alpha;
   size_t device_bytes;       /* HBM held by the cache, workspace included */
+  int32_t factor_tier;       /* rskv_factor_tier */
+  size_t host_bytes;         /* pinned host memory held (host factor tier) */
 } rskv_cache_info;
 
 int rskv_cache_info_get(const rskv_cache* cache, rskv_cache_info* info);

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "librskv.so")
 
 F32, BF16 = 0, 1
 DTYPE_NAMES = {F32: "f32", BF16: "bf16"}
+TIERS = {"hbm": 0, "host": 1}  # where the span factors live
 
 
 class RskvError(RuntimeError):
@@ -30,7 +31,8 @@ class BuildOpts(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("context_len", C.c_int32), ("dtype", C.c_int32),
                 ("anchor_frac", C.c_double), ("alpha", C.c_float), ("proj", C.c_void_p),
-                ("n_proj", C.c_int32), ("tail_capacity", C.c_int32), ("k_max_cap", C.c_int32)]
+                ("n_proj", C.c_int32), ("tail_capacity", C.c_int32), ("k_max_cap", C.c_int32),
+                ("factor_tier", C.c_int32)]
 
 
 class CacheInfo(C.Structure):
@@ -39,7 +41,8 @@ class CacheInfo(C.Structure):
                 ("dtype", C.c_int32), ("n_spans_max", C.c_int32), ("n_full_cap", C.c_int32),
                 ("n_span_tokens_max", C.c_int32), ("tail_capacity", C.c_int32),
                 ("appended", C.c_int32), ("k_max_cap", C.c_int32), ("alpha", C.c_float),
-                ("device_bytes", C.c_size_t)]
+                ("device_bytes", C.c_size_t), ("factor_tier", C.c_int32),
+                ("host_bytes", C.c_size_t)]
 
 
 _ARRAY_FIELDS = ["n_anchor", "n_spans", "n_full", "n_span_tokens", "span_id", "span_start",
@@ -203,16 +206,17 @@ class Cache:
 
 def build_spans(surprisal, K, V, rank: int, anchor_frac: float, n_q_heads: Optional[int] = None,
                 alpha: float = 8.0, proj=None, tail_capacity: int = 0,
-                k_max_cap: int = 0) -> Cache:
+                k_max_cap: int = 0, factor_tier: str = "hbm") -> Cache:
     """Build a cache.  surprisal [B][T] fp32; K, V [B][Hkv][T][d] (fp32 or
-    bf16) on the GPU; proj [1 or Hkv][d][d] fp32 on the GPU or None."""
+    bf16) on the GPU; proj [1 or Hkv][d][d] fp32 on the GPU or None;
+    factor_tier "hbm" or "host" (span factors in pinned host memory)."""
     torch = _torch()
     B, Hkv, T, d = K.shape
     dt = _dtype_code(K)
     opts = BuildOpts(batch=B, n_q_heads=n_q_heads or Hkv, n_kv_heads=Hkv, head_dim=d,
                      context_len=T, dtype=dt, anchor_frac=float(anchor_frac), alpha=float(alpha),
                      proj=None, n_proj=0, tail_capacity=int(tail_capacity),
-                     k_max_cap=int(k_max_cap))
+                     k_max_cap=int(k_max_cap), factor_tier=TIERS[factor_tier])
     args = [_dev(surprisal, "surprisal", (B, T), torch.float32),
             _dev(K, "K", (B, Hkv, T, d)), _dev(V, "V", (B, Hkv, T, d), K.dtype)]
     if proj is not None:
@@ -266,7 +270,7 @@ def append_token(cache: Cache, k, v, h=None):
 
 def cache_import(arrays: dict, n_q_heads: int, rank: int, dtype: str, context_len: int,
                  alpha: float = 8.0, proj: Optional[np.ndarray] = None,
-                 tail_capacity: int = 0, k_max_cap: int = 0) -> Cache:
+                 tail_capacity: int = 0, k_max_cap: int = 0, factor_tier: str = "hbm") -> Cache:
     """Create a cache from host arrays in the canonical (export) layout."""
     dt = BF16 if dtype == "bf16" else F32
     et = np.uint16 if dt == BF16 else np.float32
@@ -282,7 +286,7 @@ def cache_import(arrays: dict, n_q_heads: int, rank: int, dtype: str, context_le
     opts = BuildOpts(batch=B, n_q_heads=n_q_heads, n_kv_heads=Hkv, head_dim=d,
                      context_len=context_len, dtype=dt, anchor_frac=0.0, alpha=float(alpha),
                      proj=None, n_proj=0, tail_capacity=int(tail_capacity),
-                     k_max_cap=int(k_max_cap))
+                     k_max_cap=int(k_max_cap), factor_tier=TIERS[factor_tier])
     if proj is not None:
         keep["_proj"] = np.ascontiguousarray(proj, dtype=np.float32)
         opts.proj = keep["_proj"].ctypes.data

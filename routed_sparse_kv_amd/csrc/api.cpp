@@ -57,6 +57,8 @@ int check_opts(const rskv_build_opts* o, int rank) {
   if (o->proj != nullptr && o->n_proj != 1 && o->n_proj != o->n_kv_heads)
     return fail(RSKV_EINVAL, "n_proj must be 1 or n_kv_heads");
   if (!(o->alpha == o->alpha)) return fail(RSKV_EINVAL, "alpha is NaN");
+  if (o->factor_tier != RSKV_TIER_HBM && o->factor_tier != RSKV_TIER_HOST)
+    return fail(RSKV_EINVAL, "factor_tier must be RSKV_TIER_HBM or RSKV_TIER_HOST");
   return RSKV_OK;
 }
 
@@ -84,11 +86,30 @@ int dev_alloc_bytes(rskv_cache* c, void** p, size_t bytes, const char* what) {
   return rc;
 }
 
+// Zero-filled pinned host memory, tracked by the cache; the kernels use the
+// same address (unified addressing) and read it over the host link.
+int host_alloc_bytes(rskv_cache* c, void** p, size_t bytes, const char* what) {
+  *p = nullptr;
+  bytes = std::max<size_t>(bytes, 1);
+  void* q = nullptr;
+  hipError_t e = hipHostMalloc(&q, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(RSKV_ENOMEM, std::string("pinned host allocation failed: ") + what);
+  }
+  memset(q, 0, bytes);
+  c->host_allocs.push_back(q);
+  c->host_bytes += bytes;
+  *p = q;
+  return RSKV_OK;
+}
+
 void free_cache(rskv_cache* c) {
   if (c == nullptr) return;
   if (c->last_stream != nullptr) (void)hipStreamSynchronize(c->last_stream);
   (void)hipDeviceSynchronize();
   for (void* p : c->allocs) (void)hipFree(p);
+  for (void* p : c->host_allocs) (void)hipHostFree(p);
   for (auto* list : {&c->prof.pending, &c->prof.app_pending})
     for (hipEvent_t e : *list)
       if (e != nullptr) (void)hipEventDestroy(e);
@@ -145,10 +166,15 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   ALLOC(v.log_len, c->B * S, "log_len");
   ALLOCB(v.k_full, z.full * es, "k_full");
   ALLOCB(v.v_full, z.full * es, "v_full");
-  ALLOCB(v.a_k, z.a * es, "a_k");
-  ALLOCB(v.a_v, z.a * es, "a_v");
-  ALLOCB(v.w_k, z.w * es, "w_k");
-  ALLOCB(v.w_v, z.wv * es, "w_v");
+  const bool host = c->factor_tier == RSKV_TIER_HOST;
+#define ALLOCF(ptr, n, what)                                                      \
+  if ((rc = host ? host_alloc_bytes(c, &(ptr), (n), what)                         \
+                 : dev_alloc_bytes(c, &(ptr), (n), what)) != RSKV_OK) return rc
+  ALLOCF(v.a_k, z.a * es, "a_k");
+  ALLOCF(v.a_v, z.a * es, "a_v");
+  ALLOCF(v.w_k, z.w * es, "w_k");
+  ALLOCF(v.w_v, z.wv * es, "w_v");
+#undef ALLOCF
   ALLOC(v.z, U * S, "z");
   ALLOC(v.slogit, z.slogit, "slogit");
   ALLOC(v.sel, U * S, "sel");
@@ -166,10 +192,12 @@ int alloc_arrays(rskv_cache* c, hipStream_t st) {
   RSKV_HIP(hipMemsetAsync(v.vmean, 0, z.vmean * es, st), "memset vmean");
   RSKV_HIP(hipMemsetAsync(v.k_full, 0, z.full * es, st), "memset k_full");
   RSKV_HIP(hipMemsetAsync(v.v_full, 0, z.full * es, st), "memset v_full");
-  RSKV_HIP(hipMemsetAsync(v.a_k, 0, z.a * es, st), "memset a_k");
-  RSKV_HIP(hipMemsetAsync(v.a_v, 0, z.a * es, st), "memset a_v");
-  RSKV_HIP(hipMemsetAsync(v.w_k, 0, z.w * es, st), "memset w_k");
-  RSKV_HIP(hipMemsetAsync(v.w_v, 0, z.wv * es, st), "memset w_v");
+  if (!host) {  // host-tier factors are zeroed at allocation
+    RSKV_HIP(hipMemsetAsync(v.a_k, 0, z.a * es, st), "memset a_k");
+    RSKV_HIP(hipMemsetAsync(v.a_v, 0, z.a * es, st), "memset a_v");
+    RSKV_HIP(hipMemsetAsync(v.w_k, 0, z.w * es, st), "memset w_k");
+    RSKV_HIP(hipMemsetAsync(v.w_v, 0, z.wv * es, st), "memset w_v");
+  }
   RSKV_HIP(hipMemsetAsync(v.log_len, 0, c->B * S * sizeof(float), st), "memset log_len");
   RSKV_HIP(hipMemsetAsync(v.slogit, 0, z.slogit * sizeof(float), st), "memset slogit");
   RSKV_HIP(hipMemsetAsync(v.n_sel, 0, U * sizeof(int32_t), st), "memset n_sel");
@@ -191,6 +219,7 @@ void init_header(rskv_cache* c, const rskv_build_opts* o, int rank) {
   c->alpha = o->alpha > 0.f ? o->alpha : 8.f;
   c->tail_cap = o->tail_capacity;
   c->n_proj = o->proj != nullptr ? o->n_proj : 0;
+  c->factor_tier = o->factor_tier;
 }
 
 int copy_proj(rskv_cache* c, const rskv_build_opts* o, hipStream_t st, bool from_host) {
@@ -322,7 +351,7 @@ int export_arrays(const rskv_cache* c, const std::vector<int>& ns, rskv_host_arr
   std::vector<E> tmp;
   auto fetch = [&](const void* src, size_t n) -> int {
     tmp.assign(n, E(0));
-    hipError_t e = hipMemcpy(tmp.data(), src, n * sizeof(E), hipMemcpyDeviceToHost);
+    hipError_t e = hipMemcpy(tmp.data(), src, n * sizeof(E), hipMemcpyDefault);
     return e == hipSuccess ? RSKV_OK : hip_fail(e, "export copy");
   };
   int rc;
@@ -331,7 +360,7 @@ int export_arrays(const rskv_cache* c, const std::vector<int>& ns, rskv_host_arr
              "export summary");
   }
   if (a->w_k) {
-    RSKV_HIP(hipMemcpy(a->w_k, v.w_k, z.w * sizeof(E), hipMemcpyDeviceToHost), "export w_k");
+    RSKV_HIP(hipMemcpy(a->w_k, v.w_k, z.w * sizeof(E), hipMemcpyDefault), "export w_k");
   }
   if (a->vmean) {
     if ((rc = fetch(v.vmean, z.vmean))) return rc;
@@ -372,7 +401,7 @@ int import_arrays(rskv_cache* c, const rskv_host_arrays* a, int S_in, int F_in, 
   Relayout<E> rl{c, a->span_len, S_in, c->h_n_spans.data()};
   std::vector<E> tmp;
   auto put = [&](void* dst, size_t n, const char* what) -> int {
-    hipError_t e = hipMemcpy(dst, tmp.data(), n * sizeof(E), hipMemcpyHostToDevice);
+    hipError_t e = hipMemcpy(dst, tmp.data(), n * sizeof(E), hipMemcpyDefault);
     return e == hipSuccess ? RSKV_OK : hip_fail(e, what);
   };
   int rc;
@@ -671,6 +700,8 @@ int rskv_cache_info_get(const rskv_cache* c, rskv_cache_info* info) {
   info->k_max_cap = c->k_max_cap;
   info->alpha = c->alpha;
   info->device_bytes = c->bytes;
+  info->factor_tier = c->factor_tier;
+  info->host_bytes = c->host_bytes;
   return RSKV_OK;
 }
 

@@ -119,8 +119,11 @@ struct rskv_cache {
   int nsplit_max = 1;
   std::vector<int32_t> h_n_anchor, h_n_spans, h_n_full0, h_n_span_tokens, h_n_tok_pad;
   rskv::DeviceArrays dev;
-  std::vector<void*> allocs;
+  std::vector<void*> allocs;       // device memory
   size_t bytes = 0;
+  int factor_tier = 0;             // RSKV_TIER_HBM or RSKV_TIER_HOST
+  std::vector<void*> host_allocs;  // pinned host memory (host factor tier)
+  size_t host_bytes = 0;
   hipStream_t last_stream = nullptr;
   rskv::Profile prof;
 };

@@ -36,7 +36,8 @@ def gpu_build(wl, device="cuda", **over):
     P = torch.from_numpy(wl.P).to(device) if wl.P is not None else None
     cache = rskv.build_spans(H, K, V, cfg["rank"], cfg["anchor_frac"], n_q_heads=cfg["Hq"],
                              alpha=cfg["alpha"], proj=P, tail_capacity=cfg["tail_capacity"],
-                             k_max_cap=cfg.get("k_max_cap", 0))
+                             k_max_cap=cfg.get("k_max_cap", 0),
+                             factor_tier=cfg.get("factor_tier", "hbm"))
     del K, V
     return cache
 
