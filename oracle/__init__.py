@@ -5,7 +5,10 @@ execute this package: only the test-suite, the smoke check and the bench's
 CPU-baseline leg use it.  It shares no code, constants or helpers with the
 HIP library; the two are compared on the same seeded inputs.
 
-Every function follows a passage of the SEKV summary ("SEKV - KV Cache
+The submodule ``paris`` is the oracle of the token-retrieval router
+(ParisKV page); its readings and pinning status are in its own docstring.
+
+Every function of the SEKV part follows a passage of the SEKV summary ("SEKV - KV Cache
 Adattiva alla Risoluzione con Memoria Semantica Gerarchica", gist.science,
 Italian and Korean editions), cited by section name in its docstring.
 
@@ -29,3 +32,4 @@ Pinning status (what fixes each function independently of itself):
                           with a strict cut at 1/2, mean-of-group routing.
 """
 from .sekv import *  # noqa: F401,F403
+from . import paris  # noqa: F401  (ParisKV-style token retrieval, its own page)

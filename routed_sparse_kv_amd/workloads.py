@@ -70,6 +70,31 @@ CONFIGS: Dict[str, dict] = {
 }
 
 
+#: Token-retrieval router parameters (ParisKV page, "Pipeline di Recupero
+#: Nativa su GPU in Due Stadi" and the sliding-window regions): subspace
+#: width m, centroids voted per subspace rho, candidate fraction (the page's
+#: example range is 5-10 %), tokens retrieved, Sink and Local sizes.  These
+#: are parameters of the input, not arithmetic of the method.
+RETRIEVAL_DEFAULTS = dict(m=8, rho=16, cand_frac=0.05, k_ret=1024, n_sink=16, n_local=512)
+
+
+def retrieval_params(**overrides) -> dict:
+    """Copy of RETRIEVAL_DEFAULTS with ``overrides`` applied."""
+    out = dict(RETRIEVAL_DEFAULTS)
+    for k, v in overrides.items():
+        if k not in out:
+            raise KeyError(f"unknown retrieval parameter {k!r}")
+        out[k] = v
+    return out
+
+
+def srht_signs(cfg: dict) -> np.ndarray:
+    """The d random signs of the retrieval router's rotation (int8, +-1),
+    drawn from ``default_rng([seed, 2**24])`` of the configuration."""
+    r = np.random.default_rng([int(cfg["seed"]), 1 << 24])
+    return np.where(r.integers(0, 2, int(cfg["d"])) == 1, 1, -1).astype(np.int8)
+
+
 def config(name: str, **overrides) -> dict:
     """Return a copy of a named configuration with ``overrides`` applied."""
     if name not in CONFIGS:
