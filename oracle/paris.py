@@ -216,8 +216,9 @@ def encode_keys(K: np.ndarray, signs: np.ndarray, m: int, codebook=None) -> dict
     """Buckets (P3), 4-bit codes (P7) and stored calibration (P8) of the rows
     of K [N][d] (fp64 values of the stored keys).
 
-    Returns buckets [N][B], neg [N][d] (sign bits), mag [N][d] (bins), w
-    [N][B] (fp32 values, as stored) and w64 (before storage rounding)."""
+    Returns buckets [N][B], u [N][d] (unit subspace directions), neg [N][d]
+    (sign bits), mag [N][d] (bins), w [N][B] (fp32 values, as stored) and
+    w64 (before storage rounding)."""
     K = np.atleast_2d(np.asarray(K, np.float64))
     N, d = K.shape
     B = d // m
@@ -239,7 +240,7 @@ def encode_keys(K: np.ndarray, signs: np.ndarray, m: int, codebook=None) -> dict
     Vq = np.where(neg, -lam[mag], lam[mag])
     den = (Vq * U).sum(axis=2)
     w64 = np.divide(knorm[:, None] * xn, den, out=np.zeros_like(xn), where=live & (den != 0))
-    return dict(buckets=buckets, neg=neg.reshape(N, d).astype(np.int64),
+    return dict(buckets=buckets, u=U.reshape(N, d), neg=neg.reshape(N, d).astype(np.int64),
                 mag=mag.reshape(N, d).astype(np.int64),
                 w=w64.astype(np.float32).astype(np.float64), w64=w64, m=m, lam=lam, beta=beta)
 

@@ -1,8 +1,10 @@
 """Span-routed mixed-resolution KV-cache decode for AMD MI355X (gfx950).
 
 The compute path is the HIP library ``lib/librskv.so`` (C ABI declared in
-``include/rskv.h``); this package only marshals arguments to it.
+``include/rskv.h`` for the span router and ``include/rskv_retrieval.h`` for
+the token-retrieval router); this package only marshals arguments to it.
 """
 from .binding import (BF16, F32, Cache, RskvError, append_kv, append_token, build_spans,  # noqa: F401
                       cache_import,
                       decode_step, lib, version)
+from .retrieval import Retrieval, build_retrieval, retrieval_decode  # noqa: F401

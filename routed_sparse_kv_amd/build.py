@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "librskv.so")
-SOURCES = ["segment.hip", "summary.hip", "factor.hip", "route.hip", "attend.hip", "api.cpp"]
+SOURCES = ["segment.hip", "summary.hip", "factor.hip", "route.hip", "attend.hip", "retrieval.hip",
+           "api.cpp", "retrieval_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -442,6 +442,10 @@ int import_arrays(rskv_cache* c, const rskv_host_arrays* a, int S_in, int F_in, 
 
 }  // namespace
 
+namespace rskv {
+int report_error(int code, const std::string& msg) { return fail(code, msg); }
+}  // namespace rskv
+
 extern "C" {
 
 const char* rskv_last_error(void) { return g_err.c_str(); }

@@ -132,6 +132,10 @@ namespace rskv {
 
 constexpr uint32_t kMagic = 0x52534b56u;  // "RSKV"
 
+// Records `msg` as the calling thread's last error (rskv_last_error) and
+// returns `code`.
+int report_error(int code, const std::string& msg);
+
 // ---- launchers (each returns hipSuccess or the first launch error)
 
 // Segmentation of every sequence; writes span_id, span starts/lengths,

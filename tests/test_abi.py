@@ -7,12 +7,12 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rskv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rskv.h", "rskv_retrieval.h")]
 LIB = os.path.join(ROOT, "routed_sparse_kv_amd", "lib", "librskv.so")
 
 
 def declared_symbols():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(rskv_[a-z_]+)\s*\(", text)))
 
@@ -21,7 +21,9 @@ def test_header_declares_the_boundary():
     syms = declared_symbols()
     for s in ("rskv_build_spans", "rskv_decode_step", "rskv_append_kv", "rskv_append_token",
               "rskv_cache_export",
-              "rskv_cache_import", "rskv_cache_destroy", "rskv_last_error"):
+              "rskv_cache_import", "rskv_cache_destroy", "rskv_last_error",
+              "rskv_retrieval_build", "rskv_retrieval_decode", "rskv_retrieval_export",
+              "rskv_retrieval_trace_get", "rskv_retrieval_destroy"):
         assert s in syms
 
 
@@ -44,6 +46,9 @@ def test_version_and_error_strings_without_gpu():
     assert b"invalid cache handle" in lib.rskv_last_error()
     lib.rskv_append_token.argtypes = [ctypes.c_void_p] * 5
     assert lib.rskv_append_token(None, None, None, None, None) == -6
+    lib.rskv_retrieval_decode.argtypes = [ctypes.c_void_p] * 5
+    assert lib.rskv_retrieval_decode(None, None, None, None, None) == -6
+    assert b"invalid retrieval handle" in lib.rskv_last_error()
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
