@@ -39,7 +39,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long_128k_bf16")
+    ap.add_argument("--workload", default=None,
+                    help="default: long_128k_bf16 (span router), million_1m_bf16 (retrieval)")
+    ap.add_argument("--router", default="span", choices=["span", "retrieval"],
+                    help="span: SEKV span routing (decode_step); retrieval: ParisKV-style "
+                         "token retrieval (rskv_retrieval_decode)")
+    ap.add_argument("--kv-tier", default="hbm", choices=["hbm", "host"],
+                    help="retrieval router: where the retrieval region's K/V live")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB per rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (units)")
@@ -51,7 +57,10 @@ def parse():
     ap.add_argument("--close-runs", default="",
                     help="instead of the decode bench: span-closing latency for these run "
                          "lengths, e.g. 4,16,32,64,128 (streaming segmentation)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.workload is None:
+        args.workload = "million_1m_bf16" if args.router == "retrieval" else "long_128k_bf16"
+    return args
 
 
 def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg, factors_only=False):
@@ -211,6 +220,200 @@ def close_latency(args):
     cache.close()
 
 
+def retrieval_step_bytes(info, esize):
+    """Algorithmic bytes of one retrieval decode step per kernel: each input
+    read once, each output written once (U units; N keys, C candidates,
+    n_sel retrieved, n_attend attended rows per unit)."""
+    U = info["batch"] * info["n_kv_heads"]
+    d, N, C = info["head_dim"], info["n_retrieval"], info["n_cand"]
+    Bs, G = d // 8, info["n_q_heads"] // info["n_kv_heads"]
+    n_sel, n_att = info["n_sel"], info["n_attend"]
+    nsplit = -(-n_att // 64)
+    part = nsplit * G * (d + 2) * 4
+    per = {
+        "query": G * d * esize + Bs * 256 + d * 8 + 8,
+        "vote": N * Bs + Bs * 256 + N * 2,          # buckets in, totals out
+        "compact": N * 2 + C * 4,                     # totals in, candidates out
+        "rerank": C * 4 + C * info["record_bytes"] + C * 4,
+        "histogram": C * 4,                          # estimates in
+        "crossing": C * 4,                           # estimates in (members out: few)
+        "threshold": 0,                              # members only (a few dozen)
+        "output": C * 4 + n_sel * 4 * 2,             # estimates in, positions out
+        "attend": n_att * 2 * d * esize + G * d * esize + n_sel * 4 + part,
+        "merge": part + G * d * 4,
+    }
+    return {k: v * U for k, v in per.items()}
+
+
+def retrieval_bench(args):
+    """Decode-step throughput of the token-retrieval router (ParisKV page):
+    seven launches per step over the whole batch.  The index is built
+    untimed; steps rotate over replicas so that one rotation touches at
+    least 1 GB (the last-level cache holds 256 MB)."""
+    import torch
+
+    import routed_sparse_kv_amd as rskv
+    from routed_sparse_kv_amd import workloads as W
+    from routed_sparse_kv_amd.retrieval import KERNELS
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    wl = W.generate(args.workload)
+    cfg = wl.cfg
+    dt = cfg["dtype"]
+    params = W.retrieval_params()
+    signs = W.srht_signs(cfg)
+    log(f"generated {args.workload} in {time.perf_counter() - t0:.1f}s")
+
+    def to_dev(a):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    K, V = to_dev(wl.K), to_dev(wl.V)
+
+    def build():
+        return rskv.build_retrieval(K, V, signs, cfg["Hq"], kv_tier=args.kv_tier, **params)
+
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    idx = [build()]
+    build_s = time.perf_counter() - tb
+    info = idx[0].info
+    esize = 2 if dt == "bf16" else 4
+    per_kernel = retrieval_step_bytes(info, esize)
+    step_b = float(sum(per_kernel.values()))
+    R = args.replicas or max(1, math.ceil(1.0e9 / step_b))
+    R = min(R, 16)
+    for _ in range(R - 1):
+        idx.append(build())
+    del K, V
+    torch.cuda.empty_cache()
+    log(f"build {build_s:.2f}s; {R} index replicas, {info['device_bytes'] / 1e9:.2f} GB device "
+        f"+ {info['host_bytes'] / 1e9:.2f} GB host each")
+    qs = [to_dev(q) for q in wl.queries]
+    B, Hkv = cfg["B"], cfg["Hkv"]
+    out = torch.empty((B, cfg["Hq"], cfg["d"]), dtype=torch.float32, device=dev)
+    ret = torch.empty((B, Hkv, params["k_ret"]), dtype=torch.int32, device=dev)
+    n_steps = args.steps
+    for i in range(args.warmup):
+        idx[i % R].decode(qs[i % len(qs)], out=out, retrieved=ret)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_steps):
+        idx[i % R].decode(qs[i % len(qs)], out=out, retrieved=ret)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / n_steps
+    e0.record()
+    for i in range(n_steps):
+        idx[0].decode(qs[i % len(qs)], out=out, retrieved=ret)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / n_steps
+    # per-kernel durations: HIP events carried by each dispatch
+    for x in idx:
+        x.profile_enable(True)
+    for i in range(n_steps):
+        idx[i % R].decode(qs[i % len(qs)], out=out, retrieved=ret)
+    torch.cuda.synchronize()
+    tot = {k: 0.0 for k in KERNELS}
+    steps = 0
+    for x in idx:
+        p = x.profile_read()
+        steps += p["steps"]
+        for k in KERNELS:
+            tot[k] += p[f"{k}_ms"]
+        x.profile_enable(False)
+    kern = {f"{k}_ms": tot[k] / max(1, steps) for k in KERNELS}
+    vote_gbps = per_kernel["vote"] / (kern["vote_ms"] / 1e3) / 1e9
+    ctx_tokens = B * cfg["T"]
+    value = ctx_tokens / (ms_step / 1e3)
+    step_gbps = step_b / (ms_step / 1e3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "context-tokens/s/head",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "router": "retrieval", "batch": B,
+                   "context": cfg["T"], "q_heads": cfg["Hq"], "kv_heads": Hkv,
+                   "head_dim": cfg["d"], **params, "n_cand": info["n_cand"],
+                   "n_attend": info["n_attend"], "replicas": R, "kv_tier": args.kv_tier},
+        "roofline": {"bound": "hbm", "achieved": vote_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": vote_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "kernel": "vote_kernel",
+                     "algorithmic_bytes_per_launch": per_kernel["vote"],
+                     "mean_launch_ms": kern["vote_ms"]},
+        "step_algorithmic_bytes": step_b,
+        "step_algorithmic_gbps": step_gbps,
+        "step_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "kernel_algorithmic_bytes": per_kernel,
+        "kernel_ms": kern,
+        "profiled_ms_per_step": sum(kern.values()),
+        "warm_ms_per_step": warm_ms,
+        "tokens_per_s_all_kv_heads": value * Hkv,
+        "build_s": build_s,
+        "index_device_bytes": info["device_bytes"],
+        "index_host_bytes": info["host_bytes"],
+    }
+    if args.kv_tier == "host":
+        rows_b = info["n_sel"] * 2 * cfg["d"] * esize * B * Hkv
+        gbps = rows_b / (kern["attend_ms"] / 1e3) / 1e9
+        res["host_link"] = {"bytes_per_step": rows_b, "achieved": gbps, "peak": 64.0,
+                            "unit": "GB/s", "frac": gbps / 64.0}
+    for x in idx:
+        x.close()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = retrieval_cpu_baseline(wl, signs, params, B * Hkv, ctx_tokens, log)
+    print(json.dumps(res))
+
+
+def retrieval_cpu_baseline(wl, signs, params, n_units, ctx_tokens, log, budget_s=12.0):
+    """The oracle's retrieval decode on one fully encoded unit (sequence 0,
+    KV head 0; the encoding is build work and untimed), over the workload's
+    queries in turn, scaled to a full step of n_units units."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paris
+    from routed_sparse_kv_amd import workloads as W
+    cfg = wl.cfg
+    dt = cfg["dtype"]
+    G = cfg["Hq"] // cfg["Hkv"]
+    Kf, Vf = W.as_f64(wl.K[0, 0], dt), W.as_f64(wl.V[0, 0], dt)
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        enc = paris.encode_unit(Kf, signs, params["m"], params["n_sink"], params["n_local"])
+        log(f"oracle encode of one unit {time.perf_counter() - t0:.1f}s (untimed)")
+        done, el = 0, 0.0
+        while el < budget_s:
+            q = W.as_f64(wl.queries[done % len(wl.queries)][0, :G], dt)
+            t1 = time.perf_counter()
+            paris.decode_unit(enc, Kf, Vf, q, signs, params["rho"], params["cand_frac"],
+                              params["k_ret"], params["n_sink"], params["n_local"])
+            el += time.perf_counter() - t1
+            done += 1
+    t_step = el / done * n_units
+    return {"value": ctx_tokens / t_step, "unit": "context-tokens/s/head", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} oracle retrieval decodes of unit (0, 0) ({cfg['T']} tokens, "
+                      f"the workload's queries in turn), {el:.1f}s single-threaded, scaled to "
+                      f"one {n_units}-unit step",
+            "seconds_per_step": t_step}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -219,6 +422,9 @@ def main():
         sys.exit(2)
     if args.close_runs:
         close_latency(args)
+        return
+    if args.router == "retrieval":
+        retrieval_bench(args)
         return
     import torch
 

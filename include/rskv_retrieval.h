@@ -91,8 +91,9 @@ int rskv_retrieval_build(const void* K, const void* V, const int8_t* signs,
 /* One decode step.  q: device [B][Hq][d] in dtype.  out: device fp32
  * [B][Hq][d].  retrieved: device int32 [B][Hkv][k_ret] or NULL; receives
  * the retrieved positions of each KV head in ascending order, padded with
- * -1 past the n_sel = min(k_ret, C) retrieved.  Seven stream-ordered
- * launches (two when nothing can be retrieved, three to pad `retrieved`), no
+ * -1 past the n_sel = min(k_ret, C) retrieved.  At most ten
+ * stream-ordered launches (two when nothing can be retrieved, three to pad
+ * `retrieved`), no
  * host synchronisation, no allocation; calls on one index must
  * not overlap (they share its workspace).  Errors: RSKV_ESTATE (bad
  * handle), RSKV_EINVAL (NULL q or out), RSKV_EHIP. */
@@ -104,7 +105,7 @@ typedef struct {
   int32_t n_sink;       /* effective Sink rows s = min(n_sink, T) */
   int32_t local_start;  /* l0: first Local position */
   int32_t n_retrieval;  /* N = l0 - s keys in the retrieval region */
-  int32_t n_cand;       /* C = min(N, ceil(cand_frac N)) */
+  int32_t n_cand;       /* C = min(N, ceil(cand_frac N)), at most 2^21 */
   int32_t n_sel;        /* min(k_ret, C) retrieved per KV head */
   int32_t n_attend;     /* s + n_sel + (T - l0) tokens attended per head */
   int32_t record_bytes; /* bytes of one key's RSQ-IP record (codes + w) */
@@ -151,11 +152,12 @@ int rskv_retrieval_trace_get(const rskv_retrieval* index, rskv_retrieval_trace* 
 
 /* Kernel time of the decode steps while enabled (per-dispatch start/stop
  * events, summed): [0] query rotation and vote table, [1] vote totals,
- * [2] candidate threshold and compaction, [3] rerank, [4] top-k,
- * [5] attention, [6] merge. */
+ * [2] candidate threshold and compaction, [3] rerank, [4] estimate
+ * histogram, [5] crossing bin and its members, [6] exact top-k threshold,
+ * [7] ordered top-k output, [8] attention, [9] merge. */
 typedef struct {
   int64_t steps;
-  double ms[7];
+  double ms[10];
 } rskv_retrieval_profile;
 
 int rskv_retrieval_profile_enable(rskv_retrieval* index, int32_t on);

@@ -91,7 +91,7 @@ __all__ = [
     "hadamard", "rotate", "srht", "pattern_matrix", "bucket_of", "query_ranks",
     "vote_table", "coarse_scores", "n_candidates", "top_by_score", "magnitude_codebook",
     "encode_keys", "estimate", "as_decision", "top_by_value", "regions", "encode_unit",
-    "decode_unit", "ESTIMATE_BAND",
+    "decode_unit", "attend", "ESTIMATE_BAND",
 ]
 
 #: Relative band inside which two correct implementations may order values
@@ -322,7 +322,15 @@ def decode_unit(enc: dict, K: np.ndarray, V: np.ndarray, q_group: np.ndarray,
         retrieved = ret[pick]
     res["retrieved"] = retrieved
     use = np.concatenate([sink, retrieved if forced is None else np.asarray(forced), local])
-    logits = q_group @ K[use].T / math.sqrt(d)
-    p = np.exp(logits - logits.max(axis=1, keepdims=True))
-    res["out"] = (p @ V[use]) / p.sum(axis=1, keepdims=True)
+    res["out"] = attend(K, V, q_group, use)
     return res
+
+
+def attend(K: np.ndarray, V: np.ndarray, q_group: np.ndarray, positions: np.ndarray) -> np.ndarray:
+    """P12: one exact softmax per query head over the given positions of the
+    stored K/V, logits <q, k> / sqrt(d); returns [G][d]."""
+    K = np.asarray(K, np.float64)
+    idx = np.asarray(positions, np.int64)
+    logits = np.asarray(q_group, np.float64) @ K[idx].T / math.sqrt(K.shape[1])
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return (p @ np.asarray(V, np.float64)[idx]) / p.sum(axis=1, keepdims=True)

@@ -17,7 +17,10 @@ constexpr int kChunk = 4096;    // keys per vote / compaction workgroup
 constexpr int kMaxBins = 264;   // vote totals 0 .. (d/8) * rho <= 256, padded
 constexpr int kRows = 64;       // attention rows per workgroup (one per lane)
 constexpr int kMaxRho = 16;
-constexpr int kKernels = 7;     // decode launches (profile slots)
+constexpr int kKernels = 10;    // decode launches (profile slots)
+constexpr int kSelBlock = 2048; // estimates per top-k workgroup (one block)
+constexpr int kSelBins = 4096;  // value bins of the top-k histogram
+constexpr int kSelMaxBlocks = 1024;  // blocks per unit the top-k handles
 
 // sigma as bits: bit c of w[c / 32] set <=> sigma_c = -1 (d <= 128).
 struct SignMask {
@@ -42,6 +45,8 @@ struct rskv_retrieval {
   // regions: Sink [0, ns), retrieval [ns, l0) (N keys), Local [l0, T) (nl)
   int ns = 0, l0 = 0, nl = 0, N = 0, C = 0, n_sel = 0, n_att = 0, n_near = 0;
   int rec_bytes = 0, nchunk = 0, nbins = 0, nsplit = 0;
+  int nsb = 0;      // top-k blocks per unit, ceil(C / kSelBlock)
+  int nrwg = 0;     // rerank workgroups per unit, ceil(C / 256)
   size_t npad = 0;  // pitch of the per-unit score arrays
   rskv::ret::SignMask signs{};
   rskv::ret::Codebook cb{};
@@ -62,6 +67,16 @@ struct rskv_retrieval {
   int32_t* thr = nullptr;      // [U][2]
   int32_t* cand = nullptr;     // [U][C]
   float* est = nullptr;        // [U][C]
+  uint32_t* rmm = nullptr;     // [U][nrwg][2] smallest / largest estimate (order keys)
+                               // of each rerank workgroup
+  uint32_t* rng = nullptr;     // [U][2] the unit's estimate range (order keys)
+  uint32_t* ehtot = nullptr;   // [U][kSelBins] histogram of the estimates over the range
+  int32_t* gtb = nullptr;      // [U][nsb] keys above the crossing bin, per block
+  float* lval = nullptr;       // [U][C] crossing-bin members: estimate
+  int32_t* lidx = nullptr;     // [U][C] crossing-bin members: candidate index
+  uint32_t* lcnt = nullptr;    // [U] crossing-bin members
+  int32_t* soff = nullptr;     // [U][nsb] first output slot of each block
+  int32_t* selp = nullptr;     // [U][2] threshold (fp32 bits), last tied index taken
   int32_t* sel = nullptr;      // [U][n_sel]
   float* part = nullptr;       // [U][nsplit][G][d + 2]
   std::vector<void*> allocs;
@@ -85,7 +100,7 @@ constexpr uint32_t kMagic = 0x52534b52u;  // "RSKR"
 // caller's K [U][T][d].
 hipError_t launch_encode(const rskv_retrieval* r, const void* K, hipStream_t st);
 
-// One decode step (seven launches); `ev` is null or holds kKernels start/stop
+// One decode step (at most ten launches); `ev` is null or holds kKernels start/stop
 // pairs, one per launch (a skipped launch leaves its pair unrecorded and
 // `recorded[k]` false).
 hipError_t launch_decode(const rskv_retrieval* r, const void* q, float* out, int32_t* retrieved,

@@ -8,13 +8,15 @@
 // "Reranking dei Candidati (RSQ-IP)") is stored.
 //
 // Decode ("Pipeline di Recupero Nativa su GPU in Due Stadi"), per unit
-// (sequence b, KV head h), seven launches:
+// (sequence b, KV head h), at most ten launches:
 //   query     rotated group-mean query, vote table of every subspace
 //   vote      vote total of every key; per-chunk and per-unit histograms
 //   compact   smallest candidate score (prologue), then the candidates in
 //             position order (ties to the lower position)
 //   rerank    RSQ-IP estimate of every candidate (fp64, decided in fp32)
-//   select    k_ret largest estimates (radix select, ties to lower position)
+//   top-k     k_ret largest estimates over the whole chip in four launches
+//             (histogram, crossing bin, exact threshold, ordered output;
+//             ties to the lower position)
 //   attend    one softmax over Sink, retrieved and Local rows, split in
 //             64-row slices
 //   merge     the slices' partial softmax states
@@ -235,18 +237,23 @@ __global__ __launch_bounds__(256) void encode_kernel(const typename Elem<DT>::T*
 
 // ------------------------------------------------------------- decode
 
-// Grid (d/8 subspaces, U).  Every workgroup rotates the unit's group-mean
-// query (fp64, Hadamard levels through LDS), then ranks the 256 sign
-// patterns of its subspace by <q~_b, c_p> (ties to the lower pattern) and
-// writes the votes rho - rank for the top rho.  Workgroup 0 of the unit also
-// stores q~ and ||q-bar|| and clears the unit's vote-total histogram.
+// Grid (d/8 subspaces, U), 1024 threads.  Every workgroup rotates the
+// unit's group-mean query (fp64, Hadamard levels through LDS), then ranks the
+// 256 sign patterns of its subspace by <q~_b, c_p> (ties to the lower
+// pattern): four threads per pattern each count the better patterns among
+// an interleaved quarter, and two shuffles add the counts.  The top rho
+// patterns get rho - rank votes.  Workgroup 0 of the unit also stores q~ and
+// ||q-bar|| and clears the unit's vote-total histogram; the workgroups
+// together clear the unit's estimate histogram and top-k member count.
 template <int DT>
-__global__ __launch_bounds__(256) void query_kernel(const typename Elem<DT>::T* __restrict__ q,
-                                                    int Hq, int Hkv, int G, int d, SignMask sg,
-                                                    int rho, double* __restrict__ qt_out,
-                                                    double* __restrict__ qn_out,
-                                                    uint8_t* __restrict__ votes,
-                                                    uint32_t* __restrict__ tot) {
+__global__ __launch_bounds__(1024) void query_kernel(const typename Elem<DT>::T* __restrict__ q,
+                                                     int Hq, int Hkv, int G, int d, SignMask sg,
+                                                     int rho, double* __restrict__ qt_out,
+                                                     double* __restrict__ qn_out,
+                                                     uint8_t* __restrict__ votes,
+                                                     uint32_t* __restrict__ tot,
+                                                     uint32_t* __restrict__ ehtot,
+                                                     uint32_t* __restrict__ lcnt) {
   typedef Elem<DT> E;
   const int sb = blockIdx.x;
   const int u = blockIdx.y;
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(256) void query_kernel(const typename Elem<DT>::T* 
   const int h = u - b * Hkv;
   const int t = threadIdx.x;
   __shared__ double y[128];
-  __shared__ double red[4];
+  __shared__ double red[16];
   __shared__ double sc[256];
   double qb = 0.0;
   if (t < d) {
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(256) void query_kernel(const typename Elem<DT>::T* 
     for (int g = 0; g < G; ++g) qb += static_cast<double>(E::ld(q, base + static_cast<size_t>(g) * d));
     qb /= static_cast<double>(G);
   }
-  const double nq2 = block_sum<256>(qb * qb, red);
+  const double nq2 = block_sum<1024>(qb * qb, red);
   if (t < d) y[t] = sign_negative(sg, t) ? -qb : qb;
   __syncthreads();
   for (int hh = 1; hh < d; hh <<= 1) {
@@ -278,24 +285,36 @@ __global__ __launch_bounds__(256) void query_kernel(const typename Elem<DT>::T* 
   const double scale = qn * sqrt(static_cast<double>(d));
   if (sb == 0) {
     if (t < d) qt_out[static_cast<size_t>(u) * d + t] = scale > 0.0 ? y[t] / scale : 0.0;
-    if (t == 0) qn_out[u] = qn;
+    if (t == 0) {
+      qn_out[u] = qn;
+      lcnt[u] = 0u;
+    }
     for (int i = t; i < kMaxBins; i += blockDim.x) tot[static_cast<size_t>(u) * kMaxBins + i] = 0u;
   }
+  for (int i = sb * blockDim.x + t; i < kSelBins; i += gridDim.x * blockDim.x)
+    ehtot[static_cast<size_t>(u) * kSelBins + i] = 0u;
+  const int p = t >> 2;
+  const int part = t & 3;
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const double v = scale > 0.0 ? y[sb * 8 + i] / scale : 0.0;
-    s += ((t >> i) & 1) ? -v : v;
+    s += ((p >> i) & 1) ? -v : v;
   }
-  sc[t] = s;
+  if (part == 0) sc[p] = s;
   __syncthreads();
   int rank = 0;
-  for (int p = 0; p < 256; ++p) {
-    const double o = sc[p];
-    rank += (o > s || (o == s && p < t)) ? 1 : 0;
+#pragma unroll 16
+  for (int jj = 0; jj < 64; ++jj) {
+    const int o_p = 4 * jj + part;
+    const double o = sc[o_p];
+    rank += (o > s || (o == s && o_p < p)) ? 1 : 0;
   }
-  votes[(static_cast<size_t>(u) * (d / 8) + sb) * 256 + t] =
-      static_cast<uint8_t>(rank < rho ? rho - rank : 0);
+  rank += __shfl_xor(rank, 1, kWave);
+  rank += __shfl_xor(rank, 2, kWave);
+  if (part == 0)
+    votes[(static_cast<size_t>(u) * (d / 8) + sb) * 256 + p] =
+        static_cast<uint8_t>(rank < rho ? rho - rank : 0);
 }
 
 // Grid (nchunk, U): kChunk consecutive keys per workgroup.  Vote totals by
@@ -366,6 +385,20 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint16_t* __restrict
   __shared__ uint32_t suf[kMaxBins + 1];
   __shared__ int red[4];
   __shared__ unsigned long long sbuf[5];
+  // this thread's 16 keys (loaded first: independent of the threshold)
+  const int i0 = c * kChunk + t * 16;
+  const uint16_t* sp = scores + static_cast<size_t>(u) * npad + i0;
+  uint16_t v[16];
+  {
+    const uint4 a = reinterpret_cast<const uint4*>(sp)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(sp)[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[2 * j] = static_cast<uint16_t>(w[j] & 0xffffu);
+      v[2 * j + 1] = static_cast<uint16_t>(w[j] >> 16);
+    }
+  }
   suffix_counts(tot + static_cast<size_t>(u) * kMaxBins, nbins, suf);
   if (t == 0) suf[nbins] = 0u;
   __syncthreads();
@@ -373,10 +406,10 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint16_t* __restrict
   for (int s = t; s < nbins; s += blockDim.x)
     if (suf[s] >= static_cast<uint32_t>(C)) cand_s = s;
   {
-    int v = cand_s;
+    int mv = cand_s;
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-    if ((t & (kWave - 1)) == 0) red[t / kWave] = v;
+    for (int o = kWave / 2; o > 0; o >>= 1) mv = max(mv, __shfl_xor(mv, o, kWave));
+    if ((t & (kWave - 1)) == 0) red[t / kWave] = mv;
     __syncthreads();
     cand_s = max(max(red[0], red[1]), max(red[2], red[3]));
     __syncthreads();
@@ -399,20 +432,6 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint16_t* __restrict
   const int eqB = static_cast<int>(packed >> 32);
   const int out0 = gtB + min(quota, eqB);
   const int q_here = max(0, quota - eqB);
-  // this thread's 16 keys
-  const int i0 = c * kChunk + t * 16;
-  const uint16_t* sp = scores + static_cast<size_t>(u) * npad + i0;
-  uint16_t v[16];
-  {
-    const uint4 a = reinterpret_cast<const uint4*>(sp)[0];
-    const uint4 b = reinterpret_cast<const uint4*>(sp)[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[2 * j] = static_cast<uint16_t>(w[j] & 0xffffu);
-      v[2 * j + 1] = static_cast<uint16_t>(w[j] >> 16);
-    }
-  }
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -453,7 +472,8 @@ __global__ __launch_bounds__(256) void rerank_kernel(const uint8_t* __restrict__
                                                      const int32_t* __restrict__ cand, int C,
                                                      const double* __restrict__ qt_all,
                                                      const double* __restrict__ qn_all,
-                                                     Codebook cb, float* __restrict__ est) {
+                                                     Codebook cb, float* __restrict__ est,
+                                                     uint32_t* __restrict__ rmm) {
   const int u = blockIdx.y;
   const int t = threadIdx.x;
   const int k = blockIdx.x * 256 + t;
@@ -467,130 +487,482 @@ __global__ __launch_bounds__(256) void rerank_kernel(const uint8_t* __restrict__
     tq[e] = (e & 8) ? -p : p;
   }
   __syncthreads();
-  if (k >= C) return;
-  // candidate indices lie in [0, N); the clamp only keeps a bad index in bounds
-  const int i = min(max(cand[static_cast<size_t>(u) * C + k], 0), N - 1);
-  const uint4* rp = reinterpret_cast<const uint4*>(rec + (static_cast<size_t>(u) * N + i) * D);
-  uint32_t code[D / 8];
-  float w[D / 8];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  if (k < C) {
+    // candidate indices lie in [0, N); the clamp only keeps a bad index in bounds
+    const int i = min(max(cand[static_cast<size_t>(u) * C + k], 0), N - 1);
+    const uint4* rp = reinterpret_cast<const uint4*>(rec + (static_cast<size_t>(u) * N + i) * D);
+    uint32_t code[D / 8];
+    float w[D / 8];
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const uint4 a = rp[j];
-    code[4 * j] = a.x; code[4 * j + 1] = a.y; code[4 * j + 2] = a.z; code[4 * j + 3] = a.w;
-    const uint4 b = rp[D / 32 + j];
-    w[4 * j] = __uint_as_float(b.x); w[4 * j + 1] = __uint_as_float(b.y);
-    w[4 * j + 2] = __uint_as_float(b.z); w[4 * j + 3] = __uint_as_float(b.w);
+    for (int j = 0; j < D / 32; ++j) {
+      const uint4 a = rp[j];
+      code[4 * j] = a.x; code[4 * j + 1] = a.y; code[4 * j + 2] = a.z; code[4 * j + 3] = a.w;
+      const uint4 b = rp[D / 32 + j];
+      w[4 * j] = __uint_as_float(b.x); w[4 * j + 1] = __uint_as_float(b.y);
+      w[4 * j + 2] = __uint_as_float(b.z); w[4 * j + 3] = __uint_as_float(b.w);
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int b = 0; b < D / 8; ++b) {
+      double dot = 0.0;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) dot += tq[(b * 8 + tt) * 16 + ((code[b] >> (4 * tt)) & 15u)];
+      acc += static_cast<double>(w[b]) * dot;
+    }
+    const float ev = static_cast<float>(qn_all[u] * acc);
+    est[static_cast<size_t>(u) * C + k] = ev;
+    kmin = kmax = f32_order_key(ev);
   }
-  double acc = 0.0;
+  // this workgroup's estimate range (order keys), for the top-k histogram
+  __shared__ uint32_t red[8];
 #pragma unroll
-  for (int b = 0; b < D / 8; ++b) {
-    double dot = 0.0;
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) dot += tq[(b * 8 + tt) * 16 + ((code[b] >> (4 * tt)) & 15u)];
-    acc += static_cast<double>(w[b]) * dot;
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, kWave)));
+    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, kWave)));
   }
-  est[static_cast<size_t>(u) * C + k] = static_cast<float>(qn_all[u] * acc);
+  if ((t & (kWave - 1)) == 0) {
+    red[t / kWave] = kmin;
+    red[4 + t / kWave] = kmax;
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint2 mm;
+    mm.x = min(min(red[0], red[1]), min(red[2], red[3]));
+    mm.y = max(max(red[4], red[5]), max(red[6], red[7]));
+    reinterpret_cast<uint2*>(rmm)[static_cast<size_t>(u) * gridDim.x + blockIdx.x] = mm;
+  }
 }
 
-// Grid U, 1024 threads.  Radix select (8-bit digits from the top, per-wave
-// histograms in LDS) of the n_sel largest fp32 estimates; then an ordered
-// pass writes the retrieved positions ascending: keys above the threshold
-// key, and the first `quota` keys equal to it.
-__global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ est,
-                                                      const int32_t* __restrict__ cand, int C,
-                                                      int n_sel, int k_ret, int first,
-                                                      int32_t* __restrict__ sel,
-                                                      int32_t* __restrict__ retrieved) {
-  constexpr int NT = 1024, NW = NT / kWave;
+// Block-wide minimum / maximum over NT threads (`buf` holds NT/64 floats).
+template <int NT>
+__device__ __forceinline__ float block_min(float v, float* buf) {
+  constexpr int NW = NT / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) buf[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = buf[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = fminf(r, buf[w]);
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* buf) {
+  constexpr int NW = NT / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) buf[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = buf[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = fmaxf(r, buf[w]);
+  __syncthreads();
+  return r;
+}
+
+// Lanes of this wave below the calling lane, as a mask.
+__device__ __forceinline__ unsigned long long lanes_below() {
+  return (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
+}
+
+// Monotone bin of x in [lo, hi] over NB bins, scale = NB / (hi - lo) (the
+// width formed in fp64, so it is finite for any fp32 pair).  Rounding of
+// x - lo and of the product preserves order (an fp32 overflow to +inf
+// included, clamped before the conversion), so every key of a higher bin is
+// larger than every key of a lower bin; lo falls in bin 0 and hi in bin
+// NB - 1.
+template <int NB>
+__device__ __forceinline__ int range_bin(float x, float lo, float scale) {
+  return static_cast<int>(fminf((x - lo) * scale, static_cast<float>(NB - 1)));
+}
+
+// Inverse of f32_order_key (for keys of finite values).
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The unit's estimate range [lo, hi] (from the order keys in rng) and the
+// bin scale over it, identical in every kernel that bins estimates.
+struct EstRange {
+  float lo, hi, scale;
+};
+
+__device__ __forceinline__ EstRange est_range(uint32_t kmin, uint32_t kmax) {
+  EstRange r;
+  r.lo = f32_from_order_key(kmin);
+  r.hi = f32_from_order_key(kmax);
+  r.scale = r.lo < r.hi
+                ? static_cast<float>(kSelBins / (static_cast<double>(r.hi) - static_cast<double>(r.lo)))
+                : 0.f;
+  return r;
+}
+
+// Crossing bin of a histogram held in LDS (NB bins, counts from the top):
+// the bin where the count of keys in higher bins stays below `rem` and the
+// count including it reaches `rem`.  Sets *bin and *above (keys in higher
+// bins); every thread of the workgroup calls it.
+template <int NT, int NB>
+__device__ __forceinline__ void crossing_bin(const uint32_t* hist, uint32_t rem,
+                                             unsigned long long* sbuf, int* s_bin,
+                                             uint32_t* s_above) {
+  constexpr int BPT = NB / NT;
+  const int t = threadIdx.x;
+  uint32_t s4 = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) s4 += hist[NB - 1 - (BPT * t + i)];
+  unsigned long long total;
+  uint32_t above =
+      static_cast<uint32_t>(block_excl_scan<NT>(static_cast<unsigned long long>(s4), sbuf, &total));
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const uint32_t ci = hist[NB - 1 - (BPT * t + i)];
+    if (above < rem && above + ci >= rem) {
+      *s_bin = NB - 1 - (BPT * t + i);
+      *s_above = above;
+    }
+    above += ci;
+  }
+  __syncthreads();
+}
+
+// Value-range refinement over the `len` keys at `src` (LDS or global
+// memory, read with stride NT): histogram the keys inside [lo, hi] over NB
+// equal-width bins, keep the crossing bin, shrink [lo, hi] to its smallest
+// and largest key, until lo == hi.  Each round shrinks the range at least
+// NB-fold, so fp32 needs at most a few dozen rounds.  Returns the value all
+// remaining keys share; *rem becomes the number of them to take.
+template <int NT, int NB>
+__device__ float refine_range(const float* src, int len, float lo, float hi, uint32_t* rem,
+                              uint32_t* hist, float* fbuf, unsigned long long* sbuf, int* s_bin,
+                              uint32_t* s_above) {
+  const int t = threadIdx.x;
+  for (int round = 0; round < 64 && lo < hi; ++round) {
+    for (int i = t; i < NB; i += NT) hist[i] = 0u;
+    __syncthreads();
+    const float scale =
+        static_cast<float>(NB / (static_cast<double>(hi) - static_cast<double>(lo)));
+    for (int k = t; k < len; k += NT) {
+      const float x = src[k];
+      if (x >= lo && x <= hi) atomicAdd(&hist[range_bin<NB>(x, lo, scale)], 1u);
+    }
+    __syncthreads();
+    crossing_bin<NT, NB>(hist, *rem, sbuf, s_bin, s_above);
+    const int bsel = *s_bin;
+    *rem -= *s_above;
+    float nlo = INFINITY, nhi = -INFINITY;
+    for (int k = t; k < len; k += NT) {
+      const float x = src[k];
+      if (x >= lo && x <= hi && range_bin<NB>(x, lo, scale) == bsel) {
+        nlo = x < nlo ? x : nlo;
+        nhi = x > nhi ? x : nhi;
+      }
+    }
+    lo = block_min<NT>(nlo, fbuf);
+    hi = block_max<NT>(nhi, fbuf);
+  }
+  return lo;
+}
+
+// The top-k selection of each unit (the n_sel largest fp32 estimates, ties
+// to the lower candidate index, output ascending) runs over the whole chip
+// in four launches, with blocks of kSelBlock candidates:
+//   ehist_kernel   the unit's range [lo, hi] from the rerank workgroups, and
+//                  the histogram of the estimates over kSelBins equal-width
+//                  bins of it (binning is monotone in the value, so every
+//                  key of a higher bin exceeds every key of a lower one);
+//   cross_kernel   the crossing bin b1 (keys of higher bins are all taken,
+//                  keys of lower bins none); per block, the keys above b1;
+//                  the keys inside b1 go to a member list;
+//   thresh_kernel  exact value-range refinement over the members gives the
+//                  threshold T and the number of ties at T to take, a radix
+//                  select over the tied members' indices the last tied index
+//                  taken; per block, the output offset;
+//   output_kernel  each block writes its taken candidates in index order.
+// When every estimate is equal the first n_sel candidates are taken; when
+// n_sel >= C all are, and only the output kernel runs.
+
+// Grid (nsb, U), 256 threads.
+__global__ __launch_bounds__(256) void ehist_kernel(const float* __restrict__ est, int C, int nrwg,
+                                                    const uint32_t* __restrict__ rmm,
+                                                    uint32_t* __restrict__ rng,
+                                                    uint32_t* __restrict__ ehtot) {
+  const int blk = blockIdx.x;
+  const int u = blockIdx.y;
+  const int t = threadIdx.x;
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t red[8];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  const uint2* mm = reinterpret_cast<const uint2*>(rmm) + static_cast<size_t>(u) * nrwg;
+  for (int i = t; i < nrwg; i += 256) {
+    const uint2 v = mm[i];
+    kmin = min(kmin, v.x);
+    kmax = max(kmax, v.y);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, kWave)));
+    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, kWave)));
+  }
+  if ((t & (kWave - 1)) == 0) {
+    red[t / kWave] = kmin;
+    red[4 + t / kWave] = kmax;
+  }
+  for (int i = t; i < kSelBins; i += 256) hist[i] = 0u;
+  __syncthreads();
+  kmin = min(min(red[0], red[1]), min(red[2], red[3]));
+  kmax = max(max(red[4], red[5]), max(red[6], red[7]));
+  if (blk == 0 && t == 0) {
+    rng[2 * u] = kmin;
+    rng[2 * u + 1] = kmax;
+  }
+  const EstRange r = est_range(kmin, kmax);
+  if (!(r.lo < r.hi)) return;  // every estimate equal: no histogram needed
+  const float* e = est + static_cast<size_t>(u) * C + static_cast<size_t>(blk) * kSelBlock;
+  const int n = min(kSelBlock, C - blk * kSelBlock);
+#pragma unroll
+  for (int j = 0; j < kSelBlock / 256; ++j) {
+    const int k = j * 256 + t;
+    if (k < n) atomicAdd(&hist[range_bin<kSelBins>(e[k], r.lo, r.scale)], 1u);
+  }
+  __syncthreads();
+  uint32_t* out = ehtot + static_cast<size_t>(u) * kSelBins;
+  for (int i = t; i < kSelBins; i += 256) {
+    const uint32_t c = hist[i];
+    if (c) atomicAdd(&out[i], c);
+  }
+}
+
+// Loads the unit's estimate histogram into LDS (NT threads).
+template <int NT>
+__device__ __forceinline__ void load_hist(const uint32_t* __restrict__ ehtot, int u, uint32_t* hist) {
+  const uint4* src = reinterpret_cast<const uint4*>(ehtot + static_cast<size_t>(u) * kSelBins);
+  for (int i = threadIdx.x; i < kSelBins / 4; i += NT) reinterpret_cast<uint4*>(hist)[i] = src[i];
+  __syncthreads();
+}
+
+// Grid (nsb, U), 256 threads.
+__global__ __launch_bounds__(256) void cross_kernel(const float* __restrict__ est, int C, int n_sel,
+                                                    int nsb, const uint32_t* __restrict__ rng,
+                                                    const uint32_t* __restrict__ ehtot,
+                                                    int32_t* __restrict__ gtb,
+                                                    float* __restrict__ lval,
+                                                    int32_t* __restrict__ lidx,
+                                                    uint32_t* __restrict__ lcnt) {
+  const int blk = blockIdx.x;
+  const int u = blockIdx.y;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ unsigned long long sbuf[5];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  const EstRange r = est_range(rng[2 * u], rng[2 * u + 1]);
+  if (!(r.lo < r.hi)) return;
+  load_hist<256>(ehtot, u, hist);
+  crossing_bin<256, kSelBins>(hist, static_cast<uint32_t>(n_sel), sbuf, &s_bin, &s_above);
+  const int b1 = s_bin;
+  const float* e = est + static_cast<size_t>(u) * C;
+  uint32_t gt = 0;
+  const unsigned long long below = lanes_below();
+#pragma unroll
+  for (int j = 0; j < kSelBlock / 256; ++j) {
+    const int k = blk * kSelBlock + j * 256 + t;
+    float x = 0.f;
+    int b = -1;
+    if (k < C) {
+      x = e[k];
+      b = range_bin<kSelBins>(x, r.lo, r.scale);
+    }
+    gt += b > b1 ? 1u : 0u;
+    // members of the crossing bin: one atomic per wave
+    const unsigned long long bm = __ballot(b == b1);
+    if (bm) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&lcnt[u], static_cast<uint32_t>(__popcll(bm)));
+      base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0, kWave));
+      if (b == b1) {
+        const uint32_t slot = base + static_cast<uint32_t>(__popcll(bm & below));
+        if (slot < static_cast<uint32_t>(C)) {
+          lval[static_cast<size_t>(u) * C + slot] = x;
+          lidx[static_cast<size_t>(u) * C + slot] = k;
+        }
+      }
+    }
+  }
+  const uint32_t g = block_sum<256>(gt, reinterpret_cast<uint32_t*>(sbuf));
+  if (t == 0) gtb[static_cast<size_t>(u) * nsb + blk] = static_cast<int32_t>(g);
+}
+
+// Grid U, 1024 threads.
+__global__ __launch_bounds__(1024) void thresh_kernel(int C, int n_sel, int nsb,
+                                                      const uint32_t* __restrict__ rng,
+                                                      const uint32_t* __restrict__ ehtot,
+                                                      const int32_t* __restrict__ gtb,
+                                                      const float* __restrict__ lval,
+                                                      const int32_t* __restrict__ lidx,
+                                                      const uint32_t* __restrict__ lcnt,
+                                                      int32_t* __restrict__ soff,
+                                                      int32_t* __restrict__ selp) {
+  constexpr int NT = 1024, NW = NT / kWave, NB = kSelBins;
   const int u = blockIdx.x;
+  const int t = threadIdx.x;
+  __shared__ uint32_t hist[NB];
+  __shared__ uint32_t cntb[kSelMaxBlocks];
+  __shared__ float fbuf[NW];
+  __shared__ unsigned long long sbuf[NW + 1];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  const EstRange r = est_range(rng[2 * u], rng[2 * u + 1]);
+  float T = r.lo;
+  int k_tie = n_sel - 1;
+  if (r.lo < r.hi) {
+    uint32_t rem = static_cast<uint32_t>(n_sel);
+    load_hist<NT>(ehtot, u, hist);
+    crossing_bin<NT, NB>(hist, rem, sbuf, &s_bin, &s_above);
+    rem -= s_above;
+    const int m = static_cast<int>(min(lcnt[u], static_cast<uint32_t>(C)));
+    const float* lv = lval + static_cast<size_t>(u) * C;
+    const int32_t* li = lidx + static_cast<size_t>(u) * C;
+    float nlo = INFINITY, nhi = -INFINITY;
+    for (int i = t; i < m; i += NT) {
+      const float x = lv[i];
+      nlo = x < nlo ? x : nlo;
+      nhi = x > nhi ? x : nhi;
+    }
+    const float lo = block_min<NT>(nlo, fbuf);
+    const float hi = block_max<NT>(nhi, fbuf);
+    T = refine_range<NT, NB>(lv, m, lo, hi, &rem, hist, fbuf, sbuf, &s_bin, &s_above);
+    // the rem-th smallest index among the members equal to T: radix select,
+    // 11 + 11 bits (indices are below 2^21 + 2^11)
+    uint32_t want = rem, hb = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 11 : 0;
+      for (int i = t; i < 2048; i += NT) hist[i] = 0u;
+      __syncthreads();
+      for (int i = t; i < m; i += NT) {
+        const int k = li[i];
+        if (lv[i] == T && (pass == 0 || (static_cast<uint32_t>(k) >> 11) == hb))
+          atomicAdd(&hist[(static_cast<uint32_t>(k) >> shift) & 2047u], 1u);
+      }
+      __syncthreads();
+      // ascending crossing: two bins per thread, counts from the bottom
+      const uint32_t c0 = hist[2 * t], c1 = hist[2 * t + 1];
+      unsigned long long tot;
+      const uint32_t below_cnt = static_cast<uint32_t>(
+          block_excl_scan<NT>(static_cast<unsigned long long>(c0 + c1), sbuf, &tot));
+      if (below_cnt < want && below_cnt + c0 >= want) {
+        s_bin = 2 * t;
+        s_above = below_cnt;
+      } else if (below_cnt + c0 < want && below_cnt + c0 + c1 >= want) {
+        s_bin = 2 * t + 1;
+        s_above = below_cnt + c0;
+      }
+      __syncthreads();
+      want -= s_above;
+      if (pass == 0)
+        hb = static_cast<uint32_t>(s_bin);
+      else
+        k_tie = static_cast<int>((hb << 11) | static_cast<uint32_t>(s_bin));
+      __syncthreads();
+    }
+    // members taken, per block
+    for (int i = t; i < nsb; i += NT) cntb[i] = 0u;
+    __syncthreads();
+    for (int i = t; i < m; i += NT) {
+      const float x = lv[i];
+      const int k = li[i];
+      if ((x > T || (x == T && k <= k_tie)) && k >= 0 && k < C) atomicAdd(&cntb[k / kSelBlock], 1u);
+    }
+    __syncthreads();
+  }
+  // output offsets of the blocks (one block per thread)
+  const int b = t;
+  uint32_t taken = 0;
+  if (b < nsb) {
+    if (r.lo < r.hi)
+      taken = cntb[b] + static_cast<uint32_t>(gtb[static_cast<size_t>(u) * nsb + b]);
+    else  // every estimate equal: the first n_sel candidates
+      taken = static_cast<uint32_t>(min(max(n_sel - b * kSelBlock, 0), kSelBlock));
+  }
+  unsigned long long tot;
+  const unsigned long long ex =
+      block_excl_scan<NT>(static_cast<unsigned long long>(taken), sbuf, &tot);
+  if (b < nsb) soff[static_cast<size_t>(u) * nsb + b] = static_cast<int32_t>(ex);
+  if (t == 0) {
+    selp[2 * u] = __float_as_int(T);
+    selp[2 * u + 1] = k_tie;
+  }
+}
+
+// Grid (max(nsb, 1), U), 256 threads: block blk writes its taken candidates
+// in index order (slot j, wave, lane) from its output offset; with n_sel >=
+// C every candidate is taken and block blk starts at blk * kSelBlock.  The
+// caller's buffer is padded with -1 past n_sel by block 0.
+__global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ est,
+                                                     const int32_t* __restrict__ cand, int C,
+                                                     int n_sel, int k_ret, int first, int nsb,
+                                                     const int32_t* __restrict__ soff,
+                                                     const int32_t* __restrict__ selp,
+                                                     int32_t* __restrict__ sel,
+                                                     int32_t* __restrict__ retrieved) {
+  constexpr int NW = 256 / kWave, NS = kSelBlock / 256;
+  const int blk = blockIdx.x;
+  const int u = blockIdx.y;
   const int t = threadIdx.x;
   const int wave = t / kWave;
   const int lane = t & (kWave - 1);
-  __shared__ uint32_t wh[NW][256];
-  __shared__ uint32_t total[256];
-  __shared__ uint32_t s_digit, s_above;
-  __shared__ unsigned long long sbuf[NW + 1];
-  const float* e = est + static_cast<size_t>(u) * C;
-  const int32_t* cd = cand + static_cast<size_t>(u) * C;
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t remaining = static_cast<uint32_t>(n_sel);
+  __shared__ uint32_t cnt[NS * NW];
   const bool all = n_sel >= C;
+  float T = 0.f;
+  int k_tie = -1, base = blk * kSelBlock;
   if (!all) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      for (int i = t; i < NW * 256; i += NT) (&wh[0][0])[i] = 0u;
-      __syncthreads();
-      for (int k = t; k < C; k += NT) {
-        const uint32_t key = f32_order_key(e[k]);
-        if ((key & pmask) == prefix) atomicAdd(&wh[wave][(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (t < 256) {
-        uint32_t s = 0;
+    T = __int_as_float(selp[2 * u]);
+    k_tie = selp[2 * u + 1];
+    base = soff[static_cast<size_t>(u) * nsb + blk];
+  }
+  const float* e = est + static_cast<size_t>(u) * C;
+  bool take[NS];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) s += wh[w][t];
-        total[t] = s;
+  for (int j = 0; j < NS; ++j) {
+    const int k = blk * kSelBlock + j * 256 + t;
+    bool tk = false;
+    if (k < C) {
+      if (all) {
+        tk = true;
+      } else {
+        const float x = e[k];
+        tk = x > T || (x == T && k <= k_tie);
       }
-      __syncthreads();
-      if (t < kWave) {
-        // lane l holds digits 4l .. 4l+3; suffix counts from the top digit
-        uint32_t v[4], tot4 = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[j] = total[4 * lane + j];
-          tot4 += v[j];
-        }
-        uint32_t run = wave_suffix_incl(tot4) - tot4;  // digits above this lane's
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          const uint32_t above = run;
-          run += v[j];
-          if (above < remaining && run >= remaining) {
-            s_digit = static_cast<uint32_t>(4 * lane + j);
-            s_above = above;
-          }
-        }
-      }
-      __syncthreads();
-      remaining -= s_above;
-      prefix |= s_digit << shift;
-      pmask |= 255u << shift;
-      __syncthreads();
     }
+    take[j] = tk;
+    const unsigned long long b = __ballot(tk);
+    if (lane == 0) cnt[j * NW + wave] = static_cast<uint32_t>(__popcll(b));
   }
-  // ordered output over contiguous blocks of candidates
-  const int per = (C + NT - 1) / NT;
-  const int k0 = min(C, t * per);
-  const int k1 = min(C, k0 + per);
-  uint32_t gt = 0, eq = 0;
-  for (int k = k0; k < k1; ++k) {
-    const uint32_t key = f32_order_key(e[k]);
-    gt += (all || key > prefix) ? 1u : 0u;
-    eq += (!all && key == prefix) ? 1u : 0u;
+  __syncthreads();
+  if (t < kWave) {
+    const uint32_t c = t < NS * NW ? cnt[t] : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (t < NS * NW) cnt[t] = incl - c;
   }
-  unsigned long long tot;
-  const unsigned long long ex = block_excl_scan<NT>(
-      static_cast<unsigned long long>(gt) | (static_cast<unsigned long long>(eq) << 32), sbuf, &tot);
-  uint32_t tie = static_cast<uint32_t>(ex >> 32);
-  int off = static_cast<int>(ex & 0xffffffffull) + static_cast<int>(min(remaining, tie));
+  __syncthreads();
   int32_t* so = sel + static_cast<size_t>(u) * n_sel;
   int32_t* ro = retrieved ? retrieved + static_cast<size_t>(u) * k_ret : nullptr;
-  for (int k = k0; k < k1; ++k) {
-    const uint32_t key = f32_order_key(e[k]);
-    bool take = all || key > prefix;
-    if (!all && key == prefix) {
-      take = tie < remaining;
-      ++tie;
-    }
-    if (take && off < n_sel) {
-      const int32_t p = first + cd[k];
+  const unsigned long long below = lanes_below();
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const unsigned long long b = __ballot(take[j]);
+    const int off = base + static_cast<int>(cnt[j * NW + wave]) + __popcll(b & below);
+    if (take[j] && off < n_sel) {
+      const int32_t p = first + cand[static_cast<size_t>(u) * C + blk * kSelBlock + j * 256 + t];
       so[off] = p;
       if (ro) ro[off] = p;
     }
-    off += take ? 1 : 0;
   }
-  if (ro)
-    for (int j = n_sel + t; j < k_ret; j += NT) ro[j] = -1;
+  if (ro && blk == 0)
+    for (int j = n_sel + t; j < k_ret; j += 256) ro[j] = -1;
 }
 
 // Grid (nsplit, U): 64 attended rows per workgroup (Sink rows, then the
@@ -688,29 +1060,32 @@ __global__ __launch_bounds__(256) void attend_kernel(
   }
 }
 
-// Grid U: out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s.
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part, int nsplit,
-                                                    int G, int D, int Hq, int Hkv,
-                                                    float* __restrict__ out) {
-  const int u = blockIdx.x;
+// Grid (G, U), d threads: out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s
+// for query head g of unit u.  The maximum and the denominator are reduced
+// over the slices in parallel; each thread then sums its column.
+template <int D>
+__global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part, int nsplit,
+                                                  int G, int Hq, int Hkv,
+                                                  float* __restrict__ out) {
+  constexpr int NW = D / kWave;
+  const int g = blockIdx.x;
+  const int u = blockIdx.y;
   const int b = u / Hkv;
   const int h = u - b * Hkv;
+  const int c = threadIdx.x;
+  __shared__ float buf[NW];
   const size_t stride = static_cast<size_t>(G) * (D + 2);
-  const float* p0 = part + static_cast<size_t>(u) * nsplit * stride;
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int g = e / D;
-    const int c = e - g * D;
-    const float* p = p0 + static_cast<size_t>(g) * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * stride + D]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float f = expf(p[s * stride + D] - M);
-      num += f * p[s * stride + c];
-      den += f * p[s * stride + D + 1];
-    }
-    out[(static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G + g) * D + c] = num / den;
-  }
+  const float* p = part + static_cast<size_t>(u) * nsplit * stride + static_cast<size_t>(g) * (D + 2);
+  float mx = -INFINITY;
+  for (int s = c; s < nsplit; s += D) mx = fmaxf(mx, p[s * stride + D]);
+  const float M = block_max<D>(mx, buf);
+  float dl = 0.f;
+  for (int s = c; s < nsplit; s += D) dl += expf(p[s * stride + D] - M) * p[s * stride + D + 1];
+  const float den = block_sum<D>(dl, buf);
+  float num = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) num += expf(p[s * stride + D] - M) * p[s * stride + c];
+  out[(static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G + g) * D + c] = num / den;
 }
 
 template <int DT>
@@ -744,8 +1119,8 @@ hipError_t decode_impl(const rskv_retrieval* r, const void* qv, float* out, int3
     for (int k = 0; k < kKernels; ++k) recorded[k] = false;
   hipError_t e = hipSuccess;
   if (active) {
-    e = launch(query_kernel<DT>, dim3(r->Bs, U), dim3(256), 0, st, E(0), q, r->Hq, r->Hkv, r->G,
-               r->d, r->signs, r->rho, r->qt, r->qn, r->votes, r->tot);
+    e = launch(query_kernel<DT>, dim3(r->Bs, U), dim3(1024), 0, st, E(0), q, r->Hq, r->Hkv, r->G,
+               r->d, r->signs, r->rho, r->qt, r->qn, r->votes, r->tot, r->ehtot, r->lcnt);
     if (e != hipSuccess) return e;
     if (r->Bs == 16)
       e = launch(vote_kernel<16>, dim3(r->nchunk, U), dim3(256), 0, st, E(1),
@@ -765,18 +1140,37 @@ hipError_t decode_impl(const rskv_retrieval* r, const void* qv, float* out, int3
       e = launch(rerank_kernel<128>, dim3((r->C + 255) / 256, U), dim3(256), 0, st, E(3),
                  static_cast<const uint8_t*>(r->rec), r->N, static_cast<const int32_t*>(r->cand),
                  r->C, static_cast<const double*>(r->qt), static_cast<const double*>(r->qn),
-                 r->cb, r->est);
+                 r->cb, r->est, r->rmm);
     else
       e = launch(rerank_kernel<64>, dim3((r->C + 255) / 256, U), dim3(256), 0, st, E(3),
                  static_cast<const uint8_t*>(r->rec), r->N, static_cast<const int32_t*>(r->cand),
                  r->C, static_cast<const double*>(r->qt), static_cast<const double*>(r->qn),
-                 r->cb, r->est);
+                 r->cb, r->est, r->rmm);
+    if (e != hipSuccess) return e;
+  }
+  if (active && r->n_sel < r->C) {
+    e = launch(ehist_kernel, dim3(r->nsb, U), dim3(256), 0, st, E(4),
+               static_cast<const float*>(r->est), r->C, r->nrwg,
+               static_cast<const uint32_t*>(r->rmm), r->rng, r->ehtot);
+    if (e != hipSuccess) return e;
+    e = launch(cross_kernel, dim3(r->nsb, U), dim3(256), 0, st, E(5),
+               static_cast<const float*>(r->est), r->C, r->n_sel, r->nsb,
+               static_cast<const uint32_t*>(r->rng), static_cast<const uint32_t*>(r->ehtot),
+               r->gtb, r->lval, r->lidx, r->lcnt);
+    if (e != hipSuccess) return e;
+    e = launch(thresh_kernel, dim3(U), dim3(1024), 0, st, E(6), r->C, r->n_sel, r->nsb,
+               static_cast<const uint32_t*>(r->rng), static_cast<const uint32_t*>(r->ehtot),
+               static_cast<const int32_t*>(r->gtb), static_cast<const float*>(r->lval),
+               static_cast<const int32_t*>(r->lidx), static_cast<const uint32_t*>(r->lcnt),
+               r->soff, r->selp);
     if (e != hipSuccess) return e;
   }
   if (active || (retrieved != nullptr && r->k_ret > 0)) {
-    e = launch(select_kernel, dim3(U), dim3(1024), 0, st, E(4), static_cast<const float*>(r->est),
-               static_cast<const int32_t*>(r->cand), active ? r->C : 0, r->n_sel, r->k_ret, r->ns,
-               r->sel, retrieved);
+    const int Ca = active ? r->C : 0;
+    e = launch(output_kernel, dim3(active ? r->nsb : 1, U), dim3(256), 0, st, E(7),
+               static_cast<const float*>(r->est), static_cast<const int32_t*>(r->cand), Ca, r->n_sel,
+               r->k_ret, r->ns, r->nsb, static_cast<const int32_t*>(r->soff),
+               static_cast<const int32_t*>(r->selp), r->sel, retrieved);
     if (e != hipSuccess) return e;
   }
   const T* kn = static_cast<const T*>(r->k_near);
@@ -784,16 +1178,19 @@ hipError_t decode_impl(const rskv_retrieval* r, const void* qv, float* out, int3
   const T* kf = static_cast<const T*>(r->k_far);
   const T* vf = static_cast<const T*>(r->v_far);
   if (r->d == 128)
-    e = launch(attend_kernel<DT, 128>, dim3(r->nsplit, U), dim3(256), 0, st, E(5), q, kn, vn, kf,
+    e = launch(attend_kernel<DT, 128>, dim3(r->nsplit, U), dim3(256), 0, st, E(8), q, kn, vn, kf,
                vf, static_cast<const int32_t*>(r->sel), r->Hq, r->Hkv, r->G, r->ns, r->n_sel, r->N,
                r->n_near, r->n_att, r->nsplit, r->part);
   else
-    e = launch(attend_kernel<DT, 64>, dim3(r->nsplit, U), dim3(256), 0, st, E(5), q, kn, vn, kf,
+    e = launch(attend_kernel<DT, 64>, dim3(r->nsplit, U), dim3(256), 0, st, E(8), q, kn, vn, kf,
                vf, static_cast<const int32_t*>(r->sel), r->Hq, r->Hkv, r->G, r->ns, r->n_sel, r->N,
                r->n_near, r->n_att, r->nsplit, r->part);
   if (e != hipSuccess) return e;
-  return launch(merge_kernel, dim3(U), dim3(256), 0, st, E(6), static_cast<const float*>(r->part),
-                r->nsplit, r->G, r->d, r->Hq, r->Hkv, out);
+  if (r->d == 128)
+    return launch(merge_kernel<128>, dim3(r->G, U), dim3(128), 0, st, E(9),
+                  static_cast<const float*>(r->part), r->nsplit, r->G, r->Hq, r->Hkv, out);
+  return launch(merge_kernel<64>, dim3(r->G, U), dim3(64), 0, st, E(9),
+                static_cast<const float*>(r->part), r->nsplit, r->G, r->Hq, r->Hkv, out);
 }
 
 }  // namespace

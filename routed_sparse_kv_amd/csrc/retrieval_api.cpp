@@ -222,6 +222,11 @@ int rskv_retrieval_build(const void* K, const void* V, const int8_t* signs,
     r->npad = static_cast<size_t>(r->nchunk) * R::kChunk;
     r->nbins = r->Bs * r->rho + 1;
     r->nsplit = (r->n_att + R::kRows - 1) / R::kRows;
+    r->nsb = (r->C + R::kSelBlock - 1) / R::kSelBlock;
+    r->nrwg = (r->C + 255) / 256;
+    if (r->nsb > R::kSelMaxBlocks)
+      return report_error(RSKV_EINVAL, "too many candidates: ceil(cand_frac * N) must be <= " +
+                                           std::to_string(R::kSelBlock * R::kSelMaxBlocks));
     make_codebook(r->m, &r->cb);
 
     const size_t U = static_cast<size_t>(r->B) * r->Hkv;
@@ -250,6 +255,15 @@ int rskv_retrieval_build(const void* K, const void* V, const int8_t* signs,
         (rc = dev_array(r, &r->thr, U * 2, "thresholds")) ||
         (rc = dev_array(r, &r->cand, U * r->C, "candidates")) ||
         (rc = dev_array(r, &r->est, U * r->C, "estimates")) ||
+        (rc = dev_array(r, &r->rmm, U * r->nrwg * 2, "estimate ranges")) ||
+        (rc = dev_array(r, &r->rng, U * 2, "estimate ranges")) ||
+        (rc = dev_array(r, &r->ehtot, U * R::kSelBins, "estimate histograms")) ||
+        (rc = dev_array(r, &r->gtb, U * r->nsb, "top-k block counts")) ||
+        (rc = dev_array(r, &r->lval, U * r->C, "top-k members")) ||
+        (rc = dev_array(r, &r->lidx, U * r->C, "top-k members")) ||
+        (rc = dev_array(r, &r->lcnt, U, "top-k member counts")) ||
+        (rc = dev_array(r, &r->soff, U * r->nsb, "top-k offsets")) ||
+        (rc = dev_array(r, &r->selp, U * 2, "top-k thresholds")) ||
         (rc = dev_array(r, &r->sel, U * r->n_sel, "retrieved")) ||
         (rc = dev_array(r, &r->part, U * r->nsplit * r->G * (d + 2), "partials")))
       return rc;

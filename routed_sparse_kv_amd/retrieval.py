@@ -38,11 +38,12 @@ class RetrievalTrace(C.Structure):
 
 
 class RetrievalProfile(C.Structure):
-    _fields_ = [("steps", C.c_int64), ("ms", C.c_double * 7)]
+    _fields_ = [("steps", C.c_int64), ("ms", C.c_double * 10)]
 
 
-#: Names of the seven decode launches, in the order of RetrievalProfile.ms.
-KERNELS = ("query", "vote", "compact", "rerank", "select", "attend", "merge")
+#: Names of the ten decode launches, in the order of RetrievalProfile.ms.
+KERNELS = ("query", "vote", "compact", "rerank", "histogram", "crossing", "threshold", "output",
+           "attend", "merge")
 
 _ready = False
 

@@ -55,6 +55,9 @@ CASES = {
                        dict(rho=16, cand_frac=0.0, k_ret=20, n_sink=4, n_local=4)),
     "no_sink_local": ("gqa_32k_bf16", dict(T=6000, Hkv=1, Hq=4, steps=2),
                       dict(rho=1, cand_frac=0.03, k_ret=40, n_sink=0, n_local=0)),
+    # more candidates than the top-k kernel keeps in registers (1024 x 64)
+    "select_from_memory": ("tiny_fp32_2k", dict(T=70100, steps=1),
+                           dict(rho=16, cand_frac=1.0, k_ret=300, n_sink=50, n_local=50)),
 }
 
 
@@ -152,7 +155,7 @@ def check_step(tr, res, enc, u, info, what):
     return check_retrieved(tr["retrieved"][u], res, n_sel, first, what)
 
 
-def run_case(wl, params, kv_tier="hbm", zero_keys=False, zero_query=False):
+def run_case(wl, params, kv_tier="hbm", zero_keys=False, zero_query=False, dup_keys=False):
     import torch
     cfg = wl.cfg
     dt, B, Hq, Hkv = wl.dtype, cfg["B"], cfg["Hq"], cfg["Hkv"]
@@ -167,6 +170,16 @@ def run_case(wl, params, kv_tier="hbm", zero_keys=False, zero_query=False):
         h9 = np.array([-1.0 if bin(i & 9).count("1") % 2 else 1.0 for i in range(d)])
         K[:, :, 5::97] = W.store(np.zeros(d, np.float32), dt)
         K[:, :, 11::101] = W.store((signs * (1.0 + h9) / d).astype(np.float32), dt)
+    if dup_keys:
+        # one key repeated at many positions, aligned with the first query's
+        # group mean: its copies share one estimate, and more of them than
+        # k_ret rank at the top, so the cut falls inside an exact tie
+        G_ = Hq // Hkv
+        q0 = W.as_f64(wl.queries[0], dt)
+        for b in range(B):
+            for h in range(Hkv):
+                qb = q0[b, h * G_:(h + 1) * G_].mean(axis=0)
+                K[b, h, 100::37] = W.store((3.0 * qb / np.linalg.norm(qb)).astype(np.float32), dt)
     idx = gpu_index(K, V, signs, Hq, dt, kv_tier=kv_tier, **params)
     info = idx.info
     say(f"  N={info['n_retrieval']} C={info['n_cand']} n_sel={info['n_sel']} "
@@ -247,6 +260,14 @@ def test_retrieval_zero_keys_and_query():
     run_case(wl, dict(rho=16, cand_frac=0.05, k_ret=40, n_sink=4, n_local=16), zero_query=True)
 
 
+def test_retrieval_tied_estimates():
+    """The k_ret-th estimate is shared by many equal keys: the retrieved
+    copies are the ones at the lowest positions."""
+    wl = W.generate("gqa_32k_bf16", B=1, Hkv=2, Hq=8, T=9001, steps=1)
+    say("[retrieval tied estimates]")
+    run_case(wl, dict(rho=16, cand_frac=0.05, k_ret=64, n_sink=16, n_local=128), dup_keys=True)
+
+
 def test_retrieval_host_tier_matches_hbm():
     """K/V of the retrieval region in pinned host memory: identical results."""
     import torch
@@ -290,3 +311,88 @@ def test_retrieval_argument_errors():
     idx.close()
     with pytest.raises(RskvError):
         idx.decode(torch.zeros((1, 1, 64), device="cuda"))
+
+
+@pytest.mark.timeout(900)
+def test_retrieval_full_size():
+    """The million-token workload at its real shape (8 KV heads, 1M tokens)
+    in the configuration bench.py times.  The oracle checks what it can
+    compute one by one: 2048 sampled keys of every unit (buckets, codes, w),
+    every unit's rotated query and vote table, 512 sampled candidates'
+    estimates, and three units' outputs; and properties at full size: the
+    vote totals are the oracle's table applied to the (sample-checked)
+    buckets, the candidates are the oracle's top ceil(gamma N) of those
+    totals, the retrieved set is the oracle's top k_ret of the GPU's fp32
+    estimates."""
+    import torch
+    say("[retrieval full] generate million_1m_bf16")
+    wl = W.generate("million_1m_bf16")
+    cfg = wl.cfg
+    dt, B, Hkv = wl.dtype, cfg["B"], cfg["Hkv"]
+    G = cfg["Hq"] // Hkv
+    params = W.retrieval_params()
+    signs = W.srht_signs(cfg)
+    say("[retrieval full] build")
+    idx = gpu_index(wl.K, wl.V, signs, cfg["Hq"], dt, **params)
+    info = idx.info
+    N, C, n_sel, first = info["n_retrieval"], info["n_cand"], info["n_sel"], info["n_sink"]
+    say(f"  N={N} C={C} n_sel={n_sel} n_attend={info['n_attend']}")
+    ex = idx.export()
+    cb = P.magnitude_codebook(8)
+    check_codebook(ex, cb)
+    rng = np.random.default_rng(7)
+    U = B * Hkv
+    for u in range(U):
+        b, h = divmod(u, Hkv)
+        rows = np.sort(rng.choice(N, 2048, replace=False))
+        enc = P.encode_keys(W.as_f64(wl.K[b, h, first + rows], dt), signs, 8, cb)
+        check_encoding(ex["buckets"][u, rows], ex["codes"][u, rows], ex["w"][u, rows], enc,
+                       f"unit {u} sampled keys")
+    worst = 0.0
+    for s in range(2):
+        qn = wl.queries[s]
+        ret = torch.full((B, Hkv, params["k_ret"]), -7, dtype=torch.int32, device="cuda")
+        say(f"[retrieval full] decode step {s}")
+        out = idx.decode(dev_tensor(qn, dt), retrieved=ret)
+        torch.cuda.synchronize()
+        tr = idx.trace()
+        gret = ret.cpu().numpy()
+        out = out.cpu().numpy().astype(np.float64)
+        qf = W.as_f64(qn, dt)
+        for u in range(U):
+            b, h = divmod(u, Hkv)
+            what = f"step {s} unit {u}"
+            qg = qf[b, h * G:(h + 1) * G]
+            qbar = qg.sum(axis=0) / G
+            qt = P.srht(qbar, signs)[0]
+            qnorm = float(np.linalg.norm(qbar))
+            assert np.max(np.abs(tr["q_rot"][u] - qt)) <= 1e-14, f"{what}: rotated query"
+            assert abs(tr["q_norm"][u] - qnorm) <= 1e-13 * max(1.0, qnorm), f"{what}: |q|"
+            assert not vote_ambiguous(qt, 8, params["rho"]), f"{what}: near-tied pattern scores"
+            table = P.vote_table(qt, 8, params["rho"])
+            assert np.array_equal(tr["votes"][u].astype(np.int64), table), f"{what}: votes"
+            sc = P.coarse_scores(ex["buckets"][u].astype(np.int64), table)
+            assert np.array_equal(tr["scores"][u].astype(np.int64), sc), f"{what}: totals"
+            cand = P.top_by_score(sc, C)
+            assert np.array_equal(tr["cand"][u], cand), f"{what}: candidates"
+            pick = np.sort(rng.choice(C, 512, replace=False))
+            enc = P.encode_keys(W.as_f64(wl.K[b, h, first + cand[pick]], dt), signs, 8, cb)
+            dec = P.as_decision(P.estimate(enc, np.arange(512), qt, qnorm))
+            d_ulp = np.abs(tr["est"][u, pick].astype(np.float64) - dec.astype(np.float64))
+            assert (d_ulp <= np.spacing(np.abs(dec)).astype(np.float64)).all(), \
+                f"{what}: sampled estimates"
+            want = first + cand[P.top_by_value(tr["est"][u], n_sel)]
+            assert np.array_equal(tr["retrieved"][u], want), f"{what}: retrieved set"
+            assert np.array_equal(gret[b, h, :n_sel], want) and (gret[b, h, n_sel:] == -1).all()
+        for u in sorted({0, U - 1, int(rng.integers(U))}):
+            b, h = divmod(u, Hkv)
+            T = cfg["T"]
+            sink, _, local = P.regions(T, params["n_sink"], params["n_local"])
+            use = np.concatenate([sink, gret[b, h, :n_sel], local])
+            ref = P.attend(W.as_f64(wl.K[b, h], dt), W.as_f64(wl.V[b, h], dt),
+                           qf[b, h * G:(h + 1) * G], use)
+            err = float(np.max(np.abs(out[b, h * G:(h + 1) * G] - ref)))
+            worst = max(worst, err)
+            assert err <= TOL[dt], f"step {s} unit {u}: max abs err {err:.3e}"
+    idx.close()
+    say(f"[retrieval full] max abs err {worst:.2e}")

@@ -49,7 +49,7 @@ MUTATIONS = {
     "local region one short": ("l0 = max(s, T - n_local)", "l0 = max(s, T - n_local + 1)"),
     "sink dropped": ("use = np.concatenate([sink, retrieved", "use = np.concatenate([sink[:0], retrieved"),
     "first query routes": ("qbar = q_group.sum(axis=0) / q_group.shape[0]", "qbar = q_group[0]"),
-    "logit scale 1/d": ("logits = q_group @ K[use].T / math.sqrt(d)", "logits = q_group @ K[use].T / d"),
+    "logit scale 1/d": ("K[idx].T / math.sqrt(K.shape[1])", "K[idx].T / K.shape[1]"),
     "calibration kept in fp64": ("w=w64.astype(np.float32).astype(np.float64)", "w=w64"),
 }
 
