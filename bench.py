@@ -260,6 +260,13 @@ def retrieval_bench(args):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        # a plain copy of known size: reads and writes exactly 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t0 = time.perf_counter()
     wl = W.generate(args.workload)
     cfg = wl.cfg

@@ -319,7 +319,11 @@ __global__ __launch_bounds__(1024) void query_kernel(const typename Elem<DT>::T*
 
 // Grid (nchunk, U): kChunk consecutive keys per workgroup.  Vote totals by
 // table lookups in LDS; per-chunk counts of totals >= s (for the ordered
-// compaction) and the unit's histogram (global atomics, no return).
+// compaction) and the unit's histogram (global atomics, no return).  Totals
+// of 0, a third of the keys, are counted per wave.  (Measured on MI355X:
+// tables replicated per LDS bank with one persistent workgroup per compute
+// unit, and 4-bit conflict-free tables, were both slower; the kernel is
+// bound by its ~32 VALU + 16 LDS instructions per key beside 18 HBM bytes.)
 template <int BS>
 __global__ __launch_bounds__(256) void vote_kernel(const uint8_t* __restrict__ buckets,
                                                    const uint8_t* __restrict__ votes, int N,
@@ -343,6 +347,7 @@ __global__ __launch_bounds__(256) void vote_kernel(const uint8_t* __restrict__ b
 #pragma unroll 4
   for (int k = 0; k < kChunk / 256; ++k) {
     const int i = i0 + k * 256 + t;
+    bool zero = false;
     if (i < N) {
       uint32_t w[BS / 4];
       if constexpr (BS == 16) {
@@ -356,8 +361,12 @@ __global__ __launch_bounds__(256) void vote_kernel(const uint8_t* __restrict__ b
 #pragma unroll
       for (int j = 0; j < BS; ++j) s += vt[j * 256 + ((w[j >> 2] >> (8 * (j & 3))) & 255u)];
       sc[i] = static_cast<uint16_t>(s);
-      atomicAdd(&hist[s], 1u);
+      if (s != 0) atomicAdd(&hist[s], 1u);
+      zero = s == 0;
     }
+    // totals of 0, a third of the keys, are counted per wave
+    const unsigned long long z = __ballot(i < N && zero);
+    if ((t & (kWave - 1)) == 0 && z) atomicAdd(&hist[0], static_cast<uint32_t>(__popcll(z)));
   }
   __syncthreads();
   suffix_counts(hist, nbins, chist + (static_cast<size_t>(u) * nchunk + c) * kMaxBins);
