@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const typename Elem<DT>::T*
 // ------------------------------------------------------------- decode
 
 // Grid (d/8 subspaces, U), 1024 threads.  Every workgroup rotates the
-// unit's group-mean query (fp64, Hadamard levels through LDS), then ranks the
+// unit's group-mean query (fp64, in wave 0: Hadamard levels by shuffles,
+// the top level of d = 128 within the lane), then ranks the
 // 256 sign patterns of its subspace by <q~_b, c_p> (ties to the lower
 // pattern): four threads per pattern each count the better patterns among
 // an interleaved quarter, and two shuffles add the counts.  The top rho
@@ -260,45 +261,66 @@ __global__ __launch_bounds__(1024) void query_kernel(const typename Elem<DT>::T*
   const int b = u / Hkv;
   const int h = u - b * Hkv;
   const int t = threadIdx.x;
-  __shared__ double y[128];
-  __shared__ double red[16];
+  __shared__ double y[128];  // q~ (scaled)
   __shared__ double sc[256];
-  double qb = 0.0;
-  if (t < d) {
-    const size_t base = (static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G) * d + t;
-    for (int g = 0; g < G; ++g) qb += static_cast<double>(E::ld(q, base + static_cast<size_t>(g) * d));
-    qb /= static_cast<double>(G);
-  }
-  const double nq2 = block_sum<1024>(qb * qb, red);
-  if (t < d) y[t] = sign_negative(sg, t) ? -qb : qb;
-  __syncthreads();
-  for (int hh = 1; hh < d; hh <<= 1) {
-    if (t < d / 2) {
-      const int i = (t / hh) * 2 * hh + (t % hh);
-      const double a = y[i], c = y[i + hh];
-      y[i] = a + c;
-      y[i + hh] = a - c;
+  if (t < kWave) {
+    // wave 0: group mean, norm and Hadamard levels in registers and
+    // shuffles; lane l holds coordinates l and l + 64 (d = 128)
+    const size_t base = (static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G) * d;
+    double x[2] = {0.0, 0.0};
+    const int nv = d / kWave;  // 1 or 2 coordinates per lane
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if (v < nv) {
+        const int c = t + v * kWave;
+        double a = 0.0;
+        for (int g = 0; g < G; ++g) a += static_cast<double>(E::ld(q, base + static_cast<size_t>(g) * d + c));
+        x[v] = a / static_cast<double>(G);
+      }
     }
-    __syncthreads();
-  }
-  const double qn = sqrt(nq2);
-  const double scale = qn * sqrt(static_cast<double>(d));
-  if (sb == 0) {
-    if (t < d) qt_out[static_cast<size_t>(u) * d + t] = scale > 0.0 ? y[t] / scale : 0.0;
-    if (t == 0) {
+    const double qn = sqrt(wave_sum(x[0] * x[0] + x[1] * x[1]));
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      if (v < nv && sign_negative(sg, t + v * kWave)) x[v] = -x[v];
+    // (a, b) -> (a + b, a - b) on every bit level of the coordinate index
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const double pv = __shfl_xor(x[v], o, kWave);
+        x[v] = (t & o) ? pv - x[v] : x[v] + pv;
+      }
+    }
+    if (nv == 2) {
+      const double a = x[0], c = x[1];
+      x[0] = a + c;
+      x[1] = a - c;
+    }
+    const double scale = qn * sqrt(static_cast<double>(d));
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if (v < nv) {
+        const double qt = scale > 0.0 ? x[v] / scale : 0.0;
+        y[t + v * kWave] = qt;
+        if (sb == 0) qt_out[static_cast<size_t>(u) * d + t + v * kWave] = qt;
+      }
+    }
+    if (sb == 0 && t == 0) {
       qn_out[u] = qn;
       lcnt[u] = 0u;
     }
-    for (int i = t; i < kMaxBins; i += blockDim.x) tot[static_cast<size_t>(u) * kMaxBins + i] = 0u;
   }
+  if (sb == 0)
+    for (int i = t; i < kMaxBins; i += blockDim.x) tot[static_cast<size_t>(u) * kMaxBins + i] = 0u;
   for (int i = sb * blockDim.x + t; i < kSelBins; i += gridDim.x * blockDim.x)
     ehtot[static_cast<size_t>(u) * kSelBins + i] = 0u;
+  __syncthreads();
   const int p = t >> 2;
   const int part = t & 3;
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const double v = scale > 0.0 ? y[sb * 8 + i] / scale : 0.0;
+    const double v = y[sb * 8 + i];
     s += ((p >> i) & 1) ? -v : v;
   }
   if (part == 0) sc[p] = s;
@@ -805,7 +827,11 @@ __global__ __launch_bounds__(256) void cross_kernel(const float* __restrict__ es
   if (t == 0) gtb[static_cast<size_t>(u) * nsb + blk] = static_cast<int32_t>(g);
 }
 
-// Grid U, 1024 threads.
+// Grid U, 1024 threads.  Members of the crossing bin up to kRankCap are
+// ranked directly in LDS; more fall back to value-range refinement and a
+// radix select of the last tied index over the member list in memory.
+constexpr int kRankCap = kSelBins / 2;
+
 __global__ __launch_bounds__(1024) void thresh_kernel(int C, int n_sel, int nsb,
                                                       const uint32_t* __restrict__ rng,
                                                       const uint32_t* __restrict__ ehtot,
@@ -835,6 +861,43 @@ __global__ __launch_bounds__(1024) void thresh_kernel(int C, int n_sel, int nsb,
     const int m = static_cast<int>(min(lcnt[u], static_cast<uint32_t>(C)));
     const float* lv = lval + static_cast<size_t>(u) * C;
     const int32_t* li = lidx + static_cast<size_t>(u) * C;
+    if (m <= kRankCap) {
+      // few members (the usual case): copy them to LDS (into the histogram's
+      // space) and rank them by (estimate descending, index ascending); the
+      // member of rank rem - 1 is the last one taken, so it gives T and the
+      // last tied index at once
+      float* mv = reinterpret_cast<float*>(hist);
+      int32_t* mi = reinterpret_cast<int32_t*>(hist) + kRankCap;
+      for (int i = t; i < m; i += NT) {
+        mv[i] = lv[i];
+        mi[i] = li[i];
+      }
+      __syncthreads();
+      for (int i = t; i < m; i += NT) {
+        const float v = mv[i];
+        const int k = mi[i];
+        uint32_t rank = 0;
+        for (int j = 0; j < m; ++j) {
+          const float o = mv[j];
+          rank += (o > v || (o == v && mi[j] < k)) ? 1u : 0u;
+        }
+        if (rank == rem - 1) {
+          s_bin = k;
+          fbuf[0] = v;
+        }
+      }
+      __syncthreads();
+      T = fbuf[0];
+      k_tie = s_bin;
+      for (int i = t; i < nsb; i += NT) cntb[i] = 0u;
+      __syncthreads();
+      for (int i = t; i < m; i += NT) {
+        const float x = mv[i];
+        const int k = mi[i];
+        if ((x > T || (x == T && k <= k_tie)) && k >= 0 && k < C) atomicAdd(&cntb[k / kSelBlock], 1u);
+      }
+      __syncthreads();
+    } else {
     float nlo = INFINITY, nhi = -INFINITY;
     for (int i = t; i < m; i += NT) {
       const float x = lv[i];
@@ -886,6 +949,7 @@ __global__ __launch_bounds__(1024) void thresh_kernel(int C, int n_sel, int nsb,
       if ((x > T || (x == T && k <= k_tie)) && k >= 0 && k < C) atomicAdd(&cntb[k / kSelBlock], 1u);
     }
     __syncthreads();
+    }
   }
   // output offsets of the blocks (one block per thread)
   const int b = t;

@@ -155,7 +155,7 @@ def check_step(tr, res, enc, u, info, what):
     return check_retrieved(tr["retrieved"][u], res, n_sel, first, what)
 
 
-def run_case(wl, params, kv_tier="hbm", zero_keys=False, zero_query=False, dup_keys=False):
+def run_case(wl, params, kv_tier="hbm", zero_keys=False, zero_query=False, dup_keys=0):
     import torch
     cfg = wl.cfg
     dt, B, Hq, Hkv = wl.dtype, cfg["B"], cfg["Hq"], cfg["Hkv"]
@@ -179,7 +179,7 @@ def run_case(wl, params, kv_tier="hbm", zero_keys=False, zero_query=False, dup_k
         for b in range(B):
             for h in range(Hkv):
                 qb = q0[b, h * G_:(h + 1) * G_].mean(axis=0)
-                K[b, h, 100::37] = W.store((3.0 * qb / np.linalg.norm(qb)).astype(np.float32), dt)
+                K[b, h, 100::dup_keys] = W.store((3.0 * qb / np.linalg.norm(qb)).astype(np.float32), dt)
     idx = gpu_index(K, V, signs, Hq, dt, kv_tier=kv_tier, **params)
     info = idx.info
     say(f"  N={info['n_retrieval']} C={info['n_cand']} n_sel={info['n_sel']} "
@@ -260,12 +260,17 @@ def test_retrieval_zero_keys_and_query():
     run_case(wl, dict(rho=16, cand_frac=0.05, k_ret=40, n_sink=4, n_local=16), zero_query=True)
 
 
-def test_retrieval_tied_estimates():
-    """The k_ret-th estimate is shared by many equal keys: the retrieved
-    copies are the ones at the lowest positions."""
+@pytest.mark.parametrize("stride", [37, 2])
+def test_retrieval_tied_estimates(stride):
+    """The k_ret-th estimate is shared by many equal keys (a key copied to
+    every stride-th position): the retrieved copies are the ones at the
+    lowest positions.  With stride 2 the top-k's crossing bin holds more
+    members than it ranks in LDS (the refinement path)."""
     wl = W.generate("gqa_32k_bf16", B=1, Hkv=2, Hq=8, T=9001, steps=1)
-    say("[retrieval tied estimates]")
-    run_case(wl, dict(rho=16, cand_frac=0.05, k_ret=64, n_sink=16, n_local=128), dup_keys=True)
+    say(f"[retrieval tied estimates, stride {stride}]")
+    params = dict(rho=16, cand_frac=0.05 if stride > 2 else 0.9, k_ret=64, n_sink=16,
+                  n_local=128)
+    run_case(wl, params, dup_keys=stride)
 
 
 def test_retrieval_host_tier_matches_hbm():
