@@ -99,21 +99,25 @@ def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg, factors_only=False):
     return route + attend + out, attend
 
 
-def kernel_sha():
+ATTEND_SOURCES = ("attend.hip", "common.h")
+RETRIEVAL_SOURCES = ("retrieval.hip", "retrieval.h", "common.h")
+
+
+def kernel_sha(files=ATTEND_SOURCES):
     h = hashlib.sha256()
-    for f in ("attend.hip", "common.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "routed_sparse_kv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
+def committed_traffic(workload, kernel="attend", files=ATTEND_SOURCES):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha") != kernel_sha():
+    if rec.get("kernel_sha") != kernel_sha(files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -360,7 +364,8 @@ def retrieval_bench(args):
                    "head_dim": cfg["d"], **params, "n_cand": info["n_cand"],
                    "n_attend": info["n_attend"], "replicas": R, "kv_tier": args.kv_tier},
         "roofline": {"bound": "hbm", "achieved": vote_gbps, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": vote_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": vote_gbps / PEAK_HBM_GBPS,
+                     "traffic": committed_traffic(args.workload, "vote", RETRIEVAL_SOURCES),
                      "kernel": "vote_kernel",
                      "algorithmic_bytes_per_launch": per_kernel["vote"],
                      "mean_launch_ms": kern["vote_ms"]},
