@@ -6,7 +6,9 @@ CPU-baseline leg use it.  It shares no code, constants or helpers with the
 HIP library; the two are compared on the same seeded inputs.
 
 The submodule ``paris`` is the oracle of the token-retrieval router
-(ParisKV page); its readings and pinning status are in its own docstring.
+(ParisKV page) and ``qevict`` that of the window-routed three-tier cache
+(QEvict page); their readings and pinning status are in their own
+docstrings.
 
 Every function of the SEKV part follows a passage of the SEKV summary ("SEKV - KV Cache
 Adattiva alla Risoluzione con Memoria Semantica Gerarchica", gist.science,
@@ -33,3 +35,4 @@ Pinning status (what fixes each function independently of itself):
 """
 from .sekv import *  # noqa: F401,F403
 from . import paris  # noqa: F401  (ParisKV-style token retrieval, its own page)
+from . import qevict  # noqa: F401  (QEvict-form window routing, its own page)
