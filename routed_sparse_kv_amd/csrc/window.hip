@@ -1,0 +1,867 @@
+// Window-routed three-tier cache (QEvict summary, "Metodologia: QEvict"):
+// decode kernels.
+//
+//   attend_mfma_kernel  bf16 caches.  Each wave walks a contiguous range of
+//       the unit's attended windows (full-precision ones first, then INT2
+//       ones; ranges balanced by a per-window cost) with an online softmax
+//       per query head.  Full windows: QK and PV products on 16x16x32 bf16
+//       MFMAs straight from the K16 / V32 tiles.  INT2 windows: the codes
+//       are widened to bf16 in registers (two byte permutes per code pair)
+//       and fed to the same MFMAs; the fp32 scales and minima are applied
+//       around the products:
+//         <q, k_r> = sum_grp scale_r,grp <q_grp, code_r,grp> + min_r,grp sum(q_grp)
+//         sum_r p_r v_r = sum_r (p_r scale_r,grp) code_r + sum_r p_r min_r,grp
+//       which is the dequantised arithmetic up to association.  fp32
+//       factors enter an MFMA as a bf16 hi + lo pair.  The four waves of a
+//       workgroup merge in LDS and write one partial.
+//   attend_valu_kernel  fp32 caches: a block-cooperative fp32 version that
+//       dequantises INT2 rows exactly (mn + code * scale, two roundings).
+//   merge_kernel        log-sum-exp merge of a unit's partials; on routing
+//       steps it also keeps each head's maximum and denominator.
+//   route_kernel        routing event: window masses from the per-window
+//       softmax statistics, cumulative scores, ranking of the windows not
+//       evicted (bitonic sort in LDS), new tiers, the next attended list and
+//       the lists of ledger writes and promotions.
+//   transition_kernel   first demotions quantise a window into the ledger;
+//       promotions write the dequantised values back into the full store.
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "window.h"
+
+namespace rskv {
+namespace win {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCostFull = 4;  // work cost of a full-precision window
+constexpr int kCostQuant = 1; // and of an INT2 window
+constexpr int kTargetWaves = 8192;
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// fp32 x as bf16 hi + lo (hi + lo equals x to ~16 significant bits).
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 hb = static_cast<__bf16>(x[e]);
+    hi[e] = hb;
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hb));
+  }
+}
+
+// Eight 2-bit codes (one byte each in m0 = codes 0..3, m1 = codes 4..7) as
+// bf16 0.0 .. 3.0.  A byte permute builds the selector [c, c + 4] per code
+// and a second one looks the two bytes of bf16(c) up in the tables
+// lo = {00, 80, 00, 40}, hi = {00, 3f, 40, 40}.
+__device__ __forceinline__ uint32_t widen2(uint32_t m, uint32_t sel) {
+  const uint32_t s = __builtin_amdgcn_perm(m | 0x04040404u, m, sel);
+  return __builtin_amdgcn_perm(0x40403f00u, 0x40008000u, s);
+}
+__device__ __forceinline__ bf16x8 decode8(uint32_t word, int half) {
+  const uint32_t m0 = (word >> (4 * half)) & 0x03030303u;
+  const uint32_t m1 = (word >> (4 * half + 2)) & 0x03030303u;
+  const u32x4 v{widen2(m0, 0x05010400u), widen2(m0, 0x07030602u), widen2(m1, 0x05010400u),
+                widen2(m1, 0x07030602u)};
+  return as8(v);
+}
+
+// Dequantised INT2 value mn + code * scale: the product is rounded to fp32
+// before the sum (contraction into a fused multiply-add is switched off).
+__device__ __forceinline__ float dequant(float code, float scale, float mn) {
+#pragma clang fp contract(off)
+  const float p = code * scale;
+  return mn + p;
+}
+
+// First attended window of range v of nv (ranges balanced by cost).
+__device__ __forceinline__ int range_start(int v, int nv, int nf, int nit) {
+  const long long fullc = static_cast<long long>(kCostFull) * nf;
+  const long long tot = fullc + static_cast<long long>(kCostQuant) * (nit - nf);
+  const long long b = tot * v / nv;
+  if (b <= fullc) return static_cast<int>((b + kCostFull - 1) / kCostFull);
+  return nf + static_cast<int>((b - fullc + kCostQuant - 1) / kCostQuant);
+}
+
+// ---------------------------------------------------------------- build
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void build_kernel(const typename Elem<DT>::T* __restrict__ K,
+                                                    const typename Elem<DT>::T* __restrict__ V,
+                                                    int T, int rows_pad,
+                                                    typename Elem<DT>::T* __restrict__ kf,
+                                                    typename Elem<DT>::T* __restrict__ vf) {
+  typedef typename Elem<DT>::T E;
+  const int u = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;  // (row, 8-column chunk)
+  if (e >= rows_pad * (D / 8)) return;
+  const int r = e / (D / 8);
+  const int c0 = (e - r * (D / 8)) * 8;
+  const size_t src = (static_cast<size_t>(u) * T + r) * D + c0;
+  const size_t dst = static_cast<size_t>(u) * rows_pad * D;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const E kx = r < T ? K[src + j] : E(0);
+    const E vx = r < T ? V[src + j] : E(0);
+    kf[dst + k16_off(r, c0 + j, D)] = kx;
+    vf[dst + v32_off(r, c0 + j, D)] = vx;
+  }
+}
+
+// --------------------------------------------------------- attention (MFMA)
+
+template <int D, bool MASS>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kf,
+    const uint16_t* __restrict__ vf, const uint32_t* __restrict__ codes,
+    const float* __restrict__ qsc, const int32_t* __restrict__ items, int nW, int T, int Hq,
+    int Hkv, int G, int nf, int nit, int nsplit, float* __restrict__ part,
+    float2* __restrict__ wstat) {
+  constexpr int NG = D / kGroup;
+  constexpr int KB = D / 32;   // 32-column blocks of the QK product
+  constexpr int CB = D / 16;   // 16-column blocks of the output
+  constexpr int SQ = 256 * NG; // scale floats per window
+  const int u = blockIdx.y;
+  const int b = u / Hkv;
+  const int h = u - b * Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int v = blockIdx.x * 4 + wave;
+  const int k0 = range_start(v, nsplit * 4, nf, nit);
+  const int k1 = range_start(v + 1, nsplit * 4, nf, nit);
+
+  // query operand (head n, columns 32 kb + 8 g + 0..7) and its group sums
+  const bool hv = n < G;
+  bf16x8 qb[KB];
+  float qsum[NG];
+#pragma unroll
+  for (int x = 0; x < NG; ++x) qsum[x] = 0.f;
+  {
+    const uint16_t* qp = q + (static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G + (hv ? n : 0)) * D + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qp + kb * 32);
+      if (!hv) x = u32x4{0u, 0u, 0u, 0u};
+      qb[kb] = as8(x);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s += __uint_as_float(x[e] << 16) + __uint_as_float(x[e] & 0xffff0000u);
+      qsum[kb / 2] += s;
+    }
+#pragma unroll
+    for (int x = 0; x < NG; ++x) {
+      qsum[x] += __shfl_xor(qsum[x], 16, kWave);
+      qsum[x] += __shfl_xor(qsum[x], 32, kWave);
+    }
+  }
+  const float sl = 1.0f / sqrtf(static_cast<float>(D));
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float amn[NG];
+#pragma unroll
+  for (int x = 0; x < NG; ++x) amn[x] = 0.f;
+
+  for (int k = k0; k < k1; ++k) {
+    // the routing kernel only lists windows < nW; the clamp keeps a bad entry in bounds
+    const int w = min(max(items[static_cast<size_t>(u) * nW + k], 0), nW - 1);
+    const int nvalid = min(kRows, T - w * kRows);
+    const size_t wb = static_cast<size_t>(u) * nW + w;
+    const bool full = k < nf;
+    float s[4][4];
+    u32x4 vw[NG];
+    const float* qv = qsc + wb * SQ + 128 * NG;
+    if (full) {
+      const uint16_t* kt = kf + wb * kRows * D + lane * 8;
+      u32x4 ka[4][KB];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          ka[rb][kb] = *reinterpret_cast<const u32x4*>(kt + (rb * KB + kb) * 512);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 c{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) c = mma(as8(ka[rb][kb]), qb[kb], c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[rb][i] = c[i] * sl;
+      }
+    } else {
+      const uint32_t* cw = codes + wb * (8 * D);
+      u32x4 kw[NG];
+#pragma unroll
+      for (int p = 0; p < NG; ++p) {
+        kw[p] = *reinterpret_cast<const u32x4*>(cw + (p * 64 + lane) * 4);
+        vw[p] = *reinterpret_cast<const u32x4*>(cw + 4 * D + (p * 64 + lane) * 4);
+      }
+      const float* qk = qsc + wb * SQ;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        // rows 16 rb + 4 g + i: [i][grp][scale, min]
+        float sc[4 * NG * 2];
+#pragma unroll
+        for (int x = 0; x < 2 * NG; ++x) {
+          const float4 t4 = *reinterpret_cast<const float4*>(qk + (rb * 16 + 4 * g) * 2 * NG + 4 * x);
+          sc[4 * x] = t4.x;
+          sc[4 * x + 1] = t4.y;
+          sc[4 * x + 2] = t4.z;
+          sc[4 * x + 3] = t4.w;
+        }
+        f32x4 cg[NG];
+#pragma unroll
+        for (int x = 0; x < NG; ++x) cg[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int o = rb * KB + kb;
+          const int t = o >> 1;
+          const bf16x8 a = decode8(kw[t >> 2][t & 3], o & 1);
+          cg[kb / 2] = mma(a, qb[kb], cg[kb / 2]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float z = 0.f;
+#pragma unroll
+          for (int x = 0; x < NG; ++x)
+            z += sc[(i * NG + x) * 2] * cg[x][i] + sc[(i * NG + x) * 2 + 1] * qsum[x];
+          s[rb][i] = z * sl;
+        }
+      }
+    }
+    // rows past the context
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (rb * 16 + 4 * g + i >= nvalid) s[rb][i] = -INFINITY;
+
+    // online softmax for head n (rows spread over the 4 lane groups)
+    float cm = s[0][0];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[rb][i]);
+    cm = fmaxf(cm, __shfl_xor(cm, 16, kWave));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, kWave));
+    if (MASS) {
+      float ws = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws += __expf(s[rb][i] - cm);
+      ws += __shfl_xor(ws, 16, kWave);
+      ws += __shfl_xor(ws, 32, kWave);
+      if (g == 0 && hv) wstat[(static_cast<size_t>(u) * nW + k) * G + n] = make_float2(cm, ws);
+    }
+    const float mnew = fmaxf(m, cm);
+    const float fac = __expf(m - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[rb][i] = __expf(s[rb][i] - mnew);
+        ps += s[rb][i];
+      }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * fac + ps;
+    m = mnew;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] *= fac;
+#pragma unroll
+    for (int x = 0; x < NG; ++x) amn[x] *= fac;
+
+    // PV: A = values (column 16 cb + n, rows v32_row(g, .)), B = p (head n)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float pp[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pp[e] = s[2 * rb][e];
+        pp[4 + e] = s[2 * rb + 1][e];
+      }
+      if (full) {
+        bf16x8 hi, lo;
+        split8(pp, hi, lo);
+        const uint16_t* vt = vf + wb * kRows * D + lane * 8;
+        u32x4 va[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          va[cb] = *reinterpret_cast<const u32x4*>(vt + (rb * CB + cb) * 512);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          acc[cb] = mma(as8(va[cb]), hi, acc[cb]);
+          acc[cb] = mma(as8(va[cb]), lo, acc[cb]);
+        }
+      } else {
+        // rows v32_row(g, e) of block rb: [e][grp][scale, min]
+        float sc[8 * NG * 2];
+#pragma unroll
+        for (int x = 0; x < 4 * NG; ++x) {
+          const float4 t4 = *reinterpret_cast<const float4*>(qv + (rb * 4 + g) * 16 * NG + 4 * x);
+          sc[4 * x] = t4.x;
+          sc[4 * x + 1] = t4.y;
+          sc[4 * x + 2] = t4.z;
+          sc[4 * x + 3] = t4.w;
+        }
+        bf16x8 hi[NG], lo[NG];
+#pragma unroll
+        for (int x = 0; x < NG; ++x) {
+          float pw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pw[e] = pp[e] * sc[(e * NG + x) * 2];
+            amn[x] += pp[e] * sc[(e * NG + x) * 2 + 1];
+          }
+          split8(pw, hi[x], lo[x]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int o = rb * CB + cb;
+          const int t = o >> 1;
+          const bf16x8 a = decode8(vw[t >> 2][t & 3], o & 1);
+          acc[cb] = mma(a, hi[cb >> 2], acc[cb]);
+          acc[cb] = mma(a, lo[cb >> 2], acc[cb]);
+        }
+      }
+    }
+  }
+  // minima terms of the INT2 values, summed over the lane groups' rows
+#pragma unroll
+  for (int x = 0; x < NG; ++x) {
+    amn[x] += __shfl_xor(amn[x], 16, kWave);
+    amn[x] += __shfl_xor(amn[x], 32, kWave);
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[cb][i] += amn[cb >> 2];
+
+  // merge the four waves
+  __shared__ float sm[4][kMaxG], sl4[4][kMaxG];
+  __shared__ float so[4][kMaxG][D];
+  if (g == 0) {
+    sm[wave][n] = m;
+    sl4[wave][n] = l;
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) so[wave][n][cb * 16 + 4 * g + i] = acc[cb][i];
+  __syncthreads();
+  float* pb = part + (static_cast<size_t>(u) * nsplit + blockIdx.x) * G * (D + 2);
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D;
+    const int c = e - hh * D;
+    const float M = fmaxf(fmaxf(sm[0][hh], sm[1][hh]), fmaxf(sm[2][hh], sm[3][hh]));
+    float o = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float f = sm[x][hh] == -INFINITY ? 0.f : __expf(sm[x][hh] - M);
+        o += f * so[x][hh][c];
+        L += f * sl4[x][hh];
+      }
+    }
+    pb[hh * (D + 2) + c] = o;
+    if (c == 0) {
+      pb[hh * (D + 2) + D] = M;
+      pb[hh * (D + 2) + D + 1] = L;
+    }
+  }
+}
+
+// --------------------------------------------------------- attention (VALU)
+
+template <int DT, int D, bool MASS>
+__global__ __launch_bounds__(256) void attend_valu_kernel(
+    const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ kf,
+    const typename Elem<DT>::T* __restrict__ vf, const uint32_t* __restrict__ codes,
+    const float* __restrict__ qsc, const int32_t* __restrict__ items, int nW, int T, int Hq,
+    int Hkv, int G, int nf, int nit, int nsplit, float* __restrict__ part,
+    float2* __restrict__ wstat) {
+  typedef Elem<DT> E;
+  constexpr int NG = D / kGroup;
+  constexpr int SQ = 256 * NG;
+  constexpr int NO = (kMaxG * D + 255) / 256;  // outputs per thread
+  const int u = blockIdx.y;
+  const int b = u / Hkv;
+  const int h = u - b * Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int k0 = range_start(blockIdx.x, nsplit, nf, nit);
+  const int k1 = range_start(blockIdx.x + 1, nsplit, nf, nit);
+  __shared__ float qs[kMaxG][D];
+  __shared__ float xs[kRows][D + 1];
+  __shared__ float pl[kMaxG][kRows];
+  __shared__ float mrun[kMaxG], lrun[kMaxG], fac[kMaxG];
+  const size_t qbase = (static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G) * D;
+  for (int e = tid; e < G * D; e += 256) qs[e / D][e % D] = E::ld(q, qbase + e);
+  if (tid < kMaxG) {
+    mrun[tid] = -INFINITY;
+    lrun[tid] = 0.f;
+  }
+  float acc[NO];
+#pragma unroll
+  for (int j = 0; j < NO; ++j) acc[j] = 0.f;
+  const float sl = 1.0f / sqrtf(static_cast<float>(D));
+  const size_t ub = static_cast<size_t>(u) * nW * kRows * D;
+
+  // rows of window w, side 0 (K) or 1 (V), as fp32 into xs
+  auto stage = [&](int w, bool full, int side) {
+    const size_t wb = static_cast<size_t>(u) * nW + w;
+    const uint32_t* cw = codes + wb * (8 * D);
+    const float* qw = qsc + wb * SQ;
+    for (int e = tid; e < kRows * D; e += 256) {
+      const int r = e / D;
+      const int c = e - r * D;
+      float x;
+      if (full) {
+        const size_t o = ub + (side == 0 ? k16_off(w * kRows + r, c, D) : v32_off(w * kRows + r, c, D));
+        x = E::ld(side == 0 ? kf : vf, o);
+      } else {
+        int bit;
+        const int wd = code_word(side, r, c, D, &bit);
+        const float code = static_cast<float>((cw[wd] >> bit) & 3u);
+        const int grp = c / kGroup;
+        const float sc = qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)];
+        const float mn = qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)];
+        x = dequant(code, sc, mn);
+      }
+      xs[r][c] = x;
+    }
+  };
+
+  for (int k = k0; k < k1; ++k) {
+    const int w = min(max(items[static_cast<size_t>(u) * nW + k], 0), nW - 1);
+    const int nvalid = min(kRows, T - w * kRows);
+    const bool full = k < nf;
+    __syncthreads();
+    stage(w, full, 0);
+    __syncthreads();
+    for (int e = tid; e < G * kRows; e += 256) {
+      const int hh = e / kRows;
+      const int r = e - hh * kRows;
+      float a = 0.f;
+      for (int c = 0; c < D; ++c) a += qs[hh][c] * xs[r][c];
+      pl[hh][r] = r < nvalid ? a * sl : -INFINITY;
+    }
+    __syncthreads();
+    for (int hh = wave; hh < G; hh += 4) {
+      const float s = pl[hh][lane];
+      const float cm = wave_max(s);
+      if (MASS) {
+        const float ws = wave_sum(expf(s - cm));
+        if (lane == 0) wstat[(static_cast<size_t>(u) * nW + k) * G + hh] = make_float2(cm, ws);
+      }
+      const float mo = mrun[hh];
+      const float mnew = fmaxf(mo, cm);
+      const float p = expf(s - mnew);
+      const float ps = wave_sum(p);
+      pl[hh][lane] = p;
+      if (lane == 0) {
+        const float f = expf(mo - mnew);
+        fac[hh] = f;
+        lrun[hh] = lrun[hh] * f + ps;
+        mrun[hh] = mnew;
+      }
+    }
+    stage(w, full, 1);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int e = tid + 256 * j;
+      if (e < G * D) {
+        const int hh = e / D;
+        const int c = e - hh * D;
+        float a = acc[j] * fac[hh];
+        for (int r = 0; r < kRows; ++r) a += pl[hh][r] * xs[r][c];
+        acc[j] = a;
+      }
+    }
+  }
+  __syncthreads();
+  float* pb = part + (static_cast<size_t>(u) * nsplit + blockIdx.x) * G * (D + 2);
+#pragma unroll
+  for (int j = 0; j < NO; ++j) {
+    const int e = tid + 256 * j;
+    if (e < G * D) {
+      const int hh = e / D;
+      const int c = e - hh * D;
+      pb[hh * (D + 2) + c] = acc[j];
+      if (c == 0) {
+        pb[hh * (D + 2) + D] = mrun[hh];
+        pb[hh * (D + 2) + D + 1] = lrun[hh];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- merge
+
+// Grid (G, U), D threads: out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s.
+template <int D, bool MASS>
+__global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part, int nsplit, int G,
+                                                  int Hq, int Hkv, float* __restrict__ out,
+                                                  float2* __restrict__ hstat) {
+  constexpr int NW = D / kWave;
+  const int g = blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / Hkv;
+  const int h = u - b * Hkv;
+  const int c = threadIdx.x;
+  __shared__ float buf[NW];
+  const size_t stride = static_cast<size_t>(G) * (D + 2);
+  const float* p = part + static_cast<size_t>(u) * nsplit * stride + static_cast<size_t>(g) * (D + 2);
+  float mx = -INFINITY;
+  for (int s = c; s < nsplit; s += D) mx = fmaxf(mx, p[s * stride + D]);
+  mx = wave_max(mx);
+  if ((c & 63) == 0) buf[c >> 6] = mx;
+  __syncthreads();
+  float M = buf[0];
+#pragma unroll
+  for (int x = 1; x < NW; ++x) M = fmaxf(M, buf[x]);
+  __syncthreads();
+  float dl = 0.f;
+  for (int s = c; s < nsplit; s += D) {
+    const float ms = p[s * stride + D];
+    if (ms != -INFINITY) dl += expf(ms - M) * p[s * stride + D + 1];
+  }
+  dl = wave_sum(dl);
+  if ((c & 63) == 0) buf[c >> 6] = dl;
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) den += buf[x];
+  float num = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = p[s * stride + D];
+    if (ms != -INFINITY) num += expf(ms - M) * p[s * stride + c];
+  }
+  out[(static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G + g) * D + c] = num / den;
+  if (MASS && c == 0) hstat[static_cast<size_t>(u) * G + g] = make_float2(M, den);
+}
+
+// ---------------------------------------------------------------- routing
+
+// One workgroup per unit.  Sort keys: ((~bits(score)) >> 1) with the low
+// 14 bits replaced by the window, ascending = score descending, ties to the
+// lower window (scores are >= 0, so their bit patterns order like them);
+// evicted windows and padding sort last.
+template <int NP>
+__global__ __launch_bounds__(1024) void route_kernel(
+    const float2* __restrict__ wstat, const float2* __restrict__ hstat, int G, int nW, int nit,
+    int n_full, int n_quant, int32_t* __restrict__ items, int8_t* __restrict__ tier,
+    double* __restrict__ score, double* __restrict__ mass, const uint8_t* __restrict__ has_code,
+    int32_t* __restrict__ trans, int32_t* __restrict__ ntrans) {
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ unsigned long long key[NP];
+  __shared__ int cnt[2];
+  const size_t ub = static_cast<size_t>(u) * nW;
+  double* mw = reinterpret_cast<double*>(key);
+  for (int w = tid; w < NP; w += 1024) mw[w] = 0.0;
+  if (tid < 2) cnt[tid] = 0;
+  __syncthreads();
+  // masses of the attended windows
+  for (int k = tid; k < nit; k += 1024) {
+    const int w = items[ub + k];
+    double ms = 0.0;
+    for (int hh = 0; hh < G; ++hh) {
+      const float2 ws = wstat[(ub + k) * G + hh];
+      const float2 hs = hstat[static_cast<size_t>(u) * G + hh];
+      ms += static_cast<double>(ws.y) * exp(static_cast<double>(ws.x) - static_cast<double>(hs.x)) /
+            static_cast<double>(hs.y);
+    }
+    mw[w] = ms;
+  }
+  __syncthreads();
+  for (int w = tid; w < NP; w += 1024) {
+    unsigned long long kk = ~0ull;
+    if (w < nW) {
+      const double ms = mw[w];
+      mass[ub + w] = ms;
+      const double sc = score[ub + w] + ms;
+      score[ub + w] = sc;
+      if (tier[ub + w] != RSKV_TIER_EVICTED) {
+        const unsigned long long bits = static_cast<unsigned long long>(__double_as_longlong(sc));
+        kk = (((~bits) >> 1) & ~0x3fffull) | static_cast<unsigned long long>(w);
+      }
+    }
+    key[w] = kk;
+  }
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int kk = 2; kk <= NP; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < NP; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = key[i], c = key[ixj];
+          const bool up = (i & kk) == 0;
+          if ((a > c) == up) {
+            key[i] = c;
+            key[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int pos = tid; pos < nW; pos += 1024) {
+    const unsigned long long kk = key[pos];
+    if (kk == ~0ull) continue;
+    const int w = static_cast<int>(kk & 0x3fffull);
+    const int old = tier[ub + w];
+    const int nt = pos < n_full ? RSKV_TIER_FULL
+                   : pos < n_full + n_quant ? RSKV_TIER_INT2 : RSKV_TIER_EVICTED;
+    tier[ub + w] = static_cast<int8_t>(nt);
+    if (nt != RSKV_TIER_EVICTED) items[ub + pos] = w;
+    if (nt == RSKV_TIER_INT2 && old == RSKV_TIER_FULL && !has_code[ub + w])
+      trans[(static_cast<size_t>(u) * 2) * nW + atomicAdd(&cnt[0], 1)] = w;
+    if (nt == RSKV_TIER_FULL && old == RSKV_TIER_INT2)
+      trans[(static_cast<size_t>(u) * 2 + 1) * nW + atomicAdd(&cnt[1], 1)] = w;
+  }
+  __syncthreads();
+  if (tid < 2) ntrans[u * 2 + tid] = cnt[tid];
+}
+
+// ---------------------------------------------------------- transitions
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void transition_kernel(
+    typename Elem<DT>::T* __restrict__ kf, typename Elem<DT>::T* __restrict__ vf,
+    uint32_t* __restrict__ codes, float* __restrict__ qsc, uint8_t* __restrict__ has_code,
+    const int32_t* __restrict__ trans, const int32_t* __restrict__ ntrans, int nW) {
+  typedef Elem<DT> E;
+  constexpr int NG = D / kGroup;
+  constexpr int SQ = 256 * NG;
+  constexpr int WPS = 64 * (D / 16);  // code words per side
+  const int u = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nq = ntrans[u * 2];
+  const int np = ntrans[u * 2 + 1];
+  __shared__ uint8_t cb[2][kRows][D];
+  const size_t ub = static_cast<size_t>(u) * nW * kRows * D;
+  for (int idx = blockIdx.x; idx < nq + np; idx += gridDim.x) {
+    const bool quant = idx < nq;
+    const int w = quant ? trans[(static_cast<size_t>(u) * 2) * nW + idx]
+                        : trans[(static_cast<size_t>(u) * 2 + 1) * nW + (idx - nq)];
+    const size_t wb = static_cast<size_t>(u) * nW + w;
+    uint32_t* cw = codes + wb * (8 * D);
+    float* qw = qsc + wb * SQ;
+    if (quant) {
+      // one (side, row, group) per thread: minimum, maximum, scale, codes
+      for (int task = tid; task < 2 * kRows * NG; task += 256) {
+        const int side = task / (kRows * NG);
+        const int rem = task - side * kRows * NG;
+        const int r = rem / NG;
+        const int grp = rem - r * NG;
+        const typename E::T* src = side == 0 ? kf : vf;
+        float x[kGroup];
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          const int c = grp * kGroup + j;
+          const size_t o = ub + (side == 0 ? k16_off(w * kRows + r, c, D) : v32_off(w * kRows + r, c, D));
+          x[j] = E::ld(src, o);
+          mn = fminf(mn, x[j]);
+          mx = fmaxf(mx, x[j]);
+        }
+        const float sc = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          int code = 0;
+          if (sc > 0.f) {
+            const float t = rintf(__fdiv_rn(__fsub_rn(x[j], mn), sc));
+            code = static_cast<int>(fminf(fmaxf(t, 0.f), 3.f));
+          }
+          cb[side][r][grp * kGroup + j] = static_cast<uint8_t>(code);
+        }
+        qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)] = sc;
+        qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)] = mn;
+      }
+      __syncthreads();
+      for (int wd = tid; wd < 2 * WPS; wd += 256) {
+        const int side = wd / WPS;
+        const int rem = wd - side * WPS;
+        const int lane = rem / (D / 16);
+        const int t = rem - lane * (D / 16);
+        uint32_t x = 0;
+#pragma unroll
+        for (int oh = 0; oh < 2; ++oh)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            int r, c;
+            code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
+            x |= static_cast<uint32_t>(cb[side][r][c]) << (8 * (j & 3) + 2 * (2 * oh + (j >> 2)));
+          }
+        cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)] = x;
+      }
+      if (tid == 0) has_code[wb] = 1;
+    } else {
+      for (int wd = tid; wd < 2 * WPS; wd += 256) {
+        const int side = wd / WPS;
+        const int rem = wd - side * WPS;
+        const int lane = rem / (D / 16);
+        const int t = rem - lane * (D / 16);
+        const uint32_t x = cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)];
+#pragma unroll
+        for (int oh = 0; oh < 2; ++oh)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            int r, c;
+            code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
+            cb[side][r][c] = static_cast<uint8_t>((x >> (8 * (j & 3) + 2 * (2 * oh + (j >> 2)))) & 3u);
+          }
+      }
+      __syncthreads();
+      for (int e = tid; e < 2 * kRows * D; e += 256) {
+        const int side = e / (kRows * D);
+        const int rem = e - side * kRows * D;
+        const int r = rem / D;
+        const int c = rem - r * D;
+        const int grp = c / kGroup;
+        const float sc = qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)];
+        const float mn = qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)];
+        const float val = dequant(static_cast<float>(cb[side][r][c]), sc, mn);
+        if (side == 0)
+          kf[ub + k16_off(w * kRows + r, c, D)] = E::from_f32(val);
+        else
+          vf[ub + v32_off(w * kRows + r, c, D)] = E::from_f32(val);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int DT, int D>
+hipError_t decode_impl(const rskv_window* W, const void* qv, float* out, bool event, int nf, int nq,
+                       hipStream_t st, const KernelEvents* ev, bool* recorded) {
+  typedef typename Elem<DT>::T T;
+  const int U = W->B * W->Hkv;
+  const int nit = nf + nq;
+  const int nsplit = attend_nsplit(W, nf, nit);
+  auto E = [&](int k) -> const KernelEvents* {
+    if (recorded) recorded[k] = true;
+    return ev ? ev + k : nullptr;
+  };
+  if (recorded)
+    for (int k = 0; k < kKernels; ++k) recorded[k] = false;
+  const T* q = static_cast<const T*>(qv);
+  const T* kf = static_cast<const T*>(W->kf);
+  const T* vf = static_cast<const T*>(W->vf);
+  hipError_t e;
+  const dim3 grid(nsplit, U);
+  if constexpr (DT == kBF16) {
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(kf);
+    const uint16_t* v16 = reinterpret_cast<const uint16_t*>(vf);
+    if (event)
+      e = launch(attend_mfma_kernel<D, true>, grid, dim3(256), 0, st, E(0), q16, k16, v16,
+                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
+                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
+                 nsplit, W->part, W->wstat);
+    else
+      e = launch(attend_mfma_kernel<D, false>, grid, dim3(256), 0, st, E(0), q16, k16, v16,
+                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
+                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
+                 nsplit, W->part, W->wstat);
+  } else {
+    if (event)
+      e = launch(attend_valu_kernel<DT, D, true>, grid, dim3(256), 0, st, E(0), q, kf, vf,
+                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
+                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
+                 nsplit, W->part, W->wstat);
+    else
+      e = launch(attend_valu_kernel<DT, D, false>, grid, dim3(256), 0, st, E(0), q, kf, vf,
+                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
+                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
+                 nsplit, W->part, W->wstat);
+  }
+  if (e != hipSuccess) return e;
+  if (event)
+    e = launch(merge_kernel<D, true>, dim3(W->G, U), dim3(D), 0, st, E(1),
+               static_cast<const float*>(W->part), nsplit, W->G, W->Hq, W->Hkv, out, W->hstat);
+  else
+    e = launch(merge_kernel<D, false>, dim3(W->G, U), dim3(D), 0, st, E(1),
+               static_cast<const float*>(W->part), nsplit, W->G, W->Hq, W->Hkv, out, W->hstat);
+  if (e != hipSuccess || !event) return e;
+  const float2* ws = W->wstat;
+  const float2* hs = W->hstat;
+#define RSKV_ROUTE(NP)                                                                         \
+  launch(route_kernel<NP>, dim3(U), dim3(1024), 0, st, E(2), ws, hs, W->G, W->nW, nit,         \
+         W->n_full, W->n_quant, W->items, W->tier, W->score, W->mass,                           \
+         static_cast<const uint8_t*>(W->has_code), W->trans, W->ntrans)
+  if (W->nW <= 1024)
+    e = RSKV_ROUTE(1024);
+  else if (W->nW <= 4096)
+    e = RSKV_ROUTE(4096);
+  else
+    e = RSKV_ROUTE(16384);
+#undef RSKV_ROUTE
+  if (e != hipSuccess) return e;
+  const int nb = std::max(1, std::min(64, W->nW));
+  return launch(transition_kernel<DT, D>, dim3(nb, U), dim3(256), 0, st, E(3),
+                static_cast<T*>(W->kf), static_cast<T*>(W->vf), W->codes, W->qsc, W->has_code,
+                static_cast<const int32_t*>(W->trans), static_cast<const int32_t*>(W->ntrans), W->nW);
+}
+
+template <int DT, int D>
+hipError_t build_impl(const rskv_window* W, const void* K, const void* V, hipStream_t st) {
+  typedef typename Elem<DT>::T T;
+  const int U = W->B * W->Hkv;
+  const int rows = W->nW * kRows;
+  dim3 grid((rows * (D / 8) + 255) / 256, U);
+  hipLaunchKernelGGL((build_kernel<DT, D>), grid, dim3(256), 0, st, static_cast<const T*>(K),
+                     static_cast<const T*>(V), W->T, rows, static_cast<T*>(W->kf),
+                     static_cast<T*>(W->vf));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attend_nsplit(const rskv_window* W, int nf, int nit) {
+  const long long cost = static_cast<long long>(kCostFull) * nf + static_cast<long long>(kCostQuant) * (nit - nf);
+  const int U = W->B * W->Hkv;
+  // ranges of at least one full window's cost, about kTargetWaves waves in all
+  long long waves = std::min<long long>((cost + kCostFull - 1) / kCostFull, (kTargetWaves + U - 1) / U);
+  waves = std::max<long long>(waves, 1);
+  const bool mfma = W->dtype == RSKV_BF16;
+  // the MFMA kernel gives each of its four waves a range, the VALU kernel one per workgroup
+  return static_cast<int>(mfma ? (waves + 3) / 4 : waves);
+}
+
+hipError_t launch_build(const rskv_window* W, const void* K, const void* V, hipStream_t st) {
+  if (W->dtype == RSKV_BF16)
+    return W->d == 128 ? build_impl<kBF16, 128>(W, K, V, st) : build_impl<kBF16, 64>(W, K, V, st);
+  return W->d == 128 ? build_impl<kF32, 128>(W, K, V, st) : build_impl<kF32, 64>(W, K, V, st);
+}
+
+hipError_t launch_decode(const rskv_window* W, const void* q, float* out, bool event, int nf, int nq,
+                         hipStream_t st, const KernelEvents* ev, bool* recorded) {
+  if (W->dtype == RSKV_BF16)
+    return W->d == 128 ? decode_impl<kBF16, 128>(W, q, out, event, nf, nq, st, ev, recorded)
+                       : decode_impl<kBF16, 64>(W, q, out, event, nf, nq, st, ev, recorded);
+  return W->d == 128 ? decode_impl<kF32, 128>(W, q, out, event, nf, nq, st, ev, recorded)
+                     : decode_impl<kF32, 64>(W, q, out, event, nf, nq, st, ev, recorded);
+}
+
+}  // namespace win
+}  // namespace rskv

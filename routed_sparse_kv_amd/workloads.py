@@ -88,6 +88,45 @@ def retrieval_params(**overrides) -> dict:
     return out
 
 
+#: Window-routed cache parameters (QEvict page, "Metodologia: QEvict" and
+#: the LongBench results): the memory budget as a fraction of the
+#: full-precision cache (the page reports budgets of 20 % and 5 %), the
+#: share of that budget held by the full-precision tier, and the routing
+#: period R in decode steps.  Parameters of the input, not arithmetic of the
+#: method.
+WINDOW_DEFAULTS = dict(budget=0.2, full_share=0.5, route_every=4)
+
+WINDOW_ROWS = 64
+WINDOW_GROUP = 64
+
+
+def window_params(**overrides) -> dict:
+    """Copy of WINDOW_DEFAULTS with ``overrides`` applied."""
+    out = dict(WINDOW_DEFAULTS)
+    for k, v in overrides.items():
+        if k not in out:
+            raise KeyError(f"unknown window parameter {k!r}")
+        out[k] = v
+    return out
+
+
+def window_tiers(T: int, d: int, dtype: str, budget: float, full_share: float):
+    """Window counts (n_full, n_quant) per KV head that fit a byte budget of
+    ``budget`` times the full-precision cache: ``full_share`` of the budget
+    (rounded down to whole windows) at full precision, the rest in INT2
+    windows (2-bit codes plus an fp32 scale and minimum per row and group
+    of 64 coordinates, for K and V).  At least one window is kept."""
+    n_w = (T + WINDOW_ROWS - 1) // WINDOW_ROWS
+    full_b = 2 * WINDOW_ROWS * d * (2 if dtype == "bf16" else 4)
+    quant_b = 2 * WINDOW_ROWS * (d // 4) + 2 * WINDOW_ROWS * (d // WINDOW_GROUP) * 2 * 4
+    total = budget * n_w * full_b
+    n_full = int(math.floor(full_share * budget * n_w))
+    n_quant = int(max(0.0, total - n_full * full_b) // quant_b)
+    if n_full + n_quant < 1:
+        n_full = 1
+    return n_full, n_quant
+
+
 def srht_signs(cfg: dict) -> np.ndarray:
     """The d random signs of the retrieval router's rotation (int8, +-1),
     drawn from ``default_rng([seed, 2**24])`` of the configuration."""

@@ -7,7 +7,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("rskv.h", "rskv_retrieval.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rskv.h", "rskv_retrieval.h", "rskv_window.h")]
 LIB = os.path.join(ROOT, "routed_sparse_kv_amd", "lib", "librskv.so")
 
 
@@ -23,7 +23,10 @@ def test_header_declares_the_boundary():
               "rskv_cache_export",
               "rskv_cache_import", "rskv_cache_destroy", "rskv_last_error",
               "rskv_retrieval_build", "rskv_retrieval_decode", "rskv_retrieval_export",
-              "rskv_retrieval_trace_get", "rskv_retrieval_destroy"):
+              "rskv_retrieval_trace_get", "rskv_retrieval_destroy",
+              "rskv_window_build", "rskv_window_decode", "rskv_window_info_get",
+              "rskv_window_state_get", "rskv_window_profile_enable", "rskv_window_profile_read",
+              "rskv_window_destroy"):
         assert s in syms
 
 
@@ -49,6 +52,13 @@ def test_version_and_error_strings_without_gpu():
     lib.rskv_retrieval_decode.argtypes = [ctypes.c_void_p] * 5
     assert lib.rskv_retrieval_decode(None, None, None, None, None) == -6
     assert b"invalid retrieval handle" in lib.rskv_last_error()
+    lib.rskv_window_decode.argtypes = [ctypes.c_void_p] * 4
+    assert lib.rskv_window_decode(None, None, None, None) == -6
+    assert b"invalid window cache handle" in lib.rskv_last_error()
+    lib.rskv_window_build.argtypes = [ctypes.c_void_p] * 5
+    out = ctypes.c_void_p(1)
+    assert lib.rskv_window_build(None, None, None, None, ctypes.byref(out)) == -1
+    assert out.value is None
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
