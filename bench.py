@@ -41,9 +41,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None,
                     help="default: long_128k_bf16 (span router), million_1m_bf16 (retrieval)")
-    ap.add_argument("--router", default="span", choices=["span", "retrieval"],
+    ap.add_argument("--router", default="span", choices=["span", "retrieval", "window"],
                     help="span: SEKV span routing (decode_step); retrieval: ParisKV-style "
-                         "token retrieval (rskv_retrieval_decode)")
+                         "token retrieval (rskv_retrieval_decode); window: QEvict-form "
+                         "three-tier window routing (rskv_window_decode)")
     ap.add_argument("--kv-tier", default="hbm", choices=["hbm", "host"],
                     help="retrieval router: where the retrieval region's K/V live")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GB per rotation")
@@ -101,6 +102,7 @@ def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg, factors_only=False):
 
 ATTEND_SOURCES = ("attend.hip", "common.h")
 RETRIEVAL_SOURCES = ("retrieval.hip", "retrieval.h", "common.h")
+WINDOW_SOURCES = ("window.hip", "window.h", "layout.h", "common.h")
 
 
 def kernel_sha(files=ATTEND_SOURCES):
@@ -426,6 +428,214 @@ def retrieval_cpu_baseline(wl, signs, params, n_units, ctx_tokens, log, budget_s
             "seconds_per_step": t_step}
 
 
+def window_step_bytes(info, esize, nsplit, event):
+    """Algorithmic bytes of one window-router decode step per kernel, with
+    the tiers of a step after the first routing event: every attended
+    window's bytes read once (full: K and V rows; INT2: codes, scales and
+    minima), the queries read, the partial softmax states written once and
+    read once by the merge; routing steps add the per-window statistics and
+    the routing kernel's per-window state."""
+    U = info["batch"] * info["n_kv_heads"]
+    d, G, nW = info["head_dim"], info["n_q_heads"] // info["n_kv_heads"], info["n_windows"]
+    nf, nq = info["next_full"], info["next_quant"]
+    part = nsplit * G * (d + 2) * 4
+    stats = (nf + nq) * G * 8 if event else 0
+    per = {
+        "attend": nf * info["full_bytes"] + nq * info["quant_bytes"] + G * d * esize
+                  + (nf + nq) * 4 + part + stats,
+        "merge": part + G * d * 4,
+        "route": (stats + G * 8 + nW * (8 + 8 + 8 + 1 + 1) + (nf + nq) * 4) if event else 0,
+        "transition": 0,
+    }
+    return {k: v * U for k, v in per.items()}
+
+
+def window_bench(args):
+    """Decode-step throughput of the window-routed three-tier cache (QEvict
+    page): attention over the full-precision and INT2 windows plus the merge
+    on every step, and the routing event (ranking, tiers, ledger writes and
+    promotions) every route_every steps.  The cache is built untimed and
+    taken through its first routing event (which quantises every demoted
+    window into the ledger) in the warm-up; steps rotate over replicas so
+    that one rotation reads at least 1 GB."""
+    import torch
+
+    import routed_sparse_kv_amd as rskv
+    from routed_sparse_kv_amd import workloads as W
+    from routed_sparse_kv_amd.window import KERNELS
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    t0 = time.perf_counter()
+    wl = W.generate(args.workload)
+    cfg = wl.cfg
+    dt = cfg["dtype"]
+    wp = W.window_params()
+    n_full, n_quant = W.window_tiers(cfg["T"], cfg["d"], dt, wp["budget"], wp["full_share"])
+    R_ev = wp["route_every"]
+    log(f"generated {args.workload} in {time.perf_counter() - t0:.1f}s; "
+        f"n_full={n_full} n_quant={n_quant} route_every={R_ev}")
+
+    def to_dev(a):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    K, V = to_dev(wl.K), to_dev(wl.V)
+    esize = 2 if dt == "bf16" else 4
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    caches = [rskv.build_window(K, V, cfg["Hq"], n_full, n_quant, R_ev)]
+    build_s = time.perf_counter() - tb
+    info0 = caches[0].info
+    U = cfg["B"] * cfg["Hkv"]
+    per_step_est = U * (min(n_full, info0["n_windows"]) * info0["full_bytes"] +
+                        n_quant * info0["quant_bytes"])
+    NR = args.replicas or max(1, math.ceil(1.0e9 / max(per_step_est, 1)))
+    NR = min(NR, 8)
+    for _ in range(NR - 1):
+        caches.append(rskv.build_window(K, V, cfg["Hq"], n_full, n_quant, R_ev))
+    del K, V
+    torch.cuda.empty_cache()
+    log(f"build {build_s:.2f}s; {NR} cache replicas, {info0['device_bytes'] / 1e9:.2f} GB each")
+    qs = [to_dev(q) for q in wl.queries]
+    B = cfg["B"]
+    out = torch.empty((B, cfg["Hq"], cfg["d"]), dtype=torch.float32, device=dev)
+    # warm-up: every replica through its first routing event and into the
+    # steady phase; the timed steps then hold route_every-periodic events
+    warm = max(args.warmup, NR * (R_ev + 1))
+    warm += (-warm) % (NR * R_ev)
+    for i in range(warm):
+        caches[i % NR].decode(qs[i % len(qs)], out=out)
+    torch.cuda.synchronize()
+    n_steps = args.steps
+    n_steps += (-n_steps) % (NR * R_ev)  # whole routing periods on every replica
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_steps):
+        caches[i % NR].decode(qs[i % len(qs)], out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / n_steps
+    # per-kernel durations: HIP events carried by each dispatch
+    for c in caches:
+        c.profile_enable(True)
+    for i in range(n_steps):
+        caches[i % NR].decode(qs[i % len(qs)], out=out)
+    torch.cuda.synchronize()
+    tot = {k: 0.0 for k in KERNELS}
+    steps = events = 0
+    for c in caches:
+        p = c.profile_read()
+        steps += p["steps"]
+        events += p["events"]
+        for k in KERNELS:
+            tot[k] += p[f"{k}_ms"]
+        c.profile_enable(False)
+    info = caches[0].info
+    nsplit = info["next_splits"]
+    plain = window_step_bytes(info, esize, nsplit, False)
+    evb = window_step_bytes(info, esize, nsplit, True)
+    attend_ms = tot["attend"] / max(1, steps)
+    # mean attention launch: (steps - events) plain launches and `events` routing-step ones
+    attend_bytes = ((steps - events) * plain["attend"] + events * evb["attend"]) / max(1, steps)
+    attend_gbps = attend_bytes / (attend_ms / 1e3) / 1e9
+    step_b = {k: ((steps - events) * plain[k] + events * evb[k]) / max(1, steps) for k in plain}
+    step_total = float(sum(step_b.values()))
+    kern = {f"{k}_ms": tot[k] / max(1, steps) for k in KERNELS}
+    kern["route_ms_per_event"] = tot["route"] / max(1, events)
+    kern["transition_ms_per_event"] = tot["transition"] / max(1, events)
+    ctx_tokens = B * cfg["T"]
+    value = ctx_tokens / (ms_step / 1e3)
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "context-tokens/s/head",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "router": "window", "batch": B, "context": cfg["T"],
+                   "q_heads": cfg["Hq"], "kv_heads": cfg["Hkv"], "head_dim": cfg["d"],
+                   "budget": wp["budget"], "full_share": wp["full_share"],
+                   "route_every": R_ev, "n_windows": info["n_windows"], "n_full": n_full,
+                   "n_quant": n_quant, "replicas": NR},
+        "roofline": {"bound": "hbm", "achieved": attend_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": attend_gbps / PEAK_HBM_GBPS,
+                     "traffic": committed_traffic(args.workload, "window_attend", WINDOW_SOURCES),
+                     "kernel": "attend_mfma_kernel",
+                     "algorithmic_bytes_per_launch": attend_bytes,
+                     "mean_launch_ms": attend_ms},
+        "step_algorithmic_bytes": step_total,
+        "step_algorithmic_gbps": step_total / (ms_step / 1e3) / 1e9,
+        "step_frac_of_peak": step_total / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "kernel_algorithmic_bytes": step_b,
+        "kernel_ms": kern,
+        "profiled_ms_per_step": sum(tot.values()) / max(1, steps),
+        "tokens_per_s_all_kv_heads": value * cfg["Hkv"],
+        "build_s": build_s,
+        "cache_device_bytes": info["device_bytes"],
+        "bytes_read_per_unit_step": info["next_full"] * info["full_bytes"]
+                                    + info["next_quant"] * info["quant_bytes"],
+        "full_cache_bytes_per_unit": info["n_windows"] * info["full_bytes"],
+    }
+    for c in caches:
+        c.close()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = window_cpu_baseline(wl, n_full, n_quant, R_ev, U, ctx_tokens, log)
+    print(json.dumps(res))
+
+
+def window_cpu_baseline(wl, n_full, n_quant, R_ev, n_units, ctx_tokens, log, budget_s=15.0):
+    """The oracle's window decode on one unit (sequence 0, KV head 0) over
+    the workload's queries in turn; the first step (the first routing event,
+    which quantises every demoted window) is untimed.  Later steps, routing
+    events included at their period, are timed and scaled to one step of
+    n_units units."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import qevict
+    from routed_sparse_kv_amd import workloads as W
+    cfg = wl.cfg
+    dt = cfg["dtype"]
+    G = cfg["Hq"] // cfg["Hkv"]
+    st = qevict.new_unit(W.as_f64(wl.K[0, 0], dt), W.as_f64(wl.V[0, 0], dt), W.WINDOW_ROWS)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        qevict.decode_unit(st, W.as_f64(wl.queries[0][0, :G], dt), 0, R_ev, n_full, n_quant,
+                           W.WINDOW_GROUP, dt)
+        log(f"oracle first routing step of one unit {time.perf_counter() - t0:.1f}s (untimed)")
+        done, el = 0, 0.0
+        while el < budget_s or done % R_ev:
+            step = done + 1
+            q = W.as_f64(wl.queries[step % len(wl.queries)][0, :G], dt)
+            t1 = time.perf_counter()
+            qevict.decode_unit(st, q, step, R_ev, n_full, n_quant, W.WINDOW_GROUP, dt)
+            el += time.perf_counter() - t1
+            done += 1
+    t_step = el / done * n_units
+    return {"value": ctx_tokens / t_step, "unit": "context-tokens/s/head", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} oracle window decode steps of unit (0, 0) ({cfg['T']} tokens, "
+                      f"routing every {R_ev} steps, after the untimed first event), "
+                      f"{el:.1f}s single-threaded, scaled to one {n_units}-unit step",
+            "seconds_per_step": t_step}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -437,6 +647,9 @@ def main():
         return
     if args.router == "retrieval":
         retrieval_bench(args)
+        return
+    if args.router == "window":
+        window_bench(args)
         return
     import torch
 

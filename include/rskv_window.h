@@ -104,6 +104,8 @@ typedef struct {
   int64_t step;          /* decode steps done */
   int32_t next_full;     /* windows attended at full precision by the next step */
   int32_t next_quant;    /* windows attended in INT2 by the next step */
+  int32_t next_splits;   /* attention workgroups per KV head the next step launches
+                            (each writes one partial softmax state per query head) */
   int32_t full_bytes;    /* bytes read per full-precision window (K and V) */
   int32_t quant_bytes;   /* bytes read per INT2 window (codes, scales, minima) */
   size_t device_bytes;   /* device memory held */

@@ -27,9 +27,10 @@ constexpr uint32_t kMagic = 0x52534b57u;   // "RSKW"
 // [part = t / 4][lane 0..63][t % 4] for the lane's word t < d / 16, so that
 // a wave reads one side with d / 64 16-byte loads per lane.  Word t of a
 // lane holds the 8-code MFMA operands o = 2 t and 2 t + 1; code j of
-// operand o (o' = o % 2) sits at bit 8 (j % 4) + 2 (2 o' + j / 4), so that
-// (word >> 4 o') & 0x03030303 gives codes 0..3 one per byte and
-// (word >> (4 o' + 2)) & 0x03030303 codes 4..7.
+// operand o (o' = o % 2) sits at bit 4 j + 2 o', so that
+// (word >> 2 o') & 0x33333333 holds the operand's codes as the 4-bit
+// floating-point (e2m1) values 0, 0.5, 1, 1.5, one per nibble, which the
+// hardware widens to bf16 two at a time.
 //   K side, operand o = rb16 * (d / 32) + kb: lane l holds row 16 rb16 + l % 16,
 //     columns 32 kb + 8 (l / 16) + j (the A operand of the QK product).
 //   V side, operand o = rb32 * (d / 16) + cb: lane l holds column
@@ -62,7 +63,7 @@ RSKV_HD int code_word(int side, int r, int c, int d, int* bit) {
     j = (rr & 3) + 4 * (rr >> 4);
   }
   const int t = o >> 1;
-  *bit = 8 * (j & 3) + 2 * (2 * (o & 1) + (j >> 2));
+  *bit = 4 * j + 2 * (o & 1);
   return side * 4 * d + ((t >> 2) * 64 + lane) * 4 + (t & 3);
 }
 

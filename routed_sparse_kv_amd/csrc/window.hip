@@ -6,8 +6,8 @@
 //       ones; ranges balanced by a per-window cost) with an online softmax
 //       per query head.  Full windows: QK and PV products on 16x16x32 bf16
 //       MFMAs straight from the K16 / V32 tiles.  INT2 windows: the codes
-//       are widened to bf16 in registers (two byte permutes per code pair)
-//       and fed to the same MFMAs; the fp32 scales and minima are applied
+//       are widened to bf16 in registers (one packed fp4 conversion per code
+//       pair) and fed to the same MFMAs; the fp32 scales and minima are applied
 //       around the products:
 //         <q, k_r> = sum_grp scale_r,grp <q_grp, code_r,grp> + min_r,grp sum(q_grp)
 //         sum_r p_r v_r = sum_r (p_r scale_r,grp) code_r + sum_r p_r min_r,grp
@@ -39,8 +39,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCostFull = 4;  // work cost of a full-precision window
-constexpr int kCostQuant = 1; // and of an INT2 window
+constexpr int kCostFull = 2;  // work cost of a full-precision window (measured
+constexpr int kCostQuant = 1; // attention time ratio to an INT2 window)
+constexpr float kMaxSlack = 11.f;  // base-2 logits may exceed the running softmax reference by this
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTargetWaves = 8192;
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -58,20 +61,17 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
   }
 }
 
-// Eight 2-bit codes (one byte each in m0 = codes 0..3, m1 = codes 4..7) as
-// bf16 0.0 .. 3.0.  A byte permute builds the selector [c, c + 4] per code
-// and a second one looks the two bytes of bf16(c) up in the tables
-// lo = {00, 80, 00, 40}, hi = {00, 3f, 40, 40}.
-__device__ __forceinline__ uint32_t widen2(uint32_t m, uint32_t sel) {
-  const uint32_t s = __builtin_amdgcn_perm(m | 0x04040404u, m, sel);
-  return __builtin_amdgcn_perm(0x40403f00u, 0x40008000u, s);
-}
+// The eight codes of MFMA operand `half` of a ledger word as bf16 0.0 ..
+// 3.0: masked to one code per nibble they are e2m1 values c / 2, which the
+// packed fp4 -> bf16 conversion widens two at a time with scale 2.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 decode8(uint32_t word, int half) {
-  const uint32_t m0 = (word >> (4 * half)) & 0x03030303u;
-  const uint32_t m1 = (word >> (4 * half + 2)) & 0x03030303u;
-  const u32x4 v{widen2(m0, 0x05010400u), widen2(m0, 0x07030602u), widen2(m1, 0x05010400u),
-                widen2(m1, 0x07030602u)};
-  return as8(v);
+  const uint32_t nib = (word >> (2 * half)) & 0x33333333u;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, 2.0f, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, 2.0f, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, 2.0f, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, 2.0f, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Dequantised INT2 value mn + code * scale: the product is rounded to fp32
@@ -137,7 +137,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
   const int wave = tid >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int v = blockIdx.x * 4 + wave;
+  // the four waves of a workgroup take ranges a quarter of the unit apart,
+  // so that each workgroup mixes full-precision (memory-bound) and INT2
+  // (ALU-bound) windows
+  const int v = wave * nsplit + blockIdx.x;
   const int k0 = range_start(v, nsplit * 4, nf, nit);
   const int k1 = range_start(v + 1, nsplit * 4, nf, nit);
 
@@ -166,9 +169,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
       qsum[x] += __shfl_xor(qsum[x], 32, kWave);
     }
   }
-  const float sl = 1.0f / sqrtf(static_cast<float>(D));
+  // logits in base 2: <q, k> / sqrt(d) * log2(e), so that p = 2^(s - m)
+  const float sl = kLog2e / sqrtf(static_cast<float>(D));
 
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running reference and sum (base 2)
   f32x4 acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -242,12 +246,14 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
         }
       }
     }
-    // rows past the context
+    // rows past the context (the last window only)
+    if (nvalid < kRows) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (rb * 16 + 4 * g + i >= nvalid) s[rb][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i)
+          if (rb * 16 + 4 * g + i >= nvalid) s[rb][i] = -INFINITY;
+    }
 
     // online softmax for head n (rows spread over the 4 lane groups)
     float cm = s[0][0];
@@ -262,29 +268,35 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ws += __expf(s[rb][i] - cm);
+        for (int i = 0; i < 4; ++i) ws += __builtin_amdgcn_exp2f(s[rb][i] - cm);
       ws += __shfl_xor(ws, 16, kWave);
       ws += __shfl_xor(ws, 32, kWave);
-      if (g == 0 && hv) wstat[(static_cast<size_t>(u) * nW + k) * G + n] = make_float2(cm, ws);
+      if (g == 0 && hv) wstat[(static_cast<size_t>(u) * nW + k) * G + n] = make_float2(cm * kLn2, ws);
     }
-    const float mnew = fmaxf(m, cm);
-    const float fac = __expf(m - mnew);
+    // the softmax reference m moves only when a logit exceeds it by more
+    // than kMaxSlack (p <= 2^11 stays exact enough in fp32), so the state is
+    // rarely rescaled
+    const float mnew = cm > m + kMaxSlack ? cm : m;
+    if (__any(mnew != m)) {
+      const float fac = __builtin_amdgcn_exp2f(m - mnew);
+      l *= fac;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] *= fac;
+#pragma unroll
+      for (int x = 0; x < NG; ++x) amn[x] *= fac;
+      m = mnew;
+    }
     float ps = 0.f;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[rb][i] = __expf(s[rb][i] - mnew);
+        s[rb][i] = __builtin_amdgcn_exp2f(s[rb][i] - m);
         ps += s[rb][i];
       }
     ps += __shfl_xor(ps, 16, kWave);
     ps += __shfl_xor(ps, 32, kWave);
-    l = l * fac + ps;
-    m = mnew;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[cb] *= fac;
-#pragma unroll
-    for (int x = 0; x < NG; ++x) amn[x] *= fac;
+    l += ps;
 
     // PV: A = values (column 16 cb + n, rows v32_row(g, .)), B = p (head n)
 #pragma unroll
@@ -356,7 +368,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
   __shared__ float sm[4][kMaxG], sl4[4][kMaxG];
   __shared__ float so[4][kMaxG][D];
   if (g == 0) {
-    sm[wave][n] = m;
+    sm[wave][n] = m * kLn2;  // back to natural-log units for the merge
     sl4[wave][n] = l;
   }
 #pragma unroll
@@ -515,7 +527,12 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(
 
 // ---------------------------------------------------------------- merge
 
-// Grid (G, U), D threads: out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s.
+// Grid (G, U), D threads: out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s
+// for query head g of unit u.  The maximum, the weights e^{m_s - M} (kept
+// in LDS) and the denominator are reduced over the partials in parallel;
+// each thread then sums its column, eight independent loads at a time.
+constexpr int kMergeChunk = 1024;
+
 template <int D, bool MASS>
 __global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part, int nsplit, int G,
                                                   int Hq, int Hkv, float* __restrict__ out,
@@ -527,6 +544,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part
   const int h = u - b * Hkv;
   const int c = threadIdx.x;
   __shared__ float buf[NW];
+  __shared__ float wgt[kMergeChunk];
   const size_t stride = static_cast<size_t>(G) * (D + 2);
   const float* p = part + static_cast<size_t>(u) * nsplit * stride + static_cast<size_t>(g) * (D + 2);
   float mx = -INFINITY;
@@ -538,10 +556,27 @@ __global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part
 #pragma unroll
   for (int x = 1; x < NW; ++x) M = fmaxf(M, buf[x]);
   __syncthreads();
-  float dl = 0.f;
-  for (int s = c; s < nsplit; s += D) {
-    const float ms = p[s * stride + D];
-    if (ms != -INFINITY) dl += expf(ms - M) * p[s * stride + D + 1];
+  float dl = 0.f, num = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kMergeChunk) {
+    const int ns = min(kMergeChunk, nsplit - s0);
+    for (int s = c; s < ns; s += D) {
+      const float ms = p[(s0 + s) * stride + D];
+      const float wv = ms == -INFINITY ? 0.f : expf(ms - M);
+      wgt[s] = wv;
+      dl += wv * p[(s0 + s) * stride + D + 1];
+    }
+    __syncthreads();
+    const float* pc = p + static_cast<size_t>(s0) * stride + c;
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = pc[(s + j) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) num += wgt[s + j] * x[j];
+    }
+    for (; s < ns; ++s) num += wgt[s] * pc[s * stride];
+    __syncthreads();
   }
   dl = wave_sum(dl);
   if ((c & 63) == 0) buf[c >> 6] = dl;
@@ -549,11 +584,6 @@ __global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part
   float den = 0.f;
 #pragma unroll
   for (int x = 0; x < NW; ++x) den += buf[x];
-  float num = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = p[s * stride + D];
-    if (ms != -INFINITY) num += expf(ms - M) * p[s * stride + c];
-  }
   out[(static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G + g) * D + c] = num / den;
   if (MASS && c == 0) hstat[static_cast<size_t>(u) * G + g] = make_float2(M, den);
 }
@@ -710,7 +740,7 @@ __global__ __launch_bounds__(256) void transition_kernel(
           for (int j = 0; j < 8; ++j) {
             int r, c;
             code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
-            x |= static_cast<uint32_t>(cb[side][r][c]) << (8 * (j & 3) + 2 * (2 * oh + (j >> 2)));
+            x |= static_cast<uint32_t>(cb[side][r][c]) << (4 * j + 2 * oh);
           }
         cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)] = x;
       }
@@ -728,7 +758,7 @@ __global__ __launch_bounds__(256) void transition_kernel(
           for (int j = 0; j < 8; ++j) {
             int r, c;
             code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
-            cb[side][r][c] = static_cast<uint8_t>((x >> (8 * (j & 3) + 2 * (2 * oh + (j >> 2)))) & 3u);
+            cb[side][r][c] = static_cast<uint8_t>((x >> (4 * j + 2 * oh)) & 3u);
           }
       }
       __syncthreads();

@@ -248,6 +248,7 @@ int rskv_window_info_get(const rskv_window* w, rskv_window_info* i) {
   i->step = w->step;
   i->next_full = w->nf_next;
   i->next_quant = w->nq_next;
+  i->next_splits = W::attend_nsplit(w, w->nf_next, w->nf_next + w->nq_next);
   i->full_bytes = static_cast<int32_t>(2 * W::kRows * w->d * esize(w->dtype));
   i->quant_bytes = static_cast<int32_t>(W::code_words(w->d) * 4 + W::scale_floats(w->d) * 4);
   i->device_bytes = w->bytes;

@@ -26,7 +26,8 @@ class WindowInfo(C.Structure):
                 ("batch", "n_q_heads", "n_kv_heads", "head_dim", "context_len", "dtype", "n_full",
                  "n_quant", "route_every", "n_windows")] + \
                [("step", C.c_int64)] + \
-               [(n, C.c_int32) for n in ("next_full", "next_quant", "full_bytes", "quant_bytes")] + \
+               [(n, C.c_int32) for n in ("next_full", "next_quant", "next_splits", "full_bytes",
+                                         "quant_bytes")] + \
                [("device_bytes", C.c_size_t)]
 
 
