@@ -432,19 +432,25 @@ def window_step_bytes(info, esize, nsplit, event):
     """Algorithmic bytes of one window-router decode step per kernel, with
     the tiers of a step after the first routing event: every attended
     window's bytes read once (full: K and V rows; INT2: codes, scales and
-    minima), the queries read, the partial softmax states written once and
-    read once by the merge; routing steps add the per-window statistics and
-    the routing kernel's per-window state."""
+    minima), the queries and the attended list read, the partial softmax
+    states written once and read once by the merge; routing steps add the
+    per-window statistics and the routing kernel's per-window state."""
     U = info["batch"] * info["n_kv_heads"]
     d, G, nW = info["head_dim"], info["n_q_heads"] // info["n_kv_heads"], info["n_windows"]
     nf, nq = info["next_full"], info["next_quant"]
-    part = nsplit * G * (d + 2) * 4
-    stats = (nf + nq) * G * 8 if event else 0
+    part = G * (d + 2) * 4  # per workgroup
+    nit = nf + nq
+    stats = nit * G * 8 if event else 0
+    # the two attention kernels split the partials in proportion to their workgroups
+    sf = -(-min(nf, -(-4096 // U)) // 4) if nf else 0
+    sq = -(-min(nq, -(-8192 // U)) // 4) if nq else 0
     per = {
-        "attend": nf * info["full_bytes"] + nq * info["quant_bytes"] + G * d * esize
-                  + (nf + nq) * 4 + part + stats,
-        "merge": part + G * d * 4,
-        "route": (stats + G * 8 + nW * (8 + 8 + 8 + 1 + 1) + (nf + nq) * 4) if event else 0,
+        "attend_full": nf * info["full_bytes"] + (G * d * esize + nf * 4 + sf * part
+                                                  + nf * G * 8 * bool(event) if nf else 0),
+        "attend_int2": nq * info["quant_bytes"] + (G * d * esize + nq * 4 + sq * part
+                                                   + nq * G * 8 * bool(event) if nq else 0),
+        "merge": nsplit * part + G * d * 4,
+        "route": (stats + G * 8 + nW * (8 + 8 + 8 + 1 + 1) + nit * 4) if event else 0,
         "transition": 0,
     }
     return {k: v * U for k, v in per.items()}
@@ -545,15 +551,18 @@ def window_bench(args):
     nsplit = info["next_splits"]
     plain = window_step_bytes(info, esize, nsplit, False)
     evb = window_step_bytes(info, esize, nsplit, True)
-    attend_ms = tot["attend"] / max(1, steps)
-    # mean attention launch: (steps - events) plain launches and `events` routing-step ones
-    attend_bytes = ((steps - events) * plain["attend"] + events * evb["attend"]) / max(1, steps)
-    attend_gbps = attend_bytes / (attend_ms / 1e3) / 1e9
-    step_b = {k: ((steps - events) * plain[k] + events * evb[k]) / max(1, steps) for k in plain}
+    mean = lambda k: ((steps - events) * plain[k] + events * evb[k]) / max(1, steps)  # noqa: E731
+    step_b = {k: mean(k) for k in plain}
     step_total = float(sum(step_b.values()))
     kern = {f"{k}_ms": tot[k] / max(1, steps) for k in KERNELS}
     kern["route_ms_per_event"] = tot["route"] / max(1, events)
     kern["transition_ms_per_event"] = tot["transition"] / max(1, events)
+    gbps = {k: step_b[k] / (kern[f"{k}_ms"] / 1e3) / 1e9 if kern[f"{k}_ms"] > 0 else 0.0
+            for k in ("attend_full", "attend_int2")}
+    att_b = step_b["attend_full"] + step_b["attend_int2"]
+    att_ms = kern["attend_full_ms"] + kern["attend_int2_ms"]
+    # dominant kernel: the longer of the two attention launches
+    dom = "attend_int2" if kern["attend_int2_ms"] >= kern["attend_full_ms"] else "attend_full"
     ctx_tokens = B * cfg["T"]
     value = ctx_tokens / (ms_step / 1e3)
     res = {
@@ -574,12 +583,16 @@ def window_bench(args):
                    "budget": wp["budget"], "full_share": wp["full_share"],
                    "route_every": R_ev, "n_windows": info["n_windows"], "n_full": n_full,
                    "n_quant": n_quant, "replicas": NR},
-        "roofline": {"bound": "hbm", "achieved": attend_gbps, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": attend_gbps / PEAK_HBM_GBPS,
-                     "traffic": committed_traffic(args.workload, "window_attend", WINDOW_SOURCES),
-                     "kernel": "attend_mfma_kernel",
-                     "algorithmic_bytes_per_launch": attend_bytes,
-                     "mean_launch_ms": attend_ms},
+        "roofline": {"bound": "hbm", "achieved": gbps[dom], "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": gbps[dom] / PEAK_HBM_GBPS,
+                     "traffic": committed_traffic(args.workload, f"window_{dom}", WINDOW_SOURCES),
+                     "kernel": f"{dom}_kernel",
+                     "algorithmic_bytes_per_launch": step_b[dom],
+                     "mean_launch_ms": kern[f"{dom}_ms"]},
+        "attention": {"full_gbps": gbps["attend_full"], "int2_gbps": gbps["attend_int2"],
+                      "both_gbps": att_b / (att_ms / 1e3) / 1e9,
+                      "both_frac": att_b / (att_ms / 1e3) / 1e9 / PEAK_HBM_GBPS,
+                      "both_ms": att_ms, "both_bytes": att_b},
         "step_algorithmic_bytes": step_total,
         "step_algorithmic_gbps": step_total / (ms_step / 1e3) / 1e9,
         "step_frac_of_peak": step_total / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBPS,

@@ -90,8 +90,9 @@ int rskv_window_build(const void* K, const void* V, const rskv_window_opts* opts
 /* One decode step.  q: device [B][Hq][d] in dtype.  out: device fp32
  * [B][Hq][d].  Attends with the tiers in force; when the step is a routing
  * event it then updates the scores, re-tiers, quantises the windows demoted
- * for the first time into the ledger and restores promoted windows.  Two
- * stream-ordered launches on other steps, four on routing events; no host
+ * for the first time into the ledger and restores promoted windows.  At
+ * most three stream-ordered launches on other steps, five on routing
+ * events; no host
  * synchronisation, no allocation; calls on one cache must not overlap (they
  * share its workspace and state).  Errors: RSKV_ESTATE (bad handle),
  * RSKV_EINVAL (NULL q or out), RSKV_EHIP. */
@@ -138,13 +139,14 @@ typedef struct {
 int rskv_window_state_get(const rskv_window* cache, rskv_window_state* state);
 
 /* Kernel time of the decode steps while enabled (per-dispatch start/stop
- * events, summed): [0] attention over the windows, [1] merge of the
- * partial softmax states, [2] routing (masses, scores, ranking, tiers),
- * [3] ledger writes and promotions. */
+ * events, summed): [0] attention over the full-precision windows (fp32
+ * caches: over all windows), [1] attention over the INT2 windows (bf16
+ * caches), [2] merge of the partial softmax states, [3] routing (masses,
+ * scores, ranking, tiers), [4] ledger writes and promotions. */
 typedef struct {
   int64_t steps;
   int64_t events;
-  double ms[4];
+  double ms[5];
 } rskv_window_profile;
 
 int rskv_window_profile_enable(rskv_window* cache, int32_t on);

@@ -18,7 +18,7 @@ constexpr int kRows = RSKV_WINDOW_ROWS;    // positions per window
 constexpr int kGroup = RSKV_WINDOW_GROUP;  // coordinates per INT2 scale group
 constexpr int kMaxG = 16;                  // query heads per KV head (MFMA columns)
 constexpr int kMaxWindows = 16384;         // windows per unit the routing sort holds
-constexpr int kKernels = 4;                // attend, merge, route, transition
+constexpr int kKernels = 5;  // attend (full windows), attend (INT2 windows), merge, route, transition
 constexpr uint32_t kMagic = 0x52534b57u;   // "RSKW"
 
 // Ledger of one window (INT2 codes of K and V plus fp32 scales and minima).
@@ -122,8 +122,10 @@ struct rskv_window {
 namespace rskv {
 namespace win {
 
-// Attention workgroups per unit for nit attended windows, nf of them full.
-int attend_nsplit(const rskv_window* w, int nf, int nit);
+// Attention workgroups per unit for nf full and nq INT2 windows: *nsf of
+// the full-window kernel (of the block-cooperative kernel for fp32
+// caches, which takes both) and *nsq of the INT2 kernel.
+void attend_splits(const rskv_window* w, int nf, int nq, int* nsf, int* nsq);
 
 // Copies the caller's K, V [U][T][d] into the tiled store (rows past T zero).
 hipError_t launch_build(const rskv_window* w, const void* K, const void* V, hipStream_t st);

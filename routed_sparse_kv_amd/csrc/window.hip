@@ -1,19 +1,20 @@
 // Window-routed three-tier cache (QEvict summary, "Metodologia: QEvict"):
 // decode kernels.
 //
-//   attend_mfma_kernel  bf16 caches.  Each wave walks a contiguous range of
-//       the unit's attended windows (full-precision ones first, then INT2
-//       ones; ranges balanced by a per-window cost) with an online softmax
-//       per query head.  Full windows: QK and PV products on 16x16x32 bf16
-//       MFMAs straight from the K16 / V32 tiles.  INT2 windows: the codes
+//   attend_full_kernel  bf16 caches, full-precision windows.  Each wave
+//       walks a contiguous range of the unit's full windows with an online
+//       softmax per query head; QK and PV products on 16x16x32 bf16 MFMAs
+//       straight from the K16 / V32 tiles, all loads of a window issued
+//       before its first product.
+//   attend_int2_kernel  bf16 caches, INT2 windows, same structure: the codes
 //       are widened to bf16 in registers (one packed fp4 conversion per code
-//       pair) and fed to the same MFMAs; the fp32 scales and minima are applied
-//       around the products:
+//       pair) and fed to the same MFMAs; the fp32 scales and minima,
+//       staged per wave in LDS, are applied around the products:
 //         <q, k_r> = sum_grp scale_r,grp <q_grp, code_r,grp> + min_r,grp sum(q_grp)
 //         sum_r p_r v_r = sum_r (p_r scale_r,grp) code_r + sum_r p_r min_r,grp
 //       which is the dequantised arithmetic up to association.  fp32
-//       factors enter an MFMA as a bf16 hi + lo pair.  The four waves of a
-//       workgroup merge in LDS and write one partial.
+//       factors enter an MFMA as a bf16 hi + lo pair.  In both kernels the
+//       four waves of a workgroup merge in LDS and write one partial.
 //   attend_valu_kernel  fp32 caches: a block-cooperative fp32 version that
 //       dequantises INT2 rows exactly (mn + code * scale, two roundings).
 //   merge_kernel        log-sum-exp merge of a unit's partials; on routing
@@ -118,40 +119,21 @@ __global__ __launch_bounds__(256) void build_kernel(const typename Elem<DT>::T* 
 
 // --------------------------------------------------------- attention (MFMA)
 
-template <int D, bool MASS>
-__global__ __launch_bounds__(256) void attend_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kf,
-    const uint16_t* __restrict__ vf, const uint32_t* __restrict__ codes,
-    const float* __restrict__ qsc, const int32_t* __restrict__ items, int nW, int T, int Hq,
-    int Hkv, int G, int nf, int nit, int nsplit, float* __restrict__ part,
-    float2* __restrict__ wstat) {
-  constexpr int NG = D / kGroup;
-  constexpr int KB = D / 32;   // 32-column blocks of the QK product
-  constexpr int CB = D / 16;   // 16-column blocks of the output
-  constexpr int SQ = 256 * NG; // scale floats per window
-  const int u = blockIdx.y;
-  const int b = u / Hkv;
-  const int h = u - b * Hkv;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n = lane & 15;
-  const int g = lane >> 4;
-  // the four waves of a workgroup take ranges a quarter of the unit apart,
-  // so that each workgroup mixes full-precision (memory-bound) and INT2
-  // (ALU-bound) windows
-  const int v = wave * nsplit + blockIdx.x;
-  const int k0 = range_start(v, nsplit * 4, nf, nit);
-  const int k1 = range_start(v + 1, nsplit * 4, nf, nit);
-
-  // query operand (head n, columns 32 kb + 8 g + 0..7) and its group sums
-  const bool hv = n < G;
+// Query operand of a wave (head n = lane % 16, columns 32 kb + 8 (lane / 16)
+// + 0..7; zero for heads >= G) and, per 64-column group, the sum of the
+// head's query over the group.
+template <int D>
+struct QOperand {
+  static constexpr int KB = D / 32;
+  static constexpr int NG = D / kGroup;
   bf16x8 qb[KB];
   float qsum[NG];
+  __device__ __forceinline__ void load(const uint16_t* q, size_t base, int lane, int G) {
+    const int n = lane & 15, g = lane >> 4;
+    const bool hv = n < G;
+    const uint16_t* qp = q + base + static_cast<size_t>(hv ? n : 0) * D + 8 * g;
 #pragma unroll
-  for (int x = 0; x < NG; ++x) qsum[x] = 0.f;
-  {
-    const uint16_t* qp = q + (static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G + (hv ? n : 0)) * D + 8 * g;
+    for (int x = 0; x < NG; ++x) qsum[x] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       u32x4 x = *reinterpret_cast<const u32x4*>(qp + kb * 32);
@@ -169,84 +151,30 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
       qsum[x] += __shfl_xor(qsum[x], 32, kWave);
     }
   }
-  // logits in base 2: <q, k> / sqrt(d) * log2(e), so that p = 2^(s - m)
-  const float sl = kLog2e / sqrtf(static_cast<float>(D));
+};
 
-  float m = -INFINITY, l = 0.f;  // running reference and sum (base 2)
+// Online-softmax state of a wave for head n = lane % 16 over the rows its
+// lane group holds, in base 2: reference m, sum l, out^T in the MFMA
+// accumulator layout (coordinates 16 cb + 4 (lane / 16) + i).
+template <int D>
+struct SoftState {
+  static constexpr int CB = D / 16;
+  static constexpr int NG = D / kGroup;
+  float m = -INFINITY, l = 0.f;
   f32x4 acc[CB];
+  float amn[NG];  // INT2 windows: sum_r p_r min_r,grp over the lane's rows
+  __device__ __forceinline__ void init() {
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float amn[NG];
+    for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int x = 0; x < NG; ++x) amn[x] = 0.f;
-
-  for (int k = k0; k < k1; ++k) {
-    // the routing kernel only lists windows < nW; the clamp keeps a bad entry in bounds
-    const int w = min(max(items[static_cast<size_t>(u) * nW + k], 0), nW - 1);
-    const int nvalid = min(kRows, T - w * kRows);
-    const size_t wb = static_cast<size_t>(u) * nW + w;
-    const bool full = k < nf;
-    float s[4][4];
-    u32x4 vw[NG];
-    const float* qv = qsc + wb * SQ + 128 * NG;
-    if (full) {
-      const uint16_t* kt = kf + wb * kRows * D + lane * 8;
-      u32x4 ka[4][KB];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          ka[rb][kb] = *reinterpret_cast<const u32x4*>(kt + (rb * KB + kb) * 512);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        f32x4 c{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) c = mma(as8(ka[rb][kb]), qb[kb], c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[rb][i] = c[i] * sl;
-      }
-    } else {
-      const uint32_t* cw = codes + wb * (8 * D);
-      u32x4 kw[NG];
-#pragma unroll
-      for (int p = 0; p < NG; ++p) {
-        kw[p] = *reinterpret_cast<const u32x4*>(cw + (p * 64 + lane) * 4);
-        vw[p] = *reinterpret_cast<const u32x4*>(cw + 4 * D + (p * 64 + lane) * 4);
-      }
-      const float* qk = qsc + wb * SQ;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        // rows 16 rb + 4 g + i: [i][grp][scale, min]
-        float sc[4 * NG * 2];
-#pragma unroll
-        for (int x = 0; x < 2 * NG; ++x) {
-          const float4 t4 = *reinterpret_cast<const float4*>(qk + (rb * 16 + 4 * g) * 2 * NG + 4 * x);
-          sc[4 * x] = t4.x;
-          sc[4 * x + 1] = t4.y;
-          sc[4 * x + 2] = t4.z;
-          sc[4 * x + 3] = t4.w;
-        }
-        f32x4 cg[NG];
-#pragma unroll
-        for (int x = 0; x < NG; ++x) cg[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int o = rb * KB + kb;
-          const int t = o >> 1;
-          const bf16x8 a = decode8(kw[t >> 2][t & 3], o & 1);
-          cg[kb / 2] = mma(a, qb[kb], cg[kb / 2]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float z = 0.f;
-#pragma unroll
-          for (int x = 0; x < NG; ++x)
-            z += sc[(i * NG + x) * 2] * cg[x][i] + sc[(i * NG + x) * 2 + 1] * qsum[x];
-          s[rb][i] = z * sl;
-        }
-      }
-    }
-    // rows past the context (the last window only)
+    for (int x = 0; x < NG; ++x) amn[x] = 0.f;
+  }
+  // s: the window's 64 base-2 logits of head n (16 per lane) -> probabilities
+  // relative to m.  On routing steps the window's own maximum and sum go to
+  // *ws (natural-log maximum).
+  template <bool MASS>
+  __device__ __forceinline__ void update(float (&s)[4][4], int nvalid, int g, bool store,
+                                         float2* ws) {
     if (nvalid < kRows) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
@@ -254,8 +182,6 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
         for (int i = 0; i < 4; ++i)
           if (rb * 16 + 4 * g + i >= nvalid) s[rb][i] = -INFINITY;
     }
-
-    // online softmax for head n (rows spread over the 4 lane groups)
     float cm = s[0][0];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
@@ -264,17 +190,17 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
     cm = fmaxf(cm, __shfl_xor(cm, 16, kWave));
     cm = fmaxf(cm, __shfl_xor(cm, 32, kWave));
     if (MASS) {
-      float ws = 0.f;
+      float w = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ws += __builtin_amdgcn_exp2f(s[rb][i] - cm);
-      ws += __shfl_xor(ws, 16, kWave);
-      ws += __shfl_xor(ws, 32, kWave);
-      if (g == 0 && hv) wstat[(static_cast<size_t>(u) * nW + k) * G + n] = make_float2(cm * kLn2, ws);
+        for (int i = 0; i < 4; ++i) w += __builtin_amdgcn_exp2f(s[rb][i] - cm);
+      w += __shfl_xor(w, 16, kWave);
+      w += __shfl_xor(w, 32, kWave);
+      if (store) *ws = make_float2(cm * kLn2, w);
     }
-    // the softmax reference m moves only when a logit exceeds it by more
-    // than kMaxSlack (p <= 2^11 stays exact enough in fp32), so the state is
+    // the reference m moves only when a logit exceeds it by more than
+    // kMaxSlack (p <= 2^11 stays exact enough in fp32), so the state is
     // rarely rescaled
     const float mnew = cm > m + kMaxSlack ? cm : m;
     if (__any(mnew != m)) {
@@ -297,7 +223,120 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
     ps += __shfl_xor(ps, 16, kWave);
     ps += __shfl_xor(ps, 32, kWave);
     l += ps;
+  }
+};
 
+// Merge of the four waves of a workgroup (LDS, `mbuf` holds >= 4 * G * D +
+// 8 * kMaxG floats) and the workgroup's partial: per head
+// [out^T (D), max (natural log), sum].
+template <int D>
+__device__ __forceinline__ void block_partial(SoftState<D>& st, float* mbuf, int G, float* pb) {
+  constexpr int CB = D / 16;
+  constexpr int NG = D / kGroup;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  // minima terms of the INT2 values, summed over the lane groups' rows
+#pragma unroll
+  for (int x = 0; x < NG; ++x) {
+    st.amn[x] += __shfl_xor(st.amn[x], 16, kWave);
+    st.amn[x] += __shfl_xor(st.amn[x], 32, kWave);
+  }
+  float* sm = mbuf;                 // [4][kMaxG]
+  float* sl4 = mbuf + 4 * kMaxG;    // [4][kMaxG]
+  float* so = mbuf + 8 * kMaxG;     // [4][G][D]
+  __syncthreads();  // the buffer may alias a wave's staging area
+  if (g == 0) {
+    sm[wave * kMaxG + n] = st.m * kLn2;  // natural-log units for the merge
+    sl4[wave * kMaxG + n] = st.l;
+  }
+  if (n < G) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        so[(wave * G + n) * D + cb * 16 + 4 * g + i] = st.acc[cb][i] + st.amn[cb >> 2];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D;
+    const int c = e - hh * D;
+    float mw[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) mw[x] = sm[x * kMaxG + hh];
+    const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    float o = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float f = mw[x] == -INFINITY ? 0.f : __expf(mw[x] - M);
+        o += f * so[(x * G + hh) * D + c];
+        L += f * sl4[x * kMaxG + hh];
+      }
+    }
+    pb[hh * (D + 2) + c] = o;
+    if (c == 0) {
+      pb[hh * (D + 2) + D] = M;
+      pb[hh * (D + 2) + D + 1] = L;
+    }
+  }
+}
+
+// Full-precision windows [0, nf) of the attended list; grid (nsf, U), four
+// waves per workgroup each on a contiguous range.  Partials at slots
+// [0, nsf) of the unit's nsplit.
+template <int D, bool MASS>
+__global__ __launch_bounds__(256) void attend_full_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kf,
+    const uint16_t* __restrict__ vf, const int32_t* __restrict__ items, int nW, int T, int Hq,
+    int Hkv, int G, int nf, int nsplit, float* __restrict__ part, float2* __restrict__ wstat) {
+  constexpr int KB = D / 32;
+  constexpr int CB = D / 16;
+  const int u = blockIdx.y;
+  const int b = u / Hkv;
+  const int h = u - b * Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int nv = gridDim.x * 4;
+  const int v = blockIdx.x * 4 + wave;
+  const int k0 = static_cast<int>(static_cast<long long>(nf) * v / nv);
+  const int k1 = static_cast<int>(static_cast<long long>(nf) * (v + 1) / nv);
+  QOperand<D> qo;
+  qo.load(q, (static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G) * D, lane, G);
+  const float sl = kLog2e / sqrtf(static_cast<float>(D));
+  SoftState<D> st;
+  st.init();
+  for (int k = k0; k < k1; ++k) {
+    // the routing kernel only lists windows < nW; the clamp keeps a bad entry in bounds
+    const int w = min(max(items[static_cast<size_t>(u) * nW + k], 0), nW - 1);
+    const int nvalid = min(kRows, T - w * kRows);
+    const size_t wb = static_cast<size_t>(u) * nW + w;
+    const uint16_t* kt = kf + wb * kRows * D + lane * 8;
+    const uint16_t* vt = vf + wb * kRows * D + lane * 8;
+    u32x4 ka[4][KB], va[2][CB];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        ka[rb][kb] = *reinterpret_cast<const u32x4*>(kt + (rb * KB + kb) * 512);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        va[rb][cb] = *reinterpret_cast<const u32x4*>(vt + (rb * CB + cb) * 512);
+    float s[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 c{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) c = mma(as8(ka[rb][kb]), qo.qb[kb], c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[rb][i] = c[i] * sl;
+    }
+    st.template update<MASS>(s, nvalid, g, g == 0 && n < G,
+                             wstat + (static_cast<size_t>(u) * nW + k) * G + n);
     // PV: A = values (column 16 cb + n, rows v32_row(g, .)), B = p (head n)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -307,95 +346,153 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(
         pp[e] = s[2 * rb][e];
         pp[4 + e] = s[2 * rb + 1][e];
       }
-      if (full) {
-        bf16x8 hi, lo;
-        split8(pp, hi, lo);
-        const uint16_t* vt = vf + wb * kRows * D + lane * 8;
-        u32x4 va[CB];
+      bf16x8 hi, lo;
+      split8(pp, hi, lo);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          va[cb] = *reinterpret_cast<const u32x4*>(vt + (rb * CB + cb) * 512);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          acc[cb] = mma(as8(va[cb]), hi, acc[cb]);
-          acc[cb] = mma(as8(va[cb]), lo, acc[cb]);
-        }
-      } else {
-        // rows v32_row(g, e) of block rb: [e][grp][scale, min]
-        float sc[8 * NG * 2];
-#pragma unroll
-        for (int x = 0; x < 4 * NG; ++x) {
-          const float4 t4 = *reinterpret_cast<const float4*>(qv + (rb * 4 + g) * 16 * NG + 4 * x);
-          sc[4 * x] = t4.x;
-          sc[4 * x + 1] = t4.y;
-          sc[4 * x + 2] = t4.z;
-          sc[4 * x + 3] = t4.w;
-        }
-        bf16x8 hi[NG], lo[NG];
-#pragma unroll
-        for (int x = 0; x < NG; ++x) {
-          float pw[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pw[e] = pp[e] * sc[(e * NG + x) * 2];
-            amn[x] += pp[e] * sc[(e * NG + x) * 2 + 1];
-          }
-          split8(pw, hi[x], lo[x]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int o = rb * CB + cb;
-          const int t = o >> 1;
-          const bf16x8 a = decode8(vw[t >> 2][t & 3], o & 1);
-          acc[cb] = mma(a, hi[cb >> 2], acc[cb]);
-          acc[cb] = mma(a, lo[cb >> 2], acc[cb]);
-        }
+      for (int cb = 0; cb < CB; ++cb) {
+        st.acc[cb] = mma(as8(va[rb][cb]), hi, st.acc[cb]);
+        st.acc[cb] = mma(as8(va[rb][cb]), lo, st.acc[cb]);
       }
     }
   }
-  // minima terms of the INT2 values, summed over the lane groups' rows
-#pragma unroll
-  for (int x = 0; x < NG; ++x) {
-    amn[x] += __shfl_xor(amn[x], 16, kWave);
-    amn[x] += __shfl_xor(amn[x], 32, kWave);
-  }
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[cb][i] += amn[cb >> 2];
+  __shared__ float mbuf[8 * kMaxG + 4 * kMaxG * D];
+  block_partial<D>(st, mbuf, G,
+                   part + (static_cast<size_t>(u) * nsplit + blockIdx.x) * G * (D + 2));
+}
 
-  // merge the four waves
-  __shared__ float sm[4][kMaxG], sl4[4][kMaxG];
-  __shared__ float so[4][kMaxG][D];
-  if (g == 0) {
-    sm[wave][n] = m * kLn2;  // back to natural-log units for the merge
-    sl4[wave][n] = l;
-  }
+// INT2 windows [nf, nit) of the attended list; grid (nsq, U).  Each wave
+// stages a window's scales and minima (256 (d / 64) floats) in its own LDS
+// area with coalesced loads and reads them back as broadcasts.  Partials
+// at slots [split0, split0 + nsq).  The path is VALU-bound (code widening,
+// scale arithmetic, softmax); three waves per SIMD measured fastest (two
+// leave issue slots idle, four spill).
+template <int D, bool MASS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attend_int2_kernel(
+    const uint16_t* __restrict__ q, const uint32_t* __restrict__ codes,
+    const float* __restrict__ qsc, const int32_t* __restrict__ items, int nW, int T, int Hq,
+    int Hkv, int G, int nf, int nit, int split0, int nsplit, float* __restrict__ part,
+    float2* __restrict__ wstat) {
+  constexpr int NG = D / kGroup;
+  constexpr int KB = D / 32;
+  constexpr int CB = D / 16;
+  constexpr int SQ4 = 64 * NG;  // float4 of scales per window
+  const int u = blockIdx.y;
+  const int b = u / Hkv;
+  const int h = u - b * Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int nq = nit - nf;
+  const int nv = gridDim.x * 4;
+  const int v = blockIdx.x * 4 + wave;
+  const int k0 = nf + static_cast<int>(static_cast<long long>(nq) * v / nv);
+  const int k1 = nf + static_cast<int>(static_cast<long long>(nq) * (v + 1) / nv);
+  QOperand<D> qo;
+  qo.load(q, (static_cast<size_t>(b) * Hq + static_cast<size_t>(h) * G) * D, lane, G);
+  const float sl = kLog2e / sqrtf(static_cast<float>(D));
+  SoftState<D> st;
+  st.init();
+  // per wave: two staging areas of one window's scales (alternating), later
+  // reused by the workgroup merge
+  constexpr int kStage = 4 * 2 * SQ4 * 4;
+  constexpr int kMerge = 8 * kMaxG + 4 * kMaxG * D;
+  __shared__ float lds[kStage > kMerge ? kStage : kMerge];
+  float4* stage = reinterpret_cast<float4*>(lds) + wave * 2 * SQ4;
+  for (int k = k0; k < k1; ++k) {
+    const int w = min(max(items[static_cast<size_t>(u) * nW + k], 0), nW - 1);
+    const int nvalid = min(kRows, T - w * kRows);
+    const size_t wb = static_cast<size_t>(u) * nW + w;
+    const uint32_t* cw = codes + wb * (8 * D);
+    u32x4 kw[NG], vw[NG];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+    for (int p = 0; p < NG; ++p) {
+      kw[p] = *reinterpret_cast<const u32x4*>(cw + (p * 64 + lane) * 4);
+      vw[p] = *reinterpret_cast<const u32x4*>(cw + 4 * D + (p * 64 + lane) * 4);
+    }
+    float4* sq = stage + (k & 1) * SQ4;
+    {
+      const float4* src = reinterpret_cast<const float4*>(qsc + wb * (256 * NG));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) so[wave][n][cb * 16 + 4 * g + i] = acc[cb][i];
-  __syncthreads();
-  float* pb = part + (static_cast<size_t>(u) * nsplit + blockIdx.x) * G * (D + 2);
-  for (int e = tid; e < G * D; e += 256) {
-    const int hh = e / D;
-    const int c = e - hh * D;
-    const float M = fmaxf(fmaxf(sm[0][hh], sm[1][hh]), fmaxf(sm[2][hh], sm[3][hh]));
-    float o = 0.f, L = 0.f;
-    if (M != -INFINITY) {
+      for (int x = 0; x < NG; ++x) sq[x * 64 + lane] = src[x * 64 + lane];
+    }
+    // LDS operations of a wave complete in order: the reads below see the
+    // whole block
+    float s[4][4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float f = sm[x][hh] == -INFINITY ? 0.f : __expf(sm[x][hh] - M);
-        o += f * so[x][hh][c];
-        L += f * sl4[x][hh];
+    for (int rb = 0; rb < 4; ++rb) {
+      // rows 16 rb + 4 g + i: [i][grp][scale, min]
+      float sc[8 * NG];
+#pragma unroll
+      for (int x = 0; x < 2 * NG; ++x) {
+        const float4 t4 = sq[(rb * 16 + 4 * g) * NG / 2 + x];
+        sc[4 * x] = t4.x;
+        sc[4 * x + 1] = t4.y;
+        sc[4 * x + 2] = t4.z;
+        sc[4 * x + 3] = t4.w;
+      }
+      f32x4 cg[NG];
+#pragma unroll
+      for (int x = 0; x < NG; ++x) cg[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int o = rb * KB + kb;
+        const int t = o >> 1;
+        cg[kb / 2] = mma(decode8(kw[t >> 2][t & 3], o & 1), qo.qb[kb], cg[kb / 2]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float z = 0.f;
+#pragma unroll
+        for (int x = 0; x < NG; ++x)
+          z += sc[(i * NG + x) * 2] * cg[x][i] + sc[(i * NG + x) * 2 + 1] * qo.qsum[x];
+        s[rb][i] = z * sl;
       }
     }
-    pb[hh * (D + 2) + c] = o;
-    if (c == 0) {
-      pb[hh * (D + 2) + D] = M;
-      pb[hh * (D + 2) + D + 1] = L;
+    st.template update<MASS>(s, nvalid, g, g == 0 && n < G,
+                             wstat + (static_cast<size_t>(u) * nW + k) * G + n);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float pp[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pp[e] = s[2 * rb][e];
+        pp[4 + e] = s[2 * rb + 1][e];
+      }
+      // rows v32_row(g, e) of block rb: [e][grp][scale, min]
+      float sc[16 * NG];
+#pragma unroll
+      for (int x = 0; x < 4 * NG; ++x) {
+        const float4 t4 = sq[32 * NG + (rb * 4 + g) * 4 * NG + x];
+        sc[4 * x] = t4.x;
+        sc[4 * x + 1] = t4.y;
+        sc[4 * x + 2] = t4.z;
+        sc[4 * x + 3] = t4.w;
+      }
+      bf16x8 hi[NG], lo[NG];
+#pragma unroll
+      for (int x = 0; x < NG; ++x) {
+        float pw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pw[e] = pp[e] * sc[(e * NG + x) * 2];
+          st.amn[x] += pp[e] * sc[(e * NG + x) * 2 + 1];
+        }
+        split8(pw, hi[x], lo[x]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int o = rb * CB + cb;
+        const int t = o >> 1;
+        const bf16x8 a = decode8(vw[t >> 2][t & 3], o & 1);
+        st.acc[cb] = mma(a, hi[cb >> 2], st.acc[cb]);
+        st.acc[cb] = mma(a, lo[cb >> 2], st.acc[cb]);
+      }
     }
   }
+  block_partial<D>(st, lds, G,
+                   part + (static_cast<size_t>(u) * nsplit + split0 + blockIdx.x) * G * (D + 2));
 }
 
 // --------------------------------------------------------- attention (VALU)
@@ -674,21 +771,29 @@ __global__ __launch_bounds__(1024) void route_kernel(
 
 // ---------------------------------------------------------- transitions
 
+// One workgroup per listed window at a time.  A side (K, then V) of the
+// window's full-precision block, contiguous in the tiled store, is staged in
+// LDS with 16-byte loads (code_elem maps a tile slot to its row and column),
+// then quantised row by row (quantise) or rebuilt from the ledger and
+// written back with 16-byte stores (promote).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void transition_kernel(
     typename Elem<DT>::T* __restrict__ kf, typename Elem<DT>::T* __restrict__ vf,
     uint32_t* __restrict__ codes, float* __restrict__ qsc, uint8_t* __restrict__ has_code,
     const int32_t* __restrict__ trans, const int32_t* __restrict__ ntrans, int nW) {
   typedef Elem<DT> E;
+  typedef typename Elem<DT>::T T;
   constexpr int NG = D / kGroup;
   constexpr int SQ = 256 * NG;
-  constexpr int WPS = 64 * (D / 16);  // code words per side
+  constexpr int WPS = 64 * (D / 16);   // code words per side
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CH = kRows * D / EPC;  // chunks per side of a window
   const int u = blockIdx.y;
   const int tid = threadIdx.x;
   const int nq = ntrans[u * 2];
   const int np = ntrans[u * 2 + 1];
-  __shared__ uint8_t cb[2][kRows][D];
-  const size_t ub = static_cast<size_t>(u) * nW * kRows * D;
+  __shared__ float xs[kRows][D + 1];
+  __shared__ uint8_t cb[kRows][D];
   for (int idx = blockIdx.x; idx < nq + np; idx += gridDim.x) {
     const bool quant = idx < nq;
     const int w = quant ? trans[(static_cast<size_t>(u) * 2) * nW + idx]
@@ -696,88 +801,92 @@ __global__ __launch_bounds__(256) void transition_kernel(
     const size_t wb = static_cast<size_t>(u) * nW + w;
     uint32_t* cw = codes + wb * (8 * D);
     float* qw = qsc + wb * SQ;
-    if (quant) {
-      // one (side, row, group) per thread: minimum, maximum, scale, codes
-      for (int task = tid; task < 2 * kRows * NG; task += 256) {
-        const int side = task / (kRows * NG);
-        const int rem = task - side * kRows * NG;
-        const int r = rem / NG;
-        const int grp = rem - r * NG;
-        const typename E::T* src = side == 0 ? kf : vf;
-        float x[kGroup];
-        float mn = INFINITY, mx = -INFINITY;
+    for (int side = 0; side < 2; ++side) {
+      T* tile = (side == 0 ? kf : vf) + wb * kRows * D;
+      if (quant) {
+        for (int ch = tid; ch < CH; ch += 256) {
+          const uint4 raw = reinterpret_cast<const uint4*>(tile)[ch];
+          const T* el = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-          const int c = grp * kGroup + j;
-          const size_t o = ub + (side == 0 ? k16_off(w * kRows + r, c, D) : v32_off(w * kRows + r, c, D));
-          x[j] = E::ld(src, o);
-          mn = fminf(mn, x[j]);
-          mx = fmaxf(mx, x[j]);
-        }
-        const float sc = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-          int code = 0;
-          if (sc > 0.f) {
-            const float t = rintf(__fdiv_rn(__fsub_rn(x[j], mn), sc));
-            code = static_cast<int>(fminf(fmaxf(t, 0.f), 3.f));
+          for (int j = 0; j < EPC; ++j) {
+            const int o = ch * EPC + j;
+            int r, c;
+            code_elem(side, o >> 9, (o >> 3) & 63, o & 7, D, &r, &c);
+            xs[r][c] = E::ld(el, j);
           }
-          cb[side][r][grp * kGroup + j] = static_cast<uint8_t>(code);
         }
-        qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)] = sc;
-        qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)] = mn;
+        __syncthreads();
+        // one (row, group) per thread: minimum, maximum, scale, codes
+        for (int task = tid; task < kRows * NG; task += 256) {
+          const int r = task / NG;
+          const int grp = task - r * NG;
+          float mn = INFINITY, mx = -INFINITY;
+          for (int j = 0; j < kGroup; ++j) {
+            const float x = xs[r][grp * kGroup + j];
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+          }
+          const float sc = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
+          for (int j = 0; j < kGroup; ++j) {
+            int code = 0;
+            if (sc > 0.f) {
+              const float t = rintf(__fdiv_rn(__fsub_rn(xs[r][grp * kGroup + j], mn), sc));
+              code = static_cast<int>(fminf(fmaxf(t, 0.f), 3.f));
+            }
+            cb[r][grp * kGroup + j] = static_cast<uint8_t>(code);
+          }
+          qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)] = sc;
+          qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)] = mn;
+        }
+        __syncthreads();
+        for (int wd = tid; wd < WPS; wd += 256) {
+          const int lane = wd / (D / 16);
+          const int t = wd - lane * (D / 16);
+          uint32_t x = 0;
+#pragma unroll
+          for (int oh = 0; oh < 2; ++oh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              int r, c;
+              code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
+              x |= static_cast<uint32_t>(cb[r][c]) << (4 * j + 2 * oh);
+            }
+          cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)] = x;
+        }
+      } else {
+        for (int wd = tid; wd < WPS; wd += 256) {
+          const int lane = wd / (D / 16);
+          const int t = wd - lane * (D / 16);
+          const uint32_t x = cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)];
+#pragma unroll
+          for (int oh = 0; oh < 2; ++oh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              int r, c;
+              code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
+              cb[r][c] = static_cast<uint8_t>((x >> (4 * j + 2 * oh)) & 3u);
+            }
+        }
+        __syncthreads();
+        for (int ch = tid; ch < CH; ch += 256) {
+          uint4 raw;
+          T* el = reinterpret_cast<T*>(&raw);
+#pragma unroll
+          for (int j = 0; j < EPC; ++j) {
+            const int o = ch * EPC + j;
+            int r, c;
+            code_elem(side, o >> 9, (o >> 3) & 63, o & 7, D, &r, &c);
+            const int grp = c / kGroup;
+            const float sc = qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)];
+            const float mn = qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)];
+            el[j] = E::from_f32(dequant(static_cast<float>(cb[r][c]), sc, mn));
+          }
+          reinterpret_cast<uint4*>(tile)[ch] = raw;
+        }
       }
       __syncthreads();
-      for (int wd = tid; wd < 2 * WPS; wd += 256) {
-        const int side = wd / WPS;
-        const int rem = wd - side * WPS;
-        const int lane = rem / (D / 16);
-        const int t = rem - lane * (D / 16);
-        uint32_t x = 0;
-#pragma unroll
-        for (int oh = 0; oh < 2; ++oh)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            int r, c;
-            code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
-            x |= static_cast<uint32_t>(cb[side][r][c]) << (4 * j + 2 * oh);
-          }
-        cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)] = x;
-      }
-      if (tid == 0) has_code[wb] = 1;
-    } else {
-      for (int wd = tid; wd < 2 * WPS; wd += 256) {
-        const int side = wd / WPS;
-        const int rem = wd - side * WPS;
-        const int lane = rem / (D / 16);
-        const int t = rem - lane * (D / 16);
-        const uint32_t x = cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)];
-#pragma unroll
-        for (int oh = 0; oh < 2; ++oh)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            int r, c;
-            code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
-            cb[side][r][c] = static_cast<uint8_t>((x >> (4 * j + 2 * oh)) & 3u);
-          }
-      }
-      __syncthreads();
-      for (int e = tid; e < 2 * kRows * D; e += 256) {
-        const int side = e / (kRows * D);
-        const int rem = e - side * kRows * D;
-        const int r = rem / D;
-        const int c = rem - r * D;
-        const int grp = c / kGroup;
-        const float sc = qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)];
-        const float mn = qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)];
-        const float val = dequant(static_cast<float>(cb[side][r][c]), sc, mn);
-        if (side == 0)
-          kf[ub + k16_off(w * kRows + r, c, D)] = E::from_f32(val);
-        else
-          vf[ub + v32_off(w * kRows + r, c, D)] = E::from_f32(val);
-      }
     }
-    __syncthreads();
+    if (quant && tid == 0) has_code[wb] = 1;
   }
 }
 
@@ -787,7 +896,9 @@ hipError_t decode_impl(const rskv_window* W, const void* qv, float* out, bool ev
   typedef typename Elem<DT>::T T;
   const int U = W->B * W->Hkv;
   const int nit = nf + nq;
-  const int nsplit = attend_nsplit(W, nf, nit);
+  int nsf = 0, nsq = 0;
+  attend_splits(W, nf, nq, &nsf, &nsq);
+  const int nsplit = nsf + nsq;
   auto E = [&](int k) -> const KernelEvents* {
     if (recorded) recorded[k] = true;
     return ev ? ev + k : nullptr;
@@ -797,58 +908,72 @@ hipError_t decode_impl(const rskv_window* W, const void* qv, float* out, bool ev
   const T* q = static_cast<const T*>(qv);
   const T* kf = static_cast<const T*>(W->kf);
   const T* vf = static_cast<const T*>(W->vf);
-  hipError_t e;
-  const dim3 grid(nsplit, U);
+  const uint32_t* codes = W->codes;
+  const float* qsc = W->qsc;
+  const int32_t* items = W->items;
+  hipError_t e = hipSuccess;
   if constexpr (DT == kBF16) {
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
     const uint16_t* k16 = reinterpret_cast<const uint16_t*>(kf);
     const uint16_t* v16 = reinterpret_cast<const uint16_t*>(vf);
-    if (event)
-      e = launch(attend_mfma_kernel<D, true>, grid, dim3(256), 0, st, E(0), q16, k16, v16,
-                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
-                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
-                 nsplit, W->part, W->wstat);
-    else
-      e = launch(attend_mfma_kernel<D, false>, grid, dim3(256), 0, st, E(0), q16, k16, v16,
-                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
-                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
-                 nsplit, W->part, W->wstat);
+    if (nsf > 0) {
+      if (event)
+        e = launch(attend_full_kernel<D, true>, dim3(nsf, U), dim3(256), 0, st, E(0), q16, k16, v16,
+                   items, W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nsplit, W->part, W->wstat);
+      else
+        e = launch(attend_full_kernel<D, false>, dim3(nsf, U), dim3(256), 0, st, E(0), q16, k16,
+                   v16, items, W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nsplit, W->part, W->wstat);
+      if (e != hipSuccess) return e;
+    }
+    if (nsq > 0) {
+      if (event)
+        e = launch(attend_int2_kernel<D, true>, dim3(nsq, U), dim3(256), 0, st, E(1), q16, codes,
+                   qsc, items, W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit, nsf, nsplit, W->part,
+                   W->wstat);
+      else
+        e = launch(attend_int2_kernel<D, false>, dim3(nsq, U), dim3(256), 0, st, E(1), q16, codes,
+                   qsc, items, W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit, nsf, nsplit, W->part,
+                   W->wstat);
+      if (e != hipSuccess) return e;
+    }
   } else {
     if (event)
-      e = launch(attend_valu_kernel<DT, D, true>, grid, dim3(256), 0, st, E(0), q, kf, vf,
-                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
-                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
-                 nsplit, W->part, W->wstat);
+      e = launch(attend_valu_kernel<DT, D, true>, dim3(nsplit, U), dim3(256), 0, st, E(0), q, kf, vf,
+                 codes, qsc, items, W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit, nsplit, W->part,
+                 W->wstat);
     else
-      e = launch(attend_valu_kernel<DT, D, false>, grid, dim3(256), 0, st, E(0), q, kf, vf,
-                 static_cast<const uint32_t*>(W->codes), static_cast<const float*>(W->qsc),
-                 static_cast<const int32_t*>(W->items), W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit,
-                 nsplit, W->part, W->wstat);
+      e = launch(attend_valu_kernel<DT, D, false>, dim3(nsplit, U), dim3(256), 0, st, E(0), q, kf,
+                 vf, codes, qsc, items, W->nW, W->T, W->Hq, W->Hkv, W->G, nf, nit, nsplit, W->part,
+                 W->wstat);
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
   if (event)
-    e = launch(merge_kernel<D, true>, dim3(W->G, U), dim3(D), 0, st, E(1),
+    e = launch(merge_kernel<D, true>, dim3(W->G, U), dim3(D), 0, st, E(2),
                static_cast<const float*>(W->part), nsplit, W->G, W->Hq, W->Hkv, out, W->hstat);
   else
-    e = launch(merge_kernel<D, false>, dim3(W->G, U), dim3(D), 0, st, E(1),
+    e = launch(merge_kernel<D, false>, dim3(W->G, U), dim3(D), 0, st, E(2),
                static_cast<const float*>(W->part), nsplit, W->G, W->Hq, W->Hkv, out, W->hstat);
   if (e != hipSuccess || !event) return e;
   const float2* ws = W->wstat;
   const float2* hs = W->hstat;
 #define RSKV_ROUTE(NP)                                                                         \
-  launch(route_kernel<NP>, dim3(U), dim3(1024), 0, st, E(2), ws, hs, W->G, W->nW, nit,         \
+  launch(route_kernel<NP>, dim3(U), dim3(1024), 0, st, E(3), ws, hs, W->G, W->nW, nit,         \
          W->n_full, W->n_quant, W->items, W->tier, W->score, W->mass,                           \
          static_cast<const uint8_t*>(W->has_code), W->trans, W->ntrans)
   if (W->nW <= 1024)
     e = RSKV_ROUTE(1024);
+  else if (W->nW <= 2048)
+    e = RSKV_ROUTE(2048);
   else if (W->nW <= 4096)
     e = RSKV_ROUTE(4096);
+  else if (W->nW <= 8192)
+    e = RSKV_ROUTE(8192);
   else
     e = RSKV_ROUTE(16384);
 #undef RSKV_ROUTE
   if (e != hipSuccess) return e;
   const int nb = std::max(1, std::min(64, W->nW));
-  return launch(transition_kernel<DT, D>, dim3(nb, U), dim3(256), 0, st, E(3),
+  return launch(transition_kernel<DT, D>, dim3(nb, U), dim3(256), 0, st, E(4),
                 static_cast<T*>(W->kf), static_cast<T*>(W->vf), W->codes, W->qsc, W->has_code,
                 static_cast<const int32_t*>(W->trans), static_cast<const int32_t*>(W->ntrans), W->nW);
 }
@@ -867,15 +992,23 @@ hipError_t build_impl(const rskv_window* W, const void* K, const void* V, hipStr
 
 }  // namespace
 
-int attend_nsplit(const rskv_window* W, int nf, int nit) {
-  const long long cost = static_cast<long long>(kCostFull) * nf + static_cast<long long>(kCostQuant) * (nit - nf);
+void attend_splits(const rskv_window* W, int nf, int nq, int* nsf, int* nsq) {
   const int U = W->B * W->Hkv;
-  // ranges of at least one full window's cost, about kTargetWaves waves in all
+  if (W->dtype == RSKV_BF16) {
+    // one wave per window at most; about 4096 waves of the full-window
+    // kernel (two resident per SIMD) and 8192 of the INT2 one in all
+    const int wf = std::min(nf, (4096 + U - 1) / U);
+    const int wq = std::min(nq, (8192 + U - 1) / U);
+    *nsf = (wf + 3) / 4;
+    *nsq = (wq + 3) / 4;
+    return;
+  }
+  // block-cooperative kernel: one range per workgroup, ranges of at least
+  // one full window's cost
+  const long long cost = static_cast<long long>(kCostFull) * nf + static_cast<long long>(kCostQuant) * nq;
   long long waves = std::min<long long>((cost + kCostFull - 1) / kCostFull, (kTargetWaves + U - 1) / U);
-  waves = std::max<long long>(waves, 1);
-  const bool mfma = W->dtype == RSKV_BF16;
-  // the MFMA kernel gives each of its four waves a range, the VALU kernel one per workgroup
-  return static_cast<int>(mfma ? (waves + 3) / 4 : waves);
+  *nsf = static_cast<int>(std::max<long long>(waves, 1));
+  *nsq = 0;
 }
 
 hipError_t launch_build(const rskv_window* W, const void* K, const void* V, hipStream_t st) {

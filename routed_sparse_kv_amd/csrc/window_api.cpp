@@ -129,7 +129,10 @@ int rskv_window_build(const void* K, const void* V, const rskv_window_opts* o, v
     w->nq_next = 0;
     const int nf1 = std::min(w->n_full, w->nW);
     const int nq1 = std::min(w->n_quant, w->nW - nf1);
-    w->nsplit_max = std::max(W::attend_nsplit(w, w->nW, w->nW), W::attend_nsplit(w, nf1, nf1 + nq1));
+    int a0, b0, a1, b1;
+    W::attend_splits(w, w->nW, 0, &a0, &b0);
+    W::attend_splits(w, nf1, nq1, &a1, &b1);
+    w->nsplit_max = std::max(a0 + b0, a1 + b1);
 
     const size_t U = static_cast<size_t>(w->B) * w->Hkv;
     const size_t nW = static_cast<size_t>(w->nW);
@@ -248,7 +251,9 @@ int rskv_window_info_get(const rskv_window* w, rskv_window_info* i) {
   i->step = w->step;
   i->next_full = w->nf_next;
   i->next_quant = w->nq_next;
-  i->next_splits = W::attend_nsplit(w, w->nf_next, w->nf_next + w->nq_next);
+  int a, b;
+  W::attend_splits(w, w->nf_next, w->nq_next, &a, &b);
+  i->next_splits = a + b;
   i->full_bytes = static_cast<int32_t>(2 * W::kRows * w->d * esize(w->dtype));
   i->quant_bytes = static_cast<int32_t>(W::code_words(w->d) * 4 + W::scale_floats(w->d) * 4);
   i->device_bytes = w->bytes;

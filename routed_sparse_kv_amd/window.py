@@ -38,11 +38,11 @@ class WindowState(C.Structure):
 
 
 class WindowProfile(C.Structure):
-    _fields_ = [("steps", C.c_int64), ("events", C.c_int64), ("ms", C.c_double * 4)]
+    _fields_ = [("steps", C.c_int64), ("events", C.c_int64), ("ms", C.c_double * 5)]
 
 
-#: Names of the four decode launches, in the order of WindowProfile.ms.
-KERNELS = ("attend", "merge", "route", "transition")
+#: Names of the decode launches, in the order of WindowProfile.ms.
+KERNELS = ("attend_full", "attend_int2", "merge", "route", "transition")
 
 _ready = False
 
