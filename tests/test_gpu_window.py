@@ -52,6 +52,10 @@ CASES = {
     "route_every_step": ("gqa_32k_bf16", dict(B=1, Hq=8, Hkv=2, T=1500, steps=10),
                          dict(counts=(3, 6)), 1, 10),
     "short_context": ("tiny_fp32_2k", dict(T=40, Hq=2, steps=3), dict(counts=(0, 1)), 1, 3),
+    # every window holds the same K/V: all masses tie exactly and the
+    # ranking falls back to the window index
+    "tied_windows": ("gqa_32k_bf16", dict(B=1, Hq=4, Hkv=1, T=1024, steps=3), dict(counts=(4, 5),
+                                                                                  tile=64), 1, 3),
 }
 
 
@@ -166,6 +170,11 @@ def run_case(wl, n_full, n_quant, R, steps, units=None, check_store=True):
 def test_window_parity(case):
     name, over, spec, R, steps = CASES[case]
     wl = W.generate(name, **over)
+    if "tile" in spec:  # repeat the first `tile` positions over the whole context
+        t = spec["tile"]
+        reps = -(-wl.cfg["T"] // t)
+        wl.K[...] = np.tile(wl.K[:, :, :t], (1, 1, reps, 1))[:, :, :wl.cfg["T"]]
+        wl.V[...] = np.tile(wl.V[:, :, :t], (1, 1, reps, 1))[:, :, :wl.cfg["T"]]
     n_full, n_quant = tiers_for(wl.cfg, spec)
     say(f"case {case}: T={wl.cfg['T']} d={wl.cfg['d']} G={wl.cfg['Hq'] // wl.cfg['Hkv']} "
         f"n_full={n_full} n_quant={n_quant} R={R}")

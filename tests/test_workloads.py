@@ -54,3 +54,23 @@ def test_small_variants(name):
         assert len(wl.appends) == cfg["steps"]
     if cfg["P"] == "gauss":
         assert wl.P.shape == (1, cfg["d"], cfg["d"])
+
+
+def test_window_budget_counts():
+    """The window tiers fill the byte budget: n_full is the full share of
+    the budget in whole windows; n_quant INT2 windows (codes, and an fp32
+    scale and minimum per row and 64-column group, for K and V) fit in the
+    rest; one more INT2 window would exceed it."""
+    from routed_sparse_kv_amd import workloads as W
+    for T, d, dt, budget, share in ((131072, 128, "bf16", 0.2, 0.5), (32768, 128, "bf16", 0.05, 0.5),
+                                    (2065, 64, "f32", 0.2, 0.5), (5000, 64, "bf16", 0.1, 0.25)):
+        nw = -(-T // 64)
+        full_b = 2 * 64 * d * (2 if dt == "bf16" else 4)
+        quant_b = 2 * 64 * d // 4 + 2 * 64 * (d // 64) * 8
+        nf, nq = W.window_tiers(T, d, dt, budget, share)
+        assert nf == int(share * budget * nw)
+        total = budget * nw * full_b
+        assert nf * full_b + nq * quant_b <= total + 1e-9
+        assert nf * full_b + (nq + 1) * quant_b > total
+    assert W.window_tiers(100, 128, "bf16", 0.0, 0.5) == (1, 0)
+    assert W.window_tiers(131072, 128, "bf16", 0.2, 0.5) == (204, 1096)
