@@ -734,23 +734,68 @@ __global__ __launch_bounds__(1024) void route_kernel(
     key[w] = kk;
   }
   __syncthreads();
-  // bitonic sort, ascending
+  // bitonic sort, ascending.  Thread t holds elements t + 1024 r (r <
+  // NP / 1024, at least one).  Partners at stride j < 64 sit in the same
+  // wave (wave shuffles), at j >= 1024 in the same thread (registers); only
+  // strides 64..512 go through LDS.
+  constexpr int NR = NP >= 1024 ? NP / 1024 : 1;
+  const int lane = tid & 63;
+  unsigned long long v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) v[r] = tid + 1024 * r < NP ? key[tid + 1024 * r] : ~0ull;
   for (int kk = 2; kk <= NP; kk <<= 1) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < NP; i += 1024) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long a = key[i], c = key[ixj];
-          const bool up = (i & kk) == 0;
-          if ((a > c) == up) {
-            key[i] = c;
-            key[ixj] = a;
+      if (j >= 1024) {
+        const int jr = j / 1024;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int i = tid + 1024 * r;
+          if ((r & jr) == 0) {
+            const bool up = (i & kk) == 0;
+            const unsigned long long a = v[r], c = v[r | jr];
+            if ((a > c) == up) {
+              v[r] = c;
+              v[r | jr] = a;
+            }
           }
         }
+      } else if (j >= 64) {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          if (tid + 1024 * r < NP) key[tid + 1024 * r] = v[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int i = tid + 1024 * r;
+          if (i < NP) {
+            const unsigned long long c = key[i ^ j];
+            const bool up = (i & kk) == 0;
+            const bool lower = (i & j) == 0;  // i is the first of its pair
+            // the pair's first element keeps the smaller key when ascending
+            const bool take = lower == up ? c < v[r] : c > v[r];
+            if (take) v[r] = c;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int i = tid + 1024 * r;
+          const unsigned long long c = static_cast<unsigned long long>(
+              __shfl_xor(static_cast<long long>(v[r]), j, kWave));
+          const bool up = (i & kk) == 0;
+          const bool lower = (lane & j) == 0;
+          const bool take = lower == up ? c < v[r] : c > v[r];
+          if (take) v[r] = c;
+        }
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    if (tid + 1024 * r < NP) key[tid + 1024 * r] = v[r];
+  __syncthreads();
   for (int pos = tid; pos < nW; pos += 1024) {
     const unsigned long long kk = key[pos];
     if (kk == ~0ull) continue;
@@ -794,6 +839,7 @@ __global__ __launch_bounds__(256) void transition_kernel(
   const int np = ntrans[u * 2 + 1];
   __shared__ float xs[kRows][D + 1];
   __shared__ uint8_t cb[kRows][D];
+  __shared__ float qs[SQ];  // a promoted window's scales and minima
   for (int idx = blockIdx.x; idx < nq + np; idx += gridDim.x) {
     const bool quant = idx < nq;
     const int w = quant ? trans[(static_cast<size_t>(u) * 2) * nW + idx]
@@ -801,6 +847,10 @@ __global__ __launch_bounds__(256) void transition_kernel(
     const size_t wb = static_cast<size_t>(u) * nW + w;
     uint32_t* cw = codes + wb * (8 * D);
     float* qw = qsc + wb * SQ;
+    if (!quant) {
+      for (int i = tid; i < SQ; i += 256) qs[i] = qw[i];
+      // (the barrier after the code unpacking below orders these writes)
+    }
     for (int side = 0; side < 2; ++side) {
       T* tile = (side == 0 ? kf : vf) + wb * kRows * D;
       if (quant) {
@@ -877,8 +927,8 @@ __global__ __launch_bounds__(256) void transition_kernel(
             int r, c;
             code_elem(side, o >> 9, (o >> 3) & 63, o & 7, D, &r, &c);
             const int grp = c / kGroup;
-            const float sc = qw[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)];
-            const float mn = qw[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)];
+            const float sc = qs[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)];
+            const float mn = qs[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)];
             el[j] = E::from_f32(dequant(static_cast<float>(cb[r][c]), sc, mn));
           }
           reinterpret_cast<uint4*>(tile)[ch] = raw;
