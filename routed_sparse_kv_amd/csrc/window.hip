@@ -699,46 +699,77 @@ __global__ __launch_bounds__(1024) void route_kernel(
     int32_t* __restrict__ trans, int32_t* __restrict__ ntrans) {
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
+  constexpr int NR = NP >= 1024 ? NP / 1024 : 1;
   __shared__ unsigned long long key[NP];
+  __shared__ uint8_t ost[NP];  // old tier (bits 0-1), ledger flag (bit 2)
   __shared__ int cnt[2];
   const size_t ub = static_cast<size_t>(u) * nW;
+  // every independent load first: the state of this thread's windows
+  // w = tid + 1024 r and the masses of its attended windows k = tid + 1024 r
+  double sc0[NR];
+  int t0[NR], h0[NR], wk[NR];
+  double mk[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int w = tid + 1024 * r;
+    const bool in = w < nW;
+    sc0[r] = in ? score[ub + w] : 0.0;
+    t0[r] = in ? tier[ub + w] : RSKV_TIER_EVICTED;
+    h0[r] = in ? has_code[ub + w] : 0;
+    const int k = tid + 1024 * r;
+    wk[r] = -1;
+    mk[r] = 0.0;
+    if (k < nit) {
+      wk[r] = items[ub + k];
+      double ms = 0.0;
+      for (int hh = 0; hh < G; ++hh) {
+        const float2 ws = wstat[(ub + k) * G + hh];
+        const float2 hs = hstat[static_cast<size_t>(u) * G + hh];
+        ms += static_cast<double>(ws.y) * exp(static_cast<double>(ws.x) - static_cast<double>(hs.x)) /
+              static_cast<double>(hs.y);
+      }
+      mk[r] = ms;
+    }
+  }
   double* mw = reinterpret_cast<double*>(key);
-  for (int w = tid; w < NP; w += 1024) mw[w] = 0.0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int w = tid + 1024 * r;
+    if (w < NP) {
+      mw[w] = 0.0;
+      ost[w] = static_cast<uint8_t>((t0[r] & 3) | (h0[r] ? 4 : 0));
+    }
+  }
   if (tid < 2) cnt[tid] = 0;
   __syncthreads();
-  // masses of the attended windows
-  for (int k = tid; k < nit; k += 1024) {
-    const int w = items[ub + k];
-    double ms = 0.0;
-    for (int hh = 0; hh < G; ++hh) {
-      const float2 ws = wstat[(ub + k) * G + hh];
-      const float2 hs = hstat[static_cast<size_t>(u) * G + hh];
-      ms += static_cast<double>(ws.y) * exp(static_cast<double>(ws.x) - static_cast<double>(hs.x)) /
-            static_cast<double>(hs.y);
-    }
-    mw[w] = ms;
-  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    if (wk[r] >= 0 && wk[r] < nW) mw[wk[r]] = mk[r];
   __syncthreads();
-  for (int w = tid; w < NP; w += 1024) {
+  double msw[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) msw[r] = tid + 1024 * r < NP ? mw[tid + 1024 * r] : 0.0;
+  __syncthreads();  // mw aliases the keys written below
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int w = tid + 1024 * r;
     unsigned long long kk = ~0ull;
     if (w < nW) {
-      const double ms = mw[w];
-      mass[ub + w] = ms;
-      const double sc = score[ub + w] + ms;
+      mass[ub + w] = msw[r];
+      const double sc = sc0[r] + msw[r];
       score[ub + w] = sc;
-      if (tier[ub + w] != RSKV_TIER_EVICTED) {
+      if (t0[r] != RSKV_TIER_EVICTED) {
         const unsigned long long bits = static_cast<unsigned long long>(__double_as_longlong(sc));
         kk = (((~bits) >> 1) & ~0x3fffull) | static_cast<unsigned long long>(w);
       }
     }
-    key[w] = kk;
+    if (w < NP) key[w] = kk;
   }
   __syncthreads();
   // bitonic sort, ascending.  Thread t holds elements t + 1024 r (r <
   // NP / 1024, at least one).  Partners at stride j < 64 sit in the same
   // wave (wave shuffles), at j >= 1024 in the same thread (registers); only
   // strides 64..512 go through LDS.
-  constexpr int NR = NP >= 1024 ? NP / 1024 : 1;
   const int lane = tid & 63;
   unsigned long long v[NR];
 #pragma unroll
@@ -800,12 +831,12 @@ __global__ __launch_bounds__(1024) void route_kernel(
     const unsigned long long kk = key[pos];
     if (kk == ~0ull) continue;
     const int w = static_cast<int>(kk & 0x3fffull);
-    const int old = tier[ub + w];
+    const int old = ost[w] & 3;
     const int nt = pos < n_full ? RSKV_TIER_FULL
                    : pos < n_full + n_quant ? RSKV_TIER_INT2 : RSKV_TIER_EVICTED;
     tier[ub + w] = static_cast<int8_t>(nt);
     if (nt != RSKV_TIER_EVICTED) items[ub + pos] = w;
-    if (nt == RSKV_TIER_INT2 && old == RSKV_TIER_FULL && !has_code[ub + w])
+    if (nt == RSKV_TIER_INT2 && old == RSKV_TIER_FULL && !(ost[w] & 4))
       trans[(static_cast<size_t>(u) * 2) * nW + atomicAdd(&cnt[0], 1)] = w;
     if (nt == RSKV_TIER_FULL && old == RSKV_TIER_INT2)
       trans[(static_cast<size_t>(u) * 2 + 1) * nW + atomicAdd(&cnt[1], 1)] = w;
@@ -816,11 +847,12 @@ __global__ __launch_bounds__(1024) void route_kernel(
 
 // ---------------------------------------------------------- transitions
 
-// One workgroup per listed window at a time.  A side (K, then V) of the
-// window's full-precision block, contiguous in the tiled store, is staged in
-// LDS with 16-byte loads (code_elem maps a tile slot to its row and column),
-// then quantised row by row (quantise) or rebuilt from the ledger and
-// written back with 16-byte stores (promote).
+// One workgroup per listed window at a time.  Quantise: a side (K, then V)
+// of the window's full-precision block, contiguous in the tiled store, is
+// staged in LDS with 16-byte loads (code_elem maps a tile slot to its row
+// and column), quantised row by row and packed into ledger words.
+// Promote: each 16-byte chunk of the store is rebuilt from one ledger word
+// and the window's scales (staged in LDS) and written back.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void transition_kernel(
     typename Elem<DT>::T* __restrict__ kf, typename Elem<DT>::T* __restrict__ vf,
@@ -849,7 +881,7 @@ __global__ __launch_bounds__(256) void transition_kernel(
     float* qw = qsc + wb * SQ;
     if (!quant) {
       for (int i = tid; i < SQ; i += 256) qs[i] = qw[i];
-      // (the barrier after the code unpacking below orders these writes)
+      __syncthreads();
     }
     for (int side = 0; side < 2; ++side) {
       T* tile = (side == 0 ? kf : vf) + wb * kRows * D;
@@ -904,32 +936,27 @@ __global__ __launch_bounds__(256) void transition_kernel(
           cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)] = x;
         }
       } else {
-        for (int wd = tid; wd < WPS; wd += 256) {
-          const int lane = wd / (D / 16);
-          const int t = wd - lane * (D / 16);
-          const uint32_t x = cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)];
-#pragma unroll
-          for (int oh = 0; oh < 2; ++oh)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              int r, c;
-              code_elem(side, 2 * t + oh, lane, j, D, &r, &c);
-              cb[r][c] = static_cast<uint8_t>((x >> (4 * j + 2 * oh)) & 3u);
-            }
-        }
-        __syncthreads();
+        // a 16-byte chunk of the tiled store holds elements e0..e0+EPC-1 of
+        // tile slot (blk, lane): codes j = e of operand blk in that lane's
+        // ledger word
         for (int ch = tid; ch < CH; ch += 256) {
+          const int o0 = ch * EPC;
+          const int blk = o0 >> 9;
+          const int lane = (o0 >> 3) & 63;
+          const int t = blk >> 1;
+          const uint32_t word = cw[side * 4 * D + ((t >> 2) * 64 + lane) * 4 + (t & 3)];
           uint4 raw;
           T* el = reinterpret_cast<T*>(&raw);
 #pragma unroll
           for (int j = 0; j < EPC; ++j) {
-            const int o = ch * EPC + j;
+            const int e = (o0 & 7) + j;
             int r, c;
-            code_elem(side, o >> 9, (o >> 3) & 63, o & 7, D, &r, &c);
+            code_elem(side, blk, lane, e, D, &r, &c);
             const int grp = c / kGroup;
             const float sc = qs[side == 0 ? kq_off(r, grp, 0, D) : vq_off(r, grp, 0, D)];
             const float mn = qs[side == 0 ? kq_off(r, grp, 1, D) : vq_off(r, grp, 1, D)];
-            el[j] = E::from_f32(dequant(static_cast<float>(cb[r][c]), sc, mn));
+            const float code = static_cast<float>((word >> (4 * e + 2 * (blk & 1))) & 3u);
+            el[j] = E::from_f32(dequant(code, sc, mn));
           }
           reinterpret_cast<uint4*>(tile)[ch] = raw;
         }
