@@ -7,14 +7,19 @@
 //       straight from the K16 / V32 tiles, all loads of a window issued
 //       before its first product.
 //   attend_int2_kernel  bf16 caches, INT2 windows, same structure: the codes
-//       are widened to bf16 in registers (one packed fp4 conversion per code
-//       pair) and fed to the same MFMAs; the fp32 scales and minima,
-//       staged per wave in LDS, are applied around the products:
+//       are widened in registers (one packed fp4 conversion per code pair)
+//       and fed to 16x16x32 MFMAs; the fp32 scales and minima, staged per
+//       wave in LDS, are applied around the products:
 //         <q, k_r> = sum_grp scale_r,grp <q_grp, code_r,grp> + min_r,grp sum(q_grp)
 //         sum_r p_r v_r = sum_r (p_r scale_r,grp) code_r + sum_r p_r min_r,grp
-//       which is the dequantised arithmetic up to association.  fp32
-//       factors enter an MFMA as a bf16 hi + lo pair.  In both kernels the
-//       four waves of a workgroup merge in LDS and write one partial.
+//       which is the dequantised arithmetic up to association.  The QK
+//       product is exact (bf16 codes times the bf16 query, fp32 sums), so
+//       the logits, hence the masses that route the windows, keep fp32
+//       accuracy; in the PV product the weights p_r scale_r,grp enter as
+//       fp16 (relative rounding 2^-11, far inside the output tolerance of
+//       bf16 caches).  In the full-window kernel p enters as a bf16 hi + lo
+//       pair.  In both kernels the four waves of a workgroup merge in LDS
+//       and write one partial.
 //   attend_valu_kernel  fp32 caches: a block-cooperative fp32 version that
 //       dequantises INT2 rows exactly (mn + code * scale, two roundings).
 //   merge_kernel        log-sum-exp merge of a unit's partials; on routing
@@ -73,6 +78,21 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t word, int half) {
   const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, 2.0f, 2);
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, 2.0f, 3);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The same eight codes as fp16 0.0 .. 3.0 (packed fp4 -> fp16 conversion).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 decode8h(uint32_t word, int half) {
+  const uint32_t nib = (word >> (2 * half)) & 0x33333333u;
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 0);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 1);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 2);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 3);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ __forceinline__ f32x4 mmah(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Dequantised INT2 value mn + code * scale: the product is rounded to fp32
@@ -470,24 +490,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         sc[4 * x + 2] = t4.z;
         sc[4 * x + 3] = t4.w;
       }
-      bf16x8 hi[NG], lo[NG];
+      // B = p_r scale_r,grp in fp16 (one rounding, relative 2^-11: these
+      // products only weigh values, the logits above stay exact)
+      f16x8 pw[NG];
 #pragma unroll
       for (int x = 0; x < NG; ++x) {
-        float pw[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pw[e] = pp[e] * sc[(e * NG + x) * 2];
+          pw[x][e] = static_cast<_Float16>(pp[e] * sc[(e * NG + x) * 2]);
           st.amn[x] += pp[e] * sc[(e * NG + x) * 2 + 1];
         }
-        split8(pw, hi[x], lo[x]);
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int o = rb * CB + cb;
         const int t = o >> 1;
-        const bf16x8 a = decode8(vw[t >> 2][t & 3], o & 1);
-        st.acc[cb] = mma(a, hi[cb >> 2], st.acc[cb]);
-        st.acc[cb] = mma(a, lo[cb >> 2], st.acc[cb]);
+        st.acc[cb] = mmah(decode8h(vw[t >> 2][t & 3], o & 1), pw[cb >> 2], st.acc[cb]);
       }
     }
   }
