@@ -384,10 +384,10 @@ __global__ __launch_bounds__(256) void attend_full_kernel(
 // stages a window's scales and minima (256 (d / 64) floats) in its own LDS
 // area with coalesced loads and reads them back as broadcasts.  Partials
 // at slots [split0, split0 + nsq).  The path is VALU-bound (code widening,
-// scale arithmetic, softmax); three waves per SIMD measured fastest (two
-// leave issue slots idle, four spill).
+// scale arithmetic, softmax); four waves per SIMD measured fastest (a
+// handful of registers spill; three or two waves leave issue slots idle).
 template <int D, bool MASS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attend_int2_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void attend_int2_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ codes,
     const float* __restrict__ qsc, const int32_t* __restrict__ items, int nW, int T, int Hq,
     int Hkv, int G, int nf, int nit, int split0, int nsplit, float* __restrict__ part,
