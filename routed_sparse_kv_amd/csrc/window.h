@@ -67,20 +67,22 @@ RSKV_HD int code_word(int side, int r, int c, int d, int* bit) {
   return side * 4 * d + ((t >> 2) * 64 + lane) * 4 + (t & 3);
 }
 
-// Scales and minima: 256 (d / 64) floats per window.  K block first, plain
-// [row][group][scale, min]; V block next, rows in the order a lane group of
-// the PV product reads them: [rb32][g][e][group][scale, min] with row
-// 32 rb32 + v32_row(g, e).
+// Scales and minima: 256 (d / 64) floats per window, in the order the lane
+// groups of the attention kernel read them.  K block first,
+// [rb16][g][group][i][scale, min] for row 16 rb16 + 4 g + i (the rows of a
+// QK output lane group); V block next, [rb32][g][group][e][scale, min] for
+// row 32 rb32 + v32_row(g, e) (the rows of a PV operand lane group).
 RSKV_HD int scale_floats(int d) { return 256 * (d / kGroup); }
 RSKV_HD int kq_off(int r, int grp, int which, int d) {
-  return (r * (d / kGroup) + grp) * 2 + which;
+  const int ng = d / kGroup;
+  return (((r >> 2) * ng + grp) * 4 + (r & 3)) * 2 + which;
 }
 RSKV_HD int vq_off(int r, int grp, int which, int d) {
   const int ng = d / kGroup;
   const int rr = r & 31;
   const int g = (rr & 15) >> 2;
   const int e = (rr & 3) + 4 * (rr >> 4);
-  return 128 * ng + ((((r >> 5) * 4 + g) * 8 + e) * ng + grp) * 2 + which;
+  return 128 * ng + ((((r >> 5) * 4 + g) * ng + grp) * 8 + e) * 2 + which;
 }
 
 }  // namespace win

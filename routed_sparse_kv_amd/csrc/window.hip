@@ -442,33 +442,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     float s[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      // rows 16 rb + 4 g + i: [i][grp][scale, min]
-      float sc[8 * NG];
+      float z[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < 2 * NG; ++x) {
-        const float4 t4 = sq[(rb * 16 + 4 * g) * NG / 2 + x];
-        sc[4 * x] = t4.x;
-        sc[4 * x + 1] = t4.y;
-        sc[4 * x + 2] = t4.z;
-        sc[4 * x + 3] = t4.w;
+      for (int x = 0; x < NG; ++x) {
+        // group x of rows 16 rb + 4 g + i: the two 32-column blocks of the
+        // group, then [i][scale, min]
+        f32x4 cg = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int kb = 2 * x + kh;
+          const int o = rb * KB + kb;
+          const int t = o >> 1;
+          cg = mma(decode8(kw[t >> 2][t & 3], o & 1), qo.qb[kb], cg);
+        }
+        const float4 a4 = sq[((rb * 4 + g) * NG + x) * 2];
+        const float4 b4 = sq[((rb * 4 + g) * NG + x) * 2 + 1];
+        z[0] += a4.x * cg[0] + a4.y * qo.qsum[x];
+        z[1] += a4.z * cg[1] + a4.w * qo.qsum[x];
+        z[2] += b4.x * cg[2] + b4.y * qo.qsum[x];
+        z[3] += b4.z * cg[3] + b4.w * qo.qsum[x];
       }
-      f32x4 cg[NG];
 #pragma unroll
-      for (int x = 0; x < NG; ++x) cg[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int o = rb * KB + kb;
-        const int t = o >> 1;
-        cg[kb / 2] = mma(decode8(kw[t >> 2][t & 3], o & 1), qo.qb[kb], cg[kb / 2]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float z = 0.f;
-#pragma unroll
-        for (int x = 0; x < NG; ++x)
-          z += sc[(i * NG + x) * 2] * cg[x][i] + sc[(i * NG + x) * 2 + 1] * qo.qsum[x];
-        s[rb][i] = z * sl;
-      }
+      for (int i = 0; i < 4; ++i) s[rb][i] = z[i] * sl;
     }
     st.template update<MASS>(s, nvalid, g, g == 0 && n < G,
                              wstat + (static_cast<size_t>(u) * nW + k) * G + n);
@@ -480,32 +475,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
         pp[e] = s[2 * rb][e];
         pp[4 + e] = s[2 * rb + 1][e];
       }
-      // rows v32_row(g, e) of block rb: [e][grp][scale, min]
-      float sc[16 * NG];
-#pragma unroll
-      for (int x = 0; x < 4 * NG; ++x) {
-        const float4 t4 = sq[32 * NG + (rb * 4 + g) * 4 * NG + x];
-        sc[4 * x] = t4.x;
-        sc[4 * x + 1] = t4.y;
-        sc[4 * x + 2] = t4.z;
-        sc[4 * x + 3] = t4.w;
-      }
-      // B = p_r scale_r,grp in fp16 (one rounding, relative 2^-11: these
-      // products only weigh values, the logits above stay exact)
-      f16x8 pw[NG];
 #pragma unroll
       for (int x = 0; x < NG; ++x) {
+        // rows v32_row(g, e) of block rb, group x: [e][scale, min]
+        float sc[16];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const float4 t4 = sq[32 * NG + ((rb * 4 + g) * NG + x) * 4 + y];
+          sc[4 * y] = t4.x;
+          sc[4 * y + 1] = t4.y;
+          sc[4 * y + 2] = t4.z;
+          sc[4 * y + 3] = t4.w;
+        }
+        // B = p_r scale_r,x in fp16 (one rounding, relative 2^-11: these
+        // products only weigh values, the logits above stay exact)
+        f16x8 pw;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pw[x][e] = static_cast<_Float16>(pp[e] * sc[(e * NG + x) * 2]);
-          st.amn[x] += pp[e] * sc[(e * NG + x) * 2 + 1];
+          pw[e] = static_cast<_Float16>(pp[e] * sc[2 * e]);
+          st.amn[x] += pp[e] * sc[2 * e + 1];
         }
-      }
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int o = rb * CB + cb;
-        const int t = o >> 1;
-        st.acc[cb] = mmah(decode8h(vw[t >> 2][t & 3], o & 1), pw[cb >> 2], st.acc[cb]);
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int cb = 4 * x + c4;  // the 16-column blocks of group x
+          const int o = rb * CB + cb;
+          const int t = o >> 1;
+          st.acc[cb] = mmah(decode8h(vw[t >> 2][t & 3], o & 1), pw, st.acc[cb]);
+        }
       }
     }
   }
