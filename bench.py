@@ -442,8 +442,8 @@ def window_step_bytes(info, esize, nsplit, event):
     nit = nf + nq
     stats = nit * G * 8 if event else 0
     # the two attention kernels split the partials in proportion to their workgroups
-    sf = -(-min(nf, -(-4096 // U)) // 4) if nf else 0
-    sq = -(-min(nq, -(-8192 // U)) // 4) if nq else 0
+    sf = -(-min(nf, -(-2048 // U)) // 4) if nf else 0
+    sq = -(-min(nq, -(-4096 // U)) // 4) if nq else 0
     per = {
         "attend_full": nf * info["full_bytes"] + (G * d * esize + nf * 4 + sf * part
                                                   + nf * G * 8 * bool(event) if nf else 0),

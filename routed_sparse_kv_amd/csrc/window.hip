@@ -1086,10 +1086,12 @@ hipError_t build_impl(const rskv_window* W, const void* K, const void* V, hipStr
 void attend_splits(const rskv_window* W, int nf, int nq, int* nsf, int* nsq) {
   const int U = W->B * W->Hkv;
   if (W->dtype == RSKV_BF16) {
-    // one wave per window at most; about 4096 waves of the full-window
-    // kernel (two resident per SIMD) and 8192 of the INT2 one in all
-    const int wf = std::min(nf, (4096 + U - 1) / U);
-    const int wq = std::min(nq, (8192 + U - 1) / U);
+    // one wave per window at most, and one round of resident waves: about
+    // 2048 waves of the full-window kernel (two per SIMD) and 4096 of the
+    // INT2 one (four per SIMD) in all (measured: more waves lengthen the
+    // tail and the merge)
+    const int wf = std::min(nf, (2048 + U - 1) / U);
+    const int wq = std::min(nq, (4096 + U - 1) / U);
     *nsf = (wf + 3) / 4;
     *nsq = (wq + 3) / 4;
     return;
