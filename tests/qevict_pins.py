@@ -239,6 +239,35 @@ def pin_route_hand(qe):
     assert new.tolist() == [EVICTED, QUANT, EVICTED, FULL, EVICTED, EVICTED], new.tolist()
 
 
+def pin_route_brute(qe):
+    """Random tie-heavy scores over several events: each event's tiers equal
+    the brute-force definition (a live window's rank = the live windows with
+    a larger cumulative score, or an equal one and a lower index; ranks
+    below n_full full, the next n_quant INT2, the rest evicted; evicted
+    windows stay evicted)."""
+    rng = np.random.default_rng(21)
+    for trial in range(6):
+        nW = int(rng.integers(3, 12))
+        st, K, V, _ = _unit(qe, nW * 4, 4, 4, 100 + trial)
+        nf, nq = int(rng.integers(0, nW)), int(rng.integers(0, nW))
+        if nf + nq == 0:
+            nf = 1
+        total = np.zeros(nW)
+        tiers = np.zeros(nW, np.int64)
+        for ev in range(4):
+            mass = rng.integers(0, 3, nW) * 0.25  # many exact ties
+            mass[tiers == EVICTED] = 0.0
+            total = total + mass
+            live = [j for j in range(nW) if tiers[j] != EVICTED]
+            want = np.full(nW, EVICTED)
+            for j in live:
+                rank = sum(1 for i in live if total[i] > total[j] or (total[i] == total[j] and i < j))
+                want[j] = FULL if rank < nf else QUANT if rank < nf + nq else EVICTED
+            got = qe.route_unit(st, mass, nf, nq, 4, "f32")
+            assert got.tolist() == want.tolist(), (trial, ev, got.tolist(), want.tolist())
+            tiers = want
+
+
 def pin_write_once(qe):
     """Demote, promote, demote: the ledger keeps the codes of the first
     demotion (taken from the prefilled values), promotion writes the
@@ -300,4 +329,4 @@ def pin_full_budget(qe):
 
 ALL_PINS = [pin_quantize_hand, pin_quantize_constant, pin_quantize_nearest, pin_dequantize_grid,
             pin_windows, pin_attend_full, pin_attend_quant, pin_attend_mixed, pin_route_hand,
-            pin_write_once, pin_schedule, pin_full_budget]
+            pin_route_brute, pin_write_once, pin_schedule, pin_full_budget]
