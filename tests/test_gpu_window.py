@@ -15,7 +15,7 @@ stored K/V and queries.  After every step:
   * at the end of a case, the full-precision store (promoted windows
     included) is bit-exact.
 Sizes span many windows with a ragged last one; the cases cover fp32 / bf16,
-d = 64 / 128, query groups of 1 to 7, a budget holding every window at full
+d = 64 / 128, query groups of 1 to 16, a budget holding every window at full
 precision, an INT2-only budget, a single surviving window, routing at every
 step (promotions and re-demotions), a context shorter than one window and
 the 128K-token workload at full size (sampled units).
@@ -52,6 +52,10 @@ CASES = {
     "route_every_step": ("gqa_32k_bf16", dict(B=1, Hq=8, Hkv=2, T=1500, steps=10),
                          dict(counts=(3, 6)), 1, 10),
     "short_context": ("tiny_fp32_2k", dict(T=40, Hq=2, steps=3), dict(counts=(0, 1)), 1, 3),
+    # the largest query group the kernels take (16 heads per KV head)
+    "bf16_g16": ("gqa_32k_bf16", dict(B=1, Hq=16, Hkv=1, T=1500, steps=3), dict(counts=(5, 10)), 1,
+                 3),
+    "f32_g16": ("tiny_fp32_2k", dict(Hq=16, T=1100, steps=3), dict(counts=(4, 6)), 1, 3),
     # every window holds the same K/V: all masses tie exactly and the
     # ranking falls back to the window index
     "tied_windows": ("gqa_32k_bf16", dict(B=1, Hq=4, Hkv=1, T=1024, steps=3), dict(counts=(4, 5),
