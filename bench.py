@@ -100,9 +100,9 @@ def step_bytes(span_len, n_spans, n_full, sels, nsels, cfg, factors_only=False):
     return route + attend + out, attend
 
 
-ATTEND_SOURCES = ("attend.hip", "common.h")
+ATTEND_SOURCES = ("attend.hip", "common.h", "lanes.h")
 RETRIEVAL_SOURCES = ("retrieval.hip", "retrieval.h", "common.h")
-WINDOW_SOURCES = ("window.hip", "window.h", "layout.h", "common.h")
+WINDOW_SOURCES = ("window.hip", "window.h", "layout.h", "common.h", "lanes.h")
 
 
 def kernel_sha(files=ATTEND_SOURCES):

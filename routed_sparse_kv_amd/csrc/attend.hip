@@ -33,6 +33,7 @@
 
 #include "cache.h"
 #include "common.h"
+#include "lanes.h"
 
 namespace rskv {
 namespace {
@@ -94,6 +95,7 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
   }
 }
 
+
 // Online-softmax update of a wave for 8 logits per lane (lane: head l % 16,
 // rows 4 g + i and 16 + 4 g + i).  Turns x into probabilities relative to
 // the new running max and returns the factor that rescales older state.
@@ -101,8 +103,8 @@ __device__ __forceinline__ float wave_softmax8(float* x, float& m, float& l) {
   float cm = x[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
-  cm = fmaxf(cm, __shfl_xor(cm, 16, kWave));
-  cm = fmaxf(cm, __shfl_xor(cm, 32, kWave));
+  cm = fmaxf(cm, xor_lane<16>(cm));
+  cm = fmaxf(cm, xor_lane<32>(cm));
   const float mn = fmaxf(m, cm);
   const float sc = mn == -INFINITY ? 1.f : __expf(m - mn);
   float ps = 0.f;
@@ -111,8 +113,8 @@ __device__ __forceinline__ float wave_softmax8(float* x, float& m, float& l) {
     x[e] = x[e] == -INFINITY ? 0.f : __expf(x[e] - mn);
     ps += x[e];
   }
-  ps += __shfl_xor(ps, 16, kWave);
-  ps += __shfl_xor(ps, 32, kWave);
+  ps += xor_lane<16>(ps);
+  ps += xor_lane<32>(ps);
   l = l * sc + ps;
   m = mn;
   return sc;

@@ -27,6 +27,7 @@
 // writes back the XCD's L2 and serialises; the kernel boundary is cheaper.)
 #include "cache.h"
 #include "common.h"
+#include "lanes.h"
 
 namespace rskv {
 namespace {
@@ -109,8 +110,8 @@ __device__ __forceinline__ void route_tiles_bf16(RouteTiles<D>& rt, const float*
       for (int e = 0; e < 8; ++e)
         zp += rho[32 * kk + 8 * grp + e] * static_cast<double>(static_cast<float>(rt.sa[t][kk][e]));
     }
-    zp += __shfl_xor(zp, 16, kWave);
-    zp += __shfl_xor(zp, 32, kWave);
+    zp += xor_lane<16>(zp);
+    zp += xor_lane<32>(zp);
     if (grp == 0 && j0 + g16 < ns) z_out[static_cast<size_t>(u) * S + j0 + g16] = alpha * zp;
     if (head_ok) {
       // lane holds spans j0 + 4 grp + i of head g16

@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "lanes.h"
 #include "window.h"
 
 namespace rskv {
@@ -167,8 +168,8 @@ struct QOperand {
     }
 #pragma unroll
     for (int x = 0; x < NG; ++x) {
-      qsum[x] += __shfl_xor(qsum[x], 16, kWave);
-      qsum[x] += __shfl_xor(qsum[x], 32, kWave);
+      qsum[x] += xor_lane<16>(qsum[x]);
+      qsum[x] += xor_lane<32>(qsum[x]);
     }
   }
 };
@@ -207,16 +208,16 @@ struct SoftState {
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[rb][i]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16, kWave));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, kWave));
+    cm = fmaxf(cm, xor_lane<16>(cm));
+    cm = fmaxf(cm, xor_lane<32>(cm));
     if (MASS) {
       float w = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) w += __builtin_amdgcn_exp2f(s[rb][i] - cm);
-      w += __shfl_xor(w, 16, kWave);
-      w += __shfl_xor(w, 32, kWave);
+      w += xor_lane<16>(w);
+      w += xor_lane<32>(w);
       if (store) *ws = make_float2(cm * kLn2, w);
     }
     // the reference m moves only when a logit exceeds it by more than
@@ -240,8 +241,8 @@ struct SoftState {
         s[rb][i] = __builtin_amdgcn_exp2f(s[rb][i] - m);
         ps += s[rb][i];
       }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
+    ps += xor_lane<16>(ps);
+    ps += xor_lane<32>(ps);
     l += ps;
   }
 };
@@ -258,8 +259,8 @@ __device__ __forceinline__ void block_partial(SoftState<D>& st, float* mbuf, int
   // minima terms of the INT2 values, summed over the lane groups' rows
 #pragma unroll
   for (int x = 0; x < NG; ++x) {
-    st.amn[x] += __shfl_xor(st.amn[x], 16, kWave);
-    st.amn[x] += __shfl_xor(st.amn[x], 32, kWave);
+    st.amn[x] += xor_lane<16>(st.amn[x]);
+    st.amn[x] += xor_lane<32>(st.amn[x]);
   }
   float* sm = mbuf;                 // [4][kMaxG]
   float* sl4 = mbuf + 4 * kMaxG;    // [4][kMaxG]
