@@ -356,6 +356,9 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int k = 0; k < KR; ++k) zr[k] = L.z[pidx(tid + kAttThreads * k)];
     };
+    // candidates z > tau: count and value range (padding slots hold -inf)
+    int c_loc = 0;
+    double lo = INFINITY, hi = -INFINITY;
     {
       double zr[KR];
       int lr[KR], tr[KR];
@@ -371,11 +374,14 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int k = 0; k < KR; ++k)
         if (tid + kAttThreads * k >= ns) zr[k] = -INFINITY;
-      // the first chunk of this wave is in flight while the workgroup
-      // selects; issued unconditionally (a wave without chunks re-reads the
-      // last one and drops it), so that waits for the values above count
-      // exactly these loads
-      issue_full(min(wglob, max(nFI, 1) - 1) * kChunk, pbuf);
+#pragma unroll
+      for (int k = 0; k < KR; ++k) {
+        if (zr[k] > tau) {
+          ++c_loc;
+          lo = fmin(lo, zr[k]);
+          hi = fmax(hi, zr[k]);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
         const int i = tid + kAttThreads * k;  // < kFuseSpans
@@ -383,7 +389,11 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         L.len[pidx(i)] = lr[k];
         L.tpad[pidx(i)] = tr[k];
       }
-      for (int w = tid; w < kFuseSpans / 32; w += kAttThreads) L.mask[w] = 0u;
+      // the first chunk of this wave is in flight while the workgroup
+      // selects; it is issued once the scores have arrived (issued earlier,
+      // it delays them), unconditionally (a wave without chunks re-reads the
+      // last one and drops it)
+      issue_full(min(wglob, max(nFI, 1) - 1) * kChunk, pbuf);
     }
     // Position in index order of this thread's flagged slots: ballots per
     // slot row, wave totals in LDS, one barrier.  Returns the count before
@@ -469,25 +479,8 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
       __syncthreads();
     };
-    // candidates z > tau: count and value range (padding slots hold -inf;
-    // each thread reads back the score slots it wrote)
-    int c_loc = 0;
-    double lo = INFINITY, hi = -INFINITY;
-    {
-      double zr[KR];
-      load_z(zr);
-#pragma unroll
-      for (int k = 0; k < KR; ++k) {
-        if (zr[k] > tau) {
-          ++c_loc;
-          lo = fmin(lo, zr[k]);
-          hi = fmax(hi, zr[k]);
-        }
-      }
-    }
     const int n_cand = block4_sum(c_loc, L, 0);
     block4_min_max_f64(lo, hi, L);
-    f_step();
     double zs = INFINITY;  // pick: z > tau && (z > zs || (z == zs && j <= js))
     int js = -1;
     if (k_max > 0 && n_cand > 0) {
@@ -608,10 +601,12 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       const bool f = (pm >> k) & 1u;
       const unsigned long long bal = __ballot(f);
       const int base = __builtin_amdgcn_readlane(rbase, k);
-      if (f) {
-        const int i = tid + kAttThreads * k;
-        L.elist[base + __popcll(bal & below)].x = i;
-        atomicOr(&L.mask[i >> 5], 1u << (i & 31));
+      if (f) L.elist[base + __popcll(bal & below)].x = tid + kAttThreads * k;
+      // the row's ballot is the bitmask of spans 256 k + 64 wave .. +63
+      if (lane == 0) {
+        const int w0 = (kAttThreads * k + kWave * wave) >> 5;
+        L.mask[w0] = static_cast<unsigned>(bal);
+        L.mask[w0 + 1] = static_cast<unsigned>(bal >> 32);
       }
     }
     __syncthreads();
