@@ -28,7 +28,9 @@
 // merge_kernel (next launch) combines the partials of a unit with the
 // log-sum-exp rule.  Merging inside the attention kernel would need a
 // device-scope release per workgroup, which on gfx950 writes back the XCD's
-// L2 and serialises across workgroups; the kernel boundary is cheaper.
+// L2 and serialises across workgroups (measured at the 128K-context shape:
+// 150 us per attention launch instead of 54); the kernel boundary is
+// cheaper.
 #include <stdlib.h>
 
 #include "cache.h"
