@@ -164,19 +164,13 @@ struct FusedLds {
   int cand_j[256];
   double s_zs;
   int s_bin, s_above, s_cnt, s_js;
+  int s_ncand;  // values gathered for the exact rank (reset with each histogram)
   int rng[5];
 };
 
-// Sum of v over the block (4 waves) and min/max of 64-bit keys; `slot`
-// selects one of the LDS scratch rows (consecutive calls use different
-// rows, so a single barrier per call suffices).
-__device__ __forceinline__ int block4_sum(int v, FusedLds& L, int slot) {
-  const int wave = threadIdx.x >> 6;
-  const int t = __builtin_amdgcn_readlane(wave_incl_scan_dpp(v), 63);
-  if ((threadIdx.x & 63) == 0) L.ired[slot][wave] = t;
-  __syncthreads();
-  return L.ired[slot][0] + L.ired[slot][1] + L.ired[slot][2] + L.ired[slot][3];
-}
+// Block (4 waves) reductions over the LDS scratch rows; `slot` selects a
+// row (consecutive calls use different rows, so a single barrier per call
+// suffices).
 // Exclusive prefix of v over the block (thread order) and the total.
 __device__ __forceinline__ int block4_excl(int v, FusedLds& L, int slot, int* total) {
   const int wave = threadIdx.x >> 6;
@@ -430,13 +424,10 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // kept entry (z*, j*).
     auto rank_bin = [&](const double* zr, const int* bin, int bs, int cb, int rem, double& zs_,
                         int& js_) {
-      __syncthreads();
-      if (tid == 0) L.s_above = 0;
-      __syncthreads();
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
         if (bin[k] == bs) {
-          const int slot = atomicAdd(&L.s_above, 1);
+          const int slot = atomicAdd(&L.s_ncand, 1);
           if (slot < kAttThreads) {
             L.cand_z[slot] = zr[k];
             L.cand_j[slot] = tid + kAttThreads * k;
@@ -481,8 +472,23 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
       __syncthreads();
     };
-    const int n_cand = block4_sum(c_loc, L, 0);
-    block4_min_max_f64(lo, hi, L);
+    int n_cand;
+    {
+      const int cw = __builtin_amdgcn_readlane(wave_incl_scan_dpp(c_loc), 63);
+      wave_min_max_f64(lo, hi);
+      if (lane == 0) {
+        L.ired[0][wave] = cw;
+        L.dred[0][wave] = lo;
+        L.dred[1][wave] = hi;
+      }
+      __syncthreads();
+      n_cand = L.ired[0][0] + L.ired[0][1] + L.ired[0][2] + L.ired[0][3];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        lo = fmin(lo, L.dred[0][w]);
+        hi = fmax(hi, L.dred[1][w]);
+      }
+    }
     double zs = INFINITY;  // pick: z > tau && (z > zs || (z == zs && j <= js))
     int js = -1;
     if (k_max > 0 && n_cand > 0) {
@@ -533,6 +539,7 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                            : -1;
           }
           for (int x = tid; x < 1024; x += kAttThreads) L.hist[x] = 0;
+          if (tid == 0) L.s_ncand = 0;
           __syncthreads();
 #pragma unroll
           for (int k = 0; k < KR; ++k)
@@ -630,6 +637,11 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         pre += c4[x];
       }
     }
+    fb = nFI;  // every chunk is assigned statically
+    const int nFP = nFI - fb;
+    const int nSI = (ns + kChunk - 1) / kChunk;
+    const int NI = nsel + nFP + nSI;  // items of the ranges
+    if (tid < 5) L.rng[tid] = NI;     // (boundaries no item reaches)
     __syncthreads();
     if (s == 0) {
       if (sel_out != nullptr)
@@ -644,11 +656,7 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // each thread tests its items against the five boundaries of this
     // workgroup.
     const long long W = 4ll * gridDim.x;
-    fb = nFI;  // every chunk is assigned statically
     {
-      const int nFP = nFI - fb;
-      const int nSI = (ns + kChunk - 1) / kChunk;
-      const int NI = nsel + nFP + nSI;
       const long long C = static_cast<long long>(e_cost) + static_cast<long long>(nFP) * wc.full +
                           static_cast<long long>(nSI) * wc.summ;
       auto mid2 = [&](int i) -> long long {  // 2 P_i + c_i
@@ -661,8 +669,6 @@ attend_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         return 2ll * (e_cost + static_cast<long long>(nFP) * wc.full +
                       static_cast<long long>(i - nsel - nFP) * wc.summ) + wc.summ;
       };
-      if (tid < 5) L.rng[tid] = NI;
-      __syncthreads();
       for (int i = tid; i < NI; i += kAttThreads) {
         const long long mi = mid2(i) * W;
         const long long mp = i > 0 ? mid2(i - 1) * W : -1;
