@@ -146,3 +146,102 @@ def compare_decode(oc, q_np, out_gpu, sels, tau, k_max, alpha, P, dtype, units=N
         err = max(err, float(np.max(np.abs(out_gpu[b, sl] - ref["out"][b, sl]))))
     assert err <= TOL[dtype], f"{what}: max abs err {err:.3e} > {TOL[dtype]}"
     return err, excused
+
+
+def ulps(a, b, dtype):
+    """Distance of a from b in units of the last stored place of b."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    mant = 8 if dtype == "bf16" else 24
+    _, e = np.frexp(np.where(b == 0, 1.0, np.abs(b)))
+    ulp = np.ldexp(1.0, e - mant)
+    return np.abs(a - b) / ulp
+
+
+def check_segmentation_tables(ex, H, anchor_frac, what=""):
+    """Every sequence's segmentation in a GPU export against oracle.segment
+    on the same surprisal, bit-exact: anchor count, span ids, span starts and
+    lengths, full-resolution positions, and the streaming state (anchor
+    threshold theta = smallest anchor surprisal, full-resolution row of the
+    last anchor).  Only build-time tables: call before any append."""
+    B, T = H.shape
+    n_a = oracle.n_anchors(T, anchor_frac)
+    for b in range(B):
+        sg = oracle.segment(H[b], n_a)
+        ns, nf = len(sg["span_len"]), len(sg["fr_pos"])
+        w = f"{what} sequence {b}"
+        assert ex["n_anchor"][b] == sg["n_a"], w
+        assert ex["n_spans"][b] == ns, w
+        assert ex["n_full"][b] == nf, w
+        assert ex["n_span_tokens"][b] == int(sg["span_len"].sum()), w
+        assert np.array_equal(ex["span_id"][b], sg["span_id"]), w
+        assert np.array_equal(ex["span_start"][b, :ns], sg["span_start"]), w
+        assert np.array_equal(ex["span_len"][b, :ns], sg["span_len"]), w
+        assert np.array_equal(ex["full_pos"][b, :nf], sg["fr_pos"]), w
+        assert (ex["full_pos"][b, nf:] == -1).all(), w
+        anchors = np.flatnonzero(sg["span_id"] == -1)
+        if len(anchors):
+            assert ex["theta"][b] == np.float32(H[b, anchors].min()), w
+            assert ex["last_anchor"][b] == int(np.searchsorted(sg["fr_pos"], anchors[-1])), w
+        else:
+            assert np.isinf(ex["theta"][b]) and ex["last_anchor"][b] == -1, w
+    return n_a
+
+
+def check_full_rows(ex, K, V, b, h, what=""):
+    """Packed full-resolution rows of unit (b, h) are the input rows at the
+    exported positions, bit for bit (stored dtype)."""
+    nf = int(ex["n_full"][b])
+    pos = ex["full_pos"][b, :nf].astype(np.int64)
+    assert np.array_equal(ex["k_full"][b, h, :nf], K[b, h, pos]), f"{what} K rows {(b, h)}"
+    assert np.array_equal(ex["v_full"][b, h, :nf], V[b, h, pos]), f"{what} V rows {(b, h)}"
+
+
+def check_summaries(ex, H, Kf, Vf, b, h, js, dtype, what=""):
+    """Summaries and value means of spans js of unit (b, h) within one
+    stored ulp of the oracle's (from the same input rows), ln|S| exact.
+    Returns the largest distance in ulp."""
+    worst = 0.0
+    lens = ex["span_len"][b, js].astype(np.float64)
+    assert np.array_equal(ex["log_len"][b, js], np.log(lens).astype(np.float32)), what
+    s = oracle.from_stored(ex["summary"][b, h, js], dtype)
+    vb = oracle.from_stored(ex["vmean"][b, h, js], dtype)
+    for i, j in enumerate(js):
+        st, ln = int(ex["span_start"][b, j]), int(ex["span_len"][b, j])
+        s_ref = oracle.round_stored(oracle.span_summary(H[b, st:st + ln], Kf[st:st + ln]), dtype)
+        v_ref = oracle.round_stored(oracle.span_value_mean(Vf[st:st + ln]), dtype)
+        worst = max(worst, ulps(s[i], s_ref, dtype).max(), ulps(vb[i], v_ref, dtype).max())
+    assert worst <= 1.0, f"{what} unit {(b, h)}: summaries differ by {worst} ulp"
+    return worst
+
+
+def check_factor_products(ex, Kf, Vf, b, h, js, dtype, rank, what=""):
+    """A W of spans js of unit (b, h) against the oracle's factors of the
+    same input rows (relative Frobenius error bounded by the storage
+    rounding of A and W), and the Eckart-Young residual.  Spans whose
+    rank-r truncation is not unique (sigma_r = sigma_{r+1} to 1e-6) are
+    skipped.  Returns the number of spans checked."""
+    rel = 2e-6 if dtype == "f32" else 3 * 2.0 ** -8
+    ns = int(ex["n_spans"][b])
+    offs = np.concatenate([[0], np.cumsum(ex["span_len"][b, :ns].astype(np.int64))])
+    checked = 0
+    for j in js:
+        st, ln = int(ex["span_start"][b, j]), int(ex["span_len"][b, j])
+        for X, akey, wkey in ((Kf[st:st + ln], "a_k", "w_k"), (Vf[st:st + ln], "a_v", "w_v")):
+            A = oracle.from_stored(ex[akey][b, h, offs[j]:offs[j + 1]], dtype)
+            Wt = oracle.from_stored(ex[wkey][b, h, j], dtype)
+            prod = A @ Wt
+            sig = np.linalg.svd(X, compute_uv=False)
+            rj = min(rank, ln, X.shape[1])
+            gap = (sig[rj - 1] - sig[rj]) / sig[0] if rj < len(sig) else 1.0
+            if gap < 1e-6:
+                continue  # truncation not unique
+            Ao, Wo = oracle.truncated_svd(X, rank)
+            nx = np.linalg.norm(X)
+            err = np.linalg.norm(prod - Ao @ Wo) / nx
+            assert err <= rel * np.sqrt(rank), f"{what} unit {(b, h)} span {j}: product err {err:.2e}"
+            res = np.linalg.norm(X - prod) ** 2
+            assert res <= np.sum(sig[rj:] ** 2) + (2 * rel * nx) ** 2 + 1e-9 * nx ** 2, \
+                f"{what} unit {(b, h)} span {j}: residual above Eckart-Young"
+            checked += 1
+    return checked

@@ -106,8 +106,19 @@ def test_full_rank_expansion_is_dense_attention(dtype):
     compare_decode(oracle_view(cache.export()), q, out, sels, -math.inf, ns, 8.0, None, dtype,
                    what="full rank")
     # the method itself: fp32 factors rebuild the tokens to fp32 rounding;
-    # bf16 factors carry 2^-8 relative rounding into every rebuilt key/value
-    assert err <= (TOL[dtype] if dtype == "f32" else 4e-2)
+    # bf16 factors carry 2^-8 relative rounding into every rebuilt key/value,
+    # so even the oracle's own bf16 cache sits about 1.1e-2 from dense
+    # attention on these inputs.  The bound is that figure plus a margin for
+    # the different (equally valid) rounding of the GPU's factors.
+    oc = oracle.build_cache(H, oracle.from_stored(K, dtype), oracle.from_stored(V, dtype), 20, p,
+                            dtype, Hq=Hkv * G)
+    ref = oracle.decode_step(oc, oracle.from_stored(q, dtype), -math.inf, int(oc["n_s"].max()),
+                             8.0)["out"]
+    own = float(np.max(np.abs(ref - dense.numpy())))
+    say(f"[full rank {dtype}] oracle's own cache vs dense {own:.2e}")
+    bound = TOL[dtype] if dtype == "f32" else 1.5e-2
+    assert own <= bound
+    assert err <= bound
     cache.close()
 
 
