@@ -124,29 +124,119 @@ def committed_traffic(workload, kernel="attend", files=ATTEND_SOURCES):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(ex_unit_views, q_steps, cfg, n_units_total, budget_s=20.0):
-    """Time the oracle's decode on sampled units; scale to one full step."""
+def host_cores():
+    """CPU cores this process may use, at most 16 (the host share of one
+    GPU on a shared machine)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_worker(conn):
+    """One host core's share of the oracle baseline.  Runs in a process
+    forked before the GPU is touched, and never touches it; single-threaded
+    BLAS.  Messages: ("views", units, views, queries, cfg) stores unit
+    caches; ("decode", n_steps) decodes every stored unit once per step,
+    step s with query s % len(queries), and returns (start, end, routes of
+    the first len(queries) steps); ("build", H, K, V, rank, p, dtype, Hq)
+    builds one unit's cache and returns (start, end); None ends."""
     import oracle
     from threadpoolctl import threadpool_limits
-    G = cfg["Hq"] // cfg["Hkv"]
-    P = None
-    done, el = 0, 0.0
-    views = list(ex_unit_views)
+    units, views, queries, cfg = [], [], [], None
     with threadpool_limits(limits=1):
-        for rep in range(1000):
-            for (b, h), oc in views:
-                qs = q_steps[(rep + b) % len(q_steps)]
-                q = oracle.from_stored(qs[b:b + 1, h * G:(h + 1) * G], cfg["dtype"])
-                if cfg.get("P") is not None:
-                    P = cfg["_P"][0:1] if cfg["_P"].shape[0] == 1 else cfg["_P"][h:h + 1]
-                t0 = time.perf_counter()
-                oracle.decode_step(oc, q, cfg["tau"], cfg["k_max"], cfg["alpha"], P)
-                el += time.perf_counter() - t0
-                done += 1
-            if el > budget_s:
+        while True:
+            msg = conn.recv()
+            if msg is None:
                 break
-    t_step = el / done * n_units_total
-    return done, el, t_step
+            if msg[0] == "views":
+                _, units, views, queries, cfg = msg
+                conn.send("ok")
+            elif msg[0] == "decode":
+                n_steps = msg[1]
+                G = cfg["Hq"] // cfg["Hkv"]
+                routes = {}
+                t0 = time.monotonic()
+                for st in range(n_steps):
+                    qs = queries[st % len(queries)]
+                    for (b, h), oc in zip(units, views):
+                        P = cfg["_P"]
+                        if P is not None:
+                            P = P[0:1] if P.shape[0] == 1 else P[h:h + 1]
+                        q = oracle.from_stored(qs[b:b + 1, h * G:(h + 1) * G], cfg["dtype"])
+                        r = oracle.decode_step(oc, q, cfg["tau"], cfg["k_max"], cfg["alpha"], P)
+                        if st < len(queries):
+                            rt = r["routes"][(0, 0)]
+                            routes[(st, b, h)] = (rt["E"], len(rt["near_tau"]), rt["rank_tie"])
+                conn.send((t0, time.monotonic(), routes))
+            elif msg[0] == "build":
+                _, H, K, V, rank, p, dtype, Hq = msg
+                t0 = time.monotonic()
+                oracle.build_cache(H, K, V, rank, p, dtype, Hq=Hq)
+                conn.send((t0, time.monotonic()))
+
+
+class OracleCores:
+    """A pool of forked oracle workers, one per host core.  Create it before
+    the GPU is initialised: the children only run the CPU oracle."""
+
+    def __init__(self, n):
+        import multiprocessing as mp
+        ctx = mp.get_context("fork")
+        self.n = n
+        self.conns, self.procs = [], []
+        for _ in range(n):
+            a, b = ctx.Pipe()
+            pr = ctx.Process(target=_oracle_worker, args=(b,), daemon=True)
+            pr.start()
+            self.conns.append(a)
+            self.procs.append(pr)
+
+    def close(self):
+        for c in self.conns:
+            try:
+                c.send(None)
+            except Exception:
+                pass
+        for pr in self.procs:
+            pr.join(timeout=10)
+
+    def decode_wall(self, units, views, queries, cfg, budget_s):
+        """Wall seconds of one oracle step over `units` (one unit per task,
+        dealt round-robin to the workers), and the oracle's routes of the
+        first len(queries) steps."""
+        used = min(self.n, len(units))
+        for w in range(used):
+            mine = list(range(w, len(units), used))
+            self.conns[w].send(("views", [units[i] for i in mine], [views[i] for i in mine],
+                                queries, cfg))
+        for w in range(used):
+            assert self.conns[w].recv() == "ok"
+
+        def run(n_steps):
+            for w in range(used):
+                self.conns[w].send(("decode", n_steps))
+            res = [self.conns[w].recv() for w in range(used)]
+            routes = {}
+            for _, _, r in res:
+                routes.update(r)
+            return max(r[1] for r in res) - min(r[0] for r in res), routes
+
+        wall1, routes = run(len(queries))  # also warms every worker
+        n_steps = int(min(2000, max(len(queries), budget_s / max(wall1 / len(queries), 1e-6))))
+        wall, _ = run(n_steps)
+        return wall / n_steps, n_steps, wall, routes
+
+    def build_wall(self, jobs):
+        """Wall seconds of building the given units' caches concurrently."""
+        res = []
+        for i in range(0, len(jobs), self.n):
+            batch = jobs[i:i + self.n]
+            for w, job in enumerate(batch):
+                self.conns[w].send(("build",) + job)
+            res += [self.conns[w].recv() for w in range(len(batch))]
+        return max(r[1] for r in res) - min(r[0] for r in res)
 
 
 def unit_view(ex, b, h):
@@ -664,6 +754,52 @@ def main():
     if args.router == "window":
         window_bench(args)
         return
+    # the oracle's host-core workers are forked before the GPU is touched
+    cores = None if args.no_cpu_baseline else OracleCores(host_cores())
+    try:
+        span_bench(args, cores)
+    finally:
+        if cores is not None:
+            cores.close()
+
+
+def selection_report(caches, qs, cfg, sels_by_query, rskv):
+    """Selection ambiguity from the GPU's own routing scores, after the
+    timed steps: per distinct query, every unit's scores z (rskv_decode_scores)
+    give the spans within 1e-5 of tau (near_tau), the units whose k-th and
+    (k+1)-th largest candidate scores are that close (rank_ties), and the
+    units whose selection differs from the exact top-k of those scores
+    (ties to the lower index; own_score_mismatch, expected 0)."""
+    import torch
+    band = 1e-5
+    B, Hkv, kmax, tau = cfg["B"], cfg["Hkv"], cfg["k_max"], cfg["tau"]
+    near = ties = mism = 0
+    for qi, q in enumerate(qs):
+        rskv.decode_step(caches[0], q, tau, kmax, sel=sels_by_query[qi][0],
+                         n_sel=sels_by_query[qi][1])
+        torch.cuda.synchronize()
+        z, ns = caches[0].scores()
+        s_np = sels_by_query[qi][0].cpu().numpy() if kmax else np.zeros((B, Hkv, 0), np.int32)
+        n_np = sels_by_query[qi][1].cpu().numpy()
+        for b in range(B):
+            for h in range(Hkv):
+                zz = z[b, h, :ns[b]]
+                near += int(np.sum(np.abs(zz - tau) <= band))
+                cand = np.flatnonzero(zz > tau)
+                if len(cand) > kmax:
+                    order = np.lexsort((cand, -zz[cand]))
+                    E = np.sort(cand[order[:kmax]])
+                    if kmax > 0 and zz[cand[order[kmax - 1]]] - zz[cand[order[kmax]]] <= band:
+                        ties += 1
+                else:
+                    E = cand
+                if not np.array_equal(E, s_np[b, h, :n_np[b, h]]):
+                    mism += 1
+    return {"queries": len(qs), "units": B * Hkv, "band": band, "near_tau": near,
+            "rank_ties": ties, "own_score_mismatch": mism}
+
+
+def span_bench(args, cores):
     import torch
 
     import routed_sparse_kv_amd as rskv
@@ -855,20 +991,51 @@ def main():
         res["host_link"] = {"bytes_per_step": fb, "achieved": gbps, "peak": 64.0,
                             "unit": "GB/s", "frac": gbps / 64.0}
 
-    if not args.no_cpu_baseline:
+    # selection ambiguity from the GPU's scores, one untimed decode per query
+    by_query = [(torch.zeros((B, Hkv, kmax), dtype=torch.int32, device=dev) if kmax else None,
+                 torch.zeros((B, Hkv), dtype=torch.int32, device=dev)) for _ in qs]
+    res["selection"] = selection_report(caches, qs, cfg, by_query, rskv)
+
+    if cores is not None:
         U = B * Hkv
-        n_cpu = args.cpu_units or min(U, 8)
-        rng = np.random.default_rng(0)
-        units = [(int(u // Hkv), int(u % Hkv)) for u in rng.permutation(U)[:n_cpu]]
-        views = ((u, unit_view(ex, *u)) for u in units)
-        done, el, t_step = cpu_baseline(views, wl.queries, cfg, U, budget_s=15.0)
-        res["cpu_baseline"] = {"value": ctx_tokens / t_step, "unit": "context-tokens/s/head",
-                               "cores": 1, "kind": "oracle",
-                               "sample": f"{done} oracle unit decodes ({n_cpu} distinct "
-                                         f"(sequence, KV head) units of {U}, the workload's "
-                                         f"queries in turn), {el:.1f}s single-threaded, "
-                                         f"scaled to one {U}-unit step",
-                               "seconds_per_step": t_step}
+        units = [(u // Hkv, u % Hkv) for u in range(U)]
+        if args.cpu_units:
+            rng = np.random.default_rng(0)
+            units = [units[i] for i in sorted(rng.permutation(U)[:args.cpu_units])]
+        views = [unit_view(ex, *u) for u in units]
+        t_step, n_run, wall, routes = cores.decode_wall(units, views, wl.queries, cfg, 12.0)
+        t_step *= U / len(units)
+        # the oracle's build of one sequence (its KV heads concurrently)
+        jobs = [(wl.H[0:1], W.as_f64(wl.K[0:1, h:h + 1], dt), W.as_f64(wl.V[0:1, h:h + 1], dt),
+                 cfg["rank"], cfg["anchor_frac"], dt, cfg["Hq"] // Hkv) for h in range(Hkv)]
+        build_wall = cores.build_wall(jobs)
+        base = {"value": ctx_tokens / t_step, "unit": "context-tokens/s/head",
+                "cores": cores.n, "kind": "oracle",
+                "sample": f"{n_run} oracle decode steps of {len(units)} (sequence, KV head) "
+                          f"units (each unit one task on one of {cores.n} worker processes, "
+                          f"the workload's queries in turn), {wall:.1f}s wall"
+                          + ("" if len(units) == U else f", scaled to {U} units"),
+                "seconds_per_step": t_step,
+                "build_s": build_wall,
+                "build_sample": f"oracle build_spans of sequence 0 ({cfg['T']} tokens, "
+                                f"{Hkv} KV heads concurrently on {min(Hkv, cores.n)} cores)",
+                "host_cpus_visible": os.cpu_count()}
+        if wl.appends is None:
+            # the oracle's selections on the same stored cache against the
+            # GPU's in the timed steps (replicas are identical caches)
+            diff = excused = near = ties = 0
+            for (qi, b, h), (E, n_near, tie) in routes.items():
+                i = next(i for i in range(n_steps) if i % len(qs) == qi)
+                g = sels[i][b, h, :int(nsels[i][b, h])].cpu().numpy() if kmax else np.zeros(0)
+                near += n_near
+                ties += int(tie)
+                if not np.array_equal(np.asarray(E), g):
+                    diff += 1
+                    excused += int(n_near > 0 or tie)
+            base["selection_vs_oracle"] = {"unit_queries": len(routes), "mismatch": diff,
+                                           "excused_by_band": excused, "near_tau": near,
+                                           "rank_ties": ties}
+        res["cpu_baseline"] = base
     for c in caches:
         c.close()
     print(json.dumps(res))

@@ -56,6 +56,24 @@ typedef enum rskv_dtype {
 
 typedef struct rskv_cache rskv_cache; /* opaque, owned by the library */
 
+/* Device-memory allocator of a cache: every device array it holds, its
+ * build temporaries and its decode workspace come from here.
+ *   alloc(ctx, bytes, stream): a device pointer to at least `bytes` bytes,
+ *     aligned to 256 bytes, usable by work queued on `stream` (the stream
+ *     of the call that allocates), or NULL on failure; the library then
+ *     releases what it already holds and returns RSKV_ENOMEM.
+ *   free(ctx, ptr, stream): releases a pointer that alloc returned, once
+ *     the library has synchronised `stream`, the last stream that used it.
+ *   ctx: passed back unchanged.
+ * alloc == NULL selects hipMalloc / hipFree (hipFree may itself wait for
+ * the whole device; a caching allocator such as a framework's avoids it).
+ * Pinned host memory (the host tiers) is always hipHostMalloc'd. */
+typedef struct rskv_allocator {
+  void* (*alloc)(void* ctx, size_t bytes, void* stream);
+  void (*free)(void* ctx, void* ptr, void* stream);
+  void* ctx;
+} rskv_allocator;
+
 /* Shapes and options of a cache.  K, V, q and every stored array use
  * `dtype`; surprisal, ln|S|, the projection and the output are fp32. */
 typedef struct rskv_build_opts {
@@ -81,6 +99,8 @@ typedef struct rskv_build_opts {
                             fetches the expanded spans on demand; Metodologia
                             2 and 3).  Results are identical; only the
                             expanded spans' factors cross the link. */
+  rskv_allocator allocator; /* device memory of the cache (zeroed struct:
+                               hipMalloc / hipFree) */
 } rskv_build_opts;
 
 typedef enum rskv_factor_tier {
@@ -111,11 +131,24 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V,
  *   sel:   device int32 [B][Hkv][k_max] or NULL: expanded span indices,
  *          ascending, -1 padded.
  *   n_sel: device int32 [B][Hkv] or NULL: number of expanded spans.
- * Asynchronous on `stream`; no host synchronisation and no allocation, so
- * it can be captured in a HIP graph.  Calls on one cache must not overlap
- * (they share the cache's workspace). */
+ * Asynchronous on `stream`; no host synchronisation, no allocation and no
+ * memset node (three or four kernel launches), so it can be captured in a
+ * HIP graph: a replay decodes the query then in the buffer `q` with the
+ * tau, k_max and output pointers of the captured call.  Profiling (below)
+ * must be off while capturing.  Calls on one cache must not overlap (they
+ * share the cache's workspace). */
 int rskv_decode_step(rskv_cache* cache, const void* q, float tau, int32_t k_max,
                      float* out, int32_t* sel, int32_t* n_sel, void* stream);
+
+/* Routing scores of the last rskv_decode_step on this cache (Metodologia
+ * 3: the gate's argument before the threshold), z_j = alpha <rho, s_j> in
+ * fp64, copied to the host array z [B][Hkv][S] (S = n_spans_max of
+ * rskv_cache_info; entries past n_spans[b] are unspecified), and the span
+ * counts of that step to the host array n_spans [B] (or NULL).
+ * Synchronous: waits for the cache's last stream.  Meant for reports on
+ * selection ambiguity (scores within a band of tau or of the k-th largest
+ * score). */
+int rskv_decode_scores(const rskv_cache* cache, double* z, int32_t* n_spans);
 
 /* Append one decoded token per sequence, with streaming segmentation
  * (Metodologia 1 applied to decoded tokens; the page fixes the anchor rule
@@ -208,8 +241,11 @@ int rskv_cache_import(const rskv_host_arrays* arrays, const rskv_build_opts* opt
                       int32_t rank, int32_t S, int32_t F, int32_t N, void* stream,
                       rskv_cache** out);
 
-/* Release the cache and its device memory.  Waits for work the library has
- * queued on the cache's last stream.  NULL is accepted. */
+/* Release the cache and its device memory.  Waits only for the work queued
+ * on the cache's last stream (the stream of its last build, decode or append
+ * call), then returns every allocation to the cache's allocator; work on
+ * other streams is not waited for (hipFree, the default allocator's release,
+ * may still wait for the device on its own).  NULL is accepted. */
 void rskv_cache_destroy(rskv_cache* cache);
 
 /* Per-kernel timing of decode_step: each of its four kernels (routing GEMV,

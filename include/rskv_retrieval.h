@@ -74,6 +74,8 @@ typedef struct {
                            retrieval region's K/V rows live (host: pinned
                            memory read by the kernels over the host link,
                            as the page's unified-addressing offload) */
+  rskv_allocator allocator; /* device memory of the index (rskv.h; zeroed:
+                               hipMalloc / hipFree) */
 } rskv_retrieval_opts;
 
 /* Builds the index.  K, V: device [B][Hkv][T][d] in dtype (copied; the
@@ -163,6 +165,8 @@ typedef struct {
 int rskv_retrieval_profile_enable(rskv_retrieval* index, int32_t on);
 int rskv_retrieval_profile_read(rskv_retrieval* index, rskv_retrieval_profile* prof);
 
+/* Releases the index: waits only for the work queued on its last stream,
+ * then returns every device block to its allocator.  NULL is accepted. */
 void rskv_retrieval_destroy(rskv_retrieval* index);
 
 #ifdef __cplusplus

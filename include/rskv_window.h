@@ -76,6 +76,8 @@ typedef struct {
   int32_t n_quant;      /* windows per KV head kept in INT2 by a routing
                            event, >= 0; n_full + n_quant >= 1 */
   int32_t route_every;  /* R >= 1: routing events at steps 0, R, 2R, ... */
+  rskv_allocator allocator; /* device memory of the cache (rskv.h; zeroed:
+                               hipMalloc / hipFree) */
 } rskv_window_opts;
 
 /* Builds the cache.  K, V: device [B][Hkv][T][d] in dtype (copied; the
@@ -152,6 +154,8 @@ typedef struct {
 int rskv_window_profile_enable(rskv_window* cache, int32_t on);
 int rskv_window_profile_read(rskv_window* cache, rskv_window_profile* prof);
 
+/* Releases the cache: waits only for the work queued on its last stream,
+ * then returns every device block to its allocator.  NULL is accepted. */
 void rskv_window_destroy(rskv_window* cache);
 
 #ifdef __cplusplus

@@ -7,8 +7,10 @@ fallback: if the shared library is missing, every call raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
+import weakref
 from typing import Optional
 
 import numpy as np
@@ -27,12 +29,92 @@ class RskvError(RuntimeError):
         self.code = code
 
 
+ALLOC_FN = C.CFUNCTYPE(C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p)
+FREE_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p, C.c_void_p)
+
+
+class Allocator(C.Structure):
+    """rskv_allocator: device-memory hook of a cache (zeroed: hipMalloc)."""
+    _fields_ = [("alloc", ALLOC_FN), ("free", FREE_FN), ("ctx", C.c_void_p)]
+
+
+class HookAllocator:
+    """A device allocator hook from two Python callables:
+    ``alloc(nbytes, stream) -> int`` (device pointer, 0 on failure) and
+    ``free(ptr, stream)``; ``stream`` is the hipStream_t as an int.  The
+    object must outlive every cache built with it (the caches keep a
+    reference)."""
+
+    def __init__(self, alloc, free):
+        self._alloc_py, self._free_py = alloc, free
+        self._alloc_c = ALLOC_FN(self._on_alloc)
+        self._free_c = FREE_FN(self._on_free)
+        self.struct = Allocator(self._alloc_c, self._free_c, None)
+
+    def _on_alloc(self, ctx, nbytes, stream):
+        try:
+            return self._alloc_py(int(nbytes), int(stream or 0)) or None
+        except Exception:  # an exception must not cross the C boundary
+            return None
+
+    def _on_free(self, ctx, ptr, stream):
+        try:
+            self._free_py(int(ptr), int(stream or 0))
+        except Exception:
+            pass
+
+
+_torch_hook = None
+
+
+def torch_allocator() -> HookAllocator:
+    """The hook that takes cache memory from torch's caching allocator on
+    the stream of the allocating call (the binding's default)."""
+    global _torch_hook
+    if _torch_hook is None:
+        torch = _torch()
+
+        def alloc(nbytes, stream):
+            return torch.cuda.caching_allocator_alloc(nbytes, stream=stream)
+
+        def free(ptr, stream):
+            torch.cuda.caching_allocator_delete(ptr)
+        _torch_hook = HookAllocator(alloc, free)
+    return _torch_hook
+
+
+def resolve_allocator(allocator):
+    """"torch" (default), "hip" (hipMalloc) or a HookAllocator ->
+    (struct, object to keep alive)."""
+    if allocator is None or allocator == "hip":
+        return Allocator(), None
+    if allocator == "torch":
+        allocator = torch_allocator()
+    if not isinstance(allocator, HookAllocator):
+        raise TypeError("allocator must be 'torch', 'hip' or a HookAllocator")
+    return allocator.struct, allocator
+
+
+# Handles still open at interpreter exit are closed while torch (whose
+# allocator the default hook calls) is still alive.
+_live = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live():
+    for h in list(_live):
+        try:
+            h.close()
+        except Exception:
+            pass
+
+
 class BuildOpts(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("context_len", C.c_int32), ("dtype", C.c_int32),
                 ("anchor_frac", C.c_double), ("alpha", C.c_float), ("proj", C.c_void_p),
                 ("n_proj", C.c_int32), ("tail_capacity", C.c_int32), ("k_max_cap", C.c_int32),
-                ("factor_tier", C.c_int32)]
+                ("factor_tier", C.c_int32), ("allocator", Allocator)]
 
 
 class CacheInfo(C.Structure):
@@ -85,11 +167,13 @@ def lib():
                                         i32, i32, vp, C.POINTER(vp)]
         L.rskv_cache_destroy.argtypes = [vp]
         L.rskv_cache_destroy.restype = None
+        L.rskv_decode_scores.argtypes = [vp, vp, vp]
         L.rskv_profile_enable.argtypes = [vp, i32]
         L.rskv_profile_read.argtypes = [vp, C.POINTER(Profile)]
         L.rskv_last_error.restype = C.c_char_p
         L.rskv_version.restype = C.c_char_p
-        for fn in ("rskv_build_spans", "rskv_decode_step", "rskv_append_kv", "rskv_append_token",
+        for fn in ("rskv_build_spans", "rskv_decode_step", "rskv_decode_scores", "rskv_append_kv",
+                   "rskv_append_token",
                    "rskv_cache_info_get", "rskv_cache_export", "rskv_cache_import",
                    "rskv_profile_enable", "rskv_profile_read"):
             getattr(L, fn).restype = C.c_int
@@ -136,9 +220,11 @@ def _stream():
 class Cache:
     """Owner of an rskv_cache handle."""
 
-    def __init__(self, handle: C.c_void_p):
+    def __init__(self, handle: C.c_void_p, keep=None):
         self._h = handle
+        self._keep = keep  # the allocator hook, alive while the cache is
         self.info = self._info()
+        _live.add(self)
 
     @property
     def handle(self):
@@ -194,6 +280,15 @@ class Cache:
         out["info"] = dict(i)
         return out
 
+    def scores(self):
+        """(z [B][Hkv][S] fp64, n_spans [B]) of the last decode step."""
+        i = self.info
+        z = np.zeros((i["batch"], i["n_kv_heads"], i["n_spans_max"]), np.float64)
+        ns = np.zeros(i["batch"], np.int32)
+        _check(lib().rskv_decode_scores(self.handle, C.c_void_p(z.ctypes.data),
+                                        C.c_void_p(ns.ctypes.data)))
+        return z, ns
+
     # ------------------------------------------------------------ profile
     def profile_enable(self, on: bool = True):
         _check(lib().rskv_profile_enable(self.handle, 1 if on else 0))
@@ -206,17 +301,20 @@ class Cache:
 
 def build_spans(surprisal, K, V, rank: int, anchor_frac: float, n_q_heads: Optional[int] = None,
                 alpha: float = 8.0, proj=None, tail_capacity: int = 0,
-                k_max_cap: int = 0, factor_tier: str = "hbm") -> Cache:
+                k_max_cap: int = 0, factor_tier: str = "hbm", allocator="torch") -> Cache:
     """Build a cache.  surprisal [B][T] fp32; K, V [B][Hkv][T][d] (fp32 or
     bf16) on the GPU; proj [1 or Hkv][d][d] fp32 on the GPU or None;
-    factor_tier "hbm" or "host" (span factors in pinned host memory)."""
+    factor_tier "hbm" or "host" (span factors in pinned host memory);
+    allocator "torch" (torch's caching allocator), "hip" (hipMalloc) or a
+    HookAllocator."""
     torch = _torch()
     B, Hkv, T, d = K.shape
     dt = _dtype_code(K)
+    hook, keep = resolve_allocator(allocator)
     opts = BuildOpts(batch=B, n_q_heads=n_q_heads or Hkv, n_kv_heads=Hkv, head_dim=d,
                      context_len=T, dtype=dt, anchor_frac=float(anchor_frac), alpha=float(alpha),
                      proj=None, n_proj=0, tail_capacity=int(tail_capacity),
-                     k_max_cap=int(k_max_cap), factor_tier=TIERS[factor_tier])
+                     k_max_cap=int(k_max_cap), factor_tier=TIERS[factor_tier], allocator=hook)
     args = [_dev(surprisal, "surprisal", (B, T), torch.float32),
             _dev(K, "K", (B, Hkv, T, d)), _dev(V, "V", (B, Hkv, T, d), K.dtype)]
     if proj is not None:
@@ -225,7 +323,7 @@ def build_spans(surprisal, K, V, rank: int, anchor_frac: float, n_q_heads: Optio
     h = C.c_void_p()
     _check(lib().rskv_build_spans(args[0], args[1], args[2], int(rank), C.byref(opts),
                                   _stream(), C.byref(h)))
-    return Cache(h)
+    return Cache(h, keep)
 
 
 def decode_step(cache: Cache, q, tau: float, k_max: int, out=None, sel=None, n_sel=None):
@@ -270,7 +368,8 @@ def append_token(cache: Cache, k, v, h=None):
 
 def cache_import(arrays: dict, n_q_heads: int, rank: int, dtype: str, context_len: int,
                  alpha: float = 8.0, proj: Optional[np.ndarray] = None,
-                 tail_capacity: int = 0, k_max_cap: int = 0, factor_tier: str = "hbm") -> Cache:
+                 tail_capacity: int = 0, k_max_cap: int = 0, factor_tier: str = "hbm",
+                 allocator="torch") -> Cache:
     """Create a cache from host arrays in the canonical (export) layout."""
     dt = BF16 if dtype == "bf16" else F32
     et = np.uint16 if dt == BF16 else np.float32
@@ -283,10 +382,11 @@ def cache_import(arrays: dict, n_q_heads: int, rank: int, dtype: str, context_le
     B, Hkv, S, d = keep["summary"].shape
     F = keep["k_full"].shape[2]
     N = keep["a_k"].shape[2]
+    hook, hook_ref = resolve_allocator(allocator)
     opts = BuildOpts(batch=B, n_q_heads=n_q_heads, n_kv_heads=Hkv, head_dim=d,
                      context_len=context_len, dtype=dt, anchor_frac=0.0, alpha=float(alpha),
                      proj=None, n_proj=0, tail_capacity=int(tail_capacity),
-                     k_max_cap=int(k_max_cap), factor_tier=TIERS[factor_tier])
+                     k_max_cap=int(k_max_cap), factor_tier=TIERS[factor_tier], allocator=hook)
     if proj is not None:
         keep["_proj"] = np.ascontiguousarray(proj, dtype=np.float32)
         opts.proj = keep["_proj"].ctypes.data
@@ -295,7 +395,7 @@ def cache_import(arrays: dict, n_q_heads: int, rank: int, dtype: str, context_le
     h = C.c_void_p()
     _check(lib().rskv_cache_import(C.byref(ha), C.byref(opts), int(rank), S, F, N, _stream(),
                                    C.byref(h)))
-    return Cache(h)
+    return Cache(h, hook_ref)
 
 
 def version() -> str:

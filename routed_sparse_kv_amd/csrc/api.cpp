@@ -59,6 +59,8 @@ int check_opts(const rskv_build_opts* o, int rank) {
   if (!(o->alpha == o->alpha)) return fail(RSKV_EINVAL, "alpha is NaN");
   if (o->factor_tier != RSKV_TIER_HBM && o->factor_tier != RSKV_TIER_HOST)
     return fail(RSKV_EINVAL, "factor_tier must be RSKV_TIER_HBM or RSKV_TIER_HOST");
+  if (!rskv::valid_hook(o->allocator))
+    return fail(RSKV_EINVAL, "allocator needs both alloc and free, or neither");
   return RSKV_OK;
 }
 
@@ -67,12 +69,8 @@ template <typename T>
 int dev_alloc(rskv_cache* c, T** p, size_t count, const char* what) {
   *p = nullptr;
   const size_t bytes = std::max<size_t>(count, 1) * sizeof(T);
-  void* q = nullptr;
-  hipError_t e = hipMalloc(&q, bytes);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(RSKV_ENOMEM, std::string("device allocation failed: ") + what);
-  }
+  void* q = c->mem.alloc(bytes, c->last_stream);
+  if (q == nullptr) return fail(RSKV_ENOMEM, std::string("device allocation failed: ") + what);
   c->allocs.push_back(q);
   c->bytes += bytes;
   *p = static_cast<T*>(q);
@@ -104,11 +102,11 @@ int host_alloc_bytes(rskv_cache* c, void** p, size_t bytes, const char* what) {
   return RSKV_OK;
 }
 
+// Waits for the cache's last stream only, then releases its memory.
 void free_cache(rskv_cache* c) {
   if (c == nullptr) return;
-  if (c->last_stream != nullptr) (void)hipStreamSynchronize(c->last_stream);
-  (void)hipDeviceSynchronize();
-  for (void* p : c->allocs) (void)hipFree(p);
+  (void)hipStreamSynchronize(c->last_stream);
+  for (void* p : c->allocs) c->mem.release(p, c->last_stream);
   for (void* p : c->host_allocs) (void)hipHostFree(p);
   for (auto* list : {&c->prof.pending, &c->prof.app_pending})
     for (hipEvent_t e : *list)
@@ -220,6 +218,7 @@ void init_header(rskv_cache* c, const rskv_build_opts* o, int rank) {
   c->tail_cap = o->tail_capacity;
   c->n_proj = o->proj != nullptr ? o->n_proj : 0;
   c->factor_tier = o->factor_tier;
+  c->mem.hook = o->allocator;
 }
 
 int copy_proj(rskv_cache* c, const rskv_build_opts* o, hipStream_t st, bool from_host) {
@@ -474,23 +473,22 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
     if (rc != RSKV_OK) return rc;
     std::vector<void*> tmps;
     auto tmp_alloc = [&](int32_t** p, size_t n) -> int {
-      void* q = nullptr;
-      if (hipMalloc(&q, std::max<size_t>(n, 1) * sizeof(int32_t)) != hipSuccess) {
-        (void)hipGetLastError();
+      void* q = c->mem.alloc(std::max<size_t>(n, 1) * sizeof(int32_t), st);
+      if (q == nullptr)
         return fail(RSKV_ENOMEM, "device allocation failed: segmentation temporaries");
-      }
       tmps.push_back(q);
       *p = static_cast<int32_t*>(q);
       return RSKV_OK;
     };
     struct TmpFree {
       std::vector<void*>* v;
+      const rskv::DevMem* mem;
       hipStream_t st;
       ~TmpFree() {
         if (!v->empty()) (void)hipStreamSynchronize(st);
-        for (void* p : *v) (void)hipFree(p);
+        for (void* p : *v) mem->release(p, st);
       }
-    } tmp_free{&tmps, st};
+    } tmp_free{&tmps, &c->mem, st};
     int32_t *start_tmp, *len_tmp, *tokoff_tmp, *tokpad_tmp, *full_tmp, *counts;
     const size_t BT = static_cast<size_t>(B) * T, BT1 = static_cast<size_t>(B) * (T + 1);
     if ((rc = tmp_alloc(&start_tmp, BT)) != RSKV_OK) return rc;
@@ -632,6 +630,22 @@ int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, flo
     return fail(RSKV_ENOMEM, "host allocation failed");
   } catch (...) {
     return fail(RSKV_EINVAL, "unexpected error in rskv_decode_step");
+  }
+}
+
+int rskv_decode_scores(const rskv_cache* c, double* z, int32_t* n_spans) {
+  try {
+    if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
+    if (z == nullptr) return fail(RSKV_EINVAL, "z is NULL");
+    RSKV_HIP(hipStreamSynchronize(c->last_stream), "scores synchronize");
+    const size_t n = static_cast<size_t>(c->B) * c->Hkv * c->S;
+    RSKV_HIP(hipMemcpy(z, c->dev.z, n * sizeof(double), hipMemcpyDeviceToHost), "scores copy");
+    if (n_spans != nullptr)
+      RSKV_HIP(hipMemcpy(n_spans, c->dev.n_spans, c->B * sizeof(int32_t), hipMemcpyDeviceToHost),
+               "span counts copy");
+    return RSKV_OK;
+  } catch (...) {
+    return fail(RSKV_EINVAL, "unexpected error in rskv_decode_scores");
   }
 }
 

@@ -6,9 +6,11 @@
 #include <stdint.h>
 
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/rskv.h"
+#include "devmem.h"
 #include "layout.h"
 
 namespace rskv {
@@ -79,11 +81,20 @@ struct KernelEvents {
 };
 
 // Launches `kernel`; with `ev`, the dispatch records ev->start and ev->stop.
+// Without events it is a plain launch, which a HIP graph can capture.
 template <typename... KArgs, typename... Args>
 hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
                   const KernelEvents* ev, Args... args) {
-  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev ? ev->start : nullptr,
-                        ev ? ev->stop : nullptr, 0u, args...);
+  if (ev != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev->start, ev->stop, 0u, args...);
+  } else {
+    std::tuple<KArgs...> formals{static_cast<KArgs>(args)...};
+    void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    pArgs<0>(formals, argv);
+    const hipError_t e =
+        hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, st);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 
@@ -119,6 +130,7 @@ struct rskv_cache {
   int nsplit_max = 1;
   std::vector<int32_t> h_n_anchor, h_n_spans, h_n_full0, h_n_span_tokens, h_n_tok_pad;
   rskv::DeviceArrays dev;
+  rskv::DevMem mem;                // allocator of the device memory
   std::vector<void*> allocs;       // device memory
   size_t bytes = 0;
   int factor_tier = 0;             // RSKV_TIER_HBM or RSKV_TIER_HOST

@@ -882,11 +882,11 @@ hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t 
     const size_t budget = size_t(512) << 20;
     long long nb = static_cast<long long>(budget / (slab * sizeof(double)));
     nb = std::max<long long>(1, std::min<long long>({nb, n_large, 1024}));
-    double* scratch = nullptr;
-    e = hipMalloc(&scratch, static_cast<size_t>(nb) * slab * sizeof(double));
-    if (e != hipSuccess) {
-      if (err) *err = "factor scratch allocation failed";
-      return e;
+    double* scratch =
+        static_cast<double*>(c->mem.alloc(static_cast<size_t>(nb) * slab * sizeof(double), st));
+    if (scratch == nullptr) {
+      if (err) *err = "device allocation failed: factor scratch";
+      return hipErrorOutOfMemory;
     }
     hipLaunchKernelGGL((factor_kernel<DT, false>), dim3(static_cast<unsigned>(nb)),
                        dim3(kFacThreads), 0, st, static_cast<const T*>(K),
@@ -896,7 +896,7 @@ hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t 
                        static_cast<T*>(c->dev.w_k), static_cast<T*>(c->dev.w_v), scratch, slab);
     e = hipGetLastError();
     const hipError_t e2 = hipStreamSynchronize(st);
-    (void)hipFree(scratch);
+    c->mem.release(scratch, st);
     if (e != hipSuccess) return e;
     if (e2 != hipSuccess) return e2;
   }

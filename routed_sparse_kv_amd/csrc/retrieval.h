@@ -79,6 +79,7 @@ struct rskv_retrieval {
   int32_t* selp = nullptr;     // [U][2] threshold (fp32 bits), last tied index taken
   int32_t* sel = nullptr;      // [U][n_sel]
   float* part = nullptr;       // [U][nsplit][G][d + 2]
+  rskv::DevMem mem;  // allocator of the device memory
   std::vector<void*> allocs;
   std::vector<void*> host_allocs;
   size_t bytes = 0, host_bytes = 0;

@@ -79,12 +79,9 @@ void make_codebook(int m, R::Codebook* cb) {
 int dev_alloc(rskv_retrieval* r, void** p, size_t bytes, const char* what) {
   *p = nullptr;
   bytes = std::max<size_t>(bytes, 16);
-  void* q = nullptr;
-  hipError_t e = hipMalloc(&q, bytes);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
+  void* q = r->mem.alloc(bytes, r->last_stream);
+  if (q == nullptr)
     return report_error(RSKV_ENOMEM, std::string("device allocation failed: ") + what);
-  }
   r->allocs.push_back(q);
   r->bytes += bytes;
   *p = q;
@@ -116,9 +113,9 @@ int dev_array(rskv_retrieval* r, T** p, size_t count, const char* what) {
 
 void free_index(rskv_retrieval* r) {
   if (r == nullptr) return;
-  if (r->last_stream != nullptr) (void)hipStreamSynchronize(r->last_stream);
-  (void)hipDeviceSynchronize();
-  for (void* p : r->allocs) (void)hipFree(p);
+  // the last stream only; then every block goes back to the allocator
+  (void)hipStreamSynchronize(r->last_stream);
+  for (void* p : r->allocs) r->mem.release(p, r->last_stream);
   for (void* p : r->host_allocs) (void)hipHostFree(p);
   for (hipEvent_t e : r->pending)
     if (e != nullptr) (void)hipEventDestroy(e);
@@ -152,6 +149,8 @@ int check_opts(const rskv_retrieval_opts* o) {
     return report_error(RSKV_EINVAL, "cand_frac must lie in [0, 1]");
   if (o->k_ret < 0 || o->n_sink < 0 || o->n_local < 0)
     return report_error(RSKV_EINVAL, "k_ret, n_sink and n_local must be >= 0");
+  if (!rskv::valid_hook(o->allocator))
+    return report_error(RSKV_EINVAL, "allocator needs both alloc and free, or neither");
   if (o->kv_tier != RSKV_TIER_HBM && o->kv_tier != RSKV_TIER_HOST)
     return report_error(RSKV_EINVAL, "kv_tier must be RSKV_TIER_HBM or RSKV_TIER_HOST");
   if (static_cast<long long>(o->batch) * o->n_kv_heads * o->context_len > (1ll << 31) - 1)
@@ -194,6 +193,7 @@ int rskv_retrieval_build(const void* K, const void* V, const int8_t* signs,
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     r->last_stream = st;
+    r->mem.hook = o->allocator;
     r->B = o->batch;
     r->Hq = o->n_q_heads;
     r->Hkv = o->n_kv_heads;

@@ -111,6 +111,7 @@ struct rskv_window {
   float* part = nullptr;       // [U][nsplit][G][d + 2]
   float2* wstat = nullptr;     // [U][nW][G] per attended window: max and sum of e^(s - max)
   float2* hstat = nullptr;     // [U][G] per head: softmax max and denominator
+  rskv::DevMem mem;  // allocator of the device memory
   std::vector<void*> allocs;
   size_t bytes = 0;
   hipStream_t last_stream = nullptr;

@@ -34,12 +34,9 @@ size_t esize(int dtype) { return dtype == RSKV_BF16 ? 2 : 4; }
 int dev_alloc(rskv_window* w, void** p, size_t bytes, const char* what) {
   *p = nullptr;
   bytes = std::max<size_t>(bytes, 16);
-  void* q = nullptr;
-  hipError_t e = hipMalloc(&q, bytes);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
+  void* q = w->mem.alloc(bytes, w->last_stream);
+  if (q == nullptr)
     return report_error(RSKV_ENOMEM, std::string("device allocation failed: ") + what);
-  }
   w->allocs.push_back(q);
   w->bytes += bytes;
   *p = q;
@@ -56,9 +53,9 @@ int dev_array(rskv_window* w, T** p, size_t count, const char* what) {
 
 void free_cache(rskv_window* w) {
   if (w == nullptr) return;
-  if (w->last_stream != nullptr) (void)hipStreamSynchronize(w->last_stream);
-  (void)hipDeviceSynchronize();
-  for (void* p : w->allocs) (void)hipFree(p);
+  // the last stream only; then every block goes back to the allocator
+  (void)hipStreamSynchronize(w->last_stream);
+  for (void* p : w->allocs) w->mem.release(p, w->last_stream);
   for (hipEvent_t e : w->pending)
     if (e != nullptr) (void)hipEventDestroy(e);
   for (hipEvent_t e : w->pool) (void)hipEventDestroy(e);
@@ -89,6 +86,8 @@ int check_opts(const rskv_window_opts* o) {
     return report_error(RSKV_EINVAL, "context_len must be <= 2^20");
   if (o->n_full < 0 || o->n_quant < 0 || o->n_full + o->n_quant < 1)
     return report_error(RSKV_EINVAL, "n_full and n_quant must be >= 0 with n_full + n_quant >= 1");
+  if (!rskv::valid_hook(o->allocator))
+    return report_error(RSKV_EINVAL, "allocator needs both alloc and free, or neither");
   if (o->route_every < 1) return report_error(RSKV_EINVAL, "route_every must be >= 1");
   const long long nW = (o->context_len + W::kRows - 1) / W::kRows;
   if (static_cast<long long>(o->batch) * o->n_kv_heads * nW * W::kRows * o->head_dim > (1ll << 40))
@@ -114,6 +113,7 @@ int rskv_window_build(const void* K, const void* V, const rskv_window_opts* o, v
     Guard guard{w};
     hipStream_t st = static_cast<hipStream_t>(stream);
     w->last_stream = st;
+    w->mem.hook = o->allocator;
     w->B = o->batch;
     w->Hq = o->n_q_heads;
     w->Hkv = o->n_kv_heads;

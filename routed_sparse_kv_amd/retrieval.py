@@ -8,7 +8,8 @@ from __future__ import annotations
 import ctypes as C
 import numpy as np
 
-from .binding import BF16, F32, RskvError, TIERS, _check, _dev, _dtype_code, _stream, _torch, lib
+from .binding import (BF16, F32, TIERS, Allocator, RskvError, _check, _dev, _dtype_code, _live,
+                      _stream, _torch, lib, resolve_allocator)
 
 
 class RetrievalOpts(C.Structure):
@@ -16,7 +17,7 @@ class RetrievalOpts(C.Structure):
                 ("head_dim", C.c_int32), ("context_len", C.c_int32), ("dtype", C.c_int32),
                 ("m", C.c_int32), ("rho", C.c_int32), ("cand_frac", C.c_double),
                 ("k_ret", C.c_int32), ("n_sink", C.c_int32), ("n_local", C.c_int32),
-                ("kv_tier", C.c_int32)]
+                ("kv_tier", C.c_int32), ("allocator", Allocator)]
 
 
 class RetrievalInfo(C.Structure):
@@ -73,8 +74,10 @@ def _lib():
 class Retrieval:
     """Owner of an rskv_retrieval handle."""
 
-    def __init__(self, handle: C.c_void_p):
+    def __init__(self, handle: C.c_void_p, keep=None):
         self._h = handle
+        self._keep = keep  # the allocator hook, alive while the index is
+        _live.add(self)
         ri = RetrievalInfo()
         _check(_lib().rskv_retrieval_info_get(self.handle, C.byref(ri)))
         self.info = {n: getattr(ri, n) for n, _ in RetrievalInfo._fields_}
@@ -156,24 +159,26 @@ class Retrieval:
 
 def build_retrieval(K, V, signs, n_q_heads: int, m: int = 8, rho: int = 16,
                     cand_frac: float = 0.05, k_ret: int = 1024, n_sink: int = 16,
-                    n_local: int = 512, kv_tier: str = "hbm") -> Retrieval:
+                    n_local: int = 512, kv_tier: str = "hbm", allocator="torch") -> Retrieval:
     """Build a retrieval index.  K, V [B][Hkv][T][d] (fp32 or bf16) on the
-    GPU; signs: d entries +-1 (host, any integer array)."""
+    GPU; signs: d entries +-1 (host, any integer array); allocator as in
+    build_spans."""
     B, Hkv, T, d = K.shape
     dt = _dtype_code(K)
     s = np.ascontiguousarray(np.asarray(signs), dtype=np.int8)
     if s.shape != (d,):
         raise ValueError(f"signs must have shape ({d},)")
+    hook, keep = resolve_allocator(allocator)
     opts = RetrievalOpts(batch=B, n_q_heads=int(n_q_heads), n_kv_heads=Hkv, head_dim=d,
                          context_len=T, dtype=dt, m=int(m), rho=int(rho),
                          cand_frac=float(cand_frac), k_ret=int(k_ret), n_sink=int(n_sink),
-                         n_local=int(n_local), kv_tier=TIERS[kv_tier])
+                         n_local=int(n_local), kv_tier=TIERS[kv_tier], allocator=hook)
     h = C.c_void_p()
     _check(_lib().rskv_retrieval_build(_dev(K, "K", (B, Hkv, T, d)),
                                        _dev(V, "V", (B, Hkv, T, d), K.dtype),
                                        C.c_void_p(s.ctypes.data), C.byref(opts), _stream(),
                                        C.byref(h)))
-    return Retrieval(h)
+    return Retrieval(h, keep)
 
 
 def retrieval_decode(index: Retrieval, q, out=None, retrieved=None):

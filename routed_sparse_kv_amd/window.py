@@ -8,7 +8,8 @@ from __future__ import annotations
 import ctypes as C
 import numpy as np
 
-from .binding import BF16, F32, RskvError, _check, _dev, _dtype_code, _stream, _torch, lib
+from .binding import (BF16, F32, Allocator, RskvError, _check, _dev, _dtype_code, _live, _stream,
+                      _torch, lib, resolve_allocator)
 
 ROWS = 64    #: positions per window
 GROUP = 64   #: coordinates per INT2 scale group
@@ -18,7 +19,7 @@ FULL, INT2, EVICTED = 0, 1, 2
 class WindowOpts(C.Structure):
     _fields_ = [(n, C.c_int32) for n in
                 ("batch", "n_q_heads", "n_kv_heads", "head_dim", "context_len", "dtype", "n_full",
-                 "n_quant", "route_every")]
+                 "n_quant", "route_every")] + [("allocator", Allocator)]
 
 
 class WindowInfo(C.Structure):
@@ -71,8 +72,10 @@ def _lib():
 class WindowCache:
     """Owner of an rskv_window handle."""
 
-    def __init__(self, handle: C.c_void_p):
+    def __init__(self, handle: C.c_void_p, keep=None):
         self._h = handle
+        self._keep = keep  # the allocator hook, alive while the cache is
+        _live.add(self)
 
     @property
     def handle(self):
@@ -145,17 +148,20 @@ class WindowCache:
         return dict(steps=p.steps, events=p.events, **{f"{k}_ms": p.ms[j] for j, k in enumerate(KERNELS)})
 
 
-def build_window(K, V, n_q_heads: int, n_full: int, n_quant: int, route_every: int = 1) -> WindowCache:
-    """Build a window cache.  K, V [B][Hkv][T][d] (fp32 or bf16) on the GPU."""
+def build_window(K, V, n_q_heads: int, n_full: int, n_quant: int, route_every: int = 1,
+                 allocator="torch") -> WindowCache:
+    """Build a window cache.  K, V [B][Hkv][T][d] (fp32 or bf16) on the GPU;
+    allocator as in build_spans."""
     B, Hkv, T, d = K.shape
     dt = _dtype_code(K)
+    hook, keep = resolve_allocator(allocator)
     opts = WindowOpts(batch=B, n_q_heads=int(n_q_heads), n_kv_heads=Hkv, head_dim=d,
                       context_len=T, dtype=dt, n_full=int(n_full), n_quant=int(n_quant),
-                      route_every=int(route_every))
+                      route_every=int(route_every), allocator=hook)
     h = C.c_void_p()
     _check(_lib().rskv_window_build(_dev(K, "K", (B, Hkv, T, d)), _dev(V, "V", (B, Hkv, T, d), K.dtype),
                                     C.byref(opts), _stream(), C.byref(h)))
-    return WindowCache(h)
+    return WindowCache(h, keep)
 
 
 def window_decode(cache: WindowCache, q, out=None):
