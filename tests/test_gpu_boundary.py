@@ -12,6 +12,7 @@
   * Destroy waits for the cache's last stream only: work queued on another
     stream is still running when it returns.
 """
+import gc
 import time
 
 import numpy as np
@@ -103,6 +104,8 @@ def test_allocator_hook_failure_returns_enomem_and_frees(kind):
     # spans longer than 48 tokens: the factor pass's global scratch is used
     wl = W.generate("long_128k_bf16", B=2, Hq=8, Hkv=2, T=8192, steps=1)
     build = BUILDERS[kind](wl)
+    # earlier tests' tensors must not be released while the baseline holds
+    gc.collect()
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated()
     ok = CountingHook()
