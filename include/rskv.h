@@ -140,6 +140,26 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V,
 int rskv_decode_step(rskv_cache* cache, const void* q, float tau, int32_t k_max,
                      float* out, int32_t* sel, int32_t* n_sel, void* stream);
 
+/* rskv_decode_step for callers that cannot allocate device memory or must
+ * not rely on a per-cache workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the decode workspace (routing scores, summary logits,
+ * selection lists, work ranges, partial softmax states) taken from a
+ * library-owned static device array of rskv_decode_static_capacity() bytes
+ * (32 MiB) per GPU, held until the process ends, instead of the cache's
+ * own.  Calls nothing that allocates (no hipMalloc, no events; profiling is
+ * not recorded).  The device of the cache must be current.
+ * Returns RSKV_ECAPACITY when the cache's workspace is larger than the
+ * array (rskv_decode_step then still works).  Every call on one GPU shares
+ * that GPU's array, so calls that overlap on one GPU race, even on
+ * different caches or streams; serialise them.  No part of the array needs
+ * clearing between calls (each step writes what it reads). */
+int rskv_decode_step_static(rskv_cache* cache, const void* q, float tau, int32_t k_max,
+                            float* out, int32_t* sel, int32_t* n_sel, void* stream);
+
+/* Bytes of the static decode workspace array of one GPU. */
+size_t rskv_decode_static_capacity(void);
+
 /* Routing scores of the last rskv_decode_step on this cache (Metodologia
  * 3: the gate's argument before the threshold), z_j = alpha <rho, s_j> in
  * fp64, copied to the host array z [B][Hkv][S] (S = n_spans_max of

@@ -168,11 +168,14 @@ def lib():
         L.rskv_cache_destroy.argtypes = [vp]
         L.rskv_cache_destroy.restype = None
         L.rskv_decode_scores.argtypes = [vp, vp, vp]
+        L.rskv_decode_step_static.argtypes = [vp, vp, C.c_float, i32, vp, vp, vp, vp]
+        L.rskv_decode_static_capacity.restype = C.c_size_t
         L.rskv_profile_enable.argtypes = [vp, i32]
         L.rskv_profile_read.argtypes = [vp, C.POINTER(Profile)]
         L.rskv_last_error.restype = C.c_char_p
         L.rskv_version.restype = C.c_char_p
-        for fn in ("rskv_build_spans", "rskv_decode_step", "rskv_decode_scores", "rskv_append_kv",
+        for fn in ("rskv_build_spans", "rskv_decode_step", "rskv_decode_step_static",
+                   "rskv_decode_scores", "rskv_append_kv",
                    "rskv_append_token",
                    "rskv_cache_info_get", "rskv_cache_export", "rskv_cache_import",
                    "rskv_profile_enable", "rskv_profile_read"):
@@ -341,6 +344,27 @@ def decode_step(cache: Cache, q, tau: float, k_max: int, out=None, sel=None, n_s
     _check(lib().rskv_decode_step(cache.handle, qp, C.c_float(tau), int(k_max), op, sp, np_,
                                   _stream()))
     return out
+
+
+def decode_step_static(cache: Cache, q, tau: float, k_max: int, out, sel=None, n_sel=None):
+    """decode_step through rskv_decode_step_static: the decode workspace is
+    the library's static device array (no allocation); ``out`` must be
+    given."""
+    torch = _torch()
+    i = cache.info
+    B, Hq, Hkv, d = i["batch"], i["n_q_heads"], i["n_kv_heads"], i["head_dim"]
+    qp = _dev(q, "q", (B, Hq, d), cache.torch_dtype)
+    op = _dev(out, "out", (B, Hq, d), torch.float32)
+    sp = _dev(sel, "sel", (B, Hkv, k_max), torch.int32) if sel is not None else None
+    np_ = _dev(n_sel, "n_sel", (B, Hkv), torch.int32) if n_sel is not None else None
+    _check(lib().rskv_decode_step_static(cache.handle, qp, C.c_float(tau), int(k_max), op, sp,
+                                         np_, _stream()))
+    return out
+
+
+def decode_static_capacity() -> int:
+    """Bytes of the static decode workspace of one GPU."""
+    return int(lib().rskv_decode_static_capacity())
 
 
 def append_kv(cache: Cache, k, v):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "librskv.so")
 SOURCES = ["segment.hip", "summary.hip", "factor.hip", "route.hip", "attend.hip", "retrieval.hip",
-           "window.hip", "api.cpp", "retrieval_api.cpp", "window_api.cpp"]
+           "window.hip", "static_ws.hip", "api.cpp", "retrieval_api.cpp", "window_api.cpp"]
 ARCH = "gfx950"
 
 

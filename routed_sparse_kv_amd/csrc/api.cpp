@@ -443,6 +443,118 @@ int import_arrays(rskv_cache* c, const rskv_host_arrays* a, int S_in, int F_in, 
 
 namespace rskv {
 int report_error(int code, const std::string& msg) { return fail(code, msg); }
+
+DecodeWs cache_ws(const rskv_cache* c) {
+  const auto& v = c->dev;
+  DecodeWs w;
+  w.z = v.z;
+  w.slogit = v.slogit;
+  w.sel = v.sel;
+  w.sel_desc = v.sel_desc;
+  w.n_sel = v.n_sel;
+  w.wstart = v.wstart;
+  w.part = v.part;
+  return w;
+}
+
+namespace {
+// Bytes of the workspace arrays, in DecodeWs order (sizes as alloc_arrays).
+void ws_array_bytes(const rskv_cache* c, size_t* b) {
+  const size_t U = static_cast<size_t>(c->B) * c->Hkv;
+  b[0] = U * c->S * sizeof(double);
+  b[1] = U * c->Sp * c->G * sizeof(float);
+  b[2] = U * c->S * sizeof(int32_t);
+  b[3] = U * c->S * 4 * sizeof(int32_t);
+  b[4] = U * sizeof(int32_t);
+  b[5] = U * (4 * c->nsplit_max + 1) * sizeof(int32_t);
+  b[6] = U * c->nsplit_max * c->G * (c->d + 2) * sizeof(float);
+}
+size_t align256(size_t x) { return (std::max<size_t>(x, 1) + 255) & ~size_t(255); }
+}  // namespace
+
+size_t decode_ws_bytes(const rskv_cache* c) {
+  size_t b[7], total = 0;
+  ws_array_bytes(c, b);
+  for (size_t x : b) total += align256(x);
+  return total;
+}
+
+DecodeWs carve_ws(const rskv_cache* c, void* base) {
+  size_t b[7];
+  ws_array_bytes(c, b);
+  char* p = static_cast<char*>(base);
+  void* a[7];
+  for (int i = 0; i < 7; ++i) {
+    a[i] = p;
+    p += align256(b[i]);
+  }
+  DecodeWs w;
+  w.z = static_cast<double*>(a[0]);
+  w.slogit = static_cast<float*>(a[1]);
+  w.sel = static_cast<int32_t*>(a[2]);
+  w.sel_desc = static_cast<int32_t*>(a[3]);
+  w.n_sel = static_cast<int32_t*>(a[4]);
+  w.wstart = static_cast<int32_t*>(a[5]);
+  w.part = static_cast<float*>(a[6]);
+  return w;
+}
+
+int decode_with(rskv_cache* c, const DecodeWs& ws, const void* q, float tau, int k_max,
+                float* out, int32_t* sel, int32_t* n_sel, hipStream_t st, bool profile) {
+  c->last_stream = st;
+  const int nsplit = decode_nsplit(c, k_max);
+  const int nwaves = attend_uses_mfma(c) ? 4 * nsplit : 0;
+  constexpr int kK = kProfileKernels;
+  KernelEvents ev[kK];
+  const bool prof = profile && c->prof.on;
+  if (prof) {
+    for (int i = 0; i < kK; ++i) {
+      for (hipEvent_t* e : {&ev[i].start, &ev[i].stop}) {
+        if (c->prof.pool.empty()) {
+          hipEvent_t n;
+          RSKV_HIP(hipEventCreate(&n), "event create");
+          c->prof.pool.push_back(n);
+        }
+        *e = c->prof.pool.back();
+        c->prof.pool.pop_back();
+      }
+    }
+  }
+  RSKV_HIP(launch_route(c, ws, q, st, prof ? &ev[0] : nullptr), "route kernel");
+  const bool fused = attend_fuses_topk(c, k_max);
+  const SelectArgs sa{tau, k_max, sel, n_sel};
+  if (fused) {
+    // the attention kernel selects: the top-k slot of the profile stays at 0
+    if (prof) {
+      c->prof.pool.push_back(ev[1].start);
+      c->prof.pool.push_back(ev[1].stop);
+      ev[1] = KernelEvents{};
+    }
+  } else {
+    RSKV_HIP(launch_topk(c, ws, tau, k_max, nwaves, sel, n_sel, st, prof ? &ev[1] : nullptr),
+             "topk kernel");
+  }
+  RSKV_HIP(launch_attend(c, ws, q, nsplit, fused ? &sa : nullptr, st, prof ? &ev[2] : nullptr),
+           "attend kernel");
+  RSKV_HIP(launch_merge(c, ws, nsplit, out, st, prof ? &ev[3] : nullptr), "merge kernel");
+  if (prof) {
+    for (int i = 0; i < kK; ++i) {
+      c->prof.pending.push_back(ev[i].start);
+      c->prof.pending.push_back(ev[i].stop);
+    }
+  }
+  return RSKV_OK;
+}
+
+// Argument checks shared by the decode entry points.
+int check_decode(const rskv_cache* c, const void* q, float tau, int k_max, const float* out) {
+  if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
+  if (q == nullptr || out == nullptr) return fail(RSKV_EINVAL, "q and out must be non-NULL");
+  if (tau != tau) return fail(RSKV_EINVAL, "tau is NaN");
+  if (k_max < 0) return fail(RSKV_EINVAL, "k_max must be >= 0");
+  if (k_max > c->k_max_cap) return fail(RSKV_ECAPACITY, "k_max exceeds k_max_cap");
+  return RSKV_OK;
+}
 }  // namespace rskv
 
 extern "C" {
@@ -577,55 +689,10 @@ int rskv_build_spans(const float* surprisal, const void* K, const void* V, int32
 int rskv_decode_step(rskv_cache* c, const void* q, float tau, int32_t k_max, float* out,
                      int32_t* sel, int32_t* n_sel, void* stream) {
   try {
-    if (!valid_cache(c)) return fail(RSKV_ESTATE, "invalid cache handle");
-    if (q == nullptr || out == nullptr) return fail(RSKV_EINVAL, "q and out must be non-NULL");
-    if (tau != tau) return fail(RSKV_EINVAL, "tau is NaN");
-    if (k_max < 0) return fail(RSKV_EINVAL, "k_max must be >= 0");
-    if (k_max > c->k_max_cap) return fail(RSKV_ECAPACITY, "k_max exceeds k_max_cap");
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    c->last_stream = st;
-    const int nsplit = rskv::decode_nsplit(c, k_max);
-    const int nwaves = rskv::attend_uses_mfma(c) ? 4 * nsplit : 0;
-    constexpr int kK = rskv::kProfileKernels;
-    rskv::KernelEvents ev[kK];
-    const bool prof = c->prof.on;
-    if (prof) {
-      for (int i = 0; i < kK; ++i) {
-        for (hipEvent_t* e : {&ev[i].start, &ev[i].stop}) {
-          if (c->prof.pool.empty()) {
-            hipEvent_t n;
-            RSKV_HIP(hipEventCreate(&n), "event create");
-            c->prof.pool.push_back(n);
-          }
-          *e = c->prof.pool.back();
-          c->prof.pool.pop_back();
-        }
-      }
-    }
-    RSKV_HIP(rskv::launch_route(c, q, st, prof ? &ev[0] : nullptr), "route kernel");
-    const bool fused = rskv::attend_fuses_topk(c, k_max);
-    const rskv::SelectArgs sa{tau, k_max, sel, n_sel};
-    if (fused) {
-      // the attention kernel selects: the top-k slot of the profile stays at 0
-      if (prof) {
-        c->prof.pool.push_back(ev[1].start);
-        c->prof.pool.push_back(ev[1].stop);
-        ev[1] = rskv::KernelEvents{};
-      }
-    } else {
-      RSKV_HIP(rskv::launch_topk(c, tau, k_max, nwaves, sel, n_sel, st, prof ? &ev[1] : nullptr),
-               "topk kernel");
-    }
-    RSKV_HIP(rskv::launch_attend(c, q, nsplit, fused ? &sa : nullptr, st, prof ? &ev[2] : nullptr),
-             "attend kernel");
-    RSKV_HIP(rskv::launch_merge(c, nsplit, out, st, prof ? &ev[3] : nullptr), "merge kernel");
-    if (prof) {
-      for (int i = 0; i < kK; ++i) {
-        c->prof.pending.push_back(ev[i].start);
-        c->prof.pending.push_back(ev[i].stop);
-      }
-    }
-    return RSKV_OK;
+    int rc = rskv::check_decode(c, q, tau, k_max, out);
+    if (rc != RSKV_OK) return rc;
+    return rskv::decode_with(c, rskv::cache_ws(c), q, tau, k_max, out, sel, n_sel,
+                             static_cast<hipStream_t>(stream), true);
   } catch (const std::bad_alloc&) {
     return fail(RSKV_ENOMEM, "host allocation failed");
   } catch (...) {

@@ -1222,8 +1222,8 @@ bool use_mfma(const rskv_cache* c) {
 }
 
 template <int D, int R>
-hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, const SelectArgs* sa,
-                            hipStream_t st, const KernelEvents* ev) {
+hipError_t attend_mfma_impl(const rskv_cache* c, const DecodeWs& ws, const void* q, int nsplit,
+                            const SelectArgs* sa, hipStream_t st, const KernelEvents* ev) {
   dim3 grid(nsplit, c->B * c->Hkv);
   const WorkCost wc = work_cost(c);
   const double tau = sa ? static_cast<double>(sa->tau) : 0.0;
@@ -1234,29 +1234,29 @@ hipError_t attend_mfma_impl(const rskv_cache* c, const void* q, int nsplit, cons
   return launch(kern, grid, dim3(kAttThreads), 0, st, ev, static_cast<const uint16_t*>(q),
                 static_cast<const uint16_t*>(c->dev.k_full),
                 static_cast<const uint16_t*>(c->dev.v_full), c->dev.n_full,
-                static_cast<const uint16_t*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
+                static_cast<const uint16_t*>(c->dev.vmean), ws.slogit, c->dev.n_spans,
                 static_cast<const uint16_t*>(c->dev.a_k), static_cast<const uint16_t*>(c->dev.a_v),
                 static_cast<const uint16_t*>(c->dev.w_k), static_cast<const uint16_t*>(c->dev.w_v),
-                c->dev.sel_desc, c->dev.n_sel, c->dev.wstart, c->dev.z, c->dev.span_len,
-                c->dev.tok_pad, tau, k_max, wc, so, no, c->Hkv, c->G, c->S, c->Sp, c->Fp, c->Np,
+                ws.sel_desc, ws.n_sel, ws.wstart, ws.z, c->dev.span_len, c->dev.tok_pad, tau,
+                k_max, wc, so, no, c->Hkv, c->G, c->S, c->Sp, c->Fp, c->Np,
                 4 * c->nsplit_max + 1, c->nsplit_max, 1.0f / sqrtf(static_cast<float>(D)),
-                c->dev.part);
+                ws.part);
 }
 
 template <int DT>
-hipError_t attend_valu_impl(const rskv_cache* c, const void* q, int nsplit, hipStream_t st,
-                            const KernelEvents* ev) {
+hipError_t attend_valu_impl(const rskv_cache* c, const DecodeWs& ws, const void* q, int nsplit,
+                            hipStream_t st, const KernelEvents* ev) {
   typedef typename Elem<DT>::T T;
   dim3 grid(nsplit, c->B * c->Hkv);
   return launch(attend_valu_kernel<DT>, grid, dim3(kAttThreads), 0, st, ev,
                 static_cast<const T*>(q), static_cast<const T*>(c->dev.k_full),
                 static_cast<const T*>(c->dev.v_full), c->dev.n_full,
-                static_cast<const T*>(c->dev.vmean), c->dev.slogit, c->dev.n_spans,
+                static_cast<const T*>(c->dev.vmean), ws.slogit, c->dev.n_spans,
                 static_cast<const T*>(c->dev.a_k), static_cast<const T*>(c->dev.a_v),
                 static_cast<const T*>(c->dev.w_k), static_cast<const T*>(c->dev.w_v),
-                c->dev.span_len, c->dev.tok_pad, c->dev.sel, c->dev.n_sel, c->Hkv, c->G, c->d,
+                c->dev.span_len, c->dev.tok_pad, ws.sel, ws.n_sel, c->Hkv, c->G, c->d,
                 c->S, c->Sp, c->Fp, c->Np, c->rank, nsplit, c->nsplit_max,
-                1.0f / sqrtf(static_cast<float>(c->d)), c->dev.part);
+                1.0f / sqrtf(static_cast<float>(c->d)), ws.part);
 }
 
 }  // namespace
@@ -1321,23 +1321,23 @@ int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap) {
   return m > o ? m : o;
 }
 
-hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, const SelectArgs* sa,
-                         hipStream_t st, const KernelEvents* ev) {
+hipError_t launch_attend(const rskv_cache* c, const DecodeWs& ws, const void* q, int nsplit,
+                         const SelectArgs* sa, hipStream_t st, const KernelEvents* ev) {
   if (use_mfma(c)) {
     if (c->d == 128)
-      return c->rank == 16 ? attend_mfma_impl<128, 16>(c, q, nsplit, sa, st, ev)
-                           : attend_mfma_impl<128, 8>(c, q, nsplit, sa, st, ev);
-    return c->rank == 16 ? attend_mfma_impl<64, 16>(c, q, nsplit, sa, st, ev)
-                         : attend_mfma_impl<64, 8>(c, q, nsplit, sa, st, ev);
+      return c->rank == 16 ? attend_mfma_impl<128, 16>(c, ws, q, nsplit, sa, st, ev)
+                           : attend_mfma_impl<128, 8>(c, ws, q, nsplit, sa, st, ev);
+    return c->rank == 16 ? attend_mfma_impl<64, 16>(c, ws, q, nsplit, sa, st, ev)
+                         : attend_mfma_impl<64, 8>(c, ws, q, nsplit, sa, st, ev);
   }
-  return c->dtype == kBF16 ? attend_valu_impl<kBF16>(c, q, nsplit, st, ev)
-                           : attend_valu_impl<kF32>(c, q, nsplit, st, ev);
+  return c->dtype == kBF16 ? attend_valu_impl<kBF16>(c, ws, q, nsplit, st, ev)
+                           : attend_valu_impl<kF32>(c, ws, q, nsplit, st, ev);
 }
 
-hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st,
-                        const KernelEvents* ev) {
-  return launch(merge_kernel, dim3(c->B * c->Hkv, c->G), dim3(128), 0, st, ev, c->dev.part,
-                nsplit, c->nsplit_max, c->Hkv, c->G, c->d, out);
+hipError_t launch_merge(const rskv_cache* c, const DecodeWs& ws, int nsplit, float* out,
+                        hipStream_t st, const KernelEvents* ev) {
+  return launch(merge_kernel, dim3(c->B * c->Hkv, c->G), dim3(128), 0, st, ev, ws.part, nsplit,
+                c->nsplit_max, c->Hkv, c->G, c->d, out);
 }
 
 }  // namespace rskv

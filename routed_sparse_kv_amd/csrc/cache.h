@@ -58,6 +58,22 @@ struct DeviceArrays {
   float* part = nullptr;          // [U][nsplit_max][G][d + 2] partial states
 };
 
+// Decode workspace of one step, written and read only by the decode kernels
+// of that step: routing scores, summary logits, selection lists, per-wave
+// work ranges and partial softmax states.  Every entry a kernel reads was
+// written earlier in the same step (padding reads are masked), so none of
+// it needs clearing.  rskv_decode_step uses the cache's own workspace;
+// rskv_decode_step_static carves one out of the library's static scratch.
+struct DecodeWs {
+  double* z = nullptr;         // [U][S]
+  float* slogit = nullptr;     // [U] Sp spans x G heads (slogit_off)
+  int32_t* sel = nullptr;      // [U][S]
+  int32_t* sel_desc = nullptr; // [U][S][4]
+  int32_t* n_sel = nullptr;    // [U]
+  int32_t* wstart = nullptr;   // [U][4 nsplit_max + 1]
+  float* part = nullptr;       // [U][nsplit_max][G][d + 2]
+};
+
 // Decode kernels timed per profiled step (route, top-k, attend, merge); each
 // has a start and a stop event carried by its own dispatch.
 constexpr int kProfileKernels = 4;
@@ -180,12 +196,14 @@ hipError_t launch_factor(rskv_cache* c, const void* K, const void* V, hipStream_
 
 // Decode, four launches in stream order: routing GEMV (z, summary logits),
 // top-k cap (and the attention work partition when `nwaves` > 0),
-// attention partials, merge of the partials into `out`.  `ev` (may be
-// null) receives the kernel's own start and stop times.
-hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st,
+// attention partials, merge of the partials into `out`, all with the
+// workspace `ws`.  `ev` (may be null) receives the kernel's own start and
+// stop times.
+hipError_t launch_route(const rskv_cache* c, const DecodeWs& ws, const void* q, hipStream_t st,
                         const KernelEvents* ev);
-hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int nwaves, int32_t* sel_out,
-                       int32_t* nsel_out, hipStream_t st, const KernelEvents* ev);
+hipError_t launch_topk(const rskv_cache* c, const DecodeWs& ws, float tau, int k_max, int nwaves,
+                       int32_t* sel_out, int32_t* nsel_out, hipStream_t st,
+                       const KernelEvents* ev);
 int decode_nsplit(const rskv_cache* c, int k_max);
 int decode_nsplit_max(int B, int Hkv, int S, int F, int k_max_cap);
 bool attend_uses_mfma(const rskv_cache* c);
@@ -200,10 +218,23 @@ struct SelectArgs {
   int32_t* nsel_out;  // may be null
 };
 bool attend_fuses_topk(const rskv_cache* c, int k_max);
-hipError_t launch_attend(const rskv_cache* c, const void* q, int nsplit, const SelectArgs* sel,
-                         hipStream_t st, const KernelEvents* ev);
-hipError_t launch_merge(const rskv_cache* c, int nsplit, float* out, hipStream_t st,
-                        const KernelEvents* ev);
+hipError_t launch_attend(const rskv_cache* c, const DecodeWs& ws, const void* q, int nsplit,
+                         const SelectArgs* sel, hipStream_t st, const KernelEvents* ev);
+hipError_t launch_merge(const rskv_cache* c, const DecodeWs& ws, int nsplit, float* out,
+                        hipStream_t st, const KernelEvents* ev);
+
+// The cache's own decode workspace; the bytes a workspace of this cache
+// needs (each array 256-byte aligned) and one laid out from `base`.
+DecodeWs cache_ws(const rskv_cache* c);
+size_t decode_ws_bytes(const rskv_cache* c);
+DecodeWs carve_ws(const rskv_cache* c, void* base);
+
+// One decode step with workspace `ws` (the body of rskv_decode_step; with
+// `profile` false no event is used and nothing is allocated).
+int decode_with(rskv_cache* c, const DecodeWs& ws, const void* q, float tau, int k_max,
+                float* out, int32_t* sel, int32_t* n_sel, hipStream_t st, bool profile);
+// Argument checks of the decode entry points (sets the error message).
+int check_decode(const rskv_cache* c, const void* q, float tau, int k_max, const float* out);
 
 // Streaming segmentation at append time, two launches: launch_close turns
 // the full-resolution run after the last anchor into a new span for every

@@ -444,33 +444,36 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 }
 
 template <int DT, int D>
-hipError_t route_impl(const rskv_cache* c, const void* q, hipStream_t st, const KernelEvents* ev) {
+hipError_t route_impl(const rskv_cache* c, const DecodeWs& ws, const void* q, hipStream_t st,
+                      const KernelEvents* ev) {
   typedef typename Elem<DT>::T T;
   const int nblk = (c->S + kSpansPerBlock - 1) / kSpansPerBlock;
   dim3 grid(nblk, c->B * c->Hkv);
   return launch(route_kernel<DT, D>, grid, dim3(kRouteThreads), 0, st, ev,
                 static_cast<const T*>(q), static_cast<const T*>(c->dev.summary), c->dev.log_len,
                 c->dev.n_spans, c->dev.proj, c->n_proj, c->Hkv, c->G, c->S, c->Sp, c->alpha,
-                1.0f / sqrtf(static_cast<float>(D)), c->dev.z, c->dev.slogit);
+                1.0f / sqrtf(static_cast<float>(D)), ws.z, ws.slogit);
 }
 
 }  // namespace
 
-hipError_t launch_route(const rskv_cache* c, const void* q, hipStream_t st,
+hipError_t launch_route(const rskv_cache* c, const DecodeWs& ws, const void* q, hipStream_t st,
                         const KernelEvents* ev) {
   if (c->dtype == kBF16)
-    return c->d == 128 ? route_impl<kBF16, 128>(c, q, st, ev) : route_impl<kBF16, 64>(c, q, st, ev);
-  return c->d == 128 ? route_impl<kF32, 128>(c, q, st, ev) : route_impl<kF32, 64>(c, q, st, ev);
+    return c->d == 128 ? route_impl<kBF16, 128>(c, ws, q, st, ev)
+                       : route_impl<kBF16, 64>(c, ws, q, st, ev);
+  return c->d == 128 ? route_impl<kF32, 128>(c, ws, q, st, ev)
+                     : route_impl<kF32, 64>(c, ws, q, st, ev);
 }
 
-hipError_t launch_topk(const rskv_cache* c, float tau, int k_max, int nwaves, int32_t* sel_out,
-                       int32_t* nsel_out, hipStream_t st, const KernelEvents* ev) {
+hipError_t launch_topk(const rskv_cache* c, const DecodeWs& ws, float tau, int k_max, int nwaves,
+                       int32_t* sel_out, int32_t* nsel_out, hipStream_t st,
+                       const KernelEvents* ev) {
   const WorkCost wc = work_cost(c);
-  return launch(topk_kernel, dim3(c->B * c->Hkv), dim3(kTopkThreads), 0, st, ev, c->dev.z,
+  return launch(topk_kernel, dim3(c->B * c->Hkv), dim3(kTopkThreads), 0, st, ev, ws.z,
                 c->dev.n_spans, c->dev.n_full, c->dev.span_len, c->dev.tok_pad, c->Hkv, c->G, c->S,
-                c->Sp, static_cast<double>(tau), k_max, c->dev.slogit, c->dev.sel,
-                c->dev.sel_desc, c->dev.n_sel, sel_out, nsel_out, wc, nwaves,
-                4 * c->nsplit_max + 1, c->dev.wstart);
+                c->Sp, static_cast<double>(tau), k_max, ws.slogit, ws.sel, ws.sel_desc, ws.n_sel,
+                sel_out, nsel_out, wc, nwaves, 4 * c->nsplit_max + 1, ws.wstart);
 }
 
 }  // namespace rskv
