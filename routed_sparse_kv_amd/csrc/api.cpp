@@ -980,7 +980,9 @@ int rskv_profile_read(rskv_cache* c, rskv_profile* p) {
   auto& pr = c->prof;
   constexpr int kEv = 2 * rskv::kProfileKernels;
   for (size_t i = 0; i + kEv <= pr.pending.size(); i += kEv) {
-    RSKV_HIP(hipEventSynchronize(pr.pending[i + kEv - 1]), "event sync");
+    int last = kEv - 1;  // the step's last recorded event
+    while (last > 0 && pr.pending[i + last] == nullptr) --last;
+    RSKV_HIP(hipEventSynchronize(pr.pending[i + last]), "event sync");
     for (int k = 0; k < rskv::kProfileKernels; ++k) {
       if (pr.pending[i + 2 * k] == nullptr) continue;  // kernel not launched this step
       float ms = 0.f;

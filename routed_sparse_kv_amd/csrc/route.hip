@@ -49,11 +49,13 @@ template <int D>
 struct RouteTiles {
   bf16x8 sa[kTilesPerWave][D / 32];
   bf16x8 qb[D / 32];
+  float ll[kTilesPerWave][4];  // ln|S_j| of spans j0 + 4 (lane / 16) + i
 };
 
 template <int D>
 __device__ __forceinline__ void route_load_bf16(const uint16_t* __restrict__ q,
-                                                const uint16_t* __restrict__ summ, int b, int u,
+                                                const uint16_t* __restrict__ summ,
+                                                const float* __restrict__ log_len, int b, int u,
                                                 int h, int Hkv, int ns, int S, int G,
                                                 RouteTiles<D>& rt) {
   constexpr int KK = D / 32;
@@ -70,6 +72,12 @@ __device__ __forceinline__ void route_load_bf16(const uint16_t* __restrict__ q,
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       rt.sa[t][kk] = *reinterpret_cast<const bf16x8*>(row + 32 * kk + 8 * grp);
+    // the logits' size bias, loaded with the tiles (not after the products)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jl = jw + 16 * t + 4 * grp + i;
+      rt.ll[t][i] = log_len[static_cast<size_t>(b) * S + (jl < ns ? jl : 0)];
+    }
   }
   const uint16_t* qp = q + (static_cast<size_t>(b) * Hkv * G + static_cast<size_t>(h) * G +
                             (head_ok ? g16 : 0)) * D;
@@ -79,8 +87,8 @@ __device__ __forceinline__ void route_load_bf16(const uint16_t* __restrict__ q,
 }
 
 template <int D>
-__device__ __forceinline__ void route_tiles_bf16(RouteTiles<D>& rt, const float* __restrict__ log_len,
-                                                 int b, int u, int ns, int S, int G, float alpha,
+__device__ __forceinline__ void route_tiles_bf16(RouteTiles<D>& rt, int u, int ns, int S, int G,
+                                                 float alpha,
                                                  float inv_sqrt_d, const double* rho,
                                                  double* __restrict__ z_out,
                                                  float* __restrict__ slogit_u) {
@@ -119,7 +127,7 @@ __device__ __forceinline__ void route_tiles_bf16(RouteTiles<D>& rt, const float*
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 4 * grp + i;
-        o[i] = j < ns ? lg[i] * inv_sqrt_d + log_len[static_cast<size_t>(b) * S + j] : 0.f;
+        o[i] = j < ns ? lg[i] * inv_sqrt_d + rt.ll[t][i] : 0.f;
       }
       *reinterpret_cast<f32x4*>(slogit_u + slogit_off(j0 + 4 * grp, g16, G)) = o;
     }
@@ -190,18 +198,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
   // summary tiles first: their loads overlap forming rho
   [[maybe_unused]] RouteTiles<D> rt;
-  if constexpr (DT == kBF16) route_load_bf16<D>(q, summ, b, u, h, Hkv, ns, S, G, rt);
+  if constexpr (DT == kBF16) route_load_bf16<D>(q, summ, log_len, b, u, h, Hkv, ns, S, G, rt);
 
   __shared__ double qbar[D];
   __shared__ double rho[D];
   __shared__ float qh[kMaxG][D];
   const size_t qbase = (static_cast<size_t>(b) * Hkv * G + static_cast<size_t>(h) * G) * D;
   if (tid < D) {
+    // the group's loads are issued together, then summed in head order
+    float x[kMaxG];
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g)
+      x[g] = g < G ? E::ld(q, qbase + static_cast<size_t>(g) * D + tid) : 0.f;
     double sum = 0.0;
-    for (int g = 0; g < G; ++g) {
-      const float x = E::ld(q, qbase + static_cast<size_t>(g) * D + tid);
-      qh[g][tid] = x;
-      sum += static_cast<double>(x);
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) {
+      if (g < G) {
+        qh[g][tid] = x[g];
+        sum += static_cast<double>(x[g]);
+      }
     }
     qbar[tid] = sum / static_cast<double>(G);
   }
@@ -219,7 +234,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
   __syncthreads();
   if constexpr (DT == kBF16) {
-    route_tiles_bf16<D>(rt, log_len, b, u, ns, S, G, alpha, inv_sqrt_d, rho, z_all, slogit_u);
+    route_tiles_bf16<D>(rt, u, ns, S, G, alpha, inv_sqrt_d, rho, z_all, slogit_u);
   } else {
     route_spans_f32<D>(summ, log_len, b, u, ns, S, G, alpha, inv_sqrt_d, rho, qh, z_all,
                        slogit_u);
