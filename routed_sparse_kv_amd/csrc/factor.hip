@@ -608,6 +608,484 @@ __device__ __forceinline__ void gram_store(const double (&g)[B][B], int m, int L
   __syncthreads();
 }
 
+// ---- top eigenpairs of the Gram matrix (closing path)
+//
+// The closing needs only the r_j largest eigenpairs of the m x m Gram
+// matrix G.  G is reduced to a symmetric tridiagonal T = Q^T G Q by m - 2
+// Householder reflectors (two barriers each); the r_j + 1 largest
+// eigenvalues of T come from Sturm counts by multisection (a group of
+// lanes per eigenvalue, no barriers); the eigenvectors of T from twisted
+// factorisations T - lambda I = N_t D_t N_t^T (one lane per eigenvalue,
+// three O(m) passes), which are accurate while each eigenvalue is
+// separated from its neighbours; Q's reflectors map them back to
+// eigenvectors of G.  When two of the r_j + 1 largest eigenvalues lie
+// within kClusterGap of the largest (the truncation or the basis inside
+// the cluster is then ill-determined for this method), the closing takes
+// the Jacobi path instead.
+constexpr int kMaxEig = 33;          // r_j <= 32 eigenpairs and the first one left out
+constexpr double kClusterGap = 1e-7; // relative to the largest eigenvalue
+constexpr double kSignificant = 1e-9;
+constexpr double kPivot = 1e-150;    // smallest pivot magnitude of the scaled T
+
+struct EigShared {
+  double d[128];    // diagonal of T (scaled after the reduction)
+  double e[128];    // e[k] = T[k][k+1]
+  double tau[128];  // reflector k: I - tau_k v v^T
+  double vb[2][128];  // the current and next reflector vector, 0 outside k + 1 .. m - 1
+  double p[128];    // tau_k G v of the current step, 0 outside the trailing block
+  double red[2][kCloseWaves];
+  double lam[kMaxEig];  // eigenvalues of the scaled T, largest first
+  double zn[16];        // 1 / ||z|| of the tridiagonal eigenvectors of a batch
+  double lim[3];        // Gershgorin interval of the scaled T, and the scale
+};
+
+// Sums over aligned groups of V lanes (V a power of two <= 16) by DPP
+// (quad xor 1, quad xor 2, half-row mirror, row mirror: each step adds the
+// other half of the current block, so every lane ends with the sum).
+template <int V>
+__device__ __forceinline__ double group_sum_dpp(double a) {
+  if constexpr (V >= 2) a += dpp_f64<0xb1>(a);
+  if constexpr (V >= 4) a += dpp_f64<0x4e>(a);
+  if constexpr (V >= 8) a += dpp_f64<0x141>(a);
+  if constexpr (V >= 16) a += dpp_f64<0x140>(a);
+  return a;
+}
+
+// Sum over a wave by DPP within rows of 16 lanes and lane reads across
+// them (no LDS traffic); the result is uniform.
+__device__ __forceinline__ double wave_sum_dpp(double a) {
+  a = group_sum_dpp<16>(a);
+  auto rl = [&](int l) {
+    const long long v = __double_as_longlong(a);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(v), l);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), l);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+  };
+  return (rl(0) + rl(16)) + (rl(32) + rl(48));
+}
+
+// Householder reduction of the symmetric m x m matrix A (m <= 128, both
+// triangles stored in LDS with pitch P) to tridiagonal form: reflector k,
+// H_k = I - tau_k v v^T with v_{k+1} = 1, zeroes row and column k beyond
+// the first off-diagonal entry.  The matrix lives in registers: row i
+// belongs to the L lanes tid / L = i, lane h holding columns h + L c
+// (c < C).  Once row k + 1 is final its lanes copy it to LDS, and one wave
+// forms reflector k + 1 from the copy (two entries per lane, one wave sum
+// for the norm): v scaled, zero outside k + 2 .. m - 1, goes to vb (double
+// buffered) and back into row k + 1 of A (kept for the back-transform).
+// Each step is then
+//   p = tau A v (one multiply-add per entry, a DPP sum per row; p = 0 on
+//   the rows outside the trailing block), barrier,
+//   A -= v w^T + w v^T with w = p - (tau/2)(p.v) v, written as
+//   a_ij -= v_i p_j + (p_i - tau (p.v) v_i) v_j (two multiply-adds per
+//   entry; v and p vanish outside the trailing block, so no entry needs a
+//   branch), the next reflector, barrier.
+// Column blocks of 8 left of the trailing block are skipped.  d, e receive
+// T; tau the reflectors.  Ends with a barrier.
+typedef __attribute__((address_space(3))) double lds_f64;
+typedef __attribute__((address_space(3))) EigShared lds_eig;
+template <int L, int C>
+__device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared& es_) {
+  constexpr int kBlk = C < 8 ? C : 8;
+  lds_f64* A = (lds_f64*)A_;
+  lds_eig* es = (lds_eig*)&es_;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int i = tid / L;
+  const int h = tid - i * L;
+  const bool own = i < m;
+  // whole rows of 128 entries are read: i, j < 128 and P <= 130 keep every
+  // address inside the LDS work array; entries past m are replaced by 0
+  double a[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = h + L * c;
+    const double x = A[i * P + j];
+    a[c] = own && j < m ? x : 0.0;
+  }
+  if (tid < 128) es->p[tid] = 0.0;
+  // reflector r (r <= m - 3) from row r of A in LDS, by the 64 lanes of
+  // one wave (two entries each): v scaled to v_{r+1} = 1 into vb and back
+  // into row r (kept for the back-transform), d_r, e_r = beta, tau_r
+  auto reflector = [&](int r) {
+    lds_f64* row = A + r * P;
+    const int j0 = r + 2 + lane, j1 = j0 + kWave;
+    const double x0 = j0 < m ? row[j0] : 0.0;
+    const double x1 = j1 < m ? row[j1] : 0.0;
+    const double q = wave_sum_dpp(fma(x0, x0, x1 * x1));
+    const double al = row[r + 1];
+    double tau = 0.0, scl = 0.0, beta = al;
+    if (q > 0.0) {
+      beta = -copysign(sqrt(fma(al, al, q)), al);
+      tau = (beta - al) / beta;
+      scl = 1.0 / (al - beta);
+    }
+    lds_f64* vb = es->vb[r & 1];
+    vb[lane] = lane == r + 1 ? 1.0 : (lane > r + 1 && lane < m ? row[lane] * scl : 0.0);
+    vb[lane + kWave] = lane + kWave == r + 1
+                           ? 1.0
+                           : (lane + kWave > r + 1 && lane + kWave < m ? row[lane + kWave] * scl : 0.0);
+    if (j0 < m) row[j0] = x0 * scl;
+    if (j1 < m) row[j1] = x1 * scl;
+    if (lane == 0) {
+      es->d[r] = row[r];
+      row[r + 1] = 1.0;
+      es->e[r] = beta;
+      es->tau[r] = tau;
+    }
+  };
+  if (m >= 3 && tid < kWave) reflector(0);
+  __syncthreads();
+  for (int k = 0; k + 2 < m; ++k) {
+    const double tau = es->tau[k];
+    const lds_f64* vb = es->vb[k & 1];
+    const bool act = own && i > k;
+    double pi = 0.0, vi = 0.0;
+    if (tau != 0.0) {
+      double part = 0.0;
+#pragma unroll
+      for (int b = 0; b < C / kBlk; ++b) {
+        if ((L - 1) + L * (kBlk * b + kBlk - 1) < k + 1) continue;
+#pragma unroll
+        for (int u = 0; u < kBlk; ++u) part = fma(a[kBlk * b + u], vb[h + L * (kBlk * b + u)], part);
+      }
+      part = group_sum_dpp<L>(part);
+      const double v = vb[i & 127];
+      pi = act ? tau * part : 0.0;
+      vi = act ? v : 0.0;
+    }
+    if (h == 0 && i < 128) es->p[i] = pi;
+    const double pv = wave_sum_dpp(h == 0 ? pi * vi : 0.0);
+    if (lane == 0) es->red[1][tid / kWave] = pv;
+    __syncthreads();
+    if (tau != 0.0) {
+      const double tpv = tau * ((es->red[1][0] + es->red[1][1]) + (es->red[1][2] + es->red[1][3]));
+      const double ci = pi - tpv * vi;  // w_i - (tau/2)(p.v) v_i
+#pragma unroll
+      for (int b = 0; b < C / kBlk; ++b) {
+        if ((L - 1) + L * (kBlk * b + kBlk - 1) < k + 1) continue;
+#pragma unroll
+        for (int u = 0; u < kBlk; ++u) {
+          const int j = h + L * (kBlk * b + u);
+          const double x = fma(-vi, es->p[j], a[kBlk * b + u]);
+          a[kBlk * b + u] = fma(-ci, vb[j], x);
+        }
+      }
+    }
+    if (k + 3 < m) {
+      // row k + 1 is final: to LDS as whole rows of L C entries (what
+      // spills past column m - 1 lands on later rows' LDS copies, which are
+      // not read before their own rows overwrite them), then the next
+      // reflector from it
+      if (i == k + 1) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) A[i * P + h + L * c] = a[c];
+      }
+      if (tid / kWave == ((k + 1) * L) / kWave) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        reflector(k + 1);
+      }
+    } else {  // last step: the trailing 2 x 2 block
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int j = h + L * c;
+        if (i == m - 2 && j == m - 2) es->d[m - 2] = a[c];
+        if (i == m - 2 && j == m - 1) es->e[m - 2] = a[c];
+        if (i == m - 1 && j == m - 1) es->d[m - 1] = a[c];
+      }
+    }
+    __syncthreads();
+  }
+  if (m <= 2) {
+    if (own) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int j = h + L * c;
+        if (j == i) es->d[i] = a[c];
+        if (i == 0 && j == 1 && m == 2) es->e[0] = a[c];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Rescales two consecutive terms of a three-term recurrence by the same
+// power of two (their ratio is kept) so that they stay near 1.
+__device__ __forceinline__ void rescale2(double& a, double& b) {
+  const int ex = __builtin_amdgcn_frexp_exp(fabs(a) + fabs(b));
+  a = __builtin_amdgcn_ldexp(a, -ex);
+  b = __builtin_amdgcn_ldexp(b, -ex);
+}
+
+// Number of eigenvalues of the tridiagonal T below x: the sign changes
+// along the leading principal minors det(T_i - x I), i = 0..m (Sturm),
+// from their three-term recurrence (de[i] = (d_i, e_{i-1}^2)); a zero minor
+// counts as positive (the next minor then has the sign opposite to the one
+// before, so the count is unchanged).  The last two minors are rescaled
+// every 4 steps.
+__device__ __forceinline__ int sturm_count(const double2* __restrict__ de, int m, double x) {
+  double p0 = 1.0, p1 = de[0].x - x;
+  int cnt = p1 < 0.0;
+  int i = 1;
+  // de is padded to 128 + 4 entries: the block loaded ahead stays in bounds
+  double2 qn[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) qn[u] = de[1 + u];
+  for (; i + 4 <= m; i += 4) {
+    double2 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      q[u] = qn[u];
+      qn[u] = de[i + 4 + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const double p2 = fma(q[u].x - x, p1, -q[u].y * p0);
+      cnt += (p2 < 0.0) != (p1 < 0.0);
+      p0 = p1;
+      p1 = p2;
+    }
+    rescale2(p0, p1);
+  }
+  for (; i < m; ++i) {
+    const double2 q = de[i];
+    const double p2 = fma(q.x - x, p1, -q.y * p0);
+    cnt += (p2 < 0.0) != (p1 < 0.0);
+    p0 = p1;
+    p1 = p2;
+  }
+  return cnt;
+}
+
+// The nev largest eigenvalues of T (es.d, es.e; m) into es.lam, largest
+// first, for T scaled by a power of two to entries of magnitude <= 1
+// (es.d and es.e are scaled in place, the scale goes to es.lim[2], and
+// de receives (d_i, e_{i-1}^2)).  A group of g lanes per eigenvalue
+// evaluates g Sturm counts spread evenly over its interval and keeps the
+// sub-interval where the count passes the eigenvalue's index, until the
+// interval is a few ulps wide.  Ends with a barrier.
+__device__ __forceinline__ void top_eigenvalues(int m, int nev, EigShared& es, double2* de) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  if (tid < kWave) {
+    double mx = 0.0;
+    for (int i = lane; i < m; i += kWave) {
+      mx = fmax(mx, fabs(es.d[i]));
+      if (i + 1 < m) mx = fmax(mx, fabs(es.e[i]));
+    }
+    mx = wave_max(mx);
+    const double sc =
+        mx > 0.0 ? __builtin_amdgcn_ldexp(1.0, -__builtin_amdgcn_frexp_exp(mx)) : 1.0;
+    double lo = 1e300, hi = -1e300;
+    for (int i = lane; i < m; i += kWave) {
+      const double di = es.d[i] * sc;
+      const double el = i > 0 ? es.e[i - 1] * sc : 0.0;
+      const double er = i + 1 < m ? es.e[i] * sc : 0.0;
+      lo = fmin(lo, di - fabs(el) - fabs(er));
+      hi = fmax(hi, di + fabs(el) + fabs(er));
+      de[i] = make_double2(di, el * el);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane; i < m; i += kWave) {
+      es.d[i] *= sc;
+      if (i + 1 < m) es.e[i] *= sc;
+    }
+    wave_min_max_f64(lo, hi);
+    if (lane == 0) {
+      es.lim[0] = lo;
+      es.lim[1] = hi;
+      es.lim[2] = sc;
+    }
+  }
+  __syncthreads();
+  int g = kWave;
+  while (g > 1 && g * nev > kCloseThreads) g >>= 1;
+  const int kk = tid / g;
+  const int l = tid - kk * g;
+  if (kk < nev) {
+    const int idx = m - 1 - kk;  // ascending index of the kk-th largest
+    constexpr double kEps = 2.220446049250313e-16;
+    double lo = es.lim[0], hi = es.lim[1];
+    const double pad = 4.0 * kEps * fmax(fabs(lo), fabs(hi)) + 4.0 * kEps;
+    lo -= pad;
+    hi += pad;
+    const int base = lane & ~(g - 1);
+    for (int it = 0; it < 64; ++it) {
+      if (hi - lo <= 2.0 * kEps * fmax(fabs(lo), fabs(hi)) + 2.0 * kEps) break;
+      const double w = (hi - lo) / static_cast<double>(g + 1);
+      const double x = fma(w, static_cast<double>(l + 1), lo);
+      const bool above = sturm_count(de, m, x) > idx;
+      const unsigned long long bal = __ballot(above);
+      const unsigned long long gm = g == kWave ? bal : (bal >> base) & ((1ull << g) - 1ull);
+      const int s = gm ? __builtin_ctzll(gm) : g;
+      const double nlo = s == 0 ? lo : fma(w, static_cast<double>(s), lo);
+      const double nhi = s == g ? hi : fma(w, static_cast<double>(s + 1), lo);
+      if (!(nhi - nlo < hi - lo)) break;  // no progress left at this width
+      lo = nlo;
+      hi = nhi;
+    }
+    if (l == 0) es.lam[kk] = 0.5 * (lo + hi);
+  }
+  __syncthreads();
+}
+
+// A pivot of a factorisation of T - lam I kept away from zero and
+// infinity (its sign kept).
+__device__ __forceinline__ double guard_pivot(double x) {
+  const double y = fabs(x) < kPivot ? (x < 0.0 ? -kPivot : kPivot) : x;
+  return fmin(fmax(y, -1.0 / kPivot), 1.0 / kPivot);
+}
+
+// Eigenvector of the scaled tridiagonal T (de[i] = (d_i, e_{i-1}^2), e)
+// for its eigenvalue lam by a twisted factorisation.  The top-down pivots
+// D+_i = P_{i+1} / P_i and bottom-up pivots D-_i = Q_i / Q_{i+1} are ratios
+// of the leading and trailing minors of T - lam I (three-term recurrences,
+// so the serial dependence is one multiply-add per step); gamma_i = D+_i +
+// D-_i - (d_i - lam), and at the twist t = argmin |gamma_i| the vector is
+// z_t = 1, z_i = -(e_i / D+_i) z_{i+1} above t and z_{i+1} = -(e_i /
+// D-_{i+1}) z_i below.  z (stride 16 doubles) holds D+ first, then the
+// recomputed D- below t, then the vector.  Returns ||z||^2.
+__device__ double twisted_vector(const double2* __restrict__ de, const double* __restrict__ e,
+                                 int m, double lam, double* __restrict__ z) {
+  double pa = 1.0, pb = de[0].x - lam;
+  z[0] = guard_pivot(pb);
+#pragma unroll 4
+  for (int i = 1; i < m; ++i) {
+    const double2 q = de[i];
+    const double pc = fma(q.x - lam, pb, -q.y * pa);
+    z[16 * i] = guard_pivot(pc * recip(pb));
+    pa = pb;
+    pb = pc;
+    if ((i & 3) == 0) rescale2(pa, pb);
+  }
+  double best = fabs(z[16 * (m - 1)]);
+  int t = m - 1;
+  double qa = 1.0, qb = de[m - 1].x - lam;
+#pragma unroll 4
+  for (int i = m - 2; i >= 0; --i) {
+    const double di = de[i].x - lam;
+    const double qc = fma(di, qb, -de[i + 1].y * qa);
+    const double gam = fabs(z[16 * i] + guard_pivot(qc * recip(qb)) - di);
+    if (gam < best) {
+      best = gam;
+      t = i;
+    }
+    qa = qb;
+    qb = qc;
+    if ((i & 3) == 0) rescale2(qa, qb);
+  }
+  // bottom-up pivots of rows t + 1 .. m - 1 (the same recurrence again)
+  qa = 1.0;
+  qb = de[m - 1].x - lam;
+  if (t < m - 1) z[16 * (m - 1)] = guard_pivot(qb);
+  for (int i = m - 2; i > t; --i) {
+    const double qc = fma(de[i].x - lam, qb, -de[i + 1].y * qa);
+    z[16 * i] = guard_pivot(qc * recip(qb));
+    qa = qb;
+    qb = qc;
+    if ((i & 3) == 0) rescale2(qa, qb);
+  }
+  double zi = 1.0, nrm = 1.0;
+  for (int i = t + 1; i < m; ++i) {
+    zi = -(e[i - 1] * recip(z[16 * i])) * zi;
+    z[16 * i] = zi;
+    nrm = fma(zi, zi, nrm);
+  }
+  zi = 1.0;
+  for (int i = t - 1; i >= 0; --i) {
+    zi = -(e[i] * recip(z[16 * i])) * zi;
+    z[16 * i] = zi;
+    nrm = fma(zi, zi, nrm);
+  }
+  z[16 * t] = 1.0;
+  return nrm;
+}
+
+// Eigenvectors of G for the rj largest eigenvalues in es.lam (rj <= 32):
+// the twisted vectors of T (one lane each, in batches of 16 held in `zs`,
+// 16 m doubles of LDS), normalised and spread over groups of V lanes (EV
+// elements per lane), mapped back through the reflectors kept in A (the
+// next reflector's entries are loaded while the current one is applied),
+// then written as rows lambda_k u_k^T of A (pitch P) with sig[k] =
+// lambda_k, top[k] = k.  Ends with a barrier.
+template <int V, int EV>
+__device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, EigShared& es,
+                                 const double2* de, double* zs, FactorShared& sh) {
+  const int tid = threadIdx.x;
+  const int kk = tid / V;
+  const int l = tid - kk * V;
+  double y[EV];
+#pragma unroll
+  for (int c = 0; c < EV; ++c) y[c] = 0.0;
+  for (int b0 = 0; b0 < rj; b0 += 16) {
+    if (tid < 16 && b0 + tid < rj) {
+      const double nrm = twisted_vector(de, es.e, m, es.lam[b0 + tid], zs + tid);
+      es.zn[tid] = rsqrt_nr(nrm);
+    }
+    __syncthreads();
+    if (kk >= b0 && kk < b0 + 16 && kk < rj) {
+      const double f = es.zn[kk - b0];
+#pragma unroll
+      for (int c = 0; c < EV; ++c) {
+        const int i = l + V * c;
+        if (i < m) y[c] = zs[16 * i + (kk - b0)] * f;
+      }
+    }
+    __syncthreads();
+  }
+  // u = H_0 H_1 ... H_{m-3} z, the last reflector first
+  // row s of A holds reflector s scaled (v_{s+1} = 1); reads stay inside
+  // the work array for i < 128
+  auto load_v = [&](int s, double (&v)[EV]) {
+    const lds_f64* rs = (const lds_f64*)(A + s * P);
+#pragma unroll
+    for (int c = 0; c < EV; ++c) {
+      const int i = l + V * c;
+      const double x = rs[i];
+      v[c] = i > s && i < m ? x : 0.0;
+    }
+  };
+  double vn[EV];
+  if (m >= 3) load_v(m - 3, vn);
+  for (int s = m - 3; s >= 0; --s) {
+    double v[EV];
+#pragma unroll
+    for (int c = 0; c < EV; ++c) v[c] = vn[c];
+    if (s > 0) load_v(s - 1, vn);
+    const double ts = es.tau[s];
+    if (ts == 0.0) continue;
+    double d0 = 0.0, d1 = 0.0;
+#pragma unroll
+    for (int c = 0; c < EV; ++c) {
+      if (c & 1)
+        d1 = fma(v[c], y[c], d1);
+      else
+        d0 = fma(v[c], y[c], d0);
+    }
+    const double f = ts * group_sum_dpp<V>(d0 + d1);
+#pragma unroll
+    for (int c = 0; c < EV; ++c) y[c] = fma(-f, v[c], y[c]);
+  }
+  __syncthreads();
+  if (kk < rj) {
+    const double lam = es.lam[kk] / es.lim[2];
+#pragma unroll
+    for (int c = 0; c < EV; ++c) {
+      const int i = l + V * c;
+      if (i < m) A[kk * P + i] = lam * y[c];
+    }
+    if (l == 0) {
+      sh.sig[kk] = lam;
+      sh.top[kk] = kk;
+    }
+  }
+  __syncthreads();
+}
+
 template <int DT>
 __global__ __launch_bounds__(kCloseThreads) void close_kernel(
     const float* __restrict__ h_new, const float* __restrict__ theta,
@@ -626,8 +1104,9 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
   __shared__ FactorShared sh;
   __shared__ __align__(16) double work[kCloseWork];
   __shared__ __align__(16) float stage[kBlock * (128 + 4)];  // a streamed block of X rows
-  __shared__ double part[kCloseThreads];  // partial column sums
+  __shared__ __align__(16) double part[kCloseThreads + 8];  // partial column sums; (d, e^2) pairs
   __shared__ double red[kCloseWaves];
+  __shared__ EigShared es;
   const int tid = threadIdx.x;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -656,10 +1135,10 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
     const int gs = jacobi_group<kCloseThreads>(m);
     int Lp = gs;  // rows of G padded with zeros to gs * E columns, E a power of two
     while (Lp < m) Lp *= 2;
-    const int P = jacobi_pitch(Lp, gs);
-    const bool x_after = sizeof(double) * m * P + sizeof(float) * static_cast<size_t>(n) * xp <=
+    const int Pj = jacobi_pitch(Lp, gs);
+    const bool x_after = sizeof(double) * m * Pj + sizeof(float) * static_cast<size_t>(n) * xp <=
                          sizeof(double) * kCloseWork;
-    float* const x_post = x_after ? reinterpret_cast<float*>(work + m * P) : nullptr;
+    float* const x_post = x_after ? reinterpret_cast<float*>(work + m * Pj) : nullptr;
     float* const x_pre = rows_form ? reinterpret_cast<float*>(work) : x_post;
     // rows [t0, t0 + rb) of X into dst (row pitch xp)
     auto load_rows = [&](int t0, int rb, float* dst) {
@@ -735,30 +1214,70 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
     }
     __syncthreads();
 
-    // ---- Gram matrix, Jacobi, the r_j largest (sig = sigma^2)
-    auto gram = [&](auto bsize) {
-      constexpr int B = decltype(bsize)::value;
-      double g[B][B] = {};
-      if (rows_form) {
-        gram_accumulate<B, true>(x_pre, xp, m, d, g);
-        __syncthreads();  // X is read before G takes its place
-      } else {
-        for_blocks(x_pre, [&](const float* xr, int, int rb) {
-          gram_accumulate<B, false>(xr, xp, m, rb, g);
-        });
-      }
-      gram_store<B>(g, m, Lp, work, P);
+    // ---- Gram matrix and its r_j largest eigenpairs (sig = sigma^2): the
+    // tridiagonal path, or Jacobi when the spectrum is clustered there
+    auto gram = [&](int Lg, int Pg) {
+      auto run = [&](auto bsize) {
+        constexpr int B = decltype(bsize)::value;
+        double g[B][B] = {};
+        if (rows_form) {
+          gram_accumulate<B, true>(x_pre, xp, m, d, g);
+          __syncthreads();  // X is read before G takes its place
+        } else {
+          for_blocks(x_pre, [&](const float* xr, int, int rb) {
+            gram_accumulate<B, false>(xr, xp, m, rb, g);
+          });
+        }
+        gram_store<B>(g, m, Lg, work, Pg);
+      };
+      if (m > 64)
+        run(std::integral_constant<int, 8>());
+      else if (m > 32)
+        run(std::integral_constant<int, 4>());
+      else if (m > 16)
+        run(std::integral_constant<int, 2>());
+      else
+        run(std::integral_constant<int, 1>());
     };
-    if (m > 64)
-      gram(std::integral_constant<int, 8>());
-    else if (m > 32)
-      gram(std::integral_constant<int, 4>());
-    else if (m > 16)
-      gram(std::integral_constant<int, 2>());
-    else
-      gram(std::integral_constant<int, 1>());
-    jacobi_sweeps<kCloseThreads>(work, m, Lp, P, sh);
-    const int rj = top_rows<kCloseThreads>(work, m, Lp, P, rank, sh);
+    const int rmax = min(rank, m);
+    int P = Pj;
+    int rj = 0;
+    bool tri = rmax <= kMaxEig - 1;
+    if (tri) {
+      const int Pt = m + 1 + (m & 1);  // odd pitch: a wave's rows fall in distinct banks
+      gram(m, Pt);
+      if (m > 64)
+        tridiagonalize<2, 64>(work, m, Pt, es);
+      else if (m > 32)
+        tridiagonalize<4, 16>(work, m, Pt, es);
+      else if (m > 16)
+        tridiagonalize<8, 4>(work, m, Pt, es);
+      else
+        tridiagonalize<16, 1>(work, m, Pt, es);
+      const int nev = min(rmax + 1, m);
+      double2* de = reinterpret_cast<double2*>(part);  // free after the summary
+      top_eigenvalues(m, nev, es, de);
+      const double l0 = es.lam[0];
+      for (int k = 0; k + 1 < nev; ++k)
+        if (es.lam[k] - es.lam[k + 1] <= kClusterGap * l0 && es.lam[k] > kSignificant * l0)
+          tri = false;
+      if (tri) {
+        double* zs = reinterpret_cast<double*>(stage);
+        if (rmax <= 16)
+          top_eigenvectors<16, 8>(work, m, Pt, rmax, es, de, zs, sh);
+        else
+          top_eigenvectors<8, 16>(work, m, Pt, rmax, es, de, zs, sh);
+        P = Pt;
+        rj = rmax;
+      } else if (rows_form) {
+        load_rows(0, n, x_pre);  // G took X's place
+      }
+    }
+    if (!tri) {
+      gram(Lp, Pj);
+      jacobi_sweeps<kCloseThreads>(work, m, Lp, Pj, sh);
+      rj = top_rows<kCloseThreads>(work, m, Lp, Pj, rank, sh);
+    }
     if (rows_form && x_post != nullptr) load_rows(0, n, x_post);
 
     auto a_store = [&](int t, int k, double val) {

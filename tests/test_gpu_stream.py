@@ -217,3 +217,55 @@ def test_streaming_anchor_at_the_end():
     wl.H[:, -1] = wl.H.max() + 1.0  # the last position becomes an anchor
     n_closed = _run_stream(wl, ["abbbaabt", "bbabbbab"])
     assert n_closed == 3
+
+
+def _run_patterns(runs_per_seq):
+    """Append patterns that close runs of the given lengths in each sequence
+    (one anchor first, to close the prefill tail), padded to equal length."""
+    pats = ["a" + "".join("b" * n + "a" for n in runs) for runs in runs_per_seq]
+    steps = max(len(p) for p in pats)
+    return [p + "b" * (steps - len(p)) for p in pats], steps
+
+
+# Closed runs across the closing kernel's forms: the Gram matrix is X X^T
+# (n x n) up to n = d rows and X^T X (d x d) beyond.
+LONG_RUNS = {
+    "bf16_d128": ("serving_b16_bf16", 2, [[128, 150], [64, 1, 2, 17, 100]]),
+    "f32_d64": ("tiny_fp32_2k", 1, [[64, 90, 5]]),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("case", sorted(LONG_RUNS))
+def test_streaming_long_runs(case):
+    name, B, runs = LONG_RUNS[case]
+    pats, steps = _run_patterns(runs)
+    over = dict(B=B, T=700, tail_capacity=steps + 8, steps=steps)
+    if name == "tiny_fp32_2k":
+        over["append"] = True
+    say(f"[stream long {case}] {steps} appends closing runs {runs}")
+    wl = W.generate(name, **over)
+    n_closed = _run_stream(wl, pats, decode_every=64)
+    assert n_closed >= sum(len(r) for r in runs)
+
+
+def test_streaming_equal_singular_values():
+    """Runs whose key rows are orthogonal with equal norms (every singular
+    value equal): with n <= r the truncation keeps all of them and the
+    product must give the rows back; with n > r it is not unique and only
+    the tables, summaries and decode are compared."""
+    runs = [[6], [12]]
+    pats, steps = _run_patterns(runs)
+    wl = W.generate("serving_b16_bf16", B=2, T=700, tail_capacity=steps + 8, steps=steps)
+    dt = wl.dtype
+    # appends 1 .. n of each sequence: key rows 2 e_i in every KV head
+    for b, rr in enumerate(runs):
+        for i in range(rr[0]):
+            k, v = wl.appends[1 + i]
+            k = k.copy()
+            row = np.zeros(wl.cfg["d"], np.float32)
+            row[i] = 2.0
+            k[b, :] = W.store(row, dt)
+            wl.appends[1 + i] = (k, v)
+    n_closed = _run_stream(wl, pats, decode_every=4)
+    assert n_closed == 4
