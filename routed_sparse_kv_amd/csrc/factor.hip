@@ -682,6 +682,16 @@ __device__ __forceinline__ double wave_sum_dpp(double a) {
 //   branch), the next reflector, barrier.
 // Column blocks of 8 left of the trailing block are skipped.  d, e receive
 // T; tau the reflectors.  Ends with a barrier.
+// A loaded value marked as used unconditionally (an empty asm statement
+// that takes and returns it in a register): a load whose result is then
+// selected against a constant stays one unconditional load, issued with
+// its neighbours, instead of becoming a branch around a load that waits
+// on its own.
+__device__ __forceinline__ double keep(double x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 typedef __attribute__((address_space(3))) double lds_f64;
 typedef __attribute__((address_space(3))) EigShared lds_eig;
 template <int L, int C>
@@ -698,10 +708,12 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
   // address inside the LDS work array; entries past m are replaced by 0
   double a[C];
 #pragma unroll
+  for (int c = 0; c < C; ++c) a[c] = A[i * P + h + L * c];
+#pragma unroll
   for (int c = 0; c < C; ++c) {
     const int j = h + L * c;
-    const double x = A[i * P + j];
-    a[c] = own && j < m ? x : 0.0;
+    const double kx = keep(a[c]);
+    a[c] = own && j < m ? kx : 0.0;
   }
   if (tid < 128) es->p[tid] = 0.0;
   // reflector r (r <= m - 3) from row r of A in LDS, by the 64 lanes of
@@ -709,24 +721,26 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
   // into row r (kept for the back-transform), d_r, e_r = beta, tau_r
   auto reflector = [&](int r) {
     lds_f64* row = A + r * P;
-    const int j0 = r + 2 + lane, j1 = j0 + kWave;
-    const double x0 = j0 < m ? row[j0] : 0.0;
-    const double x1 = j1 < m ? row[j1] : 0.0;
-    const double q = wave_sum_dpp(fma(x0, x0, x1 * x1));
+    double xa = row[lane], xb = row[lane + kWave];
     const double al = row[r + 1];
+    xa = keep(xa);
+    xb = keep(xb);
+    const bool ia = lane > r + 1 && lane < m, ib = lane + kWave > r + 1 && lane + kWave < m;
+    const double ya = ia ? xa : 0.0, yb = ib ? xb : 0.0;
+    const double q = wave_sum_dpp(fma(ya, ya, yb * yb));
     double tau = 0.0, scl = 0.0, beta = al;
     if (q > 0.0) {
-      beta = -copysign(sqrt(fma(al, al, q)), al);
-      tau = (beta - al) / beta;
-      scl = 1.0 / (al - beta);
+      const double s2 = fma(al, al, q);
+      beta = -copysign(s2 * rsqrt_nr(s2), al);
+      const double ib_ = recip(beta);
+      tau = (beta - al) * ib_;
+      scl = recip(al - beta);
     }
     lds_f64* vb = es->vb[r & 1];
-    vb[lane] = lane == r + 1 ? 1.0 : (lane > r + 1 && lane < m ? row[lane] * scl : 0.0);
-    vb[lane + kWave] = lane + kWave == r + 1
-                           ? 1.0
-                           : (lane + kWave > r + 1 && lane + kWave < m ? row[lane + kWave] * scl : 0.0);
-    if (j0 < m) row[j0] = x0 * scl;
-    if (j1 < m) row[j1] = x1 * scl;
+    vb[lane] = lane == r + 1 ? 1.0 : ya * scl;
+    vb[lane + kWave] = lane + kWave == r + 1 ? 1.0 : yb * scl;
+    if (ia) row[lane] = ya * scl;
+    if (ib) row[lane + kWave] = yb * scl;
     if (lane == 0) {
       es->d[r] = row[r];
       row[r + 1] = 1.0;
@@ -740,8 +754,10 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
     const double tau = es->tau[k];
     const lds_f64* vb = es->vb[k & 1];
     const bool act = own && i > k;
+    // waves whose rows all lie outside the trailing block skip both phases
+    const bool wave_live = (tid | (kWave - 1)) / L > k && (tid & ~(kWave - 1)) / L < m;
     double pi = 0.0, vi = 0.0;
-    if (tau != 0.0) {
+    if (tau != 0.0 && wave_live) {
       double part = 0.0;
 #pragma unroll
       for (int b = 0; b < C / kBlk; ++b) {
@@ -758,7 +774,7 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
     const double pv = wave_sum_dpp(h == 0 ? pi * vi : 0.0);
     if (lane == 0) es->red[1][tid / kWave] = pv;
     __syncthreads();
-    if (tau != 0.0) {
+    if (tau != 0.0 && wave_live) {
       const double tpv = tau * ((es->red[1][0] + es->red[1][1]) + (es->red[1][2] + es->red[1][3]));
       const double ci = pi - tpv * vi;  // w_i - (tau/2)(p.v) v_i
 #pragma unroll
@@ -779,7 +795,11 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
       // reflector from it
       if (i == k + 1) {
 #pragma unroll
-        for (int c = 0; c < C; ++c) A[i * P + h + L * c] = a[c];
+        for (int b = 0; b < C / kBlk; ++b) {
+          if ((L - 1) + L * (kBlk * b + kBlk - 1) < k + 1) continue;
+#pragma unroll
+          for (int u = 0; u < kBlk; ++u) A[i * P + h + L * (kBlk * b + u)] = a[kBlk * b + u];
+        }
       }
       if (tid / kWave == ((k + 1) * L) / kWave) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -949,65 +969,109 @@ __device__ __forceinline__ double guard_pivot(double x) {
 // z_t = 1, z_i = -(e_i / D+_i) z_{i+1} above t and z_{i+1} = -(e_i /
 // D-_{i+1}) z_i below.  z (stride 16 doubles) holds D+ first, then the
 // recomputed D- below t, then the vector.  Returns ||z||^2.
-__device__ double twisted_vector(const double2* __restrict__ de, const double* __restrict__ e,
-                                 int m, double lam, double* __restrict__ z) {
-  double pa = 1.0, pb = de[0].x - lam;
+// One (d_i, e_{i-1}^2) pair from an LDS view of the pair array.
+struct Pair {
+  double x, y;
+};
+__device__ __forceinline__ Pair pair_at(const lds_f64* de, int i) {
+  return Pair{de[2 * i], de[2 * i + 1]};
+}
+
+__device__ double twisted_vector(const double2* de_, const double* e_, int m, double lam,
+                                 double* z_) {
+  // LDS views; de has m + 4 readable pairs, z stride 16.  Every pass
+  // loads the operands of the next two steps ahead of the current one.
+  const lds_f64* de = (const lds_f64*)de_;
+  const lds_f64* e = (const lds_f64*)e_;
+  lds_f64* z = (lds_f64*)z_;
+  double pa = 1.0, pb = pair_at(de, 0).x - lam;
   z[0] = guard_pivot(pb);
+  {
+    Pair q1 = pair_at(de, 1), q2 = pair_at(de, 2);
 #pragma unroll 4
-  for (int i = 1; i < m; ++i) {
-    const double2 q = de[i];
-    const double pc = fma(q.x - lam, pb, -q.y * pa);
-    z[16 * i] = guard_pivot(pc * recip(pb));
-    pa = pb;
-    pb = pc;
-    if ((i & 3) == 0) rescale2(pa, pb);
+    for (int i = 1; i < m; ++i) {
+      const Pair q = q1;
+      q1 = q2;
+      q2 = pair_at(de, i + 2);
+      const double rb = recip(pb);
+      const double pc = fma(q.x - lam, pb, -q.y * pa);
+      z[16 * i] = guard_pivot(pc * rb);
+      pa = pb;
+      pb = pc;
+      if ((i & 3) == 0) rescale2(pa, pb);
+    }
   }
   double best = fabs(z[16 * (m - 1)]);
   int t = m - 1;
-  double qa = 1.0, qb = de[m - 1].x - lam;
+  // bottom-up minors Q_i = (d_i - lam) Q_{i+1} - e_i^2 Q_{i+2}, from
+  // i = m - 2 down to `stop`; at each step f(i, D-_i, d_i - lam)
+  auto bottom_up = [&](int stop, auto&& f) {
+    double qa = 1.0, qb = pair_at(de, m - 1).x - lam;
+    if (m - 2 < stop) return;
+    Pair c1 = pair_at(de, m - 2), n1 = pair_at(de, m - 1);
+    Pair c2 = pair_at(de, m >= 3 ? m - 3 : 0);
 #pragma unroll 4
-  for (int i = m - 2; i >= 0; --i) {
-    const double di = de[i].x - lam;
-    const double qc = fma(di, qb, -de[i + 1].y * qa);
-    const double gam = fabs(z[16 * i] + guard_pivot(qc * recip(qb)) - di);
-    if (gam < best) {
-      best = gam;
-      t = i;
+    for (int i = m - 2; i >= stop; --i) {
+      const Pair c = c1, n = n1;
+      n1 = c1;
+      c1 = c2;
+      c2 = pair_at(de, i >= 2 ? i - 2 : 0);
+      const double rb = recip(qb);
+      const double di = c.x - lam;
+      const double qc = fma(di, qb, -n.y * qa);
+      f(i, guard_pivot(qc * rb), di);
+      qa = qb;
+      qb = qc;
+      if ((i & 3) == 0) rescale2(qa, qb);
     }
-    qa = qb;
-    qb = qc;
-    if ((i & 3) == 0) rescale2(qa, qb);
+  };
+  {
+    double dpn = m >= 2 ? z[16 * (m - 2)] : 0.0;
+    bottom_up(0, [&](int i, double dm, double di) {
+      const double dp = dpn;
+      dpn = z[16 * (i > 0 ? i - 1 : 0)];
+      const double gam = fabs(dp + dm - di);
+      const bool better = gam < best;
+      best = better ? gam : best;
+      t = better ? i : t;
+    });
   }
   // bottom-up pivots of rows t + 1 .. m - 1 (the same recurrence again)
-  qa = 1.0;
-  qb = de[m - 1].x - lam;
-  if (t < m - 1) z[16 * (m - 1)] = guard_pivot(qb);
-  for (int i = m - 2; i > t; --i) {
-    const double qc = fma(de[i].x - lam, qb, -de[i + 1].y * qa);
-    z[16 * i] = guard_pivot(qc * recip(qb));
-    qa = qb;
-    qb = qc;
-    if ((i & 3) == 0) rescale2(qa, qb);
-  }
+  if (t < m - 1) z[16 * (m - 1)] = guard_pivot(pair_at(de, m - 1).x - lam);
+  bottom_up(t + 1, [&](int i, double dm, double) { z[16 * i] = dm; });
   double zi = 1.0, nrm = 1.0;
-  for (int i = t + 1; i < m; ++i) {
-    zi = -(e[i - 1] * recip(z[16 * i])) * zi;
-    z[16 * i] = zi;
-    nrm = fma(zi, zi, nrm);
+  {
+    double dn = t + 1 < m ? z[16 * (t + 1)] : 1.0, en = e[t];
+#pragma unroll 4
+    for (int i = t + 1; i < m; ++i) {
+      const double dd = dn, ee = en;
+      dn = z[16 * (i + 1 < m ? i + 1 : i)];
+      en = e[i];
+      zi = -(ee * recip(dd)) * zi;
+      z[16 * i] = zi;
+      nrm = fma(zi, zi, nrm);
+    }
   }
   zi = 1.0;
-  for (int i = t - 1; i >= 0; --i) {
-    zi = -(e[i] * recip(z[16 * i])) * zi;
-    z[16 * i] = zi;
-    nrm = fma(zi, zi, nrm);
+  {
+    double dn = t >= 1 ? z[16 * (t - 1)] : 1.0, en = t >= 1 ? e[t - 1] : 0.0;
+#pragma unroll 4
+    for (int i = t - 1; i >= 0; --i) {
+      const double dd = dn, ee = en;
+      dn = z[16 * (i >= 1 ? i - 1 : 0)];
+      en = e[i >= 1 ? i - 1 : 0];
+      zi = -(ee * recip(dd)) * zi;
+      z[16 * i] = zi;
+      nrm = fma(zi, zi, nrm);
+    }
   }
   z[16 * t] = 1.0;
   return nrm;
 }
 
 // Eigenvectors of G for the rj largest eigenvalues in es.lam (rj <= 32):
-// the twisted vectors of T (one lane each, in batches of 16 held in `zs`,
-// 16 m doubles of LDS), normalised and spread over groups of V lanes (EV
+// the twisted vectors of T (one lane each, four per wave, in batches of 16
+// held in `zs`, 16 m doubles of LDS), normalised and spread over groups of V lanes (EV
 // elements per lane), mapped back through the reflectors kept in A (the
 // next reflector's entries are loaded while the current one is applied),
 // then written as rows lambda_k u_k^T of A (pitch P) with sig[k] =
@@ -1021,10 +1085,13 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
   double y[EV];
 #pragma unroll
   for (int c = 0; c < EV; ++c) y[c] = 0.0;
+  // vector t of a batch goes to lane t % 4 of wave t / 4: the passes are
+  // serial recurrences, so four waves run four at a time each
+  const int tv = (tid / kWave) * 4 + (tid & (kWave - 1));
   for (int b0 = 0; b0 < rj; b0 += 16) {
-    if (tid < 16 && b0 + tid < rj) {
-      const double nrm = twisted_vector(de, es.e, m, es.lam[b0 + tid], zs + tid);
-      es.zn[tid] = rsqrt_nr(nrm);
+    if ((tid & (kWave - 1)) < 4 && b0 + tv < rj) {
+      const double nrm = twisted_vector(de, es.e, m, es.lam[b0 + tv], zs + tv);
+      es.zn[tv] = rsqrt_nr(nrm);
     }
     __syncthreads();
     if (kk >= b0 && kk < b0 + 16 && kk < rj) {
@@ -1039,25 +1106,32 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
   }
   // u = H_0 H_1 ... H_{m-3} z, the last reflector first
   // row s of A holds reflector s scaled (v_{s+1} = 1); reads stay inside
-  // the work array for i < 128
-  auto load_v = [&](int s, double (&v)[EV]) {
+  // the work array for i < 128, and the entries outside s + 1 .. m - 1 are
+  // replaced by 0 when they are used (one step after they are loaded)
+  auto load_v = [&](int s, double (&x)[EV]) {
     const lds_f64* rs = (const lds_f64*)(A + s * P);
+#pragma unroll
+    for (int c = 0; c < EV; ++c) x[c] = rs[l + V * c];
+  };
+  double vn[EV];
+  double tn = 0.0;
+  if (m >= 3) {
+    tn = es.tau[m - 3];
+    load_v(m - 3, vn);
+  }
+  for (int s = m - 3; s >= 0; --s) {
+    double v[EV];
+    const double ts = keep(tn);
 #pragma unroll
     for (int c = 0; c < EV; ++c) {
       const int i = l + V * c;
-      const double x = rs[i];
-      v[c] = i > s && i < m ? x : 0.0;
+      const double kx = keep(vn[c]);
+      v[c] = i > s && i < m ? kx : 0.0;
     }
-  };
-  double vn[EV];
-  if (m >= 3) load_v(m - 3, vn);
-  for (int s = m - 3; s >= 0; --s) {
-    double v[EV];
-#pragma unroll
-    for (int c = 0; c < EV; ++c) v[c] = vn[c];
-    if (s > 0) load_v(s - 1, vn);
-    const double ts = es.tau[s];
-    if (ts == 0.0) continue;
+    if (s > 0) {
+      tn = es.tau[s - 1];
+      load_v(s - 1, vn);
+    }
     double d0 = 0.0, d1 = 0.0;
 #pragma unroll
     for (int c = 0; c < EV; ++c) {
@@ -1066,7 +1140,7 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
       else
         d0 = fma(v[c], y[c], d0);
     }
-    const double f = ts * group_sum_dpp<V>(d0 + d1);
+    const double f = ts * group_sum_dpp<V>(d0 + d1);  // tau_s = 0: no change
 #pragma unroll
     for (int c = 0; c < EV; ++c) y[c] = fma(-f, v[c], y[c]);
   }
