@@ -78,7 +78,7 @@ typedef struct rskv_allocator {
  * `dtype`; surprisal, ln|S|, the projection and the output are fp32. */
 typedef struct rskv_build_opts {
   int32_t batch;         /* B >= 1 sequences */
-  int32_t n_q_heads;     /* Hq, a multiple of n_kv_heads */
+  int32_t n_q_heads;     /* Hq, a multiple of n_kv_heads, Hq / Hkv <= 16 */
   int32_t n_kv_heads;    /* Hkv >= 1; query head h uses KV head h / (Hq/Hkv) */
   int32_t head_dim;      /* d in {64, 128} */
   int32_t context_len;   /* T >= 1 prefilled tokens per sequence */

@@ -31,7 +31,7 @@ int hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
-constexpr int kMaxG = 8;
+constexpr int kMaxG = 16;
 constexpr int kMaxRank = 32;
 
 size_t elem_size(int dtype) { return dtype == RSKV_BF16 ? 2 : 4; }
@@ -47,7 +47,7 @@ int check_opts(const rskv_build_opts* o, int rank) {
   if (o->n_q_heads % o->n_kv_heads != 0)
     return fail(RSKV_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
   if (o->n_q_heads / o->n_kv_heads > kMaxG)
-    return fail(RSKV_EINVAL, "query group size above 8 is not supported");
+    return fail(RSKV_EINVAL, "query group size above 16 is not supported");
   if (o->head_dim != 64 && o->head_dim != 128)
     return fail(RSKV_EINVAL, "head_dim must be 64 or 128");
   if (!(o->anchor_frac >= 0.0 && o->anchor_frac <= 1.0))

@@ -43,10 +43,10 @@ namespace {
 constexpr int kAttThreads = 256;
 constexpr int kXcds = 8;  // accelerator dies of the device
 constexpr int kChunk = 32;
-constexpr int kMaxG = 8;
+constexpr int kMaxG = 16;
 constexpr int kMaxRank = 32;
-constexpr int kMaxOut = 4;           // VALU path: outputs per thread, G*d <= 1024
-constexpr int kMaxSplitMfma = 256;   // final merge keeps nsplit*G weights in LDS
+constexpr int kMaxOut = 8;           // VALU path: outputs per thread, G*d <= 2048
+constexpr int kMaxSplitMfma = 256;   // partials per unit of the MFMA path
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -32,7 +32,7 @@
 namespace rskv {
 namespace {
 
-constexpr int kMaxG = 8;
+constexpr int kMaxG = 16;
 constexpr int kRouteThreads = 256;               // 4 waves
 constexpr int kTilesPerWave = 2;                 // 16 spans per tile
 constexpr int kSpansPerBlock = 4 * kTilesPerWave * 16;

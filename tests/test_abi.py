@@ -133,3 +133,17 @@ def test_half_allocator_hook_is_rejected_before_any_device_call():
                               ctypes.byref(opts), None, ctypes.byref(out))
     assert rc == -1 and b"allocator" in lib.rskv_last_error()
     assert out.value is None
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="librskv.so not built")
+def test_query_group_above_16_is_rejected_before_any_device_call():
+    from routed_sparse_kv_amd import binding
+    lib = binding.lib()
+    opts = binding.BuildOpts(batch=1, n_q_heads=17, n_kv_heads=1, head_dim=64, context_len=8,
+                             dtype=0, anchor_frac=0.5, alpha=8.0, tail_capacity=0, k_max_cap=0,
+                             factor_tier=0)
+    out = ctypes.c_void_p(1)
+    rc = lib.rskv_build_spans(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 4,
+                              ctypes.byref(opts), None, ctypes.byref(out))
+    assert rc == -1 and b"above 16" in lib.rskv_last_error()
+    assert out.value is None

@@ -30,6 +30,10 @@ SMALL = {
     "long_bf16": ("long_128k_bf16", dict(B=2, Hq=8, Hkv=2, T=8192, k_max=24, steps=2)),
     "serving_bf16": ("serving_b16_bf16", dict(B=3, T=2053, steps=4, tail_capacity=6)),
     "drift_bf16": ("million_1m_bf16", dict(Hq=8, Hkv=2, T=16384, steps=2)),
+    # query groups of 16 heads (the MFMA tiles' full width; G d = 2048 outputs
+    # per workgroup on the fp32 path)
+    "tiny_fp32_g16": ("tiny_fp32_2k", dict(Hq=16, Hkv=1, d=128, T=2051, query="uniform")),
+    "gqa_bf16_g16": ("gqa_32k_bf16", dict(Hq=32, Hkv=2, T=4099, steps=2)),
 }
 
 
