@@ -5,16 +5,21 @@
 // (|S| x d), the rank r_j = min(r, |S|, d) truncated SVD X ~ A W with
 // A = U_r S_r (|S| x r) and W = W_r^T (r x d), zero-padded beyond r_j.
 //
-// Method: fp64 one-sided Jacobi (Hestenes) on the shorter side of X.
-//   |S| <= d: rotate pairs of rows until all rows are orthogonal, X' = J X;
-//             the rows of X' are sigma_i w_i^T, and A = X W_r.
-//   |S| >  d: rotate pairs of columns, X' = X J; the columns of X' are
-//             sigma_i u_i, so A = X'[:, top] and w_i = X^T x'_i / sigma_i^2.
-// Only the working matrix is stored (no accumulated rotation), in LDS when
-// it fits (<= 48 KB) and otherwise in a per-workgroup global slab.  Pairs of
-// a sweep follow the round-robin (circle) ordering, so each round rotates
-// cnt/2 disjoint pairs in parallel; a group of lanes handles one pair.
-// Build-time only: this kernel is not on the decode path.
+// Two methods, both in fp64:
+// - factor_kernel (build, spans whose |S| x d working matrix fits 48 KB of
+//   LDS): one-sided Jacobi (Hestenes) on the shorter side of X.
+//     |S| <= d: rotate pairs of rows until all rows are orthogonal,
+//               X' = J X; the rows of X' are sigma_i w_i^T, and A = X W_r.
+//     |S| >  d: rotate pairs of columns, X' = X J; the columns of X' are
+//               sigma_i u_i, so A = X'[:, top] and w_i = X^T x'_i / sigma_i^2.
+//   Only the working matrix is stored (no accumulated rotation).  Pairs of
+//   a sweep follow the round-robin (circle) ordering, so each round rotates
+//   cnt/2 disjoint pairs in parallel; a group of lanes handles one pair.
+// - factor_run (build of longer spans in factor_gram_kernel, and span
+//   closing in close_kernel): the r_j largest eigenpairs of the Gram matrix
+//   (see the comment above tridiagonalize), Jacobi on the Gram matrix for
+//   clustered spectra.
+// Build and closing only: none of this is on the decode path.
 #include <algorithm>
 #include <type_traits>
 #include <string>
@@ -1160,6 +1165,193 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
   __syncthreads();
 }
 
+// Rank-r_j factors of a run of n rows X (n x d) in fp64 through the Gram
+// matrix (SEKV, Metodologia 2: a span's rows are encoded by a truncated
+// SVD basis), for the closing and the build of long spans.
+// load_rows(t0, rb, dst) brings rows [t0, t0 + rb) of X into LDS as floats
+// with row pitch d + 4 and ends with a barrier; pre(x_pre, for_blocks) runs
+// once X is staged (the closing's summary); a_store(t, k, value) and
+// w_store(k, e, value) receive A (n x r_j) and W (r_j x d).  Every thread of
+// the workgroup calls it; it ends with a barrier.
+struct RunLds {
+  double* work;   // kCloseWork doubles
+  float* stage;   // kBlock rows of 128 + 4 floats
+  double* part;   // kCloseThreads + 8 doubles
+  EigShared* es;
+  FactorShared* sh;
+};
+
+template <class LoadRows, class Pre, class AOut, class WOut>
+__device__ void factor_run(int n, int d, int rank, const RunLds& L, const LoadRows& load_rows,
+                           const Pre& pre, const AOut& a_store, const WOut& w_store) {
+  const int tid = threadIdx.x;
+  double* const work = L.work;
+  float* const stage = L.stage;
+  double* const part = L.part;
+  EigShared& es = *L.es;
+  FactorShared& sh = *L.sh;
+  // ---- layout.  Rows form (G = X X^T, m = n) when n <= d, else cols
+  // form (G = X^T X, m = d).  X rows are staged as floats with pitch
+  // xp = d + 4 (rows start 4 banks apart, so a wave reading one element
+  // of 16 rows hits 16 bank groups, and stay 16-byte aligned).  While the
+  // rows form accumulates G in registers, X sits at the start of `work`,
+  // where G goes afterwards; X is kept after G (x_after) when both fit,
+  // and is otherwise streamed from global memory in 32-row blocks.
+  const int xp = d + 4;
+  const bool rows_form = n <= d;
+  const int m = rows_form ? n : d;
+  const int gs = jacobi_group<kCloseThreads>(m);
+  int Lp = gs;  // rows of G padded with zeros to gs * E columns, E a power of two
+  while (Lp < m) Lp *= 2;
+  const int Pj = jacobi_pitch(Lp, gs);
+  const bool x_after = sizeof(double) * m * Pj + sizeof(float) * static_cast<size_t>(n) * xp <=
+                       sizeof(double) * kCloseWork;
+  float* const x_post = x_after ? reinterpret_cast<float*>(work + m * Pj) : nullptr;
+  float* const x_pre = rows_form ? reinterpret_cast<float*>(work) : x_post;
+  // visits X in order of rows: f(rows pointer, t0, rb), whole when
+  // resident at x, else in 32-row blocks through `stage`
+  auto for_blocks = [&](const float* x, const auto& f) {
+    if (x != nullptr) {
+      f(x, 0, n);
+      return;
+    }
+    for (int t0 = 0; t0 < n; t0 += kBlock) {
+      const int rb = min(kBlock, n - t0);
+      load_rows(t0, rb, stage);
+      f(static_cast<const float*>(stage), t0, rb);
+      __syncthreads();
+    }
+  };
+  if (x_pre != nullptr) load_rows(0, n, x_pre);
+  pre(x_pre, for_blocks);
+
+  // ---- Gram matrix and its r_j largest eigenpairs (sig = sigma^2): the
+  // tridiagonal path, or Jacobi when the spectrum is clustered there
+  auto gram = [&](int Lg, int Pg) {
+    auto run = [&](auto bsize) {
+      constexpr int B = decltype(bsize)::value;
+      double g[B][B] = {};
+      if (rows_form) {
+        gram_accumulate<B, true>(x_pre, xp, m, d, g);
+        __syncthreads();  // X is read before G takes its place
+      } else {
+        for_blocks(x_pre, [&](const float* xr, int, int rb) {
+          gram_accumulate<B, false>(xr, xp, m, rb, g);
+        });
+      }
+      gram_store<B>(g, m, Lg, work, Pg);
+    };
+    if (m > 64)
+      run(std::integral_constant<int, 8>());
+    else if (m > 32)
+      run(std::integral_constant<int, 4>());
+    else if (m > 16)
+      run(std::integral_constant<int, 2>());
+    else
+      run(std::integral_constant<int, 1>());
+  };
+  const int rmax = min(rank, m);
+  int P = Pj;
+  int rj = 0;
+  bool tri = rmax <= kMaxEig - 1;
+  if (tri) {
+    const int Pt = m + 1 + (m & 1);  // odd pitch: a wave's rows fall in distinct banks
+    gram(m, Pt);
+    if (m > 64)
+      tridiagonalize<2, 64>(work, m, Pt, es);
+    else if (m > 32)
+      tridiagonalize<4, 16>(work, m, Pt, es);
+    else if (m > 16)
+      tridiagonalize<8, 4>(work, m, Pt, es);
+    else
+      tridiagonalize<16, 1>(work, m, Pt, es);
+    const int nev = min(rmax + 1, m);
+    double2* de = reinterpret_cast<double2*>(part);  // free after the summary
+    top_eigenvalues(m, nev, es, de);
+    const double l0 = es.lam[0];
+    for (int k = 0; k + 1 < nev; ++k)
+      if (es.lam[k] - es.lam[k + 1] <= kClusterGap * l0 && es.lam[k] > kSignificant * l0)
+        tri = false;
+    if (tri) {
+      double* zs = reinterpret_cast<double*>(stage);
+      if (rmax <= 16)
+        top_eigenvectors<16, 8>(work, m, Pt, rmax, es, de, zs, sh);
+      else
+        top_eigenvectors<8, 16>(work, m, Pt, rmax, es, de, zs, sh);
+      P = Pt;
+      rj = rmax;
+    } else if (rows_form) {
+      load_rows(0, n, x_pre);  // G took X's place
+    }
+  }
+  if (!tri) {
+    gram(Lp, Pj);
+    jacobi_sweeps<kCloseThreads>(work, m, Lp, Pj, sh);
+    rj = top_rows<kCloseThreads>(work, m, Lp, Pj, rank, sh);
+  }
+  if (rows_form && x_post != nullptr) load_rows(0, n, x_post);
+
+  if (rows_form) {
+    // A[t][k] = sigma_k u_k[t] = row_k[t] / sigma_k
+    for (int o = tid; o < n * rj; o += kCloseThreads) {
+      const int t = o / rj;
+      const int k = o - t * rj;
+      const double lam = sh.sig[sh.top[k]];
+      a_store(t, k, lam > 0.0 ? work[sh.top[k] * P + t] / sqrt(lam) : 0.0);
+    }
+    // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3; thread -> kOut outputs
+    constexpr int kOut = 32 * 128 / kCloseThreads;
+    double wacc[kOut] = {};
+    for_blocks(x_post, [&](const float* xr, int t0, int rb) {
+#pragma unroll
+      for (int q = 0; q < kOut; ++q) {
+        const int o = tid + q * kCloseThreads;
+        if (o < rj * d) {
+          const int k = o / d;
+          const int e = o - k * d;
+          const double* uk = work + sh.top[k] * P + t0;
+          for (int t = 0; t < rb; ++t)
+            wacc[q] = fma(static_cast<double>(xr[t * xp + e]), uk[t], wacc[q]);
+        }
+      }
+    });
+#pragma unroll
+    for (int q = 0; q < kOut; ++q) {
+      const int o = tid + q * kCloseThreads;
+      if (o < rj * d) {
+        const int k = o / d;
+        const double lam = sh.sig[sh.top[k]];
+        w_store(k, o - k * d, lam > 0.0 ? wacc[q] / (lam * sqrt(lam)) : 0.0);
+      }
+    }
+  } else {
+    // W[k] = w_k = row_k / sigma_k^2
+    for (int o = tid; o < rj * d; o += kCloseThreads) {
+      const int k = o / d;
+      const int e = o - k * d;
+      const double lam = sh.sig[sh.top[k]];
+      w_store(k, e, lam > 0.0 ? work[sh.top[k] * P + e] / lam : 0.0);
+    }
+    // A[t][k] = X[t] . w_k
+    for_blocks(x_post, [&](const float* xr, int t0, int rb) {
+      for (int o = tid; o < rb * rj; o += kCloseThreads) {
+        const int t = o / rj;
+        const int k = o - t * rj;
+        const double lam = sh.sig[sh.top[k]];
+        double s = 0.0;
+        if (lam > 0.0) {
+          const double* wk = work + sh.top[k] * P;
+          for (int e = 0; e < d; ++e) s = fma(static_cast<double>(xr[t * xp + e]), wk[e], s);
+          s /= lam;
+        }
+        a_store(t0 + t, k, s);
+      }
+    });
+  }
+  __syncthreads();
+
+}
+
 template <int DT>
 __global__ __launch_bounds__(kCloseThreads) void close_kernel(
     const float* __restrict__ h_new, const float* __restrict__ theta,
@@ -1182,6 +1374,7 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
   __shared__ double red[kCloseWaves];
   __shared__ EigShared es;
   const int tid = threadIdx.x;
+  const RunLds L{work, stage, part, &es, &sh};
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int kv = item & 1;
@@ -1196,25 +1389,8 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
     const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
     ST* xs = (kv ? v_full : k_full) + static_cast<size_t>(u) * Fp * d;
 
-    // ---- layout.  Rows form (G = X X^T, m = n) when n <= d, else cols
-    // form (G = X^T X, m = d).  X rows are staged as floats with pitch
-    // xp = d + 4 (rows start 4 banks apart, so a wave reading one element
-    // of 16 rows hits 16 bank groups, and stay 16-byte aligned).  While the
-    // rows form accumulates G in registers, X sits at the start of `work`,
-    // where G goes afterwards; X is kept after G (x_after) when both fit,
-    // and is otherwise streamed from global memory in 32-row blocks.
-    const int xp = d + 4;
-    const bool rows_form = n <= d;
-    const int m = rows_form ? n : d;
-    const int gs = jacobi_group<kCloseThreads>(m);
-    int Lp = gs;  // rows of G padded with zeros to gs * E columns, E a power of two
-    while (Lp < m) Lp *= 2;
-    const int Pj = jacobi_pitch(Lp, gs);
-    const bool x_after = sizeof(double) * m * Pj + sizeof(float) * static_cast<size_t>(n) * xp <=
-                         sizeof(double) * kCloseWork;
-    float* const x_post = x_after ? reinterpret_cast<float*>(work + m * Pj) : nullptr;
-    float* const x_pre = rows_form ? reinterpret_cast<float*>(work) : x_post;
     // rows [t0, t0 + rb) of X into dst (row pitch xp)
+    const int xp = d + 4;
     auto load_rows = [&](int t0, int rb, float* dst) {
       for_row_vectors(kv != 0, r0 + t0, r0 + t0 + rb, d, [&](size_t off, const int (&rr)[8],
                                                                const int (&cc)[8]) {
@@ -1226,134 +1402,53 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
       });
       __syncthreads();
     };
-    // visits X in order of rows: f(rows pointer, t0, rb), whole when
-    // resident at x, else in 32-row blocks through `stage`
-    auto for_blocks = [&](const float* x, const auto& f) {
-      if (x != nullptr) {
-        f(x, 0, n);
-        return;
-      }
-      for (int t0 = 0; t0 < n; t0 += kBlock) {
-        const int rb = min(kBlock, n - t0);
-        load_rows(t0, rb, stage);
-        f(static_cast<const float*>(stage), t0, rb);
-        __syncthreads();
-      }
-    };
-    if (x_pre != nullptr) load_rows(0, n, x_pre);
-
-    // ---- summary (K item) or value mean (V item): column sums in fp64, in
-    // row order; ng groups of d threads take interleaved rows, then the
-    // groups are added in order
-    const int ng = kCloseThreads / d;
-    const int gi = tid / d;
-    const int c = tid - gi * d;
-    const float* hr = h_full + static_cast<size_t>(b) * F + r0;
-    double acc = 0.0;
-    for_blocks(x_pre, [&](const float* xr, int t0, int rb) {
-      for (int t = gi; t < rb; t += ng)
-        acc += kv ? static_cast<double>(xr[t * xp + c])
-                  : static_cast<double>(hr[t0 + t]) * static_cast<double>(xr[t * xp + c]);
-    });
-    part[gi * d + c] = acc;
-    __syncthreads();
-    double tot = 0.0;
-    if (tid < d)
-      for (int q = 0; q < ng; ++q) tot += part[q * d + tid];
-    if (kv == 0) {
-      const double sq = wave_sum(tot * tot);
-      if ((tid & (kWave - 1)) == 0) red[tid / kWave] = sq;
+    auto pre = [&](const float* x_pre, const auto& for_blocks) {
+      // ---- summary (K item) or value mean (V item): column sums in fp64, in
+      // row order; ng groups of d threads take interleaved rows, then the
+      // groups are added in order
+      const int ng = kCloseThreads / d;
+      const int gi = tid / d;
+      const int c = tid - gi * d;
+      const float* hr = h_full + static_cast<size_t>(b) * F + r0;
+      double acc = 0.0;
+      for_blocks(x_pre, [&](const float* xr, int t0, int rb) {
+        for (int t = gi; t < rb; t += ng)
+          acc += kv ? static_cast<double>(xr[t * xp + c])
+                    : static_cast<double>(hr[t0 + t]) * static_cast<double>(xr[t * xp + c]);
+      });
+      part[gi * d + c] = acc;
       __syncthreads();
-      double norm2 = 0.0;
-      for (int w = 0; w < d / kWave; ++w) norm2 += red[w];
+      double tot = 0.0;
       if (tid < d)
-        summary[(static_cast<size_t>(u) * S + j) * d + tid] =
-            E::from_f64(norm2 > 0.0 ? tot / sqrt(norm2) : 0.0);
-    } else if (tid < d) {
-      vmean[static_cast<size_t>(u) * Sp * d + v32_off(j, tid, d)] =
-          E::from_f64(tot / static_cast<double>(n));
-    }
-    if (kv == 0 && h == 0) {
-      const int st = full_pos[static_cast<size_t>(b) * F + r0];
-      if (tid == 0) {
-        span_start[static_cast<size_t>(b) * S + j] = st;
-        span_len[static_cast<size_t>(b) * S + j] = n;
-        tok_off[static_cast<size_t>(b) * (S + 1) + j + 1] =
-            tok_off[static_cast<size_t>(b) * (S + 1) + j] + n;
-        tok_pad[static_cast<size_t>(b) * (S + 1) + j + 1] = tp + round_up(n, 16);
-        log_len[static_cast<size_t>(b) * S + j] = static_cast<float>(log(static_cast<double>(n)));
+        for (int q = 0; q < ng; ++q) tot += part[q * d + tid];
+      if (kv == 0) {
+        const double sq = wave_sum(tot * tot);
+        if ((tid & (kWave - 1)) == 0) red[tid / kWave] = sq;
+        __syncthreads();
+        double norm2 = 0.0;
+        for (int w = 0; w < d / kWave; ++w) norm2 += red[w];
+        if (tid < d)
+          summary[(static_cast<size_t>(u) * S + j) * d + tid] =
+              E::from_f64(norm2 > 0.0 ? tot / sqrt(norm2) : 0.0);
+      } else if (tid < d) {
+        vmean[static_cast<size_t>(u) * Sp * d + v32_off(j, tid, d)] =
+            E::from_f64(tot / static_cast<double>(n));
       }
-      for (int p = st + tid; p < min(st + n, T); p += kCloseThreads)
-        span_id[static_cast<size_t>(b) * T + p] = j;
-    }
-    __syncthreads();
-
-    // ---- Gram matrix and its r_j largest eigenpairs (sig = sigma^2): the
-    // tridiagonal path, or Jacobi when the spectrum is clustered there
-    auto gram = [&](int Lg, int Pg) {
-      auto run = [&](auto bsize) {
-        constexpr int B = decltype(bsize)::value;
-        double g[B][B] = {};
-        if (rows_form) {
-          gram_accumulate<B, true>(x_pre, xp, m, d, g);
-          __syncthreads();  // X is read before G takes its place
-        } else {
-          for_blocks(x_pre, [&](const float* xr, int, int rb) {
-            gram_accumulate<B, false>(xr, xp, m, rb, g);
-          });
+      if (kv == 0 && h == 0) {
+        const int st = full_pos[static_cast<size_t>(b) * F + r0];
+        if (tid == 0) {
+          span_start[static_cast<size_t>(b) * S + j] = st;
+          span_len[static_cast<size_t>(b) * S + j] = n;
+          tok_off[static_cast<size_t>(b) * (S + 1) + j + 1] =
+              tok_off[static_cast<size_t>(b) * (S + 1) + j] + n;
+          tok_pad[static_cast<size_t>(b) * (S + 1) + j + 1] = tp + round_up(n, 16);
+          log_len[static_cast<size_t>(b) * S + j] = static_cast<float>(log(static_cast<double>(n)));
         }
-        gram_store<B>(g, m, Lg, work, Pg);
-      };
-      if (m > 64)
-        run(std::integral_constant<int, 8>());
-      else if (m > 32)
-        run(std::integral_constant<int, 4>());
-      else if (m > 16)
-        run(std::integral_constant<int, 2>());
-      else
-        run(std::integral_constant<int, 1>());
-    };
-    const int rmax = min(rank, m);
-    int P = Pj;
-    int rj = 0;
-    bool tri = rmax <= kMaxEig - 1;
-    if (tri) {
-      const int Pt = m + 1 + (m & 1);  // odd pitch: a wave's rows fall in distinct banks
-      gram(m, Pt);
-      if (m > 64)
-        tridiagonalize<2, 64>(work, m, Pt, es);
-      else if (m > 32)
-        tridiagonalize<4, 16>(work, m, Pt, es);
-      else if (m > 16)
-        tridiagonalize<8, 4>(work, m, Pt, es);
-      else
-        tridiagonalize<16, 1>(work, m, Pt, es);
-      const int nev = min(rmax + 1, m);
-      double2* de = reinterpret_cast<double2*>(part);  // free after the summary
-      top_eigenvalues(m, nev, es, de);
-      const double l0 = es.lam[0];
-      for (int k = 0; k + 1 < nev; ++k)
-        if (es.lam[k] - es.lam[k + 1] <= kClusterGap * l0 && es.lam[k] > kSignificant * l0)
-          tri = false;
-      if (tri) {
-        double* zs = reinterpret_cast<double*>(stage);
-        if (rmax <= 16)
-          top_eigenvectors<16, 8>(work, m, Pt, rmax, es, de, zs, sh);
-        else
-          top_eigenvectors<8, 16>(work, m, Pt, rmax, es, de, zs, sh);
-        P = Pt;
-        rj = rmax;
-      } else if (rows_form) {
-        load_rows(0, n, x_pre);  // G took X's place
+        for (int p = st + tid; p < min(st + n, T); p += kCloseThreads)
+          span_id[static_cast<size_t>(b) * T + p] = j;
       }
-    }
-    if (!tri) {
-      gram(Lp, Pj);
-      jacobi_sweeps<kCloseThreads>(work, m, Lp, Pj, sh);
-      rj = top_rows<kCloseThreads>(work, m, Lp, Pj, rank, sh);
-    }
-    if (rows_form && x_post != nullptr) load_rows(0, n, x_post);
-
+      __syncthreads();
+    };
     auto a_store = [&](int t, int k, double val) {
       if (kv)
         a_v[static_cast<size_t>(u) * Np * rank + avt_off(tp + t, k, rank)] = E::from_f64(val);
@@ -1367,64 +1462,7 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
       else
         w_k[((static_cast<size_t>(u) * S + j) * rank + k) * d + e] = E::from_f64(val);
     };
-    if (rows_form) {
-      // A[t][k] = sigma_k u_k[t] = row_k[t] / sigma_k
-      for (int o = tid; o < n * rj; o += kCloseThreads) {
-        const int t = o / rj;
-        const int k = o - t * rj;
-        const double lam = sh.sig[sh.top[k]];
-        a_store(t, k, lam > 0.0 ? work[sh.top[k] * P + t] / sqrt(lam) : 0.0);
-      }
-      // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3; thread -> kOut outputs
-      constexpr int kOut = 32 * 128 / kCloseThreads;
-      double wacc[kOut] = {};
-      for_blocks(x_post, [&](const float* xr, int t0, int rb) {
-#pragma unroll
-        for (int q = 0; q < kOut; ++q) {
-          const int o = tid + q * kCloseThreads;
-          if (o < rj * d) {
-            const int k = o / d;
-            const int e = o - k * d;
-            const double* uk = work + sh.top[k] * P + t0;
-            for (int t = 0; t < rb; ++t)
-              wacc[q] = fma(static_cast<double>(xr[t * xp + e]), uk[t], wacc[q]);
-          }
-        }
-      });
-#pragma unroll
-      for (int q = 0; q < kOut; ++q) {
-        const int o = tid + q * kCloseThreads;
-        if (o < rj * d) {
-          const int k = o / d;
-          const double lam = sh.sig[sh.top[k]];
-          w_store(k, o - k * d, lam > 0.0 ? wacc[q] / (lam * sqrt(lam)) : 0.0);
-        }
-      }
-    } else {
-      // W[k] = w_k = row_k / sigma_k^2
-      for (int o = tid; o < rj * d; o += kCloseThreads) {
-        const int k = o / d;
-        const int e = o - k * d;
-        const double lam = sh.sig[sh.top[k]];
-        w_store(k, e, lam > 0.0 ? work[sh.top[k] * P + e] / lam : 0.0);
-      }
-      // A[t][k] = X[t] . w_k
-      for_blocks(x_post, [&](const float* xr, int t0, int rb) {
-        for (int o = tid; o < rb * rj; o += kCloseThreads) {
-          const int t = o / rj;
-          const int k = o - t * rj;
-          const double lam = sh.sig[sh.top[k]];
-          double s = 0.0;
-          if (lam > 0.0) {
-            const double* wk = work + sh.top[k] * P;
-            for (int e = 0; e < d; ++e) s = fma(static_cast<double>(xr[t * xp + e]), wk[e], s);
-            s /= lam;
-          }
-          a_store(t0 + t, k, s);
-        }
-      });
-    }
-    __syncthreads();
+    factor_run(n, d, rank, L, load_rows, pre, a_store, w_store);
 
     // ---- the run leaves the full-resolution set
     for_row_vectors(kv != 0, r0, r0 + n, d, [&](size_t off, const int (&rr)[8],
@@ -1438,27 +1476,95 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
   }
 }
 
+// Build, spans whose rows exceed factor_kernel's LDS working matrix: one
+// item per (unit, span, K or V) from the list `items` ((u S + j) 2 + kv),
+// factored through the Gram matrix as a closing is, with the rows read from
+// the row-major K/V input (16-byte vectors).
+template <int DT>
+__global__ __launch_bounds__(kCloseThreads) void factor_gram_kernel(
+    const typename Elem<DT>::T* __restrict__ K, const typename Elem<DT>::T* __restrict__ V,
+    const int32_t* __restrict__ span_start, const int32_t* __restrict__ span_len,
+    const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ items, int n_items, int T,
+    int d, int S, int Np, int Hkv, int rank, typename Elem<DT>::T* __restrict__ a_k,
+    typename Elem<DT>::T* __restrict__ a_v, typename Elem<DT>::T* __restrict__ w_k,
+    typename Elem<DT>::T* __restrict__ w_v) {
+  typedef Elem<DT> E;
+  typedef typename E::T ST;
+  __shared__ FactorShared sh;
+  __shared__ __align__(16) double work[kCloseWork];
+  __shared__ __align__(16) float stage[kBlock * (128 + 4)];
+  __shared__ __align__(16) double part[kCloseThreads + 8];
+  __shared__ EigShared es;
+  const int tid = threadIdx.x;
+  const RunLds L{work, stage, part, &es, &sh};
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int item = items[it];
+    const int kv = item & 1;
+    const int rest = item >> 1;
+    const int j = rest % S;
+    const int u = rest / S;
+    const int b = u / Hkv;
+    const int n = span_len[static_cast<size_t>(b) * S + j];
+    const int st = span_start[static_cast<size_t>(b) * S + j];
+    const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
+    const ST* X = (kv ? V : K) + (static_cast<size_t>(u) * T + st) * d;
+    const int xp = d + 4;
+    auto load_rows = [&](int t0, int rb, float* dst) {
+      const int vpr = d / 8;  // 8-element vectors per row
+      for (int idx = tid; idx < rb * vpr; idx += kCloseThreads) {
+        const int t = idx / vpr;
+        const int c8 = idx - t * vpr;
+        float v[8];
+        load8<DT>(X + static_cast<size_t>(t0 + t) * d + 8 * c8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[t * xp + 8 * c8 + e] = v[e];
+      }
+      __syncthreads();
+    };
+    auto pre = [](const float*, const auto&) {};
+    auto a_store = [&](int t, int k, double val) {
+      if (kv)
+        a_v[static_cast<size_t>(u) * Np * rank + avt_off(tp + t, k, rank)] = E::from_f64(val);
+      else
+        a_k[(static_cast<size_t>(u) * Np + tp + t) * rank + k] = E::from_f64(val);
+    };
+    auto w_store = [&](int k, int e, double val) {
+      if (kv)
+        w_v[static_cast<size_t>(u) * S * d * rank4(rank) + wvt_off(j, k, e, d, rank)] =
+            E::from_f64(val);
+      else
+        w_k[((static_cast<size_t>(u) * S + j) * rank + k) * d + e] = E::from_f64(val);
+    };
+    factor_run(n, d, rank, L, load_rows, pre, a_store, w_store);
+  }
+}
+
 template <int DT>
 hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t st,
                        std::string* err) {
   typedef typename Elem<DT>::T T;
   const int U = c->B * c->Hkv;
   const long long n_items = 2ll * U * c->S;
-  // Longest span decides the global slab size of the large-span pass.
+  // spans whose rows do not fit factor_kernel's LDS working matrix go to
+  // factor_gram_kernel through a list built from the span lengths
   std::vector<int32_t> lens(static_cast<size_t>(c->B) * c->S);
   hipError_t e = hipMemcpyAsync(lens.data(), c->dev.span_len, lens.size() * sizeof(int32_t),
                                 hipMemcpyDeviceToHost, st);
   if (e != hipSuccess) return e;
   e = hipStreamSynchronize(st);
   if (e != hipSuccess) return e;
-  long long n_large = 0;
-  int max_len = 0;
-  for (int b = 0; b < c->B; ++b)
+  std::vector<int32_t> large;
+  for (int u = 0; u < U; ++u) {
+    const int b = u / c->Hkv;
     for (int j = 0; j < c->h_n_spans[b]; ++j) {
       const int n = lens[static_cast<size_t>(b) * c->S + j];
-      max_len = std::max(max_len, n);
-      if (static_cast<long long>(n) * c->d > kLdsWork) n_large += 2 * U / c->B;
+      if (static_cast<long long>(n) * c->d > kLdsWork) {
+        const int32_t it = static_cast<int32_t>((static_cast<long long>(u) * c->S + j) * 2);
+        large.push_back(it);
+        large.push_back(it + 1);
+      }
     }
+  }
   const int grid_small = static_cast<int>(std::min<long long>(n_items, 1 << 20));
   if (n_items > 0) {
     hipLaunchKernelGGL((factor_kernel<DT, true>), dim3(grid_small), dim3(kFacThreads), 0, st,
@@ -1470,26 +1576,27 @@ hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (n_large > 0) {
-    const size_t slab = static_cast<size_t>(max_len) * c->d;
-    const size_t budget = size_t(512) << 20;
-    long long nb = static_cast<long long>(budget / (slab * sizeof(double)));
-    nb = std::max<long long>(1, std::min<long long>({nb, n_large, 1024}));
-    double* scratch =
-        static_cast<double*>(c->mem.alloc(static_cast<size_t>(nb) * slab * sizeof(double), st));
-    if (scratch == nullptr) {
-      if (err) *err = "device allocation failed: factor scratch";
+  if (!large.empty()) {
+    const size_t bytes = large.size() * sizeof(int32_t);
+    int32_t* items = static_cast<int32_t*>(c->mem.alloc(bytes, st));
+    if (items == nullptr) {
+      if (err) *err = "device allocation failed: long-span item list";
       return hipErrorOutOfMemory;
     }
-    hipLaunchKernelGGL((factor_kernel<DT, false>), dim3(static_cast<unsigned>(nb)),
-                       dim3(kFacThreads), 0, st, static_cast<const T*>(K),
-                       static_cast<const T*>(V), c->dev.span_start, c->dev.span_len,
-                       c->dev.tok_pad, c->dev.n_spans, c->T, c->d, c->S, c->Np, c->Hkv, c->rank,
-                       n_items, static_cast<T*>(c->dev.a_k), static_cast<T*>(c->dev.a_v),
-                       static_cast<T*>(c->dev.w_k), static_cast<T*>(c->dev.w_v), scratch, slab);
-    e = hipGetLastError();
+    e = hipMemcpyAsync(items, large.data(), bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) {
+      const int n_large = static_cast<int>(large.size());
+      hipLaunchKernelGGL((factor_gram_kernel<DT>), dim3(std::min(n_large, 2048)),
+                         dim3(kCloseThreads), 0, st, static_cast<const T*>(K),
+                         static_cast<const T*>(V), c->dev.span_start, c->dev.span_len,
+                         c->dev.tok_pad, items, n_large, c->T, c->d, c->S, c->Np, c->Hkv, c->rank,
+                         static_cast<T*>(c->dev.a_k), static_cast<T*>(c->dev.a_v),
+                         static_cast<T*>(c->dev.w_k), static_cast<T*>(c->dev.w_v));
+      e = hipGetLastError();
+    }
+    // the host list must outlive the copy, the device list the kernel
     const hipError_t e2 = hipStreamSynchronize(st);
-    c->mem.release(scratch, st);
+    c->mem.release(items, st);
     if (e != hipSuccess) return e;
     if (e2 != hipSuccess) return e2;
   }

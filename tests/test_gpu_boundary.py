@@ -101,7 +101,7 @@ BUILDERS = {"spans": _span_builder, "import": _import_builder, "window": _window
 
 @pytest.mark.parametrize("kind", sorted(BUILDERS))
 def test_allocator_hook_failure_returns_enomem_and_frees(kind):
-    # spans longer than 48 tokens: the factor pass's global scratch is used
+    # spans longer than 48 tokens: the build allocates its long-span item list
     wl = W.generate("long_128k_bf16", B=2, Hq=8, Hkv=2, T=8192, steps=1)
     build = BUILDERS[kind](wl)
     # earlier tests' tensors must not be released while the baseline holds
