@@ -848,11 +848,24 @@ __device__ __forceinline__ void rescale2(double& a, double& b) {
 // along the leading principal minors det(T_i - x I), i = 0..m (Sturm),
 // from their three-term recurrence (de[i] = (d_i, e_{i-1}^2)); a zero minor
 // counts as positive (the next minor then has the sign opposite to the one
-// before, so the count is unchanged).  The last two minors are rescaled
-// every 4 steps.
-__device__ __forceinline__ int sturm_count(const double2* __restrict__ de, int m, double x) {
-  double p0 = 1.0, p1 = de[0].x - x;
+// before, so the count is unchanged).  Also the Newton step -f(x) / f'(x)
+// for f(x) = det(T - x I): the derivatives of the minors follow p'_i =
+// (d_i - x) p'_{i-1} - p_{i-1} - e_{i-1}^2 p'_{i-2}.  Every 4 steps the
+// last two minors and derivatives are rescaled by one power of two.
+__device__ __forceinline__ int sturm_newton(const double2* __restrict__ de, int m, double x,
+                                            double& step) {
+  double p0 = 1.0, p1 = de[0].x - x, q0 = 0.0, q1 = -1.0;
   int cnt = p1 < 0.0;
+  auto one = [&](const double2 qq) {
+    const double a = qq.x - x;
+    const double p2 = fma(a, p1, -qq.y * p0);
+    const double q2 = fma(a, q1, -fma(qq.y, q0, p1));
+    cnt += (p2 < 0.0) != (p1 < 0.0);
+    p0 = p1;
+    p1 = p2;
+    q0 = q1;
+    q1 = q2;
+  };
   int i = 1;
   // de is padded to 128 + 4 entries: the block loaded ahead stays in bounds
   double2 qn[4];
@@ -866,31 +879,37 @@ __device__ __forceinline__ int sturm_count(const double2* __restrict__ de, int m
       qn[u] = de[i + 4 + u];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const double p2 = fma(q[u].x - x, p1, -q[u].y * p0);
-      cnt += (p2 < 0.0) != (p1 < 0.0);
-      p0 = p1;
-      p1 = p2;
-    }
-    rescale2(p0, p1);
+    for (int u = 0; u < 4; ++u) one(q[u]);
+    const int ex =
+        __builtin_amdgcn_frexp_exp((fabs(p0) + fabs(p1)) + (fabs(q0) + fabs(q1)));
+    p0 = __builtin_amdgcn_ldexp(p0, -ex);
+    p1 = __builtin_amdgcn_ldexp(p1, -ex);
+    q0 = __builtin_amdgcn_ldexp(q0, -ex);
+    q1 = __builtin_amdgcn_ldexp(q1, -ex);
   }
-  for (; i < m; ++i) {
-    const double2 q = de[i];
-    const double p2 = fma(q.x - x, p1, -q.y * p0);
-    cnt += (p2 < 0.0) != (p1 < 0.0);
-    p0 = p1;
-    p1 = p2;
-  }
+  for (; i < m; ++i) one(de[i]);
+  step = q1 != 0.0 ? -p1 / q1 : 0.0;
   return cnt;
+}
+
+// Minimum and maximum over aligned groups of g lanes (g a power of two).
+template <class T>
+__device__ __forceinline__ void group_min_max(T& mn, T& mx, int g) {
+  for (int o = 1; o < g; o <<= 1) {
+    mn = min(mn, __shfl_xor(mn, o, kWave));
+    mx = max(mx, __shfl_xor(mx, o, kWave));
+  }
 }
 
 // The nev largest eigenvalues of T (es.d, es.e; m) into es.lam, largest
 // first, for T scaled by a power of two to entries of magnitude <= 1
 // (es.d and es.e are scaled in place, the scale goes to es.lim[2], and
 // de receives (d_i, e_{i-1}^2)).  A group of g lanes per eigenvalue
-// evaluates g Sturm counts spread evenly over its interval and keeps the
-// sub-interval where the count passes the eigenvalue's index, until the
-// interval is a few ulps wide.  Ends with a barrier.
+// evaluates Sturm counts at g - 1 points spread evenly over its bracket and
+// at a Newton iterate, and keeps the smallest bracket the counts certify;
+// once the bracket holds this eigenvalue alone and the Newton step is at
+// rounding level the iterate is the eigenvalue, else the bracket narrows to
+// a few ulps.  Ends with a barrier.
 __device__ __forceinline__ void top_eigenvalues(int m, int nev, EigShared& es, double2* de) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -938,22 +957,60 @@ __device__ __forceinline__ void top_eigenvalues(int m, int nev, EigShared& es, d
     const double pad = 4.0 * kEps * fmax(fabs(lo), fabs(hi)) + 4.0 * kEps;
     lo -= pad;
     hi += pad;
+    int clo = 0, chi = m;  // eigenvalues below lo and below hi
+    double xn = 0.5 * (lo + hi), lam = xn;
     const int base = lane & ~(g - 1);
-    for (int it = 0; it < 64; ++it) {
+    bool done = false;
+    for (int it = 0; it < 64 && !done; ++it) {
       if (hi - lo <= 2.0 * kEps * fmax(fabs(lo), fabs(hi)) + 2.0 * kEps) break;
-      const double w = (hi - lo) / static_cast<double>(g + 1);
-      const double x = fma(w, static_cast<double>(l + 1), lo);
-      const bool above = sturm_count(de, m, x) > idx;
-      const unsigned long long bal = __ballot(above);
+      // g - 1 points spread evenly over (lo, hi), and the Newton iterate
+      const double w = (hi - lo) / static_cast<double>(g);
+      const double x = l < g - 1 ? fma(w, static_cast<double>(l + 1), lo) : xn;
+      double step;
+      const int cnt = sturm_newton(de, m, x, step);
+      const bool above = cnt > idx;
+      // bracket from the even points (the first one above idx, by ballot),
+      // with the counts there
+      const unsigned long long bal = __ballot(above && l < g - 1);
       const unsigned long long gm = g == kWave ? bal : (bal >> base) & ((1ull << g) - 1ull);
-      const int s = gm ? __builtin_ctzll(gm) : g;
-      const double nlo = s == 0 ? lo : fma(w, static_cast<double>(s), lo);
-      const double nhi = s == g ? hi : fma(w, static_cast<double>(s + 1), lo);
-      if (!(nhi - nlo < hi - lo)) break;  // no progress left at this width
+      const int sa = gm ? __builtin_ctzll(gm) : g - 1;  // even points 0 .. g - 2
+      const int c_hi = __shfl(cnt, base + min(sa, g - 2), kWave);
+      const int c_lo = __shfl(cnt, base + max(sa - 1, 0), kWave);
+      double nlo = sa == 0 ? lo : fma(w, static_cast<double>(sa), lo);
+      double nhi = sa == g - 1 ? hi : fma(w, static_cast<double>(sa + 1), lo);
+      int nclo = sa == 0 ? clo : c_lo;
+      int nchi = sa == g - 1 ? chi : c_hi;
+      // and the Newton point, when it falls inside
+      const int cs = __shfl(cnt, base + g - 1, kWave);
+      {
+        const double xq = __shfl(x, base + g - 1, kWave);
+        if (xq > nlo && xq < nhi) {
+          if (cs > idx) {
+            nhi = xq;
+            nchi = cs;
+          } else {
+            nlo = xq;
+            nclo = cs;
+          }
+        }
+      }
+      // the Newton point and its step, from the group's last lane
+      const double xs = __shfl(x, base + g - 1, kWave);
+      const double ss = __shfl(step, base + g - 1, kWave);
+      const double xt = xs + ss;
+      if (nchi - nclo == 1 && fabs(ss) <= 4.0 * kEps * fabs(xs) && xt >= nlo && xt <= nhi) {
+        lam = xt;  // isolated, and the Newton step is at rounding level
+        done = true;
+      }
+      if (!(nhi - nlo < hi - lo) && !done) break;  // no progress left at this width
       lo = nlo;
       hi = nhi;
+      clo = nclo;
+      chi = nchi;
+      xn = xt > lo && xt < hi ? xt : 0.5 * (lo + hi);
     }
-    if (l == 0) es.lam[kk] = 0.5 * (lo + hi);
+    if (!done) lam = 0.5 * (lo + hi);
+    if (l == 0) es.lam[kk] = lam;
   }
   __syncthreads();
 }
@@ -1182,8 +1239,9 @@ struct RunLds {
 };
 
 template <class LoadRows, class Pre, class AOut, class WOut>
-__device__ void factor_run(int n, int d, int rank, const RunLds& L, const LoadRows& load_rows,
-                           const Pre& pre, const AOut& a_store, const WOut& w_store) {
+__device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds& L,
+                                           const LoadRows& load_rows, const Pre& pre,
+                                           const AOut& a_store, const WOut& w_store) {
   const int tid = threadIdx.x;
   double* const work = L.work;
   float* const stage = L.stage;
