@@ -318,8 +318,8 @@ __device__ int top_rows(const double* work, int cnt, int L, int P, int rank,
 }
 
 // Rank-r factors of the n x d matrix X whose element (t, c) is x(t, c), in
-// fp64 (build path, kFacThreads threads).  `work` holds n*d doubles (LDS or
-// global).  Jacobi runs on the shorter side of X:
+// fp64 (build path, kFacThreads threads).  `work` holds n*d doubles of LDS.
+// Jacobi runs on the shorter side of X:
 //   n <= d: rows of X; the rotated rows are sigma_i w_i^T and A = X W_r;
 //   n >  d: columns of X; they become sigma_i u_i, so A = X'[:, top] and
 //           w_i = X^T x'_i / sigma_i^2.
@@ -388,28 +388,23 @@ __device__ void factor_matrix(const Ld& x, int n, int d, int rank, double* work,
   __syncthreads();
 }
 
-// Build: one item per (unit, span, K or V); the span's rows are read from
-// the row-major K/V inputs.  A_K rows at the span's padded offset, A_V in
-// transposed 16-row tiles, W_K rows [r][d], W_V in the paired layout
-// (layout.h).
-template <int DT, bool kLds>
+// Build: one item per (unit, span, K or V) for the spans whose rows fit the
+// LDS working matrix (longer ones go to factor_gram_kernel); the span's rows
+// are read from the row-major K/V inputs.  A_K rows at the span's padded
+// offset, A_V in transposed 16-row tiles, W_K rows [r][d], W_V in the
+// paired layout (layout.h).
+template <int DT>
 __global__ __launch_bounds__(kFacThreads) void factor_kernel(
     const typename Elem<DT>::T* __restrict__ K, const typename Elem<DT>::T* __restrict__ V,
     const int32_t* __restrict__ span_start, const int32_t* __restrict__ span_len,
     const int32_t* __restrict__ tok_pad, const int32_t* __restrict__ n_spans, int T, int d,
     int S, int Np, int Hkv, int rank, long long n_items, typename Elem<DT>::T* __restrict__ a_k,
     typename Elem<DT>::T* __restrict__ a_v, typename Elem<DT>::T* __restrict__ w_k,
-    typename Elem<DT>::T* __restrict__ w_v, double* __restrict__ scratch, size_t slab) {
+    typename Elem<DT>::T* __restrict__ w_v) {
   typedef Elem<DT> E;
   typedef typename E::T ST;
   __shared__ FactorShared sh;
-  double* work;
-  if constexpr (kLds) {
-    __shared__ double lds_work[kLdsWork];
-    work = lds_work;
-  } else {
-    work = scratch + static_cast<size_t>(blockIdx.x) * slab;
-  }
+  __shared__ double work[kLdsWork];
 
   for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int kv = static_cast<int>(item & 1);
@@ -419,8 +414,7 @@ __global__ __launch_bounds__(kFacThreads) void factor_kernel(
     const int b = u / Hkv;
     if (j >= n_spans[b]) continue;
     const int n = span_len[static_cast<size_t>(b) * S + j];
-    const bool small = static_cast<long long>(n) * d <= kLdsWork;
-    if (small != kLds) continue;
+    if (static_cast<long long>(n) * d > kLdsWork) continue;
     const int st = span_start[static_cast<size_t>(b) * S + j];
     const ST* X = (kv ? V : K) + (static_cast<size_t>(u) * T + st) * d;
     const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
@@ -1625,12 +1619,12 @@ hipError_t factor_impl(rskv_cache* c, const void* K, const void* V, hipStream_t 
   }
   const int grid_small = static_cast<int>(std::min<long long>(n_items, 1 << 20));
   if (n_items > 0) {
-    hipLaunchKernelGGL((factor_kernel<DT, true>), dim3(grid_small), dim3(kFacThreads), 0, st,
+    hipLaunchKernelGGL((factor_kernel<DT>), dim3(grid_small), dim3(kFacThreads), 0, st,
                        static_cast<const T*>(K), static_cast<const T*>(V), c->dev.span_start,
                        c->dev.span_len, c->dev.tok_pad, c->dev.n_spans, c->T, c->d, c->S, c->Np,
                        c->Hkv, c->rank, n_items, static_cast<T*>(c->dev.a_k),
                        static_cast<T*>(c->dev.a_v), static_cast<T*>(c->dev.w_k),
-                       static_cast<T*>(c->dev.w_v), nullptr, size_t(0));
+                       static_cast<T*>(c->dev.w_v));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
