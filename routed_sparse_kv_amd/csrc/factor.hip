@@ -524,28 +524,41 @@ __device__ __forceinline__ void for_row_vectors(bool vtile, int lo, int hi, int 
 }
 
 // G[a][b] (a, b < m, pitch P) += sum over q < len of Y(q, a) Y(q, b) for
-// an LDS matrix of floats, in fp64 and in order of q; thread -> B x B block
-// of G (accumulated in registers g).  kByRow: Y(q, i) = y[i * ys + q] (X
-// rows, ys the row pitch; len and ys multiples of 4, so four values of q
-// come as one 16-byte vector); otherwise Y(q, i) = y[q * ys + i] (a
-// thread's B values are contiguous and, for B >= 4, read as vectors).
+// an LDS matrix of floats, in fp64 and in order of q; thread (ta, tb) ->
+// the B x B entries of G at a = gram_index(ta, i), b = gram_index(tb, k)
+// (accumulated in registers g).  The indices of a thread are strided by nb
+// (the number of thread rows), so that the 16 lanes of a wave that differ in
+// tb read 16 neighbouring rows (or 16 neighbouring 4-column groups), which
+// fall in distinct LDS banks.  kByRow: Y(q, i) = y[i * ys + q] (X rows, ys
+// the row pitch; len and ys multiples of 4, so four values of q come as
+// one 16-byte vector); otherwise Y(q, i) = y[q * ys + i] (for B >= 4 a
+// thread's indices come in groups of four contiguous ones, read as
+// vectors).
+template <int B, bool kByRow>
+__device__ __forceinline__ int gram_index(int t, int i, int nb) {
+  if constexpr (kByRow || B % 4 != 0)
+    return t + nb * i;
+  else
+    return 4 * (t + nb * (i / 4)) + (i & 3);
+}
+
 template <int B, bool kByRow>
 __device__ __forceinline__ void gram_accumulate(const float* y, int ys, int m, int len,
                                                 double (&g)[B][B]) {
   const int tid = threadIdx.x;
   const int nb = (m + B - 1) / B;
   if (tid >= nb * nb) return;
-  const int a0 = B * (tid / nb), b0 = B * (tid % nb);
-  const bool full = a0 + B <= m && b0 + B <= m;
+  const int ta = tid / nb, tb = tid - ta * nb;
   if constexpr (kByRow) {
     for (int q = 0; q < len; q += 4) {
       float4 va[B], vb[B];
 #pragma unroll
       for (int i = 0; i < B; ++i) {
-        va[i] = a0 + i < m ? *reinterpret_cast<const float4*>(y + (a0 + i) * ys + q)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-        vb[i] = b0 + i < m ? *reinterpret_cast<const float4*>(y + (b0 + i) * ys + q)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int a = gram_index<B, kByRow>(ta, i, nb), b = gram_index<B, kByRow>(tb, i, nb);
+        va[i] = a < m ? *reinterpret_cast<const float4*>(y + a * ys + q)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        vb[i] = b < m ? *reinterpret_cast<const float4*>(y + b * ys + q)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int i = 0; i < B; ++i)
@@ -559,22 +572,29 @@ __device__ __forceinline__ void gram_accumulate(const float* y, int ys, int m, i
         }
     }
   } else {
+    // a thread's last index is below m exactly when all of them are (the
+    // indices grow with i)
+    const bool full = gram_index<B, kByRow>(ta, B - 1, nb) < m &&
+                      gram_index<B, kByRow>(tb, B - 1, nb) < m;
 #pragma unroll 4
     for (int q = 0; q < len; ++q) {
       double ya[B], yb[B];
       if (B % 4 == 0 && full) {
 #pragma unroll
         for (int i = 0; i < B; i += 4) {
-          const float4 wa = *reinterpret_cast<const float4*>(y + q * ys + a0 + i);
-          const float4 wb = *reinterpret_cast<const float4*>(y + q * ys + b0 + i);
+          const float4 wa =
+              *reinterpret_cast<const float4*>(y + q * ys + gram_index<B, kByRow>(ta, i, nb));
+          const float4 wb =
+              *reinterpret_cast<const float4*>(y + q * ys + gram_index<B, kByRow>(tb, i, nb));
           ya[i] = wa.x; ya[i + 1] = wa.y; ya[i + 2] = wa.z; ya[i + 3] = wa.w;
           yb[i] = wb.x; yb[i + 1] = wb.y; yb[i + 2] = wb.z; yb[i + 3] = wb.w;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-          ya[i] = a0 + i < m ? static_cast<double>(y[q * ys + a0 + i]) : 0.0;
-          yb[i] = b0 + i < m ? static_cast<double>(y[q * ys + b0 + i]) : 0.0;
+          const int a = gram_index<B, kByRow>(ta, i, nb), b = gram_index<B, kByRow>(tb, i, nb);
+          ya[i] = a < m ? static_cast<double>(y[q * ys + a]) : 0.0;
+          yb[i] = b < m ? static_cast<double>(y[q * ys + b]) : 0.0;
         }
       }
 #pragma unroll
@@ -585,20 +605,22 @@ __device__ __forceinline__ void gram_accumulate(const float* y, int ys, int m, i
   }
 }
 
-// Writes the thread's block of G and zeroes columns m..Lp-1.  Ends with a
-// barrier.
-template <int B>
+// Writes the thread's entries of G (indices as gram_accumulate) and zeroes
+// columns m..Lp-1.  Ends with a barrier.
+template <int B, bool kByRow>
 __device__ __forceinline__ void gram_store(const double (&g)[B][B], int m, int Lp, double* G,
                                            int P) {
   const int tid = threadIdx.x;
   const int nb = (m + B - 1) / B;
   if (tid < nb * nb) {
-    const int a0 = B * (tid / nb), b0 = B * (tid % nb);
+    const int ta = tid / nb, tb = tid - ta * nb;
 #pragma unroll
     for (int i = 0; i < B; ++i)
 #pragma unroll
-      for (int k = 0; k < B; ++k)
-        if (a0 + i < m && b0 + k < m) G[(a0 + i) * P + b0 + k] = g[i][k];
+      for (int k = 0; k < B; ++k) {
+        const int a = gram_index<B, kByRow>(ta, i, nb), b = gram_index<B, kByRow>(tb, k, nb);
+        if (a < m && b < m) G[a * P + b] = g[i][k];
+      }
   }
   for (int idx = tid; idx < m * (Lp - m); idx += kCloseThreads) {
     const int a = idx / (Lp - m);
@@ -634,7 +656,8 @@ struct EigShared {
   double p[128];    // tau_k G v of the current step, 0 outside the trailing block
   double red[2][kCloseWaves];
   double lam[kMaxEig];  // eigenvalues of the scaled T, largest first
-  double zn[16];        // 1 / ||z|| of the tridiagonal eigenvectors of a batch
+  double zn[16];        // the two halves of ||z||^2 of a batch's tridiagonal eigenvectors
+  int tw[8];            // their twist indices
   double lim[3];        // Gershgorin interval of the scaled T, and the scale
 };
 
@@ -693,27 +716,38 @@ __device__ __forceinline__ double keep(double x) {
 
 typedef __attribute__((address_space(3))) double lds_f64;
 typedef __attribute__((address_space(3))) EigShared lds_eig;
-template <int L, int C>
-__device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared& es_) {
-  constexpr int kBlk = C < 8 ? C : 8;
+template <int L, int R, int C, bool kScalarLoop>
+__device__ __noinline__ void tridiagonalize(double* A_, int m_, int P_, EigShared& es_) {
+  // arguments of a call arrive in vector registers; kScalarLoop makes them
+  // wave-uniform, so that the step loop and its block tests run on scalar
+  // registers
+  const int m = kScalarLoop ? __builtin_amdgcn_readfirstlane(m_) : m_;
+  const int P = kScalarLoop ? __builtin_amdgcn_readfirstlane(P_) : P_;
+  constexpr int kGroups = kCloseThreads / L;  // row groups of L lanes
+  constexpr int kGw = kWave / L;              // row groups per wave
+  constexpr int kBlk = kScalarLoop ? (C < 4 ? C : 4) : (C < 8 ? C : 8);
+  static_assert(kGroups * R <= 128 && L * C <= 128 && kGroups * R >= L * C, "tile");
   lds_f64* A = (lds_f64*)A_;
   lds_eig* es = (lds_eig*)&es_;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int i = tid / L;
-  const int h = tid - i * L;
-  const bool own = i < m;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const int g = tid / L;
+  const int h = tid - g * L;
   // whole rows of 128 entries are read: i, j < 128 and P <= 130 keep every
   // address inside the LDS work array; entries past m are replaced by 0
-  double a[C];
+  double a[R][C];
 #pragma unroll
-  for (int c = 0; c < C; ++c) a[c] = A[i * P + h + L * c];
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int j = h + L * c;
-    const double kx = keep(a[c]);
-    a[c] = own && j < m ? kx : 0.0;
-  }
+    for (int c = 0; c < C; ++c) a[r][c] = A[(g + kGroups * r) * P + h + L * c];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const double kx = keep(a[r][c]);
+      a[r][c] = g + kGroups * r < m && h + L * c < m ? kx : 0.0;
+    }
   if (tid < 128) es->p[tid] = 0.0;
   // reflector r (r <= m - 3) from row r of A in LDS, by the 64 lanes of
   // one wave (two entries each): v scaled to v_{r+1} = 1 into vb and back
@@ -751,39 +785,82 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
   __syncthreads();
   for (int k = 0; k + 2 < m; ++k) {
     const double tau = es->tau[k];
+    const bool refl =
+        kScalarLoop ? __builtin_amdgcn_readfirstlane(tau != 0.0 ? 1 : 0) != 0 : tau != 0.0;
     const lds_f64* vb = es->vb[k & 1];
-    const bool act = own && i > k;
-    // waves whose rows all lie outside the trailing block skip both phases
-    const bool wave_live = (tid | (kWave - 1)) / L > k && (tid & ~(kWave - 1)) / L < m;
-    double pi = 0.0, vi = 0.0;
-    if (tau != 0.0 && wave_live) {
-      double part = 0.0;
+    // slot r of this wave holds rows kGroups r + kGw wv + [0, kGw): live
+    // while one of them lies in the trailing block k + 1 .. m - 1; column
+    // block b (lane h's columns h + L c, c in [kBlk b, kBlk b + kBlk)) is
+    // live while one of its columns does
+    auto slot_live = [&](int r) {
+      const int lo = kGroups * r + kGw * wv;
+      return lo + kGw - 1 > k && lo < m;
+    };
+    auto blk_live = [&](int b) { return (L - 1) + L * (kBlk * b + kBlk - 1) > k; };
+    double pi[R], vi[R];
+    double xv[C];  // v_j of this lane's columns (live blocks only)
+    double pvl = 0.0;
+    if (refl) {
+      double part[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[r] = 0.0;
 #pragma unroll
       for (int b = 0; b < C / kBlk; ++b) {
-        if ((L - 1) + L * (kBlk * b + kBlk - 1) < k + 1) continue;
+        if (!blk_live(b)) continue;
 #pragma unroll
-        for (int u = 0; u < kBlk; ++u) part = fma(a[kBlk * b + u], vb[h + L * (kBlk * b + u)], part);
+        for (int u = 0; u < kBlk; ++u) xv[kBlk * b + u] = vb[h + L * (kBlk * b + u)];
       }
-      part = group_sum_dpp<L>(part);
-      const double v = vb[i & 127];
-      pi = act ? tau * part : 0.0;
-      vi = act ? v : 0.0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (!slot_live(r)) continue;
+#pragma unroll
+        for (int b = 0; b < C / kBlk; ++b) {
+          if (!blk_live(b)) continue;
+#pragma unroll
+          for (int u = 0; u < kBlk; ++u)
+            part[r] = fma(a[r][kBlk * b + u], xv[kBlk * b + u], part[r]);
+        }
+        part[r] = group_sum_dpp<L>(part[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = g + kGroups * r;
+        const bool act = i > k && i < m;
+        const double v = vb[i];
+        pi[r] = act ? tau * part[r] : 0.0;
+        vi[r] = act ? v : 0.0;
+        pvl = fma(pi[r], vi[r], pvl);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) pi[r] = vi[r] = 0.0;
     }
-    if (h == 0 && i < 128) es->p[i] = pi;
-    const double pv = wave_sum_dpp(h == 0 ? pi * vi : 0.0);
-    if (lane == 0) es->red[1][tid / kWave] = pv;
+    if (h == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) es->p[g + kGroups * r] = pi[r];
+    }
+    const double pv = wave_sum_dpp(h == 0 ? pvl : 0.0);
+    if (lane == 0) es->red[1][wv] = pv;
     __syncthreads();
-    if (tau != 0.0 && wave_live) {
+    if (refl) {
       const double tpv = tau * ((es->red[1][0] + es->red[1][1]) + (es->red[1][2] + es->red[1][3]));
-      const double ci = pi - tpv * vi;  // w_i - (tau/2)(p.v) v_i
+      double ci[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) ci[r] = pi[r] - tpv * vi[r];  // w_i - (tau/2)(p.v) v_i
 #pragma unroll
       for (int b = 0; b < C / kBlk; ++b) {
-        if ((L - 1) + L * (kBlk * b + kBlk - 1) < k + 1) continue;
+        if (!blk_live(b)) continue;
+        double pj[kBlk];
 #pragma unroll
-        for (int u = 0; u < kBlk; ++u) {
-          const int j = h + L * (kBlk * b + u);
-          const double x = fma(-vi, es->p[j], a[kBlk * b + u]);
-          a[kBlk * b + u] = fma(-ci, vb[j], x);
+        for (int u = 0; u < kBlk; ++u) pj[u] = es->p[h + L * (kBlk * b + u)];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (!slot_live(r)) continue;
+#pragma unroll
+          for (int u = 0; u < kBlk; ++u) {
+            const double x = fma(-vi[r], pj[u], a[r][kBlk * b + u]);
+            a[r][kBlk * b + u] = fma(-ci[r], xv[kBlk * b + u], x);
+          }
         }
       }
     }
@@ -792,15 +869,22 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
       // spills past column m - 1 lands on later rows' LDS copies, which are
       // not read before their own rows overwrite them), then the next
       // reflector from it
-      if (i == k + 1) {
+      const int g1 = (k + 1) % kGroups;
+      const int r1 = (k + 1) / kGroups;
+      if (g == g1) {
 #pragma unroll
-        for (int b = 0; b < C / kBlk; ++b) {
-          if ((L - 1) + L * (kBlk * b + kBlk - 1) < k + 1) continue;
+        for (int r = 0; r < R; ++r) {
+          if (r != r1) continue;
 #pragma unroll
-          for (int u = 0; u < kBlk; ++u) A[i * P + h + L * (kBlk * b + u)] = a[kBlk * b + u];
+          for (int b = 0; b < C / kBlk; ++b) {
+            if (!blk_live(b)) continue;
+#pragma unroll
+            for (int u = 0; u < kBlk; ++u)
+              A[(k + 1) * P + h + L * (kBlk * b + u)] = a[r][kBlk * b + u];
+          }
         }
       }
-      if (tid / kWave == ((k + 1) * L) / kWave) {
+      if (wv == g1 / kGw) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -808,24 +892,28 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m, int P, EigShared&
       }
     } else {  // last step: the trailing 2 x 2 block
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int j = h + L * c;
-        if (i == m - 2 && j == m - 2) es->d[m - 2] = a[c];
-        if (i == m - 2 && j == m - 1) es->e[m - 2] = a[c];
-        if (i == m - 1 && j == m - 1) es->d[m - 1] = a[c];
-      }
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const int i = g + kGroups * r;
+          const int j = h + L * c;
+          if (i == m - 2 && j == m - 2) es->d[m - 2] = a[r][c];
+          if (i == m - 2 && j == m - 1) es->e[m - 2] = a[r][c];
+          if (i == m - 1 && j == m - 1) es->d[m - 1] = a[r][c];
+        }
     }
     __syncthreads();
   }
   if (m <= 2) {
-    if (own) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < C; ++c) {
+        const int i = g + kGroups * r;
         const int j = h + L * c;
-        if (j == i) es->d[i] = a[c];
-        if (i == 0 && j == 1 && m == 2) es->e[0] = a[c];
+        if (i < m && j == i) es->d[i] = a[r][c];
+        if (i == 0 && j == 1 && m == 2) es->e[0] = a[r][c];
       }
-    }
     __syncthreads();
   }
 }
@@ -1016,15 +1104,6 @@ __device__ __forceinline__ double guard_pivot(double x) {
   return fmin(fmax(y, -1.0 / kPivot), 1.0 / kPivot);
 }
 
-// Eigenvector of the scaled tridiagonal T (de[i] = (d_i, e_{i-1}^2), e)
-// for its eigenvalue lam by a twisted factorisation.  The top-down pivots
-// D+_i = P_{i+1} / P_i and bottom-up pivots D-_i = Q_i / Q_{i+1} are ratios
-// of the leading and trailing minors of T - lam I (three-term recurrences,
-// so the serial dependence is one multiply-add per step); gamma_i = D+_i +
-// D-_i - (d_i - lam), and at the twist t = argmin |gamma_i| the vector is
-// z_t = 1, z_i = -(e_i / D+_i) z_{i+1} above t and z_{i+1} = -(e_i /
-// D-_{i+1}) z_i below.  z (stride 16 doubles) holds D+ first, then the
-// recomputed D- below t, then the vector.  Returns ||z||^2.
 // One (d_i, e_{i-1}^2) pair from an LDS view of the pair array.
 struct Pair {
   double x, y;
@@ -1033,102 +1112,105 @@ __device__ __forceinline__ Pair pair_at(const lds_f64* de, int i) {
   return Pair{de[2 * i], de[2 * i + 1]};
 }
 
-__device__ double twisted_vector(const double2* de_, const double* e_, int m, double lam,
-                                 double* z_) {
-  // LDS views; de has m + 4 readable pairs, z stride 16.  Every pass
-  // loads the operands of the next two steps ahead of the current one.
+// Eigenvectors of the scaled tridiagonal T (de[i] = (d_i, e_{i-1}^2), e)
+// by twisted factorisations of T - lam I.  The top-down pivots D+_i =
+// P_{i+1} / P_i and the bottom-up pivots D-_i = Q_i / Q_{i+1} are ratios of
+// the leading and trailing minors (three-term recurrences, so the serial
+// dependence is one multiply-add per step); gamma_i = D+_i + D-_i - (d_i -
+// lam), and at the twist t = argmin |gamma_i| the vector is z_t = 1, z_i =
+// -(e_i / D+_i) z_{i+1} above t and z_i = -(e_{i-1} / D-_i) z_{i-1} below.
+// The two directions of a vector run on two lanes of one wave in lockstep
+// (the same instructions on different rows), each in its own column of z
+// (stride 16 doubles): twisted_pivots, then twist_index by the whole wave,
+// then twisted_solve, which overwrites the pivots it has used with z.
+
+// dir 0: D+_i at row s of step s; dir 1: D-_i at row m - 1 - s.
+__device__ void twisted_pivots(const double2* de_, int m, double lam, int dir, double* z_) {
+  // LDS views; de has m + 4 readable pairs.  The operands of the next two
+  // steps are loaded ahead of the current one.
   const lds_f64* de = (const lds_f64*)de_;
+  lds_f64* z = (lds_f64*)z_;
+  // row of step s (prefetches past the last row stay inside de) and its
+  // pair: d_i with e_{i-1}^2 top-down, e_i^2 bottom-up
+  auto row = [&](int s) { return dir ? max(m - 1 - s, 0) : s; };
+  auto ld = [&](int s) {
+    const int i = row(s);
+    return Pair{de[2 * i], de[2 * (i + dir) + 1]};
+  };
+  const int i0 = row(0);
+  double pa = 1.0, pb = de[2 * i0] - lam;
+  z[16 * i0] = guard_pivot(pb);
+  Pair q1 = ld(1), q2 = ld(2);
+#pragma unroll 4
+  for (int s = 1; s < m; ++s) {
+    const Pair q = q1;
+    q1 = q2;
+    q2 = ld(s + 2);
+    const double rb = recip(pb);
+    const double pc = fma(q.x - lam, pb, -q.y * pa);
+    z[16 * row(s)] = guard_pivot(pc * rb);
+    pa = pb;
+    pb = pc;
+    if ((s & 3) == 0) rescale2(pa, pb);  // powers of two: the ratios are unchanged
+  }
+}
+
+// The twist of one vector, by the whole wave: argmin |gamma_i| over i < m
+// with gamma_{m-1} = D+_{m-1}, the largest such index on ties.
+__device__ int twist_index(const double2* de_, const double* zp_, const double* zm_, int m,
+                           double lam) {
+  const lds_f64* de = (const lds_f64*)de_;
+  const lds_f64* zp = (const lds_f64*)zp_;
+  const lds_f64* zm = (const lds_f64*)zm_;
+  const int lane = threadIdx.x & (kWave - 1);
+  double best = INFINITY;
+  int bi = -1;
+  for (int i = lane; i < m; i += kWave) {
+    const double dp = zp[16 * i];
+    const double gam = i == m - 1 ? fabs(dp) : fabs(dp + zm[16 * i] - (de[2 * i] - lam));
+    if (gam <= best) {
+      best = gam;
+      bi = i;
+    }
+  }
+  double mn = best;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mn = fmin(mn, __shfl_xor(mn, o, kWave));
+  int t = best == mn ? bi : -1;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) t = max(t, __shfl_xor(t, o, kWave));
+  return t >= 0 ? t : m - 1;
+}
+
+// dir 0: z_i for i = t - 1 .. 0 over the D+ column; dir 1: i = t + 1 ..
+// m - 1 over the D- column.  Returns the lane's sum of z_i^2 (dir 1 counts
+// z_t = 1 as well).
+__device__ double twisted_solve(const double* e_, int m, int t, int dir, double* z_) {
   const lds_f64* e = (const lds_f64*)e_;
   lds_f64* z = (lds_f64*)z_;
-  double pa = 1.0, pb = pair_at(de, 0).x - lam;
-  z[0] = guard_pivot(pb);
-  {
-    Pair q1 = pair_at(de, 1), q2 = pair_at(de, 2);
+  const int n = dir ? m - 1 - t : t;  // steps of this lane
+  auto row = [&](int s) { return dir ? t + s : t - s; };
+  auto eix = [&](int s) { return max(dir ? t + s - 1 : t - s, 0); };
+  double zi = 1.0, nrm = dir ? 1.0 : 0.0;
+  double dn = z[16 * row(min(1, n))], en = e[eix(min(1, n))];
 #pragma unroll 4
-    for (int i = 1; i < m; ++i) {
-      const Pair q = q1;
-      q1 = q2;
-      q2 = pair_at(de, i + 2);
-      const double rb = recip(pb);
-      const double pc = fma(q.x - lam, pb, -q.y * pa);
-      z[16 * i] = guard_pivot(pc * rb);
-      pa = pb;
-      pb = pc;
-      if ((i & 3) == 0) rescale2(pa, pb);
-    }
+  for (int s = 1; s <= n; ++s) {
+    const double dd = dn, ee = en;
+    const int s1 = min(s + 1, n);
+    dn = z[16 * row(s1)];
+    en = e[eix(s1)];
+    zi = -(ee * recip(dd)) * zi;
+    z[16 * row(s)] = zi;
+    nrm = fma(zi, zi, nrm);
   }
-  double best = fabs(z[16 * (m - 1)]);
-  int t = m - 1;
-  // bottom-up minors Q_i = (d_i - lam) Q_{i+1} - e_i^2 Q_{i+2}, from
-  // i = m - 2 down to `stop`; at each step f(i, D-_i, d_i - lam)
-  auto bottom_up = [&](int stop, auto&& f) {
-    double qa = 1.0, qb = pair_at(de, m - 1).x - lam;
-    if (m - 2 < stop) return;
-    Pair c1 = pair_at(de, m - 2), n1 = pair_at(de, m - 1);
-    Pair c2 = pair_at(de, m >= 3 ? m - 3 : 0);
-#pragma unroll 4
-    for (int i = m - 2; i >= stop; --i) {
-      const Pair c = c1, n = n1;
-      n1 = c1;
-      c1 = c2;
-      c2 = pair_at(de, i >= 2 ? i - 2 : 0);
-      const double rb = recip(qb);
-      const double di = c.x - lam;
-      const double qc = fma(di, qb, -n.y * qa);
-      f(i, guard_pivot(qc * rb), di);
-      qa = qb;
-      qb = qc;
-      if ((i & 3) == 0) rescale2(qa, qb);
-    }
-  };
-  {
-    double dpn = m >= 2 ? z[16 * (m - 2)] : 0.0;
-    bottom_up(0, [&](int i, double dm, double di) {
-      const double dp = dpn;
-      dpn = z[16 * (i > 0 ? i - 1 : 0)];
-      const double gam = fabs(dp + dm - di);
-      const bool better = gam < best;
-      best = better ? gam : best;
-      t = better ? i : t;
-    });
-  }
-  // bottom-up pivots of rows t + 1 .. m - 1 (the same recurrence again)
-  if (t < m - 1) z[16 * (m - 1)] = guard_pivot(pair_at(de, m - 1).x - lam);
-  bottom_up(t + 1, [&](int i, double dm, double) { z[16 * i] = dm; });
-  double zi = 1.0, nrm = 1.0;
-  {
-    double dn = t + 1 < m ? z[16 * (t + 1)] : 1.0, en = e[t];
-#pragma unroll 4
-    for (int i = t + 1; i < m; ++i) {
-      const double dd = dn, ee = en;
-      dn = z[16 * (i + 1 < m ? i + 1 : i)];
-      en = e[i];
-      zi = -(ee * recip(dd)) * zi;
-      z[16 * i] = zi;
-      nrm = fma(zi, zi, nrm);
-    }
-  }
-  zi = 1.0;
-  {
-    double dn = t >= 1 ? z[16 * (t - 1)] : 1.0, en = t >= 1 ? e[t - 1] : 0.0;
-#pragma unroll 4
-    for (int i = t - 1; i >= 0; --i) {
-      const double dd = dn, ee = en;
-      dn = z[16 * (i >= 1 ? i - 1 : 0)];
-      en = e[i >= 1 ? i - 1 : 0];
-      zi = -(ee * recip(dd)) * zi;
-      z[16 * i] = zi;
-      nrm = fma(zi, zi, nrm);
-    }
-  }
-  z[16 * t] = 1.0;
   return nrm;
 }
 
 // Eigenvectors of G for the rj largest eigenvalues in es.lam (rj <= 32):
-// the twisted vectors of T (one lane each, four per wave, in batches of 16
-// held in `zs`, 16 m doubles of LDS), normalised and spread over groups of V lanes (EV
-// elements per lane), mapped back through the reflectors kept in A (the
+// the twisted vectors of T (two lanes each, two vectors per wave, in
+// batches of 8 held in `zs`, 16 m doubles of LDS: a column of top-down and
+// one of bottom-up pivots per vector), normalised and spread over groups of
+// V lanes (EV elements per lane), mapped back through the reflectors kept in A (the
 // next reflector's entries are loaded while the current one is applied),
 // then written as rows lambda_k u_k^T of A (pitch P) with sig[k] =
 // lambda_k, top[k] = k.  Ends with a barrier.
@@ -1141,21 +1223,46 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
   double y[EV];
 #pragma unroll
   for (int c = 0; c < EV; ++c) y[c] = 0.0;
-  // vector t of a batch goes to lane t % 4 of wave t / 4: the passes are
-  // serial recurrences, so four waves run four at a time each
-  const int tv = (tid / kWave) * 4 + (tid & (kWave - 1));
-  for (int b0 = 0; b0 < rj; b0 += 16) {
-    if ((tid & (kWave - 1)) < 4 && b0 + tv < rj) {
-      const double nrm = twisted_vector(de, es.e, m, es.lam[b0 + tv], zs + tv);
-      es.zn[tv] = rsqrt_nr(nrm);
-    }
+  // vector c of a batch of 8 belongs to wave c / 2: its top-down pass on
+  // lane 2 (c % 2), its bottom-up pass on the next lane (columns c and
+  // c + 8 of zs); the passes are serial recurrences, so each wave runs four
+  // at a time
+  const int wl = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int vec = 2 * wv + (wl >> 1);
+  const int dir = wl & 1;
+  for (int b0 = 0; b0 < rj; b0 += 8) {
+    const bool piv = wl < 4 && b0 + vec < rj;
+    if (piv) twisted_pivots(de, m, es.lam[b0 + vec], dir, zs + vec + 8 * dir);
+    // the pivots of this wave's vectors are read by the whole wave: LDS
+    // operations of a wave complete in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int tw[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (b0 + 2 * wv + j < rj)
+        tw[j] = twist_index(de, zs + 2 * wv + j, zs + 2 * wv + j + 8, m, es.lam[b0 + 2 * wv + j]);
+    if (wl < 2) es.tw[2 * wv + wl] = tw[wl];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (piv)
+      es.zn[2 * vec + dir] =
+          twisted_solve(es.e, m, (wl >> 1) ? tw[1] : tw[0], dir, zs + vec + 8 * dir);
     __syncthreads();
-    if (kk >= b0 && kk < b0 + 16 && kk < rj) {
-      const double f = es.zn[kk - b0];
+    if (kk >= b0 && kk < b0 + 8 && kk < rj) {
+      const int c0 = kk - b0;
+      const int t = es.tw[c0];
+      const double f = rsqrt_nr(es.zn[2 * c0 + 1] + es.zn[2 * c0]);
 #pragma unroll
       for (int c = 0; c < EV; ++c) {
         const int i = l + V * c;
-        if (i < m) y[c] = zs[16 * i + (kk - b0)] * f;
+        if (i < m) {
+          const double za = zs[16 * i + c0], zb = zs[16 * i + c0 + 8];
+          y[c] = (i < t ? za : (i > t ? zb : 1.0)) * f;
+        }
       }
     }
     __syncthreads();
@@ -1286,12 +1393,13 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
       if (rows_form) {
         gram_accumulate<B, true>(x_pre, xp, m, d, g);
         __syncthreads();  // X is read before G takes its place
+        gram_store<B, true>(g, m, Lg, work, Pg);
       } else {
         for_blocks(x_pre, [&](const float* xr, int, int rb) {
           gram_accumulate<B, false>(xr, xp, m, rb, g);
         });
+        gram_store<B, false>(g, m, Lg, work, Pg);
       }
-      gram_store<B>(g, m, Lg, work, Pg);
     };
     if (m > 64)
       run(std::integral_constant<int, 8>());
@@ -1310,13 +1418,13 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
     const int Pt = m + 1 + (m & 1);  // odd pitch: a wave's rows fall in distinct banks
     gram(m, Pt);
     if (m > 64)
-      tridiagonalize<2, 64>(work, m, Pt, es);
+      tridiagonalize<8, 4, 16, true>(work, m, Pt, es);
     else if (m > 32)
-      tridiagonalize<4, 16>(work, m, Pt, es);
+      tridiagonalize<4, 1, 16, false>(work, m, Pt, es);
     else if (m > 16)
-      tridiagonalize<8, 4>(work, m, Pt, es);
+      tridiagonalize<8, 1, 4, false>(work, m, Pt, es);
     else
-      tridiagonalize<16, 1>(work, m, Pt, es);
+      tridiagonalize<16, 1, 1, false>(work, m, Pt, es);
     const int nev = min(rmax + 1, m);
     double2* de = reinterpret_cast<double2*>(part);  // free after the summary
     top_eigenvalues(m, nev, es, de);
@@ -1351,19 +1459,53 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
       const double lam = sh.sig[sh.top[k]];
       a_store(t, k, lam > 0.0 ? work[sh.top[k] * P + t] / sqrt(lam) : 0.0);
     }
-    // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3; thread -> kOut outputs
+    // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3: thread -> outputs
+    // o = tid + q T (k = o / d, e = o % d), q < nq; the outputs advance
+    // through the rows together, four chains of four rows at a time, so
+    // that 32 loads are in flight per round trip (indices past the last
+    // output are clamped and their sums dropped)
     constexpr int kOut = 32 * 128 / kCloseThreads;
+    const int nq = __builtin_amdgcn_readfirstlane((rj * d + kCloseThreads - 1) / kCloseThreads);
+    const int last = rj * d > 0 ? rj * d - 1 : 0;
+    int eo[kOut], uo[kOut];
+#pragma unroll
+    for (int q = 0; q < kOut; ++q) {
+      const int o = min(tid + q * kCloseThreads, last);
+      const int k = o / d;
+      eo[q] = o - k * d;
+      uo[q] = sh.top[k] * P;
+    }
     double wacc[kOut] = {};
     for_blocks(x_post, [&](const float* xr, int t0, int rb) {
+      const double* ub = work + t0;
+      int t = 0;
+      for (; t + 4 <= rb; t += 4) {
 #pragma unroll
-      for (int q = 0; q < kOut; ++q) {
-        const int o = tid + q * kCloseThreads;
-        if (o < rj * d) {
-          const int k = o / d;
-          const int e = o - k * d;
-          const double* uk = work + sh.top[k] * P + t0;
-          for (int t = 0; t < rb; ++t)
-            wacc[q] = fma(static_cast<double>(xr[t * xp + e]), uk[t], wacc[q]);
+        for (int q0 = 0; q0 < kOut; q0 += 4) {
+          if (q0 >= nq) break;
+          float xv[4][4];
+          double uv[4][4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              xv[q][i] = xr[(t + i) * xp + eo[q0 + q]];
+              uv[q][i] = ub[uo[q0 + q] + t + i];
+            }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              wacc[q0 + q] = fma(static_cast<double>(xv[q][i]), uv[q][i], wacc[q0 + q]);
+        }
+      }
+      for (; t < rb; ++t) {
+#pragma unroll
+        for (int q0 = 0; q0 < kOut; q0 += 4) {
+          if (q0 >= nq) break;
+#pragma unroll
+          for (int q = q0; q < q0 + 4; ++q)
+            wacc[q] = fma(static_cast<double>(xr[t * xp + eo[q]]), ub[uo[q] + t], wacc[q]);
         }
       }
     });
@@ -1384,19 +1526,22 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
       const double lam = sh.sig[sh.top[k]];
       w_store(k, e, lam > 0.0 ? work[sh.top[k] * P + e] / lam : 0.0);
     }
-    // A[t][k] = X[t] . w_k
+    // A[t][k] = X[t] . w_k, as four interleaved partial sums (d % 4 == 0)
     for_blocks(x_post, [&](const float* xr, int t0, int rb) {
       for (int o = tid; o < rb * rj; o += kCloseThreads) {
         const int t = o / rj;
         const int k = o - t * rj;
         const double lam = sh.sig[sh.top[k]];
-        double s = 0.0;
-        if (lam > 0.0) {
-          const double* wk = work + sh.top[k] * P;
-          for (int e = 0; e < d; ++e) s = fma(static_cast<double>(xr[t * xp + e]), wk[e], s);
-          s /= lam;
+        const double* wk = work + sh.top[k] * P;
+        const float* xt = xr + t * xp;
+        double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+        for (int e = 0; e < d; e += 4) {
+          s0 = fma(static_cast<double>(xt[e]), wk[e], s0);
+          s1 = fma(static_cast<double>(xt[e + 1]), wk[e + 1], s1);
+          s2 = fma(static_cast<double>(xt[e + 2]), wk[e + 2], s2);
+          s3 = fma(static_cast<double>(xt[e + 3]), wk[e + 3], s3);
         }
-        a_store(t0 + t, k, s);
+        a_store(t0 + t, k, lam > 0.0 ? ((s0 + s1) + (s2 + s3)) / lam : 0.0);
       }
     });
   }
