@@ -523,111 +523,6 @@ __device__ __forceinline__ void for_row_vectors(bool vtile, int lo, int hi, int 
   }
 }
 
-// G[a][b] (a, b < m, pitch P) += sum over q < len of Y(q, a) Y(q, b) for
-// an LDS matrix of floats, in fp64 and in order of q; thread (ta, tb) ->
-// the B x B entries of G at a = gram_index(ta, i), b = gram_index(tb, k)
-// (accumulated in registers g).  The indices of a thread are strided by nb
-// (the number of thread rows), so that the 16 lanes of a wave that differ in
-// tb read 16 neighbouring rows (or 16 neighbouring 4-column groups), which
-// fall in distinct LDS banks.  kByRow: Y(q, i) = y[i * ys + q] (X rows, ys
-// the row pitch; len and ys multiples of 4, so four values of q come as
-// one 16-byte vector); otherwise Y(q, i) = y[q * ys + i] (for B >= 4 a
-// thread's indices come in groups of four contiguous ones, read as
-// vectors).
-template <int B, bool kByRow>
-__device__ __forceinline__ int gram_index(int t, int i, int nb) {
-  if constexpr (kByRow || B % 4 != 0)
-    return t + nb * i;
-  else
-    return 4 * (t + nb * (i / 4)) + (i & 3);
-}
-
-template <int B, bool kByRow>
-__device__ __forceinline__ void gram_accumulate(const float* y, int ys, int m, int len,
-                                                double (&g)[B][B]) {
-  const int tid = threadIdx.x;
-  const int nb = (m + B - 1) / B;
-  if (tid >= nb * nb) return;
-  const int ta = tid / nb, tb = tid - ta * nb;
-  if constexpr (kByRow) {
-    for (int q = 0; q < len; q += 4) {
-      float4 va[B], vb[B];
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const int a = gram_index<B, kByRow>(ta, i, nb), b = gram_index<B, kByRow>(tb, i, nb);
-        va[i] = a < m ? *reinterpret_cast<const float4*>(y + a * ys + q)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-        vb[i] = b < m ? *reinterpret_cast<const float4*>(y + b * ys + q)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < B; ++i)
-#pragma unroll
-        for (int k = 0; k < B; ++k) {
-          double acc = g[i][k];
-          acc = fma(static_cast<double>(va[i].x), static_cast<double>(vb[k].x), acc);
-          acc = fma(static_cast<double>(va[i].y), static_cast<double>(vb[k].y), acc);
-          acc = fma(static_cast<double>(va[i].z), static_cast<double>(vb[k].z), acc);
-          g[i][k] = fma(static_cast<double>(va[i].w), static_cast<double>(vb[k].w), acc);
-        }
-    }
-  } else {
-    // a thread's last index is below m exactly when all of them are (the
-    // indices grow with i)
-    const bool full = gram_index<B, kByRow>(ta, B - 1, nb) < m &&
-                      gram_index<B, kByRow>(tb, B - 1, nb) < m;
-#pragma unroll 4
-    for (int q = 0; q < len; ++q) {
-      double ya[B], yb[B];
-      if (B % 4 == 0 && full) {
-#pragma unroll
-        for (int i = 0; i < B; i += 4) {
-          const float4 wa =
-              *reinterpret_cast<const float4*>(y + q * ys + gram_index<B, kByRow>(ta, i, nb));
-          const float4 wb =
-              *reinterpret_cast<const float4*>(y + q * ys + gram_index<B, kByRow>(tb, i, nb));
-          ya[i] = wa.x; ya[i + 1] = wa.y; ya[i + 2] = wa.z; ya[i + 3] = wa.w;
-          yb[i] = wb.x; yb[i + 1] = wb.y; yb[i + 2] = wb.z; yb[i + 3] = wb.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-          const int a = gram_index<B, kByRow>(ta, i, nb), b = gram_index<B, kByRow>(tb, i, nb);
-          ya[i] = a < m ? static_cast<double>(y[q * ys + a]) : 0.0;
-          yb[i] = b < m ? static_cast<double>(y[q * ys + b]) : 0.0;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < B; ++i)
-#pragma unroll
-        for (int k = 0; k < B; ++k) g[i][k] = fma(ya[i], yb[k], g[i][k]);
-    }
-  }
-}
-
-// Writes the thread's entries of G (indices as gram_accumulate) and zeroes
-// columns m..Lp-1.  Ends with a barrier.
-template <int B, bool kByRow>
-__device__ __forceinline__ void gram_store(const double (&g)[B][B], int m, int Lp, double* G,
-                                           int P) {
-  const int tid = threadIdx.x;
-  const int nb = (m + B - 1) / B;
-  if (tid < nb * nb) {
-    const int ta = tid / nb, tb = tid - ta * nb;
-#pragma unroll
-    for (int i = 0; i < B; ++i)
-#pragma unroll
-      for (int k = 0; k < B; ++k) {
-        const int a = gram_index<B, kByRow>(ta, i, nb), b = gram_index<B, kByRow>(tb, k, nb);
-        if (a < m && b < m) G[a * P + b] = g[i][k];
-      }
-  }
-  for (int idx = tid; idx < m * (Lp - m); idx += kCloseThreads) {
-    const int a = idx / (Lp - m);
-    G[a * P + m + (idx - a * (Lp - m))] = 0.0;
-  }
-  __syncthreads();
-}
 
 // ---- top eigenpairs of the Gram matrix (closing path)
 //
@@ -716,6 +611,190 @@ __device__ __forceinline__ double keep(double x) {
 
 typedef __attribute__((address_space(3))) double lds_f64;
 typedef __attribute__((address_space(3))) EigShared lds_eig;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// G[a][b] (a, b < m <= 128, pitch P) = sum over q of Y(q, a) Y(q, b), in
+// fp64 on 16 x 16 x 4 matrix-core products.  The 16 x 16 tiles (ta, tb) of
+// G with ta <= tb are dealt to the four waves in turn (at most kT each; G
+// is symmetric, a tile off the diagonal is stored twice), and a wave
+// advances all of its tiles through the rows q of Y four at a time.  A wave
+// always runs kT tiles, so that the loads of all of them are issued
+// together; the ones past the last tile repeat tile (0, 0) and are not
+// stored.  Operands of lane l for rows q0 .. q0 + 3: A[i][k] = Y(q0 + l /
+// 16, 16 ta + l % 16) and B[k][j] = Y(q0 + l / 16, 16 tb + l % 16); lane l
+// holds D[l / 16 + 4 e][l % 16] of the product.  kByRow: Y(q, i) = y[i ys
+// + q] (X rows: G = X X^T); otherwise Y(q, i) = y[q ys + i] (G = X^T X).
+// Indices a >= m and rows q >= len read 0.
+template <int kT>
+struct GramTiles {
+  f64x4 acc[kT];
+  int ta[kT], tb[kT];
+  int nt, ntiles, wv;
+
+  __device__ __forceinline__ void init(int m) {
+    nt = (m + 15) / 16;
+    ntiles = nt * (nt + 1) / 2;
+    wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      int r = wv + 4 * i, a = 0;  // upper-triangle tile r, row by row
+      if (r >= ntiles) r = 0;
+      while (a < nt && r >= nt - a) {
+        r -= nt - a;
+        ++a;
+      }
+      ta[i] = a;
+      tb[i] = a + r;
+    }
+  }
+
+  // partial sums of earlier blocks (upper tiles as store() left them), or 0
+  __device__ __forceinline__ void load(bool zero, int m, const lds_f64* G, int P) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      const int b = 16 * tb[i] + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * ta[i] + (lane >> 4) + 4 * e;
+        acc[i][e] = zero || a >= m || b >= m ? 0.0 : G[a * P + b];
+      }
+    }
+  }
+
+  template <bool kByRow>
+  __device__ __forceinline__ void accumulate(const lds_f32* y, int ys, int m, int len) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15, lk = lane >> 4;
+    for (int q0 = 0; q0 < len; q0 += 4) {
+      const int q = q0 + lk;
+      const int qc = min(q, len - 1);
+      double xa[kT], xb[kT];
+#pragma unroll
+      for (int i = 0; i < kT; ++i) {
+        const int a = 16 * ta[i] + li, b = 16 * tb[i] + li;  // < 128
+        const float fa = kByRow ? y[a * ys + q] : y[qc * ys + a];
+        const float fb = kByRow ? y[b * ys + q] : y[qc * ys + b];
+        const bool ok = kByRow || q < len;
+        xa[i] = ok && a < m ? static_cast<double>(fa) : 0.0;
+        xb[i] = ok && b < m ? static_cast<double>(fb) : 0.0;
+      }
+#pragma unroll
+      for (int i = 0; i < kT; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[i], xb[i], acc[i], 0, 0, 0);
+    }
+  }
+
+  // upper tiles; with both, the mirror images of the tiles off the diagonal
+  __device__ __forceinline__ void store(bool both, int m, lds_f64* G, int P) const {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      if (wv + 4 * i >= ntiles) break;
+      const int b = 16 * tb[i] + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * ta[i] + (lane >> 4) + 4 * e;
+        if (a < m && b < m) {
+          G[a * P + b] = acc[i][e];
+          if (both && ta[i] != tb[i]) G[b * P + a] = acc[i][e];
+        }
+      }
+    }
+  }
+};
+
+// One block of rows of Y into G (GramTiles): `first` starts from zero,
+// otherwise from the upper tiles that the previous block stored; `last`
+// stores both triangles.  By rows, Y is X at the place of G, so the waves
+// meet at a barrier between the last read of X and the first store.  A
+// call of its own (its registers are not shared with the caller's).
+template <int kT, bool kByRow>
+__device__ __noinline__ void gram_block(const float* y_, int ys_, int m_, int len_, double* G_,
+                                        int P_, int first_, int last_) {
+  const int ys = __builtin_amdgcn_readfirstlane(ys_);
+  const int m = __builtin_amdgcn_readfirstlane(m_);
+  const int len = __builtin_amdgcn_readfirstlane(len_);
+  const int P = __builtin_amdgcn_readfirstlane(P_);
+  const bool first = __builtin_amdgcn_readfirstlane(first_) != 0;
+  const bool last = __builtin_amdgcn_readfirstlane(last_) != 0;
+  lds_f64* G = (lds_f64*)G_;
+  GramTiles<kT> gt;
+  gt.init(m);
+  gt.load(first, m, G, P);
+  gt.template accumulate<kByRow>((const lds_f32*)y_, ys, m, len);
+  if (kByRow) __syncthreads();
+  gt.store(last, m, G, P);
+}
+
+// S[k][e] = sum over t < n of X[t][e] R[k][t] (k < rj <= 32, e < d; X: n
+// rows of floats with pitch xp, R: rows of doubles with pitch P, S: pitch
+// d), in fp64 and in order of t.  Thread -> outputs o = tid + q T (k = o /
+// d, e = o % d) for q < nq: with d dividing T (d = 64 or 128) a thread's
+// outputs share the column e, so one load of X[t][e] serves them all; the
+// outputs advance through the rows together, four rows at a time (indices
+// past the last output are clamped and their sums dropped).  A call of its
+// own; ends with a barrier.
+__device__ __noinline__ void rows_product(const float* x_, int xp_, int n_, int d_, int rj_,
+                                          const double* r_, int P_, double* s_) {
+  constexpr int kOut = 32 * 128 / kCloseThreads;
+  const int xp = __builtin_amdgcn_readfirstlane(xp_);
+  const int n = __builtin_amdgcn_readfirstlane(n_);
+  const int d = __builtin_amdgcn_readfirstlane(d_);
+  const int rj = __builtin_amdgcn_readfirstlane(rj_);
+  const int P = __builtin_amdgcn_readfirstlane(P_);
+  const lds_f32* x = (const lds_f32*)x_;
+  const lds_f64* r = (const lds_f64*)r_;
+  lds_f64* s = (lds_f64*)s_;
+  const int tid = threadIdx.x;
+  const int tot = rj * d;
+  const int nq = (tot + kCloseThreads - 1) / kCloseThreads;
+  const int last = tot > 0 ? tot - 1 : 0;
+  const int e = tid % d;
+  int uo[kOut];
+  double acc[kOut];
+#pragma unroll
+  for (int q = 0; q < kOut; ++q) {
+    uo[q] = min(tid + q * kCloseThreads, last) / d * P;
+    acc[q] = 0.0;
+  }
+  int t = 0;
+  for (; t + 4 <= n; t += 4) {
+    double xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = static_cast<double>(x[(t + i) * xp + e]);
+#pragma unroll
+    for (int q0 = 0; q0 < kOut; q0 += 4) {
+      if (q0 >= nq) break;
+      double uv[4][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uv[q][i] = r[uo[q0 + q] + t + i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[q0 + q] = fma(xv[i], uv[q][i], acc[q0 + q]);
+    }
+  }
+  for (; t < n; ++t) {
+    const double xv = static_cast<double>(x[t * xp + e]);
+#pragma unroll
+    for (int q0 = 0; q0 < kOut; q0 += 4) {
+      if (q0 >= nq) break;
+#pragma unroll
+      for (int q = q0; q < q0 + 4; ++q) acc[q] = fma(xv, r[uo[q] + t], acc[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kOut; ++q) {
+    const int o = tid + q * kCloseThreads;
+    if (o < tot) s[o] = acc[q];
+  }
+  __syncthreads();
+}
+
 template <int L, int R, int C, bool kScalarLoop>
 __device__ __noinline__ void tridiagonalize(double* A_, int m_, int P_, EigShared& es_) {
   // arguments of a call arrive in vector registers; kScalarLoop makes them
@@ -756,6 +835,7 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m_, int P_, EigShare
     lds_f64* row = A + r * P;
     double xa = row[lane], xb = row[lane + kWave];
     const double al = row[r + 1];
+    const double dr = row[r];
     xa = keep(xa);
     xb = keep(xb);
     const bool ia = lane > r + 1 && lane < m, ib = lane + kWave > r + 1 && lane + kWave < m;
@@ -770,13 +850,16 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m_, int P_, EigShare
       scl = recip(al - beta);
     }
     lds_f64* vb = es->vb[r & 1];
-    vb[lane] = lane == r + 1 ? 1.0 : ya * scl;
-    vb[lane + kWave] = lane + kWave == r + 1 ? 1.0 : yb * scl;
-    if (ia) row[lane] = ya * scl;
-    if (ib) row[lane + kWave] = yb * scl;
+    const double va = lane == r + 1 ? 1.0 : ya * scl;
+    const double vc = lane + kWave == r + 1 ? 1.0 : yb * scl;
+    vb[lane] = va;
+    vb[lane + kWave] = vc;
+    // row r keeps v for the back-transform, with zeros left of v_{r+1}
+    // (entries past m - 1 stay as they are: no write leaves the row)
+    if (lane < m) row[lane] = va;
+    if (lane + kWave < m) row[lane + kWave] = vc;
     if (lane == 0) {
-      es->d[r] = row[r];
-      row[r + 1] = 1.0;
+      es->d[r] = dr;
       es->e[r] = beta;
       es->tau[r] = tau;
     }
@@ -1268,9 +1351,10 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
     __syncthreads();
   }
   // u = H_0 H_1 ... H_{m-3} z, the last reflector first
-  // row s of A holds reflector s scaled (v_{s+1} = 1); reads stay inside
-  // the work array for i < 128, and the entries outside s + 1 .. m - 1 are
-  // replaced by 0 when they are used (one step after they are loaded)
+  // row s of A holds reflector s scaled (v_{s+1} = 1), with zeros left of
+  // v_{s+1}; reads stay inside the work array for i < 128, and the entries
+  // past m - 1 (another row's, or never written) are replaced by 0 when
+  // they are used (one step after they are loaded)
   auto load_v = [&](int s, double (&x)[EV]) {
     const lds_f64* rs = (const lds_f64*)(A + s * P);
 #pragma unroll
@@ -1282,14 +1366,16 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
     tn = es.tau[m - 3];
     load_v(m - 3, vn);
   }
+  bool inm[EV];
+#pragma unroll
+  for (int c = 0; c < EV; ++c) inm[c] = l + V * c < m;
   for (int s = m - 3; s >= 0; --s) {
     double v[EV];
     const double ts = keep(tn);
 #pragma unroll
     for (int c = 0; c < EV; ++c) {
-      const int i = l + V * c;
       const double kx = keep(vn[c]);
-      v[c] = i > s && i < m ? kx : 0.0;
+      v[c] = inm[c] ? kx : 0.0;
     }
     if (s > 0) {
       tn = es.tau[s - 1];
@@ -1387,28 +1473,30 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
   // ---- Gram matrix and its r_j largest eigenpairs (sig = sigma^2): the
   // tridiagonal path, or Jacobi when the spectrum is clustered there
   auto gram = [&](int Lg, int Pg) {
-    auto run = [&](auto bsize) {
-      constexpr int B = decltype(bsize)::value;
-      double g[B][B] = {};
+    auto run = [&](auto tiles) {
+      constexpr int kT = decltype(tiles)::value;
       if (rows_form) {
-        gram_accumulate<B, true>(x_pre, xp, m, d, g);
-        __syncthreads();  // X is read before G takes its place
-        gram_store<B, true>(g, m, Lg, work, Pg);
+        gram_block<kT, true>(x_pre, xp, m, d, work, Pg, 1, 1);
       } else {
-        for_blocks(x_pre, [&](const float* xr, int, int rb) {
-          gram_accumulate<B, false>(xr, xp, m, rb, g);
+        for_blocks(x_pre, [&](const float* xr, int t0, int rb) {
+          gram_block<kT, false>(xr, xp, m, rb, work, Pg, t0 == 0, t0 + rb == n);
         });
-        gram_store<B, false>(g, m, Lg, work, Pg);
       }
     };
-    if (m > 64)
-      run(std::integral_constant<int, 8>());
+    // tiles per wave: ceil(nt (nt + 1) / 8) for nt = ceil(m / 16) tiles a side
+    if (m > 96)
+      run(std::integral_constant<int, 9>());
+    else if (m > 64)
+      run(std::integral_constant<int, 6>());
     else if (m > 32)
-      run(std::integral_constant<int, 4>());
-    else if (m > 16)
-      run(std::integral_constant<int, 2>());
+      run(std::integral_constant<int, 3>());
     else
       run(std::integral_constant<int, 1>());
+    for (int idx = tid; idx < m * (Lg - m); idx += kCloseThreads) {  // Jacobi's padding
+      const int a = idx / (Lg - m);
+      work[a * Pg + m + (idx - a * (Lg - m))] = 0.0;
+    }
+    __syncthreads();
   };
   const int rmax = min(rank, m);
   int P = Pj;
@@ -1449,7 +1537,13 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
     jacobi_sweeps<kCloseThreads>(work, m, Lp, Pj, sh);
     rj = top_rows<kCloseThreads>(work, m, Lp, Pj, rank, sh);
   }
-  if (rows_form && x_post != nullptr) load_rows(0, n, x_post);
+  // rows form after the tridiagonal path: the rj eigenvector rows are rows
+  // 0 .. rj - 1 of work (top[k] = k); X goes back to LDS right after them
+  // and the products S = R X after X (rj P + n xp / 2 + rj d doubles fit:
+  // n <= d <= 128, P <= 130, rj <= 32)
+  float* const x_out = rows_form && tri ? reinterpret_cast<float*>(work + rj * P) : x_post;
+  double* const s_out = rows_form && tri ? work + rj * P + (n * xp + 1) / 2 : nullptr;
+  if (rows_form && x_out != nullptr) load_rows(0, n, x_out);
 
   if (rows_form) {
     // A[t][k] = sigma_k u_k[t] = row_k[t] / sigma_k
@@ -1459,63 +1553,73 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
       const double lam = sh.sig[sh.top[k]];
       a_store(t, k, lam > 0.0 ? work[sh.top[k] * P + t] / sqrt(lam) : 0.0);
     }
-    // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3: thread -> outputs
-    // o = tid + q T (k = o / d, e = o % d), q < nq; the outputs advance
-    // through the rows together, four chains of four rows at a time, so
-    // that 32 loads are in flight per round trip (indices past the last
-    // output are clamped and their sums dropped)
-    constexpr int kOut = 32 * 128 / kCloseThreads;
-    const int nq = __builtin_amdgcn_readfirstlane((rj * d + kCloseThreads - 1) / kCloseThreads);
-    const int last = rj * d > 0 ? rj * d - 1 : 0;
-    int eo[kOut], uo[kOut];
-#pragma unroll
-    for (int q = 0; q < kOut; ++q) {
-      const int o = min(tid + q * kCloseThreads, last);
-      const int k = o / d;
-      eo[q] = o - k * d;
-      uo[q] = sh.top[k] * P;
-    }
-    double wacc[kOut] = {};
-    for_blocks(x_post, [&](const float* xr, int t0, int rb) {
-      const double* ub = work + t0;
-      int t = 0;
-      for (; t + 4 <= rb; t += 4) {
-#pragma unroll
-        for (int q0 = 0; q0 < kOut; q0 += 4) {
-          if (q0 >= nq) break;
-          float xv[4][4];
-          double uv[4][4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              xv[q][i] = xr[(t + i) * xp + eo[q0 + q]];
-              uv[q][i] = ub[uo[q0 + q] + t + i];
-            }
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              wacc[q0 + q] = fma(static_cast<double>(xv[q][i]), uv[q][i], wacc[q0 + q]);
-        }
-      }
-      for (; t < rb; ++t) {
-#pragma unroll
-        for (int q0 = 0; q0 < kOut; q0 += 4) {
-          if (q0 >= nq) break;
-#pragma unroll
-          for (int q = q0; q < q0 + 4; ++q)
-            wacc[q] = fma(static_cast<double>(xr[t * xp + eo[q]]), ub[uo[q] + t], wacc[q]);
-        }
-      }
-    });
-#pragma unroll
-    for (int q = 0; q < kOut; ++q) {
-      const int o = tid + q * kCloseThreads;
-      if (o < rj * d) {
+    if (s_out != nullptr) {
+      // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3
+      rows_product(x_out, xp, n, d, rj, work, P, s_out);
+      for (int o = tid; o < rj * d; o += kCloseThreads) {
         const int k = o / d;
-        const double lam = sh.sig[sh.top[k]];
-        w_store(k, o - k * d, lam > 0.0 ? wacc[q] / (lam * sqrt(lam)) : 0.0);
+        const double lam = sh.sig[k];
+        w_store(k, o - k * d, lam > 0.0 ? s_out[o] / (lam * sqrt(lam)) : 0.0);
+      }
+    } else {
+      // W[k][e] = sum_t X[t][e] row_k[t] / sigma_k^3: thread -> outputs
+      // o = tid + q T (k = o / d, e = o % d), q < nq; the outputs advance
+      // through the rows together, four chains of four rows at a time, so
+      // that 32 loads are in flight per round trip (indices past the last
+      // output are clamped and their sums dropped)
+      constexpr int kOut = 32 * 128 / kCloseThreads;
+      const int nq = __builtin_amdgcn_readfirstlane((rj * d + kCloseThreads - 1) / kCloseThreads);
+      const int last = rj * d > 0 ? rj * d - 1 : 0;
+      int eo[kOut], uo[kOut];
+#pragma unroll
+      for (int q = 0; q < kOut; ++q) {
+        const int o = min(tid + q * kCloseThreads, last);
+        const int k = o / d;
+        eo[q] = o - k * d;
+        uo[q] = sh.top[k] * P;
+      }
+      double wacc[kOut] = {};
+      for_blocks(x_post, [&](const float* xr, int t0, int rb) {
+        const double* ub = work + t0;
+        int t = 0;
+        for (; t + 4 <= rb; t += 4) {
+#pragma unroll
+          for (int q0 = 0; q0 < kOut; q0 += 4) {
+            if (q0 >= nq) break;
+            float xv[4][4];
+            double uv[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                xv[q][i] = xr[(t + i) * xp + eo[q0 + q]];
+                uv[q][i] = ub[uo[q0 + q] + t + i];
+              }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                wacc[q0 + q] = fma(static_cast<double>(xv[q][i]), uv[q][i], wacc[q0 + q]);
+          }
+        }
+        for (; t < rb; ++t) {
+#pragma unroll
+          for (int q0 = 0; q0 < kOut; q0 += 4) {
+            if (q0 >= nq) break;
+#pragma unroll
+            for (int q = q0; q < q0 + 4; ++q)
+              wacc[q] = fma(static_cast<double>(xr[t * xp + eo[q]]), ub[uo[q] + t], wacc[q]);
+          }
+        }
+      });
+#pragma unroll
+      for (int q = 0; q < kOut; ++q) {
+        const int o = tid + q * kCloseThreads;
+        if (o < rj * d) {
+          const int k = o / d;
+          const double lam = sh.sig[sh.top[k]];
+          w_store(k, o - k * d, lam > 0.0 ? wacc[q] / (lam * sqrt(lam)) : 0.0);
+        }
       }
     }
   } else {
