@@ -1198,8 +1198,7 @@ __device__ __forceinline__ Pair pair_at(const lds_f64* de, int i) {
 // Eigenvectors of the scaled tridiagonal T (de[i] = (d_i, e_{i-1}^2), e)
 // by twisted factorisations of T - lam I.  The top-down pivots D+_i =
 // P_{i+1} / P_i and the bottom-up pivots D-_i = Q_i / Q_{i+1} are ratios of
-// the leading and trailing minors (three-term recurrences, so the serial
-// dependence is one multiply-add per step); gamma_i = D+_i + D-_i - (d_i -
+// the leading and trailing minors; gamma_i = D+_i + D-_i - (d_i -
 // lam), and at the twist t = argmin |gamma_i| the vector is z_t = 1, z_i =
 // -(e_i / D+_i) z_{i+1} above t and z_i = -(e_{i-1} / D-_i) z_{i-1} below.
 // The two directions of a vector run on two lanes of one wave in lockstep
@@ -1207,7 +1206,12 @@ __device__ __forceinline__ Pair pair_at(const lds_f64* de, int i) {
 // (stride 16 doubles): twisted_pivots, then twist_index by the whole wave,
 // then twisted_solve, which overwrites the pivots it has used with z.
 
-// dir 0: D+_i at row s of step s; dir 1: D-_i at row m - 1 - s.
+// dir 0: D+_i at row s of step s; dir 1: D-_i at row m - 1 - s, by the
+// pivot recurrences D+_i = (d_i - lam) - e_{i-1}^2 / D+_{i-1} and D-_i =
+// (d_i - lam) - e_i^2 / D-_{i+1} (the ratios of successive minors; a pivot
+// is kept away from zero and infinity before it is divided by).  The pass
+// is bound by its instruction count, not by the dependence through the
+// reciprocal.
 __device__ void twisted_pivots(const double2* de_, int m, double lam, int dir, double* z_) {
   // LDS views; de has m + 4 readable pairs.  The operands of the next two
   // steps are loaded ahead of the current one.
@@ -1221,20 +1225,16 @@ __device__ void twisted_pivots(const double2* de_, int m, double lam, int dir, d
     return Pair{de[2 * i], de[2 * (i + dir) + 1]};
   };
   const int i0 = row(0);
-  double pa = 1.0, pb = de[2 * i0] - lam;
-  z[16 * i0] = guard_pivot(pb);
+  double D = guard_pivot(de[2 * i0] - lam);
+  z[16 * i0] = D;
   Pair q1 = ld(1), q2 = ld(2);
 #pragma unroll 4
   for (int s = 1; s < m; ++s) {
     const Pair q = q1;
     q1 = q2;
     q2 = ld(s + 2);
-    const double rb = recip(pb);
-    const double pc = fma(q.x - lam, pb, -q.y * pa);
-    z[16 * row(s)] = guard_pivot(pc * rb);
-    pa = pb;
-    pb = pc;
-    if ((s & 3) == 0) rescale2(pa, pb);  // powers of two: the ratios are unchanged
+    D = guard_pivot(fma(-q.y, recip(D), q.x - lam));
+    z[16 * row(s)] = D;
   }
 }
 
