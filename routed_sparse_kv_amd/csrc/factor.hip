@@ -1522,10 +1522,25 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
         tri = false;
     if (tri) {
       double* zs = reinterpret_cast<double*>(stage);
-      if (rmax <= 16)
-        top_eigenvectors<16, 8>(work, m, Pt, rmax, es, de, zs, sh);
-      else
-        top_eigenvectors<8, 16>(work, m, Pt, rmax, es, de, zs, sh);
+      // groups of V lanes per vector, EV >= m / V entries per lane (the
+      // back-transform's steps cost about EV instructions each)
+      if (rmax <= 16) {
+        if (m > 64)
+          top_eigenvectors<16, 8>(work, m, Pt, rmax, es, de, zs, sh);
+        else if (m > 32)
+          top_eigenvectors<16, 4>(work, m, Pt, rmax, es, de, zs, sh);
+        else if (m > 16)
+          top_eigenvectors<16, 2>(work, m, Pt, rmax, es, de, zs, sh);
+        else
+          top_eigenvectors<16, 1>(work, m, Pt, rmax, es, de, zs, sh);
+      } else {
+        if (m > 64)
+          top_eigenvectors<8, 16>(work, m, Pt, rmax, es, de, zs, sh);
+        else if (m > 32)
+          top_eigenvectors<8, 8>(work, m, Pt, rmax, es, de, zs, sh);
+        else
+          top_eigenvectors<8, 4>(work, m, Pt, rmax, es, de, zs, sh);
+      }
       P = Pt;
       rj = rmax;
     } else if (rows_form) {
