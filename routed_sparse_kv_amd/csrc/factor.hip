@@ -1726,11 +1726,31 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
       const int gi = tid / d;
       const int c = tid - gi * d;
       const float* hr = h_full + static_cast<size_t>(b) * F + r0;
+      // the weights (surprisal for K, 1 for V) of up to 256 rows at a time
+      // go to LDS first (es.tau is free until the reduction), so that the
+      // sum's loads are LDS loads, four rows' issued together
+      float* wbuf = reinterpret_cast<float*>(es.tau);
       double acc = 0.0;
       for_blocks(x_pre, [&](const float* xr, int t0, int rb) {
-        for (int t = gi; t < rb; t += ng)
-          acc += kv ? static_cast<double>(xr[t * xp + c])
-                    : static_cast<double>(hr[t0 + t]) * static_cast<double>(xr[t * xp + c]);
+        for (int c0 = 0; c0 < rb; c0 += 256) {
+          const int cn = min(256, rb - c0);
+          __syncthreads();  // the previous chunk's weights are read
+          if (tid < cn) wbuf[tid] = kv ? 1.0f : hr[t0 + c0 + tid];
+          __syncthreads();
+          const float* xc = xr + c0 * xp + c;
+          int t = gi;
+          for (; t + 3 * ng < cn; t += 4 * ng) {
+            float w[4], x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              w[i] = wbuf[t + i * ng];
+              x[i] = xc[(t + i * ng) * xp];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc += static_cast<double>(w[i]) * static_cast<double>(x[i]);
+          }
+          for (; t < cn; t += ng) acc += static_cast<double>(wbuf[t]) * static_cast<double>(xc[t * xp]);
+        }
       });
       part[gi * d + c] = acc;
       __syncthreads();
