@@ -1111,18 +1111,41 @@ __device__ __forceinline__ void top_eigenvalues(int m, int nev, EigShared& es, d
     }
   }
   __syncthreads();
+  constexpr double kEps = 2.220446049250313e-16;
+  double lo0 = es.lim[0], hi0 = es.lim[1];
+  {
+    const double pad = 4.0 * kEps * fmax(fabs(lo0), fabs(hi0)) + 4.0 * kEps;
+    lo0 -= pad;
+    hi0 += pad;
+  }
+  // one round with every lane first: the counts at 256 evenly spaced
+  // points x_c = lo0 + (c + 1) w0 (x_255 = hi0) bracket every eigenvalue to
+  // a 256th of the interval (es.p is free once T is formed)
+  const double w0 = (hi0 - lo0) / static_cast<double>(kCloseThreads);
+  int* cnt0 = reinterpret_cast<int*>(es.p);
+  {
+    double step;
+    const double x = tid == kCloseThreads - 1 ? hi0 : fma(w0, static_cast<double>(tid + 1), lo0);
+    cnt0[tid] = sturm_newton(de, m, x, step);
+  }
+  __syncthreads();
   int g = kWave;
   while (g > 1 && g * nev > kCloseThreads) g >>= 1;
   const int kk = tid / g;
   const int l = tid - kk * g;
   if (kk < nev) {
     const int idx = m - 1 - kk;  // ascending index of the kk-th largest
-    constexpr double kEps = 2.220446049250313e-16;
-    double lo = es.lim[0], hi = es.lim[1];
-    const double pad = 4.0 * kEps * fmax(fabs(lo), fabs(hi)) + 4.0 * kEps;
-    lo -= pad;
-    hi += pad;
-    int clo = 0, chi = m;  // eigenvalues below lo and below hi
+    // the first point whose count exceeds idx (x_255 = hi0 counts all m):
+    // the bracket (x_{jp-1}, x_jp] holds eigenvalue idx with its counts
+    // certifying it, whether or not the rounded counts grow monotonically
+    int jp = kCloseThreads - 1;
+    for (int c = l; c < kCloseThreads; c += g)
+      if (cnt0[c] > idx) jp = min(jp, c);
+    for (int o = 1; o < g; o <<= 1) jp = min(jp, __shfl_xor(jp, o, kWave));
+    double lo = jp == 0 ? lo0 : fma(w0, static_cast<double>(jp), lo0);
+    double hi = jp == kCloseThreads - 1 ? hi0 : fma(w0, static_cast<double>(jp + 1), lo0);
+    int clo = jp == 0 ? 0 : cnt0[jp - 1];  // eigenvalues below lo and below hi
+    int chi = cnt0[jp];
     double xn = 0.5 * (lo + hi), lam = xn;
     const int base = lane & ~(g - 1);
     bool done = false;
