@@ -228,19 +228,22 @@ def _run_patterns(runs_per_seq):
 
 
 # Closed runs across the closing kernel's forms: the Gram matrix is X X^T
-# (n x n) up to n = d rows and X^T X (d x d) beyond.
+# (n x n) up to n = d rows and X^T X (d x d) beyond; ranks above 16 take
+# the eigenvector tiles of eight lanes per vector.
 LONG_RUNS = {
-    "bf16_d128": ("serving_b16_bf16", 2, [[128, 150], [64, 1, 2, 17, 100]]),
-    "f32_d64": ("tiny_fp32_2k", 1, [[64, 90, 5]]),
+    "bf16_d128": ("serving_b16_bf16", 2, [[128, 150], [64, 1, 2, 17, 100]], {}),
+    "f32_d64": ("tiny_fp32_2k", 1, [[64, 90, 5]], {}),
+    "bf16_d128_r32": ("serving_b16_bf16", 2, [[40, 128], [33, 70, 150]], {"rank": 32}),
+    "f32_d64_r24": ("tiny_fp32_2k", 1, [[48, 90, 20, 12]], {"rank": 24}),
 }
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("case", sorted(LONG_RUNS))
 def test_streaming_long_runs(case):
-    name, B, runs = LONG_RUNS[case]
+    name, B, runs, extra = LONG_RUNS[case]
     pats, steps = _run_patterns(runs)
-    over = dict(B=B, T=700, tail_capacity=steps + 8, steps=steps)
+    over = dict(B=B, T=700, tail_capacity=steps + 8, steps=steps, **extra)
     if name == "tiny_fp32_2k":
         over["append"] = True
     say(f"[stream long {case}] {steps} appends closing runs {runs}")
