@@ -1122,6 +1122,7 @@ __device__ __forceinline__ void top_eigenvalues(int m, int nev, EigShared& es, d
   // points x_c = lo0 + (c + 1) w0 (x_255 = hi0) bracket every eigenvalue to
   // a 256th of the interval (es.p is free once T is formed)
   const double w0 = (hi0 - lo0) / static_cast<double>(kCloseThreads);
+  static_assert(sizeof(es.p) >= kCloseThreads * sizeof(int), "one count per lane");
   int* cnt0 = reinterpret_cast<int*>(es.p);
   {
     double step;
@@ -1752,6 +1753,7 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
       // the weights (surprisal for K, 1 for V) of up to 256 rows at a time
       // go to LDS first (es.tau is free until the reduction), so that the
       // sum's loads are LDS loads, four rows' issued together
+      static_assert(sizeof(es.tau) >= 256 * sizeof(float), "weights of 256 rows");
       float* wbuf = reinterpret_cast<float*>(es.tau);
       double acc = 0.0;
       for_blocks(x_pre, [&](const float* xr, int t0, int rb) {
