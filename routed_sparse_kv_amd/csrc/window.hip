@@ -190,12 +190,13 @@ struct SoftState {
 #pragma unroll
     for (int x = 0; x < NG; ++x) amn[x] = 0.f;
   }
-  // s: the window's 64 base-2 logits of head n (16 per lane) -> probabilities
-  // relative to m.  On routing steps the window's own maximum and sum go to
-  // *ws (natural-log maximum).
+  // s: the window's 64 scores of head n (16 per lane), whose base-2 logits
+  // are s sl (sl > 0, applied inside the maximum and the exponentials) ->
+  // probabilities relative to m.  On routing steps the window's own maximum
+  // and sum go to *ws (natural-log maximum).
   template <bool MASS>
-  __device__ __forceinline__ void update(float (&s)[4][4], int nvalid, int g, bool store,
-                                         float2* ws) {
+  __device__ __forceinline__ void update(float (&s)[4][4], float sl, int nvalid, int g,
+                                         bool store, float2* ws) {
     if (nvalid < kRows) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
@@ -210,12 +211,13 @@ struct SoftState {
       for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[rb][i]);
     cm = fmaxf(cm, xor_lane<16>(cm));
     cm = fmaxf(cm, xor_lane<32>(cm));
+    cm *= sl;
     if (MASS) {
       float w = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w += __builtin_amdgcn_exp2f(s[rb][i] - cm);
+        for (int i = 0; i < 4; ++i) w += __builtin_amdgcn_exp2f(fmaf(s[rb][i], sl, -cm));
       w += xor_lane<16>(w);
       w += xor_lane<32>(w);
       if (store) *ws = make_float2(cm * kLn2, w);
@@ -238,7 +240,7 @@ struct SoftState {
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[rb][i] = __builtin_amdgcn_exp2f(s[rb][i] - m);
+        s[rb][i] = __builtin_amdgcn_exp2f(fmaf(s[rb][i], sl, -m));
         ps += s[rb][i];
       }
     ps += xor_lane<16>(ps);
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256) void attend_full_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[rb][i] = c[i] * sl;
     }
-    st.template update<MASS>(s, nvalid, g, g == 0 && n < G,
+    st.template update<MASS>(s, 1.f, nvalid, g, g == 0 && n < G,
                              wstat + (static_cast<size_t>(u) * nW + k) * G + n);
     // PV: A = values (column 16 cb + n, rows v32_row(g, .)), B = p (head n)
 #pragma unroll
@@ -443,30 +445,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     float s[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      float z[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x4 cg[NG];
+      float4 a4[NG], b4[NG];
 #pragma unroll
       for (int x = 0; x < NG; ++x) {
         // group x of rows 16 rb + 4 g + i: the two 32-column blocks of the
         // group, then [i][scale, min]
-        f32x4 cg = f32x4{0.f, 0.f, 0.f, 0.f};
+        cg[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
           const int kb = 2 * x + kh;
           const int o = rb * KB + kb;
           const int t = o >> 1;
-          cg = mma(decode8(kw[t >> 2][t & 3], o & 1), qo.qb[kb], cg);
+          cg[x] = mma(decode8(kw[t >> 2][t & 3], o & 1), qo.qb[kb], cg[x]);
         }
-        const float4 a4 = sq[((rb * 4 + g) * NG + x) * 2];
-        const float4 b4 = sq[((rb * 4 + g) * NG + x) * 2 + 1];
-        z[0] += a4.x * cg[0] + a4.y * qo.qsum[x];
-        z[1] += a4.z * cg[1] + a4.w * qo.qsum[x];
-        z[2] += b4.x * cg[2] + b4.y * qo.qsum[x];
-        z[3] += b4.z * cg[3] + b4.w * qo.qsum[x];
+        a4[x] = sq[((rb * 4 + g) * NG + x) * 2];
+        b4[x] = sq[((rb * 4 + g) * NG + x) * 2 + 1];
+      }
+      // the minimum terms first, then one multiply-add per group for the
+      // scaled code products
+      float z[4] = {a4[0].y * qo.qsum[0], a4[0].w * qo.qsum[0], b4[0].y * qo.qsum[0],
+                    b4[0].w * qo.qsum[0]};
+#pragma unroll
+      for (int x = 1; x < NG; ++x) {
+        z[0] = fmaf(a4[x].y, qo.qsum[x], z[0]);
+        z[1] = fmaf(a4[x].w, qo.qsum[x], z[1]);
+        z[2] = fmaf(b4[x].y, qo.qsum[x], z[2]);
+        z[3] = fmaf(b4[x].w, qo.qsum[x], z[3]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[rb][i] = z[i] * sl;
+      for (int x = 0; x < NG; ++x) {
+        z[0] = fmaf(a4[x].x, cg[x][0], z[0]);
+        z[1] = fmaf(a4[x].z, cg[x][1], z[1]);
+        z[2] = fmaf(b4[x].x, cg[x][2], z[2]);
+        z[3] = fmaf(b4[x].z, cg[x][3], z[3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[rb][i] = z[i];
     }
-    st.template update<MASS>(s, nvalid, g, g == 0 && n < G,
+    st.template update<MASS>(s, sl, nvalid, g, g == 0 && n < G,
                              wstat + (static_cast<size_t>(u) * nW + k) * G + n);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
