@@ -584,12 +584,14 @@ __device__ __forceinline__ double wave_sum_dpp(double a) {
 // Householder reduction of the symmetric m x m matrix A (m <= 128, both
 // triangles stored in LDS with pitch P) to tridiagonal form: reflector k,
 // H_k = I - tau_k v v^T with v_{k+1} = 1, zeroes row and column k beyond
-// the first off-diagonal entry.  The matrix lives in registers: row i
-// belongs to the L lanes tid / L = i, lane h holding columns h + L c
-// (c < C).  Once row k + 1 is final its lanes copy it to LDS, and one wave
-// forms reflector k + 1 from the copy (two entries per lane, one wave sum
-// for the norm): v scaled, zero outside k + 2 .. m - 1, goes to vb (double
-// buffered) and back into row k + 1 of A (kept for the back-transform).
+// the first off-diagonal entry.  The matrix lives in registers: the lanes
+// form groups of L (group g = tid / L, lane h = tid % L), and lane h of
+// group g holds rows g + (T / L) r (r < R) at columns h + L c (c < C), so
+// that one LDS read of v_j or p_j serves R rows.  Once row k + 1 is final
+// its lanes copy it to LDS, and one wave forms reflector k + 1 from the
+// copy (two entries per lane, one wave sum for the norm): v scaled, zero
+// outside k + 2 .. m - 1, goes to vb (double buffered) and back into row
+// k + 1 of A (kept for the back-transform, with zeros left of v_{k+2}).
 // Each step is then
 //   p = tau A v (one multiply-add per entry, a DPP sum per row; p = 0 on
 //   the rows outside the trailing block), barrier,
@@ -597,8 +599,8 @@ __device__ __forceinline__ double wave_sum_dpp(double a) {
 //   a_ij -= v_i p_j + (p_i - tau (p.v) v_i) v_j (two multiply-adds per
 //   entry; v and p vanish outside the trailing block, so no entry needs a
 //   branch), the next reflector, barrier.
-// Column blocks of 8 left of the trailing block are skipped.  d, e receive
-// T; tau the reflectors.  Ends with a barrier.
+// Column blocks and row slots left of / above the trailing block are
+// skipped.  d, e receive T; tau the reflectors.  Ends with a barrier.
 // A loaded value marked as used unconditionally (an empty asm statement
 // that takes and returns it in a register): a load whose result is then
 // selected against a constant stays one unconditional load, issued with
@@ -1233,9 +1235,9 @@ __device__ __forceinline__ Pair pair_at(const lds_f64* de, int i) {
 // dir 0: D+_i at row s of step s; dir 1: D-_i at row m - 1 - s, by the
 // pivot recurrences D+_i = (d_i - lam) - e_{i-1}^2 / D+_{i-1} and D-_i =
 // (d_i - lam) - e_i^2 / D-_{i+1} (the ratios of successive minors; a pivot
-// is kept away from zero and infinity before it is divided by).  The pass
-// is bound by its instruction count, not by the dependence through the
-// reciprocal.
+// is kept away from zero and infinity before it is divided by); fewer
+// instructions per step than the minors' own recurrence with rescaling,
+// and measured faster.
 __device__ void twisted_pivots(const double2* de_, int m, double lam, int dir, double* z_) {
   // LDS views; de has m + 4 readable pairs.  The operands of the next two
   // steps are loaded ahead of the current one.
