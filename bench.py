@@ -287,9 +287,14 @@ def close_latency(args):
     h_none = torch.zeros(B, dtype=torch.float32, device=dev)
     h_anchor = torch.full((B,), float(np.finfo(np.float32).max), dtype=torch.float32, device=dev)
 
-    def append(h):
+    def append(h, timed=False):
         k = torch.randn((B, Hkv, d), generator=gen, device=dev).to(tdt)
         v = torch.randn((B, Hkv, d), generator=gen, device=dev).to(tdt)
+        if timed:
+            # the new rows are made before the timed launches start, so that
+            # their events see only the closing and the append
+            torch.cuda.synchronize()
+            cache.profile_enable(True)
         rskv.append_token(cache, k, v, h)
 
     append(h_anchor)  # closes the prefill tail runs
@@ -299,9 +304,7 @@ def close_latency(args):
         for _ in range(reps):
             for _ in range(n):
                 append(h_none)
-            torch.cuda.synchronize()
-            cache.profile_enable(True)
-            append(h_anchor)
+            append(h_anchor, timed=True)
             p = cache.profile_read()
             cache.profile_enable(False)
             close_us.append(p["close_ms"] * 1e3)

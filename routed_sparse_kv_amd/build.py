@@ -33,6 +33,14 @@ def _flags():
             "-Wall", "-Wno-unused-result", "-I", os.path.join(HERE, "..", "include")]
 
 
+# Per-source flags.  factor.hip: its kernels call non-inlined phase functions,
+# so the compiler cannot rule out accumulation registers being needed and
+# picks the accumulation-register form of the fp64 MFMA, copying the Gram
+# tiles' accumulators there and back around every K step; the vector-register
+# form keeps them in place.
+EXTRA_FLAGS = {"factor.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link the shared library; return its path."""
     objdir = os.path.join(LIBDIR, "obj")
@@ -42,7 +50,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *_flags(), *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if verbose or r.returncode != 0:
             sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + _filter(r.stderr))

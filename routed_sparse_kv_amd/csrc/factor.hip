@@ -40,11 +40,13 @@ constexpr int kMaxSweeps = 40;
 constexpr double kEps = 2.220446049250313e-16;
 
 // One DPP lane exchange of a double (both halves with the same control).
+// bound_ctrl: a disabled source lane reads 0 and no old value has to be
+// set up first (two instructions fewer per exchange).
 template <int kCtrl>
 __device__ __forceinline__ double dpp_f64(double v) {
   const long long i = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(i), kCtrl, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(i >> 32), kCtrl, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(i), kCtrl, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(i >> 32), kCtrl, 0xf, 0xf, true);
   return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
 }
 
@@ -568,6 +570,24 @@ __device__ __forceinline__ double group_sum_dpp(double a) {
   return a;
 }
 
+// N such sums, step by step across the N values: the chains are
+// independent, so their DPP latencies overlap (one sum after another would
+// wait out each chain in turn).
+template <int V, int N>
+__device__ __forceinline__ void group_sums_dpp(double (&a)[N]) {
+  auto step = [&](auto ctrl) {
+    double t[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) t[q] = dpp_f64<decltype(ctrl)::value>(a[q]);
+#pragma unroll
+    for (int q = 0; q < N; ++q) a[q] += t[q];
+  };
+  if constexpr (V >= 2) step(std::integral_constant<int, 0xb1>{});
+  if constexpr (V >= 4) step(std::integral_constant<int, 0x4e>{});
+  if constexpr (V >= 8) step(std::integral_constant<int, 0x141>{});
+  if constexpr (V >= 16) step(std::integral_constant<int, 0x140>{});
+}
+
 // Sum over a wave by DPP within rows of 16 lanes and lane reads across
 // them (no LDS traffic); the result is uniform.
 __device__ __forceinline__ double wave_sum_dpp(double a) {
@@ -627,7 +647,9 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // 16, 16 ta + l % 16) and B[k][j] = Y(q0 + l / 16, 16 tb + l % 16); lane l
 // holds D[l / 16 + 4 e][l % 16] of the product.  kByRow: Y(q, i) = y[i ys
 // + q] (X rows: G = X X^T); otherwise Y(q, i) = y[q ys + i] (G = X^T X).
-// Indices a >= m and rows q >= len read 0.
+// Rows q >= len read 0; indices a >= m read what the buffer holds there
+// (row a of an operand reaches only row a or column a of its tile, and
+// those entries are not stored).
 template <int kT>
 struct GramTiles {
   f64x4 acc[kT];
@@ -678,13 +700,23 @@ struct GramTiles {
         const int a = 16 * ta[i] + li, b = 16 * tb[i] + li;  // < 128
         const float fa = kByRow ? y[a * ys + q] : y[qc * ys + a];
         const float fb = kByRow ? y[b * ys + q] : y[qc * ys + b];
+        // rows a, b >= m need no mask: row a of the operand only reaches row a
+        // of the tile, and tile entries past m - 1 are never stored; the K
+        // tail past len does reach every entry and is masked
         const bool ok = kByRow || q < len;
-        xa[i] = ok && a < m ? static_cast<double>(fa) : 0.0;
-        xb[i] = ok && b < m ? static_cast<double>(fb) : 0.0;
+        xa[i] = ok ? static_cast<double>(fa) : 0.0;
+        xb[i] = ok ? static_cast<double>(fb) : 0.0;
       }
 #pragma unroll
       for (int i = 0; i < kT; ++i)
         acc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[i], xb[i], acc[i], 0, 0, 0);
+      // all operand reads of the step, then their conversions, then the
+      // products: the reads are in flight together (one LDS latency per
+      // step, overlapping the previous step's products) instead of each
+      // product waiting for its own two reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2 * kT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kT, 0);
     }
   }
 
@@ -728,6 +760,87 @@ __device__ __noinline__ void gram_block(const float* y_, int ys_, int m_, int le
   gt.template accumulate<kByRow>((const lds_f32*)y_, ys, m, len);
   if (kByRow) __syncthreads();
   gt.store(last, m, G, P);
+}
+
+// G = X X^T of a run's rows held in LDS (Y(q, i) = y[i ys + q], q < len, a
+// multiple of 4), in one pass, with the tiles dealt so that each wave reads
+// few row blocks per K step: the 16-row blocks [0, 2H) cover m, waves 0 and
+// 1 take the upper triangles of blocks [0, H) and [H, 2H), waves 2 and 3
+// the two halves (by rows) of the rectangle [0, H) x [H, 2H).  A wave loads
+// each of its row blocks once per K step and reuses it for every tile
+// that has it (the dealing of gram_block reads two blocks per tile).
+// Operand and output lane layouts as in GramTiles.  Tiles of rows >= m are
+// computed and not stored.  A call of its own; X may share its LDS with
+// G: every read of X comes before the barrier, every store after it.
+template <int NR, int NC, bool kTri>
+__device__ __forceinline__ void gram_rows_tiles(const lds_f32* y, int ys, int m, int len,
+                                                lds_f64* G, int P, int r0, int c0) {
+  constexpr int kTiles = kTri ? NR * (NR + 1) / 2 : NR * NC;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int li = lane & 15, lk = lane >> 4;
+  f64x4 acc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const lds_f32* yr = y + (16 * r0 + li) * ys + lk;
+  const lds_f32* yc = y + (16 * c0 + li) * ys + lk;
+#pragma unroll 2
+  for (int q0 = 0; q0 < len; q0 += 4) {
+    double xr[NR], xc[kTri ? 1 : NC];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) xr[i] = static_cast<double>(yr[16 * i * ys + q0]);
+    if constexpr (!kTri) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) xc[j] = static_cast<double>(yc[16 * j * ys + q0]);
+    }
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+#pragma unroll
+      for (int j = kTri ? i : 0; j < (kTri ? NR : NC); ++j, ++t)
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[i], kTri ? xr[j] : xc[kTri ? 0 : j],
+                                                      acc[t], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+#pragma unroll
+    for (int j = kTri ? i : 0; j < (kTri ? NR : NC); ++j, ++t) {
+      const int ta = r0 + i, tb = (kTri ? r0 : c0) + j;
+      const int b = 16 * tb + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * ta + lk + 4 * e;
+        if (a < m && b < m) {
+          G[a * P + b] = acc[t][e];
+          if (ta != tb) G[b * P + a] = acc[t][e];
+        }
+      }
+    }
+  }
+}
+
+template <int H>
+__device__ __noinline__ void gram_rows(const float* y_, int ys_, int m_, int len_, double* G_,
+                                       int P_) {
+  const int ys = __builtin_amdgcn_readfirstlane(ys_);
+  const int m = __builtin_amdgcn_readfirstlane(m_);
+  const int len = __builtin_amdgcn_readfirstlane(len_);
+  const int P = __builtin_amdgcn_readfirstlane(P_);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const lds_f32* y = (const lds_f32*)y_;
+  lds_f64* G = (lds_f64*)G_;
+  constexpr int kRa = (H + 1) / 2;  // rectangle rows of wave 2; wave 3 takes H - kRa
+  if (wv < 2) {
+    gram_rows_tiles<H, H, true>(y, ys, m, len, G, P, wv * H, wv * H);
+  } else if (wv == 2) {
+    gram_rows_tiles<kRa, H, false>(y, ys, m, len, G, P, 0, H);
+  } else if constexpr (H - kRa > 0) {
+    gram_rows_tiles<H - kRa, H, false>(y, ys, m, len, G, P, kRa, H);
+  } else {
+    __syncthreads();  // no tiles: only the barrier the others wait at
+  }
 }
 
 // S[k][e] = sum over t < n of X[t][e] R[k][t] (k < rj <= 32, e < d; X: n
@@ -905,8 +1018,8 @@ __device__ __noinline__ void tridiagonalize(double* A_, int m_, int P_, EigShare
           for (int u = 0; u < kBlk; ++u)
             part[r] = fma(a[r][kBlk * b + u], xv[kBlk * b + u], part[r]);
         }
-        part[r] = group_sum_dpp<L>(part[r]);
       }
+      group_sums_dpp<L>(part);  // rows outside the trailing block sum zeros
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int i = g + kGroups * r;
@@ -1376,49 +1489,113 @@ __device__ __noinline__ void top_eigenvectors(double* A, int m, int P, int rj, E
     }
     __syncthreads();
   }
-  // u = H_0 H_1 ... H_{m-3} z, the last reflector first
-  // row s of A holds reflector s scaled (v_{s+1} = 1), with zeros left of
-  // v_{s+1}; reads stay inside the work array for i < 128, and the entries
-  // past m - 1 (another row's, or never written) are replaced by 0 when
-  // they are used (one step after they are loaded)
-  auto load_v = [&](int s, double (&x)[EV]) {
-    const lds_f64* rs = (const lds_f64*)(A + s * P);
+  // u = H_0 H_1 ... H_{m-3} z, by blocks of four reflectors (a, b, c, d) =
+  // (4 j, ..., 4 j + 3), the last block first.  With alpha_i = v_i . z for
+  // the current z and g_ik = v_i . v_k,
+  //   H_a H_b H_c H_d z = z - f_a v_a - f_b v_b - f_c v_c - f_d v_d,
+  //   f_d = tau_d alpha_d,  f_c = tau_c (alpha_c - g_cd f_d),
+  //   f_b = tau_b (alpha_b - g_bc f_c - g_bd f_d),
+  //   f_a = tau_a (alpha_a - g_ab f_b - g_ac f_c - g_ad f_d):
+  // four group sums per block, interleaved, instead of one per reflector
+  // (the loop is bound by instruction issue, one wave per SIMD, and the
+  // sums are most of its instructions).  Row s of A holds reflector s
+  // scaled (v_{s+1} = 1), with zeros left of v_{s+1}; reflectors past
+  // m - 3 (the first block's padding) count as v = 0, tau = 0.  Reads stay
+  // inside the work array for i < 128 and s < 128; entries past m - 1
+  // (another row's, or never written) are replaced by 0.
+  const int ms = __builtin_amdgcn_readfirstlane(m);  // uniform: scalar loop control
+  const int nblk = (max(ms - 2, 0) + 3) / 4;
+  // LDS views, converted once (generic pointers would make flat accesses)
+  const lds_f64* const Al = (const lds_f64*)A;
+  const lds_f64* const tl = (const lds_f64*)es.tau;
+  lds_f64* const gk = (lds_f64*)es.vb[0];  // [block][6]: g_ab g_ac g_ad g_bc g_bd g_cd
+  static_assert(sizeof(es.vb) >= 6 * 32 * sizeof(double), "products of 32 blocks");
+  {
+    // one block per group of 16 lanes, lane h holding entries h + 16 c
+    const int grp = tid >> 4;
+    const int h = tid & 15;
+    for (int j0 = 0; j0 < nblk; j0 += kCloseThreads / 16) {
+      const int j = min(j0 + grp, nblk - 1);
+      double g6[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int c = 0; c < EV; ++c) x[c] = rs[l + V * c];
-  };
-  double vn[EV];
-  double tn = 0.0;
-  if (m >= 3) {
-    tn = es.tau[m - 3];
-    load_v(m - 3, vn);
+      for (int c = 0; c < 8; ++c) {
+        const int i = h + 16 * c;
+        if (16 * c < ms) {
+          double w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            w[q] = (i < ms && 4 * j + q <= ms - 3) ? Al[(4 * j + q) * P + i] : 0.0;
+          g6[0] = fma(w[0], w[1], g6[0]);
+          g6[1] = fma(w[0], w[2], g6[1]);
+          g6[2] = fma(w[0], w[3], g6[2]);
+          g6[3] = fma(w[1], w[2], g6[3]);
+          g6[4] = fma(w[1], w[3], g6[4]);
+          g6[5] = fma(w[2], w[3], g6[5]);
+        }
+      }
+      group_sums_dpp<16>(g6);
+      if (h < 6 && j0 + grp < nblk) {
+        double gv = g6[0];
+#pragma unroll
+        for (int q = 1; q < 6; ++q) gv = h == q ? g6[q] : gv;
+        gk[6 * j + h] = gv;
+      }
+    }
   }
+  __syncthreads();
   bool inm[EV];
 #pragma unroll
-  for (int c = 0; c < EV; ++c) inm[c] = l + V * c < m;
-  for (int s = m - 3; s >= 0; --s) {
-    double v[EV];
-    const double ts = keep(tn);
+  for (int c = 0; c < EV; ++c) inm[c] = l + V * c < ms;
+  auto apply = [&](int j, auto first) {
+    double v[4][EV], t[4], g[6];
 #pragma unroll
-    for (int c = 0; c < EV; ++c) {
-      const double kx = keep(vn[c]);
-      v[c] = inm[c] ? kx : 0.0;
-    }
-    if (s > 0) {
-      tn = es.tau[s - 1];
-      load_v(s - 1, vn);
-    }
-    double d0 = 0.0, d1 = 0.0;
+    for (int q = 0; q < 4; ++q) {
+      const int s = 4 * j + q;
+      const lds_f64* rs = Al + s * P;
+      if constexpr (decltype(first)::value) {
+        const bool live = s <= ms - 3;
 #pragma unroll
-    for (int c = 0; c < EV; ++c) {
-      if (c & 1)
-        d1 = fma(v[c], y[c], d1);
-      else
-        d0 = fma(v[c], y[c], d0);
-    }
-    const double f = ts * group_sum_dpp<V>(d0 + d1);  // tau_s = 0: no change
+        for (int c = 0; c < EV; ++c) v[q][c] = live ? rs[l + V * c] : 0.0;
+        t[q] = live ? tl[s] : 0.0;
+      } else {
 #pragma unroll
-    for (int c = 0; c < EV; ++c) y[c] = fma(-f, v[c], y[c]);
-  }
+        for (int c = 0; c < EV; ++c) v[q][c] = rs[l + V * c];
+        t[q] = tl[s];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 6; ++q) g[q] = gk[6 * j + q];
+    // only column blocks that reach past m - 1 need the mask (a uniform test)
+#pragma unroll
+    for (int c = 0; c < EV; ++c)
+      if (V * (c + 1) > ms) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q][c] = inm[c] ? v[q][c] : 0.0;
+      }
+    double al[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double d0 = v[q][0] * y[0], d1 = 0.0;
+#pragma unroll
+      for (int c = 1; c < EV; ++c) {
+        if (c & 1)
+          d1 = fma(v[q][c], y[c], d1);
+        else
+          d0 = fma(v[q][c], y[c], d0);
+      }
+      al[q] = EV > 1 ? d0 + d1 : d0;
+    }
+    group_sums_dpp<V>(al);
+    const double fd = t[3] * al[3];
+    const double fc = t[2] * fma(-g[5], fd, al[2]);
+    const double fb = t[1] * fma(-g[4], fd, fma(-g[3], fc, al[1]));
+    const double fa = t[0] * fma(-g[2], fd, fma(-g[1], fc, fma(-g[0], fb, al[0])));
+#pragma unroll
+    for (int c = 0; c < EV; ++c)
+      y[c] = fma(-fa, v[0][c], fma(-fb, v[1][c], fma(-fc, v[2][c], fma(-fd, v[3][c], y[c]))));
+  };
+  if (nblk > 0) apply(nblk - 1, std::true_type{});
+  for (int j = nblk - 2; j >= 0; --j) apply(j, std::false_type{});
   __syncthreads();
   if (kk < rj) {
     const double lam = es.lam[kk] / es.lim[2];
@@ -1499,25 +1676,26 @@ __device__ __forceinline__ void factor_run(int n, int d, int rank, const RunLds&
   // ---- Gram matrix and its r_j largest eigenpairs (sig = sigma^2): the
   // tridiagonal path, or Jacobi when the spectrum is clustered there
   auto gram = [&](int Lg, int Pg) {
-    auto run = [&](auto tiles) {
+    auto run = [&](auto tiles, auto half) {
       constexpr int kT = decltype(tiles)::value;
       if (rows_form) {
-        gram_block<kT, true>(x_pre, xp, m, d, work, Pg, 1, 1);
+        gram_rows<decltype(half)::value>(x_pre, xp, m, d, work, Pg);
       } else {
         for_blocks(x_pre, [&](const float* xr, int t0, int rb) {
           gram_block<kT, false>(xr, xp, m, rb, work, Pg, t0 == 0, t0 + rb == n);
         });
       }
     };
-    // tiles per wave: ceil(nt (nt + 1) / 8) for nt = ceil(m / 16) tiles a side
+    // tiles per wave: ceil(nt (nt + 1) / 8) for nt = ceil(m / 16) tiles a
+    // side (gram_block); half the blocks a side, ceil(nt / 2) (gram_rows)
     if (m > 96)
-      run(std::integral_constant<int, 9>());
+      run(std::integral_constant<int, 9>(), std::integral_constant<int, 4>());
     else if (m > 64)
-      run(std::integral_constant<int, 6>());
+      run(std::integral_constant<int, 6>(), std::integral_constant<int, 3>());
     else if (m > 32)
-      run(std::integral_constant<int, 3>());
+      run(std::integral_constant<int, 3>(), std::integral_constant<int, 2>());
     else
-      run(std::integral_constant<int, 1>());
+      run(std::integral_constant<int, 1>(), std::integral_constant<int, 1>());
     for (int idx = tid; idx < m * (Lg - m); idx += kCloseThreads) {  // Jacobi's padding
       const int a = idx / (Lg - m);
       work[a * Pg + m + (idx - a * (Lg - m))] = 0.0;
