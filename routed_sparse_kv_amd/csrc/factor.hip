@@ -1896,15 +1896,26 @@ __global__ __launch_bounds__(kCloseThreads) void close_kernel(
   const int tid = threadIdx.x;
   const RunLds L{work, stage, part, &es, &sh};
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // one item per workgroup (the grid is the item count) and no item loop:
+  // with a loop the compiler computes much of the item's addressing ahead of
+  // it and keeps it in scratch memory across the phase calls
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  {
     const int kv = item & 1;
     const int u = item >> 1;
     const int b = u / Hkv;
     const int h = u - b * Hkv;
+    // the sequence's table entries, read together (one round trip before
+    // the test, one more for the span's padded offset)
     const int la = last_anchor[b];
-    const int n = n_full[b] - la - 1;
-    if (!(h_new[b] > theta[b]) || la < 0 || n <= 0) continue;
+    const int nf = n_full[b];
+    const float hn = h_new[b];
+    const float th = theta[b];
     const int j = n_spans[b];
+    const int n = nf - la - 1;
+    // (j >= 0 always: testing it keeps its read in the first round trip)
+    if (!(hn > th) || la < 0 || n <= 0 || j < 0) return;
     const int r0 = la + 1;
     const int tp = tok_pad[static_cast<size_t>(b) * (S + 1) + j];
     ST* xs = (kv ? v_full : k_full) + static_cast<size_t>(u) * Fp * d;
