@@ -843,69 +843,74 @@ __device__ __noinline__ void gram_rows(const float* y_, int ys_, int m_, int len
   }
 }
 
-// S[k][e] = sum over t < n of X[t][e] R[k][t] (k < rj <= 32, e < d; X: n
-// rows of floats with pitch xp, R: rows of doubles with pitch P, S: pitch
-// d), in fp64 and in order of t.  Thread -> outputs o = tid + q T (k = o /
-// d, e = o % d) for q < nq: with d dividing T (d = 64 or 128) a thread's
-// outputs share the column e, so one load of X[t][e] serves them all; the
-// outputs advance through the rows together, four rows at a time (indices
-// past the last output are clamped and their sums dropped).  A call of its
-// own; ends with a barrier.
+// S[k][e] = sum over t < n of X[t][e] R[k][t] (k < rj <= 32, e < d, d a
+// multiple of 16; X: n rows of floats with pitch xp, R: rows of doubles
+// with pitch P, S: pitch d), in fp64 on 16 x 16 x 4 matrix-core products:
+// the output tiles (16 rows k, 16 columns e), at most 2 x 8, are dealt to
+// the waves in turn (tiles wv + 4 i), each advanced over the rows t four at
+// a time (16 rows per pass); A[k][t] = R[k][t] and B[t][e] = X[t][e], with rows t >= n and k >=
+// rj read as 0.  Lane layouts as in GramTiles.  A call of its own; ends
+// with a barrier.
 __device__ __noinline__ void rows_product(const float* x_, int xp_, int n_, int d_, int rj_,
                                           const double* r_, int P_, double* s_) {
-  constexpr int kOut = 32 * 128 / kCloseThreads;
   const int xp = __builtin_amdgcn_readfirstlane(xp_);
   const int n = __builtin_amdgcn_readfirstlane(n_);
   const int d = __builtin_amdgcn_readfirstlane(d_);
   const int rj = __builtin_amdgcn_readfirstlane(rj_);
   const int P = __builtin_amdgcn_readfirstlane(P_);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const lds_f32* x = (const lds_f32*)x_;
   const lds_f64* r = (const lds_f64*)r_;
   lds_f64* s = (lds_f64*)s_;
-  const int tid = threadIdx.x;
-  const int tot = rj * d;
-  const int nq = (tot + kCloseThreads - 1) / kCloseThreads;
-  const int last = tot > 0 ? tot - 1 : 0;
-  const int e = tid % d;
-  int uo[kOut];
-  double acc[kOut];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int li = lane & 15, lk = lane >> 4;
+  const int net = d / 16;
+  const int ntile = (rj + 15) / 16 * net;  // <= 16
+  f64x4 acc[4];
+  int tk[4], te[4];
 #pragma unroll
-  for (int q = 0; q < kOut; ++q) {
-    uo[q] = min(tid + q * kCloseThreads, last) / d * P;
-    acc[q] = 0.0;
+  for (int i = 0; i < 4; ++i) {
+    const int tile = wv + 4 * i;
+    tk[i] = tile / net;
+    te[i] = tile - tk[i] * net;
+    acc[i] = f64x4{0.0, 0.0, 0.0, 0.0};
   }
-  int t = 0;
-  for (; t + 4 <= n; t += 4) {
-    double xv[4];
+  // four K steps per pass: their operand reads are issued together
+  for (int t0 = 0; t0 < n; t0 += 16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xv[i] = static_cast<double>(x[(t + i) * xp + e]);
+    for (int i = 0; i < 4; ++i) {
+      if (wv + 4 * i >= ntile) break;  // uniform
+      const int k = 16 * tk[i] + li;
+      const int kc = min(k, rj - 1);
+      double a[4], b[4];
 #pragma unroll
-    for (int q0 = 0; q0 < kOut; q0 += 4) {
-      if (q0 >= nq) break;
-      double uv[4][4];
+      for (int st = 0; st < 4; ++st) {
+        // reads at clamped indices (no branch around them), masked after
+        const int t = t0 + 4 * st + lk;
+        const int tc = min(t, n - 1);
+        const double ra = r[kc * P + tc];
+        const double xb = static_cast<double>(x[tc * xp + 16 * te[i] + li]);
+        a[st] = t < n && k < rj ? ra : 0.0;
+        b[st] = t < n ? xb : 0.0;
+      }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) uv[q][i] = r[uo[q0 + q] + t + i];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[q0 + q] = fma(xv[i], uv[q][i], acc[q0 + q]);
+      for (int st = 0; st < 4; ++st)
+        acc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[st], b[st], acc[i], 0, 0, 0);
+      // the eight reads first, then the conversions and masks, then the
+      // products (one LDS latency per pass instead of one per K step)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   }
-  for (; t < n; ++t) {
-    const double xv = static_cast<double>(x[t * xp + e]);
 #pragma unroll
-    for (int q0 = 0; q0 < kOut; q0 += 4) {
-      if (q0 >= nq) break;
+  for (int i = 0; i < 4; ++i) {
+    if (wv + 4 * i >= ntile) break;
 #pragma unroll
-      for (int q = q0; q < q0 + 4; ++q) acc[q] = fma(xv, r[uo[q] + t], acc[q]);
+    for (int q = 0; q < 4; ++q) {
+      const int k = 16 * tk[i] + lk + 4 * q;
+      if (k < rj) s[k * d + 16 * te[i] + li] = acc[i][q];
     }
-  }
-#pragma unroll
-  for (int q = 0; q < kOut; ++q) {
-    const int o = tid + q * kCloseThreads;
-    if (o < tot) s[o] = acc[q];
   }
   __syncthreads();
 }
