@@ -235,6 +235,9 @@ LONG_RUNS = {
     "f32_d64": ("tiny_fp32_2k", 1, [[64, 90, 5]], {}),
     "bf16_d128_r32": ("serving_b16_bf16", 2, [[40, 128], [33, 70, 150]], {"rank": 32}),
     "f32_d64_r24": ("tiny_fp32_2k", 1, [[48, 90, 20, 12]], {"rank": 24}),
+    # two batches of eigenvectors with 16 lanes per vector (12 and 16 kept)
+    "bf16_d128_r12": ("serving_b16_bf16", 2, [[40, 128], [33, 70, 150]], {"rank": 12}),
+    "bf16_d128_r16": ("serving_b16_bf16", 2, [[40, 128], [33, 70, 150]], {"rank": 16}),
 }
 
 
